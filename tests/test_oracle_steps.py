@@ -1,0 +1,393 @@
+"""Pins of the oracle's per-token steps and of the layer / stack wiring.
+
+Every pin is checked against something other than the oracle's own formula: closed forms
+of special cases, invariants the pages or the mathematics fix, and a brute-force product
+form of the recurrence.  Each pin is also run against a planted mistake (a mutant of the
+oracle function, on the CPU) to show that it bites.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kda as ok
+
+RNG = np.random.default_rng
+
+
+# ----------------------------------------------------------------------------------------
+# conv + SiLU + window roll
+# ----------------------------------------------------------------------------------------
+def pin_conv(conv_fn) -> bool:
+    rng = RNG(1)
+    C = 12
+    p_seq = rng.standard_normal((6, C))
+    # identity kernel: a = SiLU(p), whatever the window holds
+    w_id = np.zeros((C, 4)); w_id[:, 3] = 1.0
+    Z = rng.standard_normal((3, C))
+    a, Z2 = conv_fn(Z, p_seq[0], w_id)
+    ok1 = np.allclose(a, p_seq[0] / (1 + np.exp(-p_seq[0])), rtol=1e-15, atol=0)
+    ok2 = np.array_equal(Z2, np.concatenate([Z[1:], p_seq[:1]]))
+    # impulse at t=0 then zeros: outputs walk back through the taps 3, 2, 1, 0
+    w = rng.standard_normal((C, 4))
+    Z = np.zeros((3, C))
+    imp = rng.standard_normal(C)
+    outs = []
+    for t in range(4):
+        a, Z = conv_fn(Z, imp if t == 0 else np.zeros(C), w)
+        outs.append(a)
+    ok3 = all(np.allclose(outs[t], ok.silu(w[:, 3 - t] * imp), rtol=1e-14, atol=1e-300)
+              for t in range(4))
+    return ok1 and ok2 and ok3
+
+
+def test_conv_pins():
+    assert pin_conv(ok.conv_silu)
+
+
+def test_conv_mutant_reversed_taps():
+    def mutant(Z, p, w):
+        return ok.conv_silu(Z, p, w[:, ::-1])
+    assert not pin_conv(mutant)
+
+
+def test_conv_mutant_window_not_rolled():
+    def mutant(Z, p, w):
+        a, _ = ok.conv_silu(Z, p, w)
+        return a, np.concatenate([p[None, :], Z[:-1]])
+    assert not pin_conv(mutant)
+
+
+# ----------------------------------------------------------------------------------------
+# head split + L2 norms
+# ----------------------------------------------------------------------------------------
+def pin_split(split_fn) -> bool:
+    rng = RNG(2)
+    H, dk, dv = 3, 8, 5
+    a = rng.standard_normal(2 * H * dk + H * dv) * 3
+    q, k, v = split_fn(a, H, dk, dv, 0.0)
+    good = np.allclose(np.linalg.norm(k, axis=1), 1.0, rtol=1e-14)
+    good &= np.allclose(np.linalg.norm(q, axis=1), dk ** -0.5, rtol=1e-14)
+    # q of head 1 is parallel to channels [dk, 2dk), k of head 0 to [H dk, H dk + dk)
+    good &= np.allclose(q[1] / np.linalg.norm(q[1]), a[dk:2 * dk] / np.linalg.norm(a[dk:2 * dk]))
+    good &= np.allclose(k[0] / np.linalg.norm(k[0]), a[H * dk:H * dk + dk] / np.linalg.norm(a[H * dk:H * dk + dk]))
+    good &= np.array_equal(v[2], a[2 * H * dk + 2 * dv: 2 * H * dk + 3 * dv])
+    return bool(good)
+
+
+def test_split_pins():
+    assert pin_split(ok.split_heads)
+
+
+def test_split_mutant_scale_on_k():
+    def mutant(a, H, dk, dv, eps):
+        q, k, v = ok.split_heads(a, H, dk, dv, eps)
+        return q / dk ** -0.5, k * dk ** -0.5, v
+    assert not pin_split(mutant)
+
+
+# ----------------------------------------------------------------------------------------
+# forget gate
+# ----------------------------------------------------------------------------------------
+def pin_gate(gate_fn) -> bool:
+    # softplus(0) = ln 2 and exp(A_log=0) = 1  =>  alpha = exp(-ln 2) = 1/2
+    a = gate_fn(np.zeros((2, 3)), np.zeros(2))
+    good = np.allclose(a, 0.5, rtol=1e-15)
+    # large positive f: softplus(f) -> f, alpha -> exp(-e^{A_log} f)
+    f = np.full((1, 2), 40.0)
+    good &= np.allclose(gate_fn(f, np.array([math.log(0.25)])), math.exp(-10.0), rtol=1e-12)
+    # large negative f: softplus(f) -> e^f, alpha -> 1 - e^{A_log} e^f
+    f = np.full((1, 1), -30.0)
+    good &= np.allclose(gate_fn(f, np.array([0.0])), math.exp(-math.exp(-30.0)), rtol=1e-15)
+    # alpha in (0, 1], and A_log -> -inf gives exactly 1
+    rng = RNG(3)
+    al = gate_fn(rng.standard_normal((4, 16)) * 3, rng.uniform(-1, 0, 4))
+    good &= bool(np.all((al > 0) & (al < 1)))
+    good &= np.array_equal(gate_fn(rng.standard_normal((2, 4)), np.array([-np.inf, -np.inf])),
+                           np.ones((2, 4)))
+    return bool(good)
+
+
+def test_gate_pins():
+    assert pin_gate(ok.forget_gate)
+
+
+def test_gate_mutant_softplus_sign():
+    def mutant(f, a_log):
+        return np.exp(-np.exp(a_log)[:, None] * ok.softplus(-f))
+    assert not pin_gate(mutant)
+
+
+def test_sigmoid_softplus_closed_forms():
+    assert ok.sigmoid(0.0) == 0.5
+    assert abs(ok.softplus(0.0) - math.log(2.0)) < 1e-16
+    z = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(ok.softplus(z), np.log1p(np.exp(z)), rtol=1e-14)
+    np.testing.assert_allclose(ok.sigmoid(z) + ok.sigmoid(-z), 1.0, rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------------------
+# delta rule
+# ----------------------------------------------------------------------------------------
+def _unit(v):
+    return v / np.linalg.norm(v, axis=-1, keepdims=True)
+
+
+def brute_force_states(S0, k, v, alpha, beta):
+    """S_T = (prod_t A_t) S0 + sum_s (prod_{t>s} A_t) beta_s k_s v_s^T with
+    A_t = (I - beta_t k_t k_t^T) diag(alpha_t), recomputed from S0 for every T."""
+    T, dk = k.shape
+    out = []
+    for Tn in range(1, T + 1):
+        S = np.zeros_like(S0)
+        for s in range(-1, Tn):
+            P = np.eye(dk)
+            for t in range(s + 1, Tn):
+                A_t = (np.eye(dk) - beta[t] * np.outer(k[t], k[t])) @ np.diag(alpha[t])
+                P = A_t @ P
+            S = S + (P @ S0 if s < 0 else P @ (beta[s] * np.outer(k[s], v[s])))
+        out.append(S)
+    return out
+
+
+def pin_delta(step_fn) -> bool:
+    rng = RNG(4)
+    H, dk, dv = 2, 6, 5
+    good = True
+    # beta = 1, unit k: the updated state maps k exactly onto v
+    S = rng.standard_normal((H, dk, dv))
+    k = _unit(rng.standard_normal((H, dk)))
+    v = rng.standard_normal((H, dv))
+    q = rng.standard_normal((H, dk))
+    alpha = rng.uniform(0.2, 1.0, (H, dk))
+    S2, _ = step_fn(S, q, k, v, alpha, np.ones(H))
+    good &= np.allclose(np.einsum("hij,hi->hj", S2, k), v, rtol=0, atol=1e-13)
+    # alpha = 1, beta = 0: unchanged
+    S2, _ = step_fn(S, q, k, v, np.ones((H, dk)), np.zeros(H))
+    good &= np.array_equal(S2, S)
+    # S0 = 0, one token: S = beta k v^T, o = beta (k.q) v
+    beta = rng.uniform(0.1, 1.0, H)
+    S2, o = step_fn(np.zeros((H, dk, dv)), q, k, v, alpha, beta)
+    good &= np.allclose(S2, beta[:, None, None] * k[:, :, None] * v[:, None, :], atol=1e-15)
+    good &= np.allclose(o, (beta * np.sum(k * q, 1))[:, None] * v, atol=1e-15)
+    # beta = 0 for T tokens: S_T = diag(prod alpha) S0
+    T = 5
+    al = rng.uniform(0.3, 1.0, (T, H, dk))
+    S2 = S
+    for t in range(T):
+        S2, _ = step_fn(S2, q, k, v, al[t], np.zeros(H))
+    good &= np.allclose(S2, np.prod(al, 0)[:, :, None] * S, rtol=1e-14)
+    # brute force over T tokens from S0 (rectangular dk != dv catches transposes)
+    T = 6
+    ks = _unit(rng.standard_normal((T, H, dk)))
+    vs = rng.standard_normal((T, H, dv))
+    qs = rng.standard_normal((T, H, dk))
+    als = rng.uniform(0.3, 1.0, (T, H, dk))
+    bs = rng.uniform(0.0, 1.0, (T, H))
+    S2 = S
+    for t in range(T):
+        S2, o = step_fn(S2, qs[t], ks[t], vs[t], als[t], bs[t])
+        for h in range(H):
+            ref = brute_force_states(S[h], ks[:t + 1, h], vs[:t + 1, h], als[:t + 1, h], bs[:t + 1, h])[-1]
+            good &= np.allclose(S2[h], ref, rtol=1e-12, atol=1e-12)
+            good &= np.allclose(o[h], ref.T @ qs[t, h], rtol=1e-12, atol=1e-12)
+    return bool(good)
+
+
+def test_delta_rule_pins():
+    assert pin_delta(ok.delta_rule_step)
+
+
+@pytest.mark.parametrize("which", ["read_before_update", "decay_on_values", "no_decay_in_error",
+                                   "transposed_readout"])
+def test_delta_rule_mutants(which):
+    def mutant(S, q, k, v, alpha, beta):
+        if which == "read_before_update":
+            S1 = alpha[:, :, None] * S
+            S_new, _ = ok.delta_rule_step(S, q, k, v, alpha, beta)
+            return S_new, np.einsum("hij,hi->hj", S1, q)
+        if which == "decay_on_values":
+            if S.shape[1] != S.shape[2]:
+                alpha = np.resize(alpha, (S.shape[0], S.shape[2]))
+            S1 = S * alpha[:, None, :]
+        else:
+            S1 = alpha[:, :, None] * S
+        base = S if which == "no_decay_in_error" else S1
+        e = np.einsum("hij,hi->hj", base, k)
+        delta = beta[:, None] * (v - e)
+        S_new = S1 + k[:, :, None] * delta[:, None, :]
+        if which == "transposed_readout":
+            n = min(S.shape[1], S.shape[2])
+            o = np.einsum("hij,hj->hi", S_new[:, :n, :n], q[:, :n])
+            o = np.resize(o, (S.shape[0], S.shape[2]))
+        else:
+            o = np.einsum("hij,hi->hj", S_new, q)
+        return S_new, o
+    assert not pin_delta(mutant)
+
+
+# ----------------------------------------------------------------------------------------
+# gated norm and RMSNorm
+# ----------------------------------------------------------------------------------------
+def test_gated_norm_rms_is_one():
+    rng = RNG(5)
+    o = rng.standard_normal((4, 32)) * 3
+    n = ok.gated_norm(o, np.ones((4, 32)), np.ones(32), 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(n * n, axis=1)), 1.0, rtol=1e-14)
+    g = rng.uniform(0.1, 1, (4, 32))
+    n2 = ok.gated_norm(o, g, np.ones(32), 0.0)
+    np.testing.assert_allclose(n2 / g, n, rtol=1e-14)
+    # per head: scaling one head does not change another
+    o2 = o.copy(); o2[0] *= 100
+    np.testing.assert_allclose(ok.gated_norm(o2, g, np.ones(32), 0.0)[1:], n2[1:], rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------
+# layer and stack wiring
+# ----------------------------------------------------------------------------------------
+def _tiny_layer(seed=7, **over):
+    w = synth.WORKLOADS["tiny"]
+    run = synth.draw_run(synth.scaled(w, seed=seed, steps=2))
+    L = ok.prepare_layer(run.layers[0], "f32", w.dims.n_heads, w.dims.d_k, w.dims.d_v)
+    for k, v in over.items():
+        setattr(L, k, v)
+    return L, run
+
+
+def pin_single_token(layer_fn) -> bool:
+    """S0 = 0, empty window, one token, RMSNorm eps 0:
+    o_h = beta_h (k_h . q_h) v_h, so n_h = sign(k_h . q_h) v_h / rms(v_h) * gate_h and
+    out = W_o n, independent of alpha and of |beta|."""
+    L, run = _tiny_layer(norm_eps=0.0)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    u = run.x[0, 0, 0].astype(np.float64)
+    out, _, _ = layer_fn(L, u[None, :], np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+    w3 = L.conv_w[:, 3]
+    K = H * dk
+    sl = lambda y: y / (1 + np.exp(-y))
+    qa = sl(w3[:K] * (L.wq @ u)).reshape(H, dk)
+    ka = sl(w3[K:2 * K] * (L.wk @ u)).reshape(H, dk)
+    va = sl(w3[2 * K:] * (L.wv @ u)).reshape(H, dv)
+    gate = 1 / (1 + np.exp(-(L.gb @ (L.ga @ u)))).reshape(H, dv)
+    sgn = np.sign(np.sum(qa * ka, axis=1))
+    n = sgn[:, None] * va / np.sqrt(np.mean(va * va, axis=1, keepdims=True)) * gate
+    return bool(np.allclose(out[0], L.wo @ n.reshape(-1), rtol=1e-10, atol=1e-12))
+
+
+def pin_two_tokens_projection(layer_fn) -> bool:
+    """alpha = 1 (A_log = -inf), beta = 1 (huge beta logits), identity conv, S0 = 0:
+    S_2 = (I - k2 k2^T) k1 v1^T + k2 v2^T, o_2 = v1 (k1.q2 - (k1.k2)(k2.q2)) + v2 (k2.q2).
+    Distinguishes the q and k slots (unlike the single-token form)."""
+    L, run = _tiny_layer(seed=8, norm_eps=0.0, l2_eps=0.0)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    L.a_log = np.full(H, -np.inf)
+    L.wbeta = np.abs(L.wbeta) * 1e4          # logits >> 40: sigmoid == 1 in float64
+    cw = np.zeros_like(L.conv_w); cw[:, 3] = 1.0
+    L.conv_w = cw
+    U = np.abs(run.x[:2, 0, 0].astype(np.float64))
+    out, S_end, _ = layer_fn(L, U, np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+    K = H * dk
+    sl = lambda y: y / (1 + np.exp(-y))
+    good = True
+    for t in range(2):
+        assert np.all(L.wbeta @ U[t] > 40)
+    qs = [sl(L.wq @ U[t]).reshape(H, dk) for t in range(2)]
+    ks = [sl(L.wk @ U[t]).reshape(H, dk) for t in range(2)]
+    vs = [sl(L.wv @ U[t]).reshape(H, dv) for t in range(2)]
+    qs = [q / np.linalg.norm(q, axis=1, keepdims=True) * dk ** -0.5 for q in qs]
+    ks = [k / np.linalg.norm(k, axis=1, keepdims=True) for k in ks]
+    gate = 1 / (1 + np.exp(-(L.gb @ (L.ga @ U[1])))).reshape(H, dv)
+    o2 = np.empty((H, dv))
+    for h in range(H):
+        k1, k2, q2, v1, v2 = ks[0][h], ks[1][h], qs[1][h], vs[0][h], vs[1][h]
+        o2[h] = v1 * (k1 @ q2 - (k1 @ k2) * (k2 @ q2)) + v2 * (k2 @ q2)
+        S2 = np.outer(k1, v1) - np.outer(k2, (k2 @ k1) * v1) + np.outer(k2, v2)
+        good &= np.allclose(S_end[h], S2, rtol=1e-9, atol=1e-9)
+    n = o2 / np.sqrt(np.mean(o2 * o2, axis=1, keepdims=True)) * gate
+    good &= np.allclose(out[1], L.wo @ n.reshape(-1), rtol=1e-8, atol=1e-10)
+    return bool(good)
+
+
+def test_layer_single_token_closed_form():
+    assert pin_single_token(ok.layer_forward)
+
+
+def test_layer_two_token_projection_form():
+    assert pin_two_tokens_projection(ok.layer_forward)
+
+
+@pytest.mark.parametrize("which", ["qk_swapped", "v_from_k", "wo_rows_permuted", "gate_on_o"])
+def test_layer_wiring_mutants(monkeypatch, which):
+    real_split = ok.split_heads
+    real_norm = ok.gated_norm
+    real = ok.layer_forward
+    if which == "qk_swapped":
+        def split(a, H, dk, dv, eps):
+            K = H * dk
+            b = np.concatenate([a[K:2 * K], a[:K], a[2 * K:]])
+            return real_split(b, H, dk, dv, eps)
+        monkeypatch.setattr(ok, "split_heads", split)
+    elif which == "v_from_k":
+        def split(a, H, dk, dv, eps):
+            q, k, v = real_split(a, H, dk, dv, eps)
+            K = H * dk
+            return q, k, a[K:K + H * dv].reshape(H, dv)
+        monkeypatch.setattr(ok, "split_heads", split)
+    elif which == "gate_on_o":
+        def norm(o, gate, w, eps):
+            return real_norm(o * gate, np.ones_like(gate), w, eps)
+        monkeypatch.setattr(ok, "gated_norm", norm)
+
+    def layer(L, U, S, Z, **kw):
+        if which == "wo_rows_permuted":
+            L = ok.OracleLayer(**{**L.__dict__, "wo": L.wo[::-1].copy()})
+        return real(L, U, S, Z, **kw)
+    assert not (pin_single_token(layer) and pin_two_tokens_projection(layer))
+
+
+def test_stack_zero_output_projection_is_identity():
+    w = synth.scaled(synth.WORKLOADS["tiny"], n_layers=3, prenorm_residual=True, steps=3)
+    run = synth.draw_run(w)
+    d = w.dims
+    layers = [ok.prepare_layer(dr, "f32", d.n_heads, d.d_k, d.d_v) for dr in run.layers]
+    for L in layers:
+        L.wo = np.zeros_like(L.wo)
+    X = run.x[:, 0, 0].astype(np.float64)
+    y, S, Z = ok.stack_step(layers, X, [np.zeros((d.n_heads, d.d_k, d.d_v))] * 3,
+                            [np.zeros((3, d.conv_channels))] * 3)
+    np.testing.assert_array_equal(y, X)
+    assert all(np.abs(s).max() > 0 for s in S)
+
+
+def test_rms_norm_has_unit_rms():
+    x = RNG(6).standard_normal((5, 100)) * 7
+    y = ok.rms_norm(x, 1.0, 0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, rtol=1e-14)
+
+
+def test_verify_commit_semantics():
+    """Accepting all T tokens every step equals plain decode of the flattened token
+    stream; accepting a < T commits exactly the state after the first a tokens."""
+    base = synth.scaled(synth.WORKLOADS["tiny"], n_layers=2, prenorm_residual=True,
+                        batch=2, steps=3, tokens=3, s0_std=0.1)
+    run = synth.draw_run(base)
+    d = base.dims
+    layers = [ok.prepare_layer(dr, "f32", d.n_heads, d.d_k, d.d_v) for dr in run.layers]
+    full = np.full((3, 2), 3, np.int32)
+    y, S, Z = ok.verify_run(layers, run.x, run.s0, full)
+    xflat = run.x.transpose(1, 0, 2, 3).reshape(2, 9, -1).transpose(1, 0, 2)[:, :, None, :]
+    y2, S2, Z2, _ = ok.decode_run(layers, xflat, run.s0, True)
+    np.testing.assert_allclose(y.transpose(1, 0, 2, 3).reshape(2, 9, -1),
+                               y2.transpose(1, 0, 2), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S2, rtol=1e-12, atol=1e-12)
+    # windows hold projections, computed by BLAS over blocks of different widths
+    np.testing.assert_allclose(Z, Z2, rtol=1e-12, atol=1e-14)
+    # one step, accept 2 of 3: state == decode of the first 2 tokens
+    acc = np.array([[2, 1]], np.int32)
+    _, S3, Z3 = ok.verify_run(layers, run.x[:1], run.s0, acc)
+    for b, a in enumerate([2, 1]):
+        xb = run.x[0, b, :a][:, None, None, :]
+        _, S4, Z4, _ = ok.decode_run(layers, xb, run.s0[:, b:b + 1], True)
+        np.testing.assert_allclose(S3[:, b], S4[:, 0], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(Z3[:, b], Z4[:, 0], rtol=1e-12, atol=1e-14)
