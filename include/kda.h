@@ -1,0 +1,187 @@
+/* kda.h -- C ABI of the MI355X (gfx950) KDA / gated-delta-rule decode library.
+ *
+ * The library runs one Kimi Delta Attention layer, or a pre-norm residual stack of them,
+ * for three call shapes: a one-token decode step, a multi-token verify with a later
+ * commit of an accepted prefix, and a chunked prefill.  The step it computes is the
+ * list under "Where the time goes" in "Thirty tiny kernels per layer: a 16% decode win
+ * for GLM-5.3-Flash on Apple Silicon" (frederic.ai), written there as the pure function
+ * (x, conv_state, state) -> (out, new_conv_state, new_state):
+ *   p = [W_q u; W_k u; W_v u]                      (u = x, or RMSNorm(x) in a stack)
+ *   a = SiLU(causal depthwise conv over the last conv_k-1 tokens and p);  window <- p
+ *   q_h = l2norm(a_q,h) * d_k^-1/2,  k_h = l2norm(a_k,h),  v_h = a_v,h
+ *   alpha = exp(-exp(A_log[h]) * softplus(F_b F_a u + dt_bias))   (per key channel)
+ *   beta_h = sigmoid((W_beta u)_h),  gate = sigmoid(G_b G_a u)
+ *   S' = diag(alpha) S;  delta = beta (v - S'^T k);  S = S' + k delta^T;  o = S^T q
+ *   n_h = RMSNorm(o_h) * o_norm_w * gate_h   (per head; torad-labs/llama.cpp PR #84,
+ *                                             the KDA output-gate commit)
+ *   out = W_o n;   stack: x <- x + out
+ *
+ * Conventions for every entry point:
+ *  - Pointers named *_dev are HIP device memory owned by the caller; pointers named
+ *    *_host are host memory owned by the caller.  The library never frees caller memory.
+ *    Device pointers must be 16-byte aligned (KDA_E_ALIGN otherwise).
+ *  - Calls that take a `stream` (a hipStream_t passed as void*, NULL = the null stream)
+ *    are asynchronous on that stream unless stated otherwise.
+ *  - Arguments are validated before anything is enqueued.  On a non-OK return nothing
+ *    was enqueued and no caller buffer was modified; kda_last_error() gives detail.
+ *    Device faults surface at the caller's next synchronisation.
+ *  - Matrices are row-major [out][in]; a GEMV contracts along the contiguous in-dim.
+ *  - One kda_model may be used by one host thread at a time.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_E_ARG = 1,          /* null pointer / bad enum / bad option */
+  KDA_E_SHAPE = 2,        /* unsupported or inconsistent sizes */
+  KDA_E_ALIGN = 3,        /* a device pointer is not 16-byte aligned */
+  KDA_E_DTYPE = 4,        /* unsupported data type for this call */
+  KDA_E_WORKSPACE = 5,    /* workspace / log buffer too small */
+  KDA_E_HIP = 6,          /* a HIP runtime call failed */
+  KDA_E_UNSUPPORTED = 7
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_Q8_0 = 2 } kda_dtype;
+
+typedef enum { KDA_OP_DECODE = 0, KDA_OP_VERIFY = 1, KDA_OP_PREFILL = 2 } kda_op;
+
+typedef struct kda_model kda_model;   /* opaque */
+
+int kda_abi_version(void);
+const char* kda_status_string(int status);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* ------------------------------------------------------------------------------------
+ * Weight packing.
+ * KDA_F32  : [rows][cols] fp32, as given.
+ * KDA_BF16 : [rows][cols] bfloat16 bit patterns, round to nearest even.
+ * KDA_Q8_0 : blocks of 32 consecutive values along a row with one fp16 scale (antirez/ds4
+ *            PR #964, the commit that requantises KDA's projections to Q8_0):
+ *              amax = max|x|, d = fp32(amax/127), d16 = fp16_rne(d),
+ *              q = clamp(round_half_away(fp32(x / d16)), -127, 127), all q = 0 if d16 = 0.
+ *            Device layout: a plane of rows*cols bytes holding q+128, then (at the next
+ *            256-byte boundary) a plane of rows*(cols/32) fp16 scales.  cols % 32 == 0.
+ * ---------------------------------------------------------------------------------- */
+/* Bytes a packed [rows][cols] matrix occupies (0 on an invalid request). */
+size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols);
+
+/* Pack fp32 src_dev [rows][cols] into dst_dev (kda_packed_bytes bytes).  Errors:
+ * KDA_E_DTYPE (unknown dtype), KDA_E_SHAPE (rows/cols <= 0, Q8_0 with cols % 32 != 0). */
+int kda_pack(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+             void* stream);
+
+/* Canonical view of a Q8_0-packed matrix: d16_dev [rows][cols/32] fp16 bit patterns and
+ * qs_dev [rows][cols] int8.  Asynchronous on `stream`. */
+int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
+                    int8_t* qs_dev, void* stream);
+
+/* ------------------------------------------------------------------------------------
+ * Model description.  The library keeps the pointers; it does not copy weights.
+ * ---------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t d_model;           /* D */
+  int32_t n_heads;           /* H */
+  int32_t d_k;               /* 64 or 128 */
+  int32_t d_v;               /* == d_k */
+  int32_t conv_k;            /* 4 */
+  int32_t rank_f;            /* low rank of the forget gate (F_a: [rank_f][D]) */
+  int32_t rank_g;            /* low rank of the output gate (G_a: [rank_g][D]) */
+  int32_t n_layers;
+  int32_t prenorm_residual;  /* 0: y = layer(x); 1: x <- x + layer(RMSNorm(x)) per layer */
+  float norm_eps;            /* RMSNorm eps (pre-norm and output norm) */
+  float l2_eps;              /* q/k L2-norm eps: x / sqrt(sum x^2 + l2_eps) */
+  int32_t wtype;             /* kda_dtype of every projection matrix */
+} kda_dims;
+
+typedef struct {
+  /* packed by kda_pack with dims.wtype; shapes [out][in]:
+   * wq, wk: [H*d_k][D]  wv: [H*d_v][D]  wo: [D][H*d_v]  fa: [rank_f][D]
+   * fb: [H*d_k][rank_f]  wbeta: [H][D]  ga: [rank_g][D]  gb: [H*d_v][rank_g] */
+  const void *wq, *wk, *wv, *wo, *fa, *fb, *wbeta, *ga, *gb;
+  const float* conv_w;    /* [C][conv_k] fp32, C = 2*H*d_k + H*d_v; tap conv_k-1 = current */
+  const float* a_log;     /* [H] */
+  const float* dt_bias;   /* [H*d_k] */
+  const float* o_norm_w;  /* [d_v] or NULL (ones) */
+} kda_layer;
+
+/* Recurrent state of all layers for `batch` sequences. */
+typedef struct {
+  float* S_dev;     /* [n_layers][batch][H][d_k][d_v] fp32, row = key channel */
+  float* conv_dev;  /* [n_layers][batch][conv_k-1][C] fp32, oldest token first */
+  int32_t batch;
+} kda_state;
+
+/* Create a model over caller-owned packed weights (layers[n_layers]).  Errors:
+ * KDA_E_ARG, KDA_E_SHAPE (d_k != d_v, d_k not 64/128, conv_k != 4, D % 32, ranks % 32
+ * for Q8_0, ...), KDA_E_ALIGN, KDA_E_HIP. */
+int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** out);
+void kda_model_destroy(kda_model* m);
+
+/* Options. */
+typedef enum {
+  KDA_OPT_GRAPH = 0,   /* 1 (default): decode steps replay a captured hipGraph of all
+                          layers, re-captured when a pointer or the batch changes */
+  KDA_OPT_TIMING = 1   /* 1: record hipEvents around every kernel launch (no graph) */
+} kda_option;
+int kda_model_set_option(kda_model* m, int option, int64_t value);
+
+/* Kernel kinds reported by kda_timing_query. */
+typedef enum { KDA_K_PROJ = 0, KDA_K_HEAD = 1, KDA_K_OUT = 2, KDA_K_COMMIT = 3,
+               KDA_K_PREFILL = 4, KDA_K_COUNT = 5 } kda_kernel_kind;
+/* Sum of event-timed durations (ms) and launch count per kernel kind since the last
+ * reset; synchronises on the recorded events.  reset != 0 clears the counters. */
+int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset);
+
+/* Device workspace bytes an op needs for `batch` sequences and `tokens` tokens each
+ * (decode: tokens = 1; verify: T; prefill: L). */
+size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t tokens);
+
+/* One decode token for every sequence of the batch (the pure step above, on all layers).
+ * x_dev [B][D] fp32 in, y_dev [B][D] fp32 out (layer output, or the final residual
+ * stream of a stack); st is read and advanced in place.  x_dev and y_dev must not
+ * overlap.  Errors: KDA_E_ARG, KDA_E_ALIGN, KDA_E_SHAPE (st->batch < 1),
+ * KDA_E_WORKSPACE, KDA_E_HIP. */
+int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                    void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Verify (multi-token, read-only on the state): T tokens per sequence, x_dev [B][T][D],
+ * run in order through every layer from the state in st, which is NOT modified.  Writes
+ * y_dev [B][T][D] for every token and a replay log (kda_verify_log_bytes) that
+ * kda_verify_commit uses.  The read-only verify and the later commit of an accepted
+ * prefix are the verify / commit-after-k modes of the gdn_step kernel in the regolith
+ * GDN audit (opus_gdn_qsa, section 2).  1 <= T <= 8. */
+size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T);
+int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
+                     const kda_state* st, void* log_dev, size_t log_bytes, void* ws_dev,
+                     size_t ws_bytes, void* stream);
+/* Commit: advance st to the state and conv window reached after accept_dev[b] tokens
+ * (device int32 [B], each in 1..T; values outside are clamped to that range) of the
+ * last kda_verify_steps on this log.  The result equals decoding those tokens. */
+int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, int32_t T,
+                      const int32_t* accept_dev, void* stream);
+
+/* Chunked prefill of L tokens per sequence through a single-layer model (n_layers == 1,
+ * prenorm_residual == 0): x_dev [B][L][D] (x_dtype KDA_BF16 bit patterns or KDA_F32),
+ * y_dev [B][L][D] fp32; st is read as the initial state and overwritten with the final
+ * state and window.  The delta rule runs in the chunked WY/UT form of the chunk_kda
+ * commit of torad-labs/llama.cpp PR #84 with an fp32 state carried across chunks;
+ * chunk must be 64.  Any L >= 1 (partial last chunk allowed). */
+int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
+                        int32_t chunk, float* y_dev, const kda_state* st, void* ws_dev,
+                        size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

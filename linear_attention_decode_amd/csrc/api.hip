@@ -1,0 +1,534 @@
+// C ABI of the KDA library (include/kda.h): validation, workspace layout, launch
+// sequencing per layer, hipGraph capture of the decode step, and event timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+using namespace kda;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+
+#define KDA_HIP(call)                                                                  \
+  do {                                                                                 \
+    hipError_t e_ = (call);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(KDA_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_));           \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+struct LayerDev {
+  PackedMat wq, wk, wv, wo, fa, fb, wbeta, ga, gb;
+  const float* conv_w;
+  const float* a_log;
+  const float* dt_bias;
+  const float* o_norm_w;
+};
+
+struct GraphKey {
+  const void* x = nullptr;
+  void* y = nullptr;
+  float* S = nullptr;
+  float* conv = nullptr;
+  void* ws = nullptr;
+  int batch = 0;
+  hipStream_t stream = nullptr;
+  bool operator==(const GraphKey& o) const {
+    return x == o.x && y == o.y && S == o.S && conv == o.conv && ws == o.ws &&
+           batch == o.batch && stream == o.stream;
+  }
+};
+
+struct TimedLaunch {
+  hipEvent_t a, b;
+  int kind;
+};
+
+struct kda_model {
+  kda_dims d;
+  std::vector<LayerDev> layers;
+  int C = 0, Kq = 0, V = 0, proj_rows = 0, proj_stride = 0;
+  float q_scale = 0.f;
+  // options
+  bool use_graph = true;
+  bool timing = false;
+  // graph cache (decode)
+  hipStream_t cap_stream = nullptr;
+  hipGraphExec_t exec = nullptr;
+  GraphKey key;
+  // timing
+  std::vector<TimedLaunch> pool;
+  size_t used = 0;
+  double total_ms[KDA_K_COUNT] = {0};
+  int64_t count[KDA_K_COUNT] = {0};
+};
+
+// ---------------------------------------------------------------------------------------
+// Workspace layout (decode / verify): proj [N][proj_stride] | o [N][V] | gate [N][V] |
+// ss [N][H][V/kHeadCols]; each region 256-byte aligned.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+struct WsLayout {
+  size_t proj = 0, o = 0, gate = 0, ss = 0, total = 0;
+};
+
+WsLayout ws_layout(const kda_model* m, int64_t N) {
+  WsLayout w;
+  size_t off = 0;
+  w.proj = off; off = align_up(off + (size_t)N * m->proj_stride * 4, 256);
+  w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
+  w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
+  w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
+  w.total = off;
+  return w;
+}
+
+int flush_timing(kda_model* m) {
+  for (size_t i = 0; i < m->used; ++i) {
+    TimedLaunch& t = m->pool[i];
+    KDA_HIP(hipEventSynchronize(t.b));
+    float ms = 0.f;
+    KDA_HIP(hipEventElapsedTime(&ms, t.a, t.b));
+    m->total_ms[t.kind] += ms;
+    m->count[t.kind] += 1;
+  }
+  m->used = 0;
+  return KDA_OK;
+}
+
+// Launch wrapper: optional event pair around the launch.
+template <typename F>
+int timed(kda_model* m, int kind, hipStream_t s, bool record, F&& launch) {
+  TimedLaunch* t = nullptr;
+  if (record) {
+    if (m->used >= 65536) {
+      int r = flush_timing(m);
+      if (r != KDA_OK) return r;
+    }
+    if (m->used == m->pool.size()) {
+      TimedLaunch n{};
+      n.kind = kind;
+      KDA_HIP(hipEventCreate(&n.a));
+      KDA_HIP(hipEventCreate(&n.b));
+      m->pool.push_back(n);
+    }
+    t = &m->pool[m->used++];
+    t->kind = kind;
+    KDA_HIP(hipEventRecord(t->a, s));
+  }
+  hipError_t e = launch();
+  if (e != hipSuccess) return fail(KDA_E_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (record) KDA_HIP(hipEventRecord(t->b, s));
+  return KDA_OK;
+}
+
+// Segment table of the fused input projection: q | k | v | f_a | g_a | beta.
+void proj_segments(const kda_model* m, const LayerDev& L, GemvParams& p, bool conv) {
+  const kda_dims& d = m->d;
+  const PackedMat mats[6] = {L.wq, L.wk, L.wv, L.fa, L.ga, L.wbeta};
+  const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
+  int tile = 0, off = 0;
+  for (int i = 0; i < 6; ++i) {
+    GemvSeg& s = p.seg[i];
+    s.m = mats[i];
+    s.rows = rows[i];
+    s.first_tile = tile;
+    s.out_off = off;
+    s.conv_chan = (conv && i < 3) ? off : -1;
+    tile += (rows[i] + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
+    off += rows[i];
+  }
+  p.nseg = 6;
+}
+
+int proj_grid(const GemvParams& p) {
+  const GemvSeg& s = p.seg[p.nseg - 1];
+  return s.first_tile + (s.rows + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
+}
+
+// One layer of decode (T = 1) or verify (T > 1): projections, per-head step, o_proj.
+int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
+                  float* S, float* win, float* proj, const WsLayout& wl, char* ws,
+                  bool write_state, hipStream_t s, bool rec) {
+  const kda_dims& d = m->d;
+  const LayerDev& L = m->layers[l];
+  const int N = B * T;
+  const bool decode = (T == 1) && write_state;
+  float* o = reinterpret_cast<float*>(ws + wl.o);
+  float* gate = reinterpret_cast<float*>(ws + wl.gate);
+  float* ss = reinterpret_cast<float*>(ws + wl.ss);
+
+  GemvParams pp;
+  proj_segments(m, L, pp, decode);
+  pp.K = d.d_model;
+  pp.N = N;
+  pp.x = x_in;
+  pp.x_stride = d.d_model;
+  pp.prenorm = d.prenorm_residual;
+  pp.eps = d.norm_eps;
+  pp.out = proj;
+  pp.out_stride = m->proj_stride;
+  pp.conv_w = L.conv_w;
+  pp.win = win;
+  pp.C = m->C;
+  const int g1 = proj_grid(pp);
+  int r = timed(m, KDA_K_PROJ, s, rec, [&] { return launch_gemv(d.wtype, kProX, pp, g1, s); });
+  if (r) return r;
+
+  HeadParams hp;
+  hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
+  hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
+  hp.B = B; hp.T = T;
+  hp.proj = proj; hp.proj_stride = m->proj_stride;
+  hp.conv_in_head = decode ? 0 : 1;
+  hp.win = win; hp.conv_w = L.conv_w;
+  hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
+  hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
+  hp.S = S; hp.write_state = write_state ? 1 : 0;
+  hp.ntok = nullptr; hp.write_out = 1;
+  hp.o = o; hp.gate = gate; hp.ss = ss;
+  hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
+  r = timed(m, KDA_K_HEAD, s, rec, [&] { return launch_head(hp, s); });
+  if (r) return r;
+
+  GemvParams po;
+  po.seg[0].m = L.wo;
+  po.seg[0].rows = d.d_model;
+  po.seg[0].first_tile = 0;
+  po.seg[0].out_off = 0;
+  po.seg[0].conv_chan = -1;
+  po.nseg = 1;
+  po.K = m->V;
+  po.N = N;
+  po.o = o; po.gate = gate; po.ss = ss; po.onw = L.o_norm_w;
+  po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / kHeadCols;
+  po.eps = d.norm_eps;
+  po.out = y;
+  po.out_stride = d.d_model;
+  po.resid = d.prenorm_residual ? x_in : nullptr;
+  const int g2 = (d.d_model + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
+  return timed(m, KDA_K_OUT, s, rec, [&] { return launch_gemv(d.wtype, kProGatedNorm, po, g2, s); });
+}
+
+size_t state_layer_stride(const kda_model* m, int B) {
+  return (size_t)B * m->d.n_heads * m->d.d_k * m->d.d_v;
+}
+size_t win_layer_stride(const kda_model* m, int B) { return (size_t)B * 3 * m->C; }
+
+int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, char* ws,
+                   hipStream_t s, bool rec) {
+  const int B = st->batch;
+  WsLayout wl = ws_layout(m, B);
+  float* proj = reinterpret_cast<float*>(ws + wl.proj);
+  for (int l = 0; l < m->d.n_layers; ++l) {
+    const float* xin = (l == 0 || !m->d.prenorm_residual) ? x : y;
+    int r = enqueue_layer(m, l, xin, y, B, 1, st->S_dev + l * state_layer_stride(m, B),
+                          st->conv_dev + l * win_layer_stride(m, B), proj, wl, ws, true, s, rec);
+    if (r) return r;
+  }
+  return KDA_OK;
+}
+
+void drop_graph(kda_model* m) {
+  if (m->exec) (void)hipGraphExecDestroy(m->exec);
+  m->exec = nullptr;
+  m->key = GraphKey{};
+}
+
+int check_state(const kda_model* m, const kda_state* st) {
+  if (!st || !st->S_dev || !st->conv_dev) return fail(KDA_E_ARG, "null state");
+  if (st->batch < 1) return fail(KDA_E_SHAPE, "state batch %d < 1", st->batch);
+  if (!aligned16(st->S_dev) || !aligned16(st->conv_dev)) return fail(KDA_E_ALIGN, "state not 16-byte aligned");
+  return KDA_OK;
+}
+
+}  // namespace
+
+// =======================================================================================
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_E_ARG: return "invalid argument";
+    case KDA_E_SHAPE: return "unsupported or inconsistent shape";
+    case KDA_E_ALIGN: return "device pointer not 16-byte aligned";
+    case KDA_E_DTYPE: return "unsupported data type";
+    case KDA_E_WORKSPACE: return "workspace too small";
+    case KDA_E_HIP: return "HIP runtime error";
+    case KDA_E_UNSUPPORTED: return "unsupported";
+    default: return "unknown status";
+  }
+}
+
+const char* kda_last_error(void) { return g_err.c_str(); }
+
+size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols) {
+  if (rows <= 0 || cols <= 0) return 0;
+  switch (dtype) {
+    case KDA_F32: return (size_t)rows * cols * 4;
+    case KDA_BF16: return (size_t)rows * cols * 2;
+    case KDA_Q8_0:
+      if (cols % 32) return 0;
+      return q8_scale_offset(rows, cols) + (size_t)rows * (cols / 32) * 2;
+    default: return 0;
+  }
+}
+
+int kda_pack(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+             void* stream) {
+  if (dtype < KDA_F32 || dtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
+  if (!src_dev || !dst_dev) return fail(KDA_E_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0) return fail(KDA_E_SHAPE, "rows/cols must be positive");
+  if (dtype == KDA_Q8_0 && cols % 32) return fail(KDA_E_SHAPE, "Q8_0 needs cols %% 32 == 0");
+  if (!aligned16(src_dev) || !aligned16(dst_dev)) return fail(KDA_E_ALIGN, "pointers must be 16-byte aligned");
+  KDA_HIP(launch_pack(dtype, src_dev, rows, cols, dst_dev, (hipStream_t)stream));
+  return KDA_OK;
+}
+
+int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
+                    int8_t* qs_dev, void* stream) {
+  if (!packed_dev || !d16_dev || !qs_dev) return fail(KDA_E_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0 || cols % 32) return fail(KDA_E_SHAPE, "bad Q8_0 shape");
+  KDA_HIP(launch_unpack_q8(packed_dev, rows, cols, d16_dev, qs_dev, (hipStream_t)stream));
+  return KDA_OK;
+}
+
+int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** out) {
+  if (!dims || !layers || !out) return fail(KDA_E_ARG, "null pointer");
+  *out = nullptr;
+  const kda_dims& d = *dims;
+  if (d.wtype < KDA_F32 || d.wtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown wtype %d", d.wtype);
+  if (d.n_layers < 1 || d.n_heads < 1 || d.d_model < 1) return fail(KDA_E_SHAPE, "sizes must be positive");
+  if (d.d_k != d.d_v) return fail(KDA_E_SHAPE, "d_k must equal d_v");
+  if (d.d_k != 64 && d.d_k != 128) return fail(KDA_E_SHAPE, "d_k must be 64 or 128");
+  if (d.conv_k != 4) return fail(KDA_E_SHAPE, "conv_k must be 4");
+  if (d.rank_f < 1 || d.rank_g < 1 || d.rank_f > 256 || d.rank_g > 256)
+    return fail(KDA_E_SHAPE, "ranks must be in 1..256");
+  const int gran = d.wtype == KDA_Q8_0 ? 32 : (d.wtype == KDA_BF16 ? 8 : 4);
+  if (d.d_model % gran || d.rank_f % gran || d.rank_g % gran || (d.n_heads * d.d_v) % gran)
+    return fail(KDA_E_SHAPE, "input dims must be multiples of %d for this weight type", gran);
+  if (d.d_model % 4) return fail(KDA_E_SHAPE, "d_model %% 4 != 0");
+  if (!(d.norm_eps >= 0.f) || !(d.l2_eps >= 0.f)) return fail(KDA_E_ARG, "eps must be >= 0");
+  kda_model* m = new kda_model();
+  m->d = d;
+  m->Kq = d.n_heads * d.d_k;
+  m->V = d.n_heads * d.d_v;
+  m->C = 2 * m->Kq + m->V;
+  m->proj_rows = m->C + d.rank_f + d.rank_g + d.n_heads;
+  m->proj_stride = (int)align_up(m->proj_rows, 4);
+  m->q_scale = (float)(1.0 / std::sqrt((double)d.d_k));
+  const int64_t D = d.d_model;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const kda_layer& s = layers[l];
+    const void* ptrs[] = {s.wq, s.wk, s.wv, s.wo, s.fa, s.fb, s.wbeta, s.ga, s.gb,
+                          s.conv_w, s.a_log, s.dt_bias};
+    for (const void* p : ptrs) {
+      if (!p) { delete m; return fail(KDA_E_ARG, "layer %d: null parameter pointer", l); }
+      if (!aligned16(p)) { delete m; return fail(KDA_E_ALIGN, "layer %d: parameter not 16-byte aligned", l); }
+    }
+    LayerDev L;
+    L.wq = packed_view(s.wq, d.wtype, m->Kq, D);
+    L.wk = packed_view(s.wk, d.wtype, m->Kq, D);
+    L.wv = packed_view(s.wv, d.wtype, m->V, D);
+    L.wo = packed_view(s.wo, d.wtype, D, m->V);
+    L.fa = packed_view(s.fa, d.wtype, d.rank_f, D);
+    L.fb = packed_view(s.fb, d.wtype, m->Kq, d.rank_f);
+    L.wbeta = packed_view(s.wbeta, d.wtype, d.n_heads, D);
+    L.ga = packed_view(s.ga, d.wtype, d.rank_g, D);
+    L.gb = packed_view(s.gb, d.wtype, m->V, d.rank_g);
+    L.conv_w = s.conv_w;
+    L.a_log = s.a_log;
+    L.dt_bias = s.dt_bias;
+    L.o_norm_w = s.o_norm_w;
+    m->layers.push_back(L);
+  }
+  hipError_t e = gemv_prepare_attributes();
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete m;
+    return fail(KDA_E_HIP, "model setup: %s", hipGetErrorString(e));
+  }
+  *out = m;
+  return KDA_OK;
+}
+
+void kda_model_destroy(kda_model* m) {
+  if (!m) return;
+  drop_graph(m);
+  for (auto& t : m->pool) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+int kda_model_set_option(kda_model* m, int option, int64_t value) {
+  if (!m) return fail(KDA_E_ARG, "null model");
+  switch (option) {
+    case KDA_OPT_GRAPH:
+      m->use_graph = value != 0;
+      if (!m->use_graph) drop_graph(m);
+      return KDA_OK;
+    case KDA_OPT_TIMING:
+      m->timing = value != 0;
+      return KDA_OK;
+    default:
+      return fail(KDA_E_ARG, "unknown option %d", option);
+  }
+}
+
+int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset) {
+  if (!m || kind < 0 || kind >= KDA_K_COUNT) return fail(KDA_E_ARG, "bad timing query");
+  int r = flush_timing(m);
+  if (r) return r;
+  if (total_ms) *total_ms = m->total_ms[kind];
+  if (launches) *launches = m->count[kind];
+  if (reset) {
+    for (int i = 0; i < KDA_K_COUNT; ++i) { m->total_ms[i] = 0; m->count[i] = 0; }
+  }
+  return KDA_OK;
+}
+
+size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t tokens) {
+  if (!m || batch < 1 || tokens < 1) return 0;
+  if (op == KDA_OP_DECODE) return ws_layout(m, batch).total;
+  if (op == KDA_OP_VERIFY) return ws_layout(m, (int64_t)batch * tokens).total;
+  return 0;
+}
+
+int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                    void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!m || !x_dev || !y_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(ws_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  if (ws_bytes < ws_layout(m, st->batch).total)
+    return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, ws_layout(m, st->batch).total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(ws_dev);
+  if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing);
+
+  GraphKey k;
+  k.x = x_dev; k.y = y_dev; k.S = st->S_dev; k.conv = st->conv_dev; k.ws = ws_dev;
+  k.batch = st->batch; k.stream = s;
+  if (!m->exec || !(k == m->key)) {
+    drop_graph(m);
+    hipGraph_t g = nullptr;
+    KDA_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
+    r = enqueue_decode(m, x_dev, y_dev, st, ws, m->cap_stream, false);
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &g);
+    if (r) { if (g) (void)hipGraphDestroy(g); return r; }
+    if (e != hipSuccess) return fail(KDA_E_HIP, "graph capture: %s", hipGetErrorString(e));
+    e = hipGraphInstantiate(&m->exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    if (e != hipSuccess) { m->exec = nullptr; return fail(KDA_E_HIP, "graph instantiate: %s", hipGetErrorString(e)); }
+    m->key = k;
+  }
+  KDA_HIP(hipGraphLaunch(m->exec, s));
+  return KDA_OK;
+}
+
+size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T) {
+  if (!m || batch < 1 || T < 1) return 0;
+  return (size_t)m->d.n_layers * batch * T * m->proj_stride * 4;
+}
+
+int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
+                     const kda_state* st, void* log_dev, size_t log_bytes, void* ws_dev,
+                     size_t ws_bytes, void* stream) {
+  if (!m || !x_dev || !y_dev || !log_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  if (T < 1 || T > 8) return fail(KDA_E_SHAPE, "T must be in 1..8");
+  if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(log_dev) || !aligned16(ws_dev))
+    return fail(KDA_E_ALIGN, "unaligned pointer");
+  const int B = st->batch;
+  if (log_bytes < kda_verify_log_bytes(m, B, T)) return fail(KDA_E_WORKSPACE, "log buffer too small");
+  WsLayout wl = ws_layout(m, (int64_t)B * T);
+  if (ws_bytes < wl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, wl.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(ws_dev);
+  float* logf = static_cast<float*>(log_dev);
+  const size_t log_layer = (size_t)B * T * m->proj_stride;
+  for (int l = 0; l < m->d.n_layers; ++l) {
+    const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
+    r = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
+                      st->conv_dev + l * win_layer_stride(m, B), logf + l * log_layer, wl, ws,
+                      false, s, m->timing);
+    if (r) return r;
+  }
+  return KDA_OK;
+}
+
+int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, int32_t T,
+                      const int32_t* accept_dev, void* stream) {
+  if (!m || !log_dev || !accept_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  if (T < 1 || T > 8) return fail(KDA_E_SHAPE, "T must be in 1..8");
+  const int B = st->batch;
+  hipStream_t s = (hipStream_t)stream;
+  const kda_dims& d = m->d;
+  const float* logf = static_cast<const float*>(log_dev);
+  const size_t log_layer = (size_t)B * T * m->proj_stride;
+  for (int l = 0; l < d.n_layers; ++l) {
+    const LayerDev& L = m->layers[l];
+    HeadParams hp;
+    hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
+    hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
+    hp.B = B; hp.T = T;
+    hp.proj = logf + l * log_layer; hp.proj_stride = m->proj_stride;
+    hp.conv_in_head = 1;
+    float* win = st->conv_dev + l * win_layer_stride(m, B);
+    hp.win = win; hp.conv_w = L.conv_w;
+    hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
+    hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
+    hp.S = st->S_dev + l * state_layer_stride(m, B);
+    hp.write_state = 1; hp.ntok = accept_dev; hp.write_out = 0;
+    hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
+    r = timed(m, KDA_K_COMMIT, s, m->timing, [&] { return launch_head(hp, s); });
+    if (r) return r;
+    r = timed(m, KDA_K_COMMIT, s, m->timing, [&] {
+      return launch_window_commit(logf + l * log_layer, m->proj_stride, win, B, T, m->C, accept_dev, s);
+    });
+    if (r) return r;
+  }
+  return KDA_OK;
+}
+
+int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
+                        int32_t chunk, float* y_dev, const kda_state* st, void* ws_dev,
+                        size_t ws_bytes, void* stream) {
+  (void)m; (void)x_dev; (void)x_dtype; (void)L; (void)chunk; (void)y_dev; (void)st;
+  (void)ws_dev; (void)ws_bytes; (void)stream;
+  return fail(KDA_E_UNSUPPORTED, "chunked prefill is not built yet");
+}
+
+}  // extern "C"

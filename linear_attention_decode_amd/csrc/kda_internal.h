@@ -1,0 +1,124 @@
+// Internal interface between the C-ABI host code and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2 };
+
+// A packed weight matrix as the kernels see it.
+struct PackedMat {
+  const uint8_t* w = nullptr;   // F32/BF16 data, or the Q8_0 byte plane (q + 128)
+  const __half* d = nullptr;    // Q8_0 scale plane [rows][cols/32]
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Byte offset of the Q8_0 scale plane inside a packed matrix.
+inline size_t q8_scale_offset(int64_t rows, int64_t cols) {
+  return align_up((size_t)rows * (size_t)cols, 256);
+}
+
+inline PackedMat packed_view(const void* base, int wt, int64_t rows, int64_t cols) {
+  PackedMat m;
+  m.w = static_cast<const uint8_t*>(base);
+  if (wt == kQ8) m.d = reinterpret_cast<const __half*>(m.w + q8_scale_offset(rows, cols));
+  return m;
+}
+
+// ---------------------------------------------------------------------------------------
+// Fused multi-matrix GEMV (projections and the output projection).
+// ---------------------------------------------------------------------------------------
+constexpr int kGemvThreads = 256;
+constexpr int kGemvRowsPerWave = 2;
+constexpr int kGemvRowsPerBlock = (kGemvThreads / 64) * kGemvRowsPerWave;
+constexpr int kMaxSegs = 6;
+
+enum GemvPrologue { kProX = 0, kProGatedNorm = 1 };
+
+struct GemvSeg {
+  PackedMat m;
+  int rows = 0;
+  int first_tile = 0;   // first block index of this matrix in the grid
+  int out_off = 0;      // column offset of this matrix's rows in an output row
+  int conv_chan = -1;   // >= 0: rows are conv channels from here; apply conv + SiLU + roll
+};
+
+struct GemvParams {
+  GemvSeg seg[kMaxSegs];
+  int nseg = 0;
+  int K = 0;            // input length
+  int N = 0;            // columns (sequences x tokens)
+  // prologue kProX: input rows x[n][x_stride], optional RMSNorm (weight ones)
+  const float* x = nullptr;
+  int x_stride = 0;
+  int prenorm = 0;
+  float eps = 0.f;
+  // prologue kProGatedNorm: n = o * rsqrt(mean_h(o^2) + eps) * o_norm_w * gate, per head
+  const float* o = nullptr;
+  const float* gate = nullptr;
+  const float* ss = nullptr;     // [N][H][ncb] partial sums of o^2
+  const float* onw = nullptr;    // [dv] or null (ones)
+  int H = 0, dv = 0, ncb = 0;
+  // output: out[n][out_stride] (+ resid[n][out_stride] if resid != null; may alias out)
+  float* out = nullptr;
+  int out_stride = 0;
+  const float* resid = nullptr;
+  // decode conv epilogue (T = 1, column n = sequence n)
+  const float* conv_w = nullptr;  // [C][4]
+  float* win = nullptr;           // [N][3][C]
+  int C = 0;
+};
+
+hipError_t launch_gemv(int wt, int prologue, const GemvParams& p, int grid, hipStream_t s);
+size_t gemv_smem_bytes(int wt, int nc, int K, int H);
+int gemv_cols_per_pass(int N);
+hipError_t gemv_prepare_attributes();
+
+// ---------------------------------------------------------------------------------------
+// Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
+// ---------------------------------------------------------------------------------------
+constexpr int kHeadThreads = 256;
+constexpr int kHeadCols = 32;      // value columns per block
+
+struct HeadParams {
+  int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
+  int B = 0, T = 0;               // sequences, tokens per sequence (column n = b*T + t)
+  const float* proj = nullptr;    // [N][proj_stride]: a or p (C) | f_lr | g_lr | beta logits
+  int proj_stride = 0;
+  int conv_in_head = 0;           // 1: proj holds pre-conv p; conv from win (read-only)
+  const float* win = nullptr;     // [B][3][C]
+  const float* conv_w = nullptr;  // [C][4]
+  int wt = 0;
+  PackedMat fb, gb;               // [H*dk][rank_f], [H*dv][rank_g]
+  const float* a_log = nullptr;
+  const float* dt_bias = nullptr;
+  float* S = nullptr;             // [B][H][dk][dv]
+  int write_state = 1;
+  const int* ntok = nullptr;      // commit: tokens to apply per sequence (clamped 1..T)
+  int write_out = 1;
+  float* o = nullptr;             // [N][H*dv]
+  float* gate = nullptr;          // [N][H*dv]
+  float* ss = nullptr;            // [N][H][dv/kHeadCols]
+  float l2_eps = 0.f;
+  float q_scale = 0.f;            // d_k^-1/2 as fp32
+};
+
+hipError_t launch_head(const HeadParams& p, hipStream_t s);
+
+// New conv window after `ntok[b]` tokens: last 3 of (window, p_0 .. p_{T-1}).
+hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,
+                                int C, const int* ntok, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------
+// Packing.
+// ---------------------------------------------------------------------------------------
+hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, void* dst,
+                       hipStream_t s);
+hipError_t launch_unpack_q8(const void* packed, int64_t rows, int64_t cols, uint16_t* d16,
+                            int8_t* qs, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,95 @@
+// Weight packing kernels: fp32 -> F32 / BF16 / Q8_0 device layouts, and the canonical
+// view of a Q8_0 matrix.  Q8_0 is the block format of the antirez/ds4 PR #964 commit that
+// requantises KDA's projections: 32 consecutive values of a row share one fp16 scale.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+__global__ void pack_copy_f32(const float* __restrict__ src, float* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[i];
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__global__ void pack_bf16(const float* __restrict__ src, uint16_t* __restrict__ dst, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t b = __float_as_uint(src[i]);
+  uint16_t r;
+  if ((b & 0x7fffffffu) > 0x7f800000u) {
+    r = (uint16_t)((b >> 16) | 0x40u);
+  } else {
+    r = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+  }
+  dst[i] = r;
+}
+
+// One thread per block of 32: amax, d = amax/127 (fp32, round to nearest), d16 = fp16
+// round-to-nearest-even of d, q = clamp(round-half-away(x / d16), -127, 127) with a
+// correctly rounded fp32 division; q = 0 everywhere when d16 == 0.  Stored as q + 128.
+__global__ void pack_q8_0(const float* __restrict__ src, int64_t rows, int64_t cols,
+                          uint8_t* __restrict__ qs, __half* __restrict__ dplane) {
+  const int64_t nb_row = cols / 32;
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= rows * nb_row) return;
+  const int64_t r = b / nb_row, j = b - r * nb_row;
+  const float* x = src + r * cols + j * 32;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = x[i];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const float d = __fdiv_rn(amax, 127.0f);
+  const __half h = __float2half_rn(d);
+  const float dq = __half2float(h);
+  uint8_t* q = qs + r * cols + j * 32;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    float t = 0.0f;
+    if (dq != 0.0f) {
+      t = roundf(__fdiv_rn(v[i], dq));
+      t = fminf(fmaxf(t, -127.0f), 127.0f);
+    }
+    q[i] = (uint8_t)((int)t + 128);
+  }
+  dplane[b] = h;
+}
+
+__global__ void unpack_q8_0(const uint8_t* __restrict__ qs, const __half* __restrict__ dplane,
+                            int64_t rows, int64_t cols, uint16_t* __restrict__ d16,
+                            int8_t* __restrict__ qo) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = rows * cols;
+  if (i < n) qo[i] = (int8_t)((int)qs[i] - 128);
+  if (i < n / 32) d16[i] = __half_as_ushort(dplane[i]);
+}
+
+static inline int grid_for(int64_t n, int t) { return (int)((n + t - 1) / t); }
+
+hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, void* dst,
+                       hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (wt == kF32) {
+    pack_copy_f32<<<grid_for(n, 256), 256, 0, s>>>(src, static_cast<float*>(dst), n);
+  } else if (wt == kBF16) {
+    pack_bf16<<<grid_for(n, 256), 256, 0, s>>>(src, static_cast<uint16_t*>(dst), n);
+  } else {
+    uint8_t* q = static_cast<uint8_t*>(dst);
+    __half* d = reinterpret_cast<__half*>(q + q8_scale_offset(rows, cols));
+    pack_q8_0<<<grid_for(n / 32, 128), 128, 0, s>>>(src, rows, cols, q, d);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_q8(const void* packed, int64_t rows, int64_t cols, uint16_t* d16,
+                            int8_t* qs, hipStream_t s) {
+  const uint8_t* q = static_cast<const uint8_t*>(packed);
+  const __half* d = reinterpret_cast<const __half*>(q + q8_scale_offset(rows, cols));
+  unpack_q8_0<<<grid_for(rows * cols, 256), 256, 0, s>>>(q, d, rows, cols, d16, qs);
+  return hipGetLastError();
+}
+
+}  // namespace kda

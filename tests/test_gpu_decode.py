@@ -1,0 +1,164 @@
+"""GPU parity of the decode path (pack, one layer, the 34-layer stack) against the oracle.
+
+Every case prints its name before running so a fault names it.  Tolerances are stated in
+tests/helpers.py (range-relative 1e-3 on outputs, 2e-3 absolute on the state); packing
+and conv-window indexing are compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kda as ok
+from tests.helpers import OUT_RTOL, STATE_ATOL, gpu_decode, gpu_model, oracle_layers, range_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available()
+    return t
+
+
+# ----------------------------------------------------------------------------------------
+# packing: bit-exact against the oracle's quantiser / rounding
+# ----------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 32), (7, 96), (64, 2048), (2048, 128), (13, 4096)])
+def test_pack_q8_0_bit_exact(torch, shape):
+    import linear_attention_decode_amd as kda
+    _say(f"pack q8_0 {shape}")
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    w = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    w[0, :32] = 0.0                                    # an all-zero block
+    if shape[1] >= 64:
+        w[-1, 32:64] *= 1e4                            # a large-scale block
+        w[-1, 33] = 0.5 * float(np.float32(w[-1, 32:64].__abs__().max()))
+    src = torch.from_numpy(w).cuda()
+    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_Q8_0, *shape), dtype=torch.uint8, device="cuda")
+    kda.kda_pack(kda.KDA_Q8_0, src, buf)
+    d16, qs = kda.kda_unpack_q8_0(buf, *shape)
+    torch.cuda.synchronize()
+    rd16, rq = ok.q8_0_quantize(w)
+    np.testing.assert_array_equal(d16.cpu().numpy().view(np.uint16), rd16.view(np.uint16))
+    np.testing.assert_array_equal(qs.cpu().numpy(), rq)
+
+
+def test_pack_q8_0_ties_bit_exact(torch):
+    import linear_attention_decode_amd as kda
+    _say("pack q8_0 ties")
+    x = np.zeros((2, 32), np.float32)
+    x[0, :8] = [127, 2.5, -2.5, 0.5, -0.5, 3.5, -3.5, 1.5]
+    x[0, 31] = -126.5
+    x[1] = np.arange(32) / 31.0
+    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_Q8_0, 2, 32), dtype=torch.uint8, device="cuda")
+    kda.kda_pack(kda.KDA_Q8_0, torch.from_numpy(x).cuda(), buf)
+    d16, qs = kda.kda_unpack_q8_0(buf, 2, 32)
+    rd16, rq = ok.q8_0_quantize(x)
+    np.testing.assert_array_equal(d16.cpu().numpy().view(np.uint16), rd16.view(np.uint16))
+    np.testing.assert_array_equal(qs.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("shape", [(3, 5), (128, 2048)])
+def test_pack_bf16_bit_exact(torch, shape):
+    import linear_attention_decode_amd as kda
+    _say(f"pack bf16 {shape}")
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal(shape) * rng.uniform(1e-3, 1e3, shape)).astype(np.float32)
+    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_BF16, *shape), dtype=torch.uint8, device="cuda")
+    kda.kda_pack(kda.KDA_BF16, torch.from_numpy(w).cuda(), buf)
+    bits = buf.cpu().numpy().view(np.uint16).reshape(shape)
+    got = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(got, ok.bf16_round(w))
+
+
+# ----------------------------------------------------------------------------------------
+# decode parity
+# ----------------------------------------------------------------------------------------
+def _decode_parity(w, steps, snap_every=0, graph=True):
+    run = synth.draw_run(w)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    y, S, Z, snaps = gpu_decode(model, run, steps, snap_every, graph)
+    ry, rS, rZ, rsnaps = ok.decode_run(layers, run.x, run.s0, w.prenorm_residual, steps=steps,
+                                       check_every=snap_every)
+    errs = [range_rel(y[t], ry[t]) for t in range(steps)]
+    assert max(errs) <= OUT_RTOL, f"output range-rel error {max(errs):.3e} at step {int(np.argmax(errs))}"
+    serr = np.abs(S - rS).max()
+    assert serr <= STATE_ATOL, f"state error {serr:.3e}"
+    for k, v in snaps.items():
+        assert np.abs(v - rsnaps[k]).max() <= STATE_ATOL, f"state error at step {k}"
+    assert range_rel(Z, rZ) <= OUT_RTOL
+    model.close()
+    return max(errs), serr
+
+
+def test_decode_tiny_layer(torch):
+    w = synth.WORKLOADS["tiny"]
+    _say(f"decode tiny D={w.dims.d_model} H={w.dims.n_heads} dk={w.dims.d_k} steps={w.steps}")
+    e, s = _decode_parity(w, w.steps)
+    _say(f"  tiny: out {e:.2e} state {s:.2e}")
+
+
+def test_decode_layer_bf16_256_steps(torch):
+    w = synth.WORKLOADS["layer"]
+    _say(f"decode layer bf16 D=2048 H=16 steps={w.steps}")
+    e, s = _decode_parity(w, w.steps, snap_every=32)
+    _say(f"  layer: out {e:.2e} state {s:.2e}")
+
+
+@pytest.mark.parametrize("wtype", ["f32", "bf16", "q8_0"])
+def test_decode_ragged_batch(torch, wtype):
+    """B=3 sequences, H=3 heads (row tiles end mid-block), a 2-layer residual stack."""
+    d = synth.LayerDims(d_model=96, n_heads=3, d_k=64, d_v=64, rank_f=32, rank_g=32)
+    base = synth.WORKLOADS["tiny"]
+    w = synth.scaled(base, dims=d, wtype=wtype, n_layers=2, prenorm_residual=True, batch=3,
+                     steps=6, s0_std=0.1, seed=21)
+    _say(f"decode ragged {wtype} B=3 H=3 L=2")
+    _decode_parity(w, w.steps, snap_every=3)
+
+
+def test_decode_stack_q8_0_full_size(torch):
+    w = synth.scaled(synth.WORKLOADS["stack"], steps=8)
+    _say("decode stack q8_0 34 layers D=2048 steps=8")
+    e, s = _decode_parity(w, w.steps)
+    _say(f"  stack: out {e:.2e} state {s:.2e}")
+
+
+def test_graph_replay_equals_eager(torch):
+    """The captured hipGraph replays exactly the eager launches (deterministic kernels)."""
+    w = synth.scaled(synth.WORKLOADS["layer"], steps=5)
+    _say("graph vs eager, layer bf16, 5 steps")
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    ya, Sa, Za, _ = gpu_decode(model, run, 5, graph=True)
+    yb, Sb, Zb, _ = gpu_decode(model, run, 5, graph=False)
+    np.testing.assert_array_equal(ya, yb)
+    np.testing.assert_array_equal(Sa, Sb)
+    np.testing.assert_array_equal(Za, Zb)
+    model.close()
+
+
+def test_conv_window_indexing_bit_exact(torch):
+    """Integer-valued weights and inputs make every projection exact in fp32, so the
+    window (copies of the last three projections, oldest first) must match bit for bit."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], steps=5, seed=9)
+    run = synth.draw_run(w)
+    rng = np.random.default_rng(9)
+    for dr in run.layers:
+        for k in ("wq", "wk", "wv"):
+            dr[k] = rng.integers(-2, 3, size=dr[k].shape).astype(np.float32)
+    run.x[:] = rng.integers(-3, 4, size=run.x.shape).astype(np.float32)
+    _say("conv window bit-exact, tiny, 5 steps")
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    _, _, Z, _ = gpu_decode(model, run, 5)
+    _, _, rZ, _ = ok.decode_run(layers, run.x, run.s0, False, steps=5)
+    np.testing.assert_array_equal(Z.astype(np.float64), rZ)
+    model.close()
