@@ -334,6 +334,12 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
   if (d.d_model % gran || d.rank_f % gran || d.rank_g % gran || (d.n_heads * d.d_v) % gran)
     return fail(KDA_E_SHAPE, "input dims must be multiples of %d for this weight type", gran);
   if (d.d_model % 4) return fail(KDA_E_SHAPE, "d_model %% 4 != 0");
+  if (d.d_model > kGemvKMax || d.n_heads * d.d_v > kGemvKMax)
+    return fail(KDA_E_SHAPE, "d_model and n_heads*d_v must be <= %d", kGemvKMax);
+  if (d.n_heads > kGemvMaxHeads) return fail(KDA_E_SHAPE, "n_heads must be <= %d", kGemvMaxHeads);
+  if (!head_supported(d.d_k, d.wtype, d.rank_f, d.rank_g))
+    return fail(KDA_E_SHAPE, "low ranks %d/%d unsupported for this weight type (need rank_f == rank_g, "
+                "a power-of-two count of 16-byte chunks per row)", d.rank_f, d.rank_g);
   if (!(d.norm_eps >= 0.f) || !(d.l2_eps >= 0.f)) return fail(KDA_E_ARG, "eps must be >= 0");
   kda_model* m = new kda_model();
   m->d = d;
@@ -368,8 +374,7 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
     L.o_norm_w = s.o_norm_w;
     m->layers.push_back(L);
   }
-  hipError_t e = gemv_prepare_attributes();
-  if (e == hipSuccess) e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  hipError_t e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) {
     delete m;
     return fail(KDA_E_HIP, "model setup: %s", hipGetErrorString(e));

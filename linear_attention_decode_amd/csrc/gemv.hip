@@ -53,23 +53,27 @@ __device__ __forceinline__ float chunk_dot(const uint4 w, const float* __restric
 
 int gemv_cols_per_pass(int N) { return N >= 8 ? 8 : (N >= 4 ? 4 : (N >= 2 ? 2 : 1)); }
 
-size_t gemv_smem_bytes(int wt, int nc, int K, int H) {
-  size_t f = (size_t)nc * K;                       // inputs
-  if (wt == kQ8) f += (size_t)nc * (K / 16);      // chunk sums
-  f += (size_t)nc * (H > 0 ? H : 1) + 64;          // per-column / per-head scales
-  return f * sizeof(float);
-}
+// Input float4s a thread loads per column without a loop (K <= 4096); larger K adds a
+// strided tail loop.
+constexpr int kXVec = 4;
 
-template <int WT, int NC, int PRO>
+// LDS is static and sized by the template (a kernel with dynamic LDS measured about twice
+// as slow on gfx950 for the same code): KMAX = 2048 takes up to 8 columns a pass, the
+// 8192 variant one column a pass.
+template <int WT, int NC, int PRO, int KMAX>
 __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) {
-  extern __shared__ float smem[];
+  __shared__ float xs[NC * KMAX];                              // [NC][K]
+  __shared__ float xsum[WT == kQ8 ? NC * (KMAX / 16) : 1];     // [NC][K/16] (Q8_0)
+  __shared__ float scal[NC * kGemvMaxHeads];                   // per-column / per-head scales
+  __shared__ float red[4 * NC];                                // [4][NC]
   constexpr int EL = WFmt<WT>::kElems;
-  constexpr int U = (WT == kQ8) ? 2 : 4;          // chunks per lane per row in flight
+  constexpr int BY = WFmt<WT>::kBytes;
+  // 16-byte chunks per lane per row kept in flight: a 2048-wide row in one pass
+  constexpr int U = (WT == kQ8) ? 2 : (WT == kBF16 ? 4 : 8);
+  constexpr int RPW = kGemvRowsPerWave;
   const int K = P.K;
+  const int K4 = K / 4;
   const int nchunk = K / EL;
-  float* xs = smem;                                // [NC][K]
-  float* xsum = xs + NC * K;                       // [NC][K/16] (Q8_0)
-  float* scal = xsum + (WT == kQ8 ? NC * (K / 16) : 0);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile = blockIdx.x;
@@ -78,93 +82,189 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
 #pragma unroll
   for (int i = 1; i < kMaxSegs; ++i)
     if (i < P.nseg && tile >= P.seg[i].first_tile) sg = P.seg[i];
-  const int row_base = (tile - sg.first_tile) * kGemvRowsPerBlock + wave * kGemvRowsPerWave;
+  const int row_base = (tile - sg.first_tile) * kGemvRowsPerBlock + wave * RPW;
+
+  uint4 wv[RPW][U];
+  float dsc[RPW][U];
+  auto load_weights = [&](int cb) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row_base + r;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = cb + u * 64 + lane;
+        wv[r][u] = make_uint4(0, 0, 0, 0);
+        dsc[r][u] = 0.0f;
+        if (row < sg.rows && c < nchunk) {
+          wv[r][u] = load_stream16(sg.m.w + ((size_t)row * K + (size_t)c * EL) * BY);
+          if constexpr (WT == kQ8) dsc[r][u] = __half2float(sg.m.d[(size_t)row * (K / 32) + (c >> 1)]);
+        }
+      }
+    }
+  };
+  // The weight stream does not depend on the input: start it before the prologue.
+  load_weights(0);
+  // Epilogue operands of the first column pass (conv taps and window, or the residual),
+  // also independent of the dot products.
+  float4 ep_w[RPW];
+  float ep_z[RPW][3], ep_r[RPW];
+  auto load_epilogue = [&](int c0) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int row = row_base + r, n = c0 + lane;
+      ep_w[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+      ep_z[r][0] = ep_z[r][1] = ep_z[r][2] = ep_r[r] = 0.0f;
+      if (row < sg.rows && lane < NC && n < P.N) {
+        if (sg.conv_chan >= 0) {
+          const int c = sg.conv_chan + row;
+          ep_w[r] = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
+          const float* z = P.win + (size_t)n * 3 * P.C + c;
+          ep_z[r][0] = z[0];
+          ep_z[r][1] = z[P.C];
+          ep_z[r][2] = z[2 * P.C];
+        }
+        if (P.resid) ep_r[r] = P.resid[(size_t)n * P.out_stride + sg.out_off + row];
+      }
+    }
+  };
+  load_epilogue(0);
 
   for (int c0 = 0; c0 < P.N; c0 += NC) {
     const int nc = min(NC, P.N - c0);
     // ---------------- prologue: the NC input columns into LDS ----------------
     if constexpr (PRO == kProX) {
+      float4 xv[NC][kXVec];
+#pragma unroll
+      for (int n = 0; n < NC; ++n)
+#pragma unroll
+        for (int m = 0; m < kXVec; ++m) {
+          const int i4 = tid + m * kGemvThreads;
+          xv[n][m] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (n < nc && i4 < K4)
+            xv[n][m] = *reinterpret_cast<const float4*>(P.x + (size_t)(c0 + n) * P.x_stride + 4 * i4);
+        }
+      float ssq[NC];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+        ssq[n] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < kXVec; ++m) {
+          const int i4 = tid + m * kGemvThreads;
+          if (i4 < K4) {
+            const float4 v = xv[n][m];
+            ssq[n] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+            *reinterpret_cast<float4*>(xs + n * K + 4 * i4) = v;
+          }
+        }
+        for (int i4 = tid + kXVec * kGemvThreads; i4 < K4; i4 += kGemvThreads) {
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (n < nc) v = *reinterpret_cast<const float4*>(P.x + (size_t)(c0 + n) * P.x_stride + 4 * i4);
+          ssq[n] += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          *reinterpret_cast<float4*>(xs + n * K + 4 * i4) = v;
+        }
+      }
       if (P.prenorm) {
-        for (int n = wave; n < nc; n += 4) {
-          const float* xr = P.x + (size_t)(c0 + n) * P.x_stride;
-          float a = 0.0f;
-          for (int k = lane; k < K; k += 64) a += xr[k] * xr[k];
-          a = wave_sum(a);
-          if (lane == 0) scal[n] = 1.0f / sqrtf(a / (float)K + P.eps);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+          const float a = wave_sum(ssq[n]);
+          if (lane == 0) red[wave * NC + n] = a;
         }
         __syncthreads();
-      }
-      for (int i = tid; i < NC * K; i += kGemvThreads) {
-        const int n = i / K, k = i - n * K;
-        float v = 0.0f;
-        if (n < nc) {
-          v = P.x[(size_t)(c0 + n) * P.x_stride + k];
-          if (P.prenorm) v *= scal[n];
+        if (tid < NC) {
+          const float a = red[tid] + red[NC + tid] + red[2 * NC + tid] + red[3 * NC + tid];
+          scal[tid] = 1.0f / sqrtf(a / (float)K + P.eps);
         }
-        xs[i] = v;
+        __syncthreads();
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+          const float sc = scal[n];
+          for (int i4 = tid; i4 < K4; i4 += kGemvThreads) {
+            float4* p = reinterpret_cast<float4*>(xs + n * K + 4 * i4);
+            float4 v = *p;
+            v.x *= sc; v.y *= sc; v.z *= sc; v.w *= sc;
+            *p = v;
+          }
+        }
       }
     } else {
       // gated RMSNorm per head over dv, from partial sums of squares
       const int H = P.H;
-      for (int i = tid; i < nc * H; i += kGemvThreads) {
-        const int n = i / H, h = i - n * H;
+      float4 ov[NC][kXVec], gv[NC][kXVec];
+#pragma unroll
+      for (int n = 0; n < NC; ++n)
+#pragma unroll
+        for (int m = 0; m < kXVec; ++m) {
+          const int i4 = tid + m * kGemvThreads;
+          ov[n][m] = make_float4(0.f, 0.f, 0.f, 0.f);
+          gv[n][m] = ov[n][m];
+          if (n < nc && i4 < K4) {
+            const size_t g = (size_t)(c0 + n) * K + 4 * i4;
+            ov[n][m] = *reinterpret_cast<const float4*>(P.o + g);
+            gv[n][m] = *reinterpret_cast<const float4*>(P.gate + g);
+          }
+        }
+      if (tid < nc * H) {
+        const int n = tid / H, h = tid - n * H;
         const float* sp = P.ss + ((size_t)(c0 + n) * H + h) * P.ncb;
         float a = 0.0f;
         for (int j = 0; j < P.ncb; ++j) a += sp[j];
-        scal[i] = 1.0f / sqrtf(a / (float)P.dv + P.eps);
+        scal[tid] = 1.0f / sqrtf(a / (float)P.dv + P.eps);
       }
       __syncthreads();
-      for (int i = tid; i < NC * K; i += kGemvThreads) {
-        const int n = i / K, k = i - n * K;
-        float v = 0.0f;
-        if (n < nc) {
-          const size_t g = (size_t)(c0 + n) * K + k;
-          const int h = k / P.dv;
-          const float w = P.onw ? P.onw[k - h * P.dv] : 1.0f;
-          v = P.o[g] * scal[n * H + h] * w * P.gate[g];
+#pragma unroll
+      for (int n = 0; n < NC; ++n) {
+#pragma unroll
+        for (int m = 0; m < kXVec; ++m) {
+          const int i4 = tid + m * kGemvThreads;
+          if (i4 < K4) {
+            const int k = 4 * i4, h = k / P.dv;
+            const float sc = n < nc ? scal[n * H + h] : 0.0f;
+            float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (P.onw) w = *reinterpret_cast<const float4*>(P.onw + (k - h * P.dv));
+            const float4 o = ov[n][m], g = gv[n][m];
+            *reinterpret_cast<float4*>(xs + n * K + k) =
+                make_float4(o.x * sc * w.x * g.x, o.y * sc * w.y * g.y, o.z * sc * w.z * g.z, o.w * sc * w.w * g.w);
+          }
         }
-        xs[i] = v;
+        for (int i4 = tid + kXVec * kGemvThreads; i4 < K4; i4 += kGemvThreads) {
+          const int k = 4 * i4, h = k / P.dv;
+          float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (n < nc) {
+            const size_t g = (size_t)(c0 + n) * K + k;
+            const float sc = scal[n * H + h];
+            float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+            if (P.onw) w = *reinterpret_cast<const float4*>(P.onw + (k - h * P.dv));
+            const float4 o = *reinterpret_cast<const float4*>(P.o + g);
+            const float4 gg = *reinterpret_cast<const float4*>(P.gate + g);
+            v = make_float4(o.x * sc * w.x * gg.x, o.y * sc * w.y * gg.y, o.z * sc * w.z * gg.z, o.w * sc * w.w * gg.w);
+          }
+          *reinterpret_cast<float4*>(xs + n * K + k) = v;
+        }
       }
     }
     __syncthreads();
     if constexpr (WT == kQ8) {
       for (int i = tid; i < NC * (K / 16); i += kGemvThreads) {
-        const float* xp = xs + (size_t)i * 16;
-        float a = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) a += xp[j];
-        xsum[i] = a;
+        const float4* xp = reinterpret_cast<const float4*>(xs + (size_t)i * 16);
+        const float4 a = xp[0], b = xp[1], c = xp[2], d = xp[3];
+        xsum[i] = ((a.x + a.y) + (a.z + a.w)) + ((b.x + b.y) + (b.z + b.w)) +
+                  ((c.x + c.y) + (c.z + c.w)) + ((d.x + d.y) + (d.z + d.w));
       }
       __syncthreads();
     }
 
     // ---------------- weight stream ----------------
-    float acc[kGemvRowsPerWave][NC];
+    float acc[RPW][NC];
 #pragma unroll
-    for (int r = 0; r < kGemvRowsPerWave; ++r)
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
       for (int n = 0; n < NC; ++n) acc[r][n] = 0.0f;
 
+    if (c0 > 0) load_epilogue(c0);
     for (int cb = 0; cb < nchunk; cb += 64 * U) {
-      uint4 wv[kGemvRowsPerWave][U];
-      float dsc[kGemvRowsPerWave][U];
+      if (c0 > 0 || cb > 0) load_weights(cb);
 #pragma unroll
-      for (int r = 0; r < kGemvRowsPerWave; ++r) {
-        const int row = row_base + r;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int c = cb + u * 64 + lane;
-          wv[r][u] = make_uint4(0, 0, 0, 0);
-          dsc[r][u] = 0.0f;
-          if (row < sg.rows && c < nchunk) {
-            const uint8_t* base = sg.m.w + ((size_t)row * K + (size_t)c * EL) * WFmt<WT>::kBytes;
-            wv[r][u] = load_stream16(base);
-            if constexpr (WT == kQ8) dsc[r][u] = __half2float(sg.m.d[(size_t)row * (K / 32) + (c >> 1)]);
-          }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kGemvRowsPerWave; ++r) {
+      for (int r = 0; r < RPW; ++r) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int c = cb + u * 64 + lane;
@@ -184,7 +284,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
 
     // ---------------- reduce + epilogue ----------------
 #pragma unroll
-    for (int r = 0; r < kGemvRowsPerWave; ++r) {
+    for (int r = 0; r < RPW; ++r) {
 #pragma unroll
       for (int n = 0; n < NC; ++n) acc[r][n] = wave_sum(acc[r][n]);
       const int row = row_base + r;
@@ -197,17 +297,16 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
         if (sg.conv_chan >= 0) {
           // causal conv over (window, this token), SiLU, window roll (one owner per channel)
           const int c = sg.conv_chan + row;
-          const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
+          const float4 w = ep_w[r];
           float* z = P.win + (size_t)n * 3 * P.C + c;
-          const float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
-          const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * v;
-          z[0] = z1;
-          z[P.C] = z2;
+          const float y = w.x * ep_z[r][0] + w.y * ep_z[r][1] + w.z * ep_z[r][2] + w.w * v;
+          z[0] = ep_z[r][1];
+          z[P.C] = ep_z[r][2];
           z[2 * P.C] = v;
           v = silu_f(y);
         }
         const size_t o = (size_t)n * P.out_stride + sg.out_off + row;
-        if (P.resid) v += P.resid[o];
+        if (P.resid) v += ep_r[r];
         P.out[o] = v;
       }
     }
@@ -217,13 +316,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
 
 template <int WT, int PRO>
 static hipError_t launch_nc(const GemvParams& p, int grid, hipStream_t s) {
-  const int nc = gemv_cols_per_pass(p.N);
-  const size_t smem = gemv_smem_bytes(WT, nc, p.K, PRO == kProGatedNorm ? p.H : 1);
-  switch (nc) {
-    case 1: gemv_kernel<WT, 1, PRO><<<grid, kGemvThreads, smem, s>>>(p); break;
-    case 2: gemv_kernel<WT, 2, PRO><<<grid, kGemvThreads, smem, s>>>(p); break;
-    case 4: gemv_kernel<WT, 4, PRO><<<grid, kGemvThreads, smem, s>>>(p); break;
-    default: gemv_kernel<WT, 8, PRO><<<grid, kGemvThreads, smem, s>>>(p); break;
+  if (p.K > kGemvKSmall) {
+    gemv_kernel<WT, 1, PRO, kGemvKMax><<<grid, kGemvThreads, 0, s>>>(p);
+    return hipGetLastError();
+  }
+  switch (gemv_cols_per_pass(p.N)) {
+    case 1: gemv_kernel<WT, 1, PRO, kGemvKSmall><<<grid, kGemvThreads, 0, s>>>(p); break;
+    case 2: gemv_kernel<WT, 2, PRO, kGemvKSmall><<<grid, kGemvThreads, 0, s>>>(p); break;
+    case 4: gemv_kernel<WT, 4, PRO, kGemvKSmall><<<grid, kGemvThreads, 0, s>>>(p); break;
+    default: gemv_kernel<WT, 8, PRO, kGemvKSmall><<<grid, kGemvThreads, 0, s>>>(p); break;
   }
   return hipGetLastError();
 }
@@ -237,33 +338,6 @@ hipError_t launch_gemv(int wt, int prologue, const GemvParams& p, int grid, hipS
   if (wt == kF32) return launch_nc<kF32, kProGatedNorm>(p, grid, s);
   if (wt == kBF16) return launch_nc<kBF16, kProGatedNorm>(p, grid, s);
   return launch_nc<kQ8, kProGatedNorm>(p, grid, s);
-}
-
-template <int WT, int PRO>
-static hipError_t set_attr_all(int big) {
-  hipError_t e;
-  e = hipFuncSetAttribute((const void*)gemv_kernel<WT, 1, PRO>, hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)gemv_kernel<WT, 2, PRO>, hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)gemv_kernel<WT, 4, PRO>, hipFuncAttributeMaxDynamicSharedMemorySize, big);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute((const void*)gemv_kernel<WT, 8, PRO>, hipFuncAttributeMaxDynamicSharedMemorySize, big);
-}
-
-// Allow the largest dynamic LDS a block may have on this device (the input columns of a
-// pass can exceed the default 64 KB).
-hipError_t gemv_prepare_attributes() {
-  int dev = 0, big = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&big, hipDeviceAttributeMaxSharedMemoryPerBlock, dev)) != hipSuccess) return e;
-  if ((e = set_attr_all<kF32, kProX>(big)) != hipSuccess) return e;
-  if ((e = set_attr_all<kBF16, kProX>(big)) != hipSuccess) return e;
-  if ((e = set_attr_all<kQ8, kProX>(big)) != hipSuccess) return e;
-  if ((e = set_attr_all<kF32, kProGatedNorm>(big)) != hipSuccess) return e;
-  if ((e = set_attr_all<kBF16, kProGatedNorm>(big)) != hipSuccess) return e;
-  return set_attr_all<kQ8, kProGatedNorm>(big);
 }
 
 }  // namespace kda

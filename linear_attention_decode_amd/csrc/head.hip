@@ -26,52 +26,42 @@
 
 namespace kda {
 
-// One row of a packed matrix dotted with an LDS vector, by a single thread.
-__device__ __forceinline__ float row_dot(const PackedMat m, int wt, int row, int K,
-                                         const float* __restrict__ x) {
-  float acc = 0.0f;
-  if (wt == kF32) {
-    const float4* w = reinterpret_cast<const float4*>(m.w) + (size_t)row * (K / 4);
-    for (int i = 0; i < K / 4; ++i) {
-      const float4 v = w[i];
-      acc += v.x * x[4 * i] + v.y * x[4 * i + 1] + v.z * x[4 * i + 2] + v.w * x[4 * i + 3];
-    }
-  } else if (wt == kBF16) {
-    const uint4* w = reinterpret_cast<const uint4*>(m.w + (size_t)row * K * 2);
-    for (int i = 0; i < K / 8; ++i) {
-      const uint4 v = w[i];
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+template <int WT>
+struct HFmt;
+template <>
+struct HFmt<kF32> { static constexpr int kElems = 4; static constexpr int kBytes = 4; };
+template <>
+struct HFmt<kBF16> { static constexpr int kElems = 8; static constexpr int kBytes = 2; };
+template <>
+struct HFmt<kQ8> { static constexpr int kElems = 16; static constexpr int kBytes = 1; };
+
+// Dot of one 16-byte chunk of a packed row with LDS inputs (Q8_0: q = byte - 128, unscaled).
+template <int WT>
+__device__ __forceinline__ float hchunk_dot(const uint4 w, const float* __restrict__ x) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.0f;
+  if constexpr (WT == kF32) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc += bf16_lo(d[j]) * x[8 * i + 2 * j] + bf16_hi(d[j]) * x[8 * i + 2 * j + 1];
-    }
+    for (int i = 0; i < 4; ++i) s += __uint_as_float(d[i]) * x[i];
+  } else if constexpr (WT == kBF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += bf16_lo(d[i]) * x[2 * i] + bf16_hi(d[i]) * x[2 * i + 1];
   } else {
-    const uint4* w = reinterpret_cast<const uint4*>(m.w + (size_t)row * K);
-    const __half* ds = m.d + (size_t)row * (K / 32);
-    for (int blk = 0; blk < K / 32; ++blk) {
-      float s = 0.0f;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint4 v = w[2 * blk + hh];
-        const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-        const float* xp = x + blk * 32 + hh * 16;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          s += ((float)(d[j] & 0xffu) - 128.0f) * xp[4 * j];
-          s += ((float)((d[j] >> 8) & 0xffu) - 128.0f) * xp[4 * j + 1];
-          s += ((float)((d[j] >> 16) & 0xffu) - 128.0f) * xp[4 * j + 2];
-          s += ((float)(d[j] >> 24) - 128.0f) * xp[4 * j + 3];
-        }
-      }
-      acc += __half2float(ds[blk]) * s;
+    for (int i = 0; i < 4; ++i) {
+      s += ((float)(d[i] & 0xffu) - 128.0f) * x[4 * i];
+      s += ((float)((d[i] >> 8) & 0xffu) - 128.0f) * x[4 * i + 1];
+      s += ((float)((d[i] >> 16) & 0xffu) - 128.0f) * x[4 * i + 2];
+      s += ((float)(d[i] >> 24) - 128.0f) * x[4 * i + 3];
     }
   }
-  return acc;
+  return s;
 }
 
 constexpr int kMaxRank = 256;
+constexpr int kMaxLrLoads = 10;   // 16-byte chunks of F_b / G_b rows per thread
 
-template <int DK>
+template <int DK, int WT>
 __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) {
   constexpr int CB = kHeadCols;
   constexpr int QPR = CB / 4;                 // column quads per row
@@ -79,6 +69,8 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
   constexpr int RPT = DK / RG;                // rows per thread
   static_assert(RPT >= 1 && RPT * RG == DK, "tile shape");
   constexpr int NCH = 2 * DK + CB;            // conv channels a block needs
+  constexpr int EL = HFmt<WT>::kElems;
+  constexpr int BY = HFmt<WT>::kBytes;
 
   __shared__ float s_qk[2 * DK];
   __shared__ float s_v[CB];
@@ -94,15 +86,41 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
   const int H = P.H, dv = P.dv, C = P.C, K = H * DK;
   const int j0 = cb * CB;
   const int ncb = dv / CB;
+  const int rl = P.rank_f + P.rank_g;
 
   int ntok = P.T;
   if (P.ntok) ntok = min(max(P.ntok[b], 1), P.T);
 
+  // ---- everything that does not depend on the token is requested first ----
   float* Sb = P.S + ((size_t)b * H + h) * DK * dv;
   float4 st[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i)
     st[i] = *reinterpret_cast<const float4*>(Sb + (size_t)(rg * RPT + i) * dv + j0 + 4 * cq);
+
+  // F_b rows h*DK .. h*DK+DK-1 (forget gate) then G_b rows of this block's columns, as
+  // (row, 16-byte chunk) items spread over the block; a row's chunks sit in adjacent lanes.
+  const int cpr = P.rank_f * BY / 16;         // chunks per row (rank_f == rank_g checked)
+  const int items = (DK + CB) * cpr;
+  const int nld = (items + kHeadThreads - 1) / kHeadThreads;
+  uint4 lw[kMaxLrLoads];
+  float lsc[kMaxLrLoads], lbias[kMaxLrLoads];
+#pragma unroll
+  for (int m = 0; m < kMaxLrLoads; ++m) {
+    lw[m] = make_uint4(0, 0, 0, 0);
+    lsc[m] = 0.0f;
+    lbias[m] = 0.0f;
+    const int it = tid + m * kHeadThreads;
+    if (m < nld && it < items) {
+      const int rloc = it / cpr, c = it - rloc * cpr;
+      const PackedMat& M = rloc < DK ? P.fb : P.gb;
+      const int rank = rloc < DK ? P.rank_f : P.rank_g;
+      const int row = rloc < DK ? h * DK + rloc : h * dv + j0 + (rloc - DK);
+      lw[m] = *reinterpret_cast<const uint4*>(M.w + ((size_t)row * rank + (size_t)c * EL) * BY);
+      if constexpr (WT == kQ8) lsc[m] = __half2float(M.d[(size_t)row * (rank / 32) + (c >> 1)]);
+      if (rloc < DK && c == 0) lbias[m] = P.dt_bias[h * DK + rloc];
+    }
+  }
 
   // conv channels of this thread: q (h*DK + i), k (K + h*DK + i), v (2K + h*dv + j0 + j)
   int chan[2];
@@ -111,6 +129,8 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
   for (int m = 0; m < 2; ++m) {
     const int ci = tid + m * kHeadThreads;
     chan[m] = -1;
+    z[m][0] = z[m][1] = z[m][2] = 0.0f;
+    cw[m][0] = cw[m][1] = cw[m][2] = cw[m][3] = 0.0f;
     if (ci < NCH) {
       chan[m] = ci < DK ? h * DK + ci : (ci < 2 * DK ? K + h * DK + (ci - DK) : 2 * K + h * dv + j0 + (ci - 2 * DK));
       if (P.conv_in_head) {
@@ -123,19 +143,30 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
       }
     }
   }
+  const float a_log_h = P.a_log[h];
 
-  const float a_h = expf(P.a_log[h]);
-  const int rl = P.rank_f + P.rank_g;
+  // token inputs (q, k, v channel values, low-rank activations, beta logit), loaded one
+  // token ahead so the first token's loads travel with the state and weight loads
+  float av[2], lrv[2], blog = 0.0f;
+  auto load_token = [&](int t) {
+    const float* prow = P.proj + (size_t)(b * P.T + t) * P.proj_stride;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int i = tid + m * kHeadThreads;
+      av[m] = i < NCH ? prow[chan[m]] : 0.0f;
+      lrv[m] = i < rl ? prow[C + i] : 0.0f;
+    }
+    if (tid == 0) blog = prow[C + rl + h];
+  };
+  load_token(0);
 
   for (int t = 0; t < ntok; ++t) {
     const int n = b * P.T + t;
-    const float* prow = P.proj + (size_t)n * P.proj_stride;
-    // ---- q, k, v channel values (post conv + SiLU) ----
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int ci = tid + m * kHeadThreads;
       if (ci < NCH) {
-        float a = prow[chan[m]];
+        float a = av[m];
         if (P.conv_in_head) {
           const float y = cw[m][0] * z[m][0] + cw[m][1] * z[m][1] + cw[m][2] * z[m][2] + cw[m][3] * a;
           z[m][0] = z[m][1];
@@ -145,10 +176,13 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
         }
         if (ci < 2 * DK) s_qk[ci] = a; else s_v[ci - 2 * DK] = a;
       }
+      const int i = tid + m * kHeadThreads;
+      if (i < rl) s_lr[i] = lrv[m];
     }
-    for (int i = tid; i < rl; i += kHeadThreads) s_lr[i] = prow[C + i];
-    if (tid == 0) s_misc[2] = sigmoid_f(prow[C + rl + h]);
+    if (tid == 0) s_misc[2] = sigmoid_f(blog);
+    if (t + 1 < ntok) load_token(t + 1);
     __syncthreads();
+    const float a_h = expf(a_log_h);
     // ---- L2 norms of q (wave 0) and k (wave 1) ----
     if (wave < 2) {
       const float* src = s_qk + wave * DK;
@@ -157,14 +191,29 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
       a = wave_sum(a);
       if (lane == 0) s_misc[wave] = 1.0f / sqrtf(a + P.l2_eps);
     }
-    // ---- forget gate (alpha, one per key channel) and output gate (this block's columns)
-    if (tid < DK) {
-      const float f = row_dot(P.fb, P.wt, h * DK + tid, P.rank_f, s_lr) + P.dt_bias[h * DK + tid];
-      s_alpha[tid] = expf(-a_h * softplus_f(f));
-    } else if (tid < DK + CB) {
-      const int j = tid - DK;
-      const float g = row_dot(P.gb, P.wt, h * dv + j0 + j, P.rank_g, s_lr + P.rank_f);
-      s_gate[j] = sigmoid_f(g);
+    // ---- forget gate alpha (per key channel) and output gate (this block's columns) ----
+#pragma unroll
+    for (int m = 0; m < kMaxLrLoads; ++m) {
+      if (m < nld) {
+        const int it = tid + m * kHeadThreads;
+        float part = 0.0f;
+        int rloc = 0, c = 0;
+        if (it < items) {
+          rloc = it / cpr;
+          c = it - rloc * cpr;
+          const float* xv = rloc < DK ? s_lr + c * EL : s_lr + P.rank_f + c * EL;
+          part = hchunk_dot<WT>(lw[m], xv);
+          if constexpr (WT == kQ8) part *= lsc[m];
+        }
+        for (int o = 1; o < cpr; o <<= 1) part += __shfl_xor(part, o, kWave);
+        if (it < items && c == 0) {
+          if (rloc < DK) {
+            s_alpha[rloc] = expf(-a_h * softplus_f(part + lbias[m]));
+          } else {
+            s_gate[rloc - DK] = sigmoid_f(part);
+          }
+        }
+      }
     }
     __syncthreads();
     const float inv_q = s_misc[0] * P.q_scale, inv_k = s_misc[1], beta = s_misc[2];
@@ -228,12 +277,32 @@ __global__ __launch_bounds__(kHeadThreads) void head_kernel(const HeadParams P) 
   }
 }
 
+template <int DK>
+static void launch_dk(const HeadParams& p, dim3 grid, hipStream_t s) {
+  if (p.wt == kF32)
+    head_kernel<DK, kF32><<<grid, kHeadThreads, 0, s>>>(p);
+  else if (p.wt == kBF16)
+    head_kernel<DK, kBF16><<<grid, kHeadThreads, 0, s>>>(p);
+  else
+    head_kernel<DK, kQ8><<<grid, kHeadThreads, 0, s>>>(p);
+}
+
+// Loads of F_b / G_b chunks a thread holds: (dk + 32 rows) x rank*bytes/16 chunks / 256.
+bool head_supported(int dk, int wt, int rank_f, int rank_g) {
+  const int by = wt == kF32 ? 4 : (wt == kBF16 ? 2 : 1);
+  if (rank_f != rank_g) return false;
+  const int cpr = rank_f * by / 16;
+  if (cpr < 1 || cpr > 64 || (cpr & (cpr - 1))) return false;
+  const int items = (dk + kHeadCols) * cpr;
+  return (items + kHeadThreads - 1) / kHeadThreads <= kMaxLrLoads;
+}
+
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
   dim3 grid(p.dv / kHeadCols, p.H, p.B);
   if (p.dk == 128)
-    head_kernel<128><<<grid, kHeadThreads, 0, s>>>(p);
+    launch_dk<128>(p, grid, s);
   else
-    head_kernel<64><<<grid, kHeadThreads, 0, s>>>(p);
+    launch_dk<64>(p, grid, s);
   return hipGetLastError();
 }
 

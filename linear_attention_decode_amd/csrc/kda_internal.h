@@ -73,10 +73,12 @@ struct GemvParams {
   int C = 0;
 };
 
+constexpr int kGemvKSmall = 2048;   // input length of the multi-column variants
+constexpr int kGemvKMax = 8192;     // longest input the GEMV takes
+constexpr int kGemvMaxHeads = 64;
+
 hipError_t launch_gemv(int wt, int prologue, const GemvParams& p, int grid, hipStream_t s);
-size_t gemv_smem_bytes(int wt, int nc, int K, int H);
 int gemv_cols_per_pass(int N);
-hipError_t gemv_prepare_attributes();
 
 // ---------------------------------------------------------------------------------------
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
@@ -108,6 +110,9 @@ struct HeadParams {
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
+// Whether the per-head kernel handles these low-rank shapes (equal ranks, a power-of-two
+// number of 16-byte chunks per row, at most 10 chunk loads per thread).
+bool head_supported(int dk, int wt, int rank_f, int rank_g);
 
 // New conv window after `ntok[b]` tokens: last 3 of (window, p_0 .. p_{T-1}).
 hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,

@@ -1,0 +1,105 @@
+"""GPU parity of multi-token verify + commit against the oracle.
+
+Verify runs T tokens per sequence through every layer from the committed state without
+changing it and records a replay log; commit advances the state to the one reached after
+the accepted prefix.  Compared per step: every token's output (accepted or not), and the
+committed state and conv window.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kda as ok
+from tests.helpers import OUT_RTOL, STATE_ATOL, gpu_model, oracle_layers, range_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def gpu_verify(model, run, steps, accept=None):
+    import torch
+    w = run.workload
+    B, T = w.batch, w.tokens
+    st = model.new_state(B)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(1, B, T)
+    log = model.verify_log(B, T)
+    acc = run.accept if accept is None else accept
+    xs = torch.from_numpy(np.ascontiguousarray(run.x[:steps])).cuda()
+    ys = torch.empty((steps, B, T, model.d_model), dtype=torch.float32, device="cuda")
+    accs = torch.from_numpy(np.ascontiguousarray(acc[:steps]).astype(np.int32)).cuda()
+    states = []
+    for t in range(steps):
+        model.verify_steps(xs[t].contiguous(), T, ys[t], st, log, ws)
+        model.verify_commit(st, log, T, accs[t].contiguous())
+        states.append((st.S.cpu().numpy().copy(), st.conv.cpu().numpy().copy()))
+    torch.cuda.synchronize()
+    return ys.cpu().numpy(), states
+
+
+def _check(w, steps, accept=None):
+    run = synth.draw_run(w)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    acc = run.accept if accept is None else accept
+    y, states = gpu_verify(model, run, steps, acc)
+    worst = 0.0
+    # oracle step by step (verify_run's commit semantics), recording each committed state
+    ry_all = np.empty((steps,) + run.x.shape[1:3] + (run.x.shape[3],))
+    S = [[np.array(run.s0[l, b], np.float64) for b in range(w.batch)] for l in range(w.n_layers)]
+    Z = [[np.zeros((3, w.dims.conv_channels)) for _ in range(w.batch)] for _ in range(w.n_layers)]
+    for t in range(steps):
+        for b in range(w.batch):
+            yb, s_new, z_new = ok.stack_step(layers, run.x[t, b].astype(np.float64),
+                                             [S[l][b] for l in range(w.n_layers)],
+                                             [Z[l][b] for l in range(w.n_layers)],
+                                             keep_after=int(min(max(acc[t, b], 1), w.tokens)))
+            ry_all[t, b] = yb
+            for l in range(w.n_layers):
+                S[l][b], Z[l][b] = s_new[l], z_new[l]
+        e = range_rel(y[t], ry_all[t])
+        worst = max(worst, e)
+        assert e <= OUT_RTOL, f"step {t}: output range-rel error {e:.3e}"
+        gS, gZ = states[t]
+        rS = np.array([[S[l][b] for b in range(w.batch)] for l in range(w.n_layers)])
+        rZ = np.array([[Z[l][b] for b in range(w.batch)] for l in range(w.n_layers)])
+        serr = np.abs(gS - rS).max()
+        assert serr <= STATE_ATOL, f"step {t}: committed state error {serr:.3e}"
+        assert range_rel(gZ, rZ) <= OUT_RTOL
+    model.close()
+    return worst
+
+
+def test_verify_small_stack():
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=2, batch=3, steps=4, seed=31)
+    _say("verify 2 layers B=3 T=4 D=2048 q8_0, 4 steps")
+    _check(w, w.steps)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_verify_token_counts(T):
+    d = synth.LayerDims(d_model=96, n_heads=3, d_k=64, d_v=64, rank_f=32, rank_g=32)
+    w = synth.scaled(synth.WORKLOADS["verify"], dims=d, n_layers=2, batch=2, steps=3, tokens=T,
+                     seed=40 + T)
+    _say(f"verify ragged dims T={T}")
+    _check(w, w.steps)
+
+
+def test_verify_accept_clamped():
+    """Accept lengths outside 1..T are clamped: 0 commits one token, 9 commits T."""
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=1, batch=2, steps=2, seed=50)
+    acc = np.array([[0, 9], [9, 0]], np.int32)
+    _say("verify accept clamping")
+    _check(w, w.steps, accept=acc)
+
+
+def test_verify_full_size_34_layers():
+    w = synth.scaled(synth.WORKLOADS["verify"], steps=3)
+    _say("verify full size: 34 layers B=8 T=4 q8_0, 3 steps")
+    e = _check(w, w.steps)
+    _say(f"  worst output error {e:.2e}")
