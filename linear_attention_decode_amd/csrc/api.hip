@@ -106,6 +106,38 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
   return w;
 }
 
+// Workspace layout (prefill, M = B*L tokens, NC = B*H*nch chunks).
+struct PfLayout {
+  size_t P = 0, FG = 0, q = 0, k = 0, v = 0, g2 = 0, beta = 0, gate = 0, W = 0, U = 0, Qt = 0,
+         Kt = 0, A = 0, dec = 0, o = 0, total = 0;
+};
+
+PfLayout pf_layout(const kda_model* m, int64_t B, int64_t L) {
+  const kda_dims& d = m->d;
+  const int64_t M = B * L, nch = (L + kChunk - 1) / kChunk, NC = B * d.n_heads * nch;
+  const int64_t K = m->Kq, V = m->V;
+  PfLayout w;
+  size_t off = 0;
+  auto take = [&](size_t& dst, int64_t floats) { dst = off; off = align_up(off + (size_t)floats * 4, 256); };
+  take(w.P, M * m->proj_stride);
+  take(w.FG, M * (K + V));
+  take(w.q, M * K);
+  take(w.k, M * K);
+  take(w.v, M * V);
+  take(w.g2, M * K);
+  take(w.beta, M * d.n_heads);
+  take(w.gate, M * V);
+  take(w.W, NC * kChunk * d.d_k);
+  take(w.U, NC * kChunk * d.d_v);
+  take(w.Qt, NC * kChunk * d.d_k);
+  take(w.Kt, NC * kChunk * d.d_k);
+  take(w.A, NC * kChunk * kChunk);
+  take(w.dec, NC * d.d_k);
+  take(w.o, M * V);
+  w.total = off;
+  return w;
+}
+
 int flush_timing(kda_model* m) {
   for (size_t i = 0; i < m->used; ++i) {
     TimedLaunch& t = m->pool[i];
@@ -425,6 +457,7 @@ size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t to
   if (!m || batch < 1 || tokens < 1) return 0;
   if (op == KDA_OP_DECODE) return ws_layout(m, batch).total;
   if (op == KDA_OP_VERIFY) return ws_layout(m, (int64_t)batch * tokens).total;
+  if (op == KDA_OP_PREFILL) return pf_layout(m, batch, tokens).total;
   return 0;
 }
 
@@ -531,9 +564,92 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
 int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
                         int32_t chunk, float* y_dev, const kda_state* st, void* ws_dev,
                         size_t ws_bytes, void* stream) {
-  (void)m; (void)x_dev; (void)x_dtype; (void)L; (void)chunk; (void)y_dev; (void)st;
-  (void)ws_dev; (void)ws_bytes; (void)stream;
-  return fail(KDA_E_UNSUPPORTED, "chunked prefill is not built yet");
+  if (!m || !x_dev || !y_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  const kda_dims& d = m->d;
+  if (d.n_layers != 1 || d.prenorm_residual)
+    return fail(KDA_E_UNSUPPORTED, "chunked prefill takes a single layer without pre-norm residual");
+  if (d.wtype != KDA_BF16) return fail(KDA_E_DTYPE, "chunked prefill needs BF16 weights (MFMA operands)");
+  if (x_dtype != KDA_BF16 && x_dtype != KDA_F32) return fail(KDA_E_DTYPE, "x must be BF16 or F32");
+  if (chunk != kChunk) return fail(KDA_E_SHAPE, "chunk must be %d", kChunk);
+  if (L < 1 || L > (1 << 30)) return fail(KDA_E_SHAPE, "L must be >= 1");
+  if (d.d_model % 64 || d.rank_f % 64 || d.rank_g % 64 || m->V % 64)
+    return fail(KDA_E_SHAPE, "prefill GEMMs need d_model, ranks and H*d_v multiples of 64");
+  if (m->C + 2 * d.n_heads > kPrefillMaxChannels)
+    return fail(KDA_E_SHAPE, "too many conv channels for the sequence pass");
+  if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(ws_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  const int B = st->batch;
+  const PfLayout wl = pf_layout(m, B, L);
+  if (ws_bytes < wl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, wl.total);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(ws_dev);
+  const LayerDev& Ly = m->layers[0];
+  const int64_t M = (int64_t)B * L;
+  const bool rec = m->timing;
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+
+  // P1: fused input projections [q|k|v|f_a|g_a|beta] on matrix cores
+  GemmParams g;
+  g.A = x_dev; g.lda = d.d_model; g.split_a = x_dtype == KDA_F32;
+  const PackedMat mats[6] = {Ly.wq, Ly.wk, Ly.wv, Ly.fa, Ly.ga, Ly.wbeta};
+  const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
+  int first = 0;
+  for (int i = 0; i < 6; ++i) {
+    g.seg_b[i] = reinterpret_cast<const uint16_t*>(mats[i].w);
+    g.seg_first[i] = first;
+    first += rows[i];
+  }
+  g.nseg = 6; g.M = (int)M; g.N = m->proj_rows; g.K = d.d_model;
+  g.C = F(wl.P); g.ldc = m->proj_stride; g.coff = 0;
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(g, s); });
+  if (r) return r;
+  // low-rank up-projections F_b f_lr and G_b g_lr (fp32 inputs as two BF16 terms)
+  GemmParams gf;
+  gf.A = F(wl.P) + m->C; gf.lda = m->proj_stride; gf.split_a = 1;
+  gf.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.fb.w); gf.nseg = 1;
+  gf.M = (int)M; gf.N = m->Kq; gf.K = d.rank_f;
+  gf.C = F(wl.FG); gf.ldc = m->Kq + m->V; gf.coff = 0;
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(gf, s); });
+  if (r) return r;
+  GemmParams gg = gf;
+  gg.A = F(wl.P) + m->C + d.rank_f;
+  gg.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.gb.w);
+  gg.N = m->V; gg.K = d.rank_g; gg.coff = m->Kq;
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(gg, s); });
+  if (r) return r;
+
+  PrefillParams p;
+  p.B = B; p.L = (int)L; p.H = d.n_heads; p.dk = d.d_k; p.dv = d.d_v; p.C = m->C;
+  p.rank_f = d.rank_f; p.rank_g = d.rank_g;
+  p.nch = (int)((L + kChunk - 1) / kChunk);
+  p.P = F(wl.P); p.proj_stride = m->proj_stride; p.FG = F(wl.FG);
+  p.win = st->conv_dev; p.win_out = st->conv_dev;
+  p.conv_w = Ly.conv_w; p.a_log = Ly.a_log; p.dt_bias = Ly.dt_bias; p.onw = Ly.o_norm_w;
+  p.l2_eps = d.l2_eps; p.q_scale = m->q_scale; p.norm_eps = d.norm_eps;
+  p.q = F(wl.q); p.k = F(wl.k); p.v = F(wl.v); p.g2 = F(wl.g2); p.beta = F(wl.beta);
+  p.gate = F(wl.gate);
+  p.W = F(wl.W); p.U = F(wl.U); p.Qt = F(wl.Qt); p.Kt = F(wl.Kt); p.A = F(wl.A); p.dec = F(wl.dec);
+  p.S = st->S_dev; p.o = F(wl.o);
+  // P2: conv + SiLU + L2 norms + gates over the sequence; then the final window
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_seq(p, s); });
+  if (r) return r;
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_window(p, s); });
+  if (r) return r;
+  // P3 / P4: chunked delta rule
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_chunk_intra(p, s); });
+  if (r) return r;
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_chunk_inter(p, s); });
+  if (r) return r;
+  // P5: gated RMSNorm, then the output projection (fp32 input as two BF16 terms)
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gated_norm(p, s); });
+  if (r) return r;
+  GemmParams go;
+  go.A = F(wl.o); go.lda = m->V; go.split_a = 1;
+  go.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.wo.w); go.nseg = 1;
+  go.M = (int)M; go.N = d.d_model; go.K = m->V;
+  go.C = y_dev; go.ldc = d.d_model; go.coff = 0;
+  return timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(go, s); });
 }
 
 }  // extern "C"

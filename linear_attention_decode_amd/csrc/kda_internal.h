@@ -119,6 +119,56 @@ hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, 
                                 int C, const int* ntok, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
+// Chunked prefill.
+// ---------------------------------------------------------------------------------------
+// C[m][coff + n] = sum_k A[m][k] B[n][k]; B = BF16 rows from up to kMaxSegs stacked
+// matrices ([rows][K] each, segment i starting at output column seg_first[i]); A = BF16
+// [M][lda] or, with split_a, FP32 [M][lda] taken as two BF16 terms.  K % 64 == 0.
+struct GemmParams {
+  const void* A = nullptr;
+  int lda = 0;
+  int split_a = 0;
+  const uint16_t* seg_b[kMaxSegs] = {};
+  int seg_first[kMaxSegs] = {};
+  int nseg = 0;
+  int M = 0, N = 0, K = 0;
+  float* C = nullptr;
+  int ldc = 0, coff = 0;
+};
+hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+
+constexpr int kChunk = 64;          // tokens per chunk of the chunked delta rule
+constexpr int kInterCols = 32;      // value columns per block of the inter-chunk kernel
+constexpr int kPrefillMaxChannels = 8192;  // conv channels + 2 heads' norms, sequence pass
+
+struct PrefillParams {
+  int B = 0, L = 0, H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
+  int nch = 0;                    // chunks per sequence
+  const float* P = nullptr;       // [B*L][proj_stride]: p (C) | f_lr | g_lr | beta logits
+  int proj_stride = 0;
+  const float* FG = nullptr;      // [B*L][H*dk + H*dv]: F_b f_lr | G_b g_lr
+  const float* win = nullptr;     // [B][3][C] initial conv window
+  float* win_out = nullptr;       // [B][3][C] final window (may alias win; own kernel)
+  const float* conv_w = nullptr;
+  const float* a_log = nullptr;
+  const float* dt_bias = nullptr;
+  const float* onw = nullptr;     // [dv] or null
+  float l2_eps = 0.f, q_scale = 0.f, norm_eps = 0.f;
+  // sequence-pass outputs, [B][H][L][dk|dv] and [B][H][L]
+  float *q = nullptr, *k = nullptr, *v = nullptr, *g2 = nullptr, *beta = nullptr;
+  float* gate = nullptr;          // [B*L][H*dv]
+  // intra-chunk outputs, per (b, h, chunk)
+  float *W = nullptr, *U = nullptr, *Qt = nullptr, *Kt = nullptr, *A = nullptr, *dec = nullptr;
+  float* S = nullptr;             // [B][H][dk][dv] state, read then overwritten
+  float* o = nullptr;             // [B*L][H*dv]: o, then the gated norm n in place
+};
+hipError_t launch_prefill_seq(const PrefillParams& p, hipStream_t s);
+hipError_t launch_prefill_window(const PrefillParams& p, hipStream_t s);
+hipError_t launch_chunk_intra(const PrefillParams& p, hipStream_t s);
+hipError_t launch_chunk_inter(const PrefillParams& p, hipStream_t s);
+hipError_t launch_gated_norm(const PrefillParams& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------
 // Packing.
 // ---------------------------------------------------------------------------------------
 hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, void* dst,
