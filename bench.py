@@ -4,8 +4,8 @@
 Workload: the 34-layer KDA stack (D=2048, 16 heads, d_k=d_v=128, all projections Q8_0,
 fp32 state [16][128][128] + 3-token conv window per layer, pre-RMSNorm residual stream),
 batch 1, synthetic seeded weights and inputs.  A step is one token through all 34 layers:
-the fused projection GEMV, the per-head delta-rule kernel and the gated-norm + output
-projection GEMV per layer, replayed as one hipGraph.
+the fused projection GEMV, the low-rank gate kernel, the per-head delta-rule kernel and
+the gated-norm + output projection GEMV per layer, replayed as one hipGraph.
 
 Prints ONE JSON line: tokens/s over K timed steps, HBM roofline of the dominant kernel
 (timed with hipEvents on the launch stream), and the CPU oracle on a bounded sample.
@@ -45,10 +45,11 @@ def algorithmic_bytes(w) -> dict:
     proj_w = q8(K, D) * 2 + q8(V, D) + q8(d.rank_f, D) + q8(d.rank_g, D) + q8(H, D)
     proj = proj_w + D * 4 + C * 3 * 4 * 2 + C * 4 * 4 + (C + d.rank_f + d.rank_g + H) * 4
     state = H * d.d_k * d.d_v * 4 * 2
-    head = state + q8(K, d.rank_f) + q8(V, d.rank_g) + (C + d.rank_f + d.rank_g + H) * 4 + V * 4 * 2
+    gates = q8(K, d.rank_f) + q8(V, d.rank_g) + (d.rank_f + d.rank_g) * 4 + (K + V) * 4
+    head = state + (C + H) * 4 + (K + V) * 4 + V * 4 * 2
     out = q8(D, V) + V * 4 * 2 + D * 4 * 2
     weights_state = proj_w + q8(K, d.rank_f) + q8(V, d.rank_g) + q8(D, V) + state
-    return {"proj": proj, "head": head, "out": out,
+    return {"proj": proj, "gates": gates, "head": head, "out": out,
             "layer_weights_state": weights_state,
             "token_weights_state": weights_state * w.n_layers}
 
@@ -141,7 +142,8 @@ def main():
     for i in range(args.steps):
         model.decode_step(xs[args.warmup + i], y, st, ws)
     torch.cuda.synchronize()
-    kinds = {"proj": kda.KDA_K_PROJ, "head": kda.KDA_K_HEAD, "out": kda.KDA_K_OUT}
+    kinds = {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES, "head": kda.KDA_K_HEAD,
+             "out": kda.KDA_K_OUT}
     times = {k: model.timing(v) for k, v in kinds.items()}
     model.set_option(kda.KDA_OPT_TIMING, 0)
     ab = algorithmic_bytes(w)

@@ -138,7 +138,7 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
 
 /* Kernel kinds reported by kda_timing_query. */
 typedef enum { KDA_K_PROJ = 0, KDA_K_HEAD = 1, KDA_K_OUT = 2, KDA_K_COMMIT = 3,
-               KDA_K_PREFILL = 4, KDA_K_COUNT = 5 } kda_kernel_kind;
+               KDA_K_PREFILL = 4, KDA_K_GATES = 5, KDA_K_COUNT = 6 } kda_kernel_kind;
 /* Sum of event-timed durations (ms) and launch count per kernel kind since the last
  * reset; synchronises on the recorded events.  reset != 0 clears the counters. */
 int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset);

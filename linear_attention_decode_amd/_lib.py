@@ -14,7 +14,7 @@ KDA_OK, KDA_E_ARG, KDA_E_SHAPE, KDA_E_ALIGN, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E
 KDA_F32, KDA_BF16, KDA_Q8_0 = 0, 1, 2
 KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL = 0, 1, 2
 KDA_OPT_GRAPH, KDA_OPT_TIMING = 0, 1
-KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL = range(5)
+KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES = range(6)
 DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0}
 
 EXPORTS = (

@@ -86,19 +86,21 @@ struct kda_model {
 };
 
 // ---------------------------------------------------------------------------------------
-// Workspace layout (decode / verify): proj [N][proj_stride] | o [N][V] | gate [N][V] |
-// ss [N][H][V/kHeadCols]; each region 256-byte aligned.
+// Workspace layout (decode / verify): proj [N][proj_stride] | alpha,gate [N][K+V] |
+// o [N][V] | gate [N][V] | ss [N][H][V/kHeadCols]; each region 256-byte aligned.
+// Verify log per layer: proj rows [N][proj_stride] then alpha,gate [N][K+V].
 // ---------------------------------------------------------------------------------------
 namespace {
 
 struct WsLayout {
-  size_t proj = 0, o = 0, gate = 0, ss = 0, total = 0;
+  size_t proj = 0, ag = 0, o = 0, gate = 0, ss = 0, total = 0;
 };
 
 WsLayout ws_layout(const kda_model* m, int64_t N) {
   WsLayout w;
   size_t off = 0;
   w.proj = off; off = align_up(off + (size_t)N * m->proj_stride * 4, 256);
+  w.ag = off;   off = align_up(off + (size_t)N * (m->Kq + m->V) * 4, 256);
   w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
   w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
   w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
@@ -201,9 +203,19 @@ int proj_grid(const GemvParams& p) {
   return s.first_tile + (s.rows + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
 }
 
-// One layer of decode (T = 1) or verify (T > 1): projections, per-head step, o_proj.
+int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, float* ag,
+                  hipStream_t s, bool rec) {
+  const kda_dims& d = m->d;
+  GatesParams gp;
+  gp.N = N; gp.K = m->Kq; gp.V = m->V; gp.dk = d.d_k; gp.rank = d.rank_f; gp.C = m->C;
+  gp.wt = d.wtype; gp.proj = proj; gp.proj_stride = m->proj_stride;
+  gp.fb = L.fb; gp.gb = L.gb; gp.a_log = L.a_log; gp.dt_bias = L.dt_bias; gp.out = ag;
+  return timed(m, KDA_K_GATES, s, rec, [&] { return launch_gates(gp, s); });
+}
+
+// One layer of decode (T = 1) or verify (T > 1): projections, gates, per-head step, o_proj.
 int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
-                  float* S, float* win, float* proj, const WsLayout& wl, char* ws,
+                  float* S, float* win, float* proj, float* ag, const WsLayout& wl, char* ws,
                   bool write_state, hipStream_t s, bool rec) {
   const kda_dims& d = m->d;
   const LayerDev& L = m->layers[l];
@@ -230,6 +242,9 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   int r = timed(m, KDA_K_PROJ, s, rec, [&] { return launch_gemv(d.wtype, kProX, pp, g1, s); });
   if (r) return r;
 
+  r = enqueue_gates(m, L, proj, N, ag, s, rec);
+  if (r) return r;
+
   HeadParams hp;
   hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
   hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
@@ -239,6 +254,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   hp.win = win; hp.conv_w = L.conv_w;
   hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
   hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
+  hp.alpha_gate = ag;
   hp.S = S; hp.write_state = write_state ? 1 : 0;
   hp.ntok = nullptr; hp.write_out = 1;
   hp.o = o; hp.gate = gate; hp.ss = ss;
@@ -275,10 +291,11 @@ int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, 
   const int B = st->batch;
   WsLayout wl = ws_layout(m, B);
   float* proj = reinterpret_cast<float*>(ws + wl.proj);
+  float* ag = reinterpret_cast<float*>(ws + wl.ag);
   for (int l = 0; l < m->d.n_layers; ++l) {
     const float* xin = (l == 0 || !m->d.prenorm_residual) ? x : y;
     int r = enqueue_layer(m, l, xin, y, B, 1, st->S_dev + l * state_layer_stride(m, B),
-                          st->conv_dev + l * win_layer_stride(m, B), proj, wl, ws, true, s, rec);
+                          st->conv_dev + l * win_layer_stride(m, B), proj, ag, wl, ws, true, s, rec);
     if (r) return r;
   }
   return KDA_OK;
@@ -495,7 +512,7 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
 
 size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T) {
   if (!m || batch < 1 || T < 1) return 0;
-  return (size_t)m->d.n_layers * batch * T * m->proj_stride * 4;
+  return (size_t)m->d.n_layers * batch * T * (m->proj_stride + m->Kq + m->V) * 4;
 }
 
 int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
@@ -514,11 +531,13 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
   float* logf = static_cast<float*>(log_dev);
-  const size_t log_layer = (size_t)B * T * m->proj_stride;
+  const size_t log_proj = (size_t)B * T * m->proj_stride;
+  const size_t log_layer = (size_t)B * T * (m->proj_stride + m->Kq + m->V);
   for (int l = 0; l < m->d.n_layers; ++l) {
     const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
+    float* lp = logf + l * log_layer;
     r = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
-                      st->conv_dev + l * win_layer_stride(m, B), logf + l * log_layer, wl, ws,
+                      st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj, wl, ws,
                       false, s, m->timing);
     if (r) return r;
   }
@@ -535,10 +554,12 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
   hipStream_t s = (hipStream_t)stream;
   const kda_dims& d = m->d;
   const float* logf = static_cast<const float*>(log_dev);
-  const size_t log_layer = (size_t)B * T * m->proj_stride;
+  const size_t log_proj = (size_t)B * T * m->proj_stride;
+  const size_t log_layer = (size_t)B * T * (m->proj_stride + m->Kq + m->V);
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerDev& L = m->layers[l];
     HeadParams hp;
+    hp.alpha_gate = logf + l * log_layer + log_proj;
     hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
     hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
     hp.B = B; hp.T = T;

@@ -8,19 +8,36 @@ namespace kda {
 
 constexpr int kWave = 64;
 
-// Sum over the 64 lanes of a wave; every lane receives the total.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// ---- cross-lane sums with DPP (VALU-rate lane permutes inside 16-lane rows) ----
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xb1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4e;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i inside each group of 8
+constexpr int kDppRor8 = 0x128;       // lane i <- lane (i+8) mod 16 inside each row of 16
+
+// Sum over aligned groups of n lanes (n in 1, 2, 4, 8, 16); every lane of a group gets it.
+__device__ __forceinline__ float group_sum(float v, int n) {
+  if (n >= 2) v += dpp_mov<kDppXor1>(v);
+  if (n >= 4) v += dpp_mov<kDppXor2>(v);
+  if (n >= 8) v += dpp_mov<kDppHalfMirror>(v);
+  if (n >= 16) v += dpp_mov<kDppRor8>(v);
   return v;
 }
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp_mov<kDppXor1>(v);
+  v += dpp_mov<kDppXor2>(v);
+  return v + dpp_mov<kDppHalfMirror>(v);
+}
+__device__ __forceinline__ float sum16(float v) { v = sum8(v); return v + dpp_mov<kDppRor8>(v); }
 
-// Sum over lanes that share (lane % width); every lane receives its group's total.
-template <int kWidth>
-__device__ __forceinline__ float wave_sum_strided(float v) {
-#pragma unroll
-  for (int o = 32; o >= kWidth; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+// Sum over the 64 lanes of a wave; every lane receives the total (wave-uniform).
+__device__ __forceinline__ float wave_sum(float v) {
+  const int b = __float_as_int(sum16(v));
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -83,8 +83,7 @@ int gemv_cols_per_pass(int N);
 // ---------------------------------------------------------------------------------------
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
 // ---------------------------------------------------------------------------------------
-constexpr int kHeadThreads = 256;
-constexpr int kHeadCols = 32;      // value columns per block
+constexpr int kHeadCols = 32;      // value columns per wave (one partial sum of o^2 each)
 
 struct HeadParams {
   int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
@@ -98,18 +97,30 @@ struct HeadParams {
   PackedMat fb, gb;               // [H*dk][rank_f], [H*dv][rank_g]
   const float* a_log = nullptr;
   const float* dt_bias = nullptr;
+  const float* alpha_gate = nullptr;  // [N][H*dk + H*dv]: alpha per key channel | output gate
   float* S = nullptr;             // [B][H][dk][dv]
   int write_state = 1;
   const int* ntok = nullptr;      // commit: tokens to apply per sequence (clamped 1..T)
   int write_out = 1;
   float* o = nullptr;             // [N][H*dv]
   float* gate = nullptr;          // [N][H*dv]
-  float* ss = nullptr;            // [N][H][dv/kHeadCols]
+  float* ss = nullptr;            // [N][H][dv/kHeadCols] partial sums of o^2
   float l2_eps = 0.f;
   float q_scale = 0.f;            // d_k^-1/2 as fp32
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
+
+struct GatesParams {
+  int N = 0, K = 0, V = 0, dk = 0, rank = 0, C = 0, wt = 0;
+  const float* proj = nullptr;    // [N][proj_stride]: f_lr at C, g_lr at C + rank
+  int proj_stride = 0;
+  PackedMat fb, gb;               // [K][rank], [V][rank]
+  const float* a_log = nullptr;   // [H]
+  const float* dt_bias = nullptr; // [K]
+  float* out = nullptr;           // [N][K + V]: alpha | gate
+};
+hipError_t launch_gates(const GatesParams& p, hipStream_t s);
 // Whether the per-head kernel handles these low-rank shapes (equal ranks, a power-of-two
 // number of 16-byte chunks per row, at most 10 chunk loads per thread).
 bool head_supported(int dk, int wt, int rank_f, int rank_g);
