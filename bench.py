@@ -49,7 +49,10 @@ def algorithmic_bytes(w) -> dict:
     head = state + (C + H) * 4 + (K + V) * 4 + V * 4 * 2
     out = q8(D, V) + V * 4 * 2 + D * 4 * 2
     weights_state = proj_w + q8(K, d.rank_f) + q8(V, d.rank_g) + q8(D, V) + state
-    return {"proj": proj, "gates": gates, "head": head, "out": out,
+    # the one-launch step: every layer's weights, state (read + write) and conv window
+    # (read + write), the input token and the output row
+    step = (weights_state + C * 3 * 4 * 2 + C * 4 * 4) * w.n_layers + D * 4 * 2
+    return {"proj": proj, "gates": gates, "head": head, "out": out, "step": step,
             "layer_weights_state": weights_state,
             "token_weights_state": weights_state * w.n_layers}
 
@@ -93,6 +96,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--per-layer", action="store_true",
+                    help="time the per-layer hipGraph path instead of the one-launch step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -123,6 +128,11 @@ def main():
     stream = torch.cuda.current_stream()
 
     model.set_option(kda.KDA_OPT_GRAPH, 1)
+    model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
+    one_launch = not args.per_layer and model.persistent_blocks() > 0
+    path = (f"one cooperative launch per token ({model.persistent_blocks()} blocks)" if one_launch
+            else "per-layer kernels replayed as one hipGraph")
+    log(f"[bench] path: {path}")
     for i in range(args.warmup):
         model.decode_step(xs[i], y, st, ws)
     torch.cuda.synchronize()
@@ -143,13 +153,15 @@ def main():
         model.decode_step(xs[args.warmup + i], y, st, ws)
     torch.cuda.synchronize()
     kinds = {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES, "head": kda.KDA_K_HEAD,
-             "out": kda.KDA_K_OUT}
+             "out": kda.KDA_K_OUT, "step": kda.KDA_K_STEP}
     times = {k: model.timing(v) for k, v in kinds.items()}
     model.set_option(kda.KDA_OPT_TIMING, 0)
     ab = algorithmic_bytes(w)
     per = {}
     for k, (ms, n) in times.items():
-        avg_us = ms * 1e3 / max(n, 1)
+        if n == 0:
+            continue
+        avg_us = ms * 1e3 / n
         per[k] = {"avg_us": avg_us, "launches": n, "bytes": ab[k],
                   "gbs": ab[k] / (avg_us * 1e-6) / 1e9}
         log(f"[bench] kernel {k}: {n} launches, avg {avg_us:.2f} us, "
@@ -180,6 +192,7 @@ def main():
                    "d_model": d.d_model, "heads": d.n_heads, "d_k": d.d_k, "d_v": d.d_v,
                    "weights": "q8_0", "state": "f32", "batch": B, "global_batch": B,
                    "seq_len": 1, "parallelism": "none (1 GPU)",
+                   "path": path,
                    "bytes_per_token": ab["token_weights_state"],
                    "step_hbm_gbs": round(step_gbs, 1),
                    "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),

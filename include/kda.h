@@ -130,15 +130,30 @@ void kda_model_destroy(kda_model* m);
 
 /* Options. */
 typedef enum {
-  KDA_OPT_GRAPH = 0,   /* 1 (default): decode steps replay a captured hipGraph of all
-                          layers, re-captured when a pointer or the batch changes */
-  KDA_OPT_TIMING = 1   /* 1: record hipEvents around every kernel launch (no graph) */
+  KDA_OPT_GRAPH = 0,      /* 1 (default): decode steps replay a captured hipGraph of all
+                             layers, re-captured when a pointer or the batch changes */
+  KDA_OPT_TIMING = 1,     /* 1: record hipEvents around every kernel launch (no graph) */
+  KDA_OPT_PERSISTENT = 2  /* 1 (default): batch-1 decode of an eligible model runs every
+                             layer in one cooperative launch (see kda_model_query) */
 } kda_option;
 int kda_model_set_option(kda_model* m, int option, int64_t value);
 
+/* Queries.  KDA_Q_PERSISTENT: number of blocks of the one-launch decode, 0 if the model is
+ * not eligible (it needs Q8_0 weights, a pre-norm residual stack, d_k = d_v = 128,
+ * H*d_v = D a multiple of 1024, and one co-resident block per CU).  The library allocates
+ * a few KB of device memory for it at kda_model_create (exchange words, layer table). */
+typedef enum { KDA_Q_PERSISTENT = 0 } kda_query;
+int kda_model_query(const kda_model* m, int what);
+
+/* Synchronises the device and reports whether a one-launch decode since the last call hit
+ * its bounded wait between blocks (KDA_E_HIP; that step's outputs and state are invalid
+ * and the exchange buffers are reset).  KDA_OK otherwise. */
+int kda_model_status(kda_model* m);
+
 /* Kernel kinds reported by kda_timing_query. */
 typedef enum { KDA_K_PROJ = 0, KDA_K_HEAD = 1, KDA_K_OUT = 2, KDA_K_COMMIT = 3,
-               KDA_K_PREFILL = 4, KDA_K_GATES = 5, KDA_K_COUNT = 6 } kda_kernel_kind;
+               KDA_K_PREFILL = 4, KDA_K_GATES = 5, KDA_K_STEP = 6,
+               KDA_K_COUNT = 7 } kda_kernel_kind;
 /* Sum of event-timed durations (ms) and launch count per kernel kind since the last
  * reset; synchronises on the recorded events.  reset != 0 clears the counters. */
 int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset);

@@ -15,7 +15,8 @@ from typing import Dict, List, Optional, Sequence
 from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
-                   KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, DTYPES, KdaError)
+                   KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP,
+                   KDA_OPT_PERSISTENT, KDA_Q_PERSISTENT, DTYPES, KdaError)
 
 _PROJ_NAMES = ("wq", "wk", "wv", "wo", "fa", "fb", "wbeta", "ga", "gb")
 
@@ -84,6 +85,14 @@ def kda_model_destroy(handle) -> None:
 
 def kda_model_set_option(handle, option: int, value: int) -> None:
     _lib.call("kda_model_set_option", handle, option, value)
+
+
+def kda_model_query(handle, what: int) -> int:
+    return _lib.lib().kda_model_query(handle, what)
+
+
+def kda_model_status(handle) -> None:
+    _lib.call("kda_model_status", handle)
 
 
 def kda_timing_query(handle, kind: int, reset: bool = False):
@@ -215,6 +224,14 @@ class KdaModel:
 
     def timing(self, kind: int, reset: bool = False):
         return kda_timing_query(self.handle, kind, reset)
+
+    def persistent_blocks(self) -> int:
+        """Blocks of the one-launch batch-1 decode (0: the model uses per-layer kernels)."""
+        return kda_model_query(self.handle, KDA_Q_PERSISTENT)
+
+    def status(self) -> None:
+        """Synchronise; raise if a one-launch decode hit its bounded inter-block wait."""
+        kda_model_status(self.handle)
 
     def decode_step(self, x, y, st: KdaStateBuf, ws, stream=None) -> None:
         kda_decode_step(self.handle, x, y, st, ws, stream)

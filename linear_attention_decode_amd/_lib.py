@@ -13,15 +13,17 @@ KDA_OK, KDA_E_ARG, KDA_E_SHAPE, KDA_E_ALIGN, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E
     KDA_E_UNSUPPORTED = range(8)
 KDA_F32, KDA_BF16, KDA_Q8_0 = 0, 1, 2
 KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL = 0, 1, 2
-KDA_OPT_GRAPH, KDA_OPT_TIMING = 0, 1
-KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES = range(6)
+KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT = 0, 1, 2
+KDA_Q_PERSISTENT = 0
+KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP = range(7)
 DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0}
 
 EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_last_error", "kda_packed_bytes", "kda_pack",
     "kda_unpack_q8_0", "kda_model_create", "kda_model_destroy", "kda_model_set_option",
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
-    "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked",
+    "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
+    "kda_model_status",
 )
 
 
@@ -69,6 +71,8 @@ def lib():
             "kda_model_create": (C.c_int, [C.POINTER(KdaDims), C.POINTER(KdaLayer), C.POINTER(vp)]),
             "kda_model_destroy": (None, [vp]),
             "kda_model_set_option": (C.c_int, [vp, C.c_int, i64]),
+            "kda_model_query": (C.c_int, [vp, C.c_int]),
+            "kda_model_status": (C.c_int, [vp]),
             "kda_timing_query": (C.c_int, [vp, C.c_int, C.POINTER(C.c_double), C.POINTER(i64), C.c_int]),
             "kda_workspace_bytes": (sz, [vp, C.c_int, i32, i64]),
             "kda_decode_step": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, sz, vp]),

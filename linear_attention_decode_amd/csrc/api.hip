@@ -78,6 +78,15 @@ struct kda_model {
   hipStream_t cap_stream = nullptr;
   hipGraphExec_t exec = nullptr;
   GraphKey key;
+  // one-launch decode (batch 1)
+  bool use_persist = true;
+  bool pers_ok = false;
+  int pers_blocks = 0;
+  PersistLayer* d_layers = nullptr;
+  uint64_t* xchg = nullptr;         // exchange words (xbuf | pbuf | gbuf | obuf)
+  int* err = nullptr;
+  uint32_t epoch = 0;
+  PersistParams pp;
   // timing
   std::vector<TimedLaunch> pool;
   size_t used = 0;
@@ -314,6 +323,82 @@ int check_state(const kda_model* m, const kda_state* st) {
   return KDA_OK;
 }
 
+// One-launch decode: eligible for batch 1, Q8_0 stacks with d_k = d_v = 128, H*d_v = D in
+// {1024, 2048}, low-rank gates of rank 32, 64 or 128, and enough co-resident blocks for the
+// static work split (one block per head, D/16 output-projection blocks after them, at most
+// 32 projection rows per block).
+size_t exchange_words(const kda_model* m) {
+  return 2 * (size_t)m->d.d_model + m->proj_rows + m->V + 3 * (size_t)kMaxPersistBlocks;
+}
+
+hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
+  const kda_dims& d = m->d;
+  const int nb = persistent_max_blocks();
+  const int ob0 = d.n_heads, nob = d.d_model / 16;
+  const int rank = d.rank_f;
+  bool ok = nb > 0 && nb <= kMaxPersistBlocks && d.wtype == KDA_Q8_0 && d.prenorm_residual &&
+            d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
+            (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
+            (rank == 32 || rank == 64 || rank == 128);
+  if (ok) {
+    const int rp = (m->proj_rows + nb - 1) / nb;
+    ok = rp <= 32 && ob0 + nob <= nb && 2 * d.d_k + d.d_v + 2 * rank + 1 <= 1024;
+  }
+  if (!ok) return hipSuccess;
+  std::vector<PersistLayer> host(d.n_layers);
+  for (int l = 0; l < d.n_layers; ++l) {
+    const LayerDev& L = m->layers[l];
+    PersistLayer& P = host[l];
+    P.seg[0] = L.wq; P.seg[1] = L.wk; P.seg[2] = L.wv; P.seg[3] = L.fa; P.seg[4] = L.ga; P.seg[5] = L.wbeta;
+    P.fb = L.fb; P.gb = L.gb; P.wo = L.wo;
+    P.conv_w = L.conv_w; P.a_log = L.a_log; P.dt_bias = L.dt_bias; P.o_norm_w = L.o_norm_w;
+  }
+  (void)layers;
+  hipError_t e = hipMalloc(&m->d_layers, sizeof(PersistLayer) * d.n_layers);
+  if (e != hipSuccess) return e;
+  e = hipMemcpy(m->d_layers, host.data(), sizeof(PersistLayer) * d.n_layers, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return e;
+  const size_t nx = 2 * (size_t)d.d_model, np = m->proj_rows, no = m->V;
+  e = hipMalloc(&m->xchg, exchange_words(m) * sizeof(uint64_t));
+  if (e != hipSuccess) return e;
+  e = hipMemset(m->xchg, 0, exchange_words(m) * sizeof(uint64_t));
+  if (e != hipSuccess) return e;
+  e = hipMalloc(&m->err, 256);
+  if (e != hipSuccess) return e;
+  e = hipMemset(m->err, 0, 256);
+  if (e != hipSuccess) return e;
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  PersistParams& p = m->pp;
+  p.n_layers = d.n_layers; p.D = d.d_model; p.H = d.n_heads; p.dk = d.d_k; p.dv = d.d_v;
+  p.C = m->C; p.rank = d.rank_f; p.proj_rows = m->proj_rows;
+  const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
+  int first = 0;
+  for (int i = 0; i < 6; ++i) { p.seg_first[i] = first; first += rows[i]; }
+  p.eps = d.norm_eps; p.l2_eps = d.l2_eps; p.q_scale = m->q_scale;
+  p.layers = m->d_layers;
+  p.xbuf = m->xchg; p.pbuf = p.xbuf + nx; p.obuf = p.pbuf + np; p.flags = p.obuf + no;
+  p.err = m->err;
+  int dev = 0, khz = 0;
+  e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return e;
+  p.timeout = (uint64_t)(khz > 0 ? khz : 100000) * 50;   // 50 ms of wall clock per wait
+  p.o_first_block = ob0; p.o_blocks = nob;
+  m->pers_blocks = nb;
+  m->pers_ok = true;
+  return hipSuccess;
+}
+
+int reset_exchange(kda_model* m) {
+  KDA_HIP(hipDeviceSynchronize());
+  KDA_HIP(hipMemset(m->xchg, 0, exchange_words(m) * sizeof(uint64_t)));
+  KDA_HIP(hipMemset(m->err, 0, 256));
+  KDA_HIP(hipDeviceSynchronize());
+  m->epoch = 0;
+  return KDA_OK;
+}
+
 }  // namespace
 
 // =======================================================================================
@@ -424,8 +509,9 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
     m->layers.push_back(L);
   }
   hipError_t e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = persist_setup(m, layers);
   if (e != hipSuccess) {
-    delete m;
+    kda_model_destroy(m);
     return fail(KDA_E_HIP, "model setup: %s", hipGetErrorString(e));
   }
   *out = m;
@@ -435,6 +521,9 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
 void kda_model_destroy(kda_model* m) {
   if (!m) return;
   drop_graph(m);
+  if (m->d_layers) (void)hipFree(m->d_layers);
+  if (m->xchg) (void)hipFree(m->xchg);
+  if (m->err) (void)hipFree(m->err);
   for (auto& t : m->pool) {
     (void)hipEventDestroy(t.a);
     (void)hipEventDestroy(t.b);
@@ -453,8 +542,34 @@ int kda_model_set_option(kda_model* m, int option, int64_t value) {
     case KDA_OPT_TIMING:
       m->timing = value != 0;
       return KDA_OK;
+    case KDA_OPT_PERSISTENT:
+      m->use_persist = value != 0;
+      return KDA_OK;
     default:
       return fail(KDA_E_ARG, "unknown option %d", option);
+  }
+}
+
+int kda_model_status(kda_model* m) {
+  if (!m) return fail(KDA_E_ARG, "null model");
+  KDA_HIP(hipDeviceSynchronize());
+  if (!m->pers_ok) return KDA_OK;
+  int err = 0;
+  KDA_HIP(hipMemcpy(&err, m->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err) {
+    int r = reset_exchange(m);
+    if (r) return r;
+    return fail(KDA_E_HIP, "one-launch decode: a wait between blocks timed out; outputs of "
+                "the affected steps are invalid");
+  }
+  return KDA_OK;
+}
+
+int kda_model_query(const kda_model* m, int what) {
+  if (!m) return -1;
+  switch (what) {
+    case KDA_Q_PERSISTENT: return m->pers_ok ? m->pers_blocks : 0;
+    default: return -1;
   }
 }
 
@@ -488,6 +603,16 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
     return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, ws_layout(m, st->batch).total);
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
+  if (m->use_persist && m->pers_ok && st->batch == 1) {
+    if (m->epoch >= 0x7fffffffu / (uint32_t)m->d.n_layers) {
+      r = reset_exchange(m);
+      if (r) return r;
+    }
+    PersistParams p = m->pp;
+    p.S = st->S_dev; p.win = st->conv_dev; p.x_in = x_dev; p.y_out = y_dev;
+    p.epoch = ++m->epoch;
+    return timed(m, KDA_K_STEP, s, m->timing, [&] { return launch_persistent(p, m->pers_blocks, s); });
+  }
   if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing);
 
   GraphKey k;

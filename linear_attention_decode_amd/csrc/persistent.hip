@@ -1,0 +1,667 @@
+// One-launch decode step for gfx950: every layer of the stack for one token (batch 1) in a
+// single cooperative launch of one block per CU.
+//
+// Per layer the blocks run three phases of the KDA step ("Where the time goes", "Thirty
+// tiny kernels per layer", frederic.ai):
+//   P  every block: RMSNorm(x) and its slice of the fused input projections
+//      [W_q; W_k; W_v; F_a; G_a; W_beta], with the causal conv + SiLU + window roll applied
+//      by the owner of each q/k/v channel;
+//   H  one block per head: the low-rank forget gate alpha and output gate (all four waves),
+//      then the gated delta rule (one wave per 32 value columns, state in registers) and the
+//      head's gated RMSNorm;
+//   O  a band of blocks: the output projection of the normalised heads plus the residual.
+// Every block streams a slice of every matrix, and it requests the next slice as soon as it
+// has used the current one, so the weights of layer l + 1 are in flight while layer l's
+// later phases run.  The weight loads go through global-address-space pointers (no flat
+// accesses) with wave-uniform row addresses, so a wave issues all of its rows back to back.
+//
+// Blocks hand activations to each other as 64-bit words (tag << 32 | fp32 bits) written
+// and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
+// the token and layer.  A consumer first watches one flag word per producer block (one
+// wave, a short sleep between polls, so polling stays far below the weight stream), then
+// fetches the data words, whose own tags it still checks.  Every wait is bounded: on a
+// timeout the block records an error word and every block leaves the kernel.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+#define KDA_GLOBAL __attribute__((address_space(1)))
+#define KDA_CONST __attribute__((address_space(4)))
+
+namespace kda {
+
+constexpr int kPT = 256;         // threads per block
+constexpr int kPRows = 8;        // max projection rows per wave
+constexpr int kORows = 4;        // max output-projection rows per wave
+constexpr int kGHItems = 8;      // gate chunks per thread in a head block
+
+using GLayer = const KDA_CONST PersistLayer;
+
+template <class T>
+__device__ __forceinline__ const KDA_GLOBAL T* gp(const T* p) { return (const KDA_GLOBAL T*)p; }
+template <class T>
+__device__ __forceinline__ KDA_GLOBAL T* gpw(T* p) { return (KDA_GLOBAL T*)p; }
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 gload4(const float* p) {
+  const f32x4 v = *(const KDA_GLOBAL f32x4*)p;
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void gstore4(float* p, const float4 v) {
+  *(KDA_GLOBAL f32x4*)p = f32x4{v.x, v.y, v.z, v.w};
+}
+
+// 16 weight bytes, streamed once per token.
+__device__ __forceinline__ uint4 wload(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load((const KDA_GLOBAL u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// Raw fp16 bits of a Q8_0 scale (converted when used, so the load is not waited on).
+__device__ __forceinline__ uint32_t sload(const __half* p) { return *(const KDA_GLOBAL uint16_t*)p; }
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return __half2float(__ushort_as_half((unsigned short)bits));
+}
+
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, float v) {
+  return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+}
+__device__ __forceinline__ void put(uint64_t* p, uint32_t tag, float v) {
+  __hip_atomic_store(gpw(p), tagged(tag, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t peek(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<KDA_GLOBAL uint64_t*>(gp(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int err_set(const PersistParams& P) {
+  return __hip_atomic_load(gpw(P.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll bookkeeping: every 32 polls look at the error word and the wall clock; give up after
+// P.timeout wall-clock ticks (tens of milliseconds, against microseconds expected).
+struct Spin {
+  uint64_t t0;
+  int n = 0;
+  __device__ Spin() : t0(wall_clock64()) {}
+  // true when the wait must stop (another block failed, or this one timed out)
+  __device__ bool stop(const PersistParams& P) {
+    if ((++n & 31) != 0) return false;
+    if (err_set(P)) return true;
+    if (wall_clock64() - t0 > P.timeout) {
+      __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return true;
+    }
+    return false;
+  }
+};
+
+enum FlagPhase { kFlagP = 0, kFlagH = 1, kFlagO = 2 };
+
+__device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase, int i) {
+  return P.flags + (size_t)phase * kMaxPersistBlocks + i;
+}
+
+// One wave: wait until flags [0, n) of `phase` carry `tag` (n <= 4 * 64).  Every flag is
+// loaded at once; only the ones not yet set are polled again.
+__device__ bool wave_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag) {
+  const int lane = threadIdx.x & 63;
+  Spin sp;
+  bool ok[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) ok[k] = lane + 64 * k >= n;
+  while (true) {
+    uint64_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (!ok[k]) w[k] = peek(flag_slot(P, phase, lane + 64 * k));
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!ok[k]) ok[k] = (uint32_t)(w[k] >> 32) == tag;
+      all &= ok[k];
+    }
+    if (__ballot(!all) == 0) return true;
+    if (sp.stop(P)) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Whole block: wave 0 watches the producer flags, the other waves wait at the barrier.
+__device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag) {
+  int bad = 0;
+  if (threadIdx.x < 64) bad = !wave_wait_flags(P, phase, n, tag);
+  return __syncthreads_or(bad) == 0;
+}
+
+// One tagged word; spins (bounded) until it carries `tag`.  Returns false on a failed wait.
+__device__ __forceinline__ bool fetch_word(const uint64_t* p, uint32_t tag, float& v, Spin& sp,
+                                           const PersistParams& P) {
+  uint64_t w = peek(p);
+  while ((uint32_t)(w >> 32) != tag) {
+    if (sp.stop(P)) return false;
+    w = peek(p);
+  }
+  v = __uint_as_float((uint32_t)w);
+  return true;
+}
+
+// Block-wide fetch of NPT * kPT tagged words into dst[] (LDS), with the sums of every 16
+// consecutive words into dsum[] and each thread's sum of squares in ss.  Thread t takes words
+// t, t + kPT, ...; every load is issued before the first tag is checked, and only words not
+// yet tagged are polled again.  The 16 lanes t & ~15 .. hold one 16-word chunk.  Ends with a
+// barrier; returns block-uniform false on a failed wait.
+template <int NPT>
+__device__ bool fetch_vec(const uint64_t* buf, uint32_t tag, float* dst, float* dsum, float& ss,
+                          const PersistParams& P) {
+  const int tid = threadIdx.x;
+  uint64_t w[NPT];
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) w[k] = peek(buf + tid + k * kPT);
+  int bad = 0;
+  Spin sp;
+  ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NPT; ++k) {
+    while (!bad && (uint32_t)(w[k] >> 32) != tag) {
+      if (sp.stop(P)) bad = 1;
+      else w[k] = peek(buf + tid + k * kPT);
+    }
+    const float v = __uint_as_float((uint32_t)w[k]);
+    const int i = tid + k * kPT;
+    dst[i] = v;
+    ss += v * v;
+    const float cs = sum16(v);
+    if ((tid & 15) == 0) dsum[i >> 4] = cs;
+  }
+  return __syncthreads_or(bad) == 0;
+}
+
+// Dot of one 16-byte Q8_0 chunk with 16 inputs held in registers.
+__device__ __forceinline__ float q8_dot16(const uint4 w, const float4 (&x)[4]) {
+  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += (float)(d[i] & 0xffu) * x[i].x;
+    s += (float)((d[i] >> 8) & 0xffu) * x[i].y;
+    s += (float)((d[i] >> 16) & 0xffu) * x[i].z;
+    s += (float)(d[i] >> 24) * x[i].w;
+  }
+  return s;
+}
+
+// Wave-wide dots of up to NR rows (the first n, n wave-uniform) whose chunks this lane holds
+// (chunk u * 64 + lane of each row) with the LDS vector xs (chunk sums in xsum).  The lane's
+// 16-element slices of xs are read once, as aligned float4s, for all rows.
+template <int U, int NR>
+__device__ __forceinline__ void dot_rows(const uint4 (&w)[NR][U], const uint32_t (&d)[NR][U],
+                                         int n, const float* xs, const float* xsum,
+                                         float (&acc)[NR]) {
+  const int lane = threadIdx.x & 63;
+  float4 xv[U][4];
+  float xc[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int c = u * 64 + lane;
+    const float4* p = reinterpret_cast<const float4*>(xs + c * 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) xv[u][k] = p[k];
+    xc[u] = xsum[c];
+  }
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float a = 0.0f;
+    if (r < n) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) a += h2f(d[r][u]) * (q8_dot16(w[r][u], xv[u]) - 128.0f * xc[u]);
+      a = wave_sum(a);
+    }
+    acc[r] = a;
+  }
+}
+
+// The projection weights of one wave's rows [r0, r1) of layer L (r0, r1 wave-uniform).
+template <int U>
+struct ProjRegs {
+  uint4 w[kPRows][U];
+  uint32_t d[kPRows][U];
+  float4 cw;               // lane r: conv taps of row r0 + r (q/k/v channels)
+  float z0, z1, z2;        // lane r: its conv window, oldest first
+};
+
+template <int U>
+__device__ __forceinline__ void issue_proj(const PersistParams& P, GLayer& L, const float* win,
+                                           int r0, int r1, ProjRegs<U>& R) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < kPRows; ++r) {
+    const int row = r0 + r;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      R.w[r][u] = make_uint4(0, 0, 0, 0);
+      R.d[r][u] = 0;
+    }
+    if (row < r1) {
+      int first = 0, seg = 0;
+#pragma unroll
+      for (int i = 1; i < 6; ++i)
+        if (row >= P.seg_first[i]) { first = P.seg_first[i]; seg = i; }
+      const uint8_t* wr = L.seg[seg].w + (size_t)(row - first) * P.D;
+      const __half* dr = L.seg[seg].d + (size_t)(row - first) * (P.D / 32);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane;
+        R.w[r][u] = wload(wr + (size_t)c * 16);
+        R.d[r][u] = sload(dr + (c >> 1));
+      }
+    }
+  }
+  const int myrow = r0 + lane;
+  R.cw = make_float4(0.f, 0.f, 0.f, 0.f);
+  R.z0 = R.z1 = R.z2 = 0.0f;
+  if (lane < kPRows && myrow < r1 && myrow < P.C) {
+    R.cw = gload4(L.conv_w + (size_t)myrow * 4);
+    R.z0 = *gp(win + myrow);
+    R.z1 = *gp(win + P.C + myrow);
+    R.z2 = *gp(win + 2 * P.C + myrow);
+  }
+}
+
+// The output-projection weights of one wave's rows [r0, r0 + n).
+template <int U>
+struct OutRegs {
+  uint4 w[kORows][U];
+  uint32_t d[kORows][U];
+};
+
+template <int U>
+__device__ __forceinline__ void issue_out(const PersistParams& P, GLayer& L, int r0, int n,
+                                          OutRegs<U>& R) {
+  const int lane = threadIdx.x & 63;
+  const int KO = P.H * P.dv;
+#pragma unroll
+  for (int r = 0; r < kORows; ++r) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      R.w[r][u] = make_uint4(0, 0, 0, 0);
+      R.d[r][u] = 0;
+    }
+    if (r < n) {
+      const uint8_t* wr = L.wo.w + (size_t)(r0 + r) * KO;
+      const __half* dr = L.wo.d + (size_t)(r0 + r) * (KO / 32);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = u * 64 + lane;
+        R.w[r][u] = wload(wr + (size_t)c * 16);
+        R.d[r][u] = sload(dr + (c >> 1));
+      }
+    }
+  }
+}
+
+// A head block's registers: wave w's state tile (rows 16 (lane & 7) .. + 16, value columns
+// 32 w + 4 (lane >> 3) .. + 4) and the block's gate-weight chunks (item i of thread t is
+// chunk (i * kPT + t) of the [alpha rows | gate rows] x rank slice).
+struct HeadRegs {
+  float4 st[16];
+  uint4 gw[kGHItems];
+  uint32_t gd[kGHItems];
+  float dtb[kGHItems];
+  float4 onw;
+  float ea;                // exp(A_log[h])
+};
+
+__device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, const float* Sl,
+                                           int h, HeadRegs& R) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int dk = P.dk, dv = P.dv, rank = P.rank, cpr = rank / 16;
+  const int j = wave * 32 + (lane >> 3) * 4, r0 = (lane & 7) * 16;
+  const float* Sb = Sl + (size_t)h * dk * dv + j;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * dv);
+  const int nitems = (dk + dv) * cpr;
+#pragma unroll
+  for (int i = 0; i < kGHItems; ++i) {
+    const int it = i * kPT + tid;
+    const int row = it / cpr, c = it - row * cpr;
+    R.gw[i] = make_uint4(0, 0, 0, 0);
+    R.gd[i] = 0;
+    R.dtb[i] = 0.0f;
+    if (it < nitems) {
+      const bool f = row < dk;
+      const PackedMat M = f ? PackedMat{L.fb.w, L.fb.d} : PackedMat{L.gb.w, L.gb.d};
+      const int r = f ? h * dk + row : h * dv + row - dk;
+      R.gw[i] = wload(M.w + (size_t)r * rank + (size_t)c * 16);
+      R.gd[i] = sload(M.d + (size_t)r * (rank / 32) + (c >> 1));
+      if (f) R.dtb[i] = *gp(L.dt_bias + r);
+    }
+  }
+  R.onw = make_float4(1.f, 1.f, 1.f, 1.f);
+  if (L.o_norm_w) R.onw = gload4(L.o_norm_w + j);
+  R.ea = *gp(L.a_log + h);   // exponentiated when used
+}
+
+// LDS of one block.
+struct Smem {
+  alignas(16) float xs[4096];          // x, then (O blocks) the normalised heads
+  float xsum[256];         // 16-element chunk sums of xs
+  float red[8];
+  float xres[4 * kORows];  // this O block's residual rows
+  alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
+  float s_al[256];         // head block: alpha rows
+  float s_gt[256];         // head block: output-gate columns
+  float s_ss[4];           // head block: per-wave partial o^2 sums
+};
+
+// Static roles of block b: its projection rows, and whether it runs a head or an
+// output-projection band.
+struct Roles {
+  int wr0, wr1;            // this wave's projection rows (wave-uniform)
+  int ob, or0, owr0, orw;  // O band index, block's first row, wave's first row, rows/wave
+};
+
+__device__ __forceinline__ Roles make_roles(const PersistParams& P, int wave) {
+  Roles R;
+  // projection rows go to blocks [H, nb): head blocks keep their loads for the state
+  const int b = blockIdx.x - P.H, nb = gridDim.x - P.H;
+  const int rp = (P.proj_rows + nb - 1) / nb;
+  const int p0 = min(P.proj_rows, max(b, 0) * rp), p1 = b < 0 ? p0 : min(P.proj_rows, p0 + rp);
+  const int rpw = (rp + 3) / 4;
+  R.wr0 = min(p1, p0 + wave * rpw);
+  R.wr1 = min(p1, R.wr0 + rpw);
+  const int ro = P.D / P.o_blocks;
+  R.ob = (int)blockIdx.x - P.o_first_block;
+  R.orw = ro / 4;
+  R.or0 = R.ob * ro;
+  R.owr0 = R.or0 + wave * R.orw;
+  return R;
+}
+
+// P phase of layer l (blocks [H, nb)): wait for x_l, RMSNorm, this block's projection rows,
+// conv epilogue; the next layer's slice is requested as soon as this one is used.
+// Returns false on a failed wait.
+template <int U, bool OBLK>
+__device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const Roles& R, int l,
+                                        uint32_t tag, ProjRegs<U>& pr) {
+  GLayer* Lt = (GLayer*)P.layers;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int D = P.D, C = P.C;
+  float* win = P.win + (size_t)l * 3 * C;
+  float ss = 0.0f;
+  if (l == 0) {
+    for (int i = tid; i < D; i += kPT) {
+      const float v = *gp(P.x_in + i);
+      sm.xs[i] = v;
+      ss += v * v;
+      const float cs = sum16(v);
+      if ((tid & 15) == 0) sm.xsum[i >> 4] = cs;
+    }
+    __syncthreads();
+  } else {
+    // x_l: all O blocks of layer l - 1
+    if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u)) return false;
+    if (!fetch_vec<4 * U>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, sm.xs, sm.xsum, ss, P)) return false;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) sm.red[wave] = ss;
+  if (OBLK && tid < 4 * R.orw) sm.xres[tid] = sm.xs[R.or0 + tid];
+  __syncthreads();
+  const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
+  float accs[kPRows];
+  dot_rows<U, kPRows>(pr.w, pr.d, R.wr1 - R.wr0, sm.xs, sm.xsum, accs);
+  // lane r finishes row wr0 + r: conv + SiLU + window roll for q/k/v channels
+  float v = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kPRows; ++r)
+    if (lane == r) v = accs[r] * sc;
+  const int row = R.wr0 + lane;
+  const bool mine = lane < kPRows && row < R.wr1;
+  const float pre = v;
+  if (mine) {
+    if (row < C) v = silu_f(pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * v);
+    put(P.pbuf + row, tag, v);
+  }
+  __syncthreads();
+  if (tid == 0) put(flag_slot(P, kFlagP, blockIdx.x - P.H), tag, 0.0f);
+  // off the critical path: roll the conv window, request the next layer's slice
+  if (mine && row < C) {
+    float* z = win + row;
+    *gpw(z) = pr.z1;
+    *gpw(z + C) = pr.z2;
+    *gpw(z + 2 * C) = pre;
+  }
+  if (l + 1 < P.n_layers) issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.wr0, R.wr1, pr);
+  return true;
+}
+
+// H phase of layer l for head h (block h): gates, delta rule, the head's gated RMSNorm.
+__device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l, uint32_t tag,
+                                        HeadRegs& hr) {
+  GLayer* Lt = (GLayer*)P.layers;
+  GLayer& L = Lt[l];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x;
+  const int H = P.H, dk = P.dk, dv = P.dv, C = P.C, K = H * dk;
+  const int rank = P.rank, cpr = rank / 16;
+  float* Sl = P.S + (size_t)l * H * dk * dv;
+  // every projection block: the head's inputs come from many of them, and waiting for all
+  // of them also orders this layer's reads of pbuf before the next layer's writes
+  if (!block_wait_flags(P, kFlagP, gridDim.x - H, tag)) return false;
+  // inputs: q [dk] | k [dk] | v [dv] | f_lr [rank] | g_lr [rank] | beta  (at most 4 per thread)
+  const int n_in = 2 * dk + dv + 2 * rank + 1;
+  {
+    uint64_t w[4];
+    int src[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + k * kPT;
+      if (i < dk) src[k] = h * dk + i;
+      else if (i < 2 * dk) src[k] = K + h * dk + (i - dk);
+      else if (i < 2 * dk + dv) src[k] = 2 * K + h * dv + (i - 2 * dk);
+      else if (i < 2 * dk + dv + 2 * rank) src[k] = C + (i - 2 * dk - dv);
+      else src[k] = C + 2 * rank + h;
+      w[k] = i < n_in ? peek(P.pbuf + src[k]) : tagged(tag, 0.0f);
+    }
+    int bad = 0;
+    Spin sp;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = tid + k * kPT;
+      while (!bad && (uint32_t)(w[k] >> 32) != tag) {
+        if (sp.stop(P)) bad = 1;
+        else w[k] = peek(P.pbuf + src[k]);
+      }
+      if (i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
+    }
+    if (__syncthreads_or(bad)) return false;
+  }
+  const float* s_q = sm.s_in;
+  const float* s_k = sm.s_in + dk;
+  const float* s_v = sm.s_in + 2 * dk;
+  const float* s_fl = sm.s_in + 2 * dk + dv;
+  const float* s_gl = s_fl + rank;
+  const float beta = sigmoid_f(sm.s_in[2 * dk + dv + 2 * rank]);
+  // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr).
+  // Item i of this thread is chunk c = tid % cpr of gate row (i * kPT + tid) / cpr (with
+  // d_k + d_v = kPT rows, a thread has exactly cpr items), so the thread needs one
+  // 16-element slice of f_lr and one of g_lr.  After the group sums, lane c of each group
+  // finishes item c: one transcendental per lane.
+  {
+    const int c = tid % cpr;
+    float4 xf[4], xg[4];
+    float sf = 0.0f, sg = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      xf[k] = reinterpret_cast<const float4*>(s_fl + c * 16)[k];
+      xg[k] = reinterpret_cast<const float4*>(s_gl + c * 16)[k];
+      sf += (xf[k].x + xf[k].y) + (xf[k].z + xf[k].w);
+      sg += (xg[k].x + xg[k].y) + (xg[k].z + xg[k].w);
+    }
+    float mine = 0.0f, bias = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kGHItems; ++i) {
+      if (i < cpr) {   // block-uniform
+        const bool f = (i * kPT + tid) / cpr < dk;
+        float part = h2f(hr.gd[i]) * (f ? q8_dot16(hr.gw[i], xf) - 128.0f * sf
+                                        : q8_dot16(hr.gw[i], xg) - 128.0f * sg);
+        part = group_sum(part, cpr);
+        if (c == i) { mine = part; bias = hr.dtb[i]; }
+      }
+    }
+    const int grow = (c * kPT + tid) / cpr;
+    if (grow < dk) sm.s_al[grow] = expf(-expf(hr.ea) * softplus_f(mine + bias));
+    else sm.s_gt[grow - dk] = sigmoid_f(mine);
+  }
+  __syncthreads();
+  // delta rule: wave w owns value columns 32 w .. 32 w + 31
+  const int rg = lane & 7, cq = lane >> 3;
+  const int j = wave * 32 + cq * 4, r0 = rg * 16;
+  float4 qv[4], kv[4], av[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    qv[k] = reinterpret_cast<const float4*>(s_q + r0)[k];
+    kv[k] = reinterpret_cast<const float4*>(s_k + r0)[k];
+    av[k] = reinterpret_cast<const float4*>(sm.s_al + r0)[k];
+  }
+  const float4 vv = *reinterpret_cast<const float4*>(s_v + j);
+  const float4 gv = *reinterpret_cast<const float4*>(sm.s_gt + j);
+  const float* qa = reinterpret_cast<const float*>(qv);
+  const float* ka = reinterpret_cast<const float*>(kv);
+  const float* aa = reinterpret_cast<const float*>(av);
+  float aq = 0.0f, ak = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    aq += qa[i] * qa[i];
+    ak += ka[i] * ka[i];
+  }
+  const float inv_q = P.q_scale / sqrtf(sum8(aq) + P.l2_eps);
+  const float inv_k = 1.0f / sqrtf(sum8(ak) + P.l2_eps);
+  float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float a = aa[i], kk = ka[i] * inv_k;
+    float4& s = hr.st[i];
+    s.x *= a; s.y *= a; s.z *= a; s.w *= a;
+    e0 += s.x * kk; e1 += s.y * kk; e2 += s.z * kk; e3 += s.w * kk;
+  }
+  e0 = sum8(e0); e1 = sum8(e1); e2 = sum8(e2); e3 = sum8(e3);
+  const float d0 = beta * (vv.x - e0), d1 = beta * (vv.y - e1);
+  const float d2 = beta * (vv.z - e2), d3 = beta * (vv.w - e3);
+  float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float kk = ka[i] * inv_k, qq = qa[i] * inv_q;
+    float4& s = hr.st[i];
+    s.x += kk * d0; s.y += kk * d1; s.z += kk * d2; s.w += kk * d3;
+    o0 += s.x * qq; o1 += s.y * qq; o2 += s.z * qq; o3 += s.w * qq;
+  }
+  o0 = sum8(o0); o1 = sum8(o1); o2 = sum8(o2); o3 = sum8(o3);
+  // the head's RMSNorm over its dv outputs: per-wave partial sums through LDS
+  float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;   // identical on the 8 lanes of a group
+  q2 += dpp_mov<kDppRor8>(q2);
+  const int qb = __float_as_int(q2);
+  const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
+                    (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
+  if (lane == 0) sm.s_ss[wave] = tot;
+  __syncthreads();
+  const float hs = 1.0f / sqrtf(((sm.s_ss[0] + sm.s_ss[1]) + (sm.s_ss[2] + sm.s_ss[3])) / (float)dv + P.eps);
+  if (rg == 0) {
+    uint64_t* ob = P.obuf + h * dv + j;
+    put(ob + 0, tag, o0 * hs * hr.onw.x * gv.x);
+    put(ob + 1, tag, o1 * hs * hr.onw.y * gv.y);
+    put(ob + 2, tag, o2 * hs * hr.onw.z * gv.z);
+    put(ob + 3, tag, o3 * hs * hr.onw.w * gv.w);
+  }
+  __syncthreads();
+  if (tid == 0) put(flag_slot(P, kFlagH, h), tag, 0.0f);
+  // off the critical path: write the state back, request the next layer's
+  float* Sb = Sl + (size_t)h * dk * dv + j;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) gstore4(Sb + (size_t)(r0 + i) * dv, hr.st[i]);
+  if (l + 1 < P.n_layers) issue_head(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, hr);
+  return true;
+}
+
+// O phase of layer l: this band's output-projection rows of the normalised heads, plus the
+// residual; the last layer also writes the output row.
+template <int U>
+__device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const Roles& R, int l,
+                                        uint32_t tag, OutRegs<U>& orr) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int D = P.D;
+  if (!block_wait_flags(P, kFlagH, P.H, tag)) return false;
+  float ssd;
+  if (!fetch_vec<4 * U>(P.obuf, tag, sm.xs, sm.xsum, ssd, P)) return false;
+  float accs[kORows];
+  dot_rows<U, kORows>(orr.w, orr.d, R.orw, sm.xs, sm.xsum, accs);
+  float v = 0.0f;
+#pragma unroll
+  for (int r = 0; r < kORows; ++r)
+    if (lane == r) v = accs[r];
+  if (lane < R.orw) {
+    const int row = R.owr0 + lane;
+    const float xn = sm.xres[row - R.or0] + v;
+    put(P.xbuf + (size_t)(l & 1) * D + row, tag, xn);
+    if (l + 1 == P.n_layers) *gpw(P.y_out + row) = xn;
+  }
+  __syncthreads();
+  if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
+  return true;
+}
+
+// The layer loop of one role: ROLE 0 projection only, 1 head block, 2 projection + output
+// band.  Each role keeps only its own prefetch registers live.  Prefetches are issued right
+// after a phase that is followed by a long wait, never just before a poll on the critical
+// path (a poll's load completes only after the loads issued before it).
+template <int U, int ROLE>
+__device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
+  GLayer* Lt = (GLayer*)P.layers;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const Roles R = make_roles(P, wave);
+  const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
+  if constexpr (ROLE == 1) {
+    HeadRegs hr;
+    issue_head(P, Lt[0], P.S, blockIdx.x, hr);
+    for (int l = 0; l < P.n_layers; ++l)
+      if (!phase_h(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
+  } else {
+    ProjRegs<U> pr;
+    issue_proj<U>(P, Lt[0], P.win, R.wr0, R.wr1, pr);
+    if constexpr (ROLE == 2) {
+      OutRegs<U> orr;
+      for (int l = 0; l < P.n_layers; ++l) {
+        const uint32_t tag = tag0 + (uint32_t)l + 1u;
+        if (!phase_p<U, true>(P, sm, R, l, tag, pr)) return;
+        issue_out<U>(P, Lt[l], R.owr0, R.orw, orr);
+        if (!phase_o<U>(P, sm, R, l, tag, orr)) return;
+      }
+    } else {
+      for (int l = 0; l < P.n_layers; ++l)
+        if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr)) return;
+    }
+  }
+}
+
+template <int U>   // 16-byte chunks per lane per row: U = D / 1024
+__global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const PersistParams P) {
+  __shared__ Smem sm;
+  const int b = blockIdx.x;
+  if (b < P.H) run_role<U, 1>(P, sm);
+  else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, 2>(P, sm);
+  else run_role<U, 0>(P, sm);
+}
+
+hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s) {
+  void* args[] = {const_cast<PersistParams*>(&p)};
+  const void* fn = p.D == 2048 ? (const void*)decode_persistent_kernel<2>
+                               : (const void*)decode_persistent_kernel<1>;
+  return hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
+}
+
+int persistent_max_blocks() {
+  int dev = 0, cus = 0, per = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_persistent_kernel<2>, kPT, 0) != hipSuccess) return 0;
+  return cus * (per > 0 ? 1 : 0);
+}
+
+}  // namespace kda

@@ -42,7 +42,7 @@ def gpu_model(run: synth.RunInputs):
 
 
 def gpu_decode(model, run: synth.RunInputs, steps: int, snapshot_every: int = 0,
-               graph: bool = True):
+               graph: bool = True, persistent: bool = True):
     """Decode `steps` tokens on the GPU from S0 / zero window.  Returns (y [steps][B][D],
     S, window, snapshots)."""
     import torch
@@ -52,6 +52,7 @@ def gpu_decode(model, run: synth.RunInputs, steps: int, snapshot_every: int = 0,
     st.S.copy_(torch.from_numpy(run.s0))
     ws = model.workspace(0, B)
     model.set_option(0, 1 if graph else 0)
+    model.set_option(2, 1 if persistent else 0)
     x_all = torch.from_numpy(np.ascontiguousarray(run.x[:steps, :, 0, :])).cuda()
     y = torch.empty((B, model.d_model), dtype=torch.float32, device="cuda")
     ys = torch.empty((steps, B, model.d_model), dtype=torch.float32, device="cuda")
@@ -63,4 +64,5 @@ def gpu_decode(model, run: synth.RunInputs, steps: int, snapshot_every: int = 0,
         if snapshot_every and (t + 1) % snapshot_every == 0:
             snaps[t + 1] = st.S.detach().cpu().numpy().copy()
     torch.cuda.synchronize()
+    model.status()
     return ys.cpu().numpy(), st.S.cpu().numpy(), st.conv.cpu().numpy(), snaps

@@ -81,11 +81,13 @@ def test_pack_bf16_bit_exact(torch, shape):
 # ----------------------------------------------------------------------------------------
 # decode parity
 # ----------------------------------------------------------------------------------------
-def _decode_parity(w, steps, snap_every=0, graph=True):
+def _decode_parity(w, steps, snap_every=0, graph=True, persistent=True, expect_persistent=None):
     run = synth.draw_run(w)
     layers = oracle_layers(run)
     model = gpu_model(run)
-    y, S, Z, snaps = gpu_decode(model, run, steps, snap_every, graph)
+    if expect_persistent is not None:
+        assert (model.persistent_blocks() > 0) == expect_persistent
+    y, S, Z, snaps = gpu_decode(model, run, steps, snap_every, graph, persistent)
     ry, rS, rZ, rsnaps = ok.decode_run(layers, run.x, run.s0, w.prenorm_residual, steps=steps,
                                        check_every=snap_every)
     errs = [range_rel(y[t], ry[t]) for t in range(steps)]
@@ -124,11 +126,20 @@ def test_decode_ragged_batch(torch, wtype):
     _decode_parity(w, w.steps, snap_every=3)
 
 
-def test_decode_stack_q8_0_full_size(torch):
+@pytest.mark.parametrize("persistent", [True, False], ids=["one-launch", "per-layer"])
+def test_decode_stack_q8_0_full_size(torch, persistent):
     w = synth.scaled(synth.WORKLOADS["stack"], steps=8)
-    _say("decode stack q8_0 34 layers D=2048 steps=8")
-    e, s = _decode_parity(w, w.steps)
+    _say(f"decode stack q8_0 34 layers D=2048 steps=8 persistent={persistent}")
+    e, s = _decode_parity(w, w.steps, persistent=persistent, expect_persistent=True)
     _say(f"  stack: out {e:.2e} state {s:.2e}")
+
+
+def test_decode_stack_one_launch_three_layers_32_steps(torch):
+    """The one-launch decode over 32 consecutive tokens (tags advance every token), with
+    the state checked every 8 steps."""
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=3, steps=32, seed=23)
+    _say("decode one-launch stack 3 layers 32 steps")
+    _decode_parity(w, w.steps, snap_every=8, expect_persistent=True)
 
 
 def test_graph_replay_equals_eager(torch):
