@@ -32,7 +32,7 @@ namespace kda {
 constexpr int kPT = 256;         // threads per block
 constexpr int kPRows = 8;        // max projection rows per wave
 constexpr int kORows = 4;        // max output-projection rows per wave
-constexpr int kGHItems = 8;      // gate chunks per thread in a head block
+constexpr int kHD = 128;         // d_k = d_v of the one-launch path
 
 using GLayer = const KDA_CONST PersistLayer;
 
@@ -99,35 +99,35 @@ __device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase
   return P.flags + (size_t)phase * kMaxPersistBlocks + i;
 }
 
-// One wave: wait until flags [0, n) of `phase` carry `tag` (n <= 4 * 64).  Every flag is
-// loaded at once; only the ones not yet set are polled again.
-__device__ bool wave_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag) {
+// One wave: wait until at least `need` of flags [0, n) of `phase` carry `tag` (n <= 4 * 64).
+// Every flag is loaded at once; only the ones not yet set are polled again.
+__device__ bool wave_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag, int need) {
   const int lane = threadIdx.x & 63;
   Spin sp;
   bool ok[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) ok[k] = lane + 64 * k >= n;
+  for (int k = 0; k < 4; ++k) ok[k] = false;
   while (true) {
     uint64_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      if (!ok[k]) w[k] = peek(flag_slot(P, phase, lane + 64 * k));
-    bool all = true;
+      if (!ok[k] && lane + 64 * k < n) w[k] = peek(flag_slot(P, phase, lane + 64 * k));
+    int cnt = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (!ok[k]) ok[k] = (uint32_t)(w[k] >> 32) == tag;
-      all &= ok[k];
+      if (!ok[k] && lane + 64 * k < n) ok[k] = (uint32_t)(w[k] >> 32) == tag;
+      cnt += __popcll(__ballot(ok[k]));
     }
-    if (__ballot(!all) == 0) return true;
+    if (cnt >= need) return true;
     if (sp.stop(P)) return false;
     __builtin_amdgcn_s_sleep(1);
   }
 }
 
 // Whole block: wave 0 watches the producer flags, the other waves wait at the barrier.
-__device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag) {
+__device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag, int need) {
   int bad = 0;
-  if (threadIdx.x < 64) bad = !wave_wait_flags(P, phase, n, tag);
+  if (threadIdx.x < 64) bad = !wave_wait_flags(P, phase, n, tag, need);
   return __syncthreads_or(bad) == 0;
 }
 
@@ -298,41 +298,39 @@ __device__ __forceinline__ void issue_out(const PersistParams& P, GLayer& L, int
 }
 
 // A head block's registers: wave w's state tile (rows 16 (lane & 7) .. + 16, value columns
-// 32 w + 4 (lane >> 3) .. + 4) and the block's gate-weight chunks (item i of thread t is
-// chunk (i * kPT + t) of the [alpha rows | gate rows] x rank slice).
+// 32 w + 4 (lane >> 3) .. + 4) and the block's gate-weight chunks: item i of thread t is
+// chunk (i * kPT + t) of the [alpha rows | gate rows] x rank slice, so with d_k + d_v = kPT
+// rows a thread has CPR items, the first CPR / 2 on alpha rows and the rest on gate rows.
+template <int CPR>   // 16-byte chunks per low-rank row: CPR = rank / 16
 struct HeadRegs {
   float4 st[16];
-  uint4 gw[kGHItems];
-  uint32_t gd[kGHItems];
-  float dtb[kGHItems];
+  uint4 gw[CPR];
+  uint32_t gd[CPR];
+  float dtb[CPR];
   float4 onw;
   float ea;                // exp(A_log[h])
 };
 
+template <int CPR>
 __device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, const float* Sl,
-                                           int h, HeadRegs& R) {
+                                           int h, HeadRegs<CPR>& R) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int dk = P.dk, dv = P.dv, rank = P.rank, cpr = rank / 16;
+  constexpr int rank = CPR * 16;
   const int j = wave * 32 + (lane >> 3) * 4, r0 = (lane & 7) * 16;
-  const float* Sb = Sl + (size_t)h * dk * dv + j;
+  const float* Sb = Sl + (size_t)h * kHD * kHD + j;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * dv);
-  const int nitems = (dk + dv) * cpr;
+  for (int i = 0; i < 16; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * kHD);
+  const int c = tid % CPR;
 #pragma unroll
-  for (int i = 0; i < kGHItems; ++i) {
-    const int it = i * kPT + tid;
-    const int row = it / cpr, c = it - row * cpr;
-    R.gw[i] = make_uint4(0, 0, 0, 0);
-    R.gd[i] = 0;
-    R.dtb[i] = 0.0f;
-    if (it < nitems) {
-      const bool f = row < dk;
-      const PackedMat M = f ? PackedMat{L.fb.w, L.fb.d} : PackedMat{L.gb.w, L.gb.d};
-      const int r = f ? h * dk + row : h * dv + row - dk;
-      R.gw[i] = wload(M.w + (size_t)r * rank + (size_t)c * 16);
-      R.gd[i] = sload(M.d + (size_t)r * (rank / 32) + (c >> 1));
-      if (f) R.dtb[i] = *gp(L.dt_bias + r);
-    }
+  for (int i = 0; i < CPR; ++i) {
+    const int row = (i * kPT + tid) / CPR;          // [0, kHD): alpha, [kHD, 2 kHD): gate
+    const bool f = i < CPR / 2;
+    const uint8_t* mw = f ? L.fb.w : L.gb.w;
+    const __half* md = f ? L.fb.d : L.gb.d;
+    const int r = f ? h * kHD + row : h * kHD + row - kHD;
+    R.gw[i] = wload(mw + (size_t)r * rank + (size_t)c * 16);
+    R.gd[i] = sload(md + (size_t)r * (rank / 32) + (c >> 1));
+    R.dtb[i] = f ? *gp(L.dt_bias + r) : 0.0f;
   }
   R.onw = make_float4(1.f, 1.f, 1.f, 1.f);
   if (L.o_norm_w) R.onw = gload4(L.o_norm_w + j);
@@ -396,8 +394,9 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
     }
     __syncthreads();
   } else {
-    // x_l: all O blocks of layer l - 1
-    if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u)) return false;
+    // x_l: once the first O block of layer l - 1 has posted (they finish together), poll
+    // the tagged words of x themselves
+    if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, 1)) return false;
     if (!fetch_vec<4 * U>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, sm.xs, sm.xsum, ss, P)) return false;
   }
   ss = wave_sum(ss);
@@ -433,18 +432,19 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
 }
 
 // H phase of layer l for head h (block h): gates, delta rule, the head's gated RMSNorm.
+template <int CPR>
 __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l, uint32_t tag,
-                                        HeadRegs& hr) {
+                                        HeadRegs<CPR>& hr) {
   GLayer* Lt = (GLayer*)P.layers;
   GLayer& L = Lt[l];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
-  const int H = P.H, dk = P.dk, dv = P.dv, C = P.C, K = H * dk;
-  const int rank = P.rank, cpr = rank / 16;
+  constexpr int dk = kHD, dv = kHD, rank = CPR * 16;
+  const int H = P.H, C = P.C, K = H * dk;
   float* Sl = P.S + (size_t)l * H * dk * dv;
-  // every projection block: the head's inputs come from many of them, and waiting for all
-  // of them also orders this layer's reads of pbuf before the next layer's writes
-  if (!block_wait_flags(P, kFlagP, gridDim.x - H, tag)) return false;
+  // the head's inputs are polled word by word (only the head blocks read them); the first
+  // projection block's flag starts the polling
+  if (!block_wait_flags(P, kFlagP, gridDim.x - H, tag, 1)) return false;
   // inputs: q [dk] | k [dk] | v [dv] | f_lr [rank] | g_lr [rank] | beta  (at most 4 per thread)
   const int n_in = 2 * dk + dv + 2 * rank + 1;
   {
@@ -480,12 +480,11 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const float* s_gl = s_fl + rank;
   const float beta = sigmoid_f(sm.s_in[2 * dk + dv + 2 * rank]);
   // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr).
-  // Item i of this thread is chunk c = tid % cpr of gate row (i * kPT + tid) / cpr (with
-  // d_k + d_v = kPT rows, a thread has exactly cpr items), so the thread needs one
-  // 16-element slice of f_lr and one of g_lr.  After the group sums, lane c of each group
-  // finishes item c: one transcendental per lane.
+  // Thread t's items all sit in chunk c = t % CPR of their rows, so it needs one 16-element
+  // slice of f_lr and one of g_lr.  After the group sums, lane c of each group finishes
+  // item c: one transcendental per lane.
   {
-    const int c = tid % cpr;
+    const int c = tid % CPR;
     float4 xf[4], xg[4];
     float sf = 0.0f, sg = 0.0f;
 #pragma unroll
@@ -497,16 +496,12 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     }
     float mine = 0.0f, bias = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kGHItems; ++i) {
-      if (i < cpr) {   // block-uniform
-        const bool f = (i * kPT + tid) / cpr < dk;
-        float part = h2f(hr.gd[i]) * (f ? q8_dot16(hr.gw[i], xf) - 128.0f * sf
-                                        : q8_dot16(hr.gw[i], xg) - 128.0f * sg);
-        part = group_sum(part, cpr);
-        if (c == i) { mine = part; bias = hr.dtb[i]; }
-      }
+    for (int i = 0; i < CPR; ++i) {
+      float part = i < CPR / 2 ? q8_dot16(hr.gw[i], xf) - 128.0f * sf : q8_dot16(hr.gw[i], xg) - 128.0f * sg;
+      part = group_sum(h2f(hr.gd[i]) * part, CPR);
+      if (c == i) { mine = part; bias = hr.dtb[i]; }
     }
-    const int grow = (c * kPT + tid) / cpr;
+    const int grow = (c * kPT + tid) / CPR;
     if (grow < dk) sm.s_al[grow] = expf(-expf(hr.ea) * softplus_f(mine + bias));
     else sm.s_gt[grow - dk] = sigmoid_f(mine);
   }
@@ -576,7 +571,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   float* Sb = Sl + (size_t)h * dk * dv + j;
 #pragma unroll
   for (int i = 0; i < 16; ++i) gstore4(Sb + (size_t)(r0 + i) * dv, hr.st[i]);
-  if (l + 1 < P.n_layers) issue_head(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, hr);
+  if (l + 1 < P.n_layers) issue_head<CPR>(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, hr);
   return true;
 }
 
@@ -587,7 +582,8 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
                                         uint32_t tag, OutRegs<U>& orr) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int D = P.D;
-  if (!block_wait_flags(P, kFlagH, P.H, tag)) return false;
+  // the normalised heads: after the first head block has posted, poll the words themselves
+  if (!block_wait_flags(P, kFlagH, P.H, tag, 1)) return false;
   float ssd;
   if (!fetch_vec<4 * U>(P.obuf, tag, sm.xs, sm.xsum, ssd, P)) return false;
   float accs[kORows];
@@ -611,17 +607,17 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
 // band.  Each role keeps only its own prefetch registers live.  Prefetches are issued right
 // after a phase that is followed by a long wait, never just before a poll on the critical
 // path (a poll's load completes only after the loads issued before it).
-template <int U, int ROLE>
+template <int U, int CPR, int ROLE>
 __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   GLayer* Lt = (GLayer*)P.layers;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const Roles R = make_roles(P, wave);
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
   if constexpr (ROLE == 1) {
-    HeadRegs hr;
-    issue_head(P, Lt[0], P.S, blockIdx.x, hr);
+    HeadRegs<CPR> hr;
+    issue_head<CPR>(P, Lt[0], P.S, blockIdx.x, hr);
     for (int l = 0; l < P.n_layers; ++l)
-      if (!phase_h(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
+      if (!phase_h<CPR>(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
   } else {
     ProjRegs<U> pr;
     issue_proj<U>(P, Lt[0], P.win, R.wr0, R.wr1, pr);
@@ -634,25 +630,34 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
         if (!phase_o<U>(P, sm, R, l, tag, orr)) return;
       }
     } else {
+      // a block left without projection rows has nothing to do: no phase waits for it, and
+      // it must not fall layers behind while it reads the residual stream
+      if (__syncthreads_or(R.wr1 > R.wr0) == 0) return;
       for (int l = 0; l < P.n_layers; ++l)
         if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr)) return;
     }
   }
 }
 
-template <int U>   // 16-byte chunks per lane per row: U = D / 1024
+// U = D / 1024 (16-byte chunks per lane per row), CPR = rank / 16
+template <int U, int CPR>
 __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const PersistParams P) {
   __shared__ Smem sm;
   const int b = blockIdx.x;
-  if (b < P.H) run_role<U, 1>(P, sm);
-  else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, 2>(P, sm);
-  else run_role<U, 0>(P, sm);
+  if (b < P.H) run_role<U, CPR, 1>(P, sm);
+  else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm);
+  else run_role<U, CPR, 0>(P, sm);
 }
 
 hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s) {
   void* args[] = {const_cast<PersistParams*>(&p)};
-  const void* fn = p.D == 2048 ? (const void*)decode_persistent_kernel<2>
-                               : (const void*)decode_persistent_kernel<1>;
+  const void* fn = nullptr;
+#define KDA_PERSIST_CASE(u, cpr) \
+  if (p.D == 1024 * (u) && p.rank == 16 * (cpr)) fn = (const void*)decode_persistent_kernel<u, cpr>;
+  KDA_PERSIST_CASE(1, 2) KDA_PERSIST_CASE(1, 4) KDA_PERSIST_CASE(1, 8)
+  KDA_PERSIST_CASE(2, 2) KDA_PERSIST_CASE(2, 4) KDA_PERSIST_CASE(2, 8)
+#undef KDA_PERSIST_CASE
+  if (!fn) return hipErrorInvalidValue;
   return hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
 }
 
@@ -660,7 +665,7 @@ int persistent_max_blocks() {
   int dev = 0, cus = 0, per = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_persistent_kernel<2>, kPT, 0) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_persistent_kernel<2, 8>, kPT, 0) != hipSuccess) return 0;
   return cus * (per > 0 ? 1 : 0);
 }
 
