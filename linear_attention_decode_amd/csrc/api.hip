@@ -325,24 +325,26 @@ int check_state(const kda_model* m, const kda_state* st) {
 
 // One-launch decode: eligible for batch 1, Q8_0 stacks with d_k = d_v = 128, H*d_v = D in
 // {1024, 2048}, low-rank gates of rank 32, 64 or 128, and enough co-resident blocks for the
-// static work split (one block per head, D/16 output-projection blocks after them, at most
-// 32 projection rows per block).
+// static work split (two blocks per head, D/16 output-projection blocks after them, at most
+// 32 projection rows per remaining block).
 size_t exchange_words(const kda_model* m) {
-  return 2 * (size_t)m->d.d_model + m->proj_rows + m->V + 3 * (size_t)kMaxPersistBlocks;
+  return 2 * (size_t)m->d.d_model + m->proj_rows + m->V + 8 * (size_t)m->d.n_heads +
+         3 * (size_t)kMaxPersistBlocks;
 }
 
 hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const kda_dims& d = m->d;
   const int nb = persistent_max_blocks();
-  const int ob0 = d.n_heads, nob = d.d_model / 16;
+  const int ob0 = 2 * d.n_heads, nob = d.d_model / 16;
   const int rank = d.rank_f;
   bool ok = nb > 0 && nb <= kMaxPersistBlocks && d.wtype == KDA_Q8_0 && d.prenorm_residual &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
             (rank == 32 || rank == 64 || rank == 128);
   if (ok) {
-    const int rp = (m->proj_rows + nb - 1) / nb;
-    ok = rp <= 32 && ob0 + nob <= nb && 2 * d.d_k + d.d_v + 2 * rank + 1 <= 1024;
+    const int np_blocks = nb - 2 * d.n_heads;      // blocks with projection rows
+    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks > 0 && np_blocks <= 256 &&
+         (m->proj_rows + np_blocks - 1) / np_blocks <= 32;
   }
   if (!ok) return hipSuccess;
   std::vector<PersistLayer> host(d.n_layers);
@@ -358,7 +360,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   e = hipMemcpy(m->d_layers, host.data(), sizeof(PersistLayer) * d.n_layers, hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
-  const size_t nx = 2 * (size_t)d.d_model, np = m->proj_rows, no = m->V;
+  const size_t nx = 2 * (size_t)d.d_model, np = m->proj_rows, no = m->V + 8 * (size_t)d.n_heads;
   e = hipMalloc(&m->xchg, exchange_words(m) * sizeof(uint64_t));
   if (e != hipSuccess) return e;
   e = hipMemset(m->xchg, 0, exchange_words(m) * sizeof(uint64_t));

@@ -6,10 +6,12 @@
 //   P  every block: RMSNorm(x) and its slice of the fused input projections
 //      [W_q; W_k; W_v; F_a; G_a; W_beta], with the causal conv + SiLU + window roll applied
 //      by the owner of each q/k/v channel;
-//   H  one block per head: the low-rank forget gate alpha and output gate (all four waves),
-//      then the gated delta rule (one wave per 32 value columns, state in registers) and the
-//      head's gated RMSNorm;
-//   O  a band of blocks: the output projection of the normalised heads plus the residual.
+//   H  two blocks per head, each owning half of its value columns: the low-rank forget gate
+//      alpha and its output-gate columns (all four waves), then the gated delta rule (one
+//      wave per 16 value columns, state in registers), posting the gated outputs and
+//      partial sums of o^2;
+//   O  a band of blocks: the heads' RMSNorm scales from those partials, the output
+//      projection of the normalised heads and the residual.
 // Every block streams a slice of every matrix, and it requests the next slice as soon as it
 // has used the current one, so the weights of layer l + 1 are in flight while layer l's
 // later phases run.  The weight loads go through global-address-space pointers (no flat
@@ -17,9 +19,12 @@
 //
 // Blocks hand activations to each other as 64-bit words (tag << 32 | fp32 bits) written
 // and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
-// the token and layer.  A consumer first watches one flag word per producer block (one
-// wave, a short sleep between polls, so polling stays far below the weight stream), then
-// fetches the data words, whose own tags it still checks.  Every wait is bounded: on a
+// the token and layer.  Each producer block also posts a flag word: the projection blocks
+// when they start a layer (their consumers, the few head blocks, then poll their input
+// words directly), the head and output blocks when they are done (their many consumers
+// watch the flags -- one wave, a short sleep between polls -- and fetch the data words once
+// the first producer has posted, so that polling stays far below the weight stream).  A
+// consumer always checks the tag of every data word it uses.  Every wait is bounded: on a
 // timeout the block records an error word and every block leaves the kernel.
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -33,6 +38,8 @@ constexpr int kPT = 256;         // threads per block
 constexpr int kPRows = 8;        // max projection rows per wave
 constexpr int kORows = 4;        // max output-projection rows per wave
 constexpr int kHD = 128;         // d_k = d_v of the one-launch path
+constexpr int kHSplit = 2;       // head blocks per head
+constexpr int kHCols = kHD / kHSplit;   // value columns of one head block (16 per wave)
 
 using GLayer = const KDA_CONST PersistLayer;
 
@@ -74,6 +81,12 @@ __device__ __forceinline__ uint64_t peek(const uint64_t* p) {
 __device__ __forceinline__ int err_set(const PersistParams& P) {
   return __hip_atomic_load(gpw(P.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every vector memory access issued so
+// far has completed.  Used before a store whose completion later waits must not include:
+// the wait counter retires in order, so a load issued before a store can otherwise only be
+// waited for together with that store.
+__device__ __forceinline__ void retire_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Poll bookkeeping: every 32 polls look at the error word and the wall clock; give up after
 // P.timeout wall-clock ticks (tens of milliseconds, against microseconds expected).
@@ -131,16 +144,26 @@ __device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint3
   return __syncthreads_or(bad) == 0;
 }
 
-// One tagged word; spins (bounded) until it carries `tag`.  Returns false on a failed wait.
-__device__ __forceinline__ bool fetch_word(const uint64_t* p, uint32_t tag, float& v, Spin& sp,
-                                           const PersistParams& P) {
-  uint64_t w = peek(p);
-  while ((uint32_t)(w >> 32) != tag) {
+// This thread's tagged words p[0], p[stride], ..., p[(n - 1) stride] (n <= N) into w[]:
+// every load is issued at once, then each round re-issues the loads of all words not yet
+// tagged, so a round costs one memory trip however many words are missing.  Returns false
+// on a failed wait.
+template <int N>
+__device__ bool poll_words(const uint64_t* p, int stride, uint32_t tag, uint64_t (&w)[N], int n,
+                           const PersistParams& P) {
+#pragma unroll
+  for (int k = 0; k < N; ++k) w[k] = k < n ? peek(p + (size_t)k * stride) : tagged(tag, 0.0f);
+  Spin sp;
+  while (true) {
+    bool all = true;
+#pragma unroll
+    for (int k = 0; k < N; ++k) all &= (uint32_t)(w[k] >> 32) == tag;
+    if (all) return true;
     if (sp.stop(P)) return false;
-    w = peek(p);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((uint32_t)(w[k] >> 32) != tag) w[k] = peek(p + (size_t)k * stride);
   }
-  v = __uint_as_float((uint32_t)w);
-  return true;
 }
 
 // Block-wide fetch of NPT * kPT tagged words into dst[] (LDS), with the sums of every 16
@@ -153,17 +176,10 @@ __device__ bool fetch_vec(const uint64_t* buf, uint32_t tag, float* dst, float* 
                           const PersistParams& P) {
   const int tid = threadIdx.x;
   uint64_t w[NPT];
-#pragma unroll
-  for (int k = 0; k < NPT; ++k) w[k] = peek(buf + tid + k * kPT);
-  int bad = 0;
-  Spin sp;
+  const int bad = !poll_words<NPT>(buf + tid, kPT, tag, w, NPT, P);
   ss = 0.0f;
 #pragma unroll
   for (int k = 0; k < NPT; ++k) {
-    while (!bad && (uint32_t)(w[k] >> 32) != tag) {
-      if (sp.stop(P)) bad = 1;
-      else w[k] = peek(buf + tid + k * kPT);
-    }
     const float v = __uint_as_float((uint32_t)w[k]);
     const int i = tid + k * kPT;
     dst[i] = v;
@@ -191,13 +207,14 @@ __device__ __forceinline__ float q8_dot16(const uint4 w, const float4 (&x)[4]) {
 // Wave-wide dots of up to NR rows (the first n, n wave-uniform) whose chunks this lane holds
 // (chunk u * 64 + lane of each row) with the LDS vector xs (chunk sums in xsum).  The lane's
 // 16-element slices of xs are read once, as aligned float4s, for all rows.
-template <int U, int NR>
+// With HSCALE, the 16-element chunk c of xs is scaled by hs[c / 8] (one head = 128 elements).
+template <int U, int NR, bool HSCALE = false>
 __device__ __forceinline__ void dot_rows(const uint4 (&w)[NR][U], const uint32_t (&d)[NR][U],
                                          int n, const float* xs, const float* xsum,
-                                         float (&acc)[NR]) {
+                                         const float* hs, float (&acc)[NR]) {
   const int lane = threadIdx.x & 63;
   float4 xv[U][4];
-  float xc[U];
+  float xc[U], cs[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int c = u * 64 + lane;
@@ -205,13 +222,17 @@ __device__ __forceinline__ void dot_rows(const uint4 (&w)[NR][U], const uint32_t
 #pragma unroll
     for (int k = 0; k < 4; ++k) xv[u][k] = p[k];
     xc[u] = xsum[c];
+    cs[u] = HSCALE ? hs[c >> 3] : 1.0f;
   }
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     float a = 0.0f;
     if (r < n) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) a += h2f(d[r][u]) * (q8_dot16(w[r][u], xv[u]) - 128.0f * xc[u]);
+      for (int u = 0; u < U; ++u) {
+        const float t = h2f(d[r][u]) * (q8_dot16(w[r][u], xv[u]) - 128.0f * xc[u]);
+        a += HSCALE ? t * cs[u] : t;
+      }
       a = wave_sum(a);
     }
     acc[r] = a;
@@ -297,44 +318,52 @@ __device__ __forceinline__ void issue_out(const PersistParams& P, GLayer& L, int
   }
 }
 
-// A head block's registers: wave w's state tile (rows 16 (lane & 7) .. + 16, value columns
-// 32 w + 4 (lane >> 3) .. + 4) and the block's gate-weight chunks: item i of thread t is
-// chunk (i * kPT + t) of the [alpha rows | gate rows] x rank slice, so with d_k + d_v = kPT
-// rows a thread has CPR items, the first CPR / 2 on alpha rows and the rest on gate rows.
+// A head block owns value columns [half * kHCols, + kHCols) of head h.  Its registers: wave
+// w's state tile (rows 8 (lane & 15) .. + 8, columns half * kHCols + 16 w + 4 (lane >> 4)
+// .. + 4) and the block's gate-weight chunks: item i of thread t is chunk (i * kPT + t) of
+// the [kHD alpha rows | kHCols gate rows] x rank slice (the first CPR / 2 items of every
+// thread are alpha rows).
 template <int CPR>   // 16-byte chunks per low-rank row: CPR = rank / 16
 struct HeadRegs {
-  float4 st[16];
-  uint4 gw[CPR];
-  uint32_t gd[CPR];
-  float dtb[CPR];
+  static constexpr int kItems = ((kHD + kHCols) * CPR + kPT - 1) / kPT;
+  float4 st[8];
+  uint4 gw[kItems];
+  uint32_t gd[kItems];
+  float dtb[kItems];
   float4 onw;
-  float ea;                // exp(A_log[h])
+  float ea;                // A_log[h], exponentiated when used
 };
 
 template <int CPR>
 __device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, const float* Sl,
-                                           int h, HeadRegs<CPR>& R) {
+                                           int h, int half, HeadRegs<CPR>& R) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int rank = CPR * 16;
-  const int j = wave * 32 + (lane >> 3) * 4, r0 = (lane & 7) * 16;
+  const int j = half * kHCols + wave * 16 + (lane >> 4) * 4, r0 = (lane & 15) * 8;
   const float* Sb = Sl + (size_t)h * kHD * kHD + j;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * kHD);
+  for (int i = 0; i < 8; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * kHD);
   const int c = tid % CPR;
 #pragma unroll
-  for (int i = 0; i < CPR; ++i) {
-    const int row = (i * kPT + tid) / CPR;          // [0, kHD): alpha, [kHD, 2 kHD): gate
+  for (int i = 0; i < HeadRegs<CPR>::kItems; ++i) {
+    const int it = i * kPT + tid;
+    const int row = it / CPR;                        // [0, kHD): alpha, then gate columns
     const bool f = i < CPR / 2;
-    const uint8_t* mw = f ? L.fb.w : L.gb.w;
-    const __half* md = f ? L.fb.d : L.gb.d;
-    const int r = f ? h * kHD + row : h * kHD + row - kHD;
-    R.gw[i] = wload(mw + (size_t)r * rank + (size_t)c * 16);
-    R.gd[i] = sload(md + (size_t)r * (rank / 32) + (c >> 1));
-    R.dtb[i] = f ? *gp(L.dt_bias + r) : 0.0f;
+    R.gw[i] = make_uint4(0, 0, 0, 0);
+    R.gd[i] = 0;
+    R.dtb[i] = 0.0f;
+    if (it < (kHD + kHCols) * CPR) {
+      const uint8_t* mw = f ? L.fb.w : L.gb.w;
+      const __half* md = f ? L.fb.d : L.gb.d;
+      const int r = f ? h * kHD + row : h * kHD + half * kHCols + (row - kHD);
+      R.gw[i] = wload(mw + (size_t)r * rank + (size_t)c * 16);
+      R.gd[i] = sload(md + (size_t)r * (rank / 32) + (c >> 1));
+      if (f) R.dtb[i] = *gp(L.dt_bias + r);
+    }
   }
   R.onw = make_float4(1.f, 1.f, 1.f, 1.f);
   if (L.o_norm_w) R.onw = gload4(L.o_norm_w + j);
-  R.ea = *gp(L.a_log + h);   // exponentiated when used
+  R.ea = *gp(L.a_log + h);
 }
 
 // LDS of one block.
@@ -344,9 +373,9 @@ struct Smem {
   float red[8];
   float xres[4 * kORows];  // this O block's residual rows
   alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
-  float s_al[256];         // head block: alpha rows
-  float s_gt[256];         // head block: output-gate columns
-  float s_ss[4];           // head block: per-wave partial o^2 sums
+  alignas(16) float s_al[kHD];     // head block: alpha rows
+  alignas(16) float s_gt[kHCols];  // head block: output-gate columns
+  float s_hs[64];                  // O blocks: per-head RMSNorm scales
 };
 
 // Static roles of block b: its projection rows, and whether it runs a head or an
@@ -358,8 +387,8 @@ struct Roles {
 
 __device__ __forceinline__ Roles make_roles(const PersistParams& P, int wave) {
   Roles R;
-  // projection rows go to blocks [H, nb): head blocks keep their loads for the state
-  const int b = blockIdx.x - P.H, nb = gridDim.x - P.H;
+  // projection rows go to blocks [kHSplit H, nb): head blocks keep their loads for the state
+  const int b = blockIdx.x - kHSplit * P.H, nb = gridDim.x - kHSplit * P.H;
   const int rp = (P.proj_rows + nb - 1) / nb;
   const int p0 = min(P.proj_rows, max(b, 0) * rp), p1 = b < 0 ? p0 : min(P.proj_rows, p0 + rp);
   const int rpw = (rp + 3) / 4;
@@ -394,18 +423,24 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
     }
     __syncthreads();
   } else {
-    // x_l: once the first O block of layer l - 1 has posted (they finish together), poll
-    // the tagged words of x themselves
+    // x_l: once the first O block of layer l - 1 has posted (they finish together), fetch
+    // the tagged words of x
     if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, 1)) return false;
     if (!fetch_vec<4 * U>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, sm.xs, sm.xsum, ss, P)) return false;
   }
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
   if (OBLK && tid < 4 * R.orw) sm.xres[tid] = sm.xs[R.or0 + tid];
+  // the flag says "this layer's projections are under way": the head blocks start polling
+  // their input words (flags are hints; every data word carries its own tag).  The
+  // prefetched weights have landed by now; retiring them first keeps the dots below from
+  // waiting for the flag store.
+  retire_vmem();
+  if (tid == 0) put(flag_slot(P, kFlagP, blockIdx.x - kHSplit * P.H), tag, 0.0f);
   __syncthreads();
   const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
   float accs[kPRows];
-  dot_rows<U, kPRows>(pr.w, pr.d, R.wr1 - R.wr0, sm.xs, sm.xsum, accs);
+  dot_rows<U, kPRows>(pr.w, pr.d, R.wr1 - R.wr0, sm.xs, sm.xsum, nullptr, accs);
   // lane r finishes row wr0 + r: conv + SiLU + window roll for q/k/v channels
   float v = 0.0f;
 #pragma unroll
@@ -418,8 +453,6 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
     if (row < C) v = silu_f(pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * v);
     put(P.pbuf + row, tag, v);
   }
-  __syncthreads();
-  if (tid == 0) put(flag_slot(P, kFlagP, blockIdx.x - P.H), tag, 0.0f);
   // off the critical path: roll the conv window, request the next layer's slice
   if (mine && row < C) {
     float* z = win + row;
@@ -431,44 +464,52 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   return true;
 }
 
-// H phase of layer l for head h (block h): gates, delta rule, the head's gated RMSNorm.
+// H phase of layer l for head block b = half * H + h: gates, delta rule on its value columns,
+// the gated outputs before the head's RMSNorm and per-wave partial sums of o^2 (the output
+// blocks finish the norm, since it spans both blocks of the head).
 template <int CPR>
 __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l, uint32_t tag,
                                         HeadRegs<CPR>& hr) {
   GLayer* Lt = (GLayer*)P.layers;
-  GLayer& L = Lt[l];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x;
   constexpr int dk = kHD, dv = kHD, rank = CPR * 16;
   const int H = P.H, C = P.C, K = H * dk;
+  const int h = blockIdx.x % H, half = blockIdx.x / H;
   float* Sl = P.S + (size_t)l * H * dk * dv;
-  // the head's inputs are polled word by word (only the head blocks read them); the first
-  // projection block's flag starts the polling
-  if (!block_wait_flags(P, kFlagP, gridDim.x - H, tag, 1)) return false;
-  // inputs: q [dk] | k [dk] | v [dv] | f_lr [rank] | g_lr [rank] | beta  (at most 4 per thread)
-  const int n_in = 2 * dk + dv + 2 * rank + 1;
+  // the head's inputs are polled word by word; the first projection block to start the
+  // layer starts the polling
+  if (!block_wait_flags(P, kFlagP, gridDim.x - kHSplit * H, tag, 1)) return false;
+  // inputs: q [dk] | k [dk] | v [kHCols] | f_lr [rank] | g_lr [rank] | beta  (<= 3 per thread)
+  constexpr int n_in = 2 * dk + kHCols + 2 * rank + 1;
+  static_assert(n_in <= 3 * kPT, "head inputs");
   {
-    uint64_t w[4];
-    int src[4];
+    uint64_t w[3];
+    int src[3];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 3; ++k) {
       const int i = tid + k * kPT;
       if (i < dk) src[k] = h * dk + i;
       else if (i < 2 * dk) src[k] = K + h * dk + (i - dk);
-      else if (i < 2 * dk + dv) src[k] = 2 * K + h * dv + (i - 2 * dk);
-      else if (i < 2 * dk + dv + 2 * rank) src[k] = C + (i - 2 * dk - dv);
+      else if (i < 2 * dk + kHCols) src[k] = 2 * K + h * dv + half * kHCols + (i - 2 * dk);
+      else if (i < 2 * dk + kHCols + 2 * rank) src[k] = C + (i - 2 * dk - kHCols);
       else src[k] = C + 2 * rank + h;
       w[k] = i < n_in ? peek(P.pbuf + src[k]) : tagged(tag, 0.0f);
     }
     int bad = 0;
     Spin sp;
+    while (true) {
+      bool all = true;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 3; ++k) all &= (uint32_t)(w[k] >> 32) == tag;
+      if (all) break;
+      if (sp.stop(P)) { bad = 1; break; }
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if ((uint32_t)(w[k] >> 32) != tag) w[k] = peek(P.pbuf + src[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
       const int i = tid + k * kPT;
-      while (!bad && (uint32_t)(w[k] >> 32) != tag) {
-        if (sp.stop(P)) bad = 1;
-        else w[k] = peek(P.pbuf + src[k]);
-      }
       if (i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
     if (__syncthreads_or(bad)) return false;
@@ -476,14 +517,15 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const float* s_q = sm.s_in;
   const float* s_k = sm.s_in + dk;
   const float* s_v = sm.s_in + 2 * dk;
-  const float* s_fl = sm.s_in + 2 * dk + dv;
+  const float* s_fl = sm.s_in + 2 * dk + kHCols;
   const float* s_gl = s_fl + rank;
-  const float beta = sigmoid_f(sm.s_in[2 * dk + dv + 2 * rank]);
+  const float beta = sigmoid_f(sm.s_in[2 * dk + kHCols + 2 * rank]);
   // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr).
   // Thread t's items all sit in chunk c = t % CPR of their rows, so it needs one 16-element
   // slice of f_lr and one of g_lr.  After the group sums, lane c of each group finishes
   // item c: one transcendental per lane.
   {
+    constexpr int NI = HeadRegs<CPR>::kItems;
     const int c = tid % CPR;
     float4 xf[4], xg[4];
     float sf = 0.0f, sg = 0.0f;
@@ -496,98 +538,116 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     }
     float mine = 0.0f, bias = 0.0f;
 #pragma unroll
-    for (int i = 0; i < CPR; ++i) {
+    for (int i = 0; i < NI; ++i) {
       float part = i < CPR / 2 ? q8_dot16(hr.gw[i], xf) - 128.0f * sf : q8_dot16(hr.gw[i], xg) - 128.0f * sg;
       part = group_sum(h2f(hr.gd[i]) * part, CPR);
       if (c == i) { mine = part; bias = hr.dtb[i]; }
     }
-    const int grow = (c * kPT + tid) / CPR;
-    if (grow < dk) sm.s_al[grow] = expf(-expf(hr.ea) * softplus_f(mine + bias));
-    else sm.s_gt[grow - dk] = sigmoid_f(mine);
+    const int it = c * kPT + tid, grow = it / CPR;
+    if (c < NI && it < (kHD + kHCols) * CPR) {
+      if (grow < dk) sm.s_al[grow] = expf(-expf(hr.ea) * softplus_f(mine + bias));
+      else sm.s_gt[grow - dk] = sigmoid_f(mine);
+    }
   }
   __syncthreads();
-  // delta rule: wave w owns value columns 32 w .. 32 w + 31
-  const int rg = lane & 7, cq = lane >> 3;
-  const int j = wave * 32 + cq * 4, r0 = rg * 16;
-  float4 qv[4], kv[4], av[4];
+  // delta rule: lane (rg, cq) holds rows 8 rg .. + 8 of columns jl .. + 4 (block-local jl)
+  const int rg = lane & 15, cq = lane >> 4;
+  const int jl = wave * 16 + cq * 4, j = half * kHCols + jl, r0 = rg * 8;
+  float4 qv[2], kv[2], av[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 2; ++k) {
     qv[k] = reinterpret_cast<const float4*>(s_q + r0)[k];
     kv[k] = reinterpret_cast<const float4*>(s_k + r0)[k];
     av[k] = reinterpret_cast<const float4*>(sm.s_al + r0)[k];
   }
-  const float4 vv = *reinterpret_cast<const float4*>(s_v + j);
-  const float4 gv = *reinterpret_cast<const float4*>(sm.s_gt + j);
+  const float4 vv = *reinterpret_cast<const float4*>(s_v + jl);
+  const float4 gv = *reinterpret_cast<const float4*>(sm.s_gt + jl);
   const float* qa = reinterpret_cast<const float*>(qv);
   const float* ka = reinterpret_cast<const float*>(kv);
   const float* aa = reinterpret_cast<const float*>(av);
   float aq = 0.0f, ak = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     aq += qa[i] * qa[i];
     ak += ka[i] * ka[i];
   }
-  const float inv_q = P.q_scale / sqrtf(sum8(aq) + P.l2_eps);
-  const float inv_k = 1.0f / sqrtf(sum8(ak) + P.l2_eps);
+  const float inv_q = P.q_scale / sqrtf(sum16(aq) + P.l2_eps);
+  const float inv_k = 1.0f / sqrtf(sum16(ak) + P.l2_eps);
   float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const float a = aa[i], kk = ka[i] * inv_k;
     float4& s = hr.st[i];
     s.x *= a; s.y *= a; s.z *= a; s.w *= a;
     e0 += s.x * kk; e1 += s.y * kk; e2 += s.z * kk; e3 += s.w * kk;
   }
-  e0 = sum8(e0); e1 = sum8(e1); e2 = sum8(e2); e3 = sum8(e3);
+  e0 = sum16(e0); e1 = sum16(e1); e2 = sum16(e2); e3 = sum16(e3);
   const float d0 = beta * (vv.x - e0), d1 = beta * (vv.y - e1);
   const float d2 = beta * (vv.z - e2), d3 = beta * (vv.w - e3);
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     const float kk = ka[i] * inv_k, qq = qa[i] * inv_q;
     float4& s = hr.st[i];
     s.x += kk * d0; s.y += kk * d1; s.z += kk * d2; s.w += kk * d3;
     o0 += s.x * qq; o1 += s.y * qq; o2 += s.z * qq; o3 += s.w * qq;
   }
-  o0 = sum8(o0); o1 = sum8(o1); o2 = sum8(o2); o3 = sum8(o3);
-  // the head's RMSNorm over its dv outputs: per-wave partial sums through LDS
-  float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;   // identical on the 8 lanes of a group
-  q2 += dpp_mov<kDppRor8>(q2);
-  const int qb = __float_as_int(q2);
-  const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
-                    (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
-  if (lane == 0) sm.s_ss[wave] = tot;
-  __syncthreads();
-  const float hs = 1.0f / sqrtf(((sm.s_ss[0] + sm.s_ss[1]) + (sm.s_ss[2] + sm.s_ss[3])) / (float)dv + P.eps);
+  o0 = sum16(o0); o1 = sum16(o1); o2 = sum16(o2); o3 = sum16(o3);
+  // gated outputs (the norm scale comes later) and this wave's partial sum of o^2
   if (rg == 0) {
     uint64_t* ob = P.obuf + h * dv + j;
-    put(ob + 0, tag, o0 * hs * hr.onw.x * gv.x);
-    put(ob + 1, tag, o1 * hs * hr.onw.y * gv.y);
-    put(ob + 2, tag, o2 * hs * hr.onw.z * gv.z);
-    put(ob + 3, tag, o3 * hs * hr.onw.w * gv.w);
+    put(ob + 0, tag, o0 * hr.onw.x * gv.x);
+    put(ob + 1, tag, o1 * hr.onw.y * gv.y);
+    put(ob + 2, tag, o2 * hr.onw.z * gv.z);
+    put(ob + 3, tag, o3 * hr.onw.w * gv.w);
   }
-  __syncthreads();
-  if (tid == 0) put(flag_slot(P, kFlagH, h), tag, 0.0f);
+  const int qb = __float_as_int(o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3);   // same on a row's lanes
+  const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
+                    (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
+  if (lane == 0) {
+    put(P.obuf + P.H * dv + (h * kHSplit + half) * 4 + wave, tag, tot);
+    if (wave == 0) put(flag_slot(P, kFlagH, blockIdx.x), tag, 0.0f);
+  }
   // off the critical path: write the state back, request the next layer's
   float* Sb = Sl + (size_t)h * dk * dv + j;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) gstore4(Sb + (size_t)(r0 + i) * dv, hr.st[i]);
-  if (l + 1 < P.n_layers) issue_head<CPR>(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, hr);
+  for (int i = 0; i < 8; ++i) gstore4(Sb + (size_t)(r0 + i) * dv, hr.st[i]);
+  if (l + 1 < P.n_layers) issue_head<CPR>(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, half, hr);
+  // (the next layer's first wait is a barrier, so LDS is not rewritten while still read)
   return true;
 }
 
 // O phase of layer l: this band's output-projection rows of the normalised heads, plus the
-// residual; the last layer also writes the output row.
+// residual; the last layer also writes the output row.  The heads' RMSNorm scales come from
+// the per-wave partial sums of o^2 that the head blocks post after their outputs.
 template <int U>
 __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const Roles& R, int l,
                                         uint32_t tag, OutRegs<U>& orr) {
   const int tid = threadIdx.x, lane = tid & 63;
-  const int D = P.D;
-  // the normalised heads: after the first head block has posted, poll the words themselves
-  if (!block_wait_flags(P, kFlagH, P.H, tag, 1)) return false;
-  float ssd;
-  if (!fetch_vec<4 * U>(P.obuf, tag, sm.xs, sm.xsum, ssd, P)) return false;
+  const int D = P.D, H = P.H, V = H * kHD;
+  constexpr int kParts = kHSplit * 4;                // o^2 partials per head
+  // once the first head block has posted, fetch the output words
+  if (!block_wait_flags(P, kFlagH, kHSplit * H, tag, 1)) return false;
+  {
+    const uint64_t* src = P.obuf + V + tid;
+    const bool has = tid < H * kParts;
+    uint64_t w = has ? peek(src) : tagged(tag, 0.0f);
+    float ssd;
+    bool ok = fetch_vec<4 * U>(P.obuf, tag, sm.xs, sm.xsum, ssd, P);   // ends with a barrier
+    int bad = !ok;
+    Spin sp;
+    while (!bad && (uint32_t)(w >> 32) != tag) {
+      if (sp.stop(P)) bad = 1;
+      else w = peek(src);
+    }
+    float v = __uint_as_float((uint32_t)w);
+    // the kParts partials of a head sit on consecutive lanes
+    v = group_sum(v, kParts);
+    if (has && tid % kParts == 0) sm.s_hs[tid / kParts] = 1.0f / sqrtf(v / (float)kHD + P.eps);
+    if (__syncthreads_or(bad)) return false;
+  }
   float accs[kORows];
-  dot_rows<U, kORows>(orr.w, orr.d, R.orw, sm.xs, sm.xsum, accs);
+  dot_rows<U, kORows, true>(orr.w, orr.d, R.orw, sm.xs, sm.xsum, sm.s_hs, accs);
   float v = 0.0f;
 #pragma unroll
   for (int r = 0; r < kORows; ++r)
@@ -615,7 +675,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
   if constexpr (ROLE == 1) {
     HeadRegs<CPR> hr;
-    issue_head<CPR>(P, Lt[0], P.S, blockIdx.x, hr);
+    issue_head<CPR>(P, Lt[0], P.S, blockIdx.x % P.H, blockIdx.x / P.H, hr);
     for (int l = 0; l < P.n_layers; ++l)
       if (!phase_h<CPR>(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
   } else {
@@ -644,7 +704,7 @@ template <int U, int CPR>
 __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const PersistParams P) {
   __shared__ Smem sm;
   const int b = blockIdx.x;
-  if (b < P.H) run_role<U, CPR, 1>(P, sm);
+  if (b < kHSplit * P.H) run_role<U, CPR, 1>(P, sm);
   else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm);
   else run_role<U, CPR, 0>(P, sm);
 }
