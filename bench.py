@@ -27,6 +27,23 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
+# scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
+# the kernel's sources hash to "sha256" (see profiles/ for the runs).
+STEP_TRAFFIC = {"bytes": 752336069,
+                "sha256": "f94807fba429a79eb8409f444c0f514801c66085bd7461f6071c1d5a320bbf7d",
+                "sources": ("persistent.hip", "kda_device.h", "kda_internal.h")}
+
+
+def step_traffic():
+    """The counted traffic of the one-launch step, or None once its sources changed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in STEP_TRAFFIC["sources"]:
+        with open(os.path.join(ROOT, "linear_attention_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return STEP_TRAFFIC["bytes"] if h.hexdigest() == STEP_TRAFFIC["sha256"] else None
+
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -74,8 +91,8 @@ def cpu_baseline(run, budget_s: float = 15.0):
     t0 = time.time()
     S = [[run.s0[l, 0].astype(np.float64)] for l in range(w.n_layers)]
     Z = [[np.zeros((3, d.conv_channels))] for _ in range(w.n_layers)]
-    while n < w.steps:
-        xt = run.x[n, 0, 0].astype(np.float64)[None, :]
+    while True:
+        xt = run.x[n % w.steps, 0, 0].astype(np.float64)[None, :]   # inputs reused cyclically
         _, s_new, z_new = ok.stack_step(layers, xt, [S[l][0] for l in range(w.n_layers)],
                                         [Z[l][0] for l in range(w.n_layers)])
         for l in range(w.n_layers):
@@ -85,7 +102,7 @@ def cpu_baseline(run, budget_s: float = 15.0):
             break
     el = time.time() - t0
     return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} decode tokens of the 34-layer Q8_0 stack, B=1, float64 "
+            "sample": f"{n} consecutive decode tokens of the 34-layer Q8_0 stack, B=1, float64 "
                       f"numpy oracle ({el:.1f}s, BLAS threads={threads}, host nproc={os.cpu_count()})"}
 
 
@@ -98,6 +115,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--per-layer", action="store_true",
                     help="time the per-layer hipGraph path instead of the one-launch step")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -105,6 +125,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration} MiB 5 times")
+        return
     import synth
     import linear_attention_decode_amd as kda
 
@@ -200,7 +229,7 @@ def main():
                                    for kk, vv in v.items()} for k, v in per.items()}},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": step_traffic() if dom == "step" else None},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
