@@ -1,16 +1,22 @@
 #!/usr/bin/env python3
 """KDA decode benchmark on one MI355X.
 
-Workload: the 34-layer KDA stack (D=2048, 16 heads, d_k=d_v=128, all projections Q8_0,
-fp32 state [16][128][128] + 3-token conv window per layer, pre-RMSNorm residual stream),
-batch 1, synthetic seeded weights and inputs.  A step is one token through all 34 layers:
-the fused projection GEMV, the low-rank gate kernel, the per-head delta-rule kernel and
-the gated-norm + output projection GEMV per layer, replayed as one hipGraph.
+Default workload (the headline metric): the 34-layer KDA stack (D=2048, 16 heads,
+d_k=d_v=128, all projections Q8_0, fp32 state [16][128][128] + 3-token conv window per
+layer, pre-RMSNorm residual stream), batch 1, synthetic seeded weights and inputs.  A step
+is one token through all 34 layers: one cooperative launch of the one-launch decode kernel
+(or, with --per-layer, the per-layer kernels replayed as one hipGraph).
 
 Prints ONE JSON line: tokens/s over K timed steps, HBM roofline of the dominant kernel
 (timed with hipEvents on the launch stream), and the CPU oracle on a bounded sample.
 
+Other workloads (--workload, one JSON line each, for the secondary measurements):
+  layer    one BF16 layer, B=1 decode (effective GB/s; the 38 MB set fits the MALL)
+  verify   the stack, B=8 sequences x T=4 tokens a step + commit of the accepted prefix
+  prefill  one BF16 layer, B=4 x L=8192 chunked prefill (MFMA-bound)
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--workload stack|layer|verify|prefill] [--per-layer]
 """
 from __future__ import annotations
 
@@ -26,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
@@ -56,8 +63,10 @@ def algorithmic_bytes(w) -> dict:
     D, K, V, H = d.d_model, d.key_dim, d.value_dim, d.n_heads
     C = d.conv_channels
 
-    def q8(rows, cols):
-        return rows * cols + rows * (cols // 32) * 2
+    def q8(rows, cols):   # packed bytes of one matrix in the workload's weight format
+        if w.wtype == "q8_0":
+            return rows * cols + rows * (cols // 32) * 2
+        return rows * cols * (2 if w.wtype == "bf16" else 4)
 
     proj_w = q8(K, D) * 2 + q8(V, D) + q8(d.rank_f, D) + q8(d.rank_g, D) + q8(H, D)
     proj = proj_w + D * 4 + C * 3 * 4 * 2 + C * 4 * 4 + (C + d.rank_f + d.rank_g + H) * 4
@@ -102,8 +111,289 @@ def cpu_baseline(run, budget_s: float = 15.0):
             break
     el = time.time() - t0
     return {"value": n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} consecutive decode tokens of the 34-layer Q8_0 stack, B=1, float64 "
-                      f"numpy oracle ({el:.1f}s, BLAS threads={threads}, host nproc={os.cpu_count()})"}
+            "sample": f"{n} consecutive decode tokens of the {w.n_layers}-layer {w.wtype} "
+                      f"workload '{w.name}', B=1, float64 numpy oracle ({el:.1f}s, BLAS "
+                      f"threads={threads}, host nproc={os.cpu_count()})"}
+
+
+def timed_kinds(model, kda, kinds):
+    """Per-kind (avg us, launches) of the event-timed launches since the last reset."""
+    out = {}
+    for k, v in kinds.items():
+        ms, n = model.timing(v)
+        if n:
+            out[k] = (ms * 1e3 / n, n)
+    return out
+
+
+def roofline_entry(per, bound, peak, unit):
+    dom = max(per, key=lambda k: per[k]["avg_us"] * per[k]["launches"])
+    ach = per[dom]["rate"]
+    return dom, {"bound": bound, "kernel": dom, "achieved": round(ach, 1), "peak": peak,
+                 "unit": unit, "frac": round(ach / peak, 4)}
+
+
+def bench_stack(args, torch, synth, kda, w, run, model):
+    d = w.dims
+    B = w.batch
+    st = model.new_state(B)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(kda.KDA_OP_DECODE, B)
+    xs = torch.from_numpy(np.ascontiguousarray(run.x[:, :, 0, :])).cuda()   # [steps][B][D]
+    y = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
+
+    model.set_option(kda.KDA_OPT_GRAPH, 1)
+    model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
+    one_launch = not args.per_layer and model.persistent_blocks() > 0 and B == 1
+    path = (f"one cooperative launch per token ({model.persistent_blocks()} blocks)" if one_launch
+            else "per-layer kernels replayed as one hipGraph")
+    log(f"[bench] path: {path}")
+    for i in range(args.warmup):
+        model.decode_step(xs[i], y, st, ws)
+    torch.cuda.synchronize()
+    # ---- timed region: K steps, inputs resident in HBM ----
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        model.decode_step(xs[args.warmup + i], y, st, ws)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    model.status()
+    tok_s = B * args.steps / el
+    ms_step = el * 1e3 / args.steps
+    log(f"[bench] {args.steps} steps in {el * 1e3:.2f} ms: {tok_s:.1f} tokens/s")
+
+    # ---- per-kernel durations with hipEvents on the launch stream (no graph) ----
+    model.set_option(kda.KDA_OPT_TIMING, 1)
+    model.timing(kda.KDA_K_PROJ, reset=True)
+    for i in range(args.steps):
+        model.decode_step(xs[args.warmup + i], y, st, ws)
+    torch.cuda.synchronize()
+    model.status()
+    times = timed_kinds(model, kda, {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES,
+                                     "head": kda.KDA_K_HEAD, "out": kda.KDA_K_OUT,
+                                     "step": kda.KDA_K_STEP})
+    model.set_option(kda.KDA_OPT_TIMING, 0)
+    ab = algorithmic_bytes(w)
+    per = {}
+    for k, (avg_us, n) in times.items():
+        per[k] = {"avg_us": avg_us, "launches": n, "bytes": ab[k],
+                  "rate": ab[k] / (avg_us * 1e-6) / 1e9}
+        log(f"[bench] kernel {k}: {n} launches, avg {avg_us:.2f} us, "
+            f"{per[k]['rate']:.0f} GB/s algorithmic")
+    dom, roof = roofline_entry(per, "hbm", HBM_PEAK_GBS, "GB/s")
+    roof["traffic"] = step_traffic() if dom == "step" else None
+    step_gbs = ab["token_weights_state"] / (ms_step * 1e-3) / 1e9
+    config = {"workload": f"kda-{w.n_layers}L-{w.wtype}-decode" if w.n_layers > 1
+              else f"kda-layer-{w.wtype}-decode",
+              "layers": w.n_layers, "d_model": d.d_model, "heads": d.n_heads, "d_k": d.d_k,
+              "d_v": d.d_v, "weights": w.wtype, "state": "f32", "batch": B, "global_batch": B,
+              "seq_len": 1, "parallelism": "none (1 GPU)", "path": path,
+              "bytes_per_token": ab["token_weights_state"],
+              "step_hbm_gbs": round(step_gbs, 1),
+              "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+              "kernels": rounded(per)}
+    if w.name == "stack":
+        config["workload"] = "kda-stack-34L-q8_0-decode"
+    metric = ("KDA decode tokens/s (34-layer stack, B=1)" if w.name == "stack"
+              else "KDA decode tokens/s (one BF16 layer, B=1)")
+    return metric, tok_s, "tokens/s", ms_step, config, roof
+
+
+def verify_bytes(w):
+    """Algorithmic bytes per verify step (B sequences x T tokens): every layer's weights once
+    and each sequence's state read once (verify) plus read + written once (commit)."""
+    d = w.dims
+    D, K, V, H = d.d_model, d.key_dim, d.value_dim, d.n_heads
+    C = d.conv_channels
+    N = w.batch * w.tokens
+
+    def q8(rows, cols):
+        return rows * cols + rows * (cols // 32) * 2
+
+    rows = C + d.rank_f + d.rank_g + H
+    proj_w = q8(K, D) * 2 + q8(V, D) + q8(d.rank_f, D) + q8(d.rank_g, D) + q8(H, D)
+    state = H * d.d_k * d.d_v * 4
+    per = {"proj": proj_w + N * (D + rows) * 4,
+           "gates": q8(K, d.rank_f) + q8(V, d.rank_g) + N * (d.rank_f + d.rank_g + K + V) * 4,
+           "head": w.batch * state + N * (rows + K + V + 2 * V) * 4,
+           "out": q8(D, V) + N * (2 * V + 2 * D) * 4,
+           "commit": w.batch * 2 * state}
+    floor = w.n_layers * (proj_w + q8(K, d.rank_f) + q8(V, d.rank_g) + q8(D, V)
+                          + w.batch * 2 * 2 * state // 2)
+    return per, floor
+
+
+def bench_verify(args, torch, synth, kda, w, run, model):
+    d = w.dims
+    B, T = w.batch, w.tokens
+    st = model.new_state(B)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(kda.KDA_OP_VERIFY, B, T)
+    vlog = model.verify_log(B, T)
+    xs = torch.from_numpy(np.ascontiguousarray(run.x)).cuda()             # [steps][B][T][D]
+    ys = torch.empty((B, T, d.d_model), dtype=torch.float32, device="cuda")
+    acc = torch.from_numpy(np.ascontiguousarray(run.accept).astype(np.int32)).cuda()
+    model.set_option(kda.KDA_OPT_GRAPH, 1)
+
+    def step(i):
+        model.verify_steps(xs[i], T, ys, st, vlog, ws)
+        model.verify_commit(st, vlog, T, acc[i])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    accepted = int(run.accept[args.warmup:args.warmup + args.steps].clip(1, T).sum())
+    pos_s = B * T * args.steps / el
+    log(f"[bench] verify {args.steps} steps in {el * 1e3:.2f} ms: {pos_s:.0f} positions/s, "
+        f"{accepted / el:.0f} accepted tokens/s")
+    model.set_option(kda.KDA_OPT_TIMING, 1)
+    model.timing(kda.KDA_K_PROJ, reset=True)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    times = timed_kinds(model, kda, {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES,
+                                     "head": kda.KDA_K_HEAD, "out": kda.KDA_K_OUT,
+                                     "commit": kda.KDA_K_COMMIT})
+    model.set_option(kda.KDA_OPT_TIMING, 0)
+    bper, floor = verify_bytes(w)
+    per = {}
+    for k, (avg_us, n) in times.items():
+        per[k] = {"avg_us": avg_us, "launches": n, "bytes": bper[k],
+                  "rate": bper[k] / (avg_us * 1e-6) / 1e9}
+        log(f"[bench] kernel {k}: {n} launches, avg {avg_us:.2f} us, "
+            f"{per[k]['rate']:.0f} GB/s algorithmic")
+    dom, roof = roofline_entry(per, "hbm", HBM_PEAK_GBS, "GB/s")
+    roof["traffic"] = None
+    ms_step = el * 1e3 / args.steps
+    gbs = floor / (ms_step * 1e-3) / 1e9
+    config = {"workload": "kda-stack-34L-q8_0-verify-B8-T4", "layers": w.n_layers,
+              "d_model": d.d_model, "heads": d.n_heads, "batch": B, "tokens_per_step": T,
+              "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
+              "accepted_tokens_per_s": round(accepted / el, 1),
+              "bytes_floor_per_step": floor, "step_hbm_gbs": round(gbs, 1),
+              "step_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "kernels": rounded(per)}
+    return ("KDA verify positions/s (34-layer stack, B=8, T=4)", pos_s, "positions/s", ms_step,
+            config, roof)
+
+
+def prefill_flops(w):
+    """Algorithmic MFMA flops of one chunked prefill call per kernel kind."""
+    d = w.dims
+    M = w.batch * w.tokens
+    rows = d.conv_channels + d.rank_f + d.rank_g + d.n_heads
+    gemm = 2 * M * (rows * d.d_model + d.key_dim * d.rank_f + d.value_dim * d.rank_g
+                    + d.d_model * d.value_dim)
+    # chunk math per (seq, head, chunk of c): L, A (2 c^2 dk), W, U (c^2 (dk + dv)),
+    # D = U - W S (c dk dv), O = Q S + A D (c dk dv + c^2 dv), S += K^T D (c dk dv)
+    c = w.chunk
+    per_chunk = 2 * (2 * c * c * d.d_k + c * c * (d.d_k + d.d_v) + 3 * c * d.d_k * d.d_v
+                     + c * c * d.d_v)
+    chunk = w.batch * d.n_heads * (w.tokens // c) * per_chunk
+    return {"gemm": gemm, "chunk": chunk}
+
+
+def bench_prefill(args, torch, synth, kda, w, run, model):
+    d = w.dims
+    B, L = w.batch, w.tokens
+    x = torch.from_numpy(np.ascontiguousarray(run.x_bits[0]).view(np.int16)).cuda()
+    y = torch.empty((B, L, d.d_model), dtype=torch.float32, device="cuda")
+    ws = model.workspace(kda.KDA_OP_PREFILL, B, L)
+    sts = [model.new_state(B) for _ in range(2)]
+
+    def call(i):
+        st = sts[i % 2]
+        st.S.zero_()
+        st.conv.zero_()
+        model.prefill_chunked(x, kda.KDA_BF16, L, w.chunk, y, st, ws)
+
+    steps, warm = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+    for i in range(warm):
+        call(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tok_s = B * L * steps / el
+    log(f"[bench] prefill {steps} calls in {el * 1e3:.2f} ms: {tok_s:.0f} tokens/s")
+    model.set_option(kda.KDA_OPT_TIMING, 1)
+    model.timing(kda.KDA_K_PROJ, reset=True)
+    for i in range(steps):
+        call(i)
+    torch.cuda.synchronize()
+    times = timed_kinds(model, kda, {"gemm": kda.KDA_K_GEMM, "chunk": kda.KDA_K_CHUNK,
+                                     "seq": kda.KDA_K_PREFILL})
+    model.set_option(kda.KDA_OPT_TIMING, 0)
+    fl = prefill_flops(w)
+    per = {}
+    for k, (avg_us, n) in times.items():
+        total = avg_us * n / steps                       # per call
+        flops = fl.get(k, 0)
+        per[k] = {"avg_us": avg_us, "launches": n, "us_per_call": total,
+                  "flops_per_call": flops,
+                  "rate": flops / (total * 1e-6) / 1e12 if flops else 0.0}
+        log(f"[bench] kernel {k}: {n} launches, {total:.1f} us per call"
+            + (f", {per[k]['rate']:.1f} TFLOP/s" if flops else ""))
+    dom = max(per, key=lambda k: per[k]["us_per_call"])
+    ach = per[dom]["rate"]
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    ms_call = el * 1e3 / steps
+    total_fl = fl["gemm"] + fl["chunk"]
+    config = {"workload": "kda-layer-bf16-prefill-B4-L8192-chunk64", "layers": 1,
+              "d_model": d.d_model, "heads": d.n_heads, "batch": B, "global_batch": B,
+              "seq_len": L, "chunk": w.chunk, "parallelism": "none (1 GPU)",
+              "flops_per_call": total_fl,
+              "call_tflops": round(total_fl / (ms_call * 1e-3) / 1e12, 2),
+              "kernels": rounded(per)}
+    return ("KDA chunked prefill tokens/s (one BF16 layer, B=4, L=8192)", tok_s, "tokens/s",
+            ms_call, config, roof)
+
+
+def rounded(per):
+    return {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+            for k, v in per.items()}
+
+
+def cpu_baseline_for(name, run, budget_s):
+    if name in ("stack", "layer"):
+        return cpu_baseline(run, budget_s)
+    from oracle import kda as ok
+    w = run.workload
+    d = w.dims
+    layers = [ok.prepare_layer(dr, w.wtype, d.n_heads, d.d_k, d.d_v, w.norm_eps, w.l2_eps)
+              for dr in run.layers]
+    import threadpoolctl
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    t0 = time.time()
+    n = 0
+    if name == "verify":
+        S = [np.array(run.s0[l, 0], np.float64) for l in range(w.n_layers)]
+        Z = [np.zeros((3, d.conv_channels)) for _ in range(w.n_layers)]
+        k = 0
+        while time.time() - t0 < budget_s:
+            i = k % w.steps
+            _, S, Z = ok.stack_step(layers, run.x[i, 0].astype(np.float64), S, Z,
+                                    keep_after=int(np.clip(run.accept[i, 0], 1, w.tokens)))
+            k += 1
+            n += w.tokens
+        el = time.time() - t0
+        return {"value": n / el, "unit": "positions/s", "cores": threads, "kind": "oracle",
+                "sample": f"{n // w.tokens} verify steps of one sequence (T={w.tokens}) through "
+                          f"the 34-layer stack, float64 oracle ({el:.1f}s)"}
+    # prefill: the sequential oracle over one whole sequence
+    L = w.tokens
+    ok.prefill_run(layers[0], run.x[0][:1, :L], run.s0[0][:1], seqs=[0])
+    el = time.time() - t0
+    return {"value": L / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one sequence of {L} tokens, token-by-token float64 oracle ({el:.1f}s)"}
 
 
 def main():
@@ -113,8 +403,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--workload", default="stack", choices=("stack", "layer", "verify", "prefill"))
     ap.add_argument("--per-layer", action="store_true",
-                    help="time the per-layer hipGraph path instead of the one-launch step")
+                    help="time the per-layer hipGraph decode instead of the one-launch step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -137,77 +428,32 @@ def main():
     import synth
     import linear_attention_decode_amd as kda
 
-    w = synth.WORKLOADS["stack"]
-    steps_needed = max(args.steps + args.warmup, 1)
-    w_run = synth.scaled(w, steps=steps_needed)
+    w = synth.WORKLOADS[args.workload]
+    if args.workload != "prefill":
+        w = synth.scaled(w, steps=max(args.steps + args.warmup, 1))
     t0 = time.time()
-    run = synth.draw_run(w_run)
+    run = synth.draw_run(w)
     log(f"[bench] drew {w.n_layers}-layer weights + inputs in {time.time() - t0:.1f}s")
     d = w.dims
     t0 = time.time()
     model = kda.KdaModel(run.layers, n_heads=d.n_heads, d_k=d.d_k, d_v=d.d_v, wtype=w.wtype,
-                         prenorm_residual=True, norm_eps=w.norm_eps, l2_eps=w.l2_eps)
-    log(f"[bench] packed Q8_0 weights on the device in {time.time() - t0:.1f}s")
-    B = 1
-    st = model.new_state(B)
-    st.S.copy_(torch.from_numpy(run.s0))
-    ws = model.workspace(kda.KDA_OP_DECODE, B)
-    xs = torch.from_numpy(np.ascontiguousarray(run.x[:, :, 0, :])).cuda()   # [steps][B][D]
-    y = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    model.set_option(kda.KDA_OPT_GRAPH, 1)
-    model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
-    one_launch = not args.per_layer and model.persistent_blocks() > 0
-    path = (f"one cooperative launch per token ({model.persistent_blocks()} blocks)" if one_launch
-            else "per-layer kernels replayed as one hipGraph")
-    log(f"[bench] path: {path}")
-    for i in range(args.warmup):
-        model.decode_step(xs[i], y, st, ws)
-    torch.cuda.synchronize()
-    # ---- timed region: K steps, inputs resident in HBM ----
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        model.decode_step(xs[args.warmup + i], y, st, ws)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    tok_s = args.steps / el
-    ms_step = el * 1e3 / args.steps
-    log(f"[bench] {args.steps} steps in {el * 1e3:.2f} ms: {tok_s:.1f} tokens/s")
-
-    # ---- per-kernel durations with hipEvents on the launch stream (no graph) ----
-    model.set_option(kda.KDA_OPT_TIMING, 1)
-    model.timing(kda.KDA_K_PROJ, reset=True)
-    for i in range(args.steps):
-        model.decode_step(xs[args.warmup + i], y, st, ws)
-    torch.cuda.synchronize()
-    kinds = {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES, "head": kda.KDA_K_HEAD,
-             "out": kda.KDA_K_OUT, "step": kda.KDA_K_STEP}
-    times = {k: model.timing(v) for k, v in kinds.items()}
-    model.set_option(kda.KDA_OPT_TIMING, 0)
-    ab = algorithmic_bytes(w)
-    per = {}
-    for k, (ms, n) in times.items():
-        if n == 0:
-            continue
-        avg_us = ms * 1e3 / n
-        per[k] = {"avg_us": avg_us, "launches": n, "bytes": ab[k],
-                  "gbs": ab[k] / (avg_us * 1e-6) / 1e9}
-        log(f"[bench] kernel {k}: {n} launches, avg {avg_us:.2f} us, "
-            f"{per[k]['gbs']:.0f} GB/s algorithmic")
-    dom = max(per, key=lambda k: per[k]["avg_us"] * per[k]["launches"])
-    ach = per[dom]["gbs"]
-    step_gbs = ab["token_weights_state"] / (ms_step * 1e-3) / 1e9
+                         prenorm_residual=w.prenorm_residual, norm_eps=w.norm_eps,
+                         l2_eps=w.l2_eps)
+    log(f"[bench] packed {w.wtype} weights on the device in {time.time() - t0:.1f}s")
+    fn = {"stack": bench_stack, "layer": bench_stack, "verify": bench_verify,
+          "prefill": bench_prefill}[args.workload]
+    metric, value, unit, ms_step, config, roof = fn(args, torch, synth, kda, w, run, model)
+    model.close()
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(run, args.cpu_budget)
-        log(f"[cpu] {cpu['sample']}: {cpu['value']:.3f} tokens/s")
+        cpu = cpu_baseline_for(args.workload, run, args.cpu_budget)
+        log(f"[cpu] {cpu['sample']}: {cpu['value']:.3f} {cpu['unit']}")
 
     out = {
-        "metric": "KDA decode tokens/s (34-layer stack, B=1)",
-        "value": round(tok_s, 2),
-        "unit": "tokens/s",
+        "metric": metric,
+        "value": round(value, 2),
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -217,23 +463,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "kda-stack-34L-q8_0-decode", "layers": w.n_layers,
-                   "d_model": d.d_model, "heads": d.n_heads, "d_k": d.d_k, "d_v": d.d_v,
-                   "weights": "q8_0", "state": "f32", "batch": B, "global_batch": B,
-                   "seq_len": 1, "parallelism": "none (1 GPU)",
-                   "path": path,
-                   "bytes_per_token": ab["token_weights_state"],
-                   "step_hbm_gbs": round(step_gbs, 1),
-                   "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
-                   "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv)
-                                   for kk, vv in v.items()} for k, v in per.items()}},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                     "traffic": step_traffic() if dom == "step" else None},
+        "config": config,
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
-    model.close()
 
 
 if __name__ == "__main__":

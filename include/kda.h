@@ -140,8 +140,10 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
 
 /* Queries.  KDA_Q_PERSISTENT: number of blocks of the one-launch decode, 0 if the model is
  * not eligible (it needs Q8_0 weights, a pre-norm residual stack, d_k = d_v = 128,
- * H*d_v = D a multiple of 1024, and one co-resident block per CU).  The library allocates
- * a few KB of device memory for it at kda_model_create (exchange words, layer table). */
+ * H*d_v = D in {1024, 2048}, rank_f = rank_g in {32, 64, 128}, H <= 32, and one
+ * co-resident block per CU with 2 H + D/16 <= CUs and at most 32 projection rows per
+ * block).  The library allocates ~130 KB of device memory for it at kda_model_create
+ * (exchange words, flags, layer table). */
 typedef enum { KDA_Q_PERSISTENT = 0 } kda_query;
 int kda_model_query(const kda_model* m, int what);
 
@@ -152,8 +154,8 @@ int kda_model_status(kda_model* m);
 
 /* Kernel kinds reported by kda_timing_query. */
 typedef enum { KDA_K_PROJ = 0, KDA_K_HEAD = 1, KDA_K_OUT = 2, KDA_K_COMMIT = 3,
-               KDA_K_PREFILL = 4, KDA_K_GATES = 5, KDA_K_STEP = 6,
-               KDA_K_COUNT = 7 } kda_kernel_kind;
+               KDA_K_PREFILL = 4, KDA_K_GATES = 5, KDA_K_STEP = 6, KDA_K_GEMM = 7,
+               KDA_K_CHUNK = 8, KDA_K_COUNT = 9 } kda_kernel_kind;
 /* Sum of event-timed durations (ms) and launch count per kernel kind since the last
  * reset; synchronises on the recorded events.  reset != 0 clears the counters. */
 int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset);

@@ -750,7 +750,7 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   }
   g.nseg = 6; g.M = (int)M; g.N = m->proj_rows; g.K = d.d_model;
   g.C = F(wl.P); g.ldc = m->proj_stride; g.coff = 0;
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(g, s); });
+  r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(g, s); });
   if (r) return r;
   // low-rank up-projections F_b f_lr and G_b g_lr (fp32 inputs as two BF16 terms)
   GemmParams gf;
@@ -758,13 +758,13 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   gf.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.fb.w); gf.nseg = 1;
   gf.M = (int)M; gf.N = m->Kq; gf.K = d.rank_f;
   gf.C = F(wl.FG); gf.ldc = m->Kq + m->V; gf.coff = 0;
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(gf, s); });
+  r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(gf, s); });
   if (r) return r;
   GemmParams gg = gf;
   gg.A = F(wl.P) + m->C + d.rank_f;
   gg.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.gb.w);
   gg.N = m->V; gg.K = d.rank_g; gg.coff = m->Kq;
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(gg, s); });
+  r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(gg, s); });
   if (r) return r;
 
   PrefillParams p;
@@ -785,9 +785,9 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_window(p, s); });
   if (r) return r;
   // P3 / P4: chunked delta rule
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_chunk_intra(p, s); });
+  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_intra(p, s); });
   if (r) return r;
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_chunk_inter(p, s); });
+  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_inter(p, s); });
   if (r) return r;
   // P5: gated RMSNorm, then the output projection (fp32 input as two BF16 terms)
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gated_norm(p, s); });
@@ -797,7 +797,7 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   go.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.wo.w); go.nseg = 1;
   go.M = (int)M; go.N = d.d_model; go.K = m->V;
   go.C = y_dev; go.ldc = d.d_model; go.coff = 0;
-  return timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gemm(go, s); });
+  return timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(go, s); });
 }
 
 }  // extern "C"
