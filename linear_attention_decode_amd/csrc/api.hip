@@ -2,6 +2,7 @@
 // sequencing per layer, hipGraph capture of the decode step, and event timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -11,6 +12,7 @@
 
 #include "kda.h"
 #include "kda_internal.h"
+#include "skinny.h"
 
 using namespace kda;
 
@@ -102,7 +104,7 @@ struct kda_model {
 namespace {
 
 struct WsLayout {
-  size_t proj = 0, ag = 0, o = 0, gate = 0, ss = 0, total = 0;
+  size_t proj = 0, ag = 0, o = 0, gate = 0, ss = 0, sk = 0, total = 0;
 };
 
 WsLayout ws_layout(const kda_model* m, int64_t N) {
@@ -113,6 +115,11 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
   w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
   w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
   w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
+  // MFMA column-fragment scratch of the skinny projections (Q8_0 with 9..64 columns)
+  const int Kmax = std::max(m->d.d_model, m->V);
+  w.sk = off;
+  if (skinny_supported(m->d.wtype, (int)N, m->d.d_model) || skinny_supported(m->d.wtype, (int)N, m->V))
+    off = align_up(off + skinny_scratch_bytes((int)N, Kmax), 256);
   w.total = off;
   return w;
 }
@@ -248,7 +255,10 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   pp.win = win;
   pp.C = m->C;
   const int g1 = proj_grid(pp);
-  int r = timed(m, KDA_K_PROJ, s, rec, [&] { return launch_gemv(d.wtype, kProX, pp, g1, s); });
+  int r = timed(m, KDA_K_PROJ, s, rec, [&] {
+    if (skinny_supported(d.wtype, N, pp.K)) return launch_skinny(kProX, pp, ws + wl.sk, s);
+    return launch_gemv(d.wtype, kProX, pp, g1, s);
+  });
   if (r) return r;
 
   r = enqueue_gates(m, L, proj, N, ag, s, rec);
@@ -287,7 +297,10 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   po.out_stride = d.d_model;
   po.resid = d.prenorm_residual ? x_in : nullptr;
   const int g2 = (d.d_model + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
-  return timed(m, KDA_K_OUT, s, rec, [&] { return launch_gemv(d.wtype, kProGatedNorm, po, g2, s); });
+  return timed(m, KDA_K_OUT, s, rec, [&] {
+    if (skinny_supported(d.wtype, N, po.K)) return launch_skinny(kProGatedNorm, po, ws + wl.sk, s);
+    return launch_gemv(d.wtype, kProGatedNorm, po, g2, s);
+  });
 }
 
 size_t state_layer_stride(const kda_model* m, int B) {

@@ -1,0 +1,15 @@
+// Q8_0 weights times 9..64 columns on the matrix cores (skinny.hip).
+#pragma once
+#include "kda_internal.h"
+
+namespace kda {
+
+// True when launch_skinny handles this product: Q8_0 weights, 8 < N <= 64 columns,
+// K a multiple of 128 and at most 4096.
+bool skinny_supported(int wt, int N, int K);
+// Device scratch the column preparation needs for N columns of length K.
+size_t skinny_scratch_bytes(int N, int K);
+// Same product, prologue and epilogue as launch_gemv(kQ8, prologue, g, ...), on MFMA.
+hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,319 @@
+// Q8_0 weights times a few columns on the matrix cores of gfx950: the projections of verify
+// (B sequences x T tokens) and of batched decode, where the vector GEMV would stream the
+// weights once per 8 columns at two VALU instructions per weight and column.
+//
+// Two launches per product:
+//   skinny_prep   one block per input column: the GEMV's prologue (RMSNorm of x, or the
+//                 gated RMSNorm of the heads), a power-of-two column scale keeping the values
+//                 well inside fp16 range, and the split x = hi + lo into two fp16 values, both
+//                 written in the B-operand layout of v_mfma_f32_16x16x32_f16, plus each
+//                 32-element block's sum of hi + lo;
+//   skinny_gemm   one block per 16 weight rows, four waves splitting K.  A lane turns 8
+//                 weight bytes u = q + 128 into the fp16 values 1024 + u with two byte
+//                 permutes per 4 bytes (1152 + q exactly), so one MFMA pair per 32-wide Q8_0
+//                 block gives sum (1152 + q) x; the block's scale and the bias 1152 * sum x
+//                 are applied to the MFMA output before it joins the fp32 sum.  The waves'
+//                 partial sums meet in LDS, then the GEMV's epilogues (conv + SiLU + window
+//                 roll, residual) run unchanged.
+// The result differs from the fp32 GEMV only by rounding: x is carried to ~22 bits by the
+// hi/lo pair, the weight values are exact, and the MFMA accumulates in fp32.
+#include "kda_device.h"
+#include "skinny.h"
+
+namespace kda {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kSkThreads = 256;
+constexpr int kSkRows = 16;        // weight rows per block
+constexpr int kSkKBMax = 32;       // 32-wide k blocks per wave: K <= 4 * 32 * 32 = 4096
+
+size_t skinny_scratch_bytes(int N, int K) {
+  const size_t NT = (size_t)(N + 15) / 16, KB = (size_t)K / 32;
+  return align_up(KB * NT * 64 * 16, 256) * 2 + align_up(KB * NT * 16 * 4, 256) +
+         align_up(NT * 16 * 4, 256);
+}
+
+bool skinny_supported(int wt, int N, int K) {
+  return wt == kQ8 && N > 8 && N <= 64 && K % 128 == 0 && K <= 4 * 32 * kSkKBMax;
+}
+
+struct SkScratch {
+  uint4* fh;        // [K/32][NT][64] fp16 x 8: hi parts, B-operand layout
+  uint4* fl;        // same, lo parts
+  float* xsum;      // [K/32][NT * 16] sum of (hi + lo) over each 32-element block
+  float* cscale;    // [NT * 16] 2^-e: the factor the column was multiplied by, inverted
+};
+
+static SkScratch carve(void* scratch, int N, int K) {
+  const size_t NT = (size_t)(N + 15) / 16, KB = (size_t)K / 32;
+  char* p = static_cast<char*>(scratch);
+  SkScratch s;
+  s.fh = reinterpret_cast<uint4*>(p);
+  p += align_up(KB * NT * 64 * 16, 256);
+  s.fl = reinterpret_cast<uint4*>(p);
+  p += align_up(KB * NT * 64 * 16, 256);
+  s.xsum = reinterpret_cast<float*>(p);
+  p += align_up(KB * NT * 16 * 4, 256);
+  s.cscale = reinterpret_cast<float*>(p);
+  return s;
+}
+
+__device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// ------------------------------------------------------------------------------------
+// skinny_prep: column n of the (prologue-applied) input -> fp16 hi/lo fragments.
+// ------------------------------------------------------------------------------------
+template <int PRO>
+__global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParams P, int NT,
+                                                                 SkScratch S) {
+  __shared__ float red[4];
+  __shared__ float scal[kGemvMaxHeads];
+  const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = P.K;
+  const bool live = n < P.N;   // block-uniform
+  // per-column factors of the prologue
+  float sc = 1.0f;
+  if (PRO == kProX && P.prenorm && live) {
+    float a = 0.0f;
+    for (int k = tid; k < K; k += kSkThreads) {
+      const float v = P.x[(size_t)n * P.x_stride + k];
+      a += v * v;
+    }
+    a = wave_sum(a);
+    if (lane == 0) red[wave] = a;
+    __syncthreads();
+    sc = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)K + P.eps);
+    __syncthreads();
+  }
+  if (PRO == kProGatedNorm && live) {
+    if (tid < P.H) {
+      const float* sp = P.ss + ((size_t)n * P.H + tid) * P.ncb;
+      float a = 0.0f;
+      for (int j = 0; j < P.ncb; ++j) a += sp[j];
+      scal[tid] = 1.0f / sqrtf(a / (float)P.dv + P.eps);
+    }
+    __syncthreads();
+  }
+  auto value = [&](int k) -> float {
+    if (!live) return 0.0f;
+    if constexpr (PRO == kProX) {
+      return P.x[(size_t)n * P.x_stride + k] * sc;
+    } else {
+      const int h = k / P.dv;
+      const float w = P.onw ? P.onw[k - h * P.dv] : 1.0f;
+      const size_t g = (size_t)n * K + k;
+      return P.o[g] * scal[h] * w * P.gate[g];
+    }
+  };
+  // power-of-two column scale: max |x| lands in [1024, 2048)
+  float amax = 0.0f;
+  for (int k = tid; k < K; k += kSkThreads) amax = fmaxf(amax, fabsf(value(k)));
+  {
+    // max over the block through the sum helpers' permutes is not available: use LDS
+    __shared__ float mx[kSkThreads];
+    mx[tid] = amax;
+    __syncthreads();
+    for (int s = kSkThreads / 2; s > 0; s >>= 1) {
+      if (tid < s) mx[tid] = fmaxf(mx[tid], mx[tid + s]);
+      __syncthreads();
+    }
+    amax = mx[0];
+  }
+  int e = 0;
+  if (amax > 0.0f) frexpf(amax, &e);           // amax in [2^(e-1), 2^e)
+  const float up = ldexpf(1.0f, 11 - e);      // amax * up in [1024, 2048)
+  if (tid == 0) S.cscale[n] = live && amax > 0.0f ? ldexpf(1.0f, e - 11) : 0.0f;
+  const int ct = n >> 4, nl = n & 15;
+  // each thread: groups of 8 consecutive k (one 16-byte fragment piece)
+  for (int g8 = tid; g8 < K / 8; g8 += kSkThreads) {
+    const int k0 = g8 * 8, kb = k0 >> 5, g = (k0 >> 3) & 3;
+    _Float16 hi[8], lo[8];
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float v = value(k0 + j) * up;
+      hi[j] = (_Float16)v;
+      const float hv = (float)hi[j];
+      lo[j] = (_Float16)(v - hv);
+      s += hv + (float)lo[j];
+    }
+    const size_t fi = ((size_t)kb * NT + ct) * 64 + nl + 16 * g;
+    S.fh[fi] = make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
+    S.fl[fi] = make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
+    // the four threads of a k block are consecutive (K / 8 per column, 4 per block)
+    s = group_sum(s, 4);
+    if (g == 0) S.xsum[(size_t)kb * NT * 16 + n] = s;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// skinny_gemm: out[n][out_off + row] = sum_k W[row][k] x[n][k] (+ epilogue)
+// ------------------------------------------------------------------------------------
+struct SkSeg {
+  PackedMat m;
+  int rows = 0, first_tile = 0, out_off = 0, conv_chan = -1;
+};
+struct SkParams {
+  SkSeg seg[kMaxSegs];
+  int nseg = 0, K = 0, N = 0;
+  SkScratch S;
+  float* out = nullptr;
+  int out_stride = 0;
+  const float* resid = nullptr;
+  const float* conv_w = nullptr;
+  float* win = nullptr;
+  int C = 0;
+};
+
+// 8 weight bytes u -> 8 fp16 values 1024 + u (byte permutes against 0x64 high bytes)
+__device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
+  const uint32_t k64 = 0x64646464u;
+  uint32_t r[4];
+  r[0] = __builtin_amdgcn_perm(k64, w.x, 0x04010400u);
+  r[1] = __builtin_amdgcn_perm(k64, w.x, 0x04030402u);
+  r[2] = __builtin_amdgcn_perm(k64, w.y, 0x04010400u);
+  r[3] = __builtin_amdgcn_perm(k64, w.y, 0x04030402u);
+  return __builtin_bit_cast(f16x8, r);
+}
+
+template <int NT>
+__global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
+  __shared__ float part[4][NT][64][4];           // per-wave partial outputs
+  __shared__ __half s_sc[kSkKBMax * 4][kSkRows];  // [k block][row] Q8_0 scales
+  __shared__ float s_xs[kSkKBMax * 4][NT * 16];   // [k block][column] block sums
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = P.K, KB = K / 32, KB4 = KB / 4;
+  // segment of this block
+  SkSeg sg = P.seg[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSegs; ++i)
+    if (i < P.nseg && (int)blockIdx.x >= P.seg[i].first_tile) sg = P.seg[i];
+  const int row0 = ((int)blockIdx.x - sg.first_tile) * kSkRows;
+  const int nrows = min(kSkRows, sg.rows - row0);
+
+  // A operand: lane holds row (lane & 15), bytes 8 (lane >> 4) .. + 7 of each k block;
+  // the wave's whole K range is requested up front
+  const int ar = min(lane & 15, nrows - 1), ag = lane >> 4;
+  const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K + 8 * ag;
+  const int kb0 = wave * KB4;
+  uint2 a[kSkKBMax];
+#pragma unroll
+  for (int j = 0; j < kSkKBMax; ++j)
+    if (j < KB4) {
+      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32));
+      a[j] = make_uint2(v.x, v.y);
+    }
+  // scales [k block][row] and block sums into LDS
+  for (int i = tid; i < KB * kSkRows; i += kSkThreads) {
+    const int r = i / KB, kb = i - r * KB;
+    s_sc[kb][r] = r < nrows ? sg.m.d[(size_t)(row0 + r) * KB + kb] : __float2half(0.0f);
+  }
+  for (int i = tid; i < KB * NT * 16; i += kSkThreads) s_xs[i / (NT * 16)][i % (NT * 16)] = P.S.xsum[i];
+  __syncthreads();
+
+  f32x4v acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  const uint4* fh = P.S.fh + lane;
+  const uint4* fl = P.S.fl + lane;
+  const int og = lane >> 4, oc = lane & 15;      // output rows 4 og .. + 3, column oc (+ 16 t)
+#pragma unroll
+  for (int j = 0; j < kSkKBMax; ++j) {
+    if (j < KB4) {
+      const int kb = kb0 + j;
+      const f16x8 av = bytes_to_f16(a[j]);
+      const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][4 * og]);
+      const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
+      const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
+      const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
+      const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const size_t fi = ((size_t)kb * NT + t) * 64;
+        const f16x8 bh = __builtin_bit_cast(f16x8, fh[fi]);
+        const f16x8 bl = __builtin_bit_cast(f16x8, fl[fi]);
+        f32x4v o = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, o, 0, 0, 0);
+        const float bias = 1152.0f * s_xs[kb][t * 16 + oc];
+        acc[t][0] += d0 * (o[0] - bias);
+        acc[t][1] += d1 * (o[1] - bias);
+        acc[t][2] += d2 * (o[2] - bias);
+        acc[t][3] += d3 * (o[3] - bias);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][t][lane][i] = acc[t][i];
+  __syncthreads();
+  // sum the four waves' partials and run the epilogue: thread -> (t, lane, i)
+  for (int e = tid; e < NT * 64 * 4; e += kSkThreads) {
+    const int t = e / 256, l = (e >> 2) & 63, i = e & 3;
+    const int row = 4 * (l >> 4) + i, n = t * 16 + (l & 15);
+    if (row >= nrows || n >= P.N) continue;
+    float v = (part[0][t][l][i] + part[1][t][l][i]) + (part[2][t][l][i] + part[3][t][l][i]);
+    v *= P.S.cscale[n];
+    const int grow = row0 + row;
+    if (sg.conv_chan >= 0) {
+      // causal conv over (window, this token), SiLU, window roll (one owner per channel)
+      const int c = sg.conv_chan + grow;
+      const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
+      float* z = P.win + (size_t)n * 3 * P.C + c;
+      const float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
+      const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * v;
+      z[0] = z1;
+      z[P.C] = z2;
+      z[2 * P.C] = v;
+      v = silu_f(y);
+    }
+    const size_t o = (size_t)n * P.out_stride + sg.out_off + grow;
+    if (P.resid) v += P.resid[o];
+    P.out[o] = v;
+  }
+}
+
+hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipStream_t s) {
+  const int NT = (g.N + 15) / 16;
+  SkParams p;
+  p.nseg = g.nseg;
+  int tiles = 0;
+  for (int i = 0; i < g.nseg; ++i) {
+    p.seg[i].m = g.seg[i].m;
+    p.seg[i].rows = g.seg[i].rows;
+    p.seg[i].first_tile = tiles;
+    p.seg[i].out_off = g.seg[i].out_off;
+    p.seg[i].conv_chan = g.seg[i].conv_chan;
+    tiles += (g.seg[i].rows + kSkRows - 1) / kSkRows;
+  }
+  p.K = g.K;
+  p.N = g.N;
+  p.S = carve(scratch, g.N, g.K);
+  p.out = g.out;
+  p.out_stride = g.out_stride;
+  p.resid = g.resid;
+  p.conv_w = g.conv_w;
+  p.win = g.win;
+  p.C = g.C;
+  if (prologue == kProX)
+    skinny_prep_kernel<kProX><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  else
+    skinny_prep_kernel<kProGatedNorm><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (NT) {
+    case 1: skinny_gemm_kernel<1><<<tiles, kSkThreads, 0, s>>>(p); break;
+    case 2: skinny_gemm_kernel<2><<<tiles, kSkThreads, 0, s>>>(p); break;
+    case 3: skinny_gemm_kernel<3><<<tiles, kSkThreads, 0, s>>>(p); break;
+    default: skinny_gemm_kernel<4><<<tiles, kSkThreads, 0, s>>>(p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

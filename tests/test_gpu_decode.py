@@ -134,6 +134,16 @@ def test_decode_stack_q8_0_full_size(torch, persistent):
     _say(f"  stack: out {e:.2e} state {s:.2e}")
 
 
+@pytest.mark.parametrize("B", [9, 12, 33])
+def test_decode_batched_q8_0_matrix_cores(torch, B):
+    """B > 8 sequences of Q8_0 decode take the MFMA projections (column count not a
+    multiple of 16 for 9 and 33; the conv epilogue runs per sequence)."""
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=2, batch=B, steps=4, seed=60 + B)
+    _say(f"decode batched q8_0 B={B} 2 layers D=2048 4 steps (MFMA projections)")
+    e, s = _decode_parity(w, w.steps, snap_every=2)
+    _say(f"  B={B}: out {e:.2e} state {s:.2e}")
+
+
 def test_decode_stack_one_launch_three_layers_32_steps(torch):
     """The one-launch decode over 32 consecutive tokens (tags advance every token), with
     the state checked every 8 steps."""

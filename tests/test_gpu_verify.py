@@ -81,6 +81,13 @@ def test_verify_small_stack():
     _check(w, w.steps)
 
 
+def test_verify_ragged_columns_matrix_cores():
+    """B=5 x T=3 = 15 token positions at D=2048: MFMA projections with a padded column tile."""
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=2, batch=5, tokens=3, steps=3, seed=35)
+    _say("verify 2 layers B=5 T=3 D=2048 q8_0, 3 steps (MFMA projections)")
+    _check(w, w.steps)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3])
 def test_verify_token_counts(T):
     d = synth.LayerDims(d_model=96, n_heads=3, d_k=64, d_v=64, rank_f=32, rank_g=32)
