@@ -98,7 +98,7 @@ struct kda_model {
 
 // ---------------------------------------------------------------------------------------
 // Workspace layout (decode / verify): proj [N][proj_stride] | alpha,gate [N][K+V] |
-// o [N][V] | gate [N][V] | ss [N][H][V/kHeadCols]; each region 256-byte aligned.
+// o [N][V] | gate [N][V] | ss [N][H][V/kHeadColsConv]; each region 256-byte aligned.
 // Verify log per layer: proj rows [N][proj_stride] then alpha,gate [N][K+V].
 // ---------------------------------------------------------------------------------------
 namespace {
@@ -114,7 +114,7 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
   w.ag = off;   off = align_up(off + (size_t)N * (m->Kq + m->V) * 4, 256);
   w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
   w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
-  w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
+  w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadColsConv) * 4, 256);
   // MFMA column-fragment scratch of the skinny projections (Q8_0 with 9..64 columns)
   const int Kmax = std::max(m->d.d_model, m->V);
   w.sk = off;
@@ -291,7 +291,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   po.K = m->V;
   po.N = N;
   po.o = o; po.gate = gate; po.ss = ss; po.onw = L.o_norm_w;
-  po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / kHeadCols;
+  po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / head_cols(hp.conv_in_head != 0);
   po.eps = d.norm_eps;
   po.out = y;
   po.out_stride = d.d_model;

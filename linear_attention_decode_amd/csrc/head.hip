@@ -57,12 +57,13 @@ __device__ __forceinline__ float hchunk_dot(const uint4 w, const float* __restri
 // ---------------------------------------------------------------------------------------
 constexpr int kGateThreads = 256;
 constexpr int kMaxRank = 256;
+constexpr int kGateCols = 16;    // columns staged per round (a multiple of every CPR)
 
 template <int WT, int CPR>
 __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P) {
   constexpr int EL = HFmt<WT>::kElems;
   constexpr int BY = HFmt<WT>::kBytes;
-  __shared__ float s_lr[2 * kMaxRank];
+  __shared__ __align__(16) float s_lr[kGateCols][2 * kMaxRank];
   const int tid = threadIdx.x;
   const int rows = P.K + P.V;
   const int it = blockIdx.x * kGateThreads + tid;
@@ -77,22 +78,55 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
     const int r = f ? row : row - P.K;
     w = *reinterpret_cast<const uint4*>(M.w + ((size_t)r * rank + (size_t)c * EL) * BY);
     if constexpr (WT == kQ8) sc = __half2float(M.d[(size_t)r * (rank / 32) + (c >> 1)]);
-    if (f && c == 0) {
+    if (f) {
       bias = P.dt_bias[row];
       ah = P.a_log[row / P.dk];
     }
   }
-  for (int n = 0; n < P.N; ++n) {
-    const float* lr = P.proj + (size_t)n * P.proj_stride + P.C;
-    for (int i = tid; i < 2 * rank; i += kGateThreads) s_lr[i] = lr[i];
+  // kGateCols columns' low-rank inputs per round, staged with independent loads; within a
+  // round, the CPR lanes of a row's group each finish one of CPR consecutive columns
+  for (int n0 = 0; n0 < P.N; n0 += kGateCols) {
+    const int nc = min(kGateCols, P.N - n0);
+    {
+      // all loads first (a fixed, unrolled count per thread), then the LDS stores
+      constexpr int kStage = kGateCols * 2 * kMaxRank / 4 / kGateThreads;
+      const int per4 = 2 * rank / 4, total4 = nc * per4;
+      float4 v[kStage];
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kGateThreads;
+        if (i < total4) {
+          const int nn = i / per4, k4 = i - nn * per4;
+          v[u] = *reinterpret_cast<const float4*>(P.proj + (size_t)(n0 + nn) * P.proj_stride + P.C + 4 * k4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kStage; ++u) {
+        const int i = tid + u * kGateThreads;
+        if (i < total4) {
+          const int nn = i / per4, k4 = i - nn * per4;
+          *reinterpret_cast<float4*>(&s_lr[nn][4 * k4]) = v[u];
+        }
+      }
+    }
     __syncthreads();
-    const float* xv = (f ? s_lr : s_lr + rank) + c * EL;
-    float part = valid ? hchunk_dot<WT>(w, xv) : 0.0f;
-    if constexpr (WT == kQ8) part *= sc;
-    part = group_sum(part, CPR);
-    if (valid && c == 0) {
-      float* out = P.out + (size_t)n * rows;
-      out[row] = f ? expf(-expf(ah) * softplus_f(part + bias)) : sigmoid_f(part);
+    for (int nb = 0; nb < nc; nb += CPR) {
+      float mine = 0.0f;
+#pragma unroll
+      for (int g = 0; g < CPR; ++g) {
+        const int nn = nb + g;
+        float part = 0.0f;
+        if (valid && nn < nc) {
+          part = hchunk_dot<WT>(w, (f ? s_lr[nn] : s_lr[nn] + rank) + c * EL);
+          if constexpr (WT == kQ8) part *= sc;
+        }
+        part = group_sum(part, CPR);
+        if (c == g) mine = part;
+      }
+      const int nn = nb + c;
+      if (valid && nn < nc)
+        P.out[(size_t)(n0 + nn) * rows + row] =
+            f ? expf(-expf(ah) * softplus_f(mine + bias)) : sigmoid_f(mine);
     }
     __syncthreads();
   }
@@ -132,21 +166,30 @@ bool head_supported(int dk, int wt, int rank_f, int rank_g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// Delta rule: one wave per (32 value columns, head, sequence).  Lane (rg = lane % 8,
-// cq = lane / 8) holds state rows rg*RPT .. rg*RPT + RPT - 1 of columns 4cq .. 4cq + 3 of
-// the wave's 32 as float4s; column sums reduce over the row groups (low lane bits) with
-// DPP, the L2 norms over the same row groups.  No LDS, no barrier.
+// Delta rule: one wave per (CW value columns, head, sequence).  Lane (rg = lane % RG,
+// cq = lane / RG, RG = 256 / CW row groups) holds state rows rg*RPT .. rg*RPT + RPT - 1 of
+// columns 4cq .. 4cq + 3 of the wave's CW as float4s; column sums reduce over the row
+// groups (low lane bits) with DPP, the L2 norms over the same row groups.  No LDS, no
+// barrier.  Decode uses CW = 32; verify / commit, which also carry each lane's conv window
+// and taps over T tokens, use CW = 16 so that everything stays in registers.
 // ---------------------------------------------------------------------------------------
-template <int DK>
+template <int RG>
+__device__ __forceinline__ float rowsum(float v) {
+  if constexpr (RG == 8) return sum8(v);
+  else return sum16(v);
+}
+
+template <int DK, int CW, bool CONV>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
-  constexpr int RPT = DK / 8;
+  constexpr int RG = 256 / CW;
+  constexpr int RPT = DK / RG;
   const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
-  const int rg = lane & 7, cq = lane >> 3;
+  const int rg = lane % RG, cq = lane / RG;
   const int H = P.H, dv = P.dv, C = P.C, K = H * DK;
-  const int j = cb * 32 + cq * 4;             // this lane's first value column in the head
+  const int j = cb * CW + cq * 4;             // this lane's first value column in the head
   const int r0 = rg * RPT;                     // this lane's first key row
-  const int nparts = dv / 32;
+  const int nparts = dv / CW;
   const int rl = P.rank_f + P.rank_g;
 
   int ntok = P.T;
@@ -162,7 +205,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   const int cq0 = h * DK + r0, ck0 = K + h * DK + r0, cv0 = 2 * K + h * dv + j;
   float zq[RPT][3], zk[RPT][3], zv[4][3];
   float4 wq[RPT], wk[RPT], wv[4];
-  if (P.conv_in_head) {
+  if constexpr (CONV) {
     const float* zw = P.win + (size_t)b * 3 * C;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -189,28 +232,44 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     return silu_f(y);
   };
 
-  for (int t = 0; t < ntok; ++t) {
+  // token inputs (q, k rows and v columns of this lane; alpha rows; gate columns; beta),
+  // requested one token ahead of their use
+  struct Tok {
+    float qv[RPT], kv[RPT], al[RPT], v4[4];
+    float4 gate;
+    float braw;
+  };
+  auto load_tok = [&](int t, Tok& x) {
     const int n = b * P.T + t;
     const float* prow = P.proj + (size_t)n * P.proj_stride;
     const float* ag = P.alpha_gate + (size_t)n * (K + H * dv);
-    // token inputs (q, k rows and v columns of this lane; alpha rows; gate columns)
-    float qv[RPT], kv[RPT], al[RPT], v4[4];
 #pragma unroll
     for (int i = 0; i < RPT; i += 4) {
       const float4 a = *reinterpret_cast<const float4*>(prow + cq0 + i);
       const float4 k4 = *reinterpret_cast<const float4*>(prow + ck0 + i);
       const float4 g4 = *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
-      qv[i] = a.x; qv[i + 1] = a.y; qv[i + 2] = a.z; qv[i + 3] = a.w;
-      kv[i] = k4.x; kv[i + 1] = k4.y; kv[i + 2] = k4.z; kv[i + 3] = k4.w;
-      al[i] = g4.x; al[i + 1] = g4.y; al[i + 2] = g4.z; al[i + 3] = g4.w;
+      x.qv[i] = a.x; x.qv[i + 1] = a.y; x.qv[i + 2] = a.z; x.qv[i + 3] = a.w;
+      x.kv[i] = k4.x; x.kv[i + 1] = k4.y; x.kv[i + 2] = k4.z; x.kv[i + 3] = k4.w;
+      x.al[i] = g4.x; x.al[i + 1] = g4.y; x.al[i + 2] = g4.z; x.al[i + 3] = g4.w;
     }
-    {
-      const float4 a = *reinterpret_cast<const float4*>(prow + cv0);
-      v4[0] = a.x; v4[1] = a.y; v4[2] = a.z; v4[3] = a.w;
-    }
-    const float4 gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
-    const float beta = sigmoid_f(prow[C + rl + h]);
-    if (P.conv_in_head) {
+    const float4 a = *reinterpret_cast<const float4*>(prow + cv0);
+    x.v4[0] = a.x; x.v4[1] = a.y; x.v4[2] = a.z; x.v4[3] = a.w;
+    x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
+    x.braw = prow[C + rl + h];
+  };
+  Tok nxt;
+  load_tok(0, nxt);
+  for (int t = 0; t < ntok; ++t) {
+    const int n = b * P.T + t;
+    Tok cur = nxt;
+    if (t + 1 < ntok) load_tok(t + 1, nxt);
+    float (&qv)[RPT] = cur.qv;
+    float (&kv)[RPT] = cur.kv;
+    float (&al)[RPT] = cur.al;
+    float (&v4)[4] = cur.v4;
+    const float4 gate = cur.gate;
+    const float beta = sigmoid_f(cur.braw);
+    if constexpr (CONV) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         qv[i] = conv(zq[i], wq[i], qv[i]);
@@ -223,8 +282,8 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     float aq = 0.0f, ak = 0.0f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) { aq += qv[i] * qv[i]; ak += kv[i] * kv[i]; }
-    const float inv_q = P.q_scale / sqrtf(sum8(aq) + P.l2_eps);
-    const float inv_k = 1.0f / sqrtf(sum8(ak) + P.l2_eps);
+    const float inv_q = P.q_scale / sqrtf(rowsum<RG>(aq) + P.l2_eps);
+    const float inv_k = 1.0f / sqrtf(rowsum<RG>(ak) + P.l2_eps);
 
     float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
 #pragma unroll
@@ -233,7 +292,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
       st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
       e0 += st[i].x * kk; e1 += st[i].y * kk; e2 += st[i].z * kk; e3 += st[i].w * kk;
     }
-    e0 = sum8(e0); e1 = sum8(e1); e2 = sum8(e2); e3 = sum8(e3);
+    e0 = rowsum<RG>(e0); e1 = rowsum<RG>(e1); e2 = rowsum<RG>(e2); e3 = rowsum<RG>(e3);
     const float d0 = beta * (v4[0] - e0), d1 = beta * (v4[1] - e1);
     const float d2 = beta * (v4[2] - e2), d3 = beta * (v4[3] - e3);
     float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
@@ -243,15 +302,16 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
       st[i].x += kk * d0; st[i].y += kk * d1; st[i].z += kk * d2; st[i].w += kk * d3;
       o0 += st[i].x * qq; o1 += st[i].y * qq; o2 += st[i].z * qq; o3 += st[i].w * qq;
     }
-    o0 = sum8(o0); o1 = sum8(o1); o2 = sum8(o2); o3 = sum8(o3);
+    o0 = rowsum<RG>(o0); o1 = rowsum<RG>(o1); o2 = rowsum<RG>(o2); o3 = rowsum<RG>(o3);
     if (P.write_out) {
       if (rg == 0) {
         const size_t g = (size_t)n * H * dv + h * dv + j;
         *reinterpret_cast<float4*>(P.o + g) = make_float4(o0, o1, o2, o3);
         *reinterpret_cast<float4*>(P.gate + g) = gate;
       }
+      // o^2 over the wave's columns: each row of 16 lanes holds 16 / RG column quads
       float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
-      q2 += dpp_mov<kDppRor8>(q2);
+      if constexpr (RG == 8) q2 += dpp_mov<kDppRor8>(q2);
       const int qb = __float_as_int(q2);
       const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
                         (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
@@ -267,11 +327,15 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
 }
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
-  dim3 grid(p.dv / 32, p.H, p.B);
-  if (p.dk == 128)
-    head_kernel<128><<<grid, 64, 0, s>>>(p);
-  else
-    head_kernel<64><<<grid, 64, 0, s>>>(p);
+  const int cw = head_cols(p.conv_in_head != 0);
+  dim3 grid(p.dv / cw, p.H, p.B);
+  if (p.conv_in_head) {
+    if (p.dk == 128) head_kernel<128, kHeadColsConv, true><<<grid, 64, 0, s>>>(p);
+    else head_kernel<64, kHeadColsConv, true><<<grid, 64, 0, s>>>(p);
+  } else {
+    if (p.dk == 128) head_kernel<128, kHeadCols, false><<<grid, 64, 0, s>>>(p);
+    else head_kernel<64, kHeadCols, false><<<grid, 64, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

@@ -84,6 +84,8 @@ int gemv_cols_per_pass(int N);
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
 // ---------------------------------------------------------------------------------------
 constexpr int kHeadCols = 32;      // value columns per wave (one partial sum of o^2 each)
+constexpr int kHeadColsConv = 16;  // the same with the conv in the head kernel (verify/commit)
+inline int head_cols(bool conv_in_head) { return conv_in_head ? kHeadColsConv : kHeadCols; }
 
 struct HeadParams {
   int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
@@ -104,7 +106,7 @@ struct HeadParams {
   int write_out = 1;
   float* o = nullptr;             // [N][H*dv]
   float* gate = nullptr;          // [N][H*dv]
-  float* ss = nullptr;            // [N][H][dv/kHeadCols] partial sums of o^2
+  float* ss = nullptr;            // [N][H][dv/head_cols(conv_in_head)] partial sums of o^2
   float l2_eps = 0.f;
   float q_scale = 0.f;            // d_k^-1/2 as fp32
 };

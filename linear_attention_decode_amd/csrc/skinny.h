@@ -5,7 +5,7 @@
 namespace kda {
 
 // True when launch_skinny handles this product: Q8_0 weights, 8 < N <= 64 columns,
-// K a multiple of 128 and at most 4096.
+// K in {2048, 4096}.
 bool skinny_supported(int wt, int N, int K);
 // Device scratch the column preparation needs for N columns of length K.
 size_t skinny_scratch_bytes(int N, int K);

@@ -28,7 +28,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kSkThreads = 256;
 constexpr int kSkRows = 16;        // weight rows per block
-constexpr int kSkKBMax = 32;       // 32-wide k blocks per wave: K <= 4 * 32 * 32 = 4096
 
 size_t skinny_scratch_bytes(int N, int K) {
   const size_t NT = (size_t)(N + 15) / 16, KB = (size_t)K / 32;
@@ -37,7 +36,7 @@ size_t skinny_scratch_bytes(int N, int K) {
 }
 
 bool skinny_supported(int wt, int N, int K) {
-  return wt == kQ8 && N > 8 && N <= 64 && K % 128 == 0 && K <= 4 * 32 * kSkKBMax;
+  return wt == kQ8 && N > 8 && N <= 64 && (K == 2048 || K == 4096);
 }
 
 struct SkScratch {
@@ -68,28 +67,21 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
 // ------------------------------------------------------------------------------------
 // skinny_prep: column n of the (prologue-applied) input -> fp16 hi/lo fragments.
 // ------------------------------------------------------------------------------------
-template <int PRO>
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// KG = K / 2048 groups of 8 consecutive elements per thread (all loaded in one pass).
+template <int PRO, int KG>
 __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParams P, int NT,
                                                                  SkScratch S) {
-  __shared__ float red[4];
+  __shared__ float red[2][4];
   __shared__ float scal[kGemvMaxHeads];
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = P.K;
+  constexpr int K = KG * 2048;
   const bool live = n < P.N;   // block-uniform
-  // per-column factors of the prologue
-  float sc = 1.0f;
-  if (PRO == kProX && P.prenorm && live) {
-    float a = 0.0f;
-    for (int k = tid; k < K; k += kSkThreads) {
-      const float v = P.x[(size_t)n * P.x_stride + k];
-      a += v * v;
-    }
-    a = wave_sum(a);
-    if (lane == 0) red[wave] = a;
-    __syncthreads();
-    sc = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)K + P.eps);
-    __syncthreads();
-  }
   if (PRO == kProGatedNorm && live) {
     if (tid < P.H) {
       const float* sp = P.ss + ((size_t)n * P.H + tid) * P.ncb;
@@ -99,53 +91,72 @@ __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParam
     }
     __syncthreads();
   }
-  auto value = [&](int k) -> float {
-    if (!live) return 0.0f;
-    if constexpr (PRO == kProX) {
-      return P.x[(size_t)n * P.x_stride + k] * sc;
-    } else {
-      const int h = k / P.dv;
-      const float w = P.onw ? P.onw[k - h * P.dv] : 1.0f;
-      const size_t g = (size_t)n * K + k;
-      return P.o[g] * scal[h] * w * P.gate[g];
+  // this thread's values: groups g8 = tid + 256 q, elements 8 g8 .. + 7
+  float v[KG][8];
+#pragma unroll
+  for (int q = 0; q < KG; ++q) {
+    const int k0 = 8 * (tid + kSkThreads * q);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (live) {
+        if constexpr (PRO == kProX) {
+          x = *reinterpret_cast<const float4*>(P.x + (size_t)n * P.x_stride + k0 + 4 * h2);
+        } else {
+          const int k = k0 + 4 * h2, hh = k / P.dv;
+          const size_t g = (size_t)n * K + k;
+          const float4 o = *reinterpret_cast<const float4*>(P.o + g);
+          const float4 gt = *reinterpret_cast<const float4*>(P.gate + g);
+          float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+          if (P.onw) w = *reinterpret_cast<const float4*>(P.onw + (k - hh * P.dv));
+          const float sc = scal[hh];
+          x = make_float4(o.x * sc * w.x * gt.x, o.y * sc * w.y * gt.y, o.z * sc * w.z * gt.z,
+                          o.w * sc * w.w * gt.w);
+        }
+      }
+      v[q][4 * h2] = x.x; v[q][4 * h2 + 1] = x.y; v[q][4 * h2 + 2] = x.z; v[q][4 * h2 + 3] = x.w;
     }
-  };
-  // power-of-two column scale: max |x| lands in [1024, 2048)
-  float amax = 0.0f;
-  for (int k = tid; k < K; k += kSkThreads) amax = fmaxf(amax, fabsf(value(k)));
-  {
-    // max over the block through the sum helpers' permutes is not available: use LDS
-    __shared__ float mx[kSkThreads];
-    mx[tid] = amax;
-    __syncthreads();
-    for (int s = kSkThreads / 2; s > 0; s >>= 1) {
-      if (tid < s) mx[tid] = fmaxf(mx[tid], mx[tid + s]);
-      __syncthreads();
-    }
-    amax = mx[0];
   }
+  // one reduction round: sum of squares (RMSNorm of x) and max |value|
+  float ssq = 0.0f, amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < KG; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ssq += v[q][e] * v[q][e];
+      amax = fmaxf(amax, fabsf(v[q][e]));
+    }
+  ssq = wave_sum(ssq);
+  amax = wave_max(amax);
+  if (lane == 0) { red[0][wave] = ssq; red[1][wave] = amax; }
+  __syncthreads();
+  float sc = 1.0f;
+  if (PRO == kProX && P.prenorm)
+    sc = 1.0f / sqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)K + P.eps);
+  amax = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3])) * sc;
+  // power-of-two column scale: max |x| lands in [1024, 2048)
   int e = 0;
   if (amax > 0.0f) frexpf(amax, &e);           // amax in [2^(e-1), 2^e)
-  const float up = ldexpf(1.0f, 11 - e);      // amax * up in [1024, 2048)
+  const float up = ldexpf(1.0f, 11 - e) * sc;
   if (tid == 0) S.cscale[n] = live && amax > 0.0f ? ldexpf(1.0f, e - 11) : 0.0f;
   const int ct = n >> 4, nl = n & 15;
-  // each thread: groups of 8 consecutive k (one 16-byte fragment piece)
-  for (int g8 = tid; g8 < K / 8; g8 += kSkThreads) {
-    const int k0 = g8 * 8, kb = k0 >> 5, g = (k0 >> 3) & 3;
+#pragma unroll
+  for (int q = 0; q < KG; ++q) {
+    const int k0 = 8 * (tid + kSkThreads * q), kb = k0 >> 5, g = (k0 >> 3) & 3;
     _Float16 hi[8], lo[8];
     float s = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float v = value(k0 + j) * up;
-      hi[j] = (_Float16)v;
+      const float x = v[q][j] * up;
+      hi[j] = (_Float16)x;
       const float hv = (float)hi[j];
-      lo[j] = (_Float16)(v - hv);
+      lo[j] = (_Float16)(x - hv);
       s += hv + (float)lo[j];
     }
     const size_t fi = ((size_t)kb * NT + ct) * 64 + nl + 16 * g;
     S.fh[fi] = make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
     S.fl[fi] = make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
-    // the four threads of a k block are consecutive (K / 8 per column, 4 per block)
+    // the four threads of a k block are consecutive lanes
     s = group_sum(s, 4);
     if (g == 0) S.xsum[(size_t)kb * NT * 16 + n] = s;
   }
@@ -181,14 +192,17 @@ __device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-template <int NT>
+// NT column tiles of 16; KB4 = K / 128 k blocks per wave.
+template <int NT, int KB4>
 __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
+  constexpr int KB = 4 * KB4;
+  constexpr int PD = 4;                          // k blocks of B fragments in flight
   __shared__ float part[4][NT][64][4];           // per-wave partial outputs
-  __shared__ __half s_sc[kSkKBMax * 4][kSkRows];  // [k block][row] Q8_0 scales
-  __shared__ float s_xs[kSkKBMax * 4][NT * 16];   // [k block][column] block sums
+  __shared__ __half s_sc[KB][kSkRows];           // [k block][row] Q8_0 scales
+  __shared__ float s_xs[KB][NT * 16];            // [k block][column] block sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int K = P.K, KB = K / 32, KB4 = KB / 4;
+  constexpr int K = KB * 32;
   // segment of this block
   SkSeg sg = P.seg[0];
 #pragma unroll
@@ -202,13 +216,26 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   const int ar = min(lane & 15, nrows - 1), ag = lane >> 4;
   const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K + 8 * ag;
   const int kb0 = wave * KB4;
-  uint2 a[kSkKBMax];
+  uint2 a[KB4];
 #pragma unroll
-  for (int j = 0; j < kSkKBMax; ++j)
-    if (j < KB4) {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32));
-      a[j] = make_uint2(v.x, v.y);
+  for (int j = 0; j < KB4; ++j) {
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32));
+    a[j] = make_uint2(v.x, v.y);
+  }
+  // B operand: a ring of PD k blocks of hi/lo fragments ahead of the MFMAs
+  const uint4* fh = P.S.fh + lane;
+  const uint4* fl = P.S.fl + lane;
+  uint4 bh[PD][NT], bl[PD][NT];
+  auto load_b = [&](int j, int slot) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const size_t fi = ((size_t)(kb0 + j) * NT + t) * 64;
+      bh[slot][t] = fh[fi];
+      bl[slot][t] = fl[fi];
     }
+  };
+#pragma unroll
+  for (int j = 0; j < PD && j < KB4; ++j) load_b(j, j);
   // scales [k block][row] and block sums into LDS
   for (int i = tid; i < KB * kSkRows; i += kSkThreads) {
     const int r = i / KB, kb = i - r * KB;
@@ -220,32 +247,32 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   f32x4v acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  const uint4* fh = P.S.fh + lane;
-  const uint4* fl = P.S.fl + lane;
   const int og = lane >> 4, oc = lane & 15;      // output rows 4 og .. + 3, column oc (+ 16 t)
 #pragma unroll
-  for (int j = 0; j < kSkKBMax; ++j) {
-    if (j < KB4) {
-      const int kb = kb0 + j;
-      const f16x8 av = bytes_to_f16(a[j]);
-      const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][4 * og]);
-      const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
-      const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
-      const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
-      const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+  for (int j = 0; j < KB4; ++j) {
+    const int kb = kb0 + j, slot = j % PD;
+    const f16x8 av = bytes_to_f16(a[j]);
+    const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][4 * og]);
+    const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
+    const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
+    const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
+    const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+    f32x4v o[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const size_t fi = ((size_t)kb * NT + t) * 64;
-        const f16x8 bh = __builtin_bit_cast(f16x8, fh[fi]);
-        const f16x8 bl = __builtin_bit_cast(f16x8, fl[fi]);
-        f32x4v o = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        o = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, o, 0, 0, 0);
-        const float bias = 1152.0f * s_xs[kb][t * 16 + oc];
-        acc[t][0] += d0 * (o[0] - bias);
-        acc[t][1] += d1 * (o[1] - bias);
-        acc[t][2] += d2 * (o[2] - bias);
-        acc[t][3] += d3 * (o[3] - bias);
-      }
+    for (int t = 0; t < NT; ++t) {
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bh[slot][t]),
+                                                    f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bl[slot][t]),
+                                                    o[t], 0, 0, 0);
+    }
+    if (j + PD < KB4) load_b(j + PD, slot);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float bias = 1152.0f * s_xs[kb][t * 16 + oc];
+      acc[t][0] += d0 * (o[t][0] - bias);
+      acc[t][1] += d1 * (o[t][1] - bias);
+      acc[t][2] += d2 * (o[t][2] - bias);
+      acc[t][3] += d3 * (o[t][3] - bias);
     }
   }
 #pragma unroll
@@ -301,18 +328,23 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.conv_w = g.conv_w;
   p.win = g.win;
   p.C = g.C;
-  if (prologue == kProX)
-    skinny_prep_kernel<kProX><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
-  else
-    skinny_prep_kernel<kProGatedNorm><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  const int KG = g.K / 2048;
+  if (prologue == kProX) {
+    if (KG == 2) skinny_prep_kernel<kProX, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+    else skinny_prep_kernel<kProX, 1><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  } else {
+    if (KG == 2) skinny_prep_kernel<kProGatedNorm, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+    else skinny_prep_kernel<kProGatedNorm, 1><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  switch (NT) {
-    case 1: skinny_gemm_kernel<1><<<tiles, kSkThreads, 0, s>>>(p); break;
-    case 2: skinny_gemm_kernel<2><<<tiles, kSkThreads, 0, s>>>(p); break;
-    case 3: skinny_gemm_kernel<3><<<tiles, kSkThreads, 0, s>>>(p); break;
-    default: skinny_gemm_kernel<4><<<tiles, kSkThreads, 0, s>>>(p); break;
-  }
+  const int KB4 = g.K / 128;
+#define KDA_SK_CASE(nt, kb4) \
+  if (NT == nt && KB4 == kb4) skinny_gemm_kernel<nt, kb4><<<tiles, kSkThreads, 0, s>>>(p);
+  KDA_SK_CASE(1, 8) KDA_SK_CASE(2, 8) KDA_SK_CASE(3, 8) KDA_SK_CASE(4, 8)
+  KDA_SK_CASE(1, 16) KDA_SK_CASE(2, 16) KDA_SK_CASE(3, 16) KDA_SK_CASE(4, 16)
+  KDA_SK_CASE(1, 32) KDA_SK_CASE(2, 32) KDA_SK_CASE(3, 32) KDA_SK_CASE(4, 32)
+#undef KDA_SK_CASE
   return hipGetLastError();
 }
 
