@@ -98,7 +98,7 @@ struct kda_model {
 
 // ---------------------------------------------------------------------------------------
 // Workspace layout (decode / verify): proj [N][proj_stride] | alpha,gate [N][K+V] |
-// o [N][V] | gate [N][V] | ss [N][H][V/kHeadColsConv]; each region 256-byte aligned.
+// o [N][V] | gate [N][V] | ss [N][H][V/kHeadCols]; each region 256-byte aligned.
 // Verify log per layer: proj rows [N][proj_stride] then alpha,gate [N][K+V].
 // ---------------------------------------------------------------------------------------
 namespace {
@@ -114,7 +114,7 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
   w.ag = off;   off = align_up(off + (size_t)N * (m->Kq + m->V) * 4, 256);
   w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
   w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
-  w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadColsConv) * 4, 256);
+  w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
   // MFMA column-fragment scratch of the skinny projections (Q8_0 with 9..64 columns)
   const int Kmax = std::max(m->d.d_model, m->V);
   w.sk = off;
@@ -230,9 +230,12 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
 }
 
 // One layer of decode (T = 1) or verify (T > 1): projections, gates, per-head step, o_proj.
+// Verify passes `act`: the projections stay pre-conv (they are logged for the commit's
+// window roll) and the activated q|k|v go to act; decode applies the conv in the
+// projection epilogue and rolls the window there.
 int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
-                  float* S, float* win, float* proj, float* ag, const WsLayout& wl, char* ws,
-                  bool write_state, hipStream_t s, bool rec) {
+                  float* S, float* win, float* proj, float* ag, float* act, const WsLayout& wl,
+                  char* ws, bool write_state, hipStream_t s, bool rec) {
   const kda_dims& d = m->d;
   const LayerDev& L = m->layers[l];
   const int N = B * T;
@@ -261,6 +264,12 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   });
   if (r) return r;
 
+  if (act) {
+    r = timed(m, KDA_K_PROJ, s, rec, [&] {
+      return launch_conv_seq(proj, m->proj_stride, win, L.conv_w, act, B, T, m->C, s);
+    });
+    if (r) return r;
+  }
   r = enqueue_gates(m, L, proj, N, ag, s, rec);
   if (r) return r;
 
@@ -269,8 +278,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
   hp.B = B; hp.T = T;
   hp.proj = proj; hp.proj_stride = m->proj_stride;
-  hp.conv_in_head = decode ? 0 : 1;
-  hp.win = win; hp.conv_w = L.conv_w;
+  hp.act = act;
   hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
   hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
   hp.alpha_gate = ag;
@@ -291,7 +299,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   po.K = m->V;
   po.N = N;
   po.o = o; po.gate = gate; po.ss = ss; po.onw = L.o_norm_w;
-  po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / head_cols(hp.conv_in_head != 0);
+  po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / kHeadCols;
   po.eps = d.norm_eps;
   po.out = y;
   po.out_stride = d.d_model;
@@ -317,7 +325,8 @@ int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, 
   for (int l = 0; l < m->d.n_layers; ++l) {
     const float* xin = (l == 0 || !m->d.prenorm_residual) ? x : y;
     int r = enqueue_layer(m, l, xin, y, B, 1, st->S_dev + l * state_layer_stride(m, B),
-                          st->conv_dev + l * win_layer_stride(m, B), proj, ag, wl, ws, true, s, rec);
+                          st->conv_dev + l * win_layer_stride(m, B), proj, ag, nullptr, wl, ws,
+                          true, s, rec);
     if (r) return r;
   }
   return KDA_OK;
@@ -652,7 +661,7 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
 
 size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T) {
   if (!m || batch < 1 || T < 1) return 0;
-  return (size_t)m->d.n_layers * batch * T * (m->proj_stride + m->Kq + m->V) * 4;
+  return (size_t)m->d.n_layers * batch * T * (m->proj_stride + m->Kq + m->V + m->C) * 4;
 }
 
 int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
@@ -671,14 +680,16 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
   float* logf = static_cast<float*>(log_dev);
+  // log per layer: pre-conv projections | alpha, gate | activated q, k, v
   const size_t log_proj = (size_t)B * T * m->proj_stride;
-  const size_t log_layer = (size_t)B * T * (m->proj_stride + m->Kq + m->V);
+  const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
+  const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
   for (int l = 0; l < m->d.n_layers; ++l) {
     const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
     float* lp = logf + l * log_layer;
     r = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
-                      st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj, wl, ws,
-                      false, s, m->timing);
+                      st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj,
+                      lp + log_proj + log_ag, wl, ws, false, s, m->timing);
     if (r) return r;
   }
   return KDA_OK;
@@ -695,7 +706,8 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
   const kda_dims& d = m->d;
   const float* logf = static_cast<const float*>(log_dev);
   const size_t log_proj = (size_t)B * T * m->proj_stride;
-  const size_t log_layer = (size_t)B * T * (m->proj_stride + m->Kq + m->V);
+  const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
+  const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerDev& L = m->layers[l];
     HeadParams hp;
@@ -704,9 +716,8 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
     hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
     hp.B = B; hp.T = T;
     hp.proj = logf + l * log_layer; hp.proj_stride = m->proj_stride;
-    hp.conv_in_head = 1;
+    hp.act = logf + l * log_layer + log_proj + log_ag;
     float* win = st->conv_dev + l * win_layer_stride(m, B);
-    hp.win = win; hp.conv_w = L.conv_w;
     hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
     hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
     hp.S = st->S_dev + l * state_layer_stride(m, B);

@@ -18,6 +18,8 @@
 
 namespace kda {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 template <int WT>
 struct HFmt;
 template <>
@@ -88,24 +90,24 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
   for (int n0 = 0; n0 < P.N; n0 += kGateCols) {
     const int nc = min(kGateCols, P.N - n0);
     {
-      // all loads first (a fixed, unrolled count per thread), then the LDS stores
+      // all loads first (a fixed, unrolled count per thread, indices clamped so no load
+      // sits behind a branch), then the LDS stores
       constexpr int kStage = kGateCols * 2 * kMaxRank / 4 / kGateThreads;
       const int per4 = 2 * rank / 4, total4 = nc * per4;
-      float4 v[kStage];
+      f32x4 v[kStage];
 #pragma unroll
       for (int u = 0; u < kStage; ++u) {
-        const int i = tid + u * kGateThreads;
-        if (i < total4) {
-          const int nn = i / per4, k4 = i - nn * per4;
-          v[u] = *reinterpret_cast<const float4*>(P.proj + (size_t)(n0 + nn) * P.proj_stride + P.C + 4 * k4);
-        }
+        const int i = min(tid + u * kGateThreads, total4 - 1);
+        const int nn = i / per4, k4 = i - nn * per4;
+        v[u] = *reinterpret_cast<const f32x4*>(P.proj + (size_t)(n0 + nn) * P.proj_stride + P.C + 4 * k4);
       }
+      __builtin_amdgcn_sched_barrier(0);   // keep the loads together, ahead of the stores
 #pragma unroll
       for (int u = 0; u < kStage; ++u) {
         const int i = tid + u * kGateThreads;
         if (i < total4) {
           const int nn = i / per4, k4 = i - nn * per4;
-          *reinterpret_cast<float4*>(&s_lr[nn][4 * k4]) = v[u];
+          *reinterpret_cast<f32x4*>(&s_lr[nn][4 * k4]) = v[u];
         }
       }
     }
@@ -170,8 +172,8 @@ bool head_supported(int dk, int wt, int rank_f, int rank_g) {
 // cq = lane / RG, RG = 256 / CW row groups) holds state rows rg*RPT .. rg*RPT + RPT - 1 of
 // columns 4cq .. 4cq + 3 of the wave's CW as float4s; column sums reduce over the row
 // groups (low lane bits) with DPP, the L2 norms over the same row groups.  No LDS, no
-// barrier.  Decode uses CW = 32; verify / commit, which also carry each lane's conv window
-// and taps over T tokens, use CW = 16 so that everything stays in registers.
+// barrier.  Tokens of a sequence (verify, commit) run in order, the next token's inputs
+// requested while the current one is computed.
 // ---------------------------------------------------------------------------------------
 template <int RG>
 __device__ __forceinline__ float rowsum(float v) {
@@ -179,7 +181,7 @@ __device__ __forceinline__ float rowsum(float v) {
   else return sum16(v);
 }
 
-template <int DK, int CW, bool CONV>
+template <int DK, int CW>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   constexpr int RG = 256 / CW;
   constexpr int RPT = DK / RG;
@@ -201,36 +203,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   for (int i = 0; i < RPT; ++i)
     st[i] = *reinterpret_cast<const float4*>(Sb + (size_t)(r0 + i) * dv);
 
-  // conv (verify / commit): window and taps of this lane's q, k rows and v columns
   const int cq0 = h * DK + r0, ck0 = K + h * DK + r0, cv0 = 2 * K + h * dv + j;
-  float zq[RPT][3], zk[RPT][3], zv[4][3];
-  float4 wq[RPT], wk[RPT], wv[4];
-  if constexpr (CONV) {
-    const float* zw = P.win + (size_t)b * 3 * C;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-#pragma unroll
-      for (int a = 0; a < 3; ++a) {
-        zq[i][a] = zw[(size_t)a * C + cq0 + i];
-        zk[i][a] = zw[(size_t)a * C + ck0 + i];
-      }
-      wq[i] = *reinterpret_cast<const float4*>(P.conv_w + (size_t)(cq0 + i) * 4);
-      wk[i] = *reinterpret_cast<const float4*>(P.conv_w + (size_t)(ck0 + i) * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int a = 0; a < 3; ++a) zv[i][a] = zw[(size_t)a * C + cv0 + i];
-      wv[i] = *reinterpret_cast<const float4*>(P.conv_w + (size_t)(cv0 + i) * 4);
-    }
-  }
-  auto conv = [](float (&z)[3], const float4 w, float p) {
-    const float y = w.x * z[0] + w.y * z[1] + w.z * z[2] + w.w * p;
-    z[0] = z[1];
-    z[1] = z[2];
-    z[2] = p;
-    return silu_f(y);
-  };
 
   // token inputs (q, k rows and v columns of this lane; alpha rows; gate columns; beta),
   // requested one token ahead of their use
@@ -242,17 +215,18 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   auto load_tok = [&](int t, Tok& x) {
     const int n = b * P.T + t;
     const float* prow = P.proj + (size_t)n * P.proj_stride;
+    const float* arow = P.act ? P.act + (size_t)n * C : prow;   // activated q | k | v
     const float* ag = P.alpha_gate + (size_t)n * (K + H * dv);
 #pragma unroll
     for (int i = 0; i < RPT; i += 4) {
-      const float4 a = *reinterpret_cast<const float4*>(prow + cq0 + i);
-      const float4 k4 = *reinterpret_cast<const float4*>(prow + ck0 + i);
+      const float4 a = *reinterpret_cast<const float4*>(arow + cq0 + i);
+      const float4 k4 = *reinterpret_cast<const float4*>(arow + ck0 + i);
       const float4 g4 = *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
       x.qv[i] = a.x; x.qv[i + 1] = a.y; x.qv[i + 2] = a.z; x.qv[i + 3] = a.w;
       x.kv[i] = k4.x; x.kv[i + 1] = k4.y; x.kv[i + 2] = k4.z; x.kv[i + 3] = k4.w;
       x.al[i] = g4.x; x.al[i + 1] = g4.y; x.al[i + 2] = g4.z; x.al[i + 3] = g4.w;
     }
-    const float4 a = *reinterpret_cast<const float4*>(prow + cv0);
+    const float4 a = *reinterpret_cast<const float4*>(arow + cv0);
     x.v4[0] = a.x; x.v4[1] = a.y; x.v4[2] = a.z; x.v4[3] = a.w;
     x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
     x.braw = prow[C + rl + h];
@@ -269,15 +243,6 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     float (&v4)[4] = cur.v4;
     const float4 gate = cur.gate;
     const float beta = sigmoid_f(cur.braw);
-    if constexpr (CONV) {
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        qv[i] = conv(zq[i], wq[i], qv[i]);
-        kv[i] = conv(zk[i], wk[i], kv[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v4[i] = conv(zv[i], wv[i], v4[i]);
-    }
     // L2 norms over the head's DK rows: local rows, then the 8 row groups
     float aq = 0.0f, ak = 0.0f;
 #pragma unroll
@@ -327,15 +292,44 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
 }
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
-  const int cw = head_cols(p.conv_in_head != 0);
-  dim3 grid(p.dv / cw, p.H, p.B);
-  if (p.conv_in_head) {
-    if (p.dk == 128) head_kernel<128, kHeadColsConv, true><<<grid, 64, 0, s>>>(p);
-    else head_kernel<64, kHeadColsConv, true><<<grid, 64, 0, s>>>(p);
-  } else {
-    if (p.dk == 128) head_kernel<128, kHeadCols, false><<<grid, 64, 0, s>>>(p);
-    else head_kernel<64, kHeadCols, false><<<grid, 64, 0, s>>>(p);
+  dim3 grid(p.dv / kHeadCols, p.H, p.B);
+  if (p.dk == 128)
+    head_kernel<128, kHeadCols><<<grid, 64, 0, s>>>(p);
+  else
+    head_kernel<64, kHeadCols><<<grid, 64, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+// Conv + SiLU over a sequence's T tokens, one thread per (channel, sequence); the window is
+// read, not rolled (verify leaves the state as committed).
+__global__ void conv_seq_kernel(const float* __restrict__ plog, int stride,
+                                const float* __restrict__ win, const float* __restrict__ conv_w,
+                                float* __restrict__ act, int T, int C) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  const int b = blockIdx.y;
+  if (c >= C) return;
+  const float* z = win + (size_t)b * 3 * C + c;
+  float z0 = z[0], z1 = z[C], z2 = z[2 * C];
+  const float4 w = *reinterpret_cast<const float4*>(conv_w + (size_t)c * 4);
+  float p[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) p[t] = plog[(size_t)(b * T + min(t, T - 1)) * stride + c];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    if (t < T) {
+      const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * p[t];
+      z0 = z1;
+      z1 = z2;
+      z2 = p[t];
+      act[(size_t)(b * T + t) * C + c] = silu_f(y);
+    }
   }
+}
+
+hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
+                           const float* conv_w, float* act, int B, int T, int C, hipStream_t s) {
+  dim3 grid((C + 255) / 256, B);
+  conv_seq_kernel<<<grid, 256, 0, s>>>(plog, proj_stride, win, conv_w, act, T, C);
   return hipGetLastError();
 }
 

@@ -84,17 +84,13 @@ int gemv_cols_per_pass(int N);
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
 // ---------------------------------------------------------------------------------------
 constexpr int kHeadCols = 32;      // value columns per wave (one partial sum of o^2 each)
-constexpr int kHeadColsConv = 16;  // the same with the conv in the head kernel (verify/commit)
-inline int head_cols(bool conv_in_head) { return conv_in_head ? kHeadColsConv : kHeadCols; }
 
 struct HeadParams {
   int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
   int B = 0, T = 0;               // sequences, tokens per sequence (column n = b*T + t)
   const float* proj = nullptr;    // [N][proj_stride]: a or p (C) | f_lr | g_lr | beta logits
   int proj_stride = 0;
-  int conv_in_head = 0;           // 1: proj holds pre-conv p; conv from win (read-only)
-  const float* win = nullptr;     // [B][3][C]
-  const float* conv_w = nullptr;  // [C][4]
+  const float* act = nullptr;     // [N][C] activated q|k|v when proj holds pre-conv p, else null
   int wt = 0;
   PackedMat fb, gb;               // [H*dk][rank_f], [H*dv][rank_g]
   const float* a_log = nullptr;
@@ -106,7 +102,7 @@ struct HeadParams {
   int write_out = 1;
   float* o = nullptr;             // [N][H*dv]
   float* gate = nullptr;          // [N][H*dv]
-  float* ss = nullptr;            // [N][H][dv/head_cols(conv_in_head)] partial sums of o^2
+  float* ss = nullptr;            // [N][H][dv/kHeadCols] partial sums of o^2
   float l2_eps = 0.f;
   float q_scale = 0.f;            // d_k^-1/2 as fp32
 };
@@ -128,6 +124,10 @@ hipError_t launch_gates(const GatesParams& p, hipStream_t s);
 bool head_supported(int dk, int wt, int rank_f, int rank_g);
 
 // New conv window after `ntok[b]` tokens: last 3 of (window, p_0 .. p_{T-1}).
+// Conv + SiLU over T tokens per sequence from the committed window (left unchanged):
+// act[b*T + t][c] from the pre-conv projections plog[b*T + t][c] (stride proj_stride).
+hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
+                           const float* conv_w, float* act, int B, int T, int C, hipStream_t s);
 hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,
                                 int C, const int* ntok, hipStream_t s);
 

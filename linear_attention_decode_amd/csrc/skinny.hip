@@ -199,7 +199,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   constexpr int PD = 4;                          // k blocks of B fragments in flight
   __shared__ float part[4][NT][64][4];           // per-wave partial outputs
   __shared__ __half s_sc[KB][kSkRows];           // [k block][row] Q8_0 scales
-  __shared__ float s_xs[KB][NT * 16];            // [k block][column] block sums
+  __shared__ __align__(16) float s_xs[KB][NT * 16];   // [k block][column] block sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int K = KB * 32;
@@ -211,6 +211,25 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   const int row0 = ((int)blockIdx.x - sg.first_tile) * kSkRows;
   const int nrows = min(kSkRows, sg.rows - row0);
 
+  // scales [k block][row] and block sums: loaded first (ahead of the weights in the
+  // in-order load counter), stored to LDS after the weight requests are out
+  // scales: row r's KB halves are contiguous; 8 per 16-byte load
+  constexpr int kScLoads = (KB * kSkRows / 8 + kSkThreads - 1) / kSkThreads;
+  u32x4 sv[kScLoads];
+#pragma unroll
+  for (int u = 0; u < kScLoads; ++u) {
+    const int i = min(tid + u * kSkThreads, KB * kSkRows / 8 - 1);
+    const int r = min(i / (KB / 8), nrows - 1), c8 = i % (KB / 8);
+    sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + r) * KB + 8 * c8);
+  }
+  constexpr int kXsLoads = (KB * NT * 4 + kSkThreads - 1) / kSkThreads;
+  f32x4v xv[kXsLoads];
+#pragma unroll
+  for (int u = 0; u < kXsLoads; ++u) {
+    const int i = min(tid + u * kSkThreads, KB * NT * 4 - 1);
+    xv[u] = reinterpret_cast<const f32x4v*>(P.S.xsum)[i];
+  }
+  __builtin_amdgcn_sched_barrier(0);
   // A operand: lane holds row (lane & 15), bytes 8 (lane >> 4) .. + 7 of each k block;
   // the wave's whole K range is requested up front
   const int ar = min(lane & 15, nrows - 1), ag = lane >> 4;
@@ -223,9 +242,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     a[j] = make_uint2(v.x, v.y);
   }
   // B operand: a ring of PD k blocks of hi/lo fragments ahead of the MFMAs
-  const uint4* fh = P.S.fh + lane;
-  const uint4* fl = P.S.fl + lane;
-  uint4 bh[PD][NT], bl[PD][NT];
+  const u32x4* fh = reinterpret_cast<const u32x4*>(P.S.fh) + lane;
+  const u32x4* fl = reinterpret_cast<const u32x4*>(P.S.fl) + lane;
+  u32x4 bh[PD][NT], bl[PD][NT];
   auto load_b = [&](int j, int slot) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -236,12 +255,27 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   };
 #pragma unroll
   for (int j = 0; j < PD && j < KB4; ++j) load_b(j, j);
-  // scales [k block][row] and block sums into LDS
-  for (int i = tid; i < KB * kSkRows; i += kSkThreads) {
-    const int r = i / KB, kb = i - r * KB;
-    s_sc[kb][r] = r < nrows ? sg.m.d[(size_t)(row0 + r) * KB + kb] : __float2half(0.0f);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+#pragma unroll
+    for (int u = 0; u < kScLoads; ++u) {
+      const int i = tid + u * kSkThreads;
+      if (i < KB * kSkRows / 8) {
+        const int r = i / (KB / 8), c8 = i % (KB / 8);
+        const uint32_t w[4] = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned short bits = (unsigned short)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+          s_sc[8 * c8 + e][r] = r < nrows ? __ushort_as_half(bits) : __float2half(0.0f);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kXsLoads; ++u) {
+      const int i = tid + u * kSkThreads;
+      if (i < KB * NT * 4) reinterpret_cast<f32x4v*>(&s_xs[0][0])[i] = xv[u];
+    }
   }
-  for (int i = tid; i < KB * NT * 16; i += kSkThreads) s_xs[i / (NT * 16)][i % (NT * 16)] = P.S.xsum[i];
   __syncthreads();
 
   f32x4v acc[NT];
