@@ -109,6 +109,7 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(const PrefillParams P)
   __shared__ float kT[DK * TP], qT[DK * TP], gT[DK * TP];
   __shared__ float s_beta[CS];
   __shared__ float Lm[CS * TP];
+  __shared__ float Xu[CS * DK];
 
   const int tid = threadIdx.x;
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -139,21 +140,24 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(const PrefillParams P)
   }
   __syncthreads();
 
-  // L and A: thread (t = tid % 64, s in a group of 16)
+  // L and A (causal: s <= t only): thread (t = tid % 64, s in a group of 16); a group
+  // entirely above the diagonal skips its channel loop
   {
     const int t = tid & (CS - 1), sg = tid / CS;
     float accL[16], accA[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) { accL[j] = 0.f; accA[j] = 0.f; }
-    for (int i = 0; i < DK; ++i) {
-      const float kt = kT[i * TP + t], qt = qT[i * TP + t], gt = gT[i * TP + t];
+    if (sg * 16 <= t) {
+      for (int i = 0; i < DK; ++i) {
+        const float kt = kT[i * TP + t], qt = qT[i * TP + t], gt = gT[i * TP + t];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const int s = sg * 16 + j;
-        const float e = exp2f(fminf(gt - gT[i * TP + s], 0.0f));
-        const float ks = kT[i * TP + s] * e;
-        accL[j] += kt * ks;
-        accA[j] += qt * ks;
+        for (int j = 0; j < 16; ++j) {
+          const int s = sg * 16 + j;
+          const float e = exp2f(fminf(gt - gT[i * TP + s], 0.0f));
+          const float ks = kT[i * TP + s] * e;
+          accL[j] += kt * ks;
+          accA[j] += qt * ks;
+        }
       }
     }
     float* Ag = P.A + chunk * CS * CS;
@@ -181,13 +185,13 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(const PrefillParams P)
   if (tid < DK) P.dec[chunk * DK + tid] = exp2f(gT[tid * TP + nt - 1]);
   __syncthreads();
 
-  // forward substitution (I + L) X = R, row by row, one right-hand-side column per thread;
-  // X lives in the (no longer needed) q tile.  Pass 0: R = beta exp(G) k -> W;
-  // pass 1: R = beta v -> U.
-  float* X = qT;                                   // [CS][DK]
-  for (int pass = 0; pass < 2; ++pass) {
-    const int col = tid;
-    if (col < DK) {
+  // forward substitution (I + L) X = R, row by row, one right-hand-side column per thread,
+  // both right-hand sides at once: threads [0, DK) solve R = beta exp(G) k -> W with X in the
+  // (no longer needed) q tile, threads [DK, 2 DK) solve R = beta v -> U with X in Xu.
+  {
+    const int pass = tid / DK, col = tid - pass * DK;
+    if (pass < 2) {
+      float* X = pass == 0 ? qT : Xu;                // [CS][DK]
       const float* vsrc = P.v + (bh * L + t0) * dv + col;
       for (int t = 0; t < CS; ++t) {
         float acc = 0.0f;
@@ -199,7 +203,6 @@ __global__ __launch_bounds__(256) void chunk_intra_kernel(const PrefillParams P)
       float* dst = (pass == 0 ? P.W : P.U) + chunk * CS * DK + col;
       for (int t = 0; t < CS; ++t) dst[(size_t)t * DK] = X[t * DK + col];
     }
-    __syncthreads();
   }
 }
 
