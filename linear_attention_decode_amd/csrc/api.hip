@@ -801,7 +801,7 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   p.l2_eps = d.l2_eps; p.q_scale = m->q_scale; p.norm_eps = d.norm_eps;
   p.q = F(wl.q); p.k = F(wl.k); p.v = F(wl.v); p.g2 = F(wl.g2); p.beta = F(wl.beta);
   p.gate = F(wl.gate);
-  p.W = F(wl.W); p.U = F(wl.U); p.Qt = F(wl.Qt); p.Kt = F(wl.Kt); p.A = F(wl.A); p.dec = F(wl.dec);
+  p.Wf = F(wl.W); p.Uf = F(wl.U); p.Qf = F(wl.Qt); p.Kf = F(wl.Kt); p.Af = F(wl.A); p.dec = F(wl.dec);
   p.S = st->S_dev; p.o = F(wl.o);
   // P2: conv + SiLU + L2 norms + gates over the sequence; then the final window
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_seq(p, s); });
@@ -809,9 +809,9 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_window(p, s); });
   if (r) return r;
   // P3 / P4: chunked delta rule
-  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_intra(p, s); });
+  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_prep(p, s); });
   if (r) return r;
-  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_inter(p, s); });
+  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_scan(p, s); });
   if (r) return r;
   // P5: gated RMSNorm, then the output projection (fp32 input as two BF16 terms)
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gated_norm(p, s); });

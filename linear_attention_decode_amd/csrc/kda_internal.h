@@ -185,7 +185,6 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
 
 constexpr int kChunk = 64;          // tokens per chunk of the chunked delta rule
-constexpr int kInterCols = 32;      // value columns per block of the inter-chunk kernel
 constexpr int kPrefillMaxChannels = 8192;  // conv channels + 2 heads' norms, sequence pass
 
 struct PrefillParams {
@@ -204,15 +203,18 @@ struct PrefillParams {
   // sequence-pass outputs, [B][H][L][dk|dv] and [B][H][L]
   float *q = nullptr, *k = nullptr, *v = nullptr, *g2 = nullptr, *beta = nullptr;
   float* gate = nullptr;          // [B*L][H*dv]
-  // intra-chunk outputs, per (b, h, chunk)
-  float *W = nullptr, *U = nullptr, *Qt = nullptr, *Kt = nullptr, *A = nullptr, *dec = nullptr;
+  // per-chunk preparation outputs, per (b, h, chunk), in matrix-core operand order: -W,
+  // q 2^G, (k 2^(G_last - G))^T and A as BF16 hi/lo fragments, U in accumulator order,
+  // dec = 2^G_last
+  void *Wf = nullptr, *Qf = nullptr, *Kf = nullptr, *Af = nullptr;
+  float *Uf = nullptr, *dec = nullptr;
   float* S = nullptr;             // [B][H][dk][dv] state, read then overwritten
   float* o = nullptr;             // [B*L][H*dv]: o, then the gated norm n in place
 };
 hipError_t launch_prefill_seq(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_window(const PrefillParams& p, hipStream_t s);
-hipError_t launch_chunk_intra(const PrefillParams& p, hipStream_t s);
-hipError_t launch_chunk_inter(const PrefillParams& p, hipStream_t s);
+hipError_t launch_chunk_prep(const PrefillParams& p, hipStream_t s);
+hipError_t launch_chunk_scan(const PrefillParams& p, hipStream_t s);
 hipError_t launch_gated_norm(const PrefillParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------

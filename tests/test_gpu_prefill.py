@@ -129,3 +129,22 @@ def test_prefill_full_size():
         e, se = _compare(y[b:b + 1], ry, S[b:b + 1], rS, Z[b:b + 1], rZ)
         _say(f"  seq {b}: out {e:.2e} state {se:.2e}")
     model.close()
+
+
+def test_prefill_strong_decay_blocks():
+    """Forget gates strong enough that a 16-token block's decay range passes 2^64 on some
+    channels (head 0: those diagonal blocks take the pairwise path) next to a head whose
+    blocks are factored with decay factors up to ~2^50 (head 1); 150 tokens (ragged)."""
+    import torch
+    w = _small(150, seed=63)
+    _say("prefill strong decay, 150 tokens, a_log = [3.0, 0.5]")
+    run = synth.draw_run(w)
+    run.layers[0]["a_log"] = np.array([3.0, 0.5], np.float32)
+    layer = oracle_layers(run)[0]
+    model = gpu_model(run)
+    st = model.new_state(w.batch)
+    st.S.copy_(torch.from_numpy(run.s0))
+    y = gpu_prefill(model, run.x[0], run.x_bits[0], st)
+    ry, rS, rZ = ok.prefill_run(layer, run.x[0], run.s0[0])
+    _compare(y, ry, st.S.cpu().numpy()[0], rS, st.conv.cpu().numpy()[0], rZ)
+    model.close()
