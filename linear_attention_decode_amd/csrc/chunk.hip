@@ -149,22 +149,34 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
   u32x4_t* Af = static_cast<u32x4_t*>(P.Af) + chunk * (4 * 2 * 2 * 64);
   f32x4_t* Uf = reinterpret_cast<f32x4_t*>(P.Uf) + chunk * ((DK / 16) * 4 * 64);
 
-  // ---- q, k and log2-decay rows of the chunk (rows past the sequence end are zero) ----
+  // ---- q, k and log2-decay rows of the chunk (rows past the sequence end are zero; their
+  //      loads read the last row, so every load is issued unconditionally) ----
   {
+    constexpr int NLD = CS * DK / 4 / 256;
     const size_t g0 = (bh * L + t0) * DK;
     const f32x4_t* gq = reinterpret_cast<const f32x4_t*>(P.q + g0);
     const f32x4_t* gk = reinterpret_cast<const f32x4_t*>(P.k + g0);
     const f32x4_t* gg = reinterpret_cast<const f32x4_t*>(P.g2 + g0);
-    for (int e = tid; e < CS * DK / 4; e += 256) {
-      const int t = e / (DK / 4), c4 = (e % (DK / 4)) * 4;
-      f32x4_t vq = {0.f, 0.f, 0.f, 0.f}, vk = vq, vg = vq;
-      if (t < nt) { vq = gq[e]; vk = gk[e]; vg = gg[e]; }
-      *reinterpret_cast<f32x4_t*>(sQ + t * RS + c4) = vq;
-      *reinterpret_cast<f32x4_t*>(sK + t * RS + c4) = vk;
-      *reinterpret_cast<f32x4_t*>(sG + t * RS + c4) = vg;
+    f32x4_t vq[NLD], vk[NLD], vg[NLD];
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int t = e / (DK / 4), c4 = e % (DK / 4);
+      const int src = min(t, nt - 1) * (DK / 4) + c4;
+      vq[u] = gq[src]; vk[u] = gk[src]; vg[u] = gg[src];
     }
     if (tid < CS) sBeta[tid] = tid < nt ? P.beta[bh * L + t0 + tid] : 0.0f;
     if (tid < NB) sFlag[tid] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int e = tid + 256 * u;
+      const int t = e / (DK / 4), c4 = (e % (DK / 4)) * 4;
+      const bool live = t < nt;
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4_t*>(sQ + t * RS + c4) = live ? vq[u] : z;
+      *reinterpret_cast<f32x4_t*>(sK + t * RS + c4) = live ? vk[u] : z;
+      *reinterpret_cast<f32x4_t*>(sG + t * RS + c4) = live ? vg[u] : z;
+    }
   }
   __syncthreads();
 
@@ -330,15 +342,18 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
 
   // ---- beta v^T over the dead q and A tiles: lane = token, 4 value columns per load ----
   {
+    constexpr int NLD = DK / 16;
     const float* gv = P.v + (bh * L + t0) * DK;
     const int t = lane;
-    const float bt = sBeta[t];
-    for (int j4 = wave; j4 < DK / 4; j4 += 4) {
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      if (t < nt) v = *reinterpret_cast<const f32x4_t*>(gv + (size_t)t * DK + 4 * j4);
+    const float bt = sBeta[t];          // zero past the sequence end
+    f32x4_t v[NLD];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) sVT[(4 * j4 + u) * AS + t] = bt * v[u];
-    }
+    for (int u = 0; u < NLD; ++u)
+      v[u] = *reinterpret_cast<const f32x4_t*>(gv + (size_t)min(t, nt - 1) * DK + 4 * (wave + 4 * u));
+#pragma unroll
+    for (int u = 0; u < NLD; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sVT[(4 * (wave + 4 * u) + e) * AS + t] = bt * v[u][e];
   }
   // ---- off-diagonal blocks of T, one block diagonal at a time:
   //      T_IJ = -T_II sum_{K=J}^{I-1} L_IK T_KJ ----
@@ -431,48 +446,183 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
 }
 
 // ---------------------------------------------------------------------------------------
-// Scan over the chunks of one (sequence, head) for 16 value columns: one wave, the state
-// columns in MFMA accumulators for the whole sequence.
+// Scan over the chunks of one (sequence, head): a block of two waves owns 32 value columns
+// (16 per wave) and keeps those state columns in MFMA accumulators for the whole sequence.
+// Each chunk's operands stream through LDS in four segments, shared by both waves:
+//   0: -W              D = -W S
+//   1: q 2^G           O = (q 2^G) S
+//   2: A | U | dec     D += U, O += A D (then stored), S <- diag(dec) S
+//   3: Kt^T            S += Kt^T D
+// Segment n lands in slot n % 4 by direct global->LDS loads issued three segments ahead,
+// so each load has three compute phases to arrive.  Every wave issues the same number of
+// loads per segment, so a wait for "at most the loads of the next two segments
+// outstanding" (vector memory operations retire in order) means the segment about to be
+// read has landed; the barrier that follows makes that true for both waves' loads.
 // ---------------------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(64) void chunk_scan_kernel(const PrefillParams P) {
-  constexpr int KS = D / 32, MTI = D / 16, NJ = D / 16;
-  const int lane = threadIdx.x, q4 = lane >> 4, r16 = lane & 15;
-  // the value tiles of one (sequence, head) on one XCD (blocks go round-robin over 8)
-  const int ng = P.B * P.H, id = blockIdx.x;
-  int g, nj;
-  if ((ng & 7) == 0) {
-    const int slot = id >> 3;
-    nj = slot % NJ;
-    g = (slot / NJ) * 8 + (id & 7);
+struct ScanSeg {
+  static constexpr int KS = D / 32, MTI = D / 16, NJ = D / 16;
+  static constexpr int FW = 4 * KS * 2 * 64;        // 16-byte entries of -W (and of q 2^G)
+  static constexpr int FK = MTI * 2 * 2 * 64;       // Kt^T
+  static constexpr int FA = 4 * 2 * 2 * 64;         // A
+  static constexpr int FU = 2 * 4 * 64;             // U, the block's two value tiles
+  static constexpr int FD = D / 4;                  // dec
+  static constexpr int S2 = FA + FU + FD;
+  static constexpr int SLOT = FW > FK ? (FW > S2 ? FW : S2) : (FK > S2 ? FK : S2);
+  // loads per wave (= per lane) of each segment
+  static constexpr int NLD[4] = {FW / 128, FW / 128, FA / 128 + FU / 128 + 1, FK / 128};
+  static_assert(FW % 128 == 0 && FK % 128 == 0 && FA % 128 == 0 && FU % 128 == 0 && FD <= 128,
+                "segment pieces are whole rounds of 128 loads");
+  static_assert(4 * SLOT * 16 <= 160 * 1024, "LDS");
+};
+
+struct ScanSrc {
+  const u32x4_t *W, *Q, *K, *A, *U, *D;
+};
+
+// One 16-byte load per active lane straight into LDS: the lanes of the wave fill
+// consecutive entries from lds_wave_base.  Issued as inline assembly so that the compiler
+// does not track it: the explicit waits below carry the ordering (nothing else in these
+// kernels uses m0).
+__device__ __forceinline__ void dma16(const u32x4_t* src, u32x4_t* lds_wave_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
+}
+
+template <int D, int SEG>
+__device__ __forceinline__ void scan_issue(const ScanSrc& g, size_t c, u32x4_t* slot, int tid,
+                                           int lane, int wave) {
+  using Sg = ScanSeg<D>;
+  if constexpr (SEG == 0 || SEG == 1) {
+    const u32x4_t* src = (SEG == 0 ? g.W : g.Q) + c * Sg::FW + tid;
+#pragma unroll
+    for (int u = 0; u < Sg::FW / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * wave);
+  } else if constexpr (SEG == 2) {
+    const u32x4_t* sa = g.A + c * Sg::FA + tid;
+#pragma unroll
+    for (int u = 0; u < Sg::FA / 128; ++u) dma16(sa + 128 * u, slot + 128 * u + 64 * wave);
+    const u32x4_t* su = g.U + c * (Sg::NJ * 4 * 64) + tid;
+#pragma unroll
+    for (int u = 0; u < Sg::FU / 128; ++u) dma16(su + 128 * u, slot + Sg::FA + 128 * u + 64 * wave);
+    if (lane < Sg::FD / 2)
+      dma16(g.D + c * Sg::FD + wave * (Sg::FD / 2) + lane, slot + Sg::FA + Sg::FU + wave * (Sg::FD / 2));
   } else {
-    g = id / NJ;
-    nj = id % NJ;
+    const u32x4_t* src = g.K + c * Sg::FK + tid;
+#pragma unroll
+    for (int u = 0; u < Sg::FK / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * wave);
+  }
+}
+
+// wait until at most N vector memory operations of this wave are outstanding and all of
+// its LDS operations are done
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
+
+// acc[mt] += sum_p F(mt, p) B[p] for the four token tiles mt, fragment mt * KS + p of the
+// slot; the fragments of step p + 1 are read while step p runs on the matrix cores.
+template <int KS>
+__device__ __forceinline__ void row_tiles_times(const u32x4_t* slot, const Frag (&B)[KS],
+                                                f32x4_t (&acc)[4], int lane) {
+  Frag cur[4], nxt[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) cur[mt] = load_frag(slot, mt * KS, lane);
+#pragma unroll
+  for (int p = 0; p < KS; ++p) {
+    if (p + 1 < KS) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) nxt[mt] = load_frag(slot, mt * KS + p + 1, lane);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = mma3(cur[mt], B[p], acc[mt]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) cur[mt] = nxt[mt];
+  }
+}
+
+// S[mt] += sum_p F(mt, p) B[p] for the MTI key tiles, fragment mt * 2 + p of the slot, two
+// key tiles per step, the next step's fragments read ahead.
+template <int MTI>
+__device__ __forceinline__ void key_tiles_times(const u32x4_t* slot, const Frag (&B)[2],
+                                                f32x4_t (&S)[MTI], int lane) {
+  Frag cur[4], nxt[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) cur[i] = load_frag(slot, i, lane);
+#pragma unroll
+  for (int m2 = 0; m2 < MTI / 2; ++m2) {
+    if (m2 + 1 < MTI / 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nxt[i] = load_frag(slot, 4 * (m2 + 1) + i, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) S[2 * m2 + (i >> 1)] = mma3(cur[i], B[i & 1], S[2 * m2 + (i >> 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cur[i] = nxt[i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) {
+  using Sg = ScanSeg<D>;
+  constexpr int KS = Sg::KS, MTI = Sg::MTI, NJ2 = Sg::NJ / 2;
+  __shared__ u32x4_t slot0[Sg::SLOT];
+  __shared__ u32x4_t slot1[Sg::SLOT];
+  __shared__ u32x4_t slot2[Sg::SLOT];
+  __shared__ u32x4_t slot3[Sg::SLOT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  // the blocks of one (sequence, head) on one XCD (blocks go round-robin over 8)
+  const int ng = P.B * P.H, id = blockIdx.x;
+  int g, nj2;
+  if ((ng & 7) == 0) {
+    const int sl = id >> 3;
+    nj2 = sl % NJ2;
+    g = (sl / NJ2) * 8 + (id & 7);
+  } else {
+    g = id / NJ2;
+    nj2 = id % NJ2;
   }
   const int b = g / P.H, h = g - b * P.H;
-  const int j = 16 * nj + r16;
-  float* Sg = P.S + (size_t)g * D * D;
+  const int j = 16 * (2 * nj2 + wave) + r16;
+  float* Sgl = P.S + (size_t)g * D * D;
+  const int nch = P.nch;
+  const size_t gc = (size_t)g * nch;
+
+  ScanSrc src;
+  src.W = static_cast<const u32x4_t*>(P.Wf) + gc * Sg::FW;
+  src.Q = static_cast<const u32x4_t*>(P.Qf) + gc * Sg::FW;
+  src.K = static_cast<const u32x4_t*>(P.Kf) + gc * Sg::FK;
+  src.A = static_cast<const u32x4_t*>(P.Af) + gc * Sg::FA;
+  src.U = reinterpret_cast<const u32x4_t*>(P.Uf) + gc * (Sg::NJ * 4 * 64) + nj2 * Sg::FU;
+  src.D = reinterpret_cast<const u32x4_t*>(P.dec) + gc * Sg::FD;
 
   f32x4_t S[MTI];
 #pragma unroll
   for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) S[mt][r] = Sg[(size_t)(16 * mt + 4 * q4 + r) * D + j];
+    for (int r = 0; r < 4; ++r) S[mt][r] = Sgl[(size_t)(16 * mt + 4 * q4 + r) * D + j];
+
+  // the first chunk's four segments
+  scan_issue<D, 0>(src, 0, slot0, tid, lane, wave);
+  scan_issue<D, 1>(src, 0, slot1, tid, lane, wave);
+  scan_issue<D, 2>(src, 0, slot2, tid, lane, wave);
+  scan_issue<D, 3>(src, 0, slot3, tid, lane, wave);
+  wait_vm_lgkm0<Sg::NLD[1] + Sg::NLD[2] + Sg::NLD[3]>();
+  block_barrier();
 
   const size_t orow = (size_t)P.H * D;
+  f32x4_t Dm[4], Om[4];
+  Frag sf[KS], df[2];
 #pragma unroll 1
-  for (int c = 0; c < P.nch; ++c) {
-    const size_t chunk = (size_t)g * P.nch + c;
-    const u32x4_t* Wf = static_cast<const u32x4_t*>(P.Wf) + chunk * (4 * KS * 2 * 64);
-    const u32x4_t* Qf = static_cast<const u32x4_t*>(P.Qf) + chunk * (4 * KS * 2 * 64);
-    const u32x4_t* Kf = static_cast<const u32x4_t*>(P.Kf) + chunk * (MTI * 2 * 2 * 64);
-    const u32x4_t* Af = static_cast<const u32x4_t*>(P.Af) + chunk * (4 * 2 * 2 * 64);
-    const f32x4_t* Uf = reinterpret_cast<const f32x4_t*>(P.Uf) + chunk * (NJ * 4 * 64) + nj * 4 * 64;
-    const f32x4_t* dec4 = reinterpret_cast<const f32x4_t*>(P.dec + chunk * D);
-    const int t0 = c * CS, nt = min(CS, P.L - t0);
-
-    // state columns as B operands: k = key channel in the permuted order
-    Frag sf[KS];
+  for (int c = 0; c < nch; ++c) {
+    const bool more = c + 1 < nch;
+    // ---- segment 0: D = -W S (state columns as B operands, k = key channel permuted) ----
 #pragma unroll
     for (int p = 0; p < KS; ++p) {
       float x[8];
@@ -480,56 +630,76 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(const PrefillParams P) {
       for (int r = 0; r < 4; ++r) { x[r] = S[2 * p][r]; x[4 + r] = S[2 * p + 1][r]; }
       sf[p] = split8(x);
     }
-    // D = U - W S and O = (q 2^G) S
-    f32x4_t Dm[4], Om[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      Dm[mt] = Uf[mt * 64 + lane];
-      Om[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int mt = 0; mt < 4; ++mt) Dm[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    row_tiles_times<KS>(slot0, sf, Dm, lane);
+    // segment 1 must have landed; segments 2, 3 may still be in flight
+    wait_vm_lgkm0<Sg::NLD[2] + Sg::NLD[3]>();
+    block_barrier();
+    if (more) scan_issue<D, 0>(src, c + 1, slot0, tid, lane, wave);
+    // ---- segment 1: O = (q 2^G) S ----
 #pragma unroll
-    for (int p = 0; p < KS; ++p)
+    for (int mt = 0; mt < 4; ++mt) Om[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    row_tiles_times<KS>(slot1, sf, Om, lane);
+    if (more) wait_vm_lgkm0<Sg::NLD[3] + Sg::NLD[0]>();
+    else wait_vm_lgkm0<Sg::NLD[3]>();
+    block_barrier();
+    if (more) scan_issue<D, 1>(src, c + 1, slot1, tid, lane, wave);
+    // ---- segment 2: D += U; O += A D; S <- diag(dec) S ----
+    {
+      const f32x4_t* sU = reinterpret_cast<const f32x4_t*>(slot2 + Sg::FA) + wave * 4 * 64;
+      const f32x4_t* sD = reinterpret_cast<const f32x4_t*>(slot2 + Sg::FA + Sg::FU);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        Dm[mt] = mma3(load_frag(Wf, mt * KS + p, lane), sf[p], Dm[mt]);
-        Om[mt] = mma3(load_frag(Qf, mt * KS + p, lane), sf[p], Om[mt]);
+      for (int mt = 0; mt < 4; ++mt) Dm[mt] += sU[mt * 64 + lane];
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float x[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { x[r] = Dm[2 * p][r]; x[4 + r] = Dm[2 * p + 1][r]; }
+        df[p] = split8(x);
       }
-    // D as B operands: k = token in the permuted order
-    Frag df[2];
+      {
+        Frag fa[6];
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      float x[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) { x[r] = Dm[2 * p][r]; x[4 + r] = Dm[2 * p + 1][r]; }
-      df[p] = split8(x);
-    }
-    // O += A D (A is zero above the diagonal: token tiles 0, 1 need only s < 32)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        if (p <= mt / 2) Om[mt] = mma3(load_frag(Af, mt * 2 + p, lane), df[p], Om[mt]);
-    // S <- diag(2^G_last) S + (k 2^(G_last - G))^T D
-#pragma unroll
-    for (int mt = 0; mt < MTI; ++mt) {
-      const f32x4_t dd = dec4[4 * mt + q4];
-      S[mt] = S[mt] * dd;
-#pragma unroll
-      for (int p = 0; p < 2; ++p) S[mt] = mma3(load_frag(Kf, mt * 2 + p, lane), df[p], S[mt]);
-    }
-    float* og = P.o + ((size_t)b * P.L + t0) * orow + (size_t)h * D + j;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * mt + 4 * q4 + r;
-        if (t < nt) og[(size_t)t * orow] = Om[mt][r];
+        for (int i = 0; i < 6; ++i) fa[i] = load_frag(slot2, i < 2 ? 2 * i : i + 2, lane);
+        // (mt, p) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1): fragment mt * 2 + p
+        Om[0] = mma3(fa[0], df[0], Om[0]);
+        Om[1] = mma3(fa[1], df[0], Om[1]);
+        Om[2] = mma3(fa[2], df[0], Om[2]);
+        Om[2] = mma3(fa[3], df[1], Om[2]);
+        Om[3] = mma3(fa[4], df[0], Om[3]);
+        Om[3] = mma3(fa[5], df[1], Om[3]);
       }
+#pragma unroll
+      for (int mt = 0; mt < MTI; ++mt) S[mt] = S[mt] * sD[4 * mt + q4];
+    }
+    if (more) wait_vm_lgkm0<Sg::NLD[0] + Sg::NLD[1]>();
+    else wait_vm_lgkm0<0>();
+    block_barrier();
+    if (more) scan_issue<D, 2>(src, c + 1, slot2, tid, lane, wave);
+    {
+      const int t0 = c * CS, nt = min(CS, P.L - t0);
+      float* og = P.o + ((size_t)b * P.L + t0) * orow + (size_t)h * D + j;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * mt + 4 * q4 + r;
+          if (t < nt) og[(size_t)t * orow] = Om[mt][r];
+        }
+    }
+    // ---- segment 3: S += (k 2^(G_last - G))^T D ----
+    key_tiles_times<MTI>(slot3, df, S, lane);
+    if (more) {
+      wait_vm_lgkm0<Sg::NLD[1] + Sg::NLD[2]>();
+      block_barrier();
+      scan_issue<D, 3>(src, c + 1, slot3, tid, lane, wave);
+    }
   }
 #pragma unroll
   for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) Sg[(size_t)(16 * mt + 4 * q4 + r) * D + j] = S[mt][r];
+    for (int r = 0; r < 4; ++r) Sgl[(size_t)(16 * mt + 4 * q4 + r) * D + j] = S[mt][r];
 }
 
 }  // namespace
@@ -544,11 +714,11 @@ hipError_t launch_chunk_prep(const PrefillParams& p, hipStream_t s) {
 }
 
 hipError_t launch_chunk_scan(const PrefillParams& p, hipStream_t s) {
-  const int blocks = p.B * p.H * (p.dk / 16);
+  const int blocks = p.B * p.H * (p.dk / 32);
   if (p.dk == 128)
-    chunk_scan_kernel<128><<<blocks, 64, 0, s>>>(p);
+    chunk_scan_kernel<128><<<blocks, 128, 0, s>>>(p);
   else
-    chunk_scan_kernel<64><<<blocks, 64, 0, s>>>(p);
+    chunk_scan_kernel<64><<<blocks, 128, 0, s>>>(p);
   return hipGetLastError();
 }
 
