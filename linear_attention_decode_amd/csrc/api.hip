@@ -126,8 +126,7 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
 
 // Workspace layout (prefill, M = B*L tokens, NC = B*H*nch chunks).
 struct PfLayout {
-  size_t P = 0, FG = 0, q = 0, k = 0, v = 0, g2 = 0, beta = 0, gate = 0, W = 0, U = 0, Qt = 0,
-         Kt = 0, A = 0, dec = 0, o = 0, total = 0;
+  size_t P = 0, xs = 0, W = 0, U = 0, Qt = 0, Kt = 0, A = 0, dec = 0, o = 0, on = 0, total = 0;
 };
 
 PfLayout pf_layout(const kda_model* m, int64_t B, int64_t L) {
@@ -138,13 +137,7 @@ PfLayout pf_layout(const kda_model* m, int64_t B, int64_t L) {
   size_t off = 0;
   auto take = [&](size_t& dst, int64_t floats) { dst = off; off = align_up(off + (size_t)floats * 4, 256); };
   take(w.P, M * m->proj_stride);
-  take(w.FG, M * (K + V));
-  take(w.q, M * K);
-  take(w.k, M * K);
-  take(w.v, M * V);
-  take(w.g2, M * K);
-  take(w.beta, M * d.n_heads);
-  take(w.gate, M * V);
+  take(w.xs, M * d.d_model);          // fp32 x as two BF16 planes (F32 input only)
   take(w.W, NC * kChunk * d.d_k);
   take(w.U, NC * kChunk * d.d_v);
   take(w.Qt, NC * kChunk * d.d_k);
@@ -152,6 +145,7 @@ PfLayout pf_layout(const kda_model* m, int64_t B, int64_t L) {
   take(w.A, NC * kChunk * kChunk);
   take(w.dec, NC * d.d_k);
   take(w.o, M * V);
+  take(w.on, M * V);                  // gated norm as two BF16 planes
   w.total = off;
   return w;
 }
@@ -746,10 +740,9 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   if (x_dtype != KDA_BF16 && x_dtype != KDA_F32) return fail(KDA_E_DTYPE, "x must be BF16 or F32");
   if (chunk != kChunk) return fail(KDA_E_SHAPE, "chunk must be %d", kChunk);
   if (L < 1 || L > (1 << 30)) return fail(KDA_E_SHAPE, "L must be >= 1");
-  if (d.d_model % 64 || d.rank_f % 64 || d.rank_g % 64 || m->V % 64)
-    return fail(KDA_E_SHAPE, "prefill GEMMs need d_model, ranks and H*d_v multiples of 64");
-  if (m->C + 2 * d.n_heads > kPrefillMaxChannels)
-    return fail(KDA_E_SHAPE, "too many conv channels for the sequence pass");
+  if (d.d_model % 64 || d.rank_g % 64 || m->V % 64)
+    return fail(KDA_E_SHAPE, "prefill GEMMs need d_model, rank_g and H*d_v multiples of 64");
+  if (d.rank_f != 64 && d.rank_f != 128) return fail(KDA_E_SHAPE, "chunked prefill needs rank_f 64 or 128");
   if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(ws_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
   const int B = st->batch;
   const PfLayout wl = pf_layout(m, B, L);
@@ -763,7 +756,19 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
 
   // P1: fused input projections [q|k|v|f_a|g_a|beta] on matrix cores
   GemmParams g;
-  g.A = x_dev; g.lda = d.d_model; g.split_a = x_dtype == KDA_F32;
+  auto U16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(ws + off); };
+  if (x_dtype == KDA_F32) {
+    uint16_t* xh = U16(wl.xs);
+    uint16_t* xl = xh + (size_t)M * d.d_model;
+    r = timed(m, KDA_K_GEMM, s, rec, [&] {
+      return launch_split_planes(static_cast<const float*>(x_dev), xh, xl, M * d.d_model, s);
+    });
+    if (r) return r;
+    g.A = xh; g.A2 = xl;
+  } else {
+    g.A = static_cast<const uint16_t*>(x_dev);
+  }
+  g.lda = d.d_model;
   const PackedMat mats[6] = {Ly.wq, Ly.wk, Ly.wv, Ly.fa, Ly.ga, Ly.wbeta};
   const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
   int first = 0;
@@ -776,48 +781,32 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   g.C = F(wl.P); g.ldc = m->proj_stride; g.coff = 0;
   r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(g, s); });
   if (r) return r;
-  // low-rank up-projections F_b f_lr and G_b g_lr (fp32 inputs as two BF16 terms)
-  GemmParams gf;
-  gf.A = F(wl.P) + m->C; gf.lda = m->proj_stride; gf.split_a = 1;
-  gf.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.fb.w); gf.nseg = 1;
-  gf.M = (int)M; gf.N = m->Kq; gf.K = d.rank_f;
-  gf.C = F(wl.FG); gf.ldc = m->Kq + m->V; gf.coff = 0;
-  r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(gf, s); });
-  if (r) return r;
-  GemmParams gg = gf;
-  gg.A = F(wl.P) + m->C + d.rank_f;
-  gg.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.gb.w);
-  gg.N = m->V; gg.K = d.rank_g; gg.coff = m->Kq;
-  r = timed(m, KDA_K_GEMM, s, rec, [&] { return launch_gemm(gg, s); });
-  if (r) return r;
-
   PrefillParams p;
   p.B = B; p.L = (int)L; p.H = d.n_heads; p.dk = d.d_k; p.dv = d.d_v; p.C = m->C;
   p.rank_f = d.rank_f; p.rank_g = d.rank_g;
   p.nch = (int)((L + kChunk - 1) / kChunk);
-  p.P = F(wl.P); p.proj_stride = m->proj_stride; p.FG = F(wl.FG);
+  p.P = F(wl.P); p.proj_stride = m->proj_stride;
   p.win = st->conv_dev; p.win_out = st->conv_dev;
   p.conv_w = Ly.conv_w; p.a_log = Ly.a_log; p.dt_bias = Ly.dt_bias; p.onw = Ly.o_norm_w;
+  p.Fb = reinterpret_cast<const uint16_t*>(Ly.fb.w);
+  p.Gb = reinterpret_cast<const uint16_t*>(Ly.gb.w);
   p.l2_eps = d.l2_eps; p.q_scale = m->q_scale; p.norm_eps = d.norm_eps;
-  p.q = F(wl.q); p.k = F(wl.k); p.v = F(wl.v); p.g2 = F(wl.g2); p.beta = F(wl.beta);
-  p.gate = F(wl.gate);
   p.Wf = F(wl.W); p.Uf = F(wl.U); p.Qf = F(wl.Qt); p.Kf = F(wl.Kt); p.Af = F(wl.A); p.dec = F(wl.dec);
   p.S = st->S_dev; p.o = F(wl.o);
-  // P2: conv + SiLU + L2 norms + gates over the sequence; then the final window
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_seq(p, s); });
+  p.on_hi = U16(wl.on); p.on_lo = p.on_hi + (size_t)M * m->V;
+  // P2 / P3: conv + SiLU, norms, gates and the WY/UT form per chunk; the final window
+  // (after the preparation, which reads the initial one); P4: the scan over chunks
+  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_prep(p, s); });
   if (r) return r;
   r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_prefill_window(p, s); });
   if (r) return r;
-  // P3 / P4: chunked delta rule
-  r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_prep(p, s); });
-  if (r) return r;
   r = timed(m, KDA_K_CHUNK, s, rec, [&] { return launch_chunk_scan(p, s); });
   if (r) return r;
-  // P5: gated RMSNorm, then the output projection (fp32 input as two BF16 terms)
-  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_gated_norm(p, s); });
+  // P5: gated RMSNorm (as BF16 hi/lo planes), then the output projection over both planes
+  r = timed(m, KDA_K_PREFILL, s, rec, [&] { return launch_chunk_gnorm(p, s); });
   if (r) return r;
   GemmParams go;
-  go.A = F(wl.o); go.lda = m->V; go.split_a = 1;
+  go.A = p.on_hi; go.A2 = p.on_lo; go.lda = m->V;
   go.seg_b[0] = reinterpret_cast<const uint16_t*>(Ly.wo.w); go.nseg = 1;
   go.M = (int)M; go.N = d.d_model; go.K = m->V;
   go.C = y_dev; go.ldc = d.d_model; go.coff = 0;

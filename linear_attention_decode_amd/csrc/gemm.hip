@@ -1,159 +1,181 @@
-// Dense GEMM on gfx950 matrix cores for the chunked prefill:
-//   C[m][coff + n] = sum_k A[m][k] * B[n][k]          (A: [M][lda], B rows: [N][K])
-// B is BF16 (the packed projection weights), possibly several matrices stacked along n
-// (a segment table, like the decode GEMV).  A is BF16, or FP32 split into two BF16 terms
-// a = hi + lo (hi = a with the low 16 bits cleared, lo = bf16(a - hi)) so that products
-// keep ~16 significant bits: C = A_hi B + A_lo B, both on MFMA with fp32 accumulation.
+// Dense GEMM on gfx950 matrix cores for the chunked prefill's projections:
+//   C[m][coff + n] = sum_k A[m][k] B[n][k]      (A: BF16 [M][lda], B rows: BF16 [N][K])
+// B may be several matrices stacked along n (a segment table).  An fp32 operand is passed
+// as two BF16 planes A = A_hi + A_lo (hi = bf16(a), lo = bf16(a - hi)); the k loop then
+// runs over both planes against the same B, i.e. C = A_hi B^T + A_lo B^T, every product
+// exact in fp32 accumulation.
 //
-// Tile 128 x 128 x 64 per block of 4 waves (2 x 2 waves of 64 x 64), v_mfma_f32_16x16x32_bf16
-// with the gfx950 operand layout: lane l holds row (l % 16) of A and column (l % 16) of B,
-// k = 8 (l / 16) .. 8 (l / 16) + 7; the 4 accumulators of lane l are rows 4 (l / 16) + r,
-// column l % 16.  LDS rows are padded by 16 bytes.
+// Block tile 256 x 256 x 32, 8 waves as 2 (m) x 4 (n), each 128 x 64 = 8 x 4 tiles of
+// v_mfma_f32_16x16x32_bf16 (lane l: row l % 16 of A and of B^T, k = 8 (l / 16) .. + 7;
+// accumulator rows 4 (l / 16) + r, column l % 16).  Operand tiles stream through a
+// four-stage LDS ring filled by direct global->LDS loads three k-steps ahead; a tile row
+// is four 16-byte chunks stored with chunk c of row r at position c ^ ((r >> 1) & 3), so
+// the fragment reads of 8 consecutive rows hit distinct banks.  Tiles are visited in
+// groups of 8 row tiles, each XCD taking a contiguous run, so the blocks running together
+// on one XCD share their A and B tiles in its L2.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
+namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kLdsRow = kBK + 8;   // bf16 elements per LDS row (16-byte pad)
+constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr int TCH = BM * BK / 8;        // 16-byte chunks per operand tile (1024)
+constexpr int GROUP_M = 8;
 
-__device__ __forceinline__ uint32_t pack_bf16x2(uint16_t lo, uint16_t hi) {
-  return (uint32_t)lo | ((uint32_t)hi << 16);
+// One 16-byte load per lane straight into LDS (the lanes of the wave fill consecutive
+// entries from lds_wave_base).  Inline assembly, so the compiler does not track it; the
+// explicit waits below order it.  Nothing else in this kernel uses m0.
+__device__ __forceinline__ void dma16(const void* src, u32x4_t* lds_wave_base) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds_wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
 }
 
-// fp32 -> (hi, lo) bf16 bit patterns with a = hi + lo + O(2^-17 |a|)
-__device__ __forceinline__ void split_bf16(float a, uint16_t& hi, uint16_t& lo) {
-  const uint32_t b = __float_as_uint(a);
-  hi = (uint16_t)(b >> 16);
-  const float r = a - __uint_as_float(b & 0xffff0000u);
-  const uint32_t rb = __float_as_uint(r);
-  lo = (uint16_t)((rb + 0x7fffu + ((rb >> 16) & 1u)) >> 16);
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <bool SPLIT>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Al[SPLIT ? kBM * kLdsRow : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLdsRow];
-
+__global__ __launch_bounds__(512) void gemm_kernel(const GemmParams P) {
+  __shared__ u32x4_t ring[NST][2 * TCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  const int q4 = lane >> 4, r16 = lane & 15;
+  const int wm = wave >> 2, wn = wave & 3;
 
-  // B row pointers of the rows this thread loads (4 chunks of 8 bf16 per thread per step)
-  const uint16_t* brow[4];
+  // tile order: XCD-contiguous runs, groups of GROUP_M row tiles
+  const int tiles_m = (P.M + BM - 1) / BM, tiles_n = (P.N + BN - 1) / BN;
+  const int nblk = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((nblk & 7) == 0) t = (t & 7) * (nblk >> 3) + (t >> 3);
+  const int per_group = GROUP_M * tiles_n;
+  const int g = t / per_group, first_m = g * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int pid_m = first_m + (t % per_group) % gsize;
+  const int pid_n = (t % per_group) / gsize;
+  const int m0 = pid_m * BM, n0 = pid_n * BN;
+
+  // per thread: two chunks of the A tile and two of the B tile per k-step
+  const uint16_t* pa[2];
+  const uint16_t* pa2[2];
+  const uint16_t* pb[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int q = tid + 256 * u;
-    const int r = q >> 3;
-    const int n = n0 + r;
-    brow[u] = nullptr;
-    if (n < P.N) {
-      int first = P.seg_first[0];
-      const uint16_t* base = P.seg_b[0];
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + 512 * u;
+    const int r = e >> 2, c = (e & 3) ^ ((r >> 1) & 3);
+    const int am = min(m0 + r, P.M - 1);
+    pa[u] = P.A + (size_t)am * P.lda + 8 * c;
+    pa2[u] = P.A2 ? P.A2 + (size_t)am * P.lda + 8 * c : pa[u];
+    const int n = min(n0 + r, P.N - 1);
+    int first = P.seg_first[0];
+    const uint16_t* base = P.seg_b[0];
 #pragma unroll
-      for (int i = 1; i < kMaxSegs; ++i)
-        if (i < P.nseg && n >= P.seg_first[i]) { first = P.seg_first[i]; base = P.seg_b[i]; }
-      brow[u] = base + (size_t)(n - first) * P.K;
-    }
+    for (int i = 1; i < kMaxSegs; ++i)
+      if (i < P.nseg && n >= P.seg_first[i]) { first = P.seg_first[i]; base = P.seg_b[i]; }
+    pb[u] = base + (size_t)(n - first) * P.K + 8 * c;
   }
-
-  f32x4_t acc[4][4];
+  const int nk = P.K / BK;
+  const int NK = P.A2 ? 2 * nk : nk;
+  auto issue = [&](int kt) {
+    const int st = kt % NST;
+    const bool second = kt >= nk;
+    const int k0 = (second ? kt - nk : kt) * BK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int u = 0; u < 2; ++u) {
+      u32x4_t* wa = &ring[st][64 * (wave + 8 * u)];
+      dma16((second ? pa2[u] : pa[u]) + k0, wa);
+      dma16(pb[u] + k0, wa + TCH);
+    }
+  };
+
+  f32x4_t acc[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < P.K; k0 += kBK) {
-    // ---- global -> LDS ----
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q >> 3, c8 = (q & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (brow[u]) v = *reinterpret_cast<const uint4*>(brow[u] + k0 + c8);
-      *reinterpret_cast<uint4*>(Bs + r * kLdsRow + c8) = v;
-    }
-    if constexpr (!SPLIT) {
-      const uint16_t* A = static_cast<const uint16_t*>(P.A);
+  for (int kt = 0; kt < NST - 1; ++kt)
+    if (kt < NK) issue(kt);
+
+  // fragment positions: row r (r16 = r % 16) and chunk q4 -> (r << 2) | (q4 ^ ((r16 >> 1) & 3))
+  const int sw = q4 ^ ((r16 >> 1) & 3);
+  const int a_off = ((128 * wm + r16) << 2) | sw;
+  const int b_off = TCH + (((64 * wn + r16) << 2) | sw);
+
+#pragma unroll 1
+  for (int kt = 0; kt < NK; ++kt) {
+    // tile kt has landed once at most the later tiles' loads are outstanding
+    const int later = min(NK - 1 - kt, NST - 2);
+    if (later >= 2) wait_vm_barrier<8>();
+    else if (later == 1) wait_vm_barrier<4>();
+    else wait_vm_barrier<0>();
+    if (kt + NST - 1 < NK) issue(kt + NST - 1);
+    const u32x4_t* st = ring[kt % NST];
+    u32x4_t af[8], bf[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int q = tid + 256 * u;
-        const int r = q >> 3, c8 = (q & 7) * 8;
-        const int m = m0 + r;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < P.M) v = *reinterpret_cast<const uint4*>(A + (size_t)m * P.lda + k0 + c8);
-        *reinterpret_cast<uint4*>(As + r * kLdsRow + c8) = v;
-      }
-    } else {
-      const float* A = static_cast<const float*>(P.A);
+    for (int i = 0; i < 8; ++i) af[i] = st[a_off + 64 * i];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = tid + 256 * u;
-        const int r = q >> 4, c4 = (q & 15) * 4;
-        const int m = m0 + r;
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m < P.M) v = *reinterpret_cast<const float4*>(A + (size_t)m * P.lda + k0 + c4);
-        uint16_t h0, h1, h2, h3, l0, l1, l2, l3;
-        split_bf16(v.x, h0, l0); split_bf16(v.y, h1, l1);
-        split_bf16(v.z, h2, l2); split_bf16(v.w, h3, l3);
-        *reinterpret_cast<uint2*>(As + r * kLdsRow + c4) = make_uint2(pack_bf16x2(h0, h1), pack_bf16x2(h2, h3));
-        *reinterpret_cast<uint2*>(Al + r * kLdsRow + c4) = make_uint2(pack_bf16x2(l0, l1), pack_bf16x2(l2, l3));
-      }
-    }
-    __syncthreads();
-    // ---- MFMA ----
+    for (int j = 0; j < 4; ++j) bf[j] = st[b_off + 64 * j];
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      const int kc = kk + 8 * (lane >> 4);
-      bf16x8_t bfr[4];
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wn * 64 + j * 16 + (lane & 15);
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(Bs + n * kLdsRow + kc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + i * 16 + (lane & 15);
-        const bf16x8_t afr = *reinterpret_cast<const bf16x8_t*>(As + m * kLdsRow + kc);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[j], acc[i][j], 0, 0, 0);
-        if constexpr (SPLIT) {
-          const bf16x8_t alr = *reinterpret_cast<const bf16x8_t*>(Al + m * kLdsRow + kc);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alr, bfr[j], acc[i][j], 0, 0, 0);
-        }
-      }
-    }
-    __syncthreads();
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                            __builtin_bit_cast(bf16x8_t, bf[j]),
+                                                            acc[i][j], 0, 0, 0);
   }
 
-  // ---- store ----
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + 64 * wn + 16 * j + r16;
+    if (col >= P.N) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-      if (col >= P.N) continue;
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
+        const int row = m0 + 128 * wm + 16 * i + 4 * q4 + r;
         if (row < P.M) P.C[(size_t)row * P.ldc + P.coff + col] = acc[i][j][r];
       }
-    }
+  }
 }
 
+// fp32 -> two BF16 planes hi = bf16(x), lo = bf16(x - hi), 4 values per thread
+__global__ void split_planes_kernel(const float* __restrict__ x, uint16_t* __restrict__ hi,
+                                    uint16_t* __restrict__ lo, int64_t n4) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const f32x4_t v = reinterpret_cast<const f32x4_t*>(x)[i];
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const __bf16 bh = (__bf16)v[e];
+    const float r = v[e] - (float)bh;
+    const __bf16 bl = (__bf16)r;
+    h[e] = __builtin_bit_cast(uint16_t, bh);
+    l[e] = __builtin_bit_cast(uint16_t, bl);
+  }
+  reinterpret_cast<uint2*>(hi)[i] = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+  reinterpret_cast<uint2*>(lo)[i] = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s) {
-  dim3 grid((p.N + kBN - 1) / kBN, (p.M + kBM - 1) / kBM);
-  if (p.split_a)
-    gemm_kernel<true><<<grid, 256, 0, s>>>(p);
-  else
-    gemm_kernel<false><<<grid, 256, 0, s>>>(p);
+  if (p.K % BK || p.lda % 8 || p.M < 1 || p.N < 1) return hipErrorInvalidValue;
+  const int blocks = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  gemm_kernel<<<blocks, 512, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_planes(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s) {
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  split_planes_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(x, hi, lo, n4);
   return hipGetLastError();
 }
 

@@ -170,52 +170,53 @@ int persistent_max_blocks();            // co-resident blocks of one per CU, 0 i
 // ---------------------------------------------------------------------------------------
 // C[m][coff + n] = sum_k A[m][k] B[n][k]; B = BF16 rows from up to kMaxSegs stacked
 // matrices ([rows][K] each, segment i starting at output column seg_first[i]); A = BF16
-// [M][lda] or, with split_a, FP32 [M][lda] taken as two BF16 terms.  K % 64 == 0.
+// [M][lda], plus optionally a second BF16 plane summed against the same B (an fp32
+// operand as hi + lo).  K % 32 == 0.
 struct GemmParams {
-  const void* A = nullptr;
+  const uint16_t* A = nullptr;    // BF16 [M][lda]
+  const uint16_t* A2 = nullptr;   // optional second BF16 plane [M][lda] (the low half of an
+                                  // fp32 operand split hi + lo), multiplied by the same B
   int lda = 0;
-  int split_a = 0;
   const uint16_t* seg_b[kMaxSegs] = {};
   int seg_first[kMaxSegs] = {};
   int nseg = 0;
-  int M = 0, N = 0, K = 0;
+  int M = 0, N = 0, K = 0;        // K a multiple of 32
   float* C = nullptr;
   int ldc = 0, coff = 0;
 };
 hipError_t launch_gemm(const GemmParams& p, hipStream_t s);
+// fp32 [n] -> BF16 planes hi = bf16(x), lo = bf16(x - hi); n a multiple of 4
+hipError_t launch_split_planes(const float* x, uint16_t* hi, uint16_t* lo, int64_t n, hipStream_t s);
 
 constexpr int kChunk = 64;          // tokens per chunk of the chunked delta rule
-constexpr int kPrefillMaxChannels = 8192;  // conv channels + 2 heads' norms, sequence pass
 
 struct PrefillParams {
   int B = 0, L = 0, H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;
   int nch = 0;                    // chunks per sequence
   const float* P = nullptr;       // [B*L][proj_stride]: p (C) | f_lr | g_lr | beta logits
   int proj_stride = 0;
-  const float* FG = nullptr;      // [B*L][H*dk + H*dv]: F_b f_lr | G_b g_lr
   const float* win = nullptr;     // [B][3][C] initial conv window
-  float* win_out = nullptr;       // [B][3][C] final window (may alias win; own kernel)
+  float* win_out = nullptr;       // [B][3][C] final window (may alias win; own kernel, after prep)
   const float* conv_w = nullptr;
   const float* a_log = nullptr;
   const float* dt_bias = nullptr;
   const float* onw = nullptr;     // [dv] or null
+  const uint16_t* Fb = nullptr;   // forget-gate up-projection, BF16 [H*dk][rank_f]
+  const uint16_t* Gb = nullptr;   // output-gate up-projection, BF16 [H*dv][rank_g]
   float l2_eps = 0.f, q_scale = 0.f, norm_eps = 0.f;
-  // sequence-pass outputs, [B][H][L][dk|dv] and [B][H][L]
-  float *q = nullptr, *k = nullptr, *v = nullptr, *g2 = nullptr, *beta = nullptr;
-  float* gate = nullptr;          // [B*L][H*dv]
   // per-chunk preparation outputs, per (b, h, chunk), in matrix-core operand order: -W,
   // q 2^G, (k 2^(G_last - G))^T and A as BF16 hi/lo fragments, U in accumulator order,
   // dec = 2^G_last
   void *Wf = nullptr, *Qf = nullptr, *Kf = nullptr, *Af = nullptr;
   float *Uf = nullptr, *dec = nullptr;
   float* S = nullptr;             // [B][H][dk][dv] state, read then overwritten
-  float* o = nullptr;             // [B*L][H*dv]: o, then the gated norm n in place
+  float* o = nullptr;             // [B*L][H*dv] scan outputs
+  uint16_t *on_hi = nullptr, *on_lo = nullptr;   // [B*L][H*dv] gated norm as BF16 hi/lo planes
 };
-hipError_t launch_prefill_seq(const PrefillParams& p, hipStream_t s);
 hipError_t launch_prefill_window(const PrefillParams& p, hipStream_t s);
 hipError_t launch_chunk_prep(const PrefillParams& p, hipStream_t s);
 hipError_t launch_chunk_scan(const PrefillParams& p, hipStream_t s);
-hipError_t launch_gated_norm(const PrefillParams& p, hipStream_t s);
+hipError_t launch_chunk_gnorm(const PrefillParams& p, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
 // Packing.
