@@ -282,19 +282,21 @@ def bench_verify(args, torch, synth, kda, w, run, model):
 
 
 def prefill_flops(w):
-    """Algorithmic MFMA flops of one chunked prefill call per kernel kind."""
+    """Algorithmic flops of one chunked prefill call per kernel kind: the two projection
+    GEMMs; the chunk kernels (the forget gate's up-projection, L, A, W, U per chunk, and the
+    scan's D, O, S products); the gated norm (the output gate's up-projection)."""
     d = w.dims
     M = w.batch * w.tokens
     rows = d.conv_channels + d.rank_f + d.rank_g + d.n_heads
-    gemm = 2 * M * (rows * d.d_model + d.key_dim * d.rank_f + d.value_dim * d.rank_g
-                    + d.d_model * d.value_dim)
+    gemm = 2 * M * (rows * d.d_model + d.d_model * d.value_dim)
     # chunk math per (seq, head, chunk of c): L, A (2 c^2 dk), W, U (c^2 (dk + dv)),
     # D = U - W S (c dk dv), O = Q S + A D (c dk dv + c^2 dv), S += K^T D (c dk dv)
     c = w.chunk
     per_chunk = 2 * (2 * c * c * d.d_k + c * c * (d.d_k + d.d_v) + 3 * c * d.d_k * d.d_v
                      + c * c * d.d_v)
-    chunk = w.batch * d.n_heads * (w.tokens // c) * per_chunk
-    return {"gemm": gemm, "chunk": chunk}
+    chunk = w.batch * d.n_heads * (w.tokens // c) * per_chunk + 2 * M * d.key_dim * d.rank_f
+    norm = 2 * M * d.value_dim * d.rank_g
+    return {"gemm": gemm, "chunk": chunk, "norm": norm}
 
 
 def bench_prefill(args, torch, synth, kda, w, run, model):
@@ -328,7 +330,7 @@ def bench_prefill(args, torch, synth, kda, w, run, model):
         call(i)
     torch.cuda.synchronize()
     times = timed_kinds(model, kda, {"gemm": kda.KDA_K_GEMM, "chunk": kda.KDA_K_CHUNK,
-                                     "seq": kda.KDA_K_PREFILL})
+                                     "norm": kda.KDA_K_PREFILL})
     model.set_option(kda.KDA_OPT_TIMING, 0)
     fl = prefill_flops(w)
     per = {}
@@ -346,7 +348,7 @@ def bench_prefill(args, torch, synth, kda, w, run, model):
             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
     ms_call = el * 1e3 / steps
-    total_fl = fl["gemm"] + fl["chunk"]
+    total_fl = sum(fl.values())
     config = {"workload": "kda-layer-bf16-prefill-B4-L8192-chunk64", "layers": 1,
               "d_model": d.d_model, "heads": d.n_heads, "batch": B, "global_batch": B,
               "seq_len": L, "chunk": w.chunk, "parallelism": "none (1 GPU)",

@@ -193,7 +193,10 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
  * y_dev [B][L][D] fp32; st is read as the initial state and overwritten with the final
  * state and window.  The delta rule runs in the chunked WY/UT form of the chunk_kda
  * commit of torad-labs/llama.cpp PR #84 with an fp32 state carried across chunks;
- * chunk must be 64.  Any L >= 1 (partial last chunk allowed). */
+ * chunk must be 64.  Any L >= 1 (partial last chunk allowed).  Needs BF16 weights,
+ * rank_f of 64 or 128, and D, rank_g and H*d_v multiples of 64 (KDA_E_SHAPE,
+ * KDA_E_DTYPE otherwise).  The products run on matrix cores with fp32 operands split into
+ * two BF16 terms (about 16 significant bits per product, fp32 accumulation). */
 int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
                         int32_t chunk, float* y_dev, const kda_state* st, void* ws_dev,
                         size_t ws_bytes, void* stream);
