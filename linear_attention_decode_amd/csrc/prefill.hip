@@ -47,6 +47,17 @@ constexpr int CS = kChunk;             // tokens per chunk
 constexpr int NB = CS / 16;            // 16-row blocks per chunk
 constexpr float kFactorMax = 64.0f;    // largest log2 factor of the factored diagonal blocks
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Hardware-approximate special functions (v_exp_f32, v_log_f32, v_rcp_f32, ~1 ulp each):
+// this path's products carry ~16 significant bits, so the precise library forms buy
+// nothing here and cost ~5x the instructions.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fsigmoid(float z) { return __builtin_amdgcn_rcpf(1.0f + fexp(-z)); }
+__device__ __forceinline__ float fsilu(float y) { return y * fsigmoid(y); }
+__device__ __forceinline__ float fsoftplus(float z) {
+  return fmaxf(z, 0.0f) + __builtin_amdgcn_logf(1.0f + fexp(-fabsf(z))) * kLn2;
+}
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -82,7 +93,7 @@ __device__ __forceinline__ void lds_barrier() {
 // gate's low-rank projection.
 // ---------------------------------------------------------------------------------------
 template <int DK, int RF>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_prep_kernel(const PrefillParams P) {
   using Lds = PrepLds<DK>;
   constexpr int RS = Lds::RS, AS = Lds::AS, KS = DK / 32;
   constexpr int FS = RF + 4;           // row stride of the staged f_lr rows
@@ -146,18 +157,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
   {
     constexpr int NG = DK / 4;
     constexpr int ITEMS = 2 * 8 * NG;
+    constexpr int NIT = ITEMS / 256;
     static_assert(ITEMS % 256 == 0, "conv items");
+    // all input rows and weights first (one round trip), then the conv of each item
+    f32x4_t xin[NIT][11], w[NIT][4];
 #pragma unroll
-    for (int u = 0; u < ITEMS / 256; ++u) {
+    for (int u = 0; u < NIT; ++u) {
       const int it = tid + 256 * u;
       const int c4 = it % NG, rg = (it / NG) % 8, mat = it / (8 * NG);
       const int ch = mat * P.H * DK + h * DK + 4 * c4;
-      f32x4_t xin[11];
 #pragma unroll
-      for (int k = 0; k < 11; ++k) xin[k] = *reinterpret_cast<const f32x4_t*>(conv_src(8 * rg - 3 + k, ch));
-      f32x4_t w[4];
+      for (int k = 0; k < 11; ++k) xin[u][k] = *reinterpret_cast<const f32x4_t*>(conv_src(8 * rg - 3 + k, ch));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const f32x4_t*>(P.conv_w + (size_t)(ch + e) * 4);
+      for (int e = 0; e < 4; ++e) w[u][e] = *reinterpret_cast<const f32x4_t*>(P.conv_w + (size_t)(ch + e) * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int it = tid + 256 * u;
+      const int c4 = it % NG, rg = (it / NG) % 8, mat = it / (8 * NG);
       float* dst = (mat ? sK : sQ) + 4 * c4;
 #pragma unroll
       for (int o = 0; o < 8; ++o) {
@@ -165,13 +182,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
         f32x4_t y;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          y[e] = silu_f(w[e][0] * xin[o][e] + w[e][1] * xin[o + 1][e] + w[e][2] * xin[o + 2][e] +
-                        w[e][3] * xin[o + 3][e]);
+          y[e] = fsilu(w[u][e][0] * xin[u][o][e] + w[u][e][1] * xin[u][o + 1][e] +
+                        w[u][e][2] * xin[u][o + 2][e] + w[u][e][3] * xin[u][o + 3][e]);
         *reinterpret_cast<f32x4_t*>(dst + t * RS) = t < nt ? y : f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
     if (tid < CS)
-      sBeta[tid] = tid < nt ? sigmoid_f(P.P[(row0 + tid) * P.proj_stride + P.C + P.rank_f + P.rank_g + h])
+      sBeta[tid] = tid < nt ? fsigmoid(P.P[(row0 + tid) * P.proj_stride + P.C + P.rank_f + P.rank_g + h])
                             : 0.0f;
     if (tid < NB) sFlag[tid] = 0.0f;
   }
@@ -203,7 +220,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[mt][n] = mma2(fa[mt], fbf[n][ks], acc[mt][n]);
     }
-    const float ea = expf(P.a_log[h]);
+    const float ea = fexp(P.a_log[h]);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
       const int i = 16 * (wave * NTW + n) + r16;
@@ -213,7 +230,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * mt + 4 * q4 + r;
-          sG[t * RS + i] = t < nt ? (-ea * softplus_f(acc[mt][n][r] + bias)) * kLog2e : 0.0f;
+          sG[t * RS + i] = t < nt ? (-ea * fsoftplus(acc[mt][n][r] + bias)) * kLog2e : 0.0f;
         }
     }
   }
@@ -498,7 +515,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const PrefillParams P) 
       for (int e = 0; e < 8; ++e) {
         const float* xi = vin[n][kk] + e;
         x[e] = sBeta[32 * kk + 8 * q4 + e] *
-               silu_f(vw[n][0] * xi[0] + vw[n][1] * xi[1] + vw[n][2] * xi[2] + vw[n][3] * xi[3]);
+               fsilu(vw[n][0] * xi[0] + vw[n][1] * xi[1] + vw[n][2] * xi[2] + vw[n][3] * xi[3]);
       }
       fv[kk] = split8(x);
     }
@@ -854,7 +871,7 @@ __global__ __launch_bounds__(256) void chunk_gnorm_kernel(const PrefillParams P)
       for (int n = 0; n < NTW; ++n) {
         const int j = 16 * (wave * NTW + n) + r16;
         const float w = P.onw ? P.onw[j] : 1.0f;
-        const float g = sigmoid_f(acc[mt][n][r]);
+        const float g = fsigmoid(acc[mt][n][r]);
         const float y = ov[mt][n][r] * sc * w * g;
         const __bf16 yh = (__bf16)y;
         const size_t at = (row0 + t) * V + (size_t)h * D + j;
