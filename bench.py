@@ -37,9 +37,9 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 752336069,
-                "sha256": "f94807fba429a79eb8409f444c0f514801c66085bd7461f6071c1d5a320bbf7d",
-                "sources": ("persistent.hip", "kda_device.h", "kda_internal.h")}
+STEP_TRAFFIC = {"bytes": 752208047,
+                "sha256": "9a044ed7bf395e84ece43caa44200e9788facf7d5109f575f40a74af0d95fc30",
+                "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
 def step_traffic():

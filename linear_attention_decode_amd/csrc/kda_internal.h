@@ -5,15 +5,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "persist.h"
+
 namespace kda {
 
 enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2 };
 
 // A packed weight matrix as the kernels see it.
-struct PackedMat {
-  const uint8_t* w = nullptr;   // F32/BF16 data, or the Q8_0 byte plane (q + 128)
-  const __half* d = nullptr;    // Q8_0 scale plane [rows][cols/32]
-};
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -130,40 +128,6 @@ hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
                            const float* conv_w, float* act, int B, int T, int C, hipStream_t s);
 hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,
                                 int C, const int* ntok, hipStream_t s);
-
-// ---------------------------------------------------------------------------------------
-// One-launch decode step (batch 1, Q8_0 weights).
-// ---------------------------------------------------------------------------------------
-struct PersistLayer {
-  PackedMat seg[6];               // W_q, W_k, W_v, F_a, G_a, W_beta  (rows [out][D])
-  PackedMat fb, gb, wo;
-  const float* conv_w = nullptr;
-  const float* a_log = nullptr;
-  const float* dt_bias = nullptr;
-  const float* o_norm_w = nullptr;
-};
-
-struct PersistParams {
-  int n_layers = 0, D = 0, H = 0, dk = 0, dv = 0, C = 0, rank = 0, proj_rows = 0;
-  int seg_first[6] = {};
-  float eps = 0.f, l2_eps = 0.f, q_scale = 0.f;
-  const PersistLayer* layers = nullptr;  // device array [n_layers]
-  float* S = nullptr;                    // [n_layers][H][dk][dv]
-  float* win = nullptr;                  // [n_layers][3][C]
-  const float* x_in = nullptr;           // [D]
-  float* y_out = nullptr;                // [D]
-  uint64_t* xbuf = nullptr;              // [2][D]      tagged residual stream
-  uint64_t* pbuf = nullptr;              // [proj_rows] tagged projections
-  uint64_t* obuf = nullptr;              // [V] tagged normalised, gated head outputs
-  uint64_t* flags = nullptr;             // [3][kMaxPersistBlocks] tagged producer flags
-  int* err = nullptr;                    // nonzero after a wait timed out
-  uint64_t timeout = 0;                  // wall-clock ticks a wait may take
-  uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)
-  int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection
-};
-constexpr int kMaxPersistBlocks = 1024;
-hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s);
-int persistent_max_blocks();            // co-resident blocks of one per CU, 0 if unavailable
 
 // ---------------------------------------------------------------------------------------
 // Chunked prefill.

@@ -27,7 +27,7 @@
 // consumer always checks the tag of every data word it uses.  Every wait is bounded: on a
 // timeout the block records an error word and every block leaves the kernel.
 #include "kda_device.h"
-#include "kda_internal.h"
+#include "persist.h"
 
 #define KDA_GLOBAL __attribute__((address_space(1)))
 #define KDA_CONST __attribute__((address_space(4)))
