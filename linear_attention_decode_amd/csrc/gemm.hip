@@ -5,14 +5,16 @@
 // runs over both planes against the same B, i.e. C = A_hi B^T + A_lo B^T, every product
 // exact in fp32 accumulation.
 //
-// Block tile 256 x 256 x 32, 8 waves as 2 (m) x 4 (n), each 128 x 64 = 8 x 4 tiles of
+// Block tile 256 x 256 x 64, 8 waves as 4 (m) x 2 (n), each 64 x 128 = 4 x 8 tiles of
 // v_mfma_f32_16x16x32_bf16 (lane l: row l % 16 of A and of B^T, k = 8 (l / 16) .. + 7;
 // accumulator rows 4 (l / 16) + r, column l % 16).  Operand tiles stream through a
-// four-stage LDS ring filled by direct global->LDS loads three k-steps ahead; a tile row
-// is four 16-byte chunks stored with chunk c of row r at position c ^ ((r >> 1) & 3), so
-// the fragment reads of 8 consecutive rows hit distinct banks.  Tiles are visited in
-// groups of 8 row tiles, each XCD taking a contiguous run, so the blocks running together
-// on one XCD share their A and B tiles in its L2.
+// two-stage LDS ring filled by direct global->LDS loads one k-step ahead; a tile row is
+// eight 16-byte chunks stored with chunk c of row r at position c ^ (r & 7), so the
+// fragment reads of 8 consecutive rows hit distinct banks.  Tiles are visited in groups of
+// 8 row tiles, each XCD taking a contiguous run, so the blocks running together on one XCD
+// share their A and B tiles in its L2.  C is written with non-temporal stores (it is read
+// back from HBM by the next kernel, not from the caches).  The tile shape, ring depth and
+// store kind were chosen by timing the two prefill projection shapes.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -23,8 +25,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, BK = 32, NST = 4;
-constexpr int TCH = BM * BK / 8;        // 16-byte chunks per operand tile (1024)
+constexpr int BM = 256, BN = 256, BK = 64, NST = 2;
+constexpr int CPR = BK / 8;              // 16-byte chunks per tile row
+constexpr int TCH = BM * CPR;           // 16-byte chunks per operand tile (2048)
+constexpr int LPT = TCH / 512;          // chunk loads per thread per operand per k-step
 constexpr int GROUP_M = 8;
 
 // One 16-byte load per lane straight into LDS (the lanes of the wave fill consecutive
@@ -45,7 +49,7 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams P) {
   __shared__ u32x4_t ring[NST][2 * TCH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave >> 1, wn = wave & 1;           // 4 x 2 waves of 64 x 128
 
   // tile order: XCD-contiguous runs, groups of GROUP_M row tiles
   const int tiles_m = (P.M + BM - 1) / BM, tiles_n = (P.N + BN - 1) / BN;
@@ -59,14 +63,14 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams P) {
   const int pid_n = (t % per_group) / gsize;
   const int m0 = pid_m * BM, n0 = pid_n * BN;
 
-  // per thread: two chunks of the A tile and two of the B tile per k-step
-  const uint16_t* pa[2];
-  const uint16_t* pa2[2];
-  const uint16_t* pb[2];
+  // per thread: LPT chunks of the A tile and LPT of the B tile per k-step
+  const uint16_t* pa[LPT];
+  const uint16_t* pa2[LPT];
+  const uint16_t* pb[LPT];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < LPT; ++u) {
     const int e = tid + 512 * u;
-    const int r = e >> 2, c = (e & 3) ^ ((r >> 1) & 3);
+    const int r = e / CPR, c = (e % CPR) ^ (r & 7);
     const int am = min(m0 + r, P.M - 1);
     pa[u] = P.A + (size_t)am * P.lda + 8 * c;
     pa2[u] = P.A2 ? P.A2 + (size_t)am * P.lda + 8 * c : pa[u];
@@ -85,61 +89,60 @@ __global__ __launch_bounds__(512) void gemm_kernel(const GemmParams P) {
     const bool second = kt >= nk;
     const int k0 = (second ? kt - nk : kt) * BK;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < LPT; ++u) {
       u32x4_t* wa = &ring[st][64 * (wave + 8 * u)];
       dma16((second ? pa2[u] : pa[u]) + k0, wa);
       dma16(pb[u] + k0, wa + TCH);
     }
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[4][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll
-  for (int kt = 0; kt < NST - 1; ++kt)
-    if (kt < NK) issue(kt);
-
-  // fragment positions: row r (r16 = r % 16) and chunk q4 -> (r << 2) | (q4 ^ ((r16 >> 1) & 3))
-  const int sw = q4 ^ ((r16 >> 1) & 3);
-  const int a_off = ((128 * wm + r16) << 2) | sw;
-  const int b_off = TCH + (((64 * wn + r16) << 2) | sw);
+  issue(0);
+  // fragment rows: 64 wm + 16 i + r16 (A), 128 wn + 16 j + r16 (B); k chunk 4 ks + q4 of the
+  // row sits at position (4 ks + q4) ^ (row & 7) = (4 ks + q4) ^ (r16 & 7)
+  const int a_row = ((64 * wm + r16) * CPR), b_row = TCH + ((128 * wn + r16) * CPR);
+  const int sw = r16 & 7;
 
 #pragma unroll 1
   for (int kt = 0; kt < NK; ++kt) {
-    // tile kt has landed once at most the later tiles' loads are outstanding
-    const int later = min(NK - 1 - kt, NST - 2);
-    if (later >= 2) wait_vm_barrier<8>();
-    else if (later == 1) wait_vm_barrier<4>();
-    else wait_vm_barrier<0>();
-    if (kt + NST - 1 < NK) issue(kt + NST - 1);
+    // tile kt has landed (no later tile is in flight yet); every wave is done with the
+    // other slot, which the next tile's loads then fill
+    wait_vm_barrier<0>();
+    if (kt + 1 < NK) issue(kt + 1);
     const u32x4_t* st = ring[kt % NST];
-    u32x4_t af[8], bf[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = st[a_off + 64 * i];
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      const int ch = (4 * ks + q4) ^ sw;
+      u32x4_t af[4], bf[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = st[b_off + 64 * j];
+      for (int i = 0; i < 4; ++i) af[i] = st[a_row + 16 * i * CPR + ch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int j = 0; j < 8; ++j) bf[j] = st[b_row + 16 * j * CPR + ch];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
-                                                            __builtin_bit_cast(bf16x8_t, bf[j]),
-                                                            acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[i]),
+                                                              __builtin_bit_cast(bf16x8_t, bf[j]),
+                                                              acc[i][j], 0, 0, 0);
+    }
   }
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int col = n0 + 64 * wn + 16 * j + r16;
+  for (int j = 0; j < 8; ++j) {
+    const int col = n0 + 128 * wn + 16 * j + r16;
     if (col >= P.N) continue;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + 128 * wm + 16 * i + 4 * q4 + r;
-        if (row < P.M) P.C[(size_t)row * P.ldc + P.coff + col] = acc[i][j][r];
+        const int row = m0 + 64 * wm + 16 * i + 4 * q4 + r;
+        if (row < P.M) __builtin_nontemporal_store(acc[i][j][r], P.C + (size_t)row * P.ldc + P.coff + col);
       }
   }
 }

@@ -135,7 +135,7 @@ hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, 
 // C[m][coff + n] = sum_k A[m][k] B[n][k]; B = BF16 rows from up to kMaxSegs stacked
 // matrices ([rows][K] each, segment i starting at output column seg_first[i]); A = BF16
 // [M][lda], plus optionally a second BF16 plane summed against the same B (an fp32
-// operand as hi + lo).  K % 32 == 0.
+// operand as hi + lo).  K % 64 == 0.
 struct GemmParams {
   const uint16_t* A = nullptr;    // BF16 [M][lda]
   const uint16_t* A2 = nullptr;   // optional second BF16 plane [M][lda] (the low half of an
@@ -144,7 +144,7 @@ struct GemmParams {
   const uint16_t* seg_b[kMaxSegs] = {};
   int seg_first[kMaxSegs] = {};
   int nseg = 0;
-  int M = 0, N = 0, K = 0;        // K a multiple of 32
+  int M = 0, N = 0, K = 0;        // K a multiple of 64
   float* C = nullptr;
   int ldc = 0, coff = 0;
 };
