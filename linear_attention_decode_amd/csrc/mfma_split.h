@@ -75,5 +75,30 @@ __device__ __forceinline__ f32x4_t mma2(const Frag& a, const u32x4_t& b, f32x4_t
   return acc;
 }
 
+
+// 4-value operands of v_mfma_f32_16x16x16_bf16 (lane l: row / column l % 16, k = 4 (l / 16)
+// .. + 3; the accumulator's rows 4 (l / 16) + r are exactly the k of a B operand).
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+struct Frag4 {
+  s16x4_t hi, lo;
+};
+__device__ __forceinline__ Frag4 split4(const f32x4_t x) {
+  Frag4 f;
+  const unsigned h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
+  const unsigned l0 = pk_bf16(x[0] - __builtin_bit_cast(float, h0 << 16), x[1] - __builtin_bit_cast(float, h0 & 0xffff0000u));
+  const unsigned l1 = pk_bf16(x[2] - __builtin_bit_cast(float, h1 << 16), x[3] - __builtin_bit_cast(float, h1 & 0xffff0000u));
+  typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+  f.hi = __builtin_bit_cast(s16x4_t, u32x2_t{h0, h1});
+  f.lo = __builtin_bit_cast(s16x4_t, u32x2_t{l0, l1});
+  return f;
+}
+// acc += a b over 16 k: lo*hi + hi*lo + hi*hi
+__device__ __forceinline__ f32x4_t mma3_16(const Frag4& a, const Frag4& b, f32x4_t acc) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+  return acc;
+}
+
 }  // namespace mfma
 }  // namespace kda

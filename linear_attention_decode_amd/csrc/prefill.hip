@@ -76,7 +76,6 @@ struct PrepLds {
   static constexpr int FLAG = BETA + CS;
   static constexpr int INV = FLAG + NB;   // inverse L2 norms of the q rows, then of the k rows
   static constexpr int TOTAL = INV + 2 * CS;
-  static constexpr int M = Q;          // three 16x16 scratch tiles of the inverse, over q
   static constexpr int FL = L;         // f_lr rows [CS][rank + 4] over L and T, before either
   static constexpr int FL_FLOATS = 2 * CS * AS;
   static_assert(TOTAL * 4 <= 160 * 1024, "LDS");
@@ -109,7 +108,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   float* sBeta = sm + Lds::BETA;
   float* sFlag = sm + Lds::FLAG;
   float* sInv = sm + Lds::INV;
-  float* sM = sm + Lds::M;
   float* sFL = sm + Lds::FL;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -433,30 +431,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   lds_barrier();
 
-  // ---- off-diagonal blocks of T, one block diagonal at a time:
-  //      T_IJ = -T_II sum_{K=J}^{I-1} L_IK T_KJ ----
+  // ---- off-diagonal blocks of T, one block diagonal at a time, on the matrix cores:
+  //      T_IJ = -T_II sum_{K=J}^{I-1} L_IK T_KJ, wave J takes block (J + d, J); the first
+  //      product's accumulator is the second product's B operand as it stands ----
 #pragma unroll 1
   for (int d = 1; d < NB; ++d) {
-    const int ntile = NB - d;
-    for (int e = tid; e < ntile * 256; e += 256) {
-      const int J = e >> 8, I = J + d, r = (e >> 4) & 15, cc = e & 15;
-      float a = 0.0f;
+    if (wave < NB - d) {
+      const int J = wave, I = J + d;
+      f32x4_t m = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K) {
-        const float* Lr = sL + (16 * I + r) * AS + 16 * K;
-        const float* Tc = sT + (16 * K) * AS + 16 * J + cc;
+        const f32x4_t la = *reinterpret_cast<const f32x4_t*>(sL + (16 * I + r16) * AS + 16 * K + 4 * q4);
+        f32x4_t tb;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) a += Lr[u] * Tc[u * AS];
+        for (int e = 0; e < 4; ++e) tb[e] = sT[(16 * K + 4 * q4 + e) * AS + 16 * J + r16];
+        m = mma3_16(split4(la), split4(tb), m);
       }
-      sM[e] = a;
-    }
-    lds_barrier();
-    for (int e = tid; e < ntile * 256; e += 256) {
-      const int J = e >> 8, I = J + d, r = (e >> 4) & 15, cc = e & 15;
-      const float* Tr = sT + (16 * I + r) * AS + 16 * I;
-      const float* Mc = sM + (J << 8) + cc;
-      float a = 0.0f;
-      for (int u = 0; u <= r; ++u) a += Tr[u] * Mc[u * 16];
-      sT[(16 * I + r) * AS + 16 * J + cc] = -a;
+      const f32x4_t ta = *reinterpret_cast<const f32x4_t*>(sT + (16 * I + r16) * AS + 16 * I + 4 * q4);
+      const f32x4_t t = mma3_16(split4(ta), split4(m), f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * q4 + r) * AS + 16 * J + r16] = -t[r];
     }
     lds_barrier();
   }
