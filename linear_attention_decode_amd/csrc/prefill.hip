@@ -286,25 +286,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   }
 
-  // ---- A (waves 0, 1) and L (waves 2, 3) as transposed products, row blocks {0,3} / {1,2}:
-  //      X^T[s][t] = sum_i (k_s 2^(R_I - G_s))[i] (x_t 2^(G_t - R_I))[i] ----
+  // ---- A and L together as transposed products, for row block I and key blocks
+  //      J in [j0, j1]:  X^T[s][t] = sum_i (k_s 2^(R_I - G_s))[i] (x_t 2^(G_t - R_I))[i],
+  //      x = q for A and k for L; the two share every decay factor.  Waves: (I 3, J 0-1),
+  //      (I 3, J 2-3), (I 2, J 0-2), (I 1, J 0-1) then (I 0, J 0).  The wave that ends a row
+  //      block at its diagonal also writes the zero blocks above it ----
   {
-    const bool isA = wave < 2;
-    const float* sX = isA ? sQ : sK;
-    float* sOut = isA ? sA : sL;
+    const int npass = wave == 3 ? 2 : 1;
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-      const int I = (wave & 1) ? 1 + pass : 3 * pass;
+    for (int pass = 0; pass < npass; ++pass) {
+      const int I = wave < 2 ? 3 : (wave == 2 ? 2 : 1 - pass);
+      const int j0 = wave == 1 ? 2 : 0;
+      const int j1 = wave == 0 ? 1 : I;
       const bool fac = sFlag[I] == 0.0f;                  // factored diagonal block
       const int t = 16 * I + r16;
-      f32x4_t acc[NB];
+      f32x4_t accA[3], accL[3];
 #pragma unroll
-      for (int J = 0; J < NB; ++J) acc[J] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < 3; ++n) { accA[n] = f32x4_t{0.f, 0.f, 0.f, 0.f}; accL[n] = accA[n]; }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const int c0 = 32 * kk + 8 * q4;
-        float x[8], g[8], rr[8];
-        lds_load8(sX + t * RS + c0, x);
+        float xq[8], xk[8], g[8], rr[8];
+        lds_load8(sQ + t * RS + c0, xq);
+        lds_load8(sK + t * RS + c0, xk);
         lds_load8(sG + t * RS + c0, g);
         if (I > 0) {
           lds_load8(sG + (16 * I - 1) * RS + c0, rr);
@@ -312,33 +316,50 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int e = 0; e < 8; ++e) rr[e] = 0.0f;
         }
-        float bv[8];
+        float bq[8], bk[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bv[e] = x[e] * ex2(g[e] - rr[e]);
-        const Frag fb = split8(bv);
+        for (int e = 0; e < 8; ++e) {
+          const float f = ex2(g[e] - rr[e]);
+          bq[e] = xq[e] * f;
+          bk[e] = xk[e] * f;
+        }
+        const Frag fq = split8(bq), fk = split8(bk);
 #pragma unroll
-        for (int J = 0; J < NB; ++J) {
-          if (J > I || (J == I && !fac)) continue;
+        for (int n = 0; n < 3; ++n) {
+          const int J = j0 + n;
+          if (J > j1 || (J == I && !fac)) continue;
           const int s = 16 * J + r16;
           float kv[8], gs[8], av[8];
           lds_load8(sK + s * RS + c0, kv);
           lds_load8(sG + s * RS + c0, gs);
 #pragma unroll
           for (int e = 0; e < 8; ++e) av[e] = kv[e] * ex2(rr[e] - gs[e]);
-          acc[J] = mma3(split8(av), fb, acc[J]);
+          const Frag fa = split8(av);
+          accA[n] = mma3(fa, fq, accA[n]);
+          accL[n] = mma3(fa, fk, accL[n]);
         }
       }
-      // acc[J], lane: X[t][s] for s = 16 J + 4 q4 + r
+      // acc[n], lane: X[t][s] for s = 16 (j0 + n) + 4 q4 + r
       const float bt = sBeta[t];
 #pragma unroll
-      for (int J = 0; J < NB; ++J) {
-        const bool live = J < I || (J == I && fac);
+      for (int n = 0; n < 3; ++n) {
+        const int J = j0 + n;
+        if (J > j1) continue;
+        const bool live = J < I || fac;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int s = 16 * J + 4 * q4 + r;
-          const float v = live ? acc[J][r] : 0.0f;
-          sOut[t * AS + s] = isA ? (s <= t ? v : 0.0f) : (s < t ? bt * v : 0.0f);
+          sA[t * AS + s] = live && s <= t ? accA[n][r] : 0.0f;
+          sL[t * AS + s] = live && s < t ? bt * accL[n][r] : 0.0f;
         }
+      }
+      if (j1 == I) {
+        for (int s = 16 * (I + 1) + 4 * q4; s < CS; s += 16)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            sA[t * AS + s + r] = 0.0f;
+            sL[t * AS + s + r] = 0.0f;
+          }
       }
     }
   }
