@@ -359,8 +359,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
             (rank == 32 || rank == 64 || rank == 128);
   if (ok) {
     const int np_blocks = nb - 2 * d.n_heads;      // blocks with projection rows
-    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks > 0 && np_blocks <= 256 &&
-         (m->proj_rows + np_blocks - 1) / np_blocks <= 32;
+    const int nq = (m->C + 31) / 32;               // q/k/v rows, 32 per block
+    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks <= 256 && nq < np_blocks &&
+         (m->proj_rows - m->C + np_blocks - nq - 1) / (np_blocks - nq) <= 32;
   }
   if (!ok) return hipSuccess;
   std::vector<PersistLayer> host(d.n_layers);
@@ -403,6 +404,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   p.timeout = (uint64_t)(khz > 0 ? khz : 100000) * 50;   // 50 ms of wall clock per wait
   p.o_first_block = ob0; p.o_blocks = nob;
+  p.q_blocks = (m->C + 31) / 32;
   m->pers_blocks = nb;
   m->pers_ok = true;
   return hipSuccess;

@@ -41,6 +41,8 @@ struct PersistParams {
   uint64_t timeout = 0;                  // wall-clock ticks a wait may take
   uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)
   int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection
+  int q_blocks = 0;                      // projection blocks [0, q_blocks) take the q/k/v rows,
+                                         // 32 each; the rest share the low-rank and beta rows
 };
 constexpr int kMaxPersistBlocks = 1024;
 hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s);

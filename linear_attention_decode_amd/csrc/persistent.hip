@@ -387,10 +387,25 @@ struct Roles {
 
 __device__ __forceinline__ Roles make_roles(const PersistParams& P, int wave) {
   Roles R;
-  // projection rows go to blocks [kHSplit H, nb): head blocks keep their loads for the state
+  // projection rows go to blocks [kHSplit H, nb) (head blocks keep their loads for the
+  // state): q/k/v rows 32 per block to the first q_blocks, then the low-rank and beta rows
+  // spread thin over the rest, so that the rows the head blocks need first (their gates)
+  // are finished early
   const int b = blockIdx.x - kHSplit * P.H, nb = gridDim.x - kHSplit * P.H;
-  const int rp = (P.proj_rows + nb - 1) / nb;
-  const int p0 = min(P.proj_rows, max(b, 0) * rp), p1 = b < 0 ? p0 : min(P.proj_rows, p0 + rp);
+  const int C = P.C, nl = nb - P.q_blocks;
+  const int rl = (P.proj_rows - C + nl - 1) / nl;
+  int p0, p1, rp;
+  if (b < 0) {
+    p0 = p1 = rp = 0;
+  } else if (b < P.q_blocks) {
+    rp = 32;
+    p0 = min(C, b * 32);
+    p1 = min(C, p0 + 32);
+  } else {
+    rp = rl;
+    p0 = min(P.proj_rows, C + (b - P.q_blocks) * rl);
+    p1 = min(P.proj_rows, p0 + rl);
+  }
   const int rpw = (rp + 3) / 4;
   R.wr0 = min(p1, p0 + wave * rpw);
   R.wr1 = min(p1, R.wr0 + rpw);
@@ -482,35 +497,50 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   // inputs: q [dk] | k [dk] | v [kHCols] | f_lr [rank] | g_lr [rank] | beta  (<= 3 per thread)
   constexpr int n_in = 2 * dk + kHCols + 2 * rank + 1;
   static_assert(n_in <= 3 * kPT, "head inputs");
-  {
-    uint64_t w[3];
-    int src[3];
+  // every input is requested at once; the low-rank rows and beta (finished first by their
+  // projection blocks) are waited for before the gates, q / k / v after them
+  constexpr int i_lr = 2 * dk + kHCols;          // first low-rank input
+  uint64_t w[3];
+  const uint64_t* src[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      const int i = tid + k * kPT;
-      if (i < dk) src[k] = h * dk + i;
-      else if (i < 2 * dk) src[k] = K + h * dk + (i - dk);
-      else if (i < 2 * dk + kHCols) src[k] = 2 * K + h * dv + half * kHCols + (i - 2 * dk);
-      else if (i < 2 * dk + kHCols + 2 * rank) src[k] = C + (i - 2 * dk - kHCols);
-      else src[k] = C + 2 * rank + h;
-      w[k] = i < n_in ? peek(P.pbuf + src[k]) : tagged(tag, 0.0f);
-    }
-    int bad = 0;
+  for (int k = 0; k < 3; ++k) {
+    const int i = min(tid + k * kPT, n_in - 1);
+    int r;
+    if (i < dk) r = h * dk + i;
+    else if (i < 2 * dk) r = K + h * dk + (i - dk);
+    else if (i < 2 * dk + kHCols) r = 2 * K + h * dv + half * kHCols + (i - 2 * dk);
+    else if (i < 2 * dk + kHCols + 2 * rank) r = C + (i - 2 * dk - kHCols);
+    else r = C + 2 * rank + h;
+    src[k] = P.pbuf + r;
+    w[k] = peek(src[k]);
+  }
+  // wait until the slots selected by `lr` (low-rank ones, or the others) carry the tag;
+  // every round re-reads all three slots, so its loads go out together
+  auto wait_slots = [&](bool lr) {
     Spin sp;
     while (true) {
       bool all = true;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) all &= (uint32_t)(w[k] >> 32) == tag;
-      if (all) break;
-      if (sp.stop(P)) { bad = 1; break; }
+      for (int k = 0; k < 3; ++k) {
+        const int i = tid + k * kPT;
+        const bool want = i < n_in && ((i >= i_lr) == lr);
+        all &= !want || (uint32_t)(w[k] >> 32) == tag;
+      }
+      if (all) return true;
+      if (sp.stop(P)) return false;
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
-        if ((uint32_t)(w[k] >> 32) != tag) w[k] = peek(P.pbuf + src[k]);
+      for (int k = 0; k < 3; ++k) {
+        const uint64_t r = peek(src[k]);
+        w[k] = (uint32_t)(w[k] >> 32) == tag ? w[k] : r;
+      }
     }
+  };
+  {
+    const int bad = !wait_slots(true);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int i = tid + k * kPT;
-      if (i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
+      if (i >= i_lr && i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
     if (__syncthreads_or(bad)) return false;
   }
@@ -549,7 +579,16 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
       else sm.s_gt[grow - dk] = sigmoid_f(mine);
     }
   }
-  __syncthreads();
+  {
+    // q, k, v
+    const int bad = !wait_slots(false);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int i = tid + k * kPT;
+      if (i < i_lr) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
+    }
+    if (__syncthreads_or(bad)) return false;
+  }
   // delta rule: lane (rg, cq) holds rows 8 rg .. + 8 of columns jl .. + 4 (block-local jl)
   const int rg = lane & 15, cq = lane >> 4;
   const int jl = wave * 16 + cq * 4, j = half * kHCols + jl, r0 = rg * 8;
