@@ -491,9 +491,8 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const int H = P.H, C = P.C, K = H * dk;
   const int h = blockIdx.x % H, half = blockIdx.x / H;
   float* Sl = P.S + (size_t)l * H * dk * dv;
-  // the head's inputs are polled word by word; the first projection block to start the
-  // layer starts the polling
-  if (!block_wait_flags(P, kFlagP, gridDim.x - kHSplit * H, tag, 1)) return false;
+  // the head's inputs are polled word by word from the start of the layer (32 blocks of
+  // ~2 KB a round, no flag first: the low-rank rows land early)
   // inputs: q [dk] | k [dk] | v [kHCols] | f_lr [rank] | g_lr [rank] | beta  (<= 3 per thread)
   constexpr int n_in = 2 * dk + kHCols + 2 * rank + 1;
   static_assert(n_in <= 3 * kPT, "head inputs");
