@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 752208047,
-                "sha256": "9a044ed7bf395e84ece43caa44200e9788facf7d5109f575f40a74af0d95fc30",
+STEP_TRAFFIC = {"bytes": 745148078,
+                "sha256": "16ac316743605046a34eb5ffd0ce40dd16428c42422373507399c61a9cbea09c",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
