@@ -422,7 +422,7 @@ __device__ __forceinline__ Roles make_roles(const PersistParams& P, int wave) {
 // Returns false on a failed wait.
 template <int U, bool OBLK>
 __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const Roles& R, int l,
-                                        uint32_t tag, ProjRegs<U>& pr) {
+                                        uint32_t tag, ProjRegs<U>& pr, OutRegs<U>* orr) {
   GLayer* Lt = (GLayer*)P.layers;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int D = P.D, C = P.C;
@@ -455,6 +455,9 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   __syncthreads();
   const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
   float accs[kPRows];
+  // an output block requests this layer's W_o rows now: they land during the dots, and the
+  // wait for the head blocks later has no loads queued ahead of its polls
+  if (OBLK) issue_out<U>(P, Lt[l], R.owr0, R.orw, *orr);
   dot_rows<U, kPRows>(pr.w, pr.d, R.wr1 - R.wr0, sm.xs, sm.xsum, nullptr, accs);
   // lane r finishes row wr0 + r: conv + SiLU + window roll for q/k/v channels
   float v = 0.0f;
@@ -723,8 +726,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
       OutRegs<U> orr;
       for (int l = 0; l < P.n_layers; ++l) {
         const uint32_t tag = tag0 + (uint32_t)l + 1u;
-        if (!phase_p<U, true>(P, sm, R, l, tag, pr)) return;
-        issue_out<U>(P, Lt[l], R.owr0, R.orw, orr);
+        if (!phase_p<U, true>(P, sm, R, l, tag, pr, &orr)) return;
         if (!phase_o<U>(P, sm, R, l, tag, orr)) return;
       }
     } else {
@@ -732,7 +734,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
       // it must not fall layers behind while it reads the residual stream
       if (__syncthreads_or(R.wr1 > R.wr0) == 0) return;
       for (int l = 0; l < P.n_layers; ++l)
-        if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr)) return;
+        if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr, nullptr)) return;
     }
   }
 }
