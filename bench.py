@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 745148078,
-                "sha256": "16ac316743605046a34eb5ffd0ce40dd16428c42422373507399c61a9cbea09c",
+STEP_TRAFFIC = {"bytes": 745144850,
+                "sha256": "298833178c0bca139dfeac267126fdbea3a7ff459b99c9e24ab6a086177f383b",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
