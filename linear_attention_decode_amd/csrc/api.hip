@@ -85,6 +85,7 @@ struct kda_model {
   bool pers_ok = false;
   int pers_blocks = 0;
   PersistLayer* d_layers = nullptr;
+  int8_t* mma_w = nullptr;          // projection rows and W_o of every layer, matrix-core order
   uint64_t* xchg = nullptr;         // exchange words (xbuf | pbuf | gbuf | obuf)
   int* err = nullptr;
   uint32_t epoch = 0;
@@ -359,21 +360,53 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
             (rank == 32 || rank == 64 || rank == 128);
   if (ok) {
     const int np_blocks = nb - 2 * d.n_heads;      // blocks with projection rows
-    const int nq = (m->C + 31) / 32;               // q/k/v rows, 32 per block
-    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks <= 256 && nq < np_blocks &&
-         (m->proj_rows - m->C + np_blocks - nq - 1) / (np_blocks - nq) <= 32;
+    const int nq = m->C / 32;                      // q/k/v rows, 32 per block
+    const int nl = (m->proj_rows - m->C + 15) / 16; // low-rank and beta rows, 16 per block
+    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks <= 256 && m->C % 32 == 0 &&
+         nq + nl <= np_blocks;
   }
   if (!ok) return hipSuccess;
+  // the rows the kernel streams, rearranged once for the matrix cores
+  const int D = d.d_model;
+  const size_t pw = mma_order_bytes(m->proj_rows, D), pd = mma_order_scales(m->proj_rows, D);
+  const size_t ow = mma_order_bytes(D, D), od = mma_order_scales(D, D);
+  const size_t per_layer = pw + ow + 2 * (pd + od);
+  hipError_t e = hipMalloc(&m->mma_w, per_layer * d.n_layers);
+  if (e != hipSuccess) return e;
   std::vector<PersistLayer> host(d.n_layers);
-  for (int l = 0; l < d.n_layers; ++l) {
+  for (int l = 0; l < d.n_layers && e == hipSuccess; ++l) {
     const LayerDev& L = m->layers[l];
     PersistLayer& P = host[l];
     P.seg[0] = L.wq; P.seg[1] = L.wk; P.seg[2] = L.wv; P.seg[3] = L.fa; P.seg[4] = L.ga; P.seg[5] = L.wbeta;
     P.fb = L.fb; P.gb = L.gb; P.wo = L.wo;
     P.conv_w = L.conv_w; P.a_log = L.a_log; P.dt_bias = L.dt_bias; P.o_norm_w = L.o_norm_w;
+    int8_t* base = m->mma_w + per_layer * l;
+    P.pw = base;
+    P.ow = base + pw;
+    P.pd = reinterpret_cast<const uint16_t*>(base + pw + ow);
+    P.od = P.pd + pd;
+    const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
+    MmaSource src{};
+    int first = 0;
+    for (int i = 0; i < 6; ++i) {
+      src.w[i] = P.seg[i].w;
+      src.d[i] = P.seg[i].d;
+      src.first[i] = first;
+      first += rows[i];
+    }
+    src.nseg = 6;
+    e = launch_mma_order(src, m->proj_rows, D, const_cast<int8_t*>(P.pw), const_cast<uint16_t*>(P.pd), nullptr);
+    if (e != hipSuccess) break;
+    MmaSource so{};
+    so.w[0] = L.wo.w;
+    so.d[0] = L.wo.d;
+    so.nseg = 1;
+    e = launch_mma_order(so, D, D, const_cast<int8_t*>(P.ow), const_cast<uint16_t*>(P.od), nullptr);
   }
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
   (void)layers;
-  hipError_t e = hipMalloc(&m->d_layers, sizeof(PersistLayer) * d.n_layers);
+  e = hipMalloc(&m->d_layers, sizeof(PersistLayer) * d.n_layers);
   if (e != hipSuccess) return e;
   e = hipMemcpy(m->d_layers, host.data(), sizeof(PersistLayer) * d.n_layers, hipMemcpyHostToDevice);
   if (e != hipSuccess) return e;
@@ -404,7 +437,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   p.timeout = (uint64_t)(khz > 0 ? khz : 100000) * 50;   // 50 ms of wall clock per wait
   p.o_first_block = ob0; p.o_blocks = nob;
-  p.q_blocks = (m->C + 31) / 32;
+  p.q_blocks = m->C / 32;
   m->pers_blocks = nb;
   m->pers_ok = true;
   return hipSuccess;
@@ -542,6 +575,7 @@ void kda_model_destroy(kda_model* m) {
   if (!m) return;
   drop_graph(m);
   if (m->d_layers) (void)hipFree(m->d_layers);
+  if (m->mma_w) (void)hipFree(m->mma_w);
   if (m->xchg) (void)hipFree(m->xchg);
   if (m->err) (void)hipFree(m->err);
   for (auto& t : m->pool) {

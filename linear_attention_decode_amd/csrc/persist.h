@@ -18,6 +18,11 @@ struct PackedMat {
 struct PersistLayer {
   PackedMat seg[6];               // W_q, W_k, W_v, F_a, G_a, W_beta  (rows [out][D])
   PackedMat fb, gb, wo;
+  // the fused projection rows and W_o rearranged for the matrix cores (mma_order_* below)
+  const int8_t* pw = nullptr;
+  const uint16_t* pd = nullptr;
+  const int8_t* ow = nullptr;
+  const uint16_t* od = nullptr;
   const float* conv_w = nullptr;
   const float* a_log = nullptr;
   const float* dt_bias = nullptr;
@@ -42,9 +47,26 @@ struct PersistParams {
   uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)
   int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection
   int q_blocks = 0;                      // projection blocks [0, q_blocks) take the q/k/v rows,
-                                         // 32 each; the rest share the low-rank and beta rows
+                                         // 32 each; the next ones the low-rank and beta rows,
+                                         // 16 each
 };
 constexpr int kMaxPersistBlocks = 1024;
+
+// Q8_0 rows [0, rows) of up to six stacked matrices (segment i starts at row first[i]) with
+// D columns, rearranged into the order the one-launch decode loads them in: tiles of 16
+// rows, each 16 rows x D bytes as [4 waves][D/512 runs][2 halves][64 lanes][16 bytes] with
+// the bytes as signed q (not q + 128), and the scales as [tile][4][64][D/512] fp16 bits.
+// Rows past `rows` are zero.  Sizes: mma_order_bytes / mma_order_scales per matrix.
+struct MmaSource {
+  const uint8_t* w[6];
+  const __half* d[6];
+  int first[6];
+  int nseg;
+};
+inline size_t mma_order_bytes(int rows, int D) { return (size_t)((rows + 15) / 16) * 16 * D; }
+inline size_t mma_order_scales(int rows, int D) { return (size_t)((rows + 15) / 16) * 16 * (D / 32); }
+hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, uint16_t* d,
+                            hipStream_t s);
 hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s);
 int persistent_max_blocks();            // co-resident blocks of one per CU, 0 if unavailable
 

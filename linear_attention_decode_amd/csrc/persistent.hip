@@ -14,18 +14,19 @@
 //      projection of the normalised heads and the residual.
 // Every block streams a slice of every matrix, and it requests the next slice as soon as it
 // has used the current one, so the weights of layer l + 1 are in flight while layer l's
-// later phases run.  The weight loads go through global-address-space pointers (no flat
-// accesses) with wave-uniform row addresses, so a wave issues all of its rows back to back.
+// later phases run.  The projections run on the int8 matrix cores: the Q8_0 bytes are the B
+// operand as they are stored, and the input vector enters as three 7-bit planes per run of
+// 128 elements (exact products, integer accumulation, the Q8_0 scales applied per block
+// afterwards).
 //
 // Blocks hand activations to each other as 64-bit words (tag << 32 | fp32 bits) written
 // and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
-// the token and layer.  Each producer block also posts a flag word: the projection blocks
-// when they start a layer (their consumers, the few head blocks, then poll their input
-// words directly), the head and output blocks when they are done (their many consumers
-// watch the flags -- one wave, a short sleep between polls -- and fetch the data words once
-// the first producer has posted, so that polling stays far below the weight stream).  A
-// consumer always checks the tag of every data word it uses.  Every wait is bounded: on a
-// timeout the block records an error word and every block leaves the kernel.
+// the token and layer.  The head blocks poll their input words directly from the start of
+// the layer; the head and output blocks also post a flag word when they are done, and their
+// many consumers watch the flags -- one wave, a short sleep between polls -- and fetch the
+// data words once the first producer has posted, so that polling stays far below the weight
+// stream.  A consumer always checks the tag of every data word it uses.  Every wait is
+// bounded: on a timeout the block records an error word and every block leaves the kernel.
 #include "kda_device.h"
 #include "persist.h"
 
@@ -35,8 +36,6 @@
 namespace kda {
 
 constexpr int kPT = 256;         // threads per block
-constexpr int kPRows = 8;        // max projection rows per wave
-constexpr int kORows = 4;        // max output-projection rows per wave
 constexpr int kHD = 128;         // d_k = d_v of the one-launch path
 constexpr int kHSplit = 2;       // head blocks per head
 constexpr int kHCols = kHD / kHSplit;   // value columns of one head block (16 per wave)
@@ -106,7 +105,7 @@ struct Spin {
   }
 };
 
-enum FlagPhase { kFlagP = 0, kFlagH = 1, kFlagO = 2 };
+enum FlagPhase { kFlagH = 1, kFlagO = 2 };
 
 __device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase, int i) {
   return P.flags + (size_t)phase * kMaxPersistBlocks + i;
@@ -144,50 +143,125 @@ __device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint3
   return __syncthreads_or(bad) == 0;
 }
 
-// This thread's tagged words p[0], p[stride], ..., p[(n - 1) stride] (n <= N) into w[]:
-// every load is issued at once, then each round re-issues the loads of all words not yet
-// tagged, so a round costs one memory trip however many words are missing.  Returns false
-// on a failed wait.
-template <int N>
-__device__ bool poll_words(const uint64_t* p, int stride, uint32_t tag, uint64_t (&w)[N], int n,
-                           const PersistParams& P) {
+// ---- matrix-core dots of the projections ----
+// A block's projection rows meet the input vector on v_mfma_i32_16x16x64_i8.  The input is
+// cut into runs of 128 elements (run rho = elements [128 rho, 128 rho + 128), one head of
+// the output projection's input); wave w owns runs rho = 4 t + w and holds, in lane j,
+// elements 128 rho + j and 128 rho + 64 + j of each (value 2 t + half).  Each run is split
+// into three signed 7-bit planes under a power-of-two scale (below), so that every product
+// with a Q8_0 weight byte is exact in the integer accumulator.  In one pair of MFMAs per run
+// lane group g (lanes 16 g .. 16 g + 15) carries Q8_0 block 4 rho + g (32 bytes, 16 per
+// MFMA) of row (lane & 15) in the B operand, and A row 4 i + p holds plane p of block i on
+// lane group i only, so accumulator row 4 g + p is plane p of block g alone and the block's
+// scale is applied afterwards (accumulator lane (n, g) holds rows 4 g .. 4 g + 3 of column
+// n).  Rows 4 g + 3 read a zero plane.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int run_elem(int k, int wave, int lane) {
+  return 512 * (k >> 1) + 128 * wave + 64 * (k & 1) + lane;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRor8>(v));
+  const int b = __float_as_int(v);
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
+}
+
+// This wave's NV tagged words of the runs it owns (NV = 2 per run) from buf into v[].  Every
+// load is issued at once; each round re-issues the loads of the words not yet tagged, so a
+// round costs one memory trip however many words are missing.  Returns false on a failed
+// wait (the values are then meaningless).
+template <int NV>
+__device__ bool poll_runs(const uint64_t* buf, uint32_t tag, float (&v)[NV], const PersistParams& P) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t* p = buf + run_elem(0, wave, lane);
+  uint64_t w[NV];
 #pragma unroll
-  for (int k = 0; k < N; ++k) w[k] = k < n ? peek(p + (size_t)k * stride) : tagged(tag, 0.0f);
+  for (int k = 0; k < NV; ++k) w[k] = peek(p + 512 * (k >> 1) + 64 * (k & 1));
   Spin sp;
+  bool ok = true;
   while (true) {
     bool all = true;
 #pragma unroll
-    for (int k = 0; k < N; ++k) all &= (uint32_t)(w[k] >> 32) == tag;
-    if (all) return true;
-    if (sp.stop(P)) return false;
+    for (int k = 0; k < NV; ++k) all &= (uint32_t)(w[k] >> 32) == tag;
+    if (all) break;
+    if (sp.stop(P)) { ok = false; break; }
 #pragma unroll
-    for (int k = 0; k < N; ++k)
-      if ((uint32_t)(w[k] >> 32) != tag) w[k] = peek(p + (size_t)k * stride);
+    for (int k = 0; k < NV; ++k)
+      if ((uint32_t)(w[k] >> 32) != tag) w[k] = peek(p + 512 * (k >> 1) + 64 * (k & 1));
   }
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = __uint_as_float((uint32_t)w[k]);
+  return ok;
 }
 
-// Block-wide fetch of NPT * kPT tagged words into dst[] (LDS), with the sums of every 16
-// consecutive words into dsum[] and each thread's sum of squares in ss.  Thread t takes words
-// t, t + kPT, ...; every load is issued before the first tag is checked, and only words not
-// yet tagged are polled again.  The 16 lanes t & ~15 .. hold one 16-word chunk.  Ends with a
-// barrier; returns block-uniform false on a failed wait.
-template <int NPT>
-__device__ bool fetch_vec(const uint64_t* buf, uint32_t tag, float* dst, float* dsum, float& ss,
-                          const PersistParams& P) {
-  const int tid = threadIdx.x;
-  uint64_t w[NPT];
-  const int bad = !poll_words<NPT>(buf + tid, kPT, tag, w, NPT, P);
-  ss = 0.0f;
+// The wave's runs as planes.  With s = 2^(6 - e), e the smallest exponent with
+// sqrt(ssw) < 2^e (ssw = the wave's sum of squares, so every |x| < 2^e), x s = x0 + x1 / 128
+// + x2 / 16384 + r with integers |x0|, |x1|, |x2| <= 64 and |r| <= 2^-15: an error of at
+// most 2^-20 of the 2-norm of the wave's 4 D / 1024 runs.  Every step is exact in fp32
+// except the three roundings to integers, done by adding 1.5 * 2^23 (which leaves the
+// integer in the low mantissa bits, whose low byte is its two's complement).  Plane p goes to
+// LDS bytes planes[p * D + element]; returns 1 / s.  Only this wave reads these bytes again.
+template <int NV, int D>
+__device__ __forceinline__ float quantize_runs(const float (&v)[NV], float ssw, int8_t* planes) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr float M = 12582912.0f;
+  const int e = (__builtin_amdgcn_frexp_expf(ssw) + 1) >> 1;
+  const float s = __builtin_amdgcn_ldexpf(1.0f, 6 - e);
 #pragma unroll
-  for (int k = 0; k < NPT; ++k) {
-    const float v = __uint_as_float((uint32_t)w[k]);
-    const int i = tid + k * kPT;
-    dst[i] = v;
-    ss += v * v;
-    const float cs = sum16(v);
-    if ((tid & 15) == 0) dsum[i >> 4] = cs;
+  for (int k = 0; k < NV; ++k) {
+    const float x = v[k];
+    const int i = run_elem(k, wave, lane);
+    const float t0 = fmaf(x, s, M), q0 = t0 - M, r0 = fmaf(x, s, -q0);
+    const float t1 = fmaf(r0, 128.0f, M), q1 = t1 - M, r1 = fmaf(r0, 128.0f, -q1);
+    const float t2 = fmaf(r1, 128.0f, M);
+    planes[i] = (int8_t)__float_as_uint(t0);
+    planes[D + i] = (int8_t)__float_as_uint(t1);
+    planes[2 * D + i] = (int8_t)__float_as_uint(t2);
   }
-  return __syncthreads_or(bad) == 0;
+  return __builtin_amdgcn_ldexpf(1.0f, e - 6);
+}
+
+// The A operands of the wave's runs (see above): lane (m, g) reads plane m & 3 of block
+// 4 rho + g when m >> 2 == g, else the zero plane 3.
+template <int NT, int D>
+__device__ __forceinline__ void run_operands(const int8_t* planes, i32x4 (&a)[NT][2]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int8_t* base = planes + ((m >> 2) == g ? (m & 3) : 3) * D + 128 * wave + 32 * g;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a[t][h] = *reinterpret_cast<const i32x4*>(base + 512 * t + 16 * h);
+}
+
+// Partial dots of the first ntiles (block-uniform) row tiles over the wave's runs: lane
+// (n, g) returns, in y[tile], inv_s times the sum over runs t of the Q8_0 scale of block
+// 4 (4 t + wave) + g of row 16 tile + n times that block's dot.
+template <int NT, int NTILE>
+__device__ __forceinline__ void mfma_tiles(const i32x4 (&a)[NT][2], const i32x4 (&w)[NTILE][NT][2],
+                                           const uint32_t (&d)[NTILE][NT], float inv_s, int ntiles,
+                                           float (&y)[NTILE]) {
+  const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile) {
+    float acc = 0.0f;
+    if (tile < ntiles) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][0], w[tile][t][0], zero, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][1], w[tile][t][1], c, 0, 0, 0);
+        const float v = fmaf((float)(c[1] * 128 + c[2]), 1.0f / 16384.0f, (float)c[0]);
+        acc = fmaf(h2f(d[tile][t]), v, acc);
+      }
+    }
+    y[tile] = acc * inv_s;
+  }
 }
 
 // Dot of one 16-byte Q8_0 chunk with 16 inputs held in registers.
@@ -204,81 +278,70 @@ __device__ __forceinline__ float q8_dot16(const uint4 w, const float4 (&x)[4]) {
   return s;
 }
 
-// Wave-wide dots of up to NR rows (the first n, n wave-uniform) whose chunks this lane holds
-// (chunk u * 64 + lane of each row) with the LDS vector xs (chunk sums in xsum).  The lane's
-// 16-element slices of xs are read once, as aligned float4s, for all rows.
-// With HSCALE, the 16-element chunk c of xs is scaled by hs[c / 8] (one head = 128 elements).
-template <int U, int NR, bool HSCALE = false>
-__device__ __forceinline__ void dot_rows(const uint4 (&w)[NR][U], const uint32_t (&d)[NR][U],
-                                         int n, const float* xs, const float* xsum,
-                                         const float* hs, float (&acc)[NR]) {
-  const int lane = threadIdx.x & 63;
-  float4 xv[U][4];
-  float xc[U], cs[U];
+// The projection weights of a block's rows [p0, p1) (p0 a multiple of 16, at most two tiles
+// of 16) of layer L in the operand layout above, read from the matrix-core order (every load
+// is 1 KB of consecutive bytes): the wave's runs of row p0 + 16 tile + (lane & 15) and the
+// scales of the lane's blocks.  Thread t < p1 - p0 also holds the conv taps and window of
+// row p0 + t (q/k/v channels).
+template <int U>
+struct ProjRegs {
+  i32x4 w[2][2 * U][2];    // [tile][run t][half]: 16 weight bytes (signed q)
+  uint32_t d[2][2 * U];    // fp16 bits of the scale of block 4 (4 t + wave) + (lane >> 4)
+  float4 cw;
+  float z0, z1, z2;        // conv window, oldest first
+};
+
+// 16 weight bytes, streamed once per token.
+__device__ __forceinline__ i32x4 wload_i(const int8_t* p) {
+  return __builtin_nontemporal_load((const KDA_GLOBAL i32x4*)p);
+}
+
+// Tile `tile` (16 rows) of a matrix in the matrix-core order: this lane's 2 x 2U chunks and
+// its 2U scales.
+template <int U>
+__device__ __forceinline__ void load_tile(const int8_t* w, const uint16_t* d, int tile,
+                                          i32x4 (&rw)[2 * U][2], uint32_t (&rd)[2 * U]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int8_t* wb = w + ((size_t)(tile * 4 + wave) * (4 * U) * 64 + lane) * 16;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int c = u * 64 + lane;
-    const float4* p = reinterpret_cast<const float4*>(xs + c * 16);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) xv[u][k] = p[k];
-    xc[u] = xsum[c];
-    cs[u] = HSCALE ? hs[c >> 3] : 1.0f;
+  for (int t = 0; t < 2 * U; ++t) {
+    rw[t][0] = wload_i(wb + (2 * t) * 1024);
+    rw[t][1] = wload_i(wb + (2 * t + 1) * 1024);
   }
+  const uint16_t* db = d + ((size_t)(tile * 4 + wave) * 64 + lane) * (2 * U);
+  if constexpr (U == 1) {
+    const uint32_t v = *(const KDA_GLOBAL uint32_t*)db;
+    rd[0] = v & 0xffffu;
+    rd[1] = v >> 16;
+  } else {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float a = 0.0f;
-    if (r < n) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float t = h2f(d[r][u]) * (q8_dot16(w[r][u], xv[u]) - 128.0f * xc[u]);
-        a += HSCALE ? t * cs[u] : t;
-      }
-      a = wave_sum(a);
+    for (int q = 0; q < U / 2; ++q) {
+      const u32x2 v = *(const KDA_GLOBAL u32x2*)(db + 4 * q);
+      rd[4 * q] = v[0] & 0xffffu;
+      rd[4 * q + 1] = v[0] >> 16;
+      rd[4 * q + 2] = v[1] & 0xffffu;
+      rd[4 * q + 3] = v[1] >> 16;
     }
-    acc[r] = a;
   }
 }
 
-// The projection weights of one wave's rows [r0, r1) of layer L (r0, r1 wave-uniform).
-template <int U>
-struct ProjRegs {
-  uint4 w[kPRows][U];
-  uint32_t d[kPRows][U];
-  float4 cw;               // lane r: conv taps of row r0 + r (q/k/v channels)
-  float z0, z1, z2;        // lane r: its conv window, oldest first
-};
-
 template <int U>
 __device__ __forceinline__ void issue_proj(const PersistParams& P, GLayer& L, const float* win,
-                                           int r0, int r1, ProjRegs<U>& R) {
-  const int lane = threadIdx.x & 63;
+                                           int p0, int p1, ProjRegs<U>& R) {
+  const int tid = threadIdx.x;
 #pragma unroll
-  for (int r = 0; r < kPRows; ++r) {
-    const int row = r0 + r;
+  for (int tile = 0; tile < 2; ++tile) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      R.w[r][u] = make_uint4(0, 0, 0, 0);
-      R.d[r][u] = 0;
+    for (int t = 0; t < 2 * U; ++t) {
+      R.w[tile][t][0] = R.w[tile][t][1] = i32x4{0, 0, 0, 0};
+      R.d[tile][t] = 0;
     }
-    if (row < r1) {
-      int first = 0, seg = 0;
-#pragma unroll
-      for (int i = 1; i < 6; ++i)
-        if (row >= P.seg_first[i]) { first = P.seg_first[i]; seg = i; }
-      const uint8_t* wr = L.seg[seg].w + (size_t)(row - first) * P.D;
-      const __half* dr = L.seg[seg].d + (size_t)(row - first) * (P.D / 32);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = u * 64 + lane;
-        R.w[r][u] = wload(wr + (size_t)c * 16);
-        R.d[r][u] = sload(dr + (c >> 1));
-      }
-    }
+    if (p0 + 16 * tile < p1) load_tile<U>(L.pw, L.pd, p0 / 16 + tile, R.w[tile], R.d[tile]);
   }
-  const int myrow = r0 + lane;
+  const int myrow = p0 + tid;
   R.cw = make_float4(0.f, 0.f, 0.f, 0.f);
   R.z0 = R.z1 = R.z2 = 0.0f;
-  if (lane < kPRows && myrow < r1 && myrow < P.C) {
+  if (myrow < p1 && myrow < P.C) {
     R.cw = gload4(L.conv_w + (size_t)myrow * 4);
     R.z0 = *gp(win + myrow);
     R.z1 = *gp(win + P.C + myrow);
@@ -286,36 +349,17 @@ __device__ __forceinline__ void issue_proj(const PersistParams& P, GLayer& L, co
   }
 }
 
-// The output-projection weights of one wave's rows [r0, r0 + n).
+// The output-projection weights of band ob (rows [16 ob, 16 ob + 16)), as for ProjRegs (the
+// input is the V = D head outputs).
 template <int U>
 struct OutRegs {
-  uint4 w[kORows][U];
-  uint32_t d[kORows][U];
+  i32x4 w[1][2 * U][2];
+  uint32_t d[1][2 * U];
 };
 
 template <int U>
-__device__ __forceinline__ void issue_out(const PersistParams& P, GLayer& L, int r0, int n,
-                                          OutRegs<U>& R) {
-  const int lane = threadIdx.x & 63;
-  const int KO = P.H * P.dv;
-#pragma unroll
-  for (int r = 0; r < kORows; ++r) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      R.w[r][u] = make_uint4(0, 0, 0, 0);
-      R.d[r][u] = 0;
-    }
-    if (r < n) {
-      const uint8_t* wr = L.wo.w + (size_t)(r0 + r) * KO;
-      const __half* dr = L.wo.d + (size_t)(r0 + r) * (KO / 32);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int c = u * 64 + lane;
-        R.w[r][u] = wload(wr + (size_t)c * 16);
-        R.d[r][u] = sload(dr + (c >> 1));
-      }
-    }
-  }
+__device__ __forceinline__ void issue_out(GLayer& L, int ob, OutRegs<U>& R) {
+  load_tile<U>(L.ow, L.od, ob, R.w[0], R.d[0]);
 }
 
 // A head block owns value columns [half * kHCols, + kHCols) of head h.  Its registers: wave
@@ -368,117 +412,112 @@ __device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, co
 
 // LDS of one block.
 struct Smem {
-  alignas(16) float xs[4096];          // x, then (O blocks) the normalised heads
-  float xsum[256];         // 16-element chunk sums of xs
+  alignas(16) int8_t planes[4 * 2048];  // [4][D] input planes of the matrix-core dots; [3] = 0
+  alignas(16) float part[32 * 16];      // [row][wave * 4 + g] partial dots of the block's rows
   float red[8];
-  float xres[4 * kORows];  // this O block's residual rows
+  float xres[16];          // this O block's residual rows
   alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
   alignas(16) float s_al[kHD];     // head block: alpha rows
   alignas(16) float s_gt[kHCols];  // head block: output-gate columns
-  float s_hs[64];                  // O blocks: per-head RMSNorm scales
 };
 
 // Static roles of block b: its projection rows, and whether it runs a head or an
 // output-projection band.
 struct Roles {
-  int wr0, wr1;            // this wave's projection rows (wave-uniform)
-  int ob, or0, owr0, orw;  // O band index, block's first row, wave's first row, rows/wave
+  int p0, p1;              // this block's projection rows
+  int ob, or0;             // O band index and its first row (16 rows per band)
 };
 
-__device__ __forceinline__ Roles make_roles(const PersistParams& P, int wave) {
+__device__ __forceinline__ Roles make_roles(const PersistParams& P) {
   Roles R;
   // projection rows go to blocks [kHSplit H, nb) (head blocks keep their loads for the
   // state): q/k/v rows 32 per block to the first q_blocks, then the low-rank and beta rows
-  // spread thin over the rest, so that the rows the head blocks need first (their gates)
-  // are finished early
-  const int b = blockIdx.x - kHSplit * P.H, nb = gridDim.x - kHSplit * P.H;
-  const int C = P.C, nl = nb - P.q_blocks;
-  const int rl = (P.proj_rows - C + nl - 1) / nl;
-  int p0, p1, rp;
+  // one tile of 16 per block, so that the rows the head blocks need first (their gates) are
+  // finished early; blocks past them have no rows
+  const int b = blockIdx.x - kHSplit * P.H;
+  const int C = P.C;
   if (b < 0) {
-    p0 = p1 = rp = 0;
+    R.p0 = R.p1 = 0;
   } else if (b < P.q_blocks) {
-    rp = 32;
-    p0 = min(C, b * 32);
-    p1 = min(C, p0 + 32);
+    R.p0 = min(C, b * 32);
+    R.p1 = min(C, R.p0 + 32);
   } else {
-    rp = rl;
-    p0 = min(P.proj_rows, C + (b - P.q_blocks) * rl);
-    p1 = min(P.proj_rows, p0 + rl);
+    R.p0 = min(P.proj_rows, C + (b - P.q_blocks) * 16);
+    R.p1 = min(P.proj_rows, R.p0 + 16);
   }
-  const int rpw = (rp + 3) / 4;
-  R.wr0 = min(p1, p0 + wave * rpw);
-  R.wr1 = min(p1, R.wr0 + rpw);
-  const int ro = P.D / P.o_blocks;
   R.ob = (int)blockIdx.x - P.o_first_block;
-  R.orw = ro / 4;
-  R.or0 = R.ob * ro;
-  R.owr0 = R.or0 + wave * R.orw;
+  R.or0 = R.ob * 16;
   return R;
 }
 
-// P phase of layer l (blocks [H, nb)): wait for x_l, RMSNorm, this block's projection rows,
-// conv epilogue; the next layer's slice is requested as soon as this one is used.
-// Returns false on a failed wait.
+// P phase of layer l (blocks [kHSplit H, nb)): wait for x_l, RMSNorm, this block's
+// projection rows, conv epilogue; the next layer's slice is requested as soon as this one is
+// used.  Returns false on a failed wait.
 template <int U, bool OBLK>
 __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const Roles& R, int l,
                                         uint32_t tag, ProjRegs<U>& pr, OutRegs<U>* orr) {
+  constexpr int D = 1024 * U, NV = 4 * U, NT = 2 * U;
   GLayer* Lt = (GLayer*)P.layers;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int D = P.D, C = P.C;
+  const int C = P.C;
   float* win = P.win + (size_t)l * 3 * C;
-  float ss = 0.0f;
+  float v[NV];
+  int bad = 0;
   if (l == 0) {
-    for (int i = tid; i < D; i += kPT) {
-      const float v = *gp(P.x_in + i);
-      sm.xs[i] = v;
-      ss += v * v;
-      const float cs = sum16(v);
-      if ((tid & 15) == 0) sm.xsum[i >> 4] = cs;
-    }
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NV; ++k) v[k] = *gp(P.x_in + run_elem(k, wave, lane));
   } else {
     // x_l: once the first O block of layer l - 1 has posted (they finish together), fetch
-    // the tagged words of x
+    // the tagged words of the wave's runs
     if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, 1)) return false;
-    if (!fetch_vec<4 * U>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, sm.xs, sm.xsum, ss, P)) return false;
+    bad = !poll_runs<NV>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, v, P);
   }
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) ss = fmaf(v[k], v[k], ss);
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
-  if (OBLK && tid < 4 * R.orw) sm.xres[tid] = sm.xs[R.or0 + tid];
-  // the flag says "this layer's projections are under way": the head blocks start polling
-  // their input words (flags are hints; every data word carries its own tag).  The
-  // prefetched weights have landed by now; retiring them first keeps the dots below from
-  // waiting for the flag store.
-  retire_vmem();
-  if (tid == 0) put(flag_slot(P, kFlagP, blockIdx.x - kHSplit * P.H), tag, 0.0f);
-  __syncthreads();
-  const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
-  float accs[kPRows];
-  // an output block requests this layer's W_o rows now: they land during the dots, and the
-  // wait for the head blocks later has no loads queued ahead of its polls
-  if (OBLK) issue_out<U>(P, Lt[l], R.owr0, R.orw, *orr);
-  dot_rows<U, kPRows>(pr.w, pr.d, R.wr1 - R.wr0, sm.xs, sm.xsum, nullptr, accs);
-  // lane r finishes row wr0 + r: conv + SiLU + window roll for q/k/v channels
-  float v = 0.0f;
+  if (OBLK) {
 #pragma unroll
-  for (int r = 0; r < kPRows; ++r)
-    if (lane == r) v = accs[r] * sc;
-  const int row = R.wr0 + lane;
-  const bool mine = lane < kPRows && row < R.wr1;
-  const float pre = v;
-  if (mine) {
-    if (row < C) v = silu_f(pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * v);
-    put(P.pbuf + row, tag, v);
+    for (int k = 0; k < NV; ++k) {
+      const int i = run_elem(k, wave, lane) - R.or0;
+      if (i >= 0 && i < 16) sm.xres[i] = v[k];
+    }
+    // this layer's W_o rows: they land during the dots, and the wait for the head blocks
+    // later has no loads queued ahead of its polls
+    issue_out<U>(Lt[l], R.ob, *orr);
   }
-  // off the critical path: roll the conv window, request the next layer's slice
-  if (mine && row < C) {
-    float* z = win + row;
-    *gpw(z) = pr.z1;
-    *gpw(z + C) = pr.z2;
-    *gpw(z + 2 * C) = pre;
+  const float inv_s = quantize_runs<NV, D>(v, ss, sm.planes);
+  i32x4 a[NT][2];
+  run_operands<NT, D>(sm.planes, a);
+  const int rows = R.p1 - R.p0, ntiles = (rows + 15) >> 4;
+  float y[2];
+  mfma_tiles<NT, 2>(a, pr.w, pr.d, inv_s, ntiles, y);
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile)
+    if (tile < ntiles) sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
+  if (__syncthreads_or(bad)) return false;
+  // thread t finishes row p0 + t: RMSNorm scale, conv + SiLU + window roll for q/k/v channels
+  if (tid < rows) {
+    const int row = R.p0 + tid;
+    const float4* q = reinterpret_cast<const float4*>(sm.part + 16 * tid);
+    const float4 s0 = q[0], s1 = q[1], s2 = q[2], s3 = q[3];
+    const float sum = ((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)) +
+                      ((s2.x + s2.y) + (s2.z + s2.w)) + ((s3.x + s3.y) + (s3.z + s3.w));
+    const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
+    const float pre = sum * sc;
+    float o = pre;
+    if (row < C) o = silu_f(pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * pre);
+    put(P.pbuf + row, tag, o);
+    // off the critical path: roll the conv window
+    if (row < C) {
+      float* z = win + row;
+      *gpw(z) = pr.z1;
+      *gpw(z + C) = pr.z2;
+      *gpw(z + 2 * C) = pre;
+    }
   }
-  if (l + 1 < P.n_layers) issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.wr0, R.wr1, pr);
+  if (l + 1 < P.n_layers) issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.p0, R.p1, pr);
   return true;
 }
 
@@ -660,47 +699,59 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
 
 // O phase of layer l: this band's output-projection rows of the normalised heads, plus the
 // residual; the last layer also writes the output row.  The heads' RMSNorm scales come from
-// the per-wave partial sums of o^2 that the head blocks post after their outputs.
+// the per-wave partial sums of o^2 that the head blocks post after their outputs; run t of
+// wave w is head 4 t + w, so each wave needs the scales of its own heads only.
 template <int U>
 __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const Roles& R, int l,
                                         uint32_t tag, OutRegs<U>& orr) {
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int D = P.D, H = P.H, V = H * kHD;
+  constexpr int D = 1024 * U, NV = 4 * U, NT = 2 * U;
   constexpr int kParts = kHSplit * 4;                // o^2 partials per head
-  // once the first head block has posted, fetch the output words
-  if (!block_wait_flags(P, kFlagH, kHSplit * H, tag, 1)) return false;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // once the first head block has posted, fetch the output words of the wave's heads and
+  // their partials (lane kParts t + i: partial i of head 4 t + wave)
+  if (!block_wait_flags(P, kFlagH, kHSplit * P.H, tag, 1)) return false;
+  const bool has = lane < kParts * NT;
+  const uint64_t* src = P.obuf + D + (4 * (has ? lane / kParts : 0) + wave) * kParts + lane % kParts;
+  uint64_t pw = has ? peek(src) : tagged(tag, 0.0f);
+  float v[NV];
+  int bad = !poll_runs<NV>(P.obuf, tag, v, P);
   {
-    const uint64_t* src = P.obuf + V + tid;
-    const bool has = tid < H * kParts;
-    uint64_t w = has ? peek(src) : tagged(tag, 0.0f);
-    float ssd;
-    bool ok = fetch_vec<4 * U>(P.obuf, tag, sm.xs, sm.xsum, ssd, P);   // ends with a barrier
-    int bad = !ok;
     Spin sp;
-    while (!bad && (uint32_t)(w >> 32) != tag) {
+    while (!bad && (uint32_t)(pw >> 32) != tag) {
       if (sp.stop(P)) bad = 1;
-      else w = peek(src);
+      else pw = peek(src);
     }
-    float v = __uint_as_float((uint32_t)w);
-    // the kParts partials of a head sit on consecutive lanes
-    v = group_sum(v, kParts);
-    if (has && tid % kParts == 0) sm.s_hs[tid / kParts] = 1.0f / sqrtf(v / (float)kHD + P.eps);
-    if (__syncthreads_or(bad)) return false;
   }
-  float accs[kORows];
-  dot_rows<U, kORows, true>(orr.w, orr.d, R.orw, sm.xs, sm.xsum, sm.s_hs, accs);
-  float v = 0.0f;
+  // the normalised heads (run t = head 4 t + wave), then their planes
+  const int ps = __float_as_int(group_sum(__uint_as_float((uint32_t)pw), kParts));
+  float ss = 0.0f;
 #pragma unroll
-  for (int r = 0; r < kORows; ++r)
-    if (lane == r) v = accs[r];
-  if (lane < R.orw) {
-    const int row = R.owr0 + lane;
-    const float xn = sm.xres[row - R.or0] + v;
+  for (int t = 0; t < NT; ++t) {
+    const float hs = 1.0f / sqrtf(__int_as_float(__builtin_amdgcn_readlane(ps, kParts * t)) / (float)kHD + P.eps);
+    v[2 * t] *= hs;
+    v[2 * t + 1] *= hs;
+    ss = fmaf(v[2 * t], v[2 * t], ss);
+    ss = fmaf(v[2 * t + 1], v[2 * t + 1], ss);
+  }
+  const float inv_s = quantize_runs<NV, D>(v, wave_sum(ss), sm.planes);
+  i32x4 a[NT][2];
+  run_operands<NT, D>(sm.planes, a);
+  float y[1];
+  mfma_tiles<NT, 1>(a, orr.w, orr.d, inv_s, 1, y);
+  sm.part[(lane & 15) * 16 + 4 * wave + (lane >> 4)] = y[0];
+  if (__syncthreads_or(bad)) return false;
+  if (tid < 16) {
+    const int row = R.or0 + tid;
+    const float4* q = reinterpret_cast<const float4*>(sm.part + 16 * tid);
+    const float4 s0 = q[0], s1 = q[1], s2 = q[2], s3 = q[3];
+    const float sum = ((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)) +
+                      ((s2.x + s2.y) + (s2.z + s2.w)) + ((s3.x + s3.y) + (s3.z + s3.w));
+    const float xn = sm.xres[tid] + sum;
     put(P.xbuf + (size_t)(l & 1) * D + row, tag, xn);
     if (l + 1 == P.n_layers) *gpw(P.y_out + row) = xn;
+    // the band's words precede its flag in this wave's store order
+    if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
   }
-  __syncthreads();
-  if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
   return true;
 }
 
@@ -711,8 +762,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
 template <int U, int CPR, int ROLE>
 __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   GLayer* Lt = (GLayer*)P.layers;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const Roles R = make_roles(P, wave);
+  const Roles R = make_roles(P);
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
   if constexpr (ROLE == 1) {
     HeadRegs<CPR> hr;
@@ -720,8 +770,11 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
     for (int l = 0; l < P.n_layers; ++l)
       if (!phase_h<CPR>(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
   } else {
+    // the zero plane of the wave's runs (no other wave reads them)
+#pragma unroll
+    for (int k = 0; k < 4 * U; ++k) sm.planes[3 * 1024 * U + run_elem(k, threadIdx.x >> 6, threadIdx.x & 63)] = 0;
     ProjRegs<U> pr;
-    issue_proj<U>(P, Lt[0], P.win, R.wr0, R.wr1, pr);
+    issue_proj<U>(P, Lt[0], P.win, R.p0, R.p1, pr);
     if constexpr (ROLE == 2) {
       OutRegs<U> orr;
       for (int l = 0; l < P.n_layers; ++l) {
@@ -732,7 +785,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
     } else {
       // a block left without projection rows has nothing to do: no phase waits for it, and
       // it must not fall layers behind while it reads the residual stream
-      if (__syncthreads_or(R.wr1 > R.wr0) == 0) return;
+      if (__syncthreads_or(R.p1 > R.p0) == 0) return;
       for (int l = 0; l < P.n_layers; ++l)
         if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr, nullptr)) return;
     }
@@ -747,6 +800,50 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const Persist
   if (b < kHSplit * P.H) run_role<U, CPR, 1>(P, sm);
   else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm);
   else run_role<U, CPR, 0>(P, sm);
+}
+
+// One thread per 16-byte chunk of the matrix-core order (persist.h): chunk
+// c = (((tile * 4 + wave) * 2U + t) * 2 + h) * 64 + lane holds row 16 tile + (lane & 15),
+// columns 128 (4 t + wave) + 32 (lane >> 4) + 16 h .. + 16, flipped from q + 128 to q; the
+// h = 0 chunk also places the scale of that row's block 16 t + 4 wave + (lane >> 4).
+template <int U>
+__global__ void mma_order_kernel(const MmaSource src, int rows, int8_t* __restrict__ w,
+                                 uint16_t* __restrict__ d, int64_t nchunks) {
+  constexpr int D = 1024 * U;
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  const int lane = (int)(c % 64);
+  int64_t r = c / 64;
+  const int h = (int)(r % 2);
+  r /= 2;
+  const int t = (int)(r % (2 * U));
+  r /= 2 * U;
+  const int wave = (int)(r % 4);
+  const int64_t tile = r / 4;
+  const int64_t row = tile * 16 + (lane & 15);
+  const int col = 128 * (4 * t + wave) + 32 * (lane >> 4) + 16 * h;
+  u32x4 out = {0u, 0u, 0u, 0u};
+  uint16_t sc = 0;
+  if (row < rows) {
+    int seg = 0;
+    for (int i = 1; i < src.nseg; ++i)
+      if (row >= src.first[i]) seg = i;
+    const int64_t rr = row - src.first[seg];
+    out = *reinterpret_cast<const u32x4*>(src.w[seg] + rr * D + col) ^ 0x80808080u;
+    sc = __half_as_ushort(src.d[seg][rr * (D / 32) + col / 32]);
+  }
+  *reinterpret_cast<u32x4*>(w + c * 16) = out;
+  if (h == 0) d[((tile * 4 + wave) * 64 + lane) * (2 * U) + t] = sc;
+}
+
+hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, uint16_t* d,
+                            hipStream_t s) {
+  if ((D != 1024 && D != 2048) || rows < 1 || src.nseg < 1 || src.nseg > 6) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)((rows + 15) / 16) * D;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (D == 1024) mma_order_kernel<1><<<blocks, 256, 0, s>>>(src, rows, w, d, n);
+  else mma_order_kernel<2><<<blocks, 256, 0, s>>>(src, rows, w, d, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s) {
