@@ -141,8 +141,7 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
 /* Queries.  KDA_Q_PERSISTENT: number of blocks of the one-launch decode, 0 if the model is
  * not eligible (it needs Q8_0 weights, a pre-norm residual stack, d_k = d_v = 128,
  * H*d_v = D in {1024, 2048}, rank_f = rank_g in {32, 64, 128}, H <= 32, and one
- * co-resident block per CU with 2 H + D/16 <= CUs and enough blocks for the projection
- * rows: C/32 + ceil((proj_rows - C)/16) <= CUs - 2 H).  For it kda_model_create allocates
+ * co-resident block per CU with 2 H + D/32 + C/48 + ceil((proj_rows - C)/16) <= CUs).  For it kda_model_create allocates
  * ~130 KB of exchange words, flags and layer table, and a copy of every layer's projection
  * rows and W_o rearranged for the matrix cores (about D*(proj_rows + D)*17/16 bytes per
  * layer; 17.4 MB at D = 2048): the one-launch decode reads that copy, so later changes to

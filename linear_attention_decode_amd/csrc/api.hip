@@ -352,18 +352,17 @@ size_t exchange_words(const kda_model* m) {
 hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const kda_dims& d = m->d;
   const int nb = persistent_max_blocks();
-  const int ob0 = 2 * d.n_heads, nob = d.d_model / 16;
+  const int ob0 = 2 * d.n_heads, nob = d.d_model / 32;
   const int rank = d.rank_f;
   bool ok = nb > 0 && nb <= kMaxPersistBlocks && d.wtype == KDA_Q8_0 && d.prenorm_residual &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
             (rank == 32 || rank == 64 || rank == 128);
   if (ok) {
-    const int np_blocks = nb - 2 * d.n_heads;      // blocks with projection rows
-    const int nq = m->C / 32;                      // q/k/v rows, 32 per block
-    const int nl = (m->proj_rows - m->C + 15) / 16; // low-rank and beta rows, 16 per block
-    ok = d.n_heads <= 32 && ob0 + nob <= nb && np_blocks <= 256 && m->C % 32 == 0 &&
-         nq + nl <= np_blocks;
+    // heads, output bands of 32 rows, q/k/v rows 48 per block, low-rank and beta rows 16 per
+    // block
+    const int nq = m->C / 48, nl = (m->proj_rows - m->C + 15) / 16;
+    ok = d.n_heads <= 32 && m->C % 48 == 0 && ob0 + nob + nq + nl <= nb;
   }
   if (!ok) return hipSuccess;
   // the rows the kernel streams, rearranged once for the matrix cores
@@ -437,7 +436,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   p.timeout = (uint64_t)(khz > 0 ? khz : 100000) * 50;   // 50 ms of wall clock per wait
   p.o_first_block = ob0; p.o_blocks = nob;
-  p.q_blocks = m->C / 32;
+  p.q_blocks = m->C / 48;
   m->pers_blocks = nb;
   m->pers_ok = true;
   return hipSuccess;

@@ -45,10 +45,11 @@ struct PersistParams {
   int* err = nullptr;                    // nonzero after a wait timed out
   uint64_t timeout = 0;                  // wall-clock ticks a wait may take
   uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)
-  int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection
-  int q_blocks = 0;                      // projection blocks [0, q_blocks) take the q/k/v rows,
-                                         // 32 each; the next ones the low-rank and beta rows,
-                                         // 16 each
+  int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection,
+                                         // 32 rows each
+  int q_blocks = 0;                      // the projection blocks after them: the first q_blocks
+                                         // take the q/k/v rows, 48 each, the next ones the
+                                         // low-rank and beta rows, 16 each
 };
 constexpr int kMaxPersistBlocks = 1024;
 

@@ -38,6 +38,8 @@ namespace kda {
 constexpr int kPT = 256;         // threads per block
 constexpr int kHD = 128;         // d_k = d_v of the one-launch path
 constexpr int kHSplit = 2;       // head blocks per head
+constexpr int kPTiles = 3;       // 16-row tiles of a projection block (48 q/k/v rows)
+constexpr int kOTiles = 2;       // 16-row tiles of an output band (32 rows)
 constexpr int kHCols = kHD / kHSplit;   // value columns of one head block (16 per wave)
 
 using GLayer = const KDA_CONST PersistLayer;
@@ -278,15 +280,15 @@ __device__ __forceinline__ float q8_dot16(const uint4 w, const float4 (&x)[4]) {
   return s;
 }
 
-// The projection weights of a block's rows [p0, p1) (p0 a multiple of 16, at most two tiles
-// of 16) of layer L in the operand layout above, read from the matrix-core order (every load
+// The projection weights of a block's rows [p0, p1) (p0 a multiple of 16, at most kPTiles
+// tiles of 16) of layer L in the operand layout above, read from the matrix-core order (every load
 // is 1 KB of consecutive bytes): the wave's runs of row p0 + 16 tile + (lane & 15) and the
 // scales of the lane's blocks.  Thread t < p1 - p0 also holds the conv taps and window of
 // row p0 + t (q/k/v channels).
 template <int U>
 struct ProjRegs {
-  i32x4 w[2][2 * U][2];    // [tile][run t][half]: 16 weight bytes (signed q)
-  uint32_t d[2][2 * U];    // fp16 bits of the scale of block 4 (4 t + wave) + (lane >> 4)
+  i32x4 w[kPTiles][2 * U][2];   // [tile][run t][half]: 16 weight bytes (signed q)
+  uint32_t d[kPTiles][2 * U];    // fp16 bits of the scale of block 4 (4 t + wave) + (lane >> 4)
   float4 cw;
   float z0, z1, z2;        // conv window, oldest first
 };
@@ -330,7 +332,7 @@ __device__ __forceinline__ void issue_proj(const PersistParams& P, GLayer& L, co
                                            int p0, int p1, ProjRegs<U>& R) {
   const int tid = threadIdx.x;
 #pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
+  for (int tile = 0; tile < kPTiles; ++tile) {
 #pragma unroll
     for (int t = 0; t < 2 * U; ++t) {
       R.w[tile][t][0] = R.w[tile][t][1] = i32x4{0, 0, 0, 0};
@@ -349,17 +351,18 @@ __device__ __forceinline__ void issue_proj(const PersistParams& P, GLayer& L, co
   }
 }
 
-// The output-projection weights of band ob (rows [16 ob, 16 ob + 16)), as for ProjRegs (the
+// The output-projection weights of band ob (rows [32 ob, 32 ob + 32)), as for ProjRegs (the
 // input is the V = D head outputs).
 template <int U>
 struct OutRegs {
-  i32x4 w[1][2 * U][2];
-  uint32_t d[1][2 * U];
+  i32x4 w[kOTiles][2 * U][2];
+  uint32_t d[kOTiles][2 * U];
 };
 
 template <int U>
 __device__ __forceinline__ void issue_out(GLayer& L, int ob, OutRegs<U>& R) {
-  load_tile<U>(L.ow, L.od, ob, R.w[0], R.d[0]);
+#pragma unroll
+  for (int tile = 0; tile < kOTiles; ++tile) load_tile<U>(L.ow, L.od, kOTiles * ob + tile, R.w[tile], R.d[tile]);
 }
 
 // A head block owns value columns [half * kHCols, + kHCols) of head h.  Its registers: wave
@@ -413,49 +416,47 @@ __device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, co
 // LDS of one block.
 struct Smem {
   alignas(16) int8_t planes[4 * 2048];  // [4][D] input planes of the matrix-core dots; [3] = 0
-  alignas(16) float part[32 * 16];      // [row][wave * 4 + g] partial dots of the block's rows
+  alignas(16) float part[48 * 16];      // [row][wave * 4 + g] partial dots of the block's rows
   float red[8];
-  float xres[16];          // this O block's residual rows
+  float xres[32];          // an output block's residual rows
   alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
   alignas(16) float s_al[kHD];     // head block: alpha rows
   alignas(16) float s_gt[kHCols];  // head block: output-gate columns
 };
 
-// Static roles of block b: its projection rows, and whether it runs a head or an
-// output-projection band.
+// Static roles of block b: [0, kHSplit H) heads, then P.o_blocks output bands of 32 rows,
+// then the projection blocks: q/k/v rows 48 per block to the first q_blocks, then the
+// low-rank and beta rows one tile of 16 per block, so that the rows the head blocks need
+// first (their gates) are finished early; blocks past them have no rows.
 struct Roles {
   int p0, p1;              // this block's projection rows
-  int ob, or0;             // O band index and its first row (16 rows per band)
+  int ob, or0;             // output band index and its first row
 };
 
 __device__ __forceinline__ Roles make_roles(const PersistParams& P) {
   Roles R;
-  // projection rows go to blocks [kHSplit H, nb) (head blocks keep their loads for the
-  // state): q/k/v rows 32 per block to the first q_blocks, then the low-rank and beta rows
-  // one tile of 16 per block, so that the rows the head blocks need first (their gates) are
-  // finished early; blocks past them have no rows
-  const int b = blockIdx.x - kHSplit * P.H;
+  const int b = blockIdx.x - P.o_first_block - P.o_blocks;
   const int C = P.C;
   if (b < 0) {
     R.p0 = R.p1 = 0;
   } else if (b < P.q_blocks) {
-    R.p0 = min(C, b * 32);
-    R.p1 = min(C, R.p0 + 32);
+    R.p0 = min(C, b * 16 * kPTiles);
+    R.p1 = min(C, R.p0 + 16 * kPTiles);
   } else {
     R.p0 = min(P.proj_rows, C + (b - P.q_blocks) * 16);
     R.p1 = min(P.proj_rows, R.p0 + 16);
   }
   R.ob = (int)blockIdx.x - P.o_first_block;
-  R.or0 = R.ob * 16;
+  R.or0 = R.ob * 16 * kOTiles;
   return R;
 }
 
-// P phase of layer l (blocks [kHSplit H, nb)): wait for x_l, RMSNorm, this block's
-// projection rows, conv epilogue; the next layer's slice is requested as soon as this one is
-// used.  Returns false on a failed wait.
-template <int U, bool OBLK>
+// P phase of layer l (projection blocks): wait for x_l, RMSNorm, this block's projection
+// rows, conv epilogue; the next layer's slice is requested as soon as this one is used.
+// Returns false on a failed wait.
+template <int U>
 __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const Roles& R, int l,
-                                        uint32_t tag, ProjRegs<U>& pr, OutRegs<U>* orr) {
+                                        uint32_t tag, ProjRegs<U>& pr) {
   constexpr int D = 1024 * U, NV = 4 * U, NT = 2 * U;
   GLayer* Lt = (GLayer*)P.layers;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -477,24 +478,14 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   for (int k = 0; k < NV; ++k) ss = fmaf(v[k], v[k], ss);
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
-  if (OBLK) {
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = run_elem(k, wave, lane) - R.or0;
-      if (i >= 0 && i < 16) sm.xres[i] = v[k];
-    }
-    // this layer's W_o rows: they land during the dots, and the wait for the head blocks
-    // later has no loads queued ahead of its polls
-    issue_out<U>(Lt[l], R.ob, *orr);
-  }
   const float inv_s = quantize_runs<NV, D>(v, ss, sm.planes);
   i32x4 a[NT][2];
   run_operands<NT, D>(sm.planes, a);
   const int rows = R.p1 - R.p0, ntiles = (rows + 15) >> 4;
-  float y[2];
-  mfma_tiles<NT, 2>(a, pr.w, pr.d, inv_s, ntiles, y);
+  float y[kPTiles];
+  mfma_tiles<NT, kPTiles>(a, pr.w, pr.d, inv_s, ntiles, y);
 #pragma unroll
-  for (int tile = 0; tile < 2; ++tile)
+  for (int tile = 0; tile < kPTiles; ++tile)
     if (tile < ntiles) sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
   if (__syncthreads_or(bad)) return false;
   // thread t finishes row p0 + t: RMSNorm scale, conv + SiLU + window roll for q/k/v channels
@@ -736,17 +727,20 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   const float inv_s = quantize_runs<NV, D>(v, wave_sum(ss), sm.planes);
   i32x4 a[NT][2];
   run_operands<NT, D>(sm.planes, a);
-  float y[1];
-  mfma_tiles<NT, 1>(a, orr.w, orr.d, inv_s, 1, y);
-  sm.part[(lane & 15) * 16 + 4 * wave + (lane >> 4)] = y[0];
+  float y[kOTiles];
+  mfma_tiles<NT, kOTiles>(a, orr.w, orr.d, inv_s, kOTiles, y);
+#pragma unroll
+  for (int tile = 0; tile < kOTiles; ++tile)
+    sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
   if (__syncthreads_or(bad)) return false;
-  if (tid < 16) {
+  if (tid < 16 * kOTiles) {
     const int row = R.or0 + tid;
     const float4* q = reinterpret_cast<const float4*>(sm.part + 16 * tid);
     const float4 s0 = q[0], s1 = q[1], s2 = q[2], s3 = q[3];
     const float sum = ((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)) +
                       ((s2.x + s2.y) + (s2.z + s2.w)) + ((s3.x + s3.y) + (s3.z + s3.w));
     const float xn = sm.xres[tid] + sum;
+    sm.xres[tid] = xn;     // the band's residual rows of the next layer
     put(P.xbuf + (size_t)(l & 1) * D + row, tag, xn);
     if (l + 1 == P.n_layers) *gpw(P.y_out + row) = xn;
     // the band's words precede its flag in this wave's store order
@@ -755,40 +749,42 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   return true;
 }
 
-// The layer loop of one role: ROLE 0 projection only, 1 head block, 2 projection + output
-// band.  Each role keeps only its own prefetch registers live.  Prefetches are issued right
-// after a phase that is followed by a long wait, never just before a poll on the critical
-// path (a poll's load completes only after the loads issued before it).
+// The layer loop of one role: ROLE 0 projection block, 1 head block, 2 output band.  Each
+// role keeps only its own prefetch registers live.  Prefetches are issued right after a phase
+// that is followed by a long wait, never just before a poll on the critical path (a poll's
+// load completes only after the loads issued before it).
 template <int U, int CPR, int ROLE>
 __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   GLayer* Lt = (GLayer*)P.layers;
   const Roles R = make_roles(P);
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
+  const int tid = threadIdx.x;
   if constexpr (ROLE == 1) {
     HeadRegs<CPR> hr;
     issue_head<CPR>(P, Lt[0], P.S, blockIdx.x % P.H, blockIdx.x / P.H, hr);
     for (int l = 0; l < P.n_layers; ++l)
       if (!phase_h<CPR>(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
-  } else {
-    // the zero plane of the wave's runs (no other wave reads them)
+    return;
+  }
+  // the zero plane of the wave's runs (no other wave reads them)
 #pragma unroll
-    for (int k = 0; k < 4 * U; ++k) sm.planes[3 * 1024 * U + run_elem(k, threadIdx.x >> 6, threadIdx.x & 63)] = 0;
+  for (int k = 0; k < 4 * U; ++k) sm.planes[3 * 1024 * U + run_elem(k, tid >> 6, tid & 63)] = 0;
+  if constexpr (ROLE == 2) {
+    OutRegs<U> orr;
+    issue_out<U>(Lt[0], R.ob, orr);
+    if (tid < 16 * kOTiles) sm.xres[tid] = *gp(P.x_in + R.or0 + tid);
+    for (int l = 0; l < P.n_layers; ++l) {
+      if (!phase_o<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, orr)) return;
+      if (l + 1 < P.n_layers) issue_out<U>(Lt[l + 1], R.ob, orr);
+    }
+  } else {
+    // a block left without projection rows has nothing to do: no phase waits for it, and
+    // it must not fall layers behind while it reads the residual stream
+    if (R.p1 <= R.p0) return;
     ProjRegs<U> pr;
     issue_proj<U>(P, Lt[0], P.win, R.p0, R.p1, pr);
-    if constexpr (ROLE == 2) {
-      OutRegs<U> orr;
-      for (int l = 0; l < P.n_layers; ++l) {
-        const uint32_t tag = tag0 + (uint32_t)l + 1u;
-        if (!phase_p<U, true>(P, sm, R, l, tag, pr, &orr)) return;
-        if (!phase_o<U>(P, sm, R, l, tag, orr)) return;
-      }
-    } else {
-      // a block left without projection rows has nothing to do: no phase waits for it, and
-      // it must not fall layers behind while it reads the residual stream
-      if (__syncthreads_or(R.p1 > R.p0) == 0) return;
-      for (int l = 0; l < P.n_layers; ++l)
-        if (!phase_p<U, false>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr, nullptr)) return;
-    }
+    for (int l = 0; l < P.n_layers; ++l)
+      if (!phase_p<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr)) return;
   }
 }
 
