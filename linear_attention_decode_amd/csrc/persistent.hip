@@ -113,37 +113,85 @@ __device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase
   return P.flags + (size_t)phase * kMaxPersistBlocks + i;
 }
 
-// One wave: wait until at least `need` of flags [0, n) of `phase` carry `tag` (n <= 4 * 64).
-// Every flag is loaded at once; only the ones not yet set are polled again.
-__device__ bool wave_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag, int need) {
-  const int lane = threadIdx.x & 63;
-  Spin sp;
-  bool ok[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) ok[k] = false;
-  while (true) {
-    uint64_t w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (!ok[k] && lane + 64 * k < n) w[k] = peek(flag_slot(P, phase, lane + 64 * k));
-    int cnt = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (!ok[k] && lane + 64 * k < n) ok[k] = (uint32_t)(w[k] >> 32) == tag;
-      cnt += __popcll(__ballot(ok[k]));
-    }
-    if (cnt >= need) return true;
-    if (sp.stop(P)) return false;
-    __builtin_amdgcn_s_sleep(1);
-  }
+// One wave, every lane active: poll the tag word *f of each lane (lanes may share a word)
+// until some lane sees `tag`, for at most 48 rounds.  Three loads stay in flight, issued
+// ~0.16 us apart (a third of a round trip to the memory side), so a posted tag is seen about
+// one spacing after it lands rather than up to a whole round trip later.  Written as one asm
+// loop so that every check waits for its own load only (vmcnt 2; the counter retires in
+// order).  Returns true when seen: up to two loads may then still be in flight into a, b, c,
+// which the caller keeps live (keep_live) until a later wait has retired them.  Returns false
+// after the 48 rounds with nothing in flight.
+__device__ __forceinline__ bool poll_tag3(const uint32_t* f, uint32_t tag, uint32_t& a, uint32_t& b,
+                                          uint32_t& c) {
+  uint32_t found, cnt;
+  asm volatile(
+      "global_load_dword %0, %5, off sc1\n\t"
+      "s_sleep 6\n\t"
+      "global_load_dword %1, %5, off sc1\n\t"
+      "s_sleep 6\n\t"
+      "global_load_dword %2, %5, off sc1\n\t"
+      "s_mov_b32 %4, 48\n\t"
+      "s_mov_b32 %3, 1\n"
+      "1:\n\t"
+      "s_waitcnt vmcnt(2)\n\t"
+      "v_cmp_eq_u32 vcc, %6, %0\n\t"
+      "s_cbranch_vccnz 2f\n\t"
+      "global_load_dword %0, %5, off sc1\n\t"
+      "s_sleep 6\n\t"
+      "s_waitcnt vmcnt(2)\n\t"
+      "v_cmp_eq_u32 vcc, %6, %1\n\t"
+      "s_cbranch_vccnz 2f\n\t"
+      "global_load_dword %1, %5, off sc1\n\t"
+      "s_sleep 6\n\t"
+      "s_waitcnt vmcnt(2)\n\t"
+      "v_cmp_eq_u32 vcc, %6, %2\n\t"
+      "s_cbranch_vccnz 2f\n\t"
+      "global_load_dword %2, %5, off sc1\n\t"
+      "s_sleep 6\n\t"
+      "s_sub_u32 %4, %4, 1\n\t"
+      "s_cmp_eq_u32 %4, 0\n\t"
+      "s_cbranch_scc0 1b\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b32 %3, 0\n"
+      "2:"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&s"(found), "=&s"(cnt)
+      : "v"(f), "s"(tag)
+      : "vcc", "scc", "memory");
+  return found != 0;
 }
 
-// Whole block: wave 0 watches the producer flags, the other waves wait at the barrier.
-__device__ bool block_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag, int need) {
-  int bad = 0;
-  if (threadIdx.x < 64) bad = !wave_wait_flags(P, phase, n, tag, need);
-  return __syncthreads_or(bad) == 0;
+// Ends the live range of poll registers whose loads a later wait has retired.
+__device__ __forceinline__ void keep_live(const uint32_t (&r)[3]) {
+  asm volatile("" : : "v"(r[0]), "v"(r[1]), "v"(r[2]) : "memory");
 }
+
+// Wave 0 watches flags [0, n) of `phase` (n <= 64) until one carries `tag`; the caller's
+// block_any then holds the other waves.  pend[] holds wave 0's poll registers (see
+// poll_tag3).  The wait is bounded by the wall clock: on a timeout the error word is recorded
+// and 1 is returned.
+__device__ int wave0_wait_flags(const PersistParams& P, int phase, int n, uint32_t tag,
+                                uint32_t (&pend)[3]) {
+  int bad = 0;
+  // every earlier load (a prefetch long landed) is retired first, in every wave: a wait for
+  // one of them after the polls would also wait for the polls still in flight
+  retire_vmem();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint32_t* f = reinterpret_cast<const uint32_t*>(flag_slot(P, phase, lane < n ? lane : 0)) + 1;
+    const uint64_t t0 = wall_clock64();
+    // (no read of the error word here: its load would make the code after the wait retire
+    // the polls still in flight)
+    while (!poll_tag3(f, tag, pend[0], pend[1], pend[2])) {
+      if (wall_clock64() - t0 > P.timeout) {
+        __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bad = 1;
+        break;
+      }
+    }
+  }
+  return bad;
+}
+
 
 // ---- matrix-core dots of the projections ----
 // A block's projection rows meet the input vector on v_mfma_i32_16x16x64_i8.  The input is
@@ -249,16 +297,26 @@ template <int NT, int NTILE>
 __device__ __forceinline__ void mfma_tiles(const i32x4 (&a)[NT][2], const i32x4 (&w)[NTILE][NT][2],
                                            const uint32_t (&d)[NTILE][NT], float inv_s, int ntiles,
                                            float (&y)[NTILE]) {
+  // every pair gets its own accumulator, so the MFMAs issue back to back before the first
+  // epilogue waits for a result
   const i32x4 zero = {0, 0, 0, 0};
+  i32x4 c[NTILE][NT];
+#pragma unroll
+  for (int tile = 0; tile < NTILE; ++tile)
+    if (tile < ntiles) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) c[tile][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][0], w[tile][t][0], zero, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) c[tile][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][1], w[tile][t][1], c[tile][t], 0, 0, 0);
+    }
 #pragma unroll
   for (int tile = 0; tile < NTILE; ++tile) {
     float acc = 0.0f;
     if (tile < ntiles) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        i32x4 c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][0], w[tile][t][0], zero, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t][1], w[tile][t][1], c, 0, 0, 0);
-        const float v = fmaf((float)(c[1] * 128 + c[2]), 1.0f / 16384.0f, (float)c[0]);
+        const i32x4 r = c[tile][t];
+        const float v = fmaf((float)(r[1] * 128 + r[2]), 1.0f / 16384.0f, (float)r[0]);
         acc = fmaf(h2f(d[tile][t]), v, acc);
       }
     }
@@ -422,7 +480,21 @@ struct Smem {
   alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
   alignas(16) float s_al[kHD];     // head block: alpha rows
   alignas(16) float s_gt[kHCols];  // head block: output-gate columns
+  alignas(16) int any[2][4];       // block_any: per-wave votes, two alternating sets
 };
+
+// Block-wide OR of pred (every thread of the block calls it): each wave's vote goes to LDS,
+// one barrier, every thread reads the four votes.  Consecutive calls of a block use the two
+// vote sets alternately (`set`), since no wave can be more than one call ahead of another.
+// Unlike __syncthreads_or (which reads the block size from memory) it issues no global load, which would make it wait for every load
+// still in flight.
+__device__ __forceinline__ bool block_any(Smem& sm, int set, int pred) {
+  const bool any = __builtin_amdgcn_ballot_w64(pred != 0) != 0;
+  if ((threadIdx.x & 63) == 0) sm.any[set][threadIdx.x >> 6] = any;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+  const int4 v = *reinterpret_cast<const int4*>(sm.any[set]);
+  return (v.x | v.y | v.z | v.w) != 0;
+}
 
 // Static roles of block b: [0, kHSplit H) heads, then P.o_blocks output bands of 32 rows,
 // then the projection blocks: q/k/v rows 48 per block to the first q_blocks, then the
@@ -470,8 +542,10 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   } else {
     // x_l: once the first O block of layer l - 1 has posted (they finish together), fetch
     // the tagged words of the wave's runs
-    if (!block_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, 1)) return false;
+    uint32_t pend[3] = {0u, 0u, 0u};
+    if (block_any(sm, 0, wave0_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, pend))) return false;
     bad = !poll_runs<NV>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, v, P);
+    keep_live(pend);
   }
   float ss = 0.0f;
 #pragma unroll
@@ -487,7 +561,7 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
 #pragma unroll
   for (int tile = 0; tile < kPTiles; ++tile)
     if (tile < ntiles) sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
-  if (__syncthreads_or(bad)) return false;
+  if (block_any(sm, 1, bad)) return false;
   // thread t finishes row p0 + t: RMSNorm scale, conv + SiLU + window roll for q/k/v channels
   if (tid < rows) {
     const int row = R.p0 + tid;
@@ -574,8 +648,13 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
       const int i = tid + k * kPT;
       if (i >= i_lr && i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
-    if (__syncthreads_or(bad)) return false;
+    if (block_any(sm, 0, bad)) return false;
   }
+  // request the q/k/v words again now: the round trip overlaps the gates below, and the
+  // replies are merged only after them
+  uint64_t again[3];
+#pragma unroll
+  for (int k = 0; k < 3; ++k) again[k] = peek(src[k]);
   const float* s_q = sm.s_in;
   const float* s_k = sm.s_in + dk;
   const float* s_v = sm.s_in + 2 * dk;
@@ -613,13 +692,15 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   }
   {
     // q, k, v
+#pragma unroll
+    for (int k = 0; k < 3; ++k) w[k] = (uint32_t)(w[k] >> 32) == tag ? w[k] : again[k];
     const int bad = !wait_slots(false);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int i = tid + k * kPT;
       if (i < i_lr) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
-    if (__syncthreads_or(bad)) return false;
+    if (block_any(sm, 1, bad)) return false;
   }
   // delta rule: lane (rg, cq) holds rows 8 rg .. + 8 of columns jl .. + 4 (block-local jl)
   const int rg = lane & 15, cq = lane >> 4;
@@ -700,7 +781,8 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // once the first head block has posted, fetch the output words of the wave's heads and
   // their partials (lane kParts t + i: partial i of head 4 t + wave)
-  if (!block_wait_flags(P, kFlagH, kHSplit * P.H, tag, 1)) return false;
+  uint32_t pend[3] = {0u, 0u, 0u};
+  if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag, pend))) return false;
   const bool has = lane < kParts * NT;
   const uint64_t* src = P.obuf + D + (4 * (has ? lane / kParts : 0) + wave) * kParts + lane % kParts;
   uint64_t pw = has ? peek(src) : tagged(tag, 0.0f);
@@ -713,6 +795,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
       else pw = peek(src);
     }
   }
+  keep_live(pend);
   // the normalised heads (run t = head 4 t + wave), then their planes
   const int ps = __float_as_int(group_sum(__uint_as_float((uint32_t)pw), kParts));
   float ss = 0.0f;
@@ -732,7 +815,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
 #pragma unroll
   for (int tile = 0; tile < kOTiles; ++tile)
     sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
-  if (__syncthreads_or(bad)) return false;
+  if (block_any(sm, 1, bad)) return false;
   if (tid < 16 * kOTiles) {
     const int row = R.or0 + tid;
     const float4* q = reinterpret_cast<const float4*>(sm.part + 16 * tid);
