@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 745144850,
-                "sha256": "298833178c0bca139dfeac267126fdbea3a7ff459b99c9e24ab6a086177f383b",
+STEP_TRAFFIC = {"bytes": 743831974,
+                "sha256": "ed7ef95ad63b260e310d4afd2d5cba354ae0974bc71df6f930783ceb1eb14190",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
