@@ -109,6 +109,17 @@ struct Spin {
 
 enum FlagPhase { kFlagH = 1, kFlagO = 2 };
 
+// Wall-clock ticks (100 MHz) a block holds its next-layer prefetch back after its phase, so
+// that the burst does not queue ahead of the polls its consumers issue meanwhile (timed:
+// 0.5-1 us of hold was 4 % faster per token than none; the weights are needed ~7 us later).
+#ifndef KDA_PREFETCH_DELAY
+#define KDA_PREFETCH_DELAY 75
+#endif
+__device__ __forceinline__ void hold_prefetch() {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < KDA_PREFETCH_DELAY) __builtin_amdgcn_s_sleep(8);
+}
+
 __device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase, int i) {
   return P.flags + (size_t)phase * kMaxPersistBlocks + i;
 }
@@ -582,7 +593,10 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
       *gpw(z + 2 * C) = pre;
     }
   }
-  if (l + 1 < P.n_layers) issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.p0, R.p1, pr);
+  if (l + 1 < P.n_layers) {
+    hold_prefetch();
+    issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.p0, R.p1, pr);
+  }
   return true;
 }
 
@@ -764,7 +778,10 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   float* Sb = Sl + (size_t)h * dk * dv + j;
 #pragma unroll
   for (int i = 0; i < 8; ++i) gstore4(Sb + (size_t)(r0 + i) * dv, hr.st[i]);
-  if (l + 1 < P.n_layers) issue_head<CPR>(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, half, hr);
+  if (l + 1 < P.n_layers) {
+    hold_prefetch();
+    issue_head<CPR>(P, Lt[l + 1], Sl + (size_t)H * dk * dv, h, half, hr);
+  }
   // (the next layer's first wait is a barrier, so LDS is not rewritten while still read)
   return true;
 }
@@ -858,7 +875,10 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
     if (tid < 16 * kOTiles) sm.xres[tid] = *gp(P.x_in + R.or0 + tid);
     for (int l = 0; l < P.n_layers; ++l) {
       if (!phase_o<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, orr)) return;
-      if (l + 1 < P.n_layers) issue_out<U>(Lt[l + 1], R.ob, orr);
+      if (l + 1 < P.n_layers) {
+        hold_prefetch();
+        issue_out<U>(Lt[l + 1], R.ob, orr);
+      }
     }
   } else {
     // a block left without projection rows has nothing to do: no phase waits for it, and
