@@ -814,11 +814,14 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   }
   keep_live(pend);
   // the normalised heads (run t = head 4 t + wave), then their planes
-  const int ps = __float_as_int(group_sum(__uint_as_float((uint32_t)pw), kParts));
+  // lane kParts t ends up with head t's sum of squares; every lane computes a scale, lane
+  // kParts t's is head t's
+  const float psum = group_sum(__uint_as_float((uint32_t)pw), kParts);
+  const int hsl = __float_as_int(1.0f / sqrtf(psum / (float)kHD + P.eps));
   float ss = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const float hs = 1.0f / sqrtf(__int_as_float(__builtin_amdgcn_readlane(ps, kParts * t)) / (float)kHD + P.eps);
+    const float hs = __int_as_float(__builtin_amdgcn_readlane(hsl, kParts * t));
     v[2 * t] *= hs;
     v[2 * t + 1] *= hs;
     ss = fmaf(v[2 * t], v[2 * t], ss);
