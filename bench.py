@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 743831974,
-                "sha256": "ed7ef95ad63b260e310d4afd2d5cba354ae0974bc71df6f930783ceb1eb14190",
+STEP_TRAFFIC = {"bytes": 744012449,
+                "sha256": "82fc037d6eed532e3657e0696ce17a771d6a26e17e20f8b84d42c65bc162d827",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
