@@ -133,8 +133,13 @@ typedef enum {
   KDA_OPT_GRAPH = 0,      /* 1 (default): decode steps replay a captured hipGraph of all
                              layers, re-captured when a pointer or the batch changes */
   KDA_OPT_TIMING = 1,     /* 1: record hipEvents around every kernel launch (no graph) */
-  KDA_OPT_PERSISTENT = 2  /* 1 (default): batch-1 decode of an eligible model runs every
+  KDA_OPT_PERSISTENT = 2, /* 1 (default): batch-1 decode of an eligible model runs every
                              layer in one cooperative launch (see kda_model_query) */
+  KDA_OPT_WAIT_US = 3     /* bound of every wait between blocks of the one-launch decode, in
+                             microseconds of wall clock; <= 0 (default) = 50 ms.  A step whose
+                             wait runs out leaves through the bound and kda_model_status
+                             reports it; limits under 100 us make the waits look at the clock
+                             after every poll round (for exercising that path) */
 } kda_option;
 int kda_model_set_option(kda_model* m, int option, int64_t value);
 

@@ -84,6 +84,7 @@ struct kda_model {
   bool use_persist = true;
   bool pers_ok = false;
   int pers_blocks = 0;
+  int wall_khz = 0;                 // wall-clock ticks per millisecond
   PersistLayer* d_layers = nullptr;
   int8_t* mma_w = nullptr;          // projection rows and W_o of every layer, matrix-core order
   uint64_t* xchg = nullptr;         // exchange words (xbuf | pbuf | gbuf | obuf)
@@ -349,6 +350,20 @@ size_t exchange_words(const kda_model* m) {
          3 * (size_t)kMaxPersistBlocks;
 }
 
+// The bound of every wait between blocks of the one-launch decode: `us` microseconds of wall
+// clock, or 50 ms when us <= 0.  Under 100 us the flag waits look at the clock after every
+// poll round (a limit that short is for exercising the timeout path).
+void set_wait_limit(kda_model* m, int64_t us) {
+  PersistParams& p = m->pp;
+  if (us <= 0) {
+    p.timeout = (uint64_t)m->wall_khz * 50;
+    p.poll_rounds = 48;
+  } else {
+    p.timeout = std::max<uint64_t>(1, (uint64_t)m->wall_khz * (uint64_t)us / 1000);
+    p.poll_rounds = us < 100 ? 1 : 48;
+  }
+}
+
 hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const kda_dims& d = m->d;
   const int nb = persistent_max_blocks();
@@ -434,7 +449,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
   if (e != hipSuccess) return e;
-  p.timeout = (uint64_t)(khz > 0 ? khz : 100000) * 50;   // 50 ms of wall clock per wait
+  m->wall_khz = khz > 0 ? khz : 100000;
+  set_wait_limit(m, 0);
   p.o_first_block = ob0; p.o_blocks = nob;
   p.q_blocks = m->C / 48;
   m->pers_blocks = nb;
@@ -597,6 +613,9 @@ int kda_model_set_option(kda_model* m, int option, int64_t value) {
       return KDA_OK;
     case KDA_OPT_PERSISTENT:
       m->use_persist = value != 0;
+      return KDA_OK;
+    case KDA_OPT_WAIT_US:
+      if (m->pers_ok) set_wait_limit(m, value);
       return KDA_OK;
     default:
       return fail(KDA_E_ARG, "unknown option %d", option);

@@ -44,6 +44,7 @@ struct PersistParams {
   uint64_t* flags = nullptr;             // [3][kMaxPersistBlocks] tagged producer flags
   int* err = nullptr;                    // nonzero after a wait timed out
   uint64_t timeout = 0;                  // wall-clock ticks a wait may take
+  int poll_rounds = 48;                  // flag-poll rounds between two looks at the clock
   uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)
   int o_first_block = 0, o_blocks = 0;  // blocks [first, first + n) run the output projection,
                                          // 32 rows each

@@ -125,15 +125,15 @@ __device__ __forceinline__ uint64_t* flag_slot(const PersistParams& P, int phase
 }
 
 // One wave, every lane active: poll the tag word *f of each lane (lanes may share a word)
-// until some lane sees `tag`, for at most 48 rounds.  Three loads stay in flight, issued
+// until some lane sees `tag`, for at most `rounds` rounds (>= 1).  Three loads stay in flight, issued
 // ~0.16 us apart (a third of a round trip to the memory side), so a posted tag is seen about
 // one spacing after it lands rather than up to a whole round trip later.  Written as one asm
 // loop so that every check waits for its own load only (vmcnt 2; the counter retires in
 // order).  Returns true when seen: up to two loads may then still be in flight into a, b, c,
 // which the caller keeps live (keep_live) until a later wait has retired them.  Returns false
-// after the 48 rounds with nothing in flight.
-__device__ __forceinline__ bool poll_tag3(const uint32_t* f, uint32_t tag, uint32_t& a, uint32_t& b,
-                                          uint32_t& c) {
+// after the rounds with nothing in flight.
+__device__ __forceinline__ bool poll_tag3(const uint32_t* f, uint32_t tag, int rounds, uint32_t& a,
+                                          uint32_t& b, uint32_t& c) {
   uint32_t found, cnt;
   asm volatile(
       "global_load_dword %0, %5, off sc1\n\t"
@@ -141,7 +141,7 @@ __device__ __forceinline__ bool poll_tag3(const uint32_t* f, uint32_t tag, uint3
       "global_load_dword %1, %5, off sc1\n\t"
       "s_sleep 6\n\t"
       "global_load_dword %2, %5, off sc1\n\t"
-      "s_mov_b32 %4, 48\n\t"
+      "s_mov_b32 %4, %7\n\t"
       "s_mov_b32 %3, 1\n"
       "1:\n\t"
       "s_waitcnt vmcnt(2)\n\t"
@@ -166,7 +166,7 @@ __device__ __forceinline__ bool poll_tag3(const uint32_t* f, uint32_t tag, uint3
       "s_mov_b32 %3, 0\n"
       "2:"
       : "=&v"(a), "=&v"(b), "=&v"(c), "=&s"(found), "=&s"(cnt)
-      : "v"(f), "s"(tag)
+      : "v"(f), "s"(tag), "s"(rounds)
       : "vcc", "scc", "memory");
   return found != 0;
 }
@@ -192,7 +192,7 @@ __device__ int wave0_wait_flags(const PersistParams& P, int phase, int n, uint32
     const uint64_t t0 = wall_clock64();
     // (no read of the error word here: its load would make the code after the wait retire
     // the polls still in flight)
-    while (!poll_tag3(f, tag, pend[0], pend[1], pend[2])) {
+    while (!poll_tag3(f, tag, P.poll_rounds, pend[0], pend[1], pend[2])) {
       if (wall_clock64() - t0 > P.timeout) {
         __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bad = 1;
@@ -221,16 +221,6 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int run_elem(int k, int wave, int lane) {
   return 512 * (k >> 1) + 128 * wave + 64 * (k & 1) + lane;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_mov<kDppXor1>(v));
-  v = fmaxf(v, dpp_mov<kDppXor2>(v));
-  v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
-  v = fmaxf(v, dpp_mov<kDppRor8>(v));
-  const int b = __float_as_int(v);
-  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 0)), __int_as_float(__builtin_amdgcn_readlane(b, 16))),
-               fmaxf(__int_as_float(__builtin_amdgcn_readlane(b, 32)), __int_as_float(__builtin_amdgcn_readlane(b, 48))));
 }
 
 // This wave's NV tagged words of the runs it owns (NV = 2 per run) from buf into v[].  Every

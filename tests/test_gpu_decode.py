@@ -183,3 +183,33 @@ def test_conv_window_indexing_bit_exact(torch):
     _, _, rZ, _ = ok.decode_run(layers, run.x, run.s0, False, steps=5)
     np.testing.assert_array_equal(Z.astype(np.float64), rZ)
     model.close()
+
+
+def test_one_launch_wait_limit_times_out_and_recovers(torch):
+    """A one-launch step whose waits between blocks run out ends through the kernel's own
+    bound: with a 1 us limit set from the host the output blocks give up on the head flags
+    at the first layer, every other wait then ends through its own bound, and
+    kda_model_status reports the step.  With the default limit restored the model decodes
+    the same tokens correctly from a fresh state."""
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=2, steps=3, seed=37)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    assert model.persistent_blocks() > 0
+    _say("one-launch decode with a 1 us wait limit: one step, expect a reported timeout")
+    model.set_option(kda.KDA_OPT_WAIT_US, 1)
+    st = model.new_state(1)
+    ws = model.workspace(0, 1)
+    x = torch.from_numpy(np.ascontiguousarray(run.x[0, :, 0, :])).cuda()
+    y = torch.empty((1, model.d_model), dtype=torch.float32, device="cuda")
+    model.decode_step(x, y, st, ws)
+    with pytest.raises(kda.KdaError):
+        model.status()
+    model.status()                      # reported once; the exchange words were reset
+    _say("  default limit again: 3 steps against the oracle")
+    model.set_option(kda.KDA_OPT_WAIT_US, 0)
+    ys, S, _, _ = gpu_decode(model, run, w.steps)
+    ry, rS, _, _ = ok.decode_run(oracle_layers(run), run.x, run.s0, w.prenorm_residual, steps=w.steps)
+    assert max(range_rel(ys[t], ry[t]) for t in range(w.steps)) <= OUT_RTOL
+    assert np.abs(S - rS).max() <= STATE_ATOL
+    model.close()
