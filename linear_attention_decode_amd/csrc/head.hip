@@ -85,9 +85,10 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
       ah = P.a_log[row / P.dk];
     }
   }
-  // kGateCols columns' low-rank inputs per round, staged with independent loads; within a
-  // round, the CPR lanes of a row's group each finish one of CPR consecutive columns
-  for (int n0 = 0; n0 < P.N; n0 += kGateCols) {
+  // kGateCols columns' low-rank inputs per round (the rounds are spread over blockIdx.y),
+  // staged with independent loads; within a round, the CPR lanes of a row's group each
+  // finish one of CPR consecutive columns
+  for (int n0 = blockIdx.y * kGateCols; n0 < P.N; n0 += gridDim.y * kGateCols) {
     const int nc = min(kGateCols, P.N - n0);
     {
       // all loads first (a fixed, unrolled count per thread, indices clamped so no load
@@ -139,7 +140,8 @@ static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
   constexpr int BY = HFmt<WT>::kBytes;
   const int cpr = p.rank * BY / 16;
   const int items = (p.K + p.V) * cpr;
-  const int grid = (items + kGateThreads - 1) / kGateThreads;
+  const dim3 grid((items + kGateThreads - 1) / kGateThreads,
+                  std::min(8, (p.N + kGateCols - 1) / kGateCols));
   switch (cpr) {
     case 1: gates_kernel<WT, 1><<<grid, kGateThreads, 0, s>>>(p); break;
     case 2: gates_kernel<WT, 2><<<grid, kGateThreads, 0, s>>>(p); break;
