@@ -4,7 +4,7 @@
 Default workload (the headline metric): the 34-layer KDA stack (D=2048, 16 heads,
 d_k=d_v=128, all projections Q8_0, fp32 state [16][128][128] + 3-token conv window per
 layer, pre-RMSNorm residual stream), batch 1, synthetic seeded weights and inputs.  A step
-is one token through all 34 layers: one cooperative launch of the one-launch decode kernel
+is one token through all 34 layers: one launch of the one-launch decode kernel
 (or, with --per-layer, the per-layer kernels replayed as one hipGraph).
 
 Prints ONE JSON line: tokens/s over K timed steps, HBM roofline of the dominant kernel
@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744012449,
-                "sha256": "82fc037d6eed532e3657e0696ce17a771d6a26e17e20f8b84d42c65bc162d827",
+STEP_TRAFFIC = {"bytes": 744042108,
+                "sha256": "b9b50c22759f8eba850125a48c09c88c2d427139294d545e91114ba0d484720a",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
@@ -145,7 +145,7 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     model.set_option(kda.KDA_OPT_GRAPH, 1)
     model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
     one_launch = not args.per_layer and model.persistent_blocks() > 0 and B == 1
-    path = (f"one cooperative launch per token ({model.persistent_blocks()} blocks)" if one_launch
+    path = (f"one launch per token ({model.persistent_blocks()} blocks)" if one_launch
             else "per-layer kernels replayed as one hipGraph")
     log(f"[bench] path: {path}")
     for i in range(args.warmup):

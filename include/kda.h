@@ -130,16 +130,23 @@ void kda_model_destroy(kda_model* m);
 
 /* Options. */
 typedef enum {
-  KDA_OPT_GRAPH = 0,      /* 1 (default): decode steps replay a captured hipGraph of all
-                             layers, re-captured when a pointer or the batch changes */
-  KDA_OPT_TIMING = 1,     /* 1: record hipEvents around every kernel launch (no graph) */
-  KDA_OPT_PERSISTENT = 2, /* 1 (default): batch-1 decode of an eligible model runs every
-                             layer in one cooperative launch (see kda_model_query) */
-  KDA_OPT_WAIT_US = 3     /* bound of every wait between blocks of the one-launch decode, in
-                             microseconds of wall clock; <= 0 (default) = 50 ms.  A step whose
-                             wait runs out leaves through the bound and kda_model_status
-                             reports it; limits under 100 us make the waits look at the clock
-                             after every poll round (for exercising that path) */
+  KDA_OPT_GRAPH = 0,       /* 1 (default): decode steps replay a captured hipGraph of all
+                              layers, re-captured when a pointer or the batch changes */
+  KDA_OPT_TIMING = 1,      /* 1: record hipEvents around every kernel launch (no graph) */
+  KDA_OPT_PERSISTENT = 2,  /* 1 (default): batch-1 decode of an eligible model runs every
+                              layer in one launch (see kda_model_query) */
+  KDA_OPT_WAIT_US = 3,     /* bound of every wait between blocks of the one-launch decode, in
+                              microseconds of wall clock; <= 0 (default) = 50 ms.  A step
+                              whose wait runs out leaves through the bound and
+                              kda_model_status reports it; limits under 100 us make the waits
+                              look at the clock after every poll round (for exercising that
+                              path) */
+  KDA_OPT_COOPERATIVE = 4  /* 0 (default): the one-launch decode is a plain launch of one
+                              block per CU, co-resident when the stream has the GPU to itself;
+                              on a GPU shared with other work a block that cannot start leaves
+                              the rest to their bounded waits and kda_model_status reports the
+                              step.  1: a cooperative launch, which guarantees co-residency
+                              and costs ~17 us more per step */
 } kda_option;
 int kda_model_set_option(kda_model* m, int option, int64_t value);
 

@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
                    KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, KDA_K_GEMM, KDA_K_CHUNK,
-                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_Q_PERSISTENT, DTYPES, KdaError)
+                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError)
 
 _PROJ_NAMES = ("wq", "wk", "wv", "wo", "fa", "fb", "wbeta", "ga", "gb")
 

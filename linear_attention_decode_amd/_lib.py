@@ -13,7 +13,7 @@ KDA_OK, KDA_E_ARG, KDA_E_SHAPE, KDA_E_ALIGN, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E
     KDA_E_UNSUPPORTED = range(8)
 KDA_F32, KDA_BF16, KDA_Q8_0 = 0, 1, 2
 KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL = 0, 1, 2
-KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US = 0, 1, 2, 3
+KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE = 0, 1, 2, 3, 4
 KDA_Q_PERSISTENT = 0
 KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, \
     KDA_K_GEMM, KDA_K_CHUNK = range(9)

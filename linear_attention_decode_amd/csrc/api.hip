@@ -82,6 +82,7 @@ struct kda_model {
   GraphKey key;
   // one-launch decode (batch 1)
   bool use_persist = true;
+  bool coop = false;                // cooperative launch of the one-launch decode
   bool pers_ok = false;
   int pers_blocks = 0;
   int wall_khz = 0;                 // wall-clock ticks per millisecond
@@ -617,6 +618,9 @@ int kda_model_set_option(kda_model* m, int option, int64_t value) {
     case KDA_OPT_WAIT_US:
       if (m->pers_ok) set_wait_limit(m, value);
       return KDA_OK;
+    case KDA_OPT_COOPERATIVE:
+      m->coop = value != 0;
+      return KDA_OK;
     default:
       return fail(KDA_E_ARG, "unknown option %d", option);
   }
@@ -683,7 +687,7 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
     PersistParams p = m->pp;
     p.S = st->S_dev; p.win = st->conv_dev; p.x_in = x_dev; p.y_out = y_dev;
     p.epoch = ++m->epoch;
-    return timed(m, KDA_K_STEP, s, m->timing, [&] { return launch_persistent(p, m->pers_blocks, s); });
+    return timed(m, KDA_K_STEP, s, m->timing, [&] { return launch_persistent(p, m->pers_blocks, m->coop, s); });
   }
   if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing);
 

@@ -69,7 +69,7 @@ inline size_t mma_order_bytes(int rows, int D) { return (size_t)((rows + 15) / 1
 inline size_t mma_order_scales(int rows, int D) { return (size_t)((rows + 15) / 16) * 16 * (D / 32); }
 hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, uint16_t* d,
                             hipStream_t s);
-hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s);
+hipError_t launch_persistent(const PersistParams& p, int blocks, bool cooperative, hipStream_t s);
 int persistent_max_blocks();            // co-resident blocks of one per CU, 0 if unavailable
 
 }  // namespace kda

@@ -938,7 +938,7 @@ hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, ui
   return hipGetLastError();
 }
 
-hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s) {
+hipError_t launch_persistent(const PersistParams& p, int blocks, bool cooperative, hipStream_t s) {
   void* args[] = {const_cast<PersistParams*>(&p)};
   const void* fn = nullptr;
 #define KDA_PERSIST_CASE(u, cpr) \
@@ -947,7 +947,12 @@ hipError_t launch_persistent(const PersistParams& p, int blocks, hipStream_t s) 
   KDA_PERSIST_CASE(2, 2) KDA_PERSIST_CASE(2, 4) KDA_PERSIST_CASE(2, 8)
 #undef KDA_PERSIST_CASE
   if (!fn) return hipErrorInvalidValue;
-  return hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
+  // a plain launch of one block per CU is co-resident on a GPU this stream has to itself
+  // (kernels of one stream run in order); on a shared GPU a block that cannot start leaves
+  // the others to their bounded waits, and the step is reported.  The cooperative launch
+  // guarantees co-residency but costs ~17 us more per step.
+  if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
+  return hipLaunchKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
 }
 
 int persistent_max_blocks() {

@@ -213,3 +213,25 @@ def test_one_launch_wait_limit_times_out_and_recovers(torch):
     assert max(range_rel(ys[t], ry[t]) for t in range(w.steps)) <= OUT_RTOL
     assert np.abs(S - rS).max() <= STATE_ATOL
     model.close()
+
+
+def test_one_launch_cooperative_launch(torch):
+    """The one-launch decode through the cooperative launch (KDA_OPT_COOPERATIVE = 1) gives
+    the same results as the default plain launch, both within the oracle's bounds."""
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=2, steps=4, seed=43)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    assert model.persistent_blocks() > 0
+    _say("one-launch decode, plain vs cooperative launch, 2 layers 4 steps")
+    ya, Sa, Za, _ = gpu_decode(model, run, w.steps)
+    model.set_option(kda.KDA_OPT_COOPERATIVE, 1)
+    yb, Sb, Zb, _ = gpu_decode(model, run, w.steps)
+    model.set_option(kda.KDA_OPT_COOPERATIVE, 0)
+    ry, rS, _, _ = ok.decode_run(oracle_layers(run), run.x, run.s0, w.prenorm_residual, steps=w.steps)
+    for ys, S in ((ya, Sa), (yb, Sb)):
+        assert max(range_rel(ys[t], ry[t]) for t in range(w.steps)) <= OUT_RTOL
+        assert np.abs(S - rS).max() <= STATE_ATOL
+    np.testing.assert_array_equal(ya, yb)
+    np.testing.assert_array_equal(Sa, Sb)
+    model.close()
