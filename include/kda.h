@@ -155,9 +155,10 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
  * H*d_v = D in {1024, 2048}, rank_f = rank_g in {32, 64, 128}, H <= 32, and one
  * co-resident block per CU with 2 H + D/32 + C/48 + ceil((proj_rows - C)/16) <= CUs).  For it kda_model_create allocates
  * ~130 KB of exchange words, flags and layer table, and a copy of every layer's projection
- * rows and W_o rearranged for the matrix cores (about D*(proj_rows + D)*17/16 bytes per
- * layer; 17.4 MB at D = 2048): the one-launch decode reads that copy, so later changes to
- * the caller's weights reach it only through a new model. */
+ * rows, W_o, F_b and G_b rearranged for the matrix cores (about
+ * (D*(proj_rows + D) + 2*D*rank)*17/16 bytes per layer; 19.0 MB at D = 2048, rank 128): the
+ * one-launch decode reads that copy, so later changes to the caller's weights reach it only
+ * through a new model. */
 typedef enum { KDA_Q_PERSISTENT = 0 } kda_query;
 int kda_model_query(const kda_model* m, int what);
 

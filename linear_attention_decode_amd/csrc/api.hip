@@ -385,7 +385,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const int D = d.d_model;
   const size_t pw = mma_order_bytes(m->proj_rows, D), pd = mma_order_scales(m->proj_rows, D);
   const size_t ow = mma_order_bytes(D, D), od = mma_order_scales(D, D);
-  const size_t per_layer = pw + ow + 2 * (pd + od);
+  const int KF = d.n_heads * d.d_k, KG = m->V, nbr = rank / 32;
+  const size_t per_layer = pw + ow + 2 * (pd + od) + (size_t)(KF + KG) * (rank + 2 * nbr);
   hipError_t e = hipMalloc(&m->mma_w, per_layer * d.n_layers);
   if (e != hipSuccess) return e;
   std::vector<PersistLayer> host(d.n_layers);
@@ -393,13 +394,18 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     const LayerDev& L = m->layers[l];
     PersistLayer& P = host[l];
     P.seg[0] = L.wq; P.seg[1] = L.wk; P.seg[2] = L.wv; P.seg[3] = L.fa; P.seg[4] = L.ga; P.seg[5] = L.wbeta;
-    P.fb = L.fb; P.gb = L.gb; P.wo = L.wo;
+    P.wo = L.wo;
     P.conv_w = L.conv_w; P.a_log = L.a_log; P.dt_bias = L.dt_bias; P.o_norm_w = L.o_norm_w;
     int8_t* base = m->mma_w + per_layer * l;
     P.pw = base;
     P.ow = base + pw;
     P.pd = reinterpret_cast<const uint16_t*>(base + pw + ow);
     P.od = P.pd + pd;
+    int8_t* gbase = base + pw + ow + 2 * (pd + od);
+    P.fbw = gbase;
+    P.gbw = gbase + (size_t)KF * rank;
+    P.fbd = reinterpret_cast<const uint16_t*>(gbase + (size_t)(KF + KG) * rank);
+    P.gbd = P.fbd + (size_t)KF * nbr;
     const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
     MmaSource src{};
     int first = 0;
@@ -417,6 +423,10 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     so.d[0] = L.wo.d;
     so.nseg = 1;
     e = launch_mma_order(so, D, D, const_cast<int8_t*>(P.ow), const_cast<uint16_t*>(P.od), nullptr);
+    if (e != hipSuccess) break;
+    e = launch_gate_order(L.fb.w, L.fb.d, KF, rank, const_cast<int8_t*>(P.fbw), const_cast<uint16_t*>(P.fbd), nullptr);
+    if (e != hipSuccess) break;
+    e = launch_gate_order(L.gb.w, L.gb.d, KG, rank, const_cast<int8_t*>(P.gbw), const_cast<uint16_t*>(P.gbd), nullptr);
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return e;

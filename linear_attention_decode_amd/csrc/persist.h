@@ -17,12 +17,17 @@ struct PackedMat {
 // ---------------------------------------------------------------------------------------
 struct PersistLayer {
   PackedMat seg[6];               // W_q, W_k, W_v, F_a, G_a, W_beta  (rows [out][D])
-  PackedMat fb, gb, wo;
+  PackedMat wo;
   // the fused projection rows and W_o rearranged for the matrix cores (mma_order_* below)
   const int8_t* pw = nullptr;
   const uint16_t* pd = nullptr;
   const int8_t* ow = nullptr;
   const uint16_t* od = nullptr;
+  // F_b and G_b rearranged for the matrix cores (gate_order_* below)
+  const int8_t* fbw = nullptr;
+  const uint16_t* fbd = nullptr;
+  const int8_t* gbw = nullptr;
+  const uint16_t* gbd = nullptr;
   const float* conv_w = nullptr;
   const float* a_log = nullptr;
   const float* dt_bias = nullptr;
@@ -69,6 +74,13 @@ inline size_t mma_order_bytes(int rows, int D) { return (size_t)((rows + 15) / 1
 inline size_t mma_order_scales(int rows, int D) { return (size_t)((rows + 15) / 16) * 16 * (D / 32); }
 hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, uint16_t* d,
                             hipStream_t s);
+// Q8_0 rows [0, rows) (rows a multiple of 16) of a matrix with `rank` columns (32, 64 or
+// 128; NB = rank / 32 blocks per row), rearranged for the one-launch decode's gate tiles:
+// per tile of 16 rows, [2 halves][NB blocks][16 rows][16 bytes] with the bytes as signed q
+// (chunk (h, g, n) = bytes [32 g + 16 h, + 16) of row n), and the scales as [tile][NB][16]
+// fp16 bits.  Sizes: rows * rank bytes and rows * NB scales.
+hipError_t launch_gate_order(const uint8_t* w_src, const __half* d_src, int rows, int rank,
+                             int8_t* w, uint16_t* d, hipStream_t s);
 hipError_t launch_persistent(const PersistParams& p, int blocks, bool cooperative, hipStream_t s);
 int persistent_max_blocks();            // co-resident blocks of one per CU, 0 if unavailable
 

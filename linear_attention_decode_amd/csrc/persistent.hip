@@ -325,20 +325,6 @@ __device__ __forceinline__ void mfma_tiles(const i32x4 (&a)[NT][2], const i32x4 
   }
 }
 
-// Dot of one 16-byte Q8_0 chunk with 16 inputs held in registers.
-__device__ __forceinline__ float q8_dot16(const uint4 w, const float4 (&x)[4]) {
-  const uint32_t d[4] = {w.x, w.y, w.z, w.w};
-  float s = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s += (float)(d[i] & 0xffu) * x[i].x;
-    s += (float)((d[i] >> 8) & 0xffu) * x[i].y;
-    s += (float)((d[i] >> 16) & 0xffu) * x[i].z;
-    s += (float)(d[i] >> 24) * x[i].w;
-  }
-  return s;
-}
-
 // The projection weights of a block's rows [p0, p1) (p0 a multiple of 16, at most kPTiles
 // tiles of 16) of layer L in the operand layout above, read from the matrix-core order (every load
 // is 1 KB of consecutive bytes): the wave's runs of row p0 + 16 tile + (lane & 15) and the
@@ -426,47 +412,49 @@ __device__ __forceinline__ void issue_out(GLayer& L, int ob, OutRegs<U>& R) {
 
 // A head block owns value columns [half * kHCols, + kHCols) of head h.  Its registers: wave
 // w's state tile (rows 8 (lane & 15) .. + 8, columns half * kHCols + 16 w + 4 (lane >> 4)
-// .. + 4) and the block's gate-weight chunks: item i of thread t is chunk (i * kPT + t) of
-// the [kHD alpha rows | kHCols gate rows] x rank slice (the first CPR / 2 items of every
-// thread are alpha rows).
-template <int CPR>   // 16-byte chunks per low-rank row: CPR = rank / 16
+// .. + 4) and the B operands of its three gate tiles (below): F_b rows 16 w and 16 (w + 4) of
+// the head (alpha), G_b rows half * kHCols + 16 w of the head (output gate).
+template <int CPR>   // CPR = rank / 16
 struct HeadRegs {
-  static constexpr int kItems = ((kHD + kHCols) * CPR + kPT - 1) / kPT;
   float4 st[8];
-  uint4 gw[kItems];
-  uint32_t gd[kItems];
-  float dtb[kItems];
+  i32x4 bw[3][2];          // [tile][half]: the lane's 16 bytes of Q8_0 block lane >> 4 of row lane & 15
+  uint32_t bd[3];          // fp16 bits of that block's scale
+  float dtb;               // dt_bias of the alpha row this lane finishes (lane groups 0 and 1)
   float4 onw;
   float ea;                // A_log[h], exponentiated when used
 };
+
+// The gate tiles in the order gate_order_kernel writes them: tile tau of a matrix is 16 rank
+// bytes, lane (n, g) reads chunk (half, g, n) when g < rank / 32 (zero otherwise).
+template <int CPR>
+__device__ __forceinline__ void load_gate_tile(const int8_t* w, const uint16_t* d, int tau,
+                                               i32x4 (&rw)[2], uint32_t& rd) {
+  constexpr int NB = CPR / 2, rank = CPR * 16;
+  const int lane = threadIdx.x & 63, n = lane & 15, g = lane >> 4;
+  rw[0] = rw[1] = i32x4{0, 0, 0, 0};
+  rd = 0;
+  if (g < NB) {
+    const int8_t* b = w + (size_t)tau * 16 * rank + (g * 16 + n) * 16;
+    rw[0] = wload_i(b);
+    rw[1] = wload_i(b + NB * 256);
+    rd = *(const KDA_GLOBAL uint16_t*)(d + ((size_t)tau * NB + g) * 16 + n);
+  }
+}
 
 template <int CPR>
 __device__ __forceinline__ void issue_head(const PersistParams& P, GLayer& L, const float* Sl,
                                            int h, int half, HeadRegs<CPR>& R) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int rank = CPR * 16;
   const int j = half * kHCols + wave * 16 + (lane >> 4) * 4, r0 = (lane & 15) * 8;
   const float* Sb = Sl + (size_t)h * kHD * kHD + j;
 #pragma unroll
   for (int i = 0; i < 8; ++i) R.st[i] = gload4(Sb + (size_t)(r0 + i) * kHD);
-  const int c = tid % CPR;
-#pragma unroll
-  for (int i = 0; i < HeadRegs<CPR>::kItems; ++i) {
-    const int it = i * kPT + tid;
-    const int row = it / CPR;                        // [0, kHD): alpha, then gate columns
-    const bool f = i < CPR / 2;
-    R.gw[i] = make_uint4(0, 0, 0, 0);
-    R.gd[i] = 0;
-    R.dtb[i] = 0.0f;
-    if (it < (kHD + kHCols) * CPR) {
-      const uint8_t* mw = f ? L.fb.w : L.gb.w;
-      const __half* md = f ? L.fb.d : L.gb.d;
-      const int r = f ? h * kHD + row : h * kHD + half * kHCols + (row - kHD);
-      R.gw[i] = wload(mw + (size_t)r * rank + (size_t)c * 16);
-      R.gd[i] = sload(md + (size_t)r * (rank / 32) + (c >> 1));
-      if (f) R.dtb[i] = *gp(L.dt_bias + r);
-    }
-  }
+  constexpr int kTilesPerHead = kHD / 16;
+  load_gate_tile<CPR>(L.fbw, L.fbd, h * kTilesPerHead + wave, R.bw[0], R.bd[0]);
+  load_gate_tile<CPR>(L.fbw, L.fbd, h * kTilesPerHead + wave + 4, R.bw[1], R.bd[1]);
+  load_gate_tile<CPR>(L.gbw, L.gbd, h * kTilesPerHead + half * (kHCols / 16) + wave, R.bw[2], R.bd[2]);
+  const int g = lane >> 4;
+  R.dtb = g < 2 ? *gp(L.dt_bias + h * kHD + 16 * (wave + 4 * g) + (lane & 15)) : 0.0f;
   R.onw = make_float4(1.f, 1.f, 1.f, 1.f);
   if (L.o_norm_w) R.onw = gload4(L.o_norm_w + j);
   R.ea = *gp(L.a_log + h);
@@ -481,6 +469,8 @@ struct Smem {
   alignas(16) float s_in[1024];  // head block: q | k | v | f_lr | g_lr | beta
   alignas(16) float s_al[kHD];     // head block: alpha rows
   alignas(16) float s_gt[kHCols];  // head block: output-gate columns
+  alignas(16) int8_t gpl[4 * 256];   // head block: planes of [f_lr | g_lr]; [3] = 0
+  float ginv[8];                     // head block: 1 / scale of each 32-element block of them
   alignas(16) int any[2][4];       // block_any: per-wave votes, two alternating sets
 };
 
@@ -494,7 +484,9 @@ __device__ __forceinline__ bool block_any(Smem& sm, int set, int pred) {
   if ((threadIdx.x & 63) == 0) sm.any[set][threadIdx.x >> 6] = any;
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
   const int4 v = *reinterpret_cast<const int4*>(sm.any[set]);
-  return (v.x | v.y | v.z | v.w) != 0;
+  // the same value in every lane: said so, so that the branches on it (and the layer loops
+  // they leave) stay scalar
+  return __builtin_amdgcn_readfirstlane(v.x | v.y | v.z | v.w) != 0;
 }
 
 // Static roles of block b: [0, kHSplit H) heads, then P.o_blocks output bands of 32 rows,
@@ -652,52 +644,89 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
       const int i = tid + k * kPT;
       if (i >= i_lr && i < n_in) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
+    // element e = i - i_lr of [f_lr | g_lr] is in this thread's slot 1 or 2, and each block of
+    // 32 of them (the Q8_0 blocks of F_b and G_b rows) fills half a wave, which turns it into
+    // three signed 7-bit planes under the block's own power-of-two scale (as the projection
+    // inputs, with a block in place of a wave's runs)
+    static_assert(i_lr % 64 == 0 && (2 * rank) % 64 == 0, "whole waves per low-rank block pair");
+    {
+      const int e1 = tid + kPT - i_lr, e2 = e1 + kPT;
+      const bool in1 = e1 >= 0 && e1 < 2 * rank, in2 = e2 >= 0 && e2 < 2 * rank;  // wave-uniform
+      if (in1 || in2) {
+        const int e = in1 ? e1 : e2;
+        const float u = __uint_as_float((uint32_t)(in1 ? w[1] : w[2]));
+        float ss = sum16(u * u);
+        ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));  // lane ^ 16
+        constexpr float M = 12582912.0f;
+        const int ex = (__builtin_amdgcn_frexp_expf(ss) + 1) >> 1;
+        const float sc = __builtin_amdgcn_ldexpf(1.0f, 6 - ex);
+        const float t0 = fmaf(u, sc, M), q0 = t0 - M, r0 = fmaf(u, sc, -q0);
+        const float t1 = fmaf(r0, 128.0f, M), q1 = t1 - M, r1 = fmaf(r0, 128.0f, -q1);
+        const float t2 = fmaf(r1, 128.0f, M);
+        sm.gpl[e] = (int8_t)__float_as_uint(t0);
+        sm.gpl[256 + e] = (int8_t)__float_as_uint(t1);
+        sm.gpl[512 + e] = (int8_t)__float_as_uint(t2);
+        if ((e & 31) == 0) sm.ginv[e >> 5] = __builtin_amdgcn_ldexpf(1.0f, ex - 6);
+      }
+    }
     if (block_any(sm, 0, bad)) return false;
   }
   // request the q/k/v words again now: the round trip overlaps the gates below, and the
-  // replies are merged only after them
+  // replies are merged only after them.  Only slots that hold q/k/v inputs are requested: a
+  // load whose result is never used frees its register at once, and reusing that register
+  // makes the code wait for the load.
   uint64_t again[3];
 #pragma unroll
-  for (int k = 0; k < 3; ++k) again[k] = peek(src[k]);
+  for (int k = 0; k < 3; ++k) {
+    again[k] = w[k];
+    if (k * kPT < i_lr && tid + k * kPT < i_lr) again[k] = peek(src[k]);
+  }
   const float* s_q = sm.s_in;
   const float* s_k = sm.s_in + dk;
   const float* s_v = sm.s_in + 2 * dk;
-  const float* s_fl = sm.s_in + 2 * dk + kHCols;
-  const float* s_gl = s_fl + rank;
   const float beta = sigmoid_f(sm.s_in[2 * dk + kHCols + 2 * rank]);
-  // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr).
-  // Thread t's items all sit in chunk c = t % CPR of their rows, so it needs one 16-element
-  // slice of f_lr and one of g_lr.  After the group sums, lane c of each group finishes
-  // item c: one transcendental per lane.
+  // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr), on the
+  // int8 matrix cores as the projections: A row 4 i + p holds plane p of block i on lane
+  // group i, B the tile's Q8_0 bytes, so accumulator lane (n, g) holds block g's three plane
+  // dots for row n.  Each block's two scales are applied there and the four lane groups
+  // summed (the same total in every group); lane group 0 then finishes alpha row 16 w + n,
+  // group 1 alpha row 16 (w + 4) + n, group 2 gate column 16 w + n.
   {
-    constexpr int NI = HeadRegs<CPR>::kItems;
-    const int c = tid % CPR;
-    float4 xf[4], xg[4];
-    float sf = 0.0f, sg = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      xf[k] = reinterpret_cast<const float4*>(s_fl + c * 16)[k];
-      xg[k] = reinterpret_cast<const float4*>(s_gl + c * 16)[k];
-      sf += (xf[k].x + xf[k].y) + (xf[k].z + xf[k].w);
-      sg += (xg[k].x + xg[k].y) + (xg[k].z + xg[k].w);
-    }
-    float mine = 0.0f, bias = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float part = i < CPR / 2 ? q8_dot16(hr.gw[i], xf) - 128.0f * sf : q8_dot16(hr.gw[i], xg) - 128.0f * sg;
-      part = group_sum(h2f(hr.gd[i]) * part, CPR);
-      if (c == i) { mine = part; bias = hr.dtb[i]; }
-    }
-    const int it = c * kPT + tid, grow = it / CPR;
-    if (c < NI && it < (kHD + kHCols) * CPR) {
-      if (grow < dk) sm.s_al[grow] = expf(-expf(hr.ea) * softplus_f(mine + bias));
-      else sm.s_gt[grow - dk] = sigmoid_f(mine);
-    }
+    constexpr int NB = CPR / 2;
+    const int m = lane & 15, g = lane >> 4;
+    const int8_t* pa = sm.gpl + ((m >> 2) == g && g < NB ? (m & 3) : 3) * 256 + 32 * g;
+    const i32x4 af0 = *reinterpret_cast<const i32x4*>(pa);
+    const i32x4 af1 = *reinterpret_cast<const i32x4*>(pa + 16);
+    const i32x4 ag0 = *reinterpret_cast<const i32x4*>(pa + rank);
+    const i32x4 ag1 = *reinterpret_cast<const i32x4*>(pa + rank + 16);
+    const i32x4 zero = {0, 0, 0, 0};
+    i32x4 c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(af0, hr.bw[0][0], zero, 0, 0, 0);
+    i32x4 c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(af0, hr.bw[1][0], zero, 0, 0, 0);
+    i32x4 c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ag0, hr.bw[2][0], zero, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(af1, hr.bw[0][1], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(af1, hr.bw[1][1], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(ag1, hr.bw[2][1], c2, 0, 0, 0);
+    // (lane groups past the last block have zero weights and take no scale)
+    const float sf = g < NB ? sm.ginv[g] : 0.0f, sg = g < NB ? sm.ginv[NB + g] : 0.0f;
+    auto planes = [](const i32x4 r) { return fmaf((float)(r[1] * 128 + r[2]), 1.0f / 16384.0f, (float)r[0]); };
+    float y0 = h2f(hr.bd[0]) * sf * planes(c0);
+    float y1 = h2f(hr.bd[1]) * sf * planes(c1);
+    float y2 = h2f(hr.bd[2]) * sg * planes(c2);
+    y0 += __shfl_xor(y0, 16);
+    y1 += __shfl_xor(y1, 16);
+    y2 += __shfl_xor(y2, 16);
+    y0 += __shfl_xor(y0, 32);
+    y1 += __shfl_xor(y1, 32);
+    y2 += __shfl_xor(y2, 32);
+    const float pre = g == 0 ? y0 : g == 1 ? y1 : y2;
+    if (g < 2) sm.s_al[16 * (wave + 4 * g) + m] = expf(-expf(hr.ea) * softplus_f(pre + hr.dtb));
+    else if (g == 2) sm.s_gt[16 * wave + m] = sigmoid_f(pre);
   }
   {
     // q, k, v
 #pragma unroll
-    for (int k = 0; k < 3; ++k) w[k] = (uint32_t)(w[k] >> 32) == tag ? w[k] : again[k];
+    for (int k = 0; k < 3; ++k)
+      if (k * kPT < i_lr) w[k] = (uint32_t)(w[k] >> 32) == tag ? w[k] : again[k];
     const int bad = !wait_slots(false);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -853,6 +882,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
   const int tid = threadIdx.x;
   if constexpr (ROLE == 1) {
+    sm.gpl[3 * 256 + tid] = 0;   // the zero plane of the gate inputs
     HeadRegs<CPR> hr;
     issue_head<CPR>(P, Lt[0], P.S, blockIdx.x % P.H, blockIdx.x / P.H, hr);
     for (int l = 0; l < P.n_layers; ++l)
@@ -870,7 +900,8 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
       if (!phase_o<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, orr)) return;
       if (l + 1 < P.n_layers) {
         hold_prefetch();
-        issue_out<U>(Lt[l + 1], R.ob, orr);
+        // (the layer index is uniform; said so, so that its table entry is a scalar load)
+        issue_out<U>(Lt[__builtin_amdgcn_readfirstlane(l + 1)], R.ob, orr);
       }
     }
   } else {
@@ -935,6 +966,35 @@ hipError_t launch_mma_order(const MmaSource& src, int rows, int D, int8_t* w, ui
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (D == 1024) mma_order_kernel<1><<<blocks, 256, 0, s>>>(src, rows, w, d, n);
   else mma_order_kernel<2><<<blocks, 256, 0, s>>>(src, rows, w, d, n);
+  return hipGetLastError();
+}
+
+// One thread per 16-byte chunk of the gate order (persist.h): chunk
+// c = ((tile * 2 + h) * NB + g) * 16 + n holds row 16 tile + n, bytes [32 g + 16 h, + 16),
+// flipped from q + 128 to q; the h = 0 chunk also places that block's scale.
+__global__ void gate_order_kernel(const uint8_t* __restrict__ src_w, const __half* __restrict__ src_d,
+                                  int rank, int8_t* __restrict__ w, uint16_t* __restrict__ d,
+                                  int64_t nchunks) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  const int nb = rank / 32;
+  const int n = (int)(c % 16);
+  int64_t r = c / 16;
+  const int g = (int)(r % nb);
+  r /= nb;
+  const int h = (int)(r % 2);
+  const int64_t tile = r / 2;
+  const int64_t row = tile * 16 + n;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src_w + row * rank + 32 * g + 16 * h);
+  *reinterpret_cast<u32x4*>(w + c * 16) = v ^ 0x80808080u;
+  if (h == 0) d[(tile * nb + g) * 16 + n] = __half_as_ushort(src_d[row * nb + g]);
+}
+
+hipError_t launch_gate_order(const uint8_t* w_src, const __half* d_src, int rows, int rank,
+                             int8_t* w, uint16_t* d, hipStream_t s) {
+  if ((rank != 32 && rank != 64 && rank != 128) || rows < 16 || rows % 16 != 0) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * rank / 16;
+  gate_order_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(w_src, d_src, rank, w, d, n);
   return hipGetLastError();
 }
 
