@@ -107,6 +107,15 @@ struct Spin {
   }
 };
 
+// The critical path's transcendentals on the hardware's base-2 exp and log, reciprocal and
+// reciprocal square root (about 1 ulp each, against the 1e-3 the step is held to); the
+// correctly rounded library forms cost 20-60 instructions each.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.44269504088896341f); }
+__device__ __forceinline__ float ln_hw(float x) { return __builtin_amdgcn_logf(x) * 0.693147180559945309f; }
+__device__ __forceinline__ float rsq_hw(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float sigmoid_hw(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-z)); }
+__device__ __forceinline__ float softplus_hw(float z) { return fmaxf(z, 0.0f) + ln_hw(1.0f + exp_hw(-fabsf(z))); }
+
 enum FlagPhase { kFlagH = 1, kFlagO = 2 };
 
 // Wall-clock ticks (100 MHz) a block holds its next-layer prefetch back after its phase, so
@@ -562,10 +571,13 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
     const float4 s0 = q[0], s1 = q[1], s2 = q[2], s3 = q[3];
     const float sum = ((s0.x + s0.y) + (s0.z + s0.w)) + ((s1.x + s1.y) + (s1.z + s1.w)) +
                       ((s2.x + s2.y) + (s2.z + s2.w)) + ((s3.x + s3.y) + (s3.z + s3.w));
-    const float sc = 1.0f / sqrtf((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
+    const float sc = rsq_hw((sm.red[0] + sm.red[1] + sm.red[2] + sm.red[3]) / (float)D + P.eps);
     const float pre = sum * sc;
     float o = pre;
-    if (row < C) o = silu_f(pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * pre);
+    if (row < C) {
+      const float cv = pr.cw.x * pr.z0 + pr.cw.y * pr.z1 + pr.cw.z * pr.z2 + pr.cw.w * pre;
+      o = cv * sigmoid_hw(cv);
+    }
     put(P.pbuf + row, tag, o);
     // off the critical path: roll the conv window
     if (row < C) {
@@ -684,7 +696,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const float* s_q = sm.s_in;
   const float* s_k = sm.s_in + dk;
   const float* s_v = sm.s_in + 2 * dk;
-  const float beta = sigmoid_f(sm.s_in[2 * dk + kHCols + 2 * rank]);
+  const float beta = sigmoid_hw(sm.s_in[2 * dk + kHCols + 2 * rank]);
   // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr), on the
   // int8 matrix cores as the projections: A row 4 i + p holds plane p of block i on lane
   // group i, B the tile's Q8_0 bytes, so accumulator lane (n, g) holds block g's three plane
@@ -719,8 +731,10 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     y1 += __shfl_xor(y1, 32);
     y2 += __shfl_xor(y2, 32);
     const float pre = g == 0 ? y0 : g == 1 ? y1 : y2;
-    if (g < 2) sm.s_al[16 * (wave + 4 * g) + m] = expf(-expf(hr.ea) * softplus_f(pre + hr.dtb));
-    else if (g == 2) sm.s_gt[16 * wave + m] = sigmoid_f(pre);
+    const float al = exp_hw(-exp_hw(hr.ea) * softplus_hw(pre + hr.dtb));   // (both forms in
+    const float gt = sigmoid_hw(pre);                                      // every lane: no branch)
+    if (g < 2) sm.s_al[16 * (wave + 4 * g) + m] = al;
+    else if (g == 2) sm.s_gt[16 * wave + m] = gt;
   }
   {
     // q, k, v
@@ -756,8 +770,8 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     aq += qa[i] * qa[i];
     ak += ka[i] * ka[i];
   }
-  const float inv_q = P.q_scale / sqrtf(sum16(aq) + P.l2_eps);
-  const float inv_k = 1.0f / sqrtf(sum16(ak) + P.l2_eps);
+  const float inv_q = P.q_scale * rsq_hw(sum16(aq) + P.l2_eps);
+  const float inv_k = rsq_hw(sum16(ak) + P.l2_eps);
   float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -836,7 +850,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   // lane kParts t ends up with head t's sum of squares; every lane computes a scale, lane
   // kParts t's is head t's
   const float psum = group_sum(__uint_as_float((uint32_t)pw), kParts);
-  const int hsl = __float_as_int(1.0f / sqrtf(psum / (float)kHD + P.eps));
+  const int hsl = __float_as_int(rsq_hw(psum / (float)kHD + P.eps));
   float ss = 0.0f;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
