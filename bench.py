@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744042108,
-                "sha256": "b9b50c22759f8eba850125a48c09c88c2d427139294d545e91114ba0d484720a",
+STEP_TRAFFIC = {"bytes": 744059130,
+                "sha256": "9fb341d1561c5517afd7b724c9441f90bb2171f157ba187c39a6fd3ba7861333",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
