@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744059130,
-                "sha256": "9fb341d1561c5517afd7b724c9441f90bb2171f157ba187c39a6fd3ba7861333",
+STEP_TRAFFIC = {"bytes": 744806259,
+                "sha256": "1e5791711cdc0f3af0d2ff3e85c89a2247f2e3fd9439be51a934763efd83c5ac",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
