@@ -152,6 +152,18 @@ def test_decode_stack_one_launch_three_layers_32_steps(torch):
     _decode_parity(w, w.steps, snap_every=8, expect_persistent=True)
 
 
+@pytest.mark.parametrize("D,rank", [(1024, 32), (1024, 128), (2048, 64)])
+def test_decode_one_launch_other_shapes(torch, D, rank):
+    """The one-launch decode at its other compiled shapes: D = 1024 (8 heads, two input runs
+    per wave) and low ranks 32 and 64, whose gate tiles leave lane groups past rank / 32
+    empty; two layers, 6 tokens, the state checked every 3."""
+    d = synth.LayerDims(d_model=D, n_heads=D // 128, d_k=128, d_v=128, rank_f=rank, rank_g=rank)
+    w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=2, steps=6, seed=70 + rank + D // 1024)
+    _say(f"decode one-launch D={D} H={D // 128} rank={rank} 2 layers 6 steps")
+    e, s = _decode_parity(w, w.steps, snap_every=3, expect_persistent=True)
+    _say(f"  D={D} rank={rank}: out {e:.2e} state {s:.2e}")
+
+
 def test_graph_replay_equals_eager(torch):
     """The captured hipGraph replays exactly the eager launches (deterministic kernels)."""
     w = synth.scaled(synth.WORKLOADS["layer"], steps=5)
