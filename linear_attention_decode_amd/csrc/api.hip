@@ -241,8 +241,10 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   float* gate = reinterpret_cast<float*>(ws + wl.gate);
   float* ss = reinterpret_cast<float*>(ws + wl.ss);
 
+  // verify on the matrix-core path runs its conv in the projection epilogue
+  const bool conv_fused = act && skinny_supported(d.wtype, N, d.d_model);
   GemvParams pp;
-  proj_segments(m, L, pp, decode);
+  proj_segments(m, L, pp, decode || conv_fused);
   pp.K = d.d_model;
   pp.N = N;
   pp.x = x_in;
@@ -254,6 +256,10 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   pp.conv_w = L.conv_w;
   pp.win = win;
   pp.C = m->C;
+  if (conv_fused) {
+    pp.act = act;
+    pp.T = T;
+  }
   const int g1 = proj_grid(pp);
   int r = timed(m, KDA_K_PROJ, s, rec, [&] {
     if (skinny_supported(d.wtype, N, pp.K)) return launch_skinny(kProX, pp, ws + wl.sk, s);
@@ -261,7 +267,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   });
   if (r) return r;
 
-  if (act) {
+  if (act && !conv_fused) {
     r = timed(m, KDA_K_PROJ, s, rec, [&] {
       return launch_conv_seq(proj, m->proj_stride, win, L.conv_w, act, B, T, m->C, s);
     });

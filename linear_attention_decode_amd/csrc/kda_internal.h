@@ -69,6 +69,10 @@ struct GemvParams {
   const float* conv_w = nullptr;  // [C][4]
   float* win = nullptr;           // [N][3][C]
   int C = 0;
+  // verify conv epilogue (launch_skinny only): columns n = b T + t; act[n][c] = SiLU of the
+  // conv over sequence b's window and its tokens 0..t, the window left as it is
+  float* act = nullptr;           // [N][C]
+  int T = 0;
 };
 
 constexpr int kGemvKSmall = 2048;   // input length of the multi-column variants

@@ -179,6 +179,8 @@ struct SkParams {
   const float* conv_w = nullptr;
   float* win = nullptr;
   int C = 0;
+  float* act = nullptr;
+  int T = 0;
 };
 
 // 8 weight bytes u -> 8 fp16 values 1024 + u (byte permutes against 0x64 high bytes)
@@ -198,6 +200,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   constexpr int KB = 4 * KB4;
   constexpr int PD = 4;                          // k blocks of B fragments in flight
   __shared__ float part[4][NT][64][4];           // per-wave partial outputs
+  __shared__ float s_row[kSkRows][NT * 16];      // verify conv: the block's rows, all columns
   __shared__ __half s_sc[KB][kSkRows];           // [k block][row] Q8_0 scales
   __shared__ __align__(16) float s_xs[KB][NT * 16];   // [k block][column] block sums
   const int tid = threadIdx.x, lane = tid & 63;
@@ -322,7 +325,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     float v = (part[0][t][l][i] + part[1][t][l][i]) + (part[2][t][l][i] + part[3][t][l][i]);
     v *= P.S.cscale[n];
     const int grow = row0 + row;
-    if (sg.conv_chan >= 0) {
+    if (sg.conv_chan >= 0 && P.act) {
+      s_row[row][n] = v;           // raw projection (logged); the conv runs below
+    } else if (sg.conv_chan >= 0) {
       // causal conv over (window, this token), SiLU, window roll (one owner per channel)
       const int c = sg.conv_chan + grow;
       const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
@@ -337,6 +342,27 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     const size_t o = (size_t)n * P.out_stride + sg.out_off + grow;
     if (P.resid) v += P.resid[o];
     P.out[o] = v;
+  }
+  if (sg.conv_chan >= 0 && P.act) {
+    // verify: each (row, sequence) runs the causal conv + SiLU over the sequence's window
+    // and its T tokens in order; the window is read, not rolled (the commit rolls it)
+    __syncthreads();
+    const int nb = P.N / P.T;
+    for (int e = tid; e < nrows * nb; e += kSkThreads) {
+      const int row = e / nb, b = e - row * nb;
+      const int c = sg.conv_chan + row0 + row;
+      const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
+      const float* z = P.win + (size_t)b * 3 * P.C + c;
+      float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
+      for (int t = 0; t < P.T; ++t) {
+        const float pv = s_row[row][b * P.T + t];
+        const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * pv;
+        z0 = z1;
+        z1 = z2;
+        z2 = pv;
+        P.act[(size_t)(b * P.T + t) * P.C + c] = silu_f(y);
+      }
+    }
   }
 }
 
@@ -362,6 +388,8 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.conv_w = g.conv_w;
   p.win = g.win;
   p.C = g.C;
+  p.act = g.act;
+  p.T = g.T;
   const int KG = g.K / 2048;
   if (prologue == kProX) {
     if (KG == 2) skinny_prep_kernel<kProX, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
