@@ -791,11 +791,8 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
     hp.S = st->S_dev + l * state_layer_stride(m, B);
     hp.write_state = 1; hp.ntok = accept_dev; hp.write_out = 0;
     hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
+    hp.win_commit = win;      // the window roll runs in the same launch, after the replay
     r = timed(m, KDA_K_COMMIT, s, m->timing, [&] { return launch_head(hp, s); });
-    if (r) return r;
-    r = timed(m, KDA_K_COMMIT, s, m->timing, [&] {
-      return launch_window_commit(logf + l * log_layer, m->proj_stride, win, B, T, m->C, accept_dev, s);
-    });
     if (r) return r;
   }
   return KDA_OK;

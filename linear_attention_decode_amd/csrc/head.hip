@@ -291,6 +291,27 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     for (int i = 0; i < RPT; ++i)
       *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];
   }
+
+  // commit: the window becomes the last 3 of (window, p_0 .. p_{a-1}) per (sequence,
+  // channel), a = the accepted tokens; every wave of the grid takes a strided share (the
+  // replay above reads the logged activations, never the window)
+  if (P.win_commit) {
+    const int nwave = gridDim.x * gridDim.y * gridDim.z;
+    const int wid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    for (int i = wid * 64 + lane; i < C * P.B; i += nwave * 64) {
+      const int sb = i / C, c = i - sb * C;
+      const int a = min(max(P.ntok[sb], 1), P.T);
+      float* z = P.win_commit + (size_t)sb * 3 * C + c;
+      float seq[3 + 8];
+      seq[0] = z[0];
+      seq[1] = z[C];
+      seq[2] = z[2 * C];
+      for (int t = 0; t < a; ++t) seq[3 + t] = P.proj[(size_t)(sb * P.T + t) * P.proj_stride + c];
+      z[0] = seq[a];
+      z[C] = seq[a + 1];
+      z[2 * C] = seq[a + 2];
+    }
+  }
 }
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
@@ -332,31 +353,6 @@ hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
                            const float* conv_w, float* act, int B, int T, int C, hipStream_t s) {
   dim3 grid((C + 255) / 256, B);
   conv_seq_kernel<<<grid, 256, 0, s>>>(plog, proj_stride, win, conv_w, act, T, C);
-  return hipGetLastError();
-}
-
-__global__ void window_commit_kernel(const float* __restrict__ plog, int stride,
-                                     float* __restrict__ win, int T, int C,
-                                     const int* __restrict__ ntok) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  const int b = blockIdx.y;
-  if (c >= C) return;
-  const int a = min(max(ntok[b], 1), T);
-  float* z = win + (size_t)b * 3 * C + c;
-  float seq[3 + 8];
-  seq[0] = z[0];
-  seq[1] = z[C];
-  seq[2] = z[2 * C];
-  for (int t = 0; t < a; ++t) seq[3 + t] = plog[(size_t)(b * T + t) * stride + c];
-  z[0] = seq[a];
-  z[C] = seq[a + 1];
-  z[2 * C] = seq[a + 2];
-}
-
-hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,
-                                int C, const int* ntok, hipStream_t s) {
-  dim3 grid((C + 255) / 256, B);
-  window_commit_kernel<<<grid, 256, 0, s>>>(plog, proj_stride, win, T, C, ntok);
   return hipGetLastError();
 }
 

@@ -107,6 +107,9 @@ struct HeadParams {
   float* ss = nullptr;            // [N][H][dv/kHeadCols] partial sums of o^2
   float l2_eps = 0.f;
   float q_scale = 0.f;            // d_k^-1/2 as fp32
+  // commit only: the layer's conv window [B][3][C], rolled by the accepted tokens' logged
+  // pre-conv projections (proj) once the replay is done (null: left alone)
+  float* win_commit = nullptr;
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
@@ -125,13 +128,10 @@ hipError_t launch_gates(const GatesParams& p, hipStream_t s);
 // number of 16-byte chunks per row, at most 10 chunk loads per thread).
 bool head_supported(int dk, int wt, int rank_f, int rank_g);
 
-// New conv window after `ntok[b]` tokens: last 3 of (window, p_0 .. p_{T-1}).
 // Conv + SiLU over T tokens per sequence from the committed window (left unchanged):
 // act[b*T + t][c] from the pre-conv projections plog[b*T + t][c] (stride proj_stride).
 hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
                            const float* conv_w, float* act, int B, int T, int C, hipStream_t s);
-hipError_t launch_window_commit(const float* plog, int proj_stride, float* win, int B, int T,
-                                int C, const int* ntok, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
 // Chunked prefill.
