@@ -47,6 +47,11 @@ struct LayerDev {
   const float* a_log;
   const float* dt_bias;
   const float* o_norm_w;
+  // F_b and G_b in gate-tile order (the one-launch decode's copy; null without it)
+  const int8_t* fbw = nullptr;
+  const uint16_t* fbd = nullptr;
+  const int8_t* gbw = nullptr;
+  const uint16_t* gbd = nullptr;
 };
 
 struct GraphKey {
@@ -223,6 +228,7 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
   gp.N = N; gp.K = m->Kq; gp.V = m->V; gp.dk = d.d_k; gp.rank = d.rank_f; gp.C = m->C;
   gp.wt = d.wtype; gp.proj = proj; gp.proj_stride = m->proj_stride;
   gp.fb = L.fb; gp.gb = L.gb; gp.a_log = L.a_log; gp.dt_bias = L.dt_bias; gp.out = ag;
+  gp.fbw = L.fbw; gp.fbd = L.fbd; gp.gbw = L.gbw; gp.gbd = L.gbd;
   return timed(m, KDA_K_GATES, s, rec, [&] { return launch_gates(gp, s); });
 }
 
@@ -472,6 +478,13 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   p.q_blocks = m->C / 48;
   m->pers_blocks = nb;
   m->pers_ok = true;
+  // the per-layer path's many-column gates read the same F_b / G_b copies
+  for (int l = 0; l < d.n_layers; ++l) {
+    m->layers[l].fbw = host[l].fbw;
+    m->layers[l].fbd = host[l].fbd;
+    m->layers[l].gbw = host[l].gbw;
+    m->layers[l].gbd = host[l].gbd;
+  }
   return hipSuccess;
 }
 

@@ -135,6 +135,101 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// The same gates for N > 1 token columns on the int8 matrix cores, from F_b and G_b in
+// gate-tile order (per tile of 16 rows: [2 halves][rank/32 blocks][16 rows][16 bytes] of
+// signed q, scales [tile][rank/32][16]).  A block takes 4 tiles (one per wave) and 8 token
+// columns.  It first turns each column's f_lr and g_lr into three signed 7-bit planes per
+// 32-element block under the block's own power-of-two scale (x s = x0 + x1/128 + x2/16384
+// + r, |r| <= 2^-15, every product exact in int32).  Then, per column, A row 4 i + p holds
+// plane p of block i on lane group i and B the tile's bytes, so accumulator lane (n, g) has
+// block g's plane dots for row n; each block's scales are applied there and the four lane
+// groups summed.  Lane group g finishes columns g and 4 + g of its row.
+// ---------------------------------------------------------------------------------------
+typedef int i32x4g __attribute__((ext_vector_type(4)));
+constexpr int kGmCols = 8;       // token columns per block
+
+template <int CPR>
+__global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
+  constexpr int NB = CPR / 2, rank = CPR * 16;     // Q8_0 blocks per row, rank
+  constexpr float M = 12582912.0f;
+  __shared__ __align__(16) int8_t gpl[kGmCols][4][256];   // [column][plane][f | g]; plane 3 = 0
+  __shared__ float ginv[kGmCols][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = blockIdx.y * kGmCols, nc = min(kGmCols, P.N - n0);
+  {
+    // thread t: column t / 32, element t % 32 of each 32-element block (a half-wave a block)
+    const int cn = tid >> 5, j = tid & 31;
+#pragma unroll
+    for (int blk = 0; blk < 2 * NB; ++blk) {
+      const float u = cn < nc ? P.proj[(size_t)(n0 + cn) * P.proj_stride + P.C + 32 * blk + j] : 0.0f;
+      float ss = sum16(u * u);
+      ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));   // lane ^ 16
+      const int ex = (__builtin_amdgcn_frexp_expf(ss) + 1) >> 1;
+      const float sc = __builtin_amdgcn_ldexpf(1.0f, 6 - ex);
+      const float t0 = fmaf(u, sc, M), q0 = t0 - M, r0 = fmaf(u, sc, -q0);
+      const float t1 = fmaf(r0, 128.0f, M), q1 = t1 - M, r1 = fmaf(r0, 128.0f, -q1);
+      const float t2 = fmaf(r1, 128.0f, M);
+      const int e = 32 * blk + j;
+      gpl[cn][0][e] = (int8_t)__float_as_uint(t0);
+      gpl[cn][1][e] = (int8_t)__float_as_uint(t1);
+      gpl[cn][2][e] = (int8_t)__float_as_uint(t2);
+      gpl[cn][3][e] = 0;
+      if (j == 0) ginv[cn][blk] = __builtin_amdgcn_ldexpf(1.0f, ex - 6);
+    }
+    // the rest of the zero plane (lane groups past the last block read it)
+    for (int e = 2 * rank + j; e < 256; e += 32) gpl[cn][3][e] = 0;
+  }
+  __syncthreads();
+  const int ftiles = P.K / 16, tau = blockIdx.x * 4 + wave;
+  if (tau >= (P.K + P.V) / 16) return;
+  const bool f = tau < ftiles;
+  const int tl = f ? tau : tau - ftiles;
+  const int m = lane & 15, g = lane >> 4;
+  i32x4g bw0 = {0, 0, 0, 0}, bw1 = {0, 0, 0, 0};
+  float dsc = 0.0f;
+  if (g < NB) {
+    const int8_t* bp = (f ? P.fbw : P.gbw) + (size_t)tl * 16 * rank + (g * 16 + m) * 16;
+    bw0 = *reinterpret_cast<const i32x4g*>(bp);
+    bw1 = *reinterpret_cast<const i32x4g*>(bp + NB * 256);
+    const uint16_t* dp = (f ? P.fbd : P.gbd) + ((size_t)tl * NB + g) * 16 + m;
+    dsc = __half2float(__ushort_as_half(*dp));
+  }
+  const int row = 16 * tau + m;              // alpha rows, then gate rows
+  float bias = 0.0f, ah = 0.0f;
+  if (f) {
+    bias = P.dt_bias[row];
+    ah = P.a_log[row / P.dk];
+  }
+  const int8_t* abase = &gpl[0][(m >> 2) == g && g < NB ? (m & 3) : 3][(f ? 0 : rank) + 32 * g];
+  const i32x4g zero = {0, 0, 0, 0};
+  float res[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    float ys[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int cn = 4 * r + q;
+      const int8_t* pa = abase + cn * 4 * 256;
+      i32x4g c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa), bw0, zero, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa + 16), bw1, c, 0, 0, 0);
+      const float v = fmaf((float)(c[1] * 128 + c[2]), 1.0f / 16384.0f, (float)c[0]);
+      float y = g < NB ? dsc * ginv[cn][(f ? 0 : NB) + g] * v : 0.0f;
+      y += __shfl_xor(y, 16);
+      y += __shfl_xor(y, 32);
+      ys[q] = y;
+    }
+    res[r] = g == 0 ? ys[0] : g == 1 ? ys[1] : g == 2 ? ys[2] : ys[3];
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int cn = 4 * r + g;
+    if (cn < nc)
+      P.out[(size_t)(n0 + cn) * (P.K + P.V) + row] =
+          f ? expf(-expf(ah) * softplus_f(res[r] + bias)) : sigmoid_f(res[r]);
+  }
+}
+
 template <int WT>
 static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
   constexpr int BY = HFmt<WT>::kBytes;
@@ -152,6 +247,15 @@ static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
 }
 
 hipError_t launch_gates(const GatesParams& p, hipStream_t s) {
+  const int nbq = p.rank / 32;
+  if (p.fbw && p.wt == kQ8 && p.N > 1 && (p.rank == 32 || p.rank == 64 || p.rank == 128) &&
+      p.K % 16 == 0 && p.V % 16 == 0) {
+    const dim3 grid(((p.K + p.V) / 16 + 3) / 4, (p.N + kGmCols - 1) / kGmCols);
+    if (nbq == 1) gates_mfma_kernel<2><<<grid, 256, 0, s>>>(p);
+    else if (nbq == 2) gates_mfma_kernel<4><<<grid, 256, 0, s>>>(p);
+    else gates_mfma_kernel<8><<<grid, 256, 0, s>>>(p);
+    return hipGetLastError();
+  }
   if (p.wt == kF32)
     launch_gates_wt<kF32>(p, s);
   else if (p.wt == kBF16)

@@ -122,6 +122,12 @@ struct GatesParams {
   const float* a_log = nullptr;   // [H]
   const float* dt_bias = nullptr; // [K]
   float* out = nullptr;           // [N][K + V]: alpha | gate
+  // Q8_0 F_b / G_b in gate-tile order (made for the one-launch decode; null if none): with
+  // them, N > 1 runs on the int8 matrix cores
+  const int8_t* fbw = nullptr;
+  const uint16_t* fbd = nullptr;
+  const int8_t* gbw = nullptr;
+  const uint16_t* gbd = nullptr;
 };
 hipError_t launch_gates(const GatesParams& p, hipStream_t s);
 // Whether the per-head kernel handles these low-rank shapes (equal ranks, a power-of-two
