@@ -97,6 +97,18 @@ def test_verify_token_counts(T):
     _check(w, w.steps)
 
 
+@pytest.mark.parametrize("D,rank", [(1024, 32), (2048, 64)])
+def test_verify_low_rank_gates_matrix_cores(D, rank):
+    """Verify of a model with the one-launch copies at ranks 32 and 64: the many-column gates
+    on the matrix cores with lane groups past rank / 32 empty, 12 columns (a full and a
+    partial group of 8); D = 1024 also takes the vector projections and the separate conv."""
+    d = synth.LayerDims(d_model=D, n_heads=D // 128, d_k=128, d_v=128, rank_f=rank, rank_g=rank)
+    w = synth.scaled(synth.WORKLOADS["verify"], dims=d, n_layers=2, batch=3, steps=3,
+                     seed=80 + rank)
+    _say(f"verify D={D} rank={rank} 2 layers B=3 T=4, 3 steps")
+    _check(w, w.steps)
+
+
 def test_verify_accept_clamped():
     """Accept lengths outside 1..T are clamped: 0 commits one token, 9 commits T."""
     w = synth.scaled(synth.WORKLOADS["verify"], n_layers=1, batch=2, steps=2, seed=50)
