@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744806259,
-                "sha256": "1e5791711cdc0f3af0d2ff3e85c89a2247f2e3fd9439be51a934763efd83c5ac",
+STEP_TRAFFIC = {"bytes": 744776139,
+                "sha256": "c8b4bedc617392f4ff558be9be178bf8f6cc8ffa113c6ebe46388e5504075c35",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 

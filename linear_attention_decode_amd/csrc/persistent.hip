@@ -1,23 +1,24 @@
 // One-launch decode step for gfx950: every layer of the stack for one token (batch 1) in a
-// single cooperative launch of one block per CU.
+// single launch of one block per CU (a plain launch by default; cooperative on request).
 //
 // Per layer the blocks run three phases of the KDA step ("Where the time goes", "Thirty
-// tiny kernels per layer", frederic.ai):
-//   P  every block: RMSNorm(x) and its slice of the fused input projections
+// tiny kernels per layer", frederic.ai), each on blocks of its own:
+//   P  projection blocks: RMSNorm(x) and their rows of the fused input projections
 //      [W_q; W_k; W_v; F_a; G_a; W_beta], with the causal conv + SiLU + window roll applied
 //      by the owner of each q/k/v channel;
 //   H  two blocks per head, each owning half of its value columns: the low-rank forget gate
-//      alpha and its output-gate columns (all four waves), then the gated delta rule (one
-//      wave per 16 value columns, state in registers), posting the gated outputs and
-//      partial sums of o^2;
-//   O  a band of blocks: the heads' RMSNorm scales from those partials, the output
-//      projection of the normalised heads and the residual.
-// Every block streams a slice of every matrix, and it requests the next slice as soon as it
-// has used the current one, so the weights of layer l + 1 are in flight while layer l's
-// later phases run.  The projections run on the int8 matrix cores: the Q8_0 bytes are the B
-// operand as they are stored, and the input vector enters as three 7-bit planes per run of
-// 128 elements (exact products, integer accumulation, the Q8_0 scales applied per block
-// afterwards).
+//      alpha and its output-gate columns (F_b, G_b on the matrix cores), then the gated
+//      delta rule (one wave per 16 value columns, state in registers), posting the gated
+//      outputs and partial sums of o^2;
+//   O  output blocks, 32 rows each: the heads' RMSNorm scales from those partials, the
+//      output projection of the normalised heads and the residual.
+// Every block streams its slice of its matrices, and it requests the next layer's slice
+// soon after it has used the current one, so the weights of layer l + 1 are in flight
+// while layer l's later phases run.  All dots run on the int8 matrix cores: the weights
+// come from copies rearranged at model creation so that each load is 1 KB of consecutive
+// signed Q8_0 bytes in B-operand order, and the input vector enters as three 7-bit planes
+// under a power-of-two scale (exact products, integer accumulation, the Q8_0 scales applied
+// per block afterwards).
 //
 // Blocks hand activations to each other as 64-bit words (tag << 32 | fp32 bits) written
 // and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
@@ -608,7 +609,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const int h = blockIdx.x % H, half = blockIdx.x / H;
   float* Sl = P.S + (size_t)l * H * dk * dv;
   // the head's inputs are polled word by word from the start of the layer (32 blocks of
-  // ~2 KB a round, no flag first: the low-rank rows land early)
+  // ~4.6 KB a round, no flag first: the low-rank rows land early)
   // inputs: q [dk] | k [dk] | v [kHCols] | f_lr [rank] | g_lr [rank] | beta  (<= 3 per thread)
   constexpr int n_in = 2 * dk + kHCols + 2 * rank + 1;
   static_assert(n_in <= 3 * kPT, "head inputs");
