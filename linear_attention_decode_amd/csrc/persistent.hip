@@ -24,7 +24,7 @@
 // and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
 // the token and layer.  The head blocks poll their input words directly from the start of
 // the layer.  The head blocks post a flag word when they are done and the output blocks one
-// when they hold the heads' outputs (about a microsecond before their own words); their many
+// when they see the first head flag (1.5-2 us before their own words); their many
 // consumers watch the flags -- one wave, a short sleep between polls -- and poll the data
 // words once the first producer has flagged, so that polling stays far below the weight
 // stream.  A consumer always checks the tag of every data word it uses.  Every wait is
@@ -544,8 +544,8 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
 #pragma unroll
     for (int k = 0; k < NV; ++k) v[k] = *gp(P.x_in + run_elem(k, wave, lane));
   } else {
-    // x_l: once the first O block of layer l - 1 holds the heads' outputs (they finish
-    // together, about a microsecond later), poll the tagged words of the wave's runs
+    // x_l: once the first O block of layer l - 1 has seen a head flag (the O blocks finish
+    // together, 1.5-2 us later), poll the tagged words of the wave's runs
     uint32_t pend[3] = {0u, 0u, 0u};
     if (block_any(sm, 0, wave0_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, pend))) return false;
     bad = !poll_runs<NV>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, v, P);
@@ -835,6 +835,10 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   // their partials (lane kParts t + i: partial i of head 4 t + wave)
   uint32_t pend[3] = {0u, 0u, 0u};
   if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag, pend))) return false;
+  // this band's flag goes out now, 1.5-2 us ahead of its x words: the projection blocks
+  // then poll the words themselves, so the fetch of the fresh words is their detection too
+  // (a flag posted with the words costs a second fetch of a fresh line)
+  if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
   const bool has = lane < kParts * NT;
   const uint64_t* src = P.obuf + D + (4 * (has ? lane / kParts : 0) + wave) * kParts + lane % kParts;
   uint64_t pw = has ? peek(src) : tagged(tag, 0.0f);
@@ -848,10 +852,6 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
     }
   }
   keep_live(pend);
-  // the flag goes out now, about a microsecond ahead of this band's x words: the projection
-  // blocks then poll the words themselves, so the fetch of the fresh words is their
-  // detection too (a flag posted with the words costs a second fetch of a fresh line)
-  if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
   // the normalised heads (run t = head 4 t + wave), then their planes
   // lane kParts t ends up with head t's sum of squares; every lane computes a scale, lane
   // kParts t's is head t's
