@@ -23,11 +23,12 @@
 // Blocks hand activations to each other as 64-bit words (tag << 32 | fp32 bits) written
 // and read with agent-scope relaxed atomics (coherent across the XCDs' L2s); the tag names
 // the token and layer.  The head blocks poll their input words directly from the start of
-// the layer.  The head blocks post a flag word when they are done and the output blocks one
-// when they see the first head flag (1.5-2 us before their own words); their many
-// consumers watch the flags -- one wave, a short sleep between polls -- and poll the data
-// words once the first producer has flagged, so that polling stays far below the weight
-// stream.  A consumer always checks the tag of every data word it uses.  Every wait is
+// the layer.  The head blocks post a flag word when they are done; the output blocks and
+// the next layer's projection blocks watch those flags -- one wave, a short sleep between
+// polls -- and poll their data words (the heads' outputs, and x, which lands 1.5-2 us later)
+// once the first head block has flagged, so that polling stays far below the weight stream
+// and a fresh word's fetch is also its detection (a flag posted with its words costs a
+// second fetch of a fresh line).  A consumer always checks the tag of every data word it uses.  Every wait is
 // bounded: on a timeout the block records an error word and every block leaves the kernel.
 #include "kda_device.h"
 #include "persist.h"
@@ -118,7 +119,7 @@ __device__ __forceinline__ float rsq_hw(float x) { return __builtin_amdgcn_rsqf(
 __device__ __forceinline__ float sigmoid_hw(float z) { return __builtin_amdgcn_rcpf(1.0f + exp_hw(-z)); }
 __device__ __forceinline__ float softplus_hw(float z) { return fmaxf(z, 0.0f) + ln_hw(1.0f + exp_hw(-fabsf(z))); }
 
-enum FlagPhase { kFlagH = 1, kFlagO = 2 };
+enum FlagPhase { kFlagH = 1 };
 
 // Wall-clock ticks (100 MHz) a block holds its next-layer prefetch back after its phase, so
 // that the burst does not queue ahead of the polls its consumers issue meanwhile (timed:
@@ -544,10 +545,11 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
 #pragma unroll
     for (int k = 0; k < NV; ++k) v[k] = *gp(P.x_in + run_elem(k, wave, lane));
   } else {
-    // x_l: once the first O block of layer l - 1 has seen a head flag (the O blocks finish
-    // together, 1.5-2 us later), poll the tagged words of the wave's runs
+    // x_l: once the first head block of layer l - 1 has flagged (the O blocks post x 1.5-2 us
+    // later), poll the tagged words of the wave's runs: already polling when the fresh words
+    // land, the fetch that brings them is also their detection
     uint32_t pend[3] = {0u, 0u, 0u};
-    if (block_any(sm, 0, wave0_wait_flags(P, kFlagO, P.o_blocks, tag - 1u, pend))) return false;
+    if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag - 1u, pend))) return false;
     bad = !poll_runs<NV>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, v, P);
     keep_live(pend);
   }
@@ -835,10 +837,6 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   // their partials (lane kParts t + i: partial i of head 4 t + wave)
   uint32_t pend[3] = {0u, 0u, 0u};
   if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag, pend))) return false;
-  // this band's flag goes out now, 1.5-2 us ahead of its x words: the projection blocks
-  // then poll the words themselves, so the fetch of the fresh words is their detection too
-  // (a flag posted with the words costs a second fetch of a fresh line)
-  if (tid == 0) put(flag_slot(P, kFlagO, R.ob), tag, 0.0f);
   const bool has = lane < kParts * NT;
   const uint64_t* src = P.obuf + D + (4 * (has ? lane / kParts : 0) + wave) * kParts + lane % kParts;
   uint64_t pw = has ? peek(src) : tagged(tag, 0.0f);
