@@ -37,8 +37,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744739598,
-                "sha256": "97672790740d9749268e7bf758765a920bc239f4e7f24f6ffbaee682281ed872",
+STEP_TRAFFIC = {"bytes": 744159919,
+                "sha256": "685c397c4822eb8738ca591b53a0487e8d519491721bde9b05b09a8014007284",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 
