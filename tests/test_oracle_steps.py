@@ -391,3 +391,156 @@ def test_verify_commit_semantics():
         _, S4, Z4, _ = ok.decode_run(layers, xb, run.s0[:, b:b + 1], True)
         np.testing.assert_allclose(S3[:, b], S4[:, 0], rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(Z3[:, b], Z4[:, 0], rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------------------
+# wiring of the pre-norm, the forget gate's inputs and beta's heads
+# ----------------------------------------------------------------------------------------
+def _single_token_out(L, u):
+    """Closed form of one token from S0 = 0 and an empty window, RMSNorm eps 0 (see
+    pin_single_token): out = W_o n with n_h = sign(k_h . q_h) v_h / rms(v_h) * gate_h."""
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    K = H * dk
+    w3 = L.conv_w[:, 3]
+    sl = lambda y: y / (1 + np.exp(-y))
+    qa = sl(w3[:K] * (L.wq @ u)).reshape(H, dk)
+    ka = sl(w3[K:2 * K] * (L.wk @ u)).reshape(H, dk)
+    va = sl(w3[2 * K:] * (L.wv @ u)).reshape(H, dv)
+    gate = 1 / (1 + np.exp(-(L.gb @ (L.ga @ u)))).reshape(H, dv)
+    sgn = np.sign(np.sum(qa * ka, axis=1))
+    n = sgn[:, None] * va / np.sqrt(np.mean(va * va, axis=1, keepdims=True)) * gate
+    return L.wo @ n.reshape(-1)
+
+
+def pin_stack_prenorm(stack_fn) -> bool:
+    """One layer of the pre-norm residual stack from S0 = 0 and an empty window:
+    (a) RMSNorm makes the layer's input scale-free, so x1(10 x) - 10 x = x1(x) - x;
+    (b) x1 - x is the single-token closed form at u = x / sqrt(mean(x^2)) (the RMS of the
+    residual stream, weight ones, eps 0), which fixes the mean (not the sum) of squares."""
+    L, run = _tiny_layer(seed=11, norm_eps=0.0)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    x = run.x[0, 0, 0].astype(np.float64) * 3.0
+    S0 = [np.zeros((H, dk, dv))]
+    Z0 = [np.zeros((3, L.channels))]
+    y1, _, _ = stack_fn([L], x[None, :], S0, Z0, eps=0.0)
+    y10, _, _ = stack_fn([L], 10.0 * x[None, :], S0, Z0, eps=0.0)
+    good = np.allclose(y10[0] - 10.0 * x, y1[0] - x, rtol=1e-9, atol=1e-11)
+    u = x / np.sqrt(np.mean(x * x))
+    good &= np.allclose(y1[0] - x, _single_token_out(L, u), rtol=1e-10, atol=1e-12)
+    return bool(good)
+
+
+def test_stack_prenorm_wiring():
+    assert pin_stack_prenorm(ok.stack_step)
+
+
+def test_stack_prenorm_mutant_no_norm():
+    def mutant(layers, X, S, Z, keep_after=None, eps=1e-6):
+        X = np.array(np.atleast_2d(X), np.float64, copy=True)
+        for l, L in enumerate(layers):
+            out, _, _ = ok.layer_forward(L, X, S[l], Z[l], keep_after=keep_after)
+            X = X + out
+        return X, None, None
+    assert not pin_stack_prenorm(mutant)
+
+
+def test_stack_prenorm_mutant_l2_norm():
+    def mutant(layers, X, S, Z, keep_after=None, eps=1e-6):
+        X = np.array(np.atleast_2d(X), np.float64, copy=True)
+        for l, L in enumerate(layers):
+            h = X / np.sqrt(np.sum(X * X, axis=-1, keepdims=True) + eps)
+            out, _, _ = ok.layer_forward(L, h, S[l], Z[l], keep_after=keep_after)
+            X = X + out
+        return X, None, None
+    assert not pin_stack_prenorm(mutant)
+
+
+def pin_forget_gate_wiring(layer_fn) -> bool:
+    """F_a = 0 makes the forget-gate input f = dt_bias exactly.  Token 1 has beta = 1 and
+    token 2 = -token 1 has beta = 0 (huge beta logits of opposite signs), so from S0 = 0
+    the delta rule reduces to S1 = k1 v1^T and S2 = diag(alpha) S1 with
+    alpha_{h,i} = exp(-exp(A_log[h]) softplus(dt_bias[h dk + i])) (the workload's gate
+    formula), evaluated here with libm scalars; the A_log values of the heads differ, so a
+    head mix-up shows.  A second case with dt_bias = 0 and F_a, F_b random checks the
+    low-rank term f = F_b (F_a u) the same way."""
+    L, run = _tiny_layer(seed=12, norm_eps=0.0)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    u1 = run.x[0, 0, 0].astype(np.float64)
+    # beta logits of several thousand: rows aligned with u1 so that W_beta u1 >> 0
+    L.wbeta = np.tile(u1 / np.linalg.norm(u1), (H, 1)) * np.linspace(3e3, 5e3, H)[:, None]
+    L.a_log = np.linspace(-0.9, 0.4, H)
+    U = np.stack([u1, -u1])
+    good = True
+    for case in ("bias", "lowrank"):
+        if case == "bias":
+            L.fa = np.zeros_like(L.fa)
+        else:
+            rng = RNG(13)
+            L.fa = rng.standard_normal(L.fa.shape) * 0.2
+            L.fb = rng.standard_normal(L.fb.shape) * 0.5
+            L.dt_bias = np.zeros_like(L.dt_bias)
+        _, S1, _ = layer_fn(L, U[:1], np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+        _, S2, _ = layer_fn(L, U, np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+        f = L.dt_bias if case == "bias" else L.fb @ (L.fa @ U[1])
+        for h in range(H):
+            for i in range(dk):
+                z = float(f[h * dk + i])
+                sp = max(z, 0.0) + math.log1p(math.exp(-abs(z)))
+                a = math.exp(-math.exp(float(L.a_log[h])) * sp)
+                good &= np.allclose(S2[h, i], a * S1[h, i], rtol=1e-12, atol=1e-15)
+    return bool(good)
+
+
+def test_forget_gate_wiring():
+    assert pin_forget_gate_wiring(ok.layer_forward)
+
+
+@pytest.mark.parametrize("which", ["no_dt_bias", "a_log_heads_reversed", "fa_fb_swapped_order"])
+def test_forget_gate_wiring_mutants(which):
+    real = ok.layer_forward
+
+    def layer(L, U, S, Z, **kw):
+        kv = dict(L.__dict__)
+        if which == "no_dt_bias":
+            kv["dt_bias"] = np.zeros_like(L.dt_bias)
+        elif which == "a_log_heads_reversed":
+            kv["a_log"] = L.a_log[::-1].copy()
+        else:   # f = F_b (F_a u) with the low-rank vector reversed in between
+            kv["fb"] = L.fb[:, ::-1].copy()
+        return real(ok.OracleLayer(**kv), U, S, Z, **kw)
+    assert not pin_forget_gate_wiring(layer)
+
+
+def pin_beta_heads(layer_fn) -> bool:
+    """One token from S0 = 0 and an empty window: S_h = beta_h k_h v_h^T with
+    beta_h = sigmoid((W_beta u)_h) and k_h, v_h the head's slices of SiLU(w[:, 3] * p)
+    (k L2-normalised); the betas of the heads differ, so a row mix-up of W_beta shows."""
+    L, run = _tiny_layer(seed=14, norm_eps=0.0, l2_eps=0.0)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    K = H * dk
+    u = run.x[0, 0, 0].astype(np.float64)
+    # spread the logits so the heads' betas are far apart
+    L.wbeta = L.wbeta * np.linspace(1.0, 8.0, H)[:, None]
+    _, S, _ = layer_fn(L, u[None, :], np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+    w3 = L.conv_w[:, 3]
+    sl = lambda y: y / (1 + np.exp(-y))
+    ka = sl(w3[K:2 * K] * (L.wk @ u)).reshape(H, dk)
+    ka = ka / np.linalg.norm(ka, axis=1, keepdims=True)
+    va = sl(w3[2 * K:] * (L.wv @ u)).reshape(H, dv)
+    good = True
+    for h in range(H):
+        b = 1.0 / (1.0 + math.exp(-float(L.wbeta[h] @ u)))
+        good &= np.allclose(S[h], b * np.outer(ka[h], va[h]), rtol=1e-12, atol=1e-15)
+    return bool(good)
+
+
+def test_beta_head_mapping():
+    assert pin_beta_heads(ok.layer_forward)
+
+
+def test_beta_head_mapping_mutant_reversed_rows():
+    real = ok.layer_forward
+
+    def layer(L, U, S, Z, **kw):
+        return real(ok.OracleLayer(**{**L.__dict__, "wbeta": L.wbeta[::-1].copy()}), U, S, Z, **kw)
+    assert not pin_beta_heads(layer)
