@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -54,6 +54,21 @@ typedef enum {
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_Q8_0 = 2 } kda_dtype;
 
 typedef enum { KDA_OP_DECODE = 0, KDA_OP_VERIFY = 1, KDA_OP_PREFILL = 2 } kda_op;
+
+/* Forget-gate forms.  f is the gate input F_b F_a u + dt_bias.
+ * KDA_GATE_KDA    per key channel: alpha = exp(-exp(A_log[h]) softplus(f))   (the workload
+ *                 text's gate); F_b [H*d_k][rank_f], dt_bias [H*d_k].
+ * KDA_GATE_SAFE   per key channel, lower-bounded: alpha = exp(gate_lb sigmoid(-f a[h])),
+ *                 with the a_log array's value of head h used as given (not exponentiated)
+ *                 and gate_lb < 0, so e^gate_lb < alpha < 1 (torad-labs/llama.cpp PR #84,
+ *                 the decay-precompute commit, which writes KDA's decay as
+ *                 exp(raw_lb * sigmoid(-(g * raw_a[h]))); "Thirty tiny kernels per layer"
+ *                 lists a "safe gate" transform in the step).  Shapes as KDA_GATE_KDA.
+ * KDA_GATE_SCALAR one gate per head (the gated delta rule's scalar gate, which the chunk_kda
+ *                 commit of the same PR contrasts with KDA's per-channel gate):
+ *                 alpha_h = exp(-exp(A_log[h]) softplus(f_h)) on every key channel of head
+ *                 h; F_b [H][rank_f], dt_bias [H]. */
+typedef enum { KDA_GATE_KDA = 0, KDA_GATE_SAFE = 1, KDA_GATE_SCALAR = 2 } kda_gate;
 
 typedef struct kda_model kda_model;   /* opaque */
 
@@ -76,15 +91,28 @@ const char* kda_last_error(void);
 /* Bytes a packed [rows][cols] matrix occupies (0 on an invalid request). */
 size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols);
 
-/* Pack fp32 src_dev [rows][cols] into dst_dev (kda_packed_bytes bytes).  Errors:
- * KDA_E_DTYPE (unknown dtype), KDA_E_SHAPE (rows/cols <= 0, Q8_0 with cols % 32 != 0). */
-int kda_pack(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+/* Pack fp32 src_host [rows][cols] (host memory) into dst_dev (kda_packed_bytes bytes):
+ * the format is applied on the host, then the bytes are copied on `stream`; the call
+ * returns once the copy is complete (synchronous), so src_host may be freed at once.
+ * Errors: KDA_E_DTYPE (unknown dtype), KDA_E_SHAPE (rows/cols <= 0, Q8_0 with
+ * cols % 32 != 0), KDA_E_ALIGN (dst_dev), KDA_E_HIP. */
+int kda_pack(int dtype, const float* src_host, int64_t rows, int64_t cols, void* dst_dev,
              void* stream);
 
-/* Canonical view of a Q8_0-packed matrix: d16_dev [rows][cols/32] fp16 bit patterns and
- * qs_dev [rows][cols] int8.  Asynchronous on `stream`. */
-int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
-                    int8_t* qs_dev, void* stream);
+/* The same packing from fp32 src_dev [rows][cols] in device memory, by a kernel;
+ * asynchronous on `stream`.  Bit-identical to kda_pack. */
+int kda_pack_device(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+                    void* stream);
+
+/* Canonical view of a Q8_0-packed matrix in host memory: d16_host [rows][cols/32] fp16 bit
+ * patterns and qs_host [rows][cols] int8.  Synchronous: the packed bytes are copied back
+ * on `stream` and unpacked on the host before the call returns. */
+int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_host,
+                    int8_t* qs_host, void* stream);
+
+/* The same view written to device memory (d16_dev, qs_dev), asynchronous on `stream`. */
+int kda_unpack_q8_0_device(const void* packed_dev, int64_t rows, int64_t cols,
+                           uint16_t* d16_dev, int8_t* qs_dev, void* stream);
 
 /* ------------------------------------------------------------------------------------
  * Model description.  The library keeps the pointers; it does not copy weights.
@@ -102,16 +130,19 @@ typedef struct {
   float norm_eps;            /* RMSNorm eps (pre-norm and output norm) */
   float l2_eps;              /* q/k L2-norm eps: x / sqrt(sum x^2 + l2_eps) */
   int32_t wtype;             /* kda_dtype of every projection matrix */
+  int32_t gate;              /* kda_gate: forget-gate form (0 = KDA) */
+  float gate_lb;             /* KDA_GATE_SAFE: lower bound of log(alpha), < 0 (else unused) */
 } kda_dims;
 
 typedef struct {
   /* packed by kda_pack with dims.wtype; shapes [out][in]:
    * wq, wk: [H*d_k][D]  wv: [H*d_v][D]  wo: [D][H*d_v]  fa: [rank_f][D]
-   * fb: [H*d_k][rank_f]  wbeta: [H][D]  ga: [rank_g][D]  gb: [H*d_v][rank_g] */
+   * fb: [H*d_k][rank_f] ([H][rank_f] for KDA_GATE_SCALAR)  wbeta: [H][D]
+   * ga: [rank_g][D]  gb: [H*d_v][rank_g] */
   const void *wq, *wk, *wv, *wo, *fa, *fb, *wbeta, *ga, *gb;
   const float* conv_w;    /* [C][conv_k] fp32, C = 2*H*d_k + H*d_v; tap conv_k-1 = current */
-  const float* a_log;     /* [H] */
-  const float* dt_bias;   /* [H*d_k] */
+  const float* a_log;     /* [H] (KDA_GATE_SAFE: the per-head factor a, used as given) */
+  const float* dt_bias;   /* [H*d_k] ([H] for KDA_GATE_SCALAR) */
   const float* o_norm_w;  /* [d_v] or NULL (ones) */
 } kda_layer;
 
@@ -164,7 +195,14 @@ int kda_model_query(const kda_model* m, int what);
 
 /* Synchronises the device and reports whether a one-launch decode since the last call hit
  * its bounded wait between blocks (KDA_E_HIP; that step's outputs and state are invalid
- * and the exchange buffers are reset).  KDA_OK otherwise. */
+ * and the exchange buffers are reset).  KDA_OK otherwise.
+ * Such a step leaves its error word set until this call: the one-launch kernel leaves at
+ * once, touching nothing, in every step enqueued after the failed one, and once the host
+ * can see the word (after the failed step has completed, e.g. at the caller's next
+ * synchronisation) kda_decode_step, kda_verify_steps, kda_verify_commit,
+ * kda_prefill_chunked and kda_conv_window_canonical refuse with KDA_E_HIP and enqueue
+ * nothing.  A caller must therefore call kda_model_status after such a refusal (and should
+ * before trusting a state after a step that ran with a short KDA_OPT_WAIT_US). */
 int kda_model_status(kda_model* m);
 
 /* Kernel kinds reported by kda_timing_query. */
@@ -187,6 +225,21 @@ size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t to
 int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
                     void* ws_dev, size_t ws_bytes, void* stream);
 
+/* Batched decode with ragged or left-padded sequences ("Thirty tiny kernels per layer",
+ * section "Taking it upstream, and finding out why it's worth less there": a left-padded
+ * batch mask and ragged per-row lengths).  active_dev: device int32 [B]; a sequence with
+ * active_dev[b] == 0 takes no token this step: its state and conv window are left exactly
+ * as they were (bit for bit), and its y_dev row is the layer (stack) output its x_dev row
+ * would have had (computed from the unchanged state; callers normally ignore it).  A
+ * sequence with a nonzero entry is decoded exactly as by kda_decode_step.  Left padding is
+ * a mask that is 0 until a sequence's first token, ragged lengths one that is 0 after its
+ * last.  Runs the per-layer kernels (never the one-launch kernel), replayed as a hipGraph
+ * keyed also on active_dev.  Errors as kda_decode_step, KDA_E_ARG for a null mask and
+ * KDA_E_ALIGN for a mask that is not 4-byte aligned. */
+int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                           const int32_t* active_dev, void* ws_dev, size_t ws_bytes,
+                           void* stream);
+
 /* Verify (multi-token, read-only on the state): T tokens per sequence, x_dev [B][T][D],
  * run in order through every layer from the state in st, which is NOT modified.  Writes
  * y_dev [B][T][D] for every token and a replay log (kda_verify_log_bytes) that
@@ -198,10 +251,21 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
                      const kda_state* st, void* log_dev, size_t log_bytes, void* ws_dev,
                      size_t ws_bytes, void* stream);
 /* Commit: advance st to the state and conv window reached after accept_dev[b] tokens
- * (device int32 [B], each in 1..T; values outside are clamped to that range) of the
- * last kda_verify_steps on this log.  The result equals decoding those tokens. */
-int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, int32_t T,
-                      const int32_t* accept_dev, void* stream);
+ * (device int32 [B], each in 1..T) of the last kda_verify_steps on this log.  The result
+ * equals decoding those tokens.  log_bytes is the size of log_dev; it must hold a verify of
+ * st->batch sequences and T tokens (kda_verify_log_bytes), else KDA_E_WORKSPACE.  The
+ * accept lengths are device data, which the host cannot read without a synchronisation:
+ * the kernel clamps a value outside 1..T to that range. */
+int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
+                      int32_t T, const int32_t* accept_dev, void* stream);
+
+/* The conv windows of every layer and sequence in the canonical layout
+ * out_dev [n_layers][B][conv_k - 1][C] fp32, oldest token first (the "conv_state" of the
+ * pure decode step in "Thirty tiny kernels per layer", section "Why mx.compile fits here
+ * and not elsewhere").  Asynchronous device-to-device copy on `stream`; st is not
+ * modified. */
+int kda_conv_window_canonical(const kda_model* m, const kda_state* st, float* out_dev,
+                              void* stream);
 
 /* Chunked prefill of L tokens per sequence through a single-layer model (n_layers == 1,
  * prenorm_residual == 0): x_dev [B][L][D] (x_dtype KDA_BF16 bit patterns or KDA_F32),

@@ -2,7 +2,8 @@
 
 The functions named ``kda_*`` mirror the C ABI of include/kda.h one to one and take
 torch CUDA tensors (device memory) plus an optional torch stream; ``KdaModel`` packs a
-layer stack's fp32 weights on the device with ``kda_pack`` and owns the packed buffers.
+layer stack's fp32 weights on the device with ``kda_pack_device`` and owns the packed
+buffers.
 PyTorch provides device memory and streams only; every step of the decode / verify /
 prefill path runs in the library's HIP kernels (libkda.so).  Importing this package
 does not load the library; the first call does, and fails loudly if it is missing.
@@ -16,7 +17,8 @@ from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
                    KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, KDA_K_GEMM, KDA_K_CHUNK,
-                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError)
+                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError,
+                   KDA_GATE_KDA, KDA_GATE_SAFE, KDA_GATE_SCALAR, GATES)
 
 _PROJ_NAMES = ("wq", "wk", "wv", "wo", "fa", "fb", "wbeta", "ga", "gb")
 
@@ -55,20 +57,41 @@ def kda_packed_bytes(dtype: int, rows: int, cols: int) -> int:
 
 
 def kda_pack(dtype: int, src, dst, stream=None) -> None:
+    """src: host fp32 [rows][cols] (numpy array or CPU tensor); dst: cuda uint8 tensor of
+    kda_packed_bytes bytes.  Synchronous."""
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(src, dtype=np.float32))
+    rows, cols = a.shape
+    assert dst.numel() * dst.element_size() >= kda_packed_bytes(dtype, rows, cols)
+    _lib.call("kda_pack", dtype, a.ctypes.data_as(C.c_void_p), rows, cols, _p(dst), _s(stream))
+
+
+def kda_pack_device(dtype: int, src, dst, stream=None) -> None:
     """src: cuda fp32 [rows][cols]; dst: cuda uint8 tensor of kda_packed_bytes bytes."""
     rows, cols = src.shape
     _dev_f32(src)
     assert dst.numel() * dst.element_size() >= kda_packed_bytes(dtype, rows, cols)
-    _lib.call("kda_pack", dtype, _p(src), rows, cols, _p(dst), _s(stream))
+    _lib.call("kda_pack_device", dtype, _p(src), rows, cols, _p(dst), _s(stream))
 
 
 def kda_unpack_q8_0(packed, rows: int, cols: int, stream=None):
-    """Canonical view of a Q8_0-packed matrix: (d16 bits as int16 [rows][cols/32],
-    q as int8 [rows][cols]) on the device."""
+    """Canonical view of a Q8_0-packed matrix in host memory: (d16 bits as uint16 numpy
+    [rows][cols/32], q as int8 numpy [rows][cols]).  Synchronous."""
+    import numpy as np
+    d16 = np.empty((rows, cols // 32), dtype=np.uint16)
+    qs = np.empty((rows, cols), dtype=np.int8)
+    _lib.call("kda_unpack_q8_0", _p(packed), rows, cols, d16.ctypes.data_as(C.c_void_p),
+              qs.ctypes.data_as(C.c_void_p), _s(stream))
+    return d16, qs
+
+
+def kda_unpack_q8_0_device(packed, rows: int, cols: int, stream=None):
+    """The same view on the device: (d16 bits as int16 [rows][cols/32], q as int8
+    [rows][cols]) cuda tensors, asynchronous on the stream."""
     torch = _torch()
     d16 = torch.empty((rows, cols // 32), dtype=torch.int16, device=packed.device)
     qs = torch.empty((rows, cols), dtype=torch.int8, device=packed.device)
-    _lib.call("kda_unpack_q8_0", _p(packed), rows, cols, _p(d16), _p(qs), _s(stream))
+    _lib.call("kda_unpack_q8_0_device", _p(packed), rows, cols, _p(d16), _p(qs), _s(stream))
     return d16, qs
 
 
@@ -119,6 +142,13 @@ def kda_decode_step(handle, x, y, st, ws, stream=None) -> None:
     _lib.call("kda_decode_step", handle, _p(x), _p(y), C.byref(s), _p(ws), ws.numel(), _s(stream))
 
 
+def kda_decode_step_masked(handle, x, y, st, active, ws, stream=None) -> None:
+    """active: cuda int32 [B]; 0 = this sequence takes no token (state and window kept)."""
+    s = _state(st)
+    _lib.call("kda_decode_step_masked", handle, _p(x), _p(y), C.byref(s), _p(active), _p(ws),
+              ws.numel(), _s(stream))
+
+
 def kda_verify_steps(handle, x, T: int, y, st, log, ws, stream=None) -> None:
     s = _state(st)
     _lib.call("kda_verify_steps", handle, _p(x), T, _p(y), C.byref(s), _p(log), log.numel(),
@@ -127,7 +157,14 @@ def kda_verify_steps(handle, x, T: int, y, st, log, ws, stream=None) -> None:
 
 def kda_verify_commit(handle, st, log, T: int, accept, stream=None) -> None:
     s = _state(st)
-    _lib.call("kda_verify_commit", handle, C.byref(s), _p(log), T, _p(accept), _s(stream))
+    _lib.call("kda_verify_commit", handle, C.byref(s), _p(log), log.numel() * log.element_size(),
+              T, _p(accept), _s(stream))
+
+
+def kda_conv_window_canonical(handle, st, out, stream=None) -> None:
+    """out: cuda fp32 [n_layers][B][conv_k - 1][C], oldest token first."""
+    s = _state(st)
+    _lib.call("kda_conv_window_canonical", handle, C.byref(s), _p(out), _s(stream))
 
 
 def kda_prefill_chunked(handle, x, x_dtype: int, L: int, chunk: int, y, st, ws, stream=None) -> None:
@@ -160,11 +197,12 @@ class KdaStateBuf:
 
 class KdaModel:
     """Packs fp32 per-layer parameter draws (dicts with the keys of include/kda.h's
-    kda_layer) into device buffers with kda_pack and creates the library model."""
+    kda_layer) into device buffers with kda_pack_device and creates the library model."""
 
     def __init__(self, layers: Sequence[Dict], *, n_heads: int, d_k: int, d_v: int,
                  wtype: str, prenorm_residual: bool, norm_eps: float = 1e-6,
-                 l2_eps: float = 1e-6, device="cuda", stream=None):
+                 l2_eps: float = 1e-6, gate: str = "kda", gate_lb: float = -5.0,
+                 device="cuda", stream=None):
         torch = _torch()
         self.device = torch.device(device)
         self.wtype = DTYPES[wtype]
@@ -175,7 +213,8 @@ class KdaModel:
         self.n_layers = len(layers)
         self.channels = 2 * n_heads * d_k + n_heads * d_v
         self.dims = _lib.KdaDims(self.d_model, n_heads, d_k, d_v, 4, self.rank_f, self.rank_g,
-                                 self.n_layers, int(prenorm_residual), norm_eps, l2_eps, self.wtype)
+                                 self.n_layers, int(prenorm_residual), norm_eps, l2_eps, self.wtype,
+                                 GATES[gate], gate_lb)
         self._keep: List = []
         self._packed: Dict = {}
         c_layers = []
@@ -187,7 +226,7 @@ class KdaModel:
                 if nb == 0:
                     raise ValueError(f"{name}: shape {tuple(w.shape)} cannot be packed as {wtype}")
                 buf = torch.empty(nb, dtype=torch.uint8, device=self.device)
-                kda_pack(self.wtype, w, buf, stream)
+                kda_pack_device(self.wtype, w, buf, stream)
                 self._keep.append(buf)
                 self._packed[(li, name)] = buf
                 ptrs[name] = buf.data_ptr()
@@ -236,11 +275,22 @@ class KdaModel:
     def decode_step(self, x, y, st: KdaStateBuf, ws, stream=None) -> None:
         kda_decode_step(self.handle, x, y, st, ws, stream)
 
+    def decode_step_masked(self, x, y, st: KdaStateBuf, active, ws, stream=None) -> None:
+        kda_decode_step_masked(self.handle, x, y, st, active, ws, stream)
+
     def verify_steps(self, x, T: int, y, st: KdaStateBuf, log, ws, stream=None) -> None:
         kda_verify_steps(self.handle, x, T, y, st, log, ws, stream)
 
     def verify_commit(self, st: KdaStateBuf, log, T: int, accept, stream=None) -> None:
         kda_verify_commit(self.handle, st, log, T, accept, stream)
+
+    def conv_window(self, st: KdaStateBuf, stream=None):
+        """The canonical conv windows [n_layers][B][3][C] (oldest first) as a new tensor."""
+        torch = _torch()
+        out = torch.empty((self.n_layers, st.batch, 3, self.channels), dtype=torch.float32,
+                          device=self.device)
+        kda_conv_window_canonical(self.handle, st, out, stream)
+        return out
 
     def verify_log(self, batch: int, T: int):
         torch = _torch()

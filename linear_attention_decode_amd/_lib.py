@@ -18,13 +18,15 @@ KDA_Q_PERSISTENT = 0
 KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, \
     KDA_K_GEMM, KDA_K_CHUNK = range(9)
 DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0}
+KDA_GATE_KDA, KDA_GATE_SAFE, KDA_GATE_SCALAR = 0, 1, 2
+GATES = {"kda": KDA_GATE_KDA, "safe": KDA_GATE_SAFE, "scalar": KDA_GATE_SCALAR}
 
 EXPORTS = (
     "kda_abi_version", "kda_status_string", "kda_last_error", "kda_packed_bytes", "kda_pack",
-    "kda_unpack_q8_0", "kda_model_create", "kda_model_destroy", "kda_model_set_option",
+    "kda_pack_device", "kda_unpack_q8_0", "kda_unpack_q8_0_device", "kda_model_create", "kda_model_destroy", "kda_model_set_option",
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
-    "kda_model_status",
+    "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
 )
 
 
@@ -33,7 +35,8 @@ class KdaDims(C.Structure):
                 ("d_v", C.c_int32), ("conv_k", C.c_int32), ("rank_f", C.c_int32),
                 ("rank_g", C.c_int32), ("n_layers", C.c_int32),
                 ("prenorm_residual", C.c_int32), ("norm_eps", C.c_float),
-                ("l2_eps", C.c_float), ("wtype", C.c_int32)]
+                ("l2_eps", C.c_float), ("wtype", C.c_int32), ("gate", C.c_int32),
+                ("gate_lb", C.c_float)]
 
 
 class KdaLayer(C.Structure):
@@ -68,7 +71,9 @@ def lib():
             "kda_last_error": (C.c_char_p, []),
             "kda_packed_bytes": (sz, [C.c_int, i64, i64]),
             "kda_pack": (C.c_int, [C.c_int, vp, i64, i64, vp, vp]),
+            "kda_pack_device": (C.c_int, [C.c_int, vp, i64, i64, vp, vp]),
             "kda_unpack_q8_0": (C.c_int, [vp, i64, i64, vp, vp, vp]),
+            "kda_unpack_q8_0_device": (C.c_int, [vp, i64, i64, vp, vp, vp]),
             "kda_model_create": (C.c_int, [C.POINTER(KdaDims), C.POINTER(KdaLayer), C.POINTER(vp)]),
             "kda_model_destroy": (None, [vp]),
             "kda_model_set_option": (C.c_int, [vp, C.c_int, i64]),
@@ -77,9 +82,11 @@ def lib():
             "kda_timing_query": (C.c_int, [vp, C.c_int, C.POINTER(C.c_double), C.POINTER(i64), C.c_int]),
             "kda_workspace_bytes": (sz, [vp, C.c_int, i32, i64]),
             "kda_decode_step": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, sz, vp]),
+            "kda_decode_step_masked": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, vp, sz, vp]),
             "kda_verify_log_bytes": (sz, [vp, i32, i32]),
             "kda_verify_steps": (C.c_int, [vp, vp, i32, vp, C.POINTER(KdaState), vp, sz, vp, sz, vp]),
-            "kda_verify_commit": (C.c_int, [vp, C.POINTER(KdaState), vp, i32, vp, vp]),
+            "kda_verify_commit": (C.c_int, [vp, C.POINTER(KdaState), vp, sz, i32, vp, vp]),
+            "kda_conv_window_canonical": (C.c_int, [vp, C.POINTER(KdaState), vp, vp]),
             "kda_prefill_chunked": (C.c_int, [vp, vp, C.c_int, i64, i32, vp, C.POINTER(KdaState), vp, sz, vp]),
         }
         for name, (res, args) in sig.items():

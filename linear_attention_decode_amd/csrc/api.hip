@@ -60,11 +60,12 @@ struct GraphKey {
   float* S = nullptr;
   float* conv = nullptr;
   void* ws = nullptr;
+  const int* active = nullptr;
   int batch = 0;
   hipStream_t stream = nullptr;
   bool operator==(const GraphKey& o) const {
     return x == o.x && y == o.y && S == o.S && conv == o.conv && ws == o.ws &&
-           batch == o.batch && stream == o.stream;
+           active == o.active && batch == o.batch && stream == o.stream;
   }
 };
 
@@ -95,6 +96,7 @@ struct kda_model {
   int8_t* mma_w = nullptr;          // projection rows and W_o of every layer, matrix-core order
   uint64_t* xchg = nullptr;         // exchange words (xbuf | pbuf | gbuf | obuf)
   int* err = nullptr;
+  int* err_host = nullptr;          // host-mapped: set by a step whose wait between blocks ran out
   uint32_t epoch = 0;
   PersistParams pp;
   // timing
@@ -228,6 +230,7 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
   gp.N = N; gp.K = m->Kq; gp.V = m->V; gp.dk = d.d_k; gp.rank = d.rank_f; gp.C = m->C;
   gp.wt = d.wtype; gp.proj = proj; gp.proj_stride = m->proj_stride;
   gp.fb = L.fb; gp.gb = L.gb; gp.a_log = L.a_log; gp.dt_bias = L.dt_bias; gp.out = ag;
+  gp.gate = d.gate; gp.gate_lb = d.gate_lb;
   gp.fbw = L.fbw; gp.fbd = L.fbd; gp.gbw = L.gbw; gp.gbd = L.gbd;
   return timed(m, KDA_K_GATES, s, rec, [&] { return launch_gates(gp, s); });
 }
@@ -238,7 +241,8 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
 // projection epilogue and rolls the window there.
 int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
                   float* S, float* win, float* proj, float* ag, float* act, const WsLayout& wl,
-                  char* ws, bool write_state, hipStream_t s, bool rec) {
+                  char* ws, bool write_state, hipStream_t s, bool rec,
+                  const int* active = nullptr) {
   const kda_dims& d = m->d;
   const LayerDev& L = m->layers[l];
   const int N = B * T;
@@ -262,6 +266,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   pp.conv_w = L.conv_w;
   pp.win = win;
   pp.C = m->C;
+  pp.active = active;
   if (conv_fused) {
     pp.act = act;
     pp.T = T;
@@ -295,6 +300,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   hp.ntok = nullptr; hp.write_out = 1;
   hp.o = o; hp.gate = gate; hp.ss = ss;
   hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
+  hp.active = active;
   r = timed(m, KDA_K_HEAD, s, rec, [&] { return launch_head(hp, s); });
   if (r) return r;
 
@@ -323,10 +329,10 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
 size_t state_layer_stride(const kda_model* m, int B) {
   return (size_t)B * m->d.n_heads * m->d.d_k * m->d.d_v;
 }
-size_t win_layer_stride(const kda_model* m, int B) { return (size_t)B * 3 * m->C; }
+size_t win_layer_stride(const kda_model* m, int B) { return (size_t)B * (m->d.conv_k - 1) * m->C; }
 
 int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, char* ws,
-                   hipStream_t s, bool rec) {
+                   hipStream_t s, bool rec, const int* active = nullptr) {
   const int B = st->batch;
   WsLayout wl = ws_layout(m, B);
   float* proj = reinterpret_cast<float*>(ws + wl.proj);
@@ -335,7 +341,7 @@ int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, 
     const float* xin = (l == 0 || !m->d.prenorm_residual) ? x : y;
     int r = enqueue_layer(m, l, xin, y, B, 1, st->S_dev + l * state_layer_stride(m, B),
                           st->conv_dev + l * win_layer_stride(m, B), proj, ag, nullptr, wl, ws,
-                          true, s, rec);
+                          true, s, rec, active);
     if (r) return r;
   }
   return KDA_OK;
@@ -383,6 +389,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const int ob0 = 2 * d.n_heads, nob = d.d_model / 32;
   const int rank = d.rank_f;
   bool ok = nb > 0 && nb <= kMaxPersistBlocks && d.wtype == KDA_Q8_0 && d.prenorm_residual &&
+            d.gate == KDA_GATE_KDA &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
             (rank == 32 || rank == 64 || rank == 128);
@@ -456,6 +463,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   e = hipMemset(m->err, 0, 256);
   if (e != hipSuccess) return e;
+  e = hipHostMalloc((void**)&m->err_host, 256, hipHostMallocDefault);
+  if (e != hipSuccess) return e;
+  *(volatile int*)m->err_host = 0;
   e = hipDeviceSynchronize();
   if (e != hipSuccess) return e;
   PersistParams& p = m->pp;
@@ -468,6 +478,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   p.layers = m->d_layers;
   p.xbuf = m->xchg; p.pbuf = p.xbuf + nx; p.obuf = p.pbuf + np; p.flags = p.obuf + no;
   p.err = m->err;
+  p.err_host = m->err_host;
   int dev = 0, khz = 0;
   e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
@@ -493,8 +504,59 @@ int reset_exchange(kda_model* m) {
   KDA_HIP(hipMemset(m->xchg, 0, exchange_words(m) * sizeof(uint64_t)));
   KDA_HIP(hipMemset(m->err, 0, 256));
   KDA_HIP(hipDeviceSynchronize());
+  *(volatile int*)m->err_host = 0;
   m->epoch = 0;
   return KDA_OK;
+}
+
+// A one-launch step whose wait between blocks ran out left the caller's state partly
+// advanced; until kda_model_status has reported it, every call that reads or writes a state
+// on this model is refused (the kernel itself also leaves at once while the device word is
+// set, for steps enqueued before the host saw it).
+int check_poison(const kda_model* m) {
+  if (m->err_host && *(volatile const int*)m->err_host)
+    return fail(KDA_E_HIP, "an earlier one-launch decode step on this model timed out in a wait "
+                "between blocks; its state is invalid: call kda_model_status to reset the model");
+  return KDA_OK;
+}
+
+// ---- host-side packing (kda_pack from host memory), the same rules as the device kernels
+void host_pack_bf16(const float* src, uint16_t* dst, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t b;
+    std::memcpy(&b, src + i, 4);
+    if ((b & 0x7fffffffu) > 0x7f800000u) dst[i] = (uint16_t)((b >> 16) | 0x40u);
+    else dst[i] = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+  }
+}
+
+// Q8_0 per block of 32: amax, d = fp32(amax / 127), d16 = fp16 round-to-nearest-even of d,
+// q = clamp(round-half-away(fp32(x / d16)), -127, 127), all q = 0 when d16 == 0; stored as
+// q + 128 with the scale plane at q8_scale_offset.
+void host_pack_q8_0(const float* src, int64_t rows, int64_t cols, uint8_t* dst) {
+  const int64_t nb = cols / 32;
+  uint16_t* dplane = reinterpret_cast<uint16_t*>(dst + q8_scale_offset(rows, cols));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < nb; ++j) {
+      const float* x = src + r * cols + j * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) amax = std::fmax(amax, std::fabs(x[i]));
+      const volatile float d = amax / 127.0f;
+      const _Float16 h = (_Float16)d;
+      const float dq = (float)h;
+      uint8_t* q = dst + r * cols + j * 32;
+      for (int i = 0; i < 32; ++i) {
+        float t = 0.0f;
+        if (dq != 0.0f) {
+          const volatile float ratio = x[i] / dq;
+          t = std::fmin(std::fmax(std::round(ratio), -127.0f), 127.0f);
+        }
+        q[i] = (uint8_t)((int)t + 128);
+      }
+      uint16_t bits;
+      std::memcpy(&bits, &h, 2);
+      dplane[r * nb + j] = bits;
+    }
 }
 
 }  // namespace
@@ -532,8 +594,26 @@ size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols) {
   }
 }
 
-int kda_pack(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+int kda_pack(int dtype, const float* src_host, int64_t rows, int64_t cols, void* dst_dev,
              void* stream) {
+  if (dtype < KDA_F32 || dtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
+  if (!src_host || !dst_dev) return fail(KDA_E_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0) return fail(KDA_E_SHAPE, "rows/cols must be positive");
+  if (dtype == KDA_Q8_0 && cols % 32) return fail(KDA_E_SHAPE, "Q8_0 needs cols %% 32 == 0");
+  if (!aligned16(dst_dev)) return fail(KDA_E_ALIGN, "dst_dev must be 16-byte aligned");
+  const size_t bytes = kda_packed_bytes(dtype, rows, cols);
+  std::vector<uint8_t> buf(bytes, 0);
+  if (dtype == KDA_F32) std::memcpy(buf.data(), src_host, (size_t)rows * cols * 4);
+  else if (dtype == KDA_BF16) host_pack_bf16(src_host, reinterpret_cast<uint16_t*>(buf.data()), rows * cols);
+  else host_pack_q8_0(src_host, rows, cols, buf.data());
+  hipStream_t s = (hipStream_t)stream;
+  KDA_HIP(hipMemcpyAsync(dst_dev, buf.data(), bytes, hipMemcpyHostToDevice, s));
+  KDA_HIP(hipStreamSynchronize(s));
+  return KDA_OK;
+}
+
+int kda_pack_device(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
+                    void* stream) {
   if (dtype < KDA_F32 || dtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
   if (!src_dev || !dst_dev) return fail(KDA_E_ARG, "null pointer");
   if (rows <= 0 || cols <= 0) return fail(KDA_E_SHAPE, "rows/cols must be positive");
@@ -543,8 +623,23 @@ int kda_pack(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* 
   return KDA_OK;
 }
 
-int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
-                    int8_t* qs_dev, void* stream) {
+int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_host,
+                    int8_t* qs_host, void* stream) {
+  if (!packed_dev || !d16_host || !qs_host) return fail(KDA_E_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0 || cols % 32) return fail(KDA_E_SHAPE, "bad Q8_0 shape");
+  const size_t bytes = kda_packed_bytes(KDA_Q8_0, rows, cols);
+  std::vector<uint8_t> buf(bytes);
+  hipStream_t s = (hipStream_t)stream;
+  KDA_HIP(hipMemcpyAsync(buf.data(), packed_dev, bytes, hipMemcpyDeviceToHost, s));
+  KDA_HIP(hipStreamSynchronize(s));
+  const size_t n = (size_t)rows * cols;
+  for (size_t i = 0; i < n; ++i) qs_host[i] = (int8_t)((int)buf[i] - 128);
+  std::memcpy(d16_host, buf.data() + q8_scale_offset(rows, cols), n / 32 * 2);
+  return KDA_OK;
+}
+
+int kda_unpack_q8_0_device(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
+                           int8_t* qs_dev, void* stream) {
   if (!packed_dev || !d16_dev || !qs_dev) return fail(KDA_E_ARG, "null pointer");
   if (rows <= 0 || cols <= 0 || cols % 32) return fail(KDA_E_SHAPE, "bad Q8_0 shape");
   KDA_HIP(launch_unpack_q8(packed_dev, rows, cols, d16_dev, qs_dev, (hipStream_t)stream));
@@ -573,6 +668,9 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
     return fail(KDA_E_SHAPE, "low ranks %d/%d unsupported for this weight type (need rank_f == rank_g, "
                 "a power-of-two count of 16-byte chunks per row)", d.rank_f, d.rank_g);
   if (!(d.norm_eps >= 0.f) || !(d.l2_eps >= 0.f)) return fail(KDA_E_ARG, "eps must be >= 0");
+  if (d.gate < KDA_GATE_KDA || d.gate > KDA_GATE_SCALAR) return fail(KDA_E_ARG, "unknown gate form %d", d.gate);
+  if (d.gate == KDA_GATE_SAFE && !(d.gate_lb < 0.f && d.gate_lb > -1e30f))
+    return fail(KDA_E_ARG, "the safe gate needs a finite gate_lb < 0");
   kda_model* m = new kda_model();
   m->d = d;
   m->Kq = d.n_heads * d.d_k;
@@ -596,7 +694,7 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
     L.wv = packed_view(s.wv, d.wtype, m->V, D);
     L.wo = packed_view(s.wo, d.wtype, D, m->V);
     L.fa = packed_view(s.fa, d.wtype, d.rank_f, D);
-    L.fb = packed_view(s.fb, d.wtype, m->Kq, d.rank_f);
+    L.fb = packed_view(s.fb, d.wtype, d.gate == KDA_GATE_SCALAR ? d.n_heads : m->Kq, d.rank_f);
     L.wbeta = packed_view(s.wbeta, d.wtype, d.n_heads, D);
     L.ga = packed_view(s.ga, d.wtype, d.rank_g, D);
     L.gb = packed_view(s.gb, d.wtype, m->V, d.rank_g);
@@ -623,6 +721,7 @@ void kda_model_destroy(kda_model* m) {
   if (m->mma_w) (void)hipFree(m->mma_w);
   if (m->xchg) (void)hipFree(m->xchg);
   if (m->err) (void)hipFree(m->err);
+  if (m->err_host) (void)hipHostFree(m->err_host);
   for (auto& t : m->pool) {
     (void)hipEventDestroy(t.a);
     (void)hipEventDestroy(t.b);
@@ -661,7 +760,7 @@ int kda_model_status(kda_model* m) {
   if (!m->pers_ok) return KDA_OK;
   int err = 0;
   KDA_HIP(hipMemcpy(&err, m->err, sizeof(int), hipMemcpyDeviceToHost));
-  if (err) {
+  if (err || *(volatile int*)m->err_host) {
     int r = reset_exchange(m);
     if (r) return r;
     return fail(KDA_E_HIP, "one-launch decode: a wait between blocks timed out; outputs of "
@@ -698,17 +797,26 @@ size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t to
   return 0;
 }
 
-int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
-                    void* ws_dev, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// One decode token for every sequence; `active` (device [B] or null) masks sequences whose
+// state and window stay as they are.  A masked step never takes the one-launch kernel.
+int decode_impl(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                const int32_t* active, void* ws_dev, size_t ws_bytes, void* stream) {
   if (!m || !x_dev || !y_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
   int r = check_state(m, st);
   if (r) return r;
   if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(ws_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  if (active && ((uintptr_t)active & 3u)) return fail(KDA_E_ALIGN, "active mask not 4-byte aligned");
   if (ws_bytes < ws_layout(m, st->batch).total)
     return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, ws_layout(m, st->batch).total);
+  r = check_poison(m);
+  if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
-  if (m->use_persist && m->pers_ok && st->batch == 1) {
+  if (!active && m->use_persist && m->pers_ok && st->batch == 1) {
     if (m->epoch >= 0x7fffffffu / (uint32_t)m->d.n_layers) {
       r = reset_exchange(m);
       if (r) return r;
@@ -718,16 +826,17 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
     p.epoch = ++m->epoch;
     return timed(m, KDA_K_STEP, s, m->timing, [&] { return launch_persistent(p, m->pers_blocks, m->coop, s); });
   }
-  if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing);
+  if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing, active);
 
   GraphKey k;
   k.x = x_dev; k.y = y_dev; k.S = st->S_dev; k.conv = st->conv_dev; k.ws = ws_dev;
+  k.active = active;
   k.batch = st->batch; k.stream = s;
   if (!m->exec || !(k == m->key)) {
     drop_graph(m);
     hipGraph_t g = nullptr;
     KDA_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
-    r = enqueue_decode(m, x_dev, y_dev, st, ws, m->cap_stream, false);
+    r = enqueue_decode(m, x_dev, y_dev, st, ws, m->cap_stream, false, active);
     hipError_t e = hipStreamEndCapture(m->cap_stream, &g);
     if (r) { if (g) (void)hipGraphDestroy(g); return r; }
     if (e != hipSuccess) return fail(KDA_E_HIP, "graph capture: %s", hipGetErrorString(e));
@@ -738,6 +847,22 @@ int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_st
   }
   KDA_HIP(hipGraphLaunch(m->exec, s));
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                    void* ws_dev, size_t ws_bytes, void* stream) {
+  return decode_impl(m, x_dev, y_dev, st, nullptr, ws_dev, ws_bytes, stream);
+}
+
+int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                           const int32_t* active_dev, void* ws_dev, size_t ws_bytes,
+                           void* stream) {
+  if (!active_dev) return fail(KDA_E_ARG, "null active mask");
+  return decode_impl(m, x_dev, y_dev, st, active_dev, ws_dev, ws_bytes, stream);
 }
 
 size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T) {
@@ -758,6 +883,8 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   if (log_bytes < kda_verify_log_bytes(m, B, T)) return fail(KDA_E_WORKSPACE, "log buffer too small");
   WsLayout wl = ws_layout(m, (int64_t)B * T);
   if (ws_bytes < wl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, wl.total);
+  r = check_poison(m);
+  if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
   float* logf = static_cast<float*>(log_dev);
@@ -776,13 +903,19 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   return KDA_OK;
 }
 
-int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, int32_t T,
-                      const int32_t* accept_dev, void* stream) {
+int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
+                      int32_t T, const int32_t* accept_dev, void* stream) {
   if (!m || !log_dev || !accept_dev) return fail(KDA_E_ARG, "null pointer");
   int r = check_state(m, st);
   if (r) return r;
   if (T < 1 || T > 8) return fail(KDA_E_SHAPE, "T must be in 1..8");
   const int B = st->batch;
+  if (log_bytes < kda_verify_log_bytes(m, B, T))
+    return fail(KDA_E_WORKSPACE, "log of %zu bytes is smaller than a verify of B=%d, T=%d writes (%zu)",
+                log_bytes, B, T, kda_verify_log_bytes(m, B, T));
+  if (!aligned16(log_dev) || ((uintptr_t)accept_dev & 3u)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  r = check_poison(m);
+  if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   const kda_dims& d = m->d;
   const float* logf = static_cast<const float*>(log_dev);
@@ -811,6 +944,21 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, in
   return KDA_OK;
 }
 
+int kda_conv_window_canonical(const kda_model* m, const kda_state* st, float* out_dev,
+                              void* stream) {
+  if (!m || !out_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  if (!aligned16(out_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  r = check_poison(m);
+  if (r) return r;
+  // the device window is already [n_layers][B][conv_k - 1][C], oldest token first
+  const size_t n = (size_t)m->d.n_layers * win_layer_stride(m, st->batch);
+  KDA_HIP(hipMemcpyAsync(out_dev, st->conv_dev, n * sizeof(float), hipMemcpyDeviceToDevice,
+                         (hipStream_t)stream));
+  return KDA_OK;
+}
+
 int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
                         int32_t chunk, float* y_dev, const kda_state* st, void* ws_dev,
                         size_t ws_bytes, void* stream) {
@@ -831,6 +979,8 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   const int B = st->batch;
   const PfLayout wl = pf_layout(m, B, L);
   if (ws_bytes < wl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, wl.total);
+  r = check_poison(m);
+  if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
   const LayerDev& Ly = m->layers[0];
@@ -873,6 +1023,7 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   p.win = st->conv_dev; p.win_out = st->conv_dev;
   p.conv_w = Ly.conv_w; p.a_log = Ly.a_log; p.dt_bias = Ly.dt_bias; p.onw = Ly.o_norm_w;
   p.Fb = reinterpret_cast<const uint16_t*>(Ly.fb.w);
+  p.gate = d.gate; p.gate_lb = d.gate_lb;
   p.Gb = reinterpret_cast<const uint16_t*>(Ly.gb.w);
   p.l2_eps = d.l2_eps; p.q_scale = m->q_scale; p.norm_eps = d.norm_eps;
   p.Wf = F(wl.W); p.Uf = F(wl.U); p.Qf = F(wl.Qt); p.Kf = F(wl.Kt); p.Af = F(wl.A); p.dec = F(wl.dec);

@@ -300,9 +300,11 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
           const float4 w = ep_w[r];
           float* z = P.win + (size_t)n * 3 * P.C + c;
           const float y = w.x * ep_z[r][0] + w.y * ep_z[r][1] + w.z * ep_z[r][2] + w.w * v;
-          z[0] = ep_z[r][1];
-          z[P.C] = ep_z[r][2];
-          z[2 * P.C] = v;
+          if (!P.active || P.active[n]) {
+            z[0] = ep_z[r][1];
+            z[P.C] = ep_z[r][2];
+            z[2 * P.C] = v;
+          }
           v = silu_f(y);
         }
         const size_t o = (size_t)n * P.out_stride + sg.out_off + row;

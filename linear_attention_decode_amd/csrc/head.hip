@@ -53,10 +53,19 @@ __device__ __forceinline__ float hchunk_dot(const uint4 w, const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------
-// Gates: alpha = exp(-exp(A_log[h]) softplus(F_b f_lr + dt_bias)) per key channel and
-// gate = sigmoid(G_b g_lr) per value channel, for N tokens.  Rows of F_b (then G_b) are
+// Gates: alpha from f = F_b f_lr + dt_bias per key channel (per head for the scalar gate)
+// and gate = sigmoid(G_b g_lr) per value channel, for N tokens.  Rows of F_b (then G_b) are
 // split into 16-byte chunks; a row's CPR chunks sit in adjacent lanes and reduce by DPP.
+// The forget-gate forms:
+//   KDA      alpha = exp(-exp(A_log[h]) softplus(f))              (per key channel)
+//   safe     alpha = exp(lb sigmoid(-f a[h])), a[h] as given      (per key channel)
+//   scalar   alpha = exp(-exp(A_log[h]) softplus(f_h))            (per head, on all channels)
 // ---------------------------------------------------------------------------------------
+__device__ __forceinline__ float forget_alpha_f(int gate, float f, float ah, float lb) {
+  if (gate == kGateSafe) return expf(lb * sigmoid_f(-f * ah));
+  return expf(-expf(ah) * softplus_f(f));
+}
+
 constexpr int kGateThreads = 256;
 constexpr int kMaxRank = 256;
 constexpr int kGateCols = 16;    // columns staged per round (a multiple of every CPR)
@@ -67,22 +76,25 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
   constexpr int BY = HFmt<WT>::kBytes;
   __shared__ __align__(16) float s_lr[kGateCols][2 * kMaxRank];
   const int tid = threadIdx.x;
-  const int rows = P.K + P.V;
+  // forget rows (one per key channel, or one per head for the scalar gate), then gate rows
+  const bool scalar = P.gate == kGateScalar;
+  const int FR = scalar ? P.K / P.dk : P.K;
+  const int rows = FR + P.V, ostride = P.K + P.V;
   const int it = blockIdx.x * kGateThreads + tid;
   const int row = it / CPR, c = it - row * CPR;
   const bool valid = row < rows;
-  const bool f = row < P.K;
+  const bool f = row < FR;
   const int rank = P.rank;
   uint4 w = make_uint4(0, 0, 0, 0);
   float sc = 1.0f, bias = 0.0f, ah = 0.0f;
   if (valid) {
     const PackedMat M = f ? P.fb : P.gb;
-    const int r = f ? row : row - P.K;
+    const int r = f ? row : row - FR;
     w = *reinterpret_cast<const uint4*>(M.w + ((size_t)r * rank + (size_t)c * EL) * BY);
     if constexpr (WT == kQ8) sc = __half2float(M.d[(size_t)r * (rank / 32) + (c >> 1)]);
     if (f) {
       bias = P.dt_bias[row];
-      ah = P.a_log[row / P.dk];
+      ah = P.a_log[scalar ? row : row / P.dk];
     }
   }
   // kGateCols columns' low-rank inputs per round (the rounds are spread over blockIdx.y),
@@ -127,9 +139,18 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
         if (c == g) mine = part;
       }
       const int nn = nb + c;
-      if (valid && nn < nc)
-        P.out[(size_t)(n0 + nn) * rows + row] =
-            f ? expf(-expf(ah) * softplus_f(mine + bias)) : sigmoid_f(mine);
+      if (valid && nn < nc) {
+        float* orow = P.out + (size_t)(n0 + nn) * ostride;
+        if (!f) {
+          orow[P.K + row - FR] = sigmoid_f(mine);
+        } else {
+          const float a = forget_alpha_f(P.gate, mine + bias, ah, P.gate_lb);
+          if (scalar)
+            for (int i = 0; i < P.dk; ++i) orow[row * P.dk + i] = a;
+          else
+            orow[row] = a;
+        }
+      }
     }
     __syncthreads();
   }
@@ -234,7 +255,7 @@ template <int WT>
 static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
   constexpr int BY = HFmt<WT>::kBytes;
   const int cpr = p.rank * BY / 16;
-  const int items = (p.K + p.V) * cpr;
+  const int items = ((p.gate == kGateScalar ? p.K / p.dk : p.K) + p.V) * cpr;
   const dim3 grid((items + kGateThreads - 1) / kGateThreads,
                   std::min(8, (p.N + kGateCols - 1) / kGateCols));
   switch (cpr) {
@@ -248,7 +269,7 @@ static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
 
 hipError_t launch_gates(const GatesParams& p, hipStream_t s) {
   const int nbq = p.rank / 32;
-  if (p.fbw && p.wt == kQ8 && p.N > 1 && (p.rank == 32 || p.rank == 64 || p.rank == 128) &&
+  if (p.fbw && p.gate == kGateKda && p.wt == kQ8 && p.N > 1 && (p.rank == 32 || p.rank == 64 || p.rank == 128) &&
       p.K % 16 == 0 && p.V % 16 == 0) {
     const dim3 grid(((p.K + p.V) / 16 + 3) / 4, (p.N + kGmCols - 1) / kGmCols);
     if (nbq == 1) gates_mfma_kernel<2><<<grid, 256, 0, s>>>(p);
@@ -390,7 +411,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     }
   }
 
-  if (P.write_state) {
+  if (P.write_state && (!P.active || P.active[b])) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];

@@ -10,6 +10,7 @@
 namespace kda {
 
 enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2 };
+enum GateForm { kGateKda = 0, kGateSafe = 1, kGateScalar = 2 };
 
 // A packed weight matrix as the kernels see it.
 
@@ -69,6 +70,8 @@ struct GemvParams {
   const float* conv_w = nullptr;  // [C][4]
   float* win = nullptr;           // [N][3][C]
   int C = 0;
+  const int* active = nullptr;    // [N] or null: a column n with active[n] == 0 leaves its
+                                  // window as it is (its outputs are still computed)
   // verify conv epilogue (launch_skinny only): columns n = b T + t; act[n][c] = SiLU of the
   // conv over sequence b's window and its tokens 0..t, the window left as it is
   float* act = nullptr;           // [N][C]
@@ -110,17 +113,22 @@ struct HeadParams {
   // commit only: the layer's conv window [B][3][C], rolled by the accepted tokens' logged
   // pre-conv projections (proj) once the replay is done (null: left alone)
   float* win_commit = nullptr;
+  // [B] or null: a sequence with active[b] == 0 keeps its state (its outputs are still
+  // computed from it)
+  const int* active = nullptr;
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
 
 struct GatesParams {
   int N = 0, K = 0, V = 0, dk = 0, rank = 0, C = 0, wt = 0;
+  int gate = 0;                   // forget-gate form (kGateKda / kGateSafe / kGateScalar)
+  float gate_lb = 0.f;            // safe gate: lower bound of log(alpha)
   const float* proj = nullptr;    // [N][proj_stride]: f_lr at C, g_lr at C + rank
   int proj_stride = 0;
   PackedMat fb, gb;               // [K][rank], [V][rank]
   const float* a_log = nullptr;   // [H]
-  const float* dt_bias = nullptr; // [K]
+  const float* dt_bias = nullptr; // [K] ([H] for the scalar gate)
   float* out = nullptr;           // [N][K + V]: alpha | gate
   // Q8_0 F_b / G_b in gate-tile order (made for the one-launch decode; null if none): with
   // them, N > 1 runs on the int8 matrix cores
@@ -175,7 +183,10 @@ struct PrefillParams {
   const float* a_log = nullptr;
   const float* dt_bias = nullptr;
   const float* onw = nullptr;     // [dv] or null
-  const uint16_t* Fb = nullptr;   // forget-gate up-projection, BF16 [H*dk][rank_f]
+  const uint16_t* Fb = nullptr;   // forget-gate up-projection, BF16 [H*dk][rank_f] ([H][rank_f]
+                                  // for the scalar gate)
+  int gate = 0;                   // forget-gate form
+  float gate_lb = 0.f;
   const uint16_t* Gb = nullptr;   // output-gate up-projection, BF16 [H*dv][rank_g]
   float l2_eps = 0.f, q_scale = 0.f, norm_eps = 0.f;
   // per-chunk preparation outputs, per (b, h, chunk), in matrix-core operand order: -W,

@@ -47,7 +47,10 @@ struct PersistParams {
   uint64_t* pbuf = nullptr;              // [proj_rows] tagged projections
   uint64_t* obuf = nullptr;              // [V] tagged normalised, gated head outputs
   uint64_t* flags = nullptr;             // [3][kMaxPersistBlocks] tagged producer flags
-  int* err = nullptr;                    // nonzero after a wait timed out
+  int* err = nullptr;                    // nonzero after a wait timed out (device word, kept
+                                         // until the host resets it)
+  int* err_host = nullptr;               // host-mapped copy of err: the host refuses further
+                                         // steps on the model once it reads nonzero
   uint64_t timeout = 0;                  // wall-clock ticks a wait may take
   int poll_rounds = 48;                  // flag-poll rounds between two looks at the clock
   uint32_t epoch = 0;                    // token counter (tags = epoch * n_layers + layer + 1)

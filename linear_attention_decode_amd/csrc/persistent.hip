@@ -85,6 +85,12 @@ __device__ __forceinline__ uint64_t peek(const uint64_t* p) {
 __device__ __forceinline__ int err_set(const PersistParams& P) {
   return __hip_atomic_load(gpw(P.err), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Records a failed wait: the device word every block checks, and the host-mapped word the
+// host checks before it launches another step on this model.
+__device__ __forceinline__ void err_raise(const PersistParams& P) {
+  __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (P.err_host) __hip_atomic_store(P.err_host, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left free): every vector memory access issued so
 // far has completed.  Used before a store whose completion later waits must not include:
@@ -103,7 +109,7 @@ struct Spin {
     if ((++n & 31) != 0) return false;
     if (err_set(P)) return true;
     if (wall_clock64() - t0 > P.timeout) {
-      __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      err_raise(P);
       return true;
     }
     return false;
@@ -202,11 +208,16 @@ __device__ int wave0_wait_flags(const PersistParams& P, int phase, int n, uint32
     const int lane = threadIdx.x;
     const uint32_t* f = reinterpret_cast<const uint32_t*>(flag_slot(P, phase, lane < n ? lane : 0)) + 1;
     const uint64_t t0 = wall_clock64();
-    // (no read of the error word here: its load would make the code after the wait retire
-    // the polls still in flight)
+    // (the error word is read only after a round of polls that found nothing, when no poll
+    // is in flight: a load issued among them would make the code after the wait retire the
+    // polls still in flight)
     while (!poll_tag3(f, tag, P.poll_rounds, pend[0], pend[1], pend[2])) {
+      if (err_set(P)) {
+        bad = 1;
+        break;
+      }
       if (wall_clock64() - t0 > P.timeout) {
-        __hip_atomic_store(gpw(P.err), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        err_raise(P);
         bad = 1;
         break;
       }
@@ -892,7 +903,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
 // that is followed by a long wait, never just before a poll on the critical path (a poll's
 // load completes only after the loads issued before it).
 template <int U, int CPR, int ROLE>
-__device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
+__device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm, int err0) {
   GLayer* Lt = (GLayer*)P.layers;
   const Roles R = make_roles(P);
   const uint32_t tag0 = P.epoch * (uint32_t)P.n_layers;
@@ -901,6 +912,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
     sm.gpl[3 * 256 + tid] = 0;   // the zero plane of the gate inputs
     HeadRegs<CPR> hr;
     issue_head<CPR>(P, Lt[0], P.S, blockIdx.x % P.H, blockIdx.x / P.H, hr);
+    if (__builtin_amdgcn_readfirstlane(err0)) return;
     for (int l = 0; l < P.n_layers; ++l)
       if (!phase_h<CPR>(P, sm, l, tag0 + (uint32_t)l + 1u, hr)) return;
     return;
@@ -911,6 +923,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
   if constexpr (ROLE == 2) {
     OutRegs<U> orr;
     issue_out<U>(Lt[0], R.ob, orr);
+    if (__builtin_amdgcn_readfirstlane(err0)) return;
     if (tid < 16 * kOTiles) sm.xres[tid] = *gp(P.x_in + R.or0 + tid);
     for (int l = 0; l < P.n_layers; ++l) {
       if (!phase_o<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, orr)) return;
@@ -926,6 +939,7 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm) {
     if (R.p1 <= R.p0) return;
     ProjRegs<U> pr;
     issue_proj<U>(P, Lt[0], P.win, R.p0, R.p1, pr);
+    if (__builtin_amdgcn_readfirstlane(err0)) return;
     for (int l = 0; l < P.n_layers; ++l)
       if (!phase_p<U>(P, sm, R, l, tag0 + (uint32_t)l + 1u, pr)) return;
   }
@@ -936,9 +950,13 @@ template <int U, int CPR>
 __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const PersistParams P) {
   __shared__ Smem sm;
   const int b = blockIdx.x;
-  if (b < kHSplit * P.H) run_role<U, CPR, 1>(P, sm);
-  else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm);
-  else run_role<U, CPR, 0>(P, sm);
+  // a model whose earlier step failed a wait keeps its error word until the host resets it:
+  // every block then leaves before it touches the state, the window or the output (the
+  // word is requested first and looked at after the block's first weight requests)
+  const int err0 = err_set(P);
+  if (b < kHSplit * P.H) run_role<U, CPR, 1>(P, sm, err0);
+  else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm, err0);
+  else run_role<U, CPR, 0>(P, sm, err0);
 }
 
 // One thread per 16-byte chunk of the matrix-core order (persist.h): chunk

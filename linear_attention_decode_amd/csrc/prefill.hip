@@ -148,7 +148,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int ks = 0; ks < RF / 32; ++ks) {
       const int i = 16 * (wave * NTW + n) + r16;
-      fbf[n][ks] = *reinterpret_cast<const u32x4_t*>(P.Fb + ((size_t)h * DK + i) * RF + 32 * ks + 8 * q4);
+      // (the scalar gate has one F_b row per head: every channel of the head reads it)
+      const size_t frow = P.gate == kGateScalar ? (size_t)h : (size_t)h * DK + i;
+      fbf[n][ks] = *reinterpret_cast<const u32x4_t*>(P.Fb + frow * RF + 32 * ks + 8 * q4);
     }
   // ---- causal conv + SiLU of the chunk's q and k channels: an item is 4 channels x 8 rows
   //      (11 input rows); rows past the sequence end are zero ----
@@ -197,7 +199,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   lds_barrier();
   // ---- forget gate: f = F_b f_lr on the matrix cores (f_lr fp32 split, F_b exact BF16),
-  //      then the per-channel log2 decay -exp(a_log) softplus(f + dt_bias) log2(e) ----
+  //      then the per-channel log2 decay: -exp(a_log) softplus(f + dt_bias) log2(e) (KDA,
+  //      and the scalar gate with one f per head), lb sigmoid(-(f + dt_bias) a) log2(e)
+  //      (the lower-bounded gate, a = a_log as given) ----
   {
     f32x4_t acc[4][NTW];
 #pragma unroll
@@ -218,17 +222,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) acc[mt][n] = mma2(fa[mt], fbf[n][ks], acc[mt][n]);
     }
-    const float ea = fexp(P.a_log[h]);
+    const bool safe = P.gate == kGateSafe;
+    const float ea = safe ? P.a_log[h] : fexp(P.a_log[h]);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
       const int i = 16 * (wave * NTW + n) + r16;
-      const float bias = P.dt_bias[h * DK + i];
+      const float bias = P.dt_bias[P.gate == kGateScalar ? h : h * DK + i];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * mt + 4 * q4 + r;
-          sG[t * RS + i] = t < nt ? (-ea * fsoftplus(acc[mt][n][r] + bias)) * kLog2e : 0.0f;
+          const float z = acc[mt][n][r] + bias;
+          const float lg = safe ? P.gate_lb * fsigmoid(-z * ea) : -ea * fsoftplus(z);
+          sG[t * RS + i] = t < nt ? lg * kLog2e : 0.0f;
         }
     }
   }

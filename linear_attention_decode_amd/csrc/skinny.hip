@@ -181,6 +181,7 @@ struct SkParams {
   int C = 0;
   float* act = nullptr;
   int T = 0;
+  const int* active = nullptr;
 };
 
 // 8 weight bytes u -> 8 fp16 values 1024 + u (byte permutes against 0x64 high bytes)
@@ -334,9 +335,11 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
       float* z = P.win + (size_t)n * 3 * P.C + c;
       const float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
       const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * v;
-      z[0] = z1;
-      z[P.C] = z2;
-      z[2 * P.C] = v;
+      if (!P.active || P.active[n]) {
+        z[0] = z1;
+        z[P.C] = z2;
+        z[2 * P.C] = v;
+      }
       v = silu_f(y);
     }
     const size_t o = (size_t)n * P.out_stride + sg.out_off + grow;
@@ -390,6 +393,7 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.C = g.C;
   p.act = g.act;
   p.T = g.T;
+  p.active = g.active;
   const int KG = g.K / 2048;
   if (prologue == kProX) {
     if (KG == 2) skinny_prep_kernel<kProX, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);

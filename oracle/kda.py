@@ -102,6 +102,57 @@ def q8_0_dequantize(d16: np.ndarray, q: np.ndarray) -> np.ndarray:
     return (d * q.astype(np.float64).reshape(rows, cols // 32, 32)).reshape(rows, cols)
 
 
+# The E2M1 element grid of MXFP4 (non-negative half; sign separate): exponent bits e and
+# mantissa bit m give 0.5 m for e = 0 and 2^(e-1) (1 + m/2) otherwise.
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mxfp4_quantize(w32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """MXFP4 quantisation of a [rows][cols] fp32 matrix, cols % 32 == 0.
+
+    MXFP4 is one of the block formats the quant-format commit of torad-labs/llama.cpp PR
+    #84 ranks at the KDA projection shapes; its definition is the OCP Microscaling (MX)
+    format specification v1.0: blocks of 32 consecutive values along a row share one
+    E8M0 scale X = 2^s, s = floor(log2(max|x|)) - 2 (2 = the exponent of E2M1's largest
+    normal), clamped to [-127, 127]; each element is the E2M1 value nearest to x / X, ties
+    to the even mantissa bit, clamped to +-6 (the largest E2M1 value).  A block of zeros
+    takes s = -127 and zero elements.
+    Returns (e8m0 = s + 127 as uint8 [rows][cols/32], codes as uint8 [rows][cols] with
+    code = sign << 3 | index into E2M1_GRID).
+    Pins: values on the grid times X come back exactly; |x - q| <= X/4 below 4 X, <= X
+    between 4 X and 6 X (the grid's spacing halves), and the saturation of (6 X, 8 X);
+    hand-worked ties."""
+    x = np.ascontiguousarray(w32, dtype=np.float32).astype(np.float64)
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError("MXFP4 needs cols % 32 == 0")
+    blocks = x.reshape(rows, cols // 32, 32)
+    amax = np.max(np.abs(blocks), axis=-1)
+    _, ex = np.frexp(amax)                       # amax = m 2^ex, m in [0.5, 1)
+    s = np.where(amax > 0, ex - 1 - 2, -127)
+    s = np.clip(s, -127, 127)
+    v = blocks / np.exp2(s)[..., None]           # exact: a power-of-two scale
+    a = np.minimum(np.abs(v), 6.0)
+    # nearest grid point; on a tie the even index (mantissa bit 0): E2M1_GRID index i has
+    # mantissa bit i & 1
+    d = np.abs(a[..., None] - E2M1_GRID)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    odd = (np.arange(8) & 1) == 1
+    idx = np.where(cand & ~odd, np.arange(8), 99).min(axis=-1)
+    idx = np.where(idx == 99, np.argmax(cand, axis=-1), idx)
+    sign = (v < 0) & (idx > 0)
+    codes = (sign.astype(np.uint8) << 3) | idx.astype(np.uint8)
+    return (s + 127).astype(np.uint8), codes.reshape(rows, cols)
+
+
+def mxfp4_dequantize(e8m0: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    rows, cols = codes.shape
+    mag = E2M1_GRID[codes & 7]
+    val = np.where(codes & 8, -mag, mag).reshape(rows, cols // 32, 32)
+    return (val * np.exp2(e8m0.astype(np.float64) - 127.0)[..., None]).reshape(rows, cols)
+
+
 PROJECTIONS = ("wq", "wk", "wv", "wo", "fa", "fb", "wbeta", "ga", "gb")
 
 
@@ -128,6 +179,8 @@ class OracleLayer:
     o_norm_w: np.ndarray   # [dv]
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
+    gate: str = "kda"      # forget-gate form: kda | safe | scalar (see forget_alpha)
+    gate_lb: float = -5.0  # lower bound of log(alpha) of the safe gate
 
     @property
     def channels(self) -> int:
@@ -135,8 +188,9 @@ class OracleLayer:
 
 
 def prepare_layer(draws: Dict[str, np.ndarray], wtype: str, n_heads: int, d_k: int,
-                  d_v: int, norm_eps: float = 1e-6, l2_eps: float = 1e-6) -> OracleLayer:
-    """Apply the projection weight format (f32 | bf16 | q8_0) to fp32 draws."""
+                  d_v: int, norm_eps: float = 1e-6, l2_eps: float = 1e-6, gate: str = "kda",
+                  gate_lb: float = -5.0) -> OracleLayer:
+    """Apply the projection weight format (f32 | bf16 | q8_0 | mxfp4) to fp32 draws."""
     def fmt(w):
         if wtype == "f32":
             return np.asarray(w, np.float32).astype(np.float64)
@@ -144,6 +198,8 @@ def prepare_layer(draws: Dict[str, np.ndarray], wtype: str, n_heads: int, d_k: i
             return bf16_round(w)
         if wtype == "q8_0":
             return q8_0_dequantize(*q8_0_quantize(w))
+        if wtype == "mxfp4":
+            return mxfp4_dequantize(*mxfp4_quantize(w))
         raise ValueError(wtype)
 
     mats = {k: fmt(draws[k]) for k in PROJECTIONS}
@@ -155,7 +211,7 @@ def prepare_layer(draws: Dict[str, np.ndarray], wtype: str, n_heads: int, d_k: i
         a_log=draws["a_log"].astype(np.float64),
         dt_bias=draws["dt_bias"].astype(np.float64),
         o_norm_w=np.ones(d_v, np.float64),
-        norm_eps=norm_eps, l2_eps=l2_eps, **mats)
+        norm_eps=norm_eps, l2_eps=l2_eps, gate=gate, gate_lb=gate_lb, **mats)
 
 
 # ---------------------------------------------------------------------------------------
@@ -213,6 +269,39 @@ def forget_gate(f: np.ndarray, a_log: np.ndarray) -> np.ndarray:
     return np.exp(-np.exp(a_log)[:, None] * softplus(f))
 
 
+def safe_gate(f: np.ndarray, a: np.ndarray, lb: float) -> np.ndarray:
+    """The lower-bounded ("safe") forget gate: alpha = exp(lb * sigmoid(-f * a[h])) per key
+    channel, with a per-head factor a used as given and lb < 0, so log(alpha) lies in
+    (lb, 0)  (torad-labs/llama.cpp PR #84, the decay-precompute commit, which writes the KDA
+    decay as exp(raw_lb * sigmoid(-(g * raw_a[h]))); "Thirty tiny kernels per layer" lists
+    the "safe gate" transform among the step's parts).  f: [H][dk].
+    Pins: f = 0 gives exp(lb / 2); the bounds e^lb < alpha < 1; a closed form per head."""
+    return np.exp(lb * sigmoid(-f * a[:, None]))
+
+
+def scalar_gate(f: np.ndarray, a_log: np.ndarray, dk: int) -> np.ndarray:
+    """The gated delta rule's scalar gate: one alpha per head,
+    alpha_h = exp(-exp(A_log[h]) * softplus(f_h)), applied to every key channel of the head
+    (the chunk_kda commit of torad-labs/llama.cpp PR #84 contrasts it with KDA's gate "one
+    per key channel").  f: [H].  Returns [H][dk].
+    Pins: constant along a head's channels; softplus(0) = ln 2 closed form; layer wiring."""
+    a = np.exp(-np.exp(a_log) * softplus(f))
+    return np.repeat(a[:, None], dk, axis=1)
+
+
+def forget_alpha(L: "OracleLayer", f: np.ndarray) -> np.ndarray:
+    """alpha [H][dk] of one token from the forget-gate input f = F_b F_a u + dt_bias
+    ([H*dk], or [H] for the scalar gate) in the layer's gate form."""
+    H, dk = L.n_heads, L.d_k
+    if L.gate == "kda":
+        return forget_gate(f.reshape(H, dk), L.a_log)
+    if L.gate == "safe":
+        return safe_gate(f.reshape(H, dk), L.a_log, L.gate_lb)
+    if L.gate == "scalar":
+        return scalar_gate(f.reshape(H), L.a_log, dk)
+    raise ValueError(L.gate)
+
+
 def delta_rule_step(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
                     alpha: np.ndarray, beta: np.ndarray):
     """Gated delta rule for every head.  S: [H][dk][dv] (row = key channel), q, k, alpha:
@@ -255,7 +344,7 @@ def layer_forward(L: OracleLayer, U: np.ndarray, S: np.ndarray, Z: np.ndarray,
     # q, k, v projections, concatenated q | k | v
     P = np.concatenate([U @ L.wq.T, U @ L.wk.T, U @ L.wv.T], axis=1)    # [T][C]
     # forget-gate input, beta, output gate
-    F = (U @ L.fa.T) @ L.fb.T + L.dt_bias                                # [T][H*dk]
+    F = (U @ L.fa.T) @ L.fb.T + L.dt_bias                   # [T][H*dk] (scalar gate: [T][H])
     Bt = sigmoid(U @ L.wbeta.T)                                         # [T][H]
     G = sigmoid((U @ L.ga.T) @ L.gb.T)                                  # [T][H*dv]
 
@@ -266,7 +355,7 @@ def layer_forward(L: OracleLayer, U: np.ndarray, S: np.ndarray, Z: np.ndarray,
     for t in range(T):
         a, Z = conv_silu(Z, P[t], L.conv_w)
         q, k, v = split_heads(a, H, dk, dv, L.l2_eps)
-        alpha = forget_gate(F[t].reshape(H, dk), L.a_log)
+        alpha = forget_alpha(L, F[t])
         S, o = delta_rule_step(S, q, k, v, alpha, Bt[t])
         n = gated_norm(o, G[t].reshape(H, dv), L.o_norm_w, L.norm_eps)
         N[t] = n.reshape(-1)

@@ -43,6 +43,9 @@ class LayerDims:
     rank_f: int
     rank_g: int
     conv_k: int = 4
+    # forget-gate form: "kda" (per key channel), "safe" (per key channel, lower-bounded),
+    # "scalar" (one gate per head: F_b is [H][rank_f] and dt_bias [H])
+    gate: str = "kda"
 
     @property
     def key_dim(self) -> int:
@@ -59,13 +62,14 @@ class LayerDims:
     def shapes(self) -> Dict[str, tuple]:
         """[out][in] row-major shapes of every per-layer parameter."""
         D, K, V = self.d_model, self.key_dim, self.value_dim
+        FR = self.n_heads if self.gate == "scalar" else K     # forget-gate rows
         return {
             "wq": (K, D), "wk": (K, D), "wv": (V, D), "wo": (D, V),
-            "fa": (self.rank_f, D), "fb": (K, self.rank_f),
+            "fa": (self.rank_f, D), "fb": (FR, self.rank_f),
             "wbeta": (self.n_heads, D),
             "ga": (self.rank_g, D), "gb": (V, self.rank_g),
             "conv_w": (self.conv_channels, self.conv_k),
-            "a_log": (self.n_heads,), "dt_bias": (K,),
+            "a_log": (self.n_heads,), "dt_bias": (FR,),
         }
 
 
@@ -97,6 +101,7 @@ class Workload:
     chunk: int = 0        # prefill chunk size
     norm_eps: float = 1e-6
     l2_eps: float = 1e-6
+    gate_lb: float = -5.0  # lower bound of log(alpha) for the "safe" gate form
 
 
 def _tiny() -> Workload:

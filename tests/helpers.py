@@ -28,7 +28,8 @@ def range_rel(y, ref) -> float:
 def oracle_layers(run: synth.RunInputs):
     w = run.workload
     d = w.dims
-    return [ok.prepare_layer(dr, w.wtype, d.n_heads, d.d_k, d.d_v, w.norm_eps, w.l2_eps)
+    return [ok.prepare_layer(dr, w.wtype, d.n_heads, d.d_k, d.d_v, w.norm_eps, w.l2_eps,
+                             gate=d.gate, gate_lb=w.gate_lb)
             for dr in run.layers]
 
 
@@ -38,7 +39,7 @@ def gpu_model(run: synth.RunInputs):
     d = w.dims
     return kda.KdaModel(run.layers, n_heads=d.n_heads, d_k=d.d_k, d_v=d.d_v, wtype=w.wtype,
                         prenorm_residual=w.prenorm_residual, norm_eps=w.norm_eps,
-                        l2_eps=w.l2_eps)
+                        l2_eps=w.l2_eps, gate=d.gate, gate_lb=w.gate_lb)
 
 
 def gpu_decode(model, run: synth.RunInputs, steps: int, snapshot_every: int = 0,

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2
 
 
 def test_packed_bytes(L):
@@ -51,17 +51,30 @@ def test_packed_bytes(L):
 def test_pack_validates_before_launch(L):
     from linear_attention_decode_amd import _lib
     p = C.c_void_p(4096)
-    assert L.kda_pack(9, p, 2, 32, p, None) == _lib.KDA_E_DTYPE
-    assert L.kda_pack(_lib.KDA_Q8_0, p, 2, 40, p, None) == _lib.KDA_E_SHAPE
-    assert L.kda_pack(_lib.KDA_F32, None, 2, 4, p, None) == _lib.KDA_E_ARG
-    assert L.kda_pack(_lib.KDA_F32, C.c_void_p(4100), 2, 4, p, None) == _lib.KDA_E_ALIGN
-    assert b"aligned" in L.kda_last_error()
+    for fn in (L.kda_pack, L.kda_pack_device):
+        assert fn(9, p, 2, 32, p, None) == _lib.KDA_E_DTYPE
+        assert fn(_lib.KDA_Q8_0, p, 2, 40, p, None) == _lib.KDA_E_SHAPE
+        assert fn(_lib.KDA_F32, None, 2, 4, p, None) == _lib.KDA_E_ARG
+        assert fn(_lib.KDA_F32, p, 2, 4, C.c_void_p(4100), None) == _lib.KDA_E_ALIGN
+        assert b"aligned" in L.kda_last_error()
+    # the device source must be aligned too; the host source need not be
+    assert L.kda_pack_device(_lib.KDA_F32, C.c_void_p(4100), 2, 4, p, None) == _lib.KDA_E_ALIGN
+
+
+def test_unpack_validates_before_copy(L):
+    from linear_attention_decode_amd import _lib
+    p = C.c_void_p(4096)
+    for fn in (L.kda_unpack_q8_0, L.kda_unpack_q8_0_device):
+        assert fn(None, 2, 32, p, p, None) == _lib.KDA_E_ARG
+        assert fn(p, 2, 40, p, p, None) == _lib.KDA_E_SHAPE
+        assert fn(p, 0, 32, p, p, None) == _lib.KDA_E_SHAPE
 
 
 def _dims(**kw):
     from linear_attention_decode_amd import _lib
     base = dict(d_model=256, n_heads=2, d_k=64, d_v=64, conv_k=4, rank_f=32, rank_g=32,
-                n_layers=1, prenorm_residual=0, norm_eps=1e-6, l2_eps=1e-6, wtype=_lib.KDA_Q8_0)
+                n_layers=1, prenorm_residual=0, norm_eps=1e-6, l2_eps=1e-6, wtype=_lib.KDA_Q8_0,
+                gate=0, gate_lb=-5.0)
     base.update(kw)
     return _lib.KdaDims(**base)
 
@@ -69,6 +82,7 @@ def _dims(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(d_k=96, d_v=96), 2), (dict(d_v=128), 2), (dict(conv_k=3), 2),
     (dict(rank_f=16), 2), (dict(d_model=250), 2), (dict(wtype=5), 4), (dict(n_layers=0), 2),
+    (dict(gate=3), 1), (dict(gate=1, gate_lb=0.0), 1), (dict(gate=1, gate_lb=float("nan")), 1),
 ])
 def test_model_create_rejects_bad_dims(L, kw, status):
     from linear_attention_decode_amd import _lib

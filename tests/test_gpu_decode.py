@@ -41,13 +41,25 @@ def test_pack_q8_0_bit_exact(torch, shape):
         w[-1, 32:64] *= 1e4                            # a large-scale block
         w[-1, 33] = 0.5 * float(np.float32(w[-1, 32:64].__abs__().max()))
     src = torch.from_numpy(w).cuda()
-    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_Q8_0, *shape), dtype=torch.uint8, device="cuda")
-    kda.kda_pack(kda.KDA_Q8_0, src, buf)
-    d16, qs = kda.kda_unpack_q8_0(buf, *shape)
+    nb = kda.kda_packed_bytes(kda.KDA_Q8_0, *shape)
+    buf = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    kda.kda_pack_device(kda.KDA_Q8_0, src, buf)
+    d16, qs = kda.kda_unpack_q8_0_device(buf, *shape)
     torch.cuda.synchronize()
     rd16, rq = ok.q8_0_quantize(w)
     np.testing.assert_array_equal(d16.cpu().numpy().view(np.uint16), rd16.view(np.uint16))
     np.testing.assert_array_equal(qs.cpu().numpy(), rq)
+    # the host-source pack and the host-side canonical view: the same bytes
+    buf2 = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    kda.kda_pack(kda.KDA_Q8_0, w, buf2)
+    hd16, hqs = kda.kda_unpack_q8_0(buf2, *shape)
+    np.testing.assert_array_equal(hd16, rd16.view(np.uint16))
+    np.testing.assert_array_equal(hqs, rq)
+    # the two byte planes (the padding between them is not written by the device kernel)
+    n, so = shape[0] * shape[1], -(-shape[0] * shape[1] // 256) * 256
+    a, b = buf2.cpu().numpy(), buf.cpu().numpy()
+    np.testing.assert_array_equal(a[:n], b[:n])
+    np.testing.assert_array_equal(a[so:so + n // 16], b[so:so + n // 16])
 
 
 def test_pack_q8_0_ties_bit_exact(torch):
@@ -57,12 +69,16 @@ def test_pack_q8_0_ties_bit_exact(torch):
     x[0, :8] = [127, 2.5, -2.5, 0.5, -0.5, 3.5, -3.5, 1.5]
     x[0, 31] = -126.5
     x[1] = np.arange(32) / 31.0
-    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_Q8_0, 2, 32), dtype=torch.uint8, device="cuda")
-    kda.kda_pack(kda.KDA_Q8_0, torch.from_numpy(x).cuda(), buf)
-    d16, qs = kda.kda_unpack_q8_0(buf, 2, 32)
     rd16, rq = ok.q8_0_quantize(x)
-    np.testing.assert_array_equal(d16.cpu().numpy().view(np.uint16), rd16.view(np.uint16))
-    np.testing.assert_array_equal(qs.cpu().numpy(), rq)
+    for host in (False, True):
+        buf = torch.empty(kda.kda_packed_bytes(kda.KDA_Q8_0, 2, 32), dtype=torch.uint8, device="cuda")
+        if host:
+            kda.kda_pack(kda.KDA_Q8_0, x, buf)
+        else:
+            kda.kda_pack_device(kda.KDA_Q8_0, torch.from_numpy(x).cuda(), buf)
+        d16, qs = kda.kda_unpack_q8_0(buf, 2, 32)
+        np.testing.assert_array_equal(d16, rd16.view(np.uint16))
+        np.testing.assert_array_equal(qs, rq)
 
 
 @pytest.mark.parametrize("shape", [(3, 5), (128, 2048)])
@@ -71,11 +87,15 @@ def test_pack_bf16_bit_exact(torch, shape):
     _say(f"pack bf16 {shape}")
     rng = np.random.default_rng(5)
     w = (rng.standard_normal(shape) * rng.uniform(1e-3, 1e3, shape)).astype(np.float32)
-    buf = torch.empty(kda.kda_packed_bytes(kda.KDA_BF16, *shape), dtype=torch.uint8, device="cuda")
-    kda.kda_pack(kda.KDA_BF16, torch.from_numpy(w).cuda(), buf)
-    bits = buf.cpu().numpy().view(np.uint16).reshape(shape)
-    got = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-    np.testing.assert_array_equal(got, ok.bf16_round(w))
+    for host in (False, True):
+        buf = torch.empty(kda.kda_packed_bytes(kda.KDA_BF16, *shape), dtype=torch.uint8, device="cuda")
+        if host:
+            kda.kda_pack(kda.KDA_BF16, w, buf)
+        else:
+            kda.kda_pack_device(kda.KDA_BF16, torch.from_numpy(w).cuda(), buf)
+        bits = buf.cpu().numpy().view(np.uint16).reshape(shape)
+        got = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        np.testing.assert_array_equal(got, ok.bf16_round(w))
 
 
 # ----------------------------------------------------------------------------------------
@@ -144,6 +164,46 @@ def test_decode_batched_q8_0_matrix_cores(torch, B):
     _say(f"  B={B}: out {e:.2e} state {s:.2e}")
 
 
+@pytest.mark.timeout(900)
+def test_decode_stack_full_run_128_steps(torch):
+    """The stack workload as configured: 34 Q8_0 layers, B=1, all 128 decode steps through
+    the one-launch kernel, every step's output and the state every 32 steps against the
+    oracle (error growth over the whole run)."""
+    w = synth.WORKLOADS["stack"]
+    _say(f"decode stack q8_0 34 layers D=2048 all {w.steps} steps, one launch, state every 32")
+    e, s = _decode_parity(w, w.steps, snap_every=32, expect_persistent=True)
+    _say(f"  stack 128 steps: out {e:.2e} state {s:.2e}")
+
+
+def test_one_launch_window_roll_bit_exact(torch):
+    """The one-launch kernel rolls each layer's window in place: after every step rows 0-1
+    are bit-for-bit rows 1-2 of the step before, and row 2 is this token's projection
+    (against the oracle's, to the output tolerance: the dots round differently)."""
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=3, steps=6, seed=45)
+    run = synth.draw_run(w)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    assert model.persistent_blocks() > 0
+    _say("one-launch window roll, 3 layers, 6 steps")
+    st = model.new_state(1)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(0, 1)
+    y = torch.empty((1, model.d_model), dtype=torch.float32, device="cuda")
+    S = [run.s0[l, 0].astype(np.float64) for l in range(w.n_layers)]
+    Z = [np.zeros((3, w.dims.conv_channels)) for _ in range(w.n_layers)]
+    prev = st.conv.cpu().numpy().copy()
+    for t in range(w.steps):
+        model.decode_step(torch.from_numpy(np.ascontiguousarray(run.x[t, :, 0, :])).cuda(), y, st, ws)
+        cur = st.conv.cpu().numpy().copy()
+        _, S, Z = ok.stack_step(layers, run.x[t, 0, 0].astype(np.float64)[None, :], S, Z)
+        np.testing.assert_array_equal(cur[:, 0, :2].view(np.uint32), prev[:, 0, 1:].view(np.uint32))
+        for l in range(w.n_layers):
+            assert range_rel(cur[l, 0, 2], Z[l][2]) <= OUT_RTOL
+        prev = cur
+    model.status()
+    model.close()
+
+
 def test_decode_stack_one_launch_three_layers_32_steps(torch):
     """The one-launch decode over 32 consecutive tokens (tags advance every token), with
     the state checked every 8 steps."""
@@ -175,6 +235,30 @@ def test_graph_replay_equals_eager(torch):
     np.testing.assert_array_equal(ya, yb)
     np.testing.assert_array_equal(Sa, Sb)
     np.testing.assert_array_equal(Za, Zb)
+    model.close()
+
+
+def test_conv_window_canonical(torch):
+    """kda_conv_window_canonical returns [n_layers][B][3][C], oldest token first: after a
+    few steps of the one-launch stack its rows equal the window the oracle holds (to the
+    output tolerance: the projections differ by rounding) and the state buffer's own bytes."""
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=2, steps=5, seed=44)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    _say("conv window canonical view, 2-layer one-launch stack, 5 steps")
+    st = model.new_state(1)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(0, 1)
+    y = torch.empty((1, model.d_model), dtype=torch.float32, device="cuda")
+    for t in range(w.steps):
+        model.decode_step(torch.from_numpy(np.ascontiguousarray(run.x[t, :, 0, :])).cuda(), y, st, ws)
+    out = model.conv_window(st)
+    torch.cuda.synchronize()
+    model.status()
+    assert tuple(out.shape) == (2, 1, 3, model.channels)
+    assert torch.equal(out, st.conv)
+    _, _, rZ, _ = ok.decode_run(oracle_layers(run), run.x, run.s0, True, steps=w.steps)
+    assert range_rel(out.cpu().numpy(), rZ) <= OUT_RTOL
     model.close()
 
 
@@ -215,6 +299,16 @@ def test_one_launch_wait_limit_times_out_and_recovers(torch):
     x = torch.from_numpy(np.ascontiguousarray(run.x[0, :, 0, :])).cuda()
     y = torch.empty((1, model.d_model), dtype=torch.float32, device="cuda")
     model.decode_step(x, y, st, ws)
+    torch.cuda.synchronize()
+    S_after, Z_after = st.S.clone(), st.conv.clone()
+    _say("  a second step before the status call: refused, nothing enqueued")
+    with pytest.raises(kda.KdaError) as ei:
+        model.decode_step(x, y, st, ws)
+    assert ei.value.status == kda._lib.KDA_E_HIP
+    with pytest.raises(kda.KdaError):
+        model.conv_window(st)
+    torch.cuda.synchronize()
+    assert torch.equal(st.S, S_after) and torch.equal(st.conv, Z_after)
     with pytest.raises(kda.KdaError):
         model.status()
     model.status()                      # reported once; the exchange words were reset

@@ -1,0 +1,135 @@
+"""GPU parity of the forget-gate forms other than KDA's per-channel softplus gate: the
+lower-bounded ("safe") gate and the per-head scalar gate of the gated delta rule, through
+decode (per-layer kernels), verify + commit and chunked prefill, against the oracle."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import kda as ok
+from tests.helpers import OUT_RTOL, STATE_ATOL, gpu_decode, gpu_model, oracle_layers, range_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", file=sys.stderr, flush=True)
+
+
+def _dims(gate, D=256, H=2, dk=64, rank=32):
+    return synth.LayerDims(d_model=D, n_heads=H, d_k=dk, d_v=dk, rank_f=rank, rank_g=rank, gate=gate)
+
+
+def _safe_params(run, seed):
+    """The safe gate's per-head factor a (used as given) spread over (0.2, 3)."""
+    rng = np.random.default_rng(seed)
+    for dr in run.layers:
+        dr["a_log"] = rng.uniform(0.2, 3.0, dr["a_log"].shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+@pytest.mark.parametrize("wtype", ["f32", "bf16", "q8_0"])
+def test_gate_forms_decode(gate, wtype):
+    """A 2-layer pre-norm stack, B=2, 12 steps; the state every 4 steps."""
+    w = synth.scaled(synth.WORKLOADS["tiny"], dims=_dims(gate), wtype=wtype, n_layers=2,
+                     prenorm_residual=True, batch=2, steps=12, s0_std=0.1, seed=101)
+    _say(f"decode gate={gate} {wtype} 2 layers B=2 12 steps")
+    run = synth.draw_run(w)
+    if gate == "safe":
+        _safe_params(run, 102)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    assert model.persistent_blocks() == 0
+    y, S, Z, snaps = gpu_decode(model, run, w.steps, 4)
+    ry, rS, rZ, rsnaps = ok.decode_run(layers, run.x, run.s0, True, check_every=4)
+    e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
+    assert e <= OUT_RTOL, e
+    assert np.abs(S - rS).max() <= STATE_ATOL
+    for k in snaps:
+        assert np.abs(snaps[k] - rsnaps[k]).max() <= STATE_ATOL
+    assert range_rel(Z, rZ) <= OUT_RTOL
+    model.close()
+    _say(f"  out {e:.2e}")
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+def test_gate_forms_full_size_stack(gate):
+    """D=2048, 16 heads, Q8_0, 3 layers (the one-launch kernel takes only the KDA gate, so
+    these run the per-layer kernels), 6 steps."""
+    d = synth.LayerDims(d_model=2048, n_heads=16, d_k=128, d_v=128, rank_f=128, rank_g=128, gate=gate)
+    w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=3, steps=6, seed=103)
+    _say(f"decode gate={gate} q8_0 D=2048 3 layers 6 steps")
+    run = synth.draw_run(w)
+    if gate == "safe":
+        _safe_params(run, 104)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    y, S, Z, _ = gpu_decode(model, run, w.steps)
+    ry, rS, rZ, _ = ok.decode_run(layers, run.x, run.s0, True)
+    e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
+    assert e <= OUT_RTOL, e
+    assert np.abs(S - rS).max() <= STATE_ATOL
+    model.close()
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+def test_gate_forms_verify_commit(gate):
+    """Verify + commit (T=3) of a 2-layer Q8_0 stack, B=3, 3 steps."""
+    import torch
+    w = synth.scaled(synth.WORKLOADS["verify"], dims=_dims(gate, D=256, H=2, dk=64, rank=32),
+                     n_layers=2, batch=3, tokens=3, steps=3, seed=105)
+    _say(f"verify gate={gate} 2 layers B=3 T=3")
+    run = synth.draw_run(w)
+    if gate == "safe":
+        _safe_params(run, 106)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    B, T = w.batch, w.tokens
+    st = model.new_state(B)
+    st.S.copy_(torch.from_numpy(run.s0))
+    ws = model.workspace(1, B, T)
+    log = model.verify_log(B, T)
+    S = [[run.s0[l, b].astype(np.float64) for b in range(B)] for l in range(2)]
+    Z = [[np.zeros((3, w.dims.conv_channels)) for _ in range(B)] for _ in range(2)]
+    y = torch.empty((B, T, model.d_model), dtype=torch.float32, device="cuda")
+    for t in range(w.steps):
+        model.verify_steps(torch.from_numpy(np.ascontiguousarray(run.x[t])).cuda(), T, y, st, log, ws)
+        model.verify_commit(st, log, T, torch.from_numpy(run.accept[t].copy()).cuda())
+        yy = y.cpu().numpy()
+        for b in range(B):
+            ry, s2, z2 = ok.stack_step(layers, run.x[t, b].astype(np.float64), [S[l][b] for l in range(2)],
+                                       [Z[l][b] for l in range(2)], keep_after=int(run.accept[t, b]))
+            assert range_rel(yy[b], ry) <= OUT_RTOL
+            for l in range(2):
+                S[l][b], Z[l][b] = s2[l], z2[l]
+        gS = st.S.cpu().numpy()
+        assert np.abs(gS - np.array([[S[l][b] for b in range(B)] for l in range(2)])).max() <= STATE_ATOL
+    model.close()
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+def test_gate_forms_prefill(gate):
+    """Chunked prefill, BF16, B=2, L=150 (a ragged last chunk), S0 != 0."""
+    import torch
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["prefill"], dims=_dims(gate, rank=64), batch=2, tokens=150,
+                     s0_std=0.1, seed=107)
+    _say(f"prefill gate={gate} D=256 B=2 L=150")
+    run = synth.draw_run(w)
+    if gate == "safe":
+        _safe_params(run, 108)
+    layer = oracle_layers(run)[0]
+    model = gpu_model(run)
+    st = model.new_state(w.batch)
+    st.S.copy_(torch.from_numpy(run.s0))
+    x = torch.from_numpy(np.ascontiguousarray(run.x_bits[0]).view(np.int16)).cuda()
+    y = torch.empty((2, 150, w.dims.d_model), dtype=torch.float32, device="cuda")
+    model.prefill_chunked(x, kda.KDA_BF16, 150, 64, y, st, model.workspace(kda.KDA_OP_PREFILL, 2, 150))
+    torch.cuda.synchronize()
+    ry, rS, rZ = ok.prefill_run(layer, run.x[0], run.s0[0])
+    yy = y.cpu().numpy()
+    e = max(range_rel(yy[b, t], ry[b, t]) for b in range(2) for t in range(150))
+    assert e <= OUT_RTOL, e
+    assert np.abs(st.S.cpu().numpy()[0] - rS).max() <= STATE_ATOL
+    model.close()

@@ -148,3 +148,70 @@ def test_prefill_strong_decay_blocks():
     ry, rS, rZ = ok.prefill_run(layer, run.x[0], run.s0[0])
     _compare(y, ry, st.S.cpu().numpy()[0], rS, st.conv.cpu().numpy()[0], rZ)
     model.close()
+
+
+def _slow_gates(run, seed):
+    """Per-channel decay rates from nearly 1 to fast: A_log per head in U(-6, -1), dt_bias
+    per key channel in U(-6, 2), so many channels keep alpha > 0.999 per token and carry
+    the state across chunk boundaries (a slow channel stays slow on every token)."""
+    rng = np.random.default_rng(seed)
+    for dr in run.layers:
+        dr["a_log"] = rng.uniform(-6.0, -1.0, dr["a_log"].shape).astype(np.float32)
+        dr["dt_bias"] = rng.uniform(-6.0, 2.0, dr["dt_bias"].shape).astype(np.float32)
+
+
+@pytest.mark.parametrize("dims", ["small", "full"])
+def test_prefill_slow_gates_carry_state(dims):
+    """Slow per-channel gates, S0 != 0, 200 tokens (four chunks, a ragged last one): the
+    state carried across each chunk end (each key row decayed by its own channel's
+    end-of-chunk factor) dominates the outputs and the final state."""
+    import torch
+    if dims == "small":
+        w = _small(200, seed=64)
+    else:
+        w = synth.scaled(synth.WORKLOADS["prefill"], batch=1, tokens=200, s0_std=0.1, seed=65)
+    _say(f"prefill slow gates {dims} D={w.dims.d_model} L=200, S0 != 0")
+    run = synth.draw_run(w)
+    _slow_gates(run, 66)
+    layer = oracle_layers(run)[0]
+    # a quarter of the channels keep more than half their state across a 64-token chunk
+    # from the bias alone (the low-rank term is small)
+    slow = np.exp(-np.exp(layer.a_log)[:, None] * ok.softplus(layer.dt_bias.reshape(len(layer.a_log), -1)))
+    assert (slow ** 64 > 0.5).mean() > 0.25
+    model = gpu_model(run)
+    st = model.new_state(w.batch)
+    st.S.copy_(torch.from_numpy(run.s0))
+    y = gpu_prefill(model, run.x[0], run.x_bits[0], st)
+    ry, rS, rZ = ok.prefill_run(layer, run.x[0], run.s0[0])
+    e, se = _compare(y, ry, st.S.cpu().numpy()[0], rS, st.conv.cpu().numpy()[0], rZ)
+    _say(f"  out {e:.2e} state {se:.2e}")
+    model.close()
+
+
+def test_prefill_window_roll_bit_exact():
+    """The window a prefill leaves holds the last three pre-conv projections, oldest first:
+    prefills of 200 and 201 tokens of the same sequence leave windows shifted by one row,
+    bit for bit (a token's projection does not depend on the call's length); prefills of 1
+    and 2 tokens from a random window keep its newest rows, bit for bit."""
+    import torch
+    w = _small(201, B=2, seed=67)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    _say("prefill window roll: L=200 vs 201, and L=1, 2 from a random window")
+    wins = {}
+    for L in (200, 201):
+        st = model.new_state(w.batch)
+        st.S.copy_(torch.from_numpy(run.s0))
+        gpu_prefill(model, np.ascontiguousarray(run.x[0][:, :L]), np.ascontiguousarray(run.x_bits[0][:, :L]), st)
+        wins[L] = st.conv.cpu().numpy()[0].copy()
+    np.testing.assert_array_equal(wins[201][:, :2].view(np.uint32), wins[200][:, 1:].view(np.uint32))
+    rng = np.random.default_rng(68)
+    z0 = rng.standard_normal((1, w.batch, 3, w.dims.conv_channels)).astype(np.float32)
+    for L in (1, 2):
+        st = model.new_state(w.batch)
+        st.S.copy_(torch.from_numpy(run.s0))
+        st.conv.copy_(torch.from_numpy(z0))
+        gpu_prefill(model, np.ascontiguousarray(run.x[0][:, :L]), np.ascontiguousarray(run.x_bits[0][:, :L]), st)
+        z = st.conv.cpu().numpy()[0]
+        np.testing.assert_array_equal(z[:, :3 - L].view(np.uint32), z0[0][:, L:].view(np.uint32))
+    model.close()

@@ -21,7 +21,11 @@ def _say(msg):
     print(f"[case] {msg}", file=sys.stderr, flush=True)
 
 
-def gpu_verify(model, run, steps, accept=None):
+def gpu_verify(model, run, steps, accept=None, snap_every=1):
+    """Verify + commit for `steps` steps.  Returns the outputs of every step and the
+    committed (S, window) after every `snap_every`-th step.  After every commit the window
+    roll is checked bit for bit: with a accepted tokens, rows [0, 3 - a) of the new window
+    are rows [a, 3) of the previous one."""
     import torch
     w = run.workload
     B, T = w.batch, w.tokens
@@ -33,21 +37,28 @@ def gpu_verify(model, run, steps, accept=None):
     xs = torch.from_numpy(np.ascontiguousarray(run.x[:steps])).cuda()
     ys = torch.empty((steps, B, T, model.d_model), dtype=torch.float32, device="cuda")
     accs = torch.from_numpy(np.ascontiguousarray(acc[:steps]).astype(np.int32)).cuda()
-    states = []
+    states = {}
     for t in range(steps):
+        prev = st.conv.clone()
         model.verify_steps(xs[t].contiguous(), T, ys[t], st, log, ws)
         model.verify_commit(st, log, T, accs[t].contiguous())
-        states.append((st.S.cpu().numpy().copy(), st.conv.cpu().numpy().copy()))
+        for b in range(B):
+            a = int(min(max(acc[t, b], 1), T))
+            if a < 3:
+                assert torch.equal(st.conv[:, b, :3 - a].view(torch.int32),
+                                   prev[:, b, a:].view(torch.int32)), f"step {t} seq {b}: window roll"
+        if (t + 1) % snap_every == 0:
+            states[t] = (st.S.cpu().numpy().copy(), st.conv.cpu().numpy().copy())
     torch.cuda.synchronize()
     return ys.cpu().numpy(), states
 
 
-def _check(w, steps, accept=None):
+def _check(w, steps, accept=None, snap_every=1):
     run = synth.draw_run(w)
     layers = oracle_layers(run)
     model = gpu_model(run)
     acc = run.accept if accept is None else accept
-    y, states = gpu_verify(model, run, steps, acc)
+    y, states = gpu_verify(model, run, steps, acc, snap_every)
     worst = 0.0
     # oracle step by step (verify_run's commit semantics), recording each committed state
     ry_all = np.empty((steps,) + run.x.shape[1:3] + (run.x.shape[3],))
@@ -65,6 +76,8 @@ def _check(w, steps, accept=None):
         e = range_rel(y[t], ry_all[t])
         worst = max(worst, e)
         assert e <= OUT_RTOL, f"step {t}: output range-rel error {e:.3e}"
+        if t not in states:
+            continue
         gS, gZ = states[t]
         rS = np.array([[S[l][b] for b in range(w.batch)] for l in range(w.n_layers)])
         rZ = np.array([[Z[l][b] for b in range(w.batch)] for l in range(w.n_layers)])
@@ -117,8 +130,29 @@ def test_verify_accept_clamped():
     _check(w, w.steps, accept=acc)
 
 
-def test_verify_full_size_34_layers():
-    w = synth.scaled(synth.WORKLOADS["verify"], steps=3)
-    _say("verify full size: 34 layers B=8 T=4 q8_0, 3 steps")
-    e = _check(w, w.steps)
+@pytest.mark.timeout(1200)
+def test_verify_full_run_64_steps():
+    """The verify workload as configured: 34 Q8_0 layers, B=8 sequences, T=4 tokens, all 64
+    verify + commit steps with the seeded accept lengths; every output, the committed state
+    every 16 steps, the window roll after every commit."""
+    w = synth.WORKLOADS["verify"]
+    _say(f"verify full size: 34 layers B=8 T=4 q8_0, all {w.steps} steps")
+    e = _check(w, w.steps, snap_every=16)
     _say(f"  worst output error {e:.2e}")
+
+
+def test_verify_commit_rejects_short_log():
+    """A log smaller than a verify of the state's batch and T is refused before anything is
+    enqueued (the replay would read past its end)."""
+    import torch
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=1, batch=2, steps=1, seed=52)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    st = model.new_state(2)
+    small = model.verify_log(2, 3)
+    acc = torch.ones(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(kda.KdaError) as ei:
+        model.verify_commit(st, small, 4, acc)
+    assert ei.value.status == kda._lib.KDA_E_WORKSPACE
+    model.close()

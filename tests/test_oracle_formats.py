@@ -107,3 +107,75 @@ def test_mutant_round_half_even_fails_golden():
     d16 = np.float16(np.float32(amax) / np.float32(127))
     q_mut = np.clip(np.rint(x / np.float32(d16)), -127, 127).astype(np.int8)[0]
     assert not np.array_equal(q_mut, blk["q"])
+
+
+# ----------------------------------------------------------------------------------------
+# MXFP4 (OCP Microscaling format specification v1.0)
+# ----------------------------------------------------------------------------------------
+MX_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "mxfp4_block.txt")
+
+
+def _read_mx_golden():
+    blocks, cur = [], None
+    with open(MX_GOLDEN) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, rest = line.partition(" ")
+            if key == "block":
+                cur = {"name": rest}
+                blocks.append(cur)
+            elif key == "x":
+                v = [float(t) for t in rest.split()]
+                cur["x"] = np.array(v + [0.0] * (32 - len(v)), np.float32)
+            elif key == "e8m0":
+                cur["e8m0"] = int(rest)
+            elif key == "codes":
+                v = [int(t) for t in rest.split()]
+                cur["codes"] = np.array(v + [0] * (32 - len(v)), np.uint8)
+    return blocks
+
+
+@pytest.mark.parametrize("blk", _read_mx_golden(), ids=lambda b: b["name"])
+def test_mxfp4_golden_blocks(blk):
+    e, c = ok.mxfp4_quantize(blk["x"][None, :])
+    assert int(e[0, 0]) == blk["e8m0"]
+    np.testing.assert_array_equal(c[0], blk["codes"])
+
+
+def test_mxfp4_grid_values_round_trip():
+    """Values on the E2M1 grid times a block's scale come back exactly (the block's largest
+    magnitude is 4 or 6 times the scale, so the scale is the one chosen)."""
+    rng = np.random.default_rng(12)
+    for s in (-20, -7, 0, 5):
+        idx = rng.integers(0, 8, (4, 64))
+        idx[:, 0] = 7
+        idx[:, 32] = 6
+        sign = rng.integers(0, 2, (4, 64))
+        x = (np.where(sign, -1.0, 1.0) * ok.E2M1_GRID[idx] * 2.0 ** s).astype(np.float32)
+        e, c = ok.mxfp4_quantize(x)
+        assert np.all(e == s + 127)
+        np.testing.assert_array_equal(ok.mxfp4_dequantize(e, c), x.astype(np.float64))
+
+
+def test_mxfp4_error_bounds():
+    """With X the block scale: |x - q| <= X/4 where |x| <= 2X (grid spacing X/2), <= X/2
+    up to 4X, <= X up to 6X, and <= 2X in the clamped range (6X, 8X); max|x| / X in [4, 8)."""
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((64, 256)) * 0.02).astype(np.float32)
+    w[3, 32:64] *= 1e3
+    w[5, :32] = 0.0
+    e, c = ok.mxfp4_quantize(w)
+    q = ok.mxfp4_dequantize(e, c)
+    X = np.repeat(np.exp2(e.astype(np.float64) - 127), 32, axis=1)
+    a = np.abs(w.astype(np.float64)) / X
+    err = np.abs(w - q) / X
+    assert np.all(err[a <= 2] <= 0.25)
+    assert np.all(err[(a > 2) & (a <= 4)] <= 0.5)
+    assert np.all(err[(a > 4) & (a <= 6)] <= 1.0)
+    assert np.all(err[a > 6] <= 2.0)
+    am = np.abs(w.reshape(64, 8, 32)).max(-1) / np.exp2(e.astype(np.float64) - 127)
+    nz = am > 0
+    assert np.all((am[nz] >= 4) & (am[nz] < 8))
+    assert np.all(c[5, :32] == 0) and e[5, 0] == 0

@@ -544,3 +544,129 @@ def test_beta_head_mapping_mutant_reversed_rows():
     def layer(L, U, S, Z, **kw):
         return real(ok.OracleLayer(**{**L.__dict__, "wbeta": L.wbeta[::-1].copy()}), U, S, Z, **kw)
     assert not pin_beta_heads(layer)
+
+
+# ----------------------------------------------------------------------------------------
+# forget-gate variants: the lower-bounded ("safe") gate and the per-head scalar gate
+# ----------------------------------------------------------------------------------------
+def pin_safe_gate(gate_fn) -> bool:
+    lb = -5.0
+    # f = 0: sigmoid(0) = 1/2, alpha = exp(lb / 2)
+    good = np.allclose(gate_fn(np.zeros((2, 3)), np.array([0.7, 2.0]), lb), math.exp(lb / 2), rtol=1e-15)
+    # f a -> +inf: alpha -> 1; f a -> -inf: alpha -> e^lb
+    good &= np.allclose(gate_fn(np.full((1, 2), 60.0), np.array([1.0]), lb), 1.0, rtol=1e-15)
+    good &= np.allclose(gate_fn(np.full((1, 2), -60.0), np.array([1.0]), lb), math.exp(lb), rtol=1e-12)
+    # per-head factor: head h at f = 1 gives exp(lb / (1 + e^{a_h})), libm scalars
+    a = np.array([0.3, 1.5, -0.4])
+    al = gate_fn(np.ones((3, 4)), a, lb)
+    for h in range(3):
+        good &= np.allclose(al[h], math.exp(lb / (1.0 + math.exp(a[h]))), rtol=1e-14)
+    # bounds
+    rng = RNG(21)
+    al = gate_fn(rng.standard_normal((4, 16)) * 4, rng.uniform(0.1, 3, 4), lb)
+    good &= bool(np.all((al > math.exp(lb)) & (al < 1)))
+    return bool(good)
+
+
+def test_safe_gate_pins():
+    assert pin_safe_gate(ok.safe_gate)
+
+
+def test_safe_gate_mutant_sign():
+    def mutant(f, a, lb):
+        return np.exp(lb * ok.sigmoid(f * a[:, None]))
+    assert not pin_safe_gate(mutant)
+
+
+def pin_scalar_gate(gate_fn) -> bool:
+    dk = 5
+    # softplus(0) = ln 2, exp(A_log = 0) = 1: alpha = 1/2 on every channel of the head
+    good = np.allclose(gate_fn(np.zeros(2), np.zeros(2), dk), 0.5, rtol=1e-15)
+    f = np.array([0.4, -1.2, 3.0])
+    a_log = np.array([-0.5, 0.2, -1.0])
+    al = gate_fn(f, a_log, dk)
+    good &= al.shape == (3, dk)
+    for h in range(3):
+        sp = max(f[h], 0.0) + math.log1p(math.exp(-abs(f[h])))
+        good &= np.allclose(al[h], math.exp(-math.exp(a_log[h]) * sp), rtol=1e-14)
+    return bool(good)
+
+
+def test_scalar_gate_pins():
+    assert pin_scalar_gate(ok.scalar_gate)
+
+
+def test_scalar_gate_mutant_head_order():
+    def mutant(f, a_log, dk):
+        return ok.scalar_gate(f, a_log[::-1].copy(), dk)
+    assert not pin_scalar_gate(mutant)
+
+
+def _gate_layer(gate, seed):
+    d = synth.LayerDims(d_model=256, n_heads=2, d_k=64, d_v=64, rank_f=16, rank_g=16, gate=gate)
+    w = synth.scaled(synth.WORKLOADS["tiny"], dims=d, steps=2, seed=seed)
+    run = synth.draw_run(w)
+    L = ok.prepare_layer(run.layers[0], "f32", 2, 64, 64, norm_eps=0.0, gate=gate, gate_lb=-5.0)
+    return L, run
+
+
+def pin_gate_variant_wiring(layer_fn, gate) -> bool:
+    """As pin_forget_gate_wiring, for the other gate forms: with F_a = 0 the gate input is
+    dt_bias exactly, and a beta = 1 token followed by a beta = 0 token gives
+    S2 = diag(alpha) S1 with alpha from the gate's closed form (libm scalars): the safe gate
+    per key channel exp(lb sigmoid(-dt_bias[h dk + i] a[h])), the scalar gate one value per
+    head exp(-exp(A_log[h]) softplus(dt_bias[h]))."""
+    L, run = _gate_layer(gate, 31)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    u1 = run.x[0, 0, 0].astype(np.float64)
+    L.wbeta = np.tile(u1 / np.linalg.norm(u1), (H, 1)) * np.linspace(3e3, 5e3, H)[:, None]
+    L.a_log = np.array([0.6, -0.8])
+    L.fa = np.zeros_like(L.fa)
+    U = np.stack([u1, -u1])
+    _, S1, _ = layer_fn(L, U[:1], np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+    _, S2, _ = layer_fn(L, U, np.zeros((H, dk, dv)), np.zeros((3, L.channels)))
+    good = True
+    for h in range(H):
+        for i in range(dk):
+            if gate == "safe":
+                z = float(L.dt_bias[h * dk + i]) * float(L.a_log[h])
+                a = math.exp(-5.0 / (1.0 + math.exp(z)))
+            else:
+                z = float(L.dt_bias[h])
+                a = math.exp(-math.exp(float(L.a_log[h])) * (max(z, 0.0) + math.log1p(math.exp(-abs(z)))))
+            good &= np.allclose(S2[h, i], a * S1[h, i], rtol=1e-12, atol=1e-15)
+    return bool(good)
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+def test_gate_variant_wiring(gate):
+    assert pin_gate_variant_wiring(ok.layer_forward, gate)
+
+
+@pytest.mark.parametrize("gate", ["safe", "scalar"])
+def test_gate_variant_wiring_mutant_kda_formula(gate):
+    """Planted mistakes fail the pins: the KDA formula on the safe gate's input, and the
+    scalar gate reading its heads' inputs in reverse order."""
+    real = ok.layer_forward
+
+    def layer(L, U, S, Z, **kw):
+        if gate == "scalar":
+            kv = dict(L.__dict__)
+            kv.update(fb=L.fb[::-1].copy(), dt_bias=L.dt_bias[::-1].copy())
+            return real(ok.OracleLayer(**kv), U, S, Z, **kw)
+        return real(ok.OracleLayer(**{**L.__dict__, "gate": "kda"}), U, S, Z, **kw)
+    assert not pin_gate_variant_wiring(layer, gate)
+
+
+def test_scalar_gate_state_decays_uniformly():
+    """With beta = 0 the scalar gate scales each head's whole state by one number: the
+    ratio S2 / S1 is constant over the head (a per-channel gate would vary)."""
+    L, run = _gate_layer("scalar", 32)
+    H, dk, dv = L.n_heads, L.d_k, L.d_v
+    L.wbeta = -1e4 * np.tile(np.sign(run.x[0, 0, 0]), (H, 1))     # beta logits << 0
+    S0 = RNG(33).standard_normal((H, dk, dv))
+    _, S1, _ = ok.layer_forward(L, run.x[:1, 0, 0].astype(np.float64), S0, np.zeros((3, L.channels)))
+    for h in range(H):
+        r = S1[h] / S0[h]
+        assert np.allclose(r, r.flat[0], rtol=1e-12)
+        assert 0 < r.flat[0] < 1
