@@ -225,6 +225,19 @@ size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t to
 int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
                     void* ws_dev, size_t ws_bytes, void* stream);
 
+/* kda_decode_step for callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same step, with its
+ * workspace in a static device array of the library (8 MiB per GPU, held by the process
+ * until it ends) instead of a caller's buffer.  It calls no hipMalloc, hipFree or other
+ * allocating routine: the kernels run as plain launches (no graph of the library's own, no
+ * timing events).  Every call on one GPU shares that array, which keeps the last call's
+ * contents; no part of it needs to start at zero.  Calls that overlap on one GPU (two
+ * streams, two threads, two models) race on it: serialise them.  Errors as
+ * kda_decode_step, and KDA_E_WORKSPACE when the batch needs more than the array holds
+ * (kda_workspace_bytes(m, KDA_OP_DECODE, batch, 1) > 8 MiB). */
+int kda_decode_step_static(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                           void* stream);
+
 /* Batched decode with ragged or left-padded sequences ("Thirty tiny kernels per layer",
  * section "Taking it upstream, and finding out why it's worth less there": a left-padded
  * batch mask and ragged per-row lengths).  active_dev: device int32 [B]; a sequence with

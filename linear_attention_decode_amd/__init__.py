@@ -142,6 +142,12 @@ def kda_decode_step(handle, x, y, st, ws, stream=None) -> None:
     _lib.call("kda_decode_step", handle, _p(x), _p(y), C.byref(s), _p(ws), ws.numel(), _s(stream))
 
 
+def kda_decode_step_static(handle, x, y, st, stream=None) -> None:
+    """kda_decode_step with the library's static workspace (allocates nothing)."""
+    s = _state(st)
+    _lib.call("kda_decode_step_static", handle, _p(x), _p(y), C.byref(s), _s(stream))
+
+
 def kda_decode_step_masked(handle, x, y, st, active, ws, stream=None) -> None:
     """active: cuda int32 [B]; 0 = this sequence takes no token (state and window kept)."""
     s = _state(st)

@@ -27,6 +27,7 @@ EXPORTS = (
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
     "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
+    "kda_decode_step_static",
 )
 
 
@@ -83,6 +84,7 @@ def lib():
             "kda_workspace_bytes": (sz, [vp, C.c_int, i32, i64]),
             "kda_decode_step": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, sz, vp]),
             "kda_decode_step_masked": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, vp, sz, vp]),
+            "kda_decode_step_static": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp]),
             "kda_verify_log_bytes": (sz, [vp, i32, i32]),
             "kda_verify_steps": (C.c_int, [vp, vp, i32, vp, C.POINTER(KdaState), vp, sz, vp, sz, vp]),
             "kda_verify_commit": (C.c_int, [vp, C.POINTER(KdaState), vp, sz, i32, vp, vp]),

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -509,6 +510,36 @@ int reset_exchange(kda_model* m) {
   return KDA_OK;
 }
 
+// ---- a device workspace for callers that cannot allocate (kda_decode_step_static) ----
+// One array per GPU for the life of the process, shared by every model and call on that
+// GPU.  In host code `scratch` names a host-side stand-in, not device memory: its device
+// address comes from hipGetSymbolAddress, taken once per device (with that device
+// current) and kept in g_scratch_ptr; only that address is ever passed to a kernel.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __attribute__((used)) __align__(256) char scratch[kStaticScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's scratch address (looked up on its first use on that device).
+int static_scratch(void** out) {
+  int dev = 0;
+  KDA_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(KDA_E_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KDA_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
 // A one-launch step whose wait between blocks ran out left the caller's state partly
 // advanced; until kda_model_status has reported it, every call that reads or writes a state
 // on this model is refused (the kernel itself also leaves at once while the device word is
@@ -704,6 +735,13 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
     L.o_norm_w = s.o_norm_w;
     m->layers.push_back(L);
   }
+  {
+    // the static scratch's address on this device, taken once here (the library's set-up
+    // call) so that kda_decode_step_static finds it ready
+    void* sp = nullptr;
+    const int r = static_scratch(&sp);
+    if (r) { delete m; return r; }
+  }
   hipError_t e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
   if (e == hipSuccess) e = persist_setup(m, layers);
   if (e != hipSuccess) {
@@ -804,7 +842,8 @@ namespace {
 // One decode token for every sequence; `active` (device [B] or null) masks sequences whose
 // state and window stay as they are.  A masked step never takes the one-launch kernel.
 int decode_impl(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
-                const int32_t* active, void* ws_dev, size_t ws_bytes, void* stream) {
+                const int32_t* active, void* ws_dev, size_t ws_bytes, void* stream,
+                bool eager = false) {
   if (!m || !x_dev || !y_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
   int r = check_state(m, st);
   if (r) return r;
@@ -824,8 +863,11 @@ int decode_impl(kda_model* m, const float* x_dev, float* y_dev, const kda_state*
     PersistParams p = m->pp;
     p.S = st->S_dev; p.win = st->conv_dev; p.x_in = x_dev; p.y_out = y_dev;
     p.epoch = ++m->epoch;
-    return timed(m, KDA_K_STEP, s, m->timing, [&] { return launch_persistent(p, m->pers_blocks, m->coop, s); });
+    return timed(m, KDA_K_STEP, s, m->timing && !eager,
+                 [&] { return launch_persistent(p, m->pers_blocks, m->coop, s); });
   }
+  // (eager: no graph capture or instantiation and no timing events, which allocate)
+  if (eager) return enqueue_decode(m, x_dev, y_dev, st, ws, s, false, active);
   if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing, active);
 
   GraphKey k;
@@ -856,6 +898,22 @@ extern "C" {
 int kda_decode_step(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
                     void* ws_dev, size_t ws_bytes, void* stream) {
   return decode_impl(m, x_dev, y_dev, st, nullptr, ws_dev, ws_bytes, stream);
+}
+
+int kda_decode_step_static(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
+                           void* stream) {
+  if (!m) return fail(KDA_E_ARG, "null model");
+  int r = check_state(m, st);
+  if (r) return r;
+  const size_t need = ws_layout(m, st->batch).total;
+  if (need > kStaticScratchBytes)
+    return fail(KDA_E_WORKSPACE, "batch %d needs %zu workspace bytes, more than the %zu of the "
+                "static scratch; use kda_decode_step with a workspace", st->batch, need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  r = static_scratch(&ws);
+  if (r) return r;
+  return decode_impl(m, x_dev, y_dev, st, nullptr, ws, kStaticScratchBytes, stream, true);
 }
 
 int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
