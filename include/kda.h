@@ -53,7 +53,7 @@ typedef enum {
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_Q8_0 = 2 } kda_dtype;
 
-typedef enum { KDA_OP_DECODE = 0, KDA_OP_VERIFY = 1, KDA_OP_PREFILL = 2 } kda_op;
+typedef enum { KDA_OP_DECODE = 0, KDA_OP_VERIFY = 1, KDA_OP_PREFILL = 2, KDA_OP_SCAN = 3 } kda_op;
 
 /* Forget-gate forms.  f is the gate input F_b F_a u + dt_bias.
  * KDA_GATE_KDA    per key channel: alpha = exp(-exp(A_log[h]) softplus(f))   (the workload
@@ -271,6 +271,23 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
  * the kernel clamps a value outside 1..T to that range. */
 int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
                       int32_t T, const int32_t* accept_dev, void* stream);
+
+/* Sequential-scan prefill of L tokens per sequence, for prompts too short for the
+ * chunked form to pay (the sequential prompt scan gdn_scan_r of the regolith audit
+ * opus_gdn_qsa, section 3): every layer of any model (any weight format and gate form,
+ * a single layer or a pre-norm stack, any batch) runs the tokens in order, layer by layer
+ * over blocks of Tc tokens (B * Tc <= 64): the projections of a block's B * Tc token
+ * columns in one pass over the weights, then per (sequence, head, 32 value columns) one
+ * wave holds its state tile in registers across the block's tokens (one read and one
+ * write of the state per block, two register passes per token), then the output
+ * projection.  The window is rolled by the block's tokens in the same launch.
+ * x_dev [B][L][D] fp32 in, y_dev [B][L][D] fp32 out (layer output, or the final
+ * residual stream of a stack); st is read as the initial state and advanced to the state
+ * after all L tokens.  The result equals L calls of kda_decode_step.  Workspace:
+ * kda_workspace_bytes(m, KDA_OP_SCAN, B, L).  Errors: KDA_E_ARG, KDA_E_ALIGN,
+ * KDA_E_SHAPE (L < 1), KDA_E_WORKSPACE, KDA_E_HIP. */
+int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
+                     const kda_state* st, void* ws_dev, size_t ws_bytes, void* stream);
 
 /* The conv windows of every layer and sequence in the canonical layout
  * out_dev [n_layers][B][conv_k - 1][C] fp32, oldest token first (the "conv_state" of the

@@ -14,7 +14,7 @@ import ctypes as C
 from typing import Dict, List, Optional, Sequence
 
 from . import _lib
-from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL,  # noqa: F401
+from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL, KDA_OP_SCAN,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
                    KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, KDA_K_GEMM, KDA_K_CHUNK,
                    KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError,
@@ -167,6 +167,12 @@ def kda_verify_commit(handle, st, log, T: int, accept, stream=None) -> None:
               T, _p(accept), _s(stream))
 
 
+def kda_prefill_scan(handle, x, L: int, y, st, ws, stream=None) -> None:
+    """x, y: cuda fp32 [B][L][D]; st advanced by L tokens."""
+    s = _state(st)
+    _lib.call("kda_prefill_scan", handle, _p(x), L, _p(y), C.byref(s), _p(ws), ws.numel(), _s(stream))
+
+
 def kda_conv_window_canonical(handle, st, out, stream=None) -> None:
     """out: cuda fp32 [n_layers][B][conv_k - 1][C], oldest token first."""
     s = _state(st)
@@ -302,6 +308,9 @@ class KdaModel:
         torch = _torch()
         return torch.empty(kda_verify_log_bytes(self.handle, batch, T), dtype=torch.uint8,
                            device=self.device)
+
+    def prefill_scan(self, x, L: int, y, st: KdaStateBuf, ws, stream=None) -> None:
+        kda_prefill_scan(self.handle, x, L, y, st, ws, stream)
 
     def prefill_chunked(self, x, x_dtype: int, L: int, chunk: int, y, st: KdaStateBuf, ws,
                         stream=None) -> None:

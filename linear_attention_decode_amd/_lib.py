@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 KDA_OK, KDA_E_ARG, KDA_E_SHAPE, KDA_E_ALIGN, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E_HIP, \
     KDA_E_UNSUPPORTED = range(8)
 KDA_F32, KDA_BF16, KDA_Q8_0 = 0, 1, 2
-KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL = 0, 1, 2
+KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL, KDA_OP_SCAN = 0, 1, 2, 3
 KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE = 0, 1, 2, 3, 4
 KDA_Q_PERSISTENT = 0
 KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, \
@@ -27,7 +27,7 @@ EXPORTS = (
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
     "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
-    "kda_decode_step_static",
+    "kda_decode_step_static", "kda_prefill_scan",
 )
 
 
@@ -85,6 +85,7 @@ def lib():
             "kda_decode_step": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, sz, vp]),
             "kda_decode_step_masked": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp, vp, sz, vp]),
             "kda_decode_step_static": (C.c_int, [vp, vp, vp, C.POINTER(KdaState), vp]),
+            "kda_prefill_scan": (C.c_int, [vp, vp, i64, vp, C.POINTER(KdaState), vp, sz, vp]),
             "kda_verify_log_bytes": (sz, [vp, i32, i32]),
             "kda_verify_steps": (C.c_int, [vp, vp, i32, vp, C.POINTER(KdaState), vp, sz, vp, sz, vp]),
             "kda_verify_commit": (C.c_int, [vp, C.POINTER(KdaState), vp, sz, i32, vp, vp]),

@@ -243,11 +243,11 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
 int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
                   float* S, float* win, float* proj, float* ag, float* act, const WsLayout& wl,
                   char* ws, bool write_state, hipStream_t s, bool rec,
-                  const int* active = nullptr) {
+                  const int* active = nullptr, bool roll = false) {
   const kda_dims& d = m->d;
   const LayerDev& L = m->layers[l];
   const int N = B * T;
-  const bool decode = (T == 1) && write_state;
+  const bool decode = (T == 1) && write_state && !act;   // (the scan passes act: conv apart)
   float* o = reinterpret_cast<float*>(ws + wl.o);
   float* gate = reinterpret_cast<float*>(ws + wl.gate);
   float* ss = reinterpret_cast<float*>(ws + wl.ss);
@@ -302,6 +302,9 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   hp.o = o; hp.gate = gate; hp.ss = ss;
   hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
   hp.active = active;
+  // a multi-token step that keeps its state (the sequential-scan prefill) rolls the window
+  // by all T tokens after the state write, in the same launch
+  if (roll) hp.win_commit = win;
   r = timed(m, KDA_K_HEAD, s, rec, [&] { return launch_head(hp, s); });
   if (r) return r;
 
@@ -538,6 +541,29 @@ int static_scratch(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return KDA_OK;
+}
+
+// Sequential-scan prefill: tokens in blocks of Tc per sequence (B * Tc <= 64 columns, the
+// matrix-core projections' range, or Tc = 1 for wide batches); per block the per-layer
+// workspace of B * Tc columns, the activated q|k|v, and staging rows for the block's input
+// and output ([B][Tc][D] each).
+struct ScanLayout {
+  int Tc = 1;
+  WsLayout wl;
+  size_t act = 0, xs = 0, ys = 0, total = 0;
+};
+
+ScanLayout scan_layout(const kda_model* m, int64_t B, int64_t L) {
+  ScanLayout s;
+  s.Tc = (int)std::max<int64_t>(1, std::min<int64_t>(L, 64 / B));
+  const int64_t N = B * s.Tc;
+  s.wl = ws_layout(m, N);
+  size_t off = s.wl.total;
+  s.act = off; off = align_up(off + (size_t)N * m->C * 4, 256);
+  s.xs = off;  off = align_up(off + (size_t)N * m->d.d_model * 4, 256);
+  s.ys = off;  off = align_up(off + (size_t)N * m->d.d_model * 4, 256);
+  s.total = off;
+  return s;
 }
 
 // A one-launch step whose wait between blocks ran out left the caller's state partly
@@ -832,6 +858,7 @@ size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t to
   if (op == KDA_OP_DECODE) return ws_layout(m, batch).total;
   if (op == KDA_OP_VERIFY) return ws_layout(m, (int64_t)batch * tokens).total;
   if (op == KDA_OP_PREFILL) return pf_layout(m, batch, tokens).total;
+  if (op == KDA_OP_SCAN) return scan_layout(m, batch, tokens).total;
   return 0;
 }
 
@@ -998,6 +1025,44 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, si
     hp.win_commit = win;      // the window roll runs in the same launch, after the replay
     r = timed(m, KDA_K_COMMIT, s, m->timing, [&] { return launch_head(hp, s); });
     if (r) return r;
+  }
+  return KDA_OK;
+}
+
+int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
+                     const kda_state* st, void* ws_dev, size_t ws_bytes, void* stream) {
+  if (!m || !x_dev || !y_dev || !ws_dev) return fail(KDA_E_ARG, "null pointer");
+  int r = check_state(m, st);
+  if (r) return r;
+  if (L < 1 || L > (1 << 30)) return fail(KDA_E_SHAPE, "L must be >= 1");
+  if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(ws_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
+  const int B = st->batch;
+  const ScanLayout sl = scan_layout(m, B, L);
+  if (ws_bytes < sl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, sl.total);
+  r = check_poison(m);
+  if (r) return r;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = static_cast<char*>(ws_dev);
+  const int D = m->d.d_model;
+  float* xs = reinterpret_cast<float*>(ws + sl.xs);
+  float* ys = reinterpret_cast<float*>(ws + sl.ys);
+  float* proj = reinterpret_cast<float*>(ws + sl.wl.proj);
+  float* ag = reinterpret_cast<float*>(ws + sl.wl.ag);
+  float* act = reinterpret_cast<float*>(ws + sl.act);
+  for (int64_t t0 = 0; t0 < L; t0 += sl.Tc) {
+    const int T = (int)std::min<int64_t>(sl.Tc, L - t0);
+    // the block's rows [B][T][D], gathered from x [B][L][D]
+    KDA_HIP(hipMemcpy2DAsync(xs, (size_t)T * D * 4, x_dev + t0 * D, (size_t)L * D * 4,
+                             (size_t)T * D * 4, B, hipMemcpyDeviceToDevice, s));
+    for (int l = 0; l < m->d.n_layers; ++l) {
+      const float* xin = (l == 0 || !m->d.prenorm_residual) ? xs : ys;
+      r = enqueue_layer(m, l, xin, ys, B, T, st->S_dev + l * state_layer_stride(m, B),
+                        st->conv_dev + l * win_layer_stride(m, B), proj, ag, act, sl.wl, ws,
+                        true, s, m->timing, nullptr, true);
+      if (r) return r;
+    }
+    KDA_HIP(hipMemcpy2DAsync(y_dev + t0 * D, (size_t)L * D * 4, ys, (size_t)T * D * 4,
+                             (size_t)T * D * 4, B, hipMemcpyDeviceToDevice, s));
   }
   return KDA_OK;
 }

@@ -425,16 +425,17 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     const int wid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
     for (int i = wid * 64 + lane; i < C * P.B; i += nwave * 64) {
       const int sb = i / C, c = i - sb * C;
-      const int a = min(max(P.ntok[sb], 1), P.T);
+      const int a = P.ntok ? min(max(P.ntok[sb], 1), P.T) : P.T;
       float* z = P.win_commit + (size_t)sb * 3 * C + c;
-      float seq[3 + 8];
-      seq[0] = z[0];
-      seq[1] = z[C];
-      seq[2] = z[2 * C];
-      for (int t = 0; t < a; ++t) seq[3 + t] = P.proj[(size_t)(sb * P.T + t) * P.proj_stride + c];
-      z[0] = seq[a];
-      z[C] = seq[a + 1];
-      z[2 * C] = seq[a + 2];
+      // row j of the new window is element a + j of (window rows 0..2, p_0 .. p_{a-1})
+      float nz[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        nz[j] = a + j < 3 ? z[(size_t)(a + j) * C]
+                          : P.proj[(size_t)(sb * P.T + a + j - 3) * P.proj_stride + c];
+      z[0] = nz[0];
+      z[C] = nz[1];
+      z[2 * C] = nz[2];
     }
   }
 }
@@ -459,17 +460,20 @@ __global__ void conv_seq_kernel(const float* __restrict__ plog, int stride,
   const float* z = win + (size_t)b * 3 * C + c;
   float z0 = z[0], z1 = z[C], z2 = z[2 * C];
   const float4 w = *reinterpret_cast<const float4*>(conv_w + (size_t)c * 4);
-  float p[8];
+  // tokens in groups of 8, each group's projections requested together
+  for (int t0 = 0; t0 < T; t0 += 8) {
+    float p[8];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) p[t] = plog[(size_t)(b * T + min(t, T - 1)) * stride + c];
+    for (int t = 0; t < 8; ++t) p[t] = plog[(size_t)(b * T + min(t0 + t, T - 1)) * stride + c];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    if (t < T) {
-      const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * p[t];
-      z0 = z1;
-      z1 = z2;
-      z2 = p[t];
-      act[(size_t)(b * T + t) * C + c] = silu_f(y);
+    for (int t = 0; t < 8; ++t) {
+      if (t0 + t < T) {
+        const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * p[t];
+        z0 = z1;
+        z1 = z2;
+        z2 = p[t];
+        act[(size_t)(b * T + t0 + t) * C + c] = silu_f(y);
+      }
     }
   }
 }
