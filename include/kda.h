@@ -51,7 +51,7 @@ typedef enum {
   KDA_E_UNSUPPORTED = 7
 } kda_status;
 
-typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_Q8_0 = 2 } kda_dtype;
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1, KDA_Q8_0 = 2, KDA_MXFP4 = 3 } kda_dtype;
 
 typedef enum { KDA_OP_DECODE = 0, KDA_OP_VERIFY = 1, KDA_OP_PREFILL = 2, KDA_OP_SCAN = 3 } kda_op;
 
@@ -87,6 +87,18 @@ const char* kda_last_error(void);
  *              q = clamp(round_half_away(fp32(x / d16)), -127, 127), all q = 0 if d16 = 0.
  *            Device layout: a plane of rows*cols bytes holding q+128, then (at the next
  *            256-byte boundary) a plane of rows*(cols/32) fp16 scales.  cols % 32 == 0.
+ * KDA_MXFP4: one of the 4-bit block formats the quant-format commit of torad-labs/llama.cpp
+ *            PR #84 ranks at the KDA projection shapes, as the OCP Microscaling (MX)
+ *            specification v1.0 defines it: blocks of 32 consecutive values along a row
+ *            share an E8M0 scale X = 2^s, s = floor(log2(max|x|)) - 2 (clamped to
+ *            [-127, 127]; -127 for a block of zeros); each element is the E2M1 value
+ *            (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives) nearest to x / X, ties to
+ *            the even mantissa bit, clamped to +-6; code = sign << 3 | grid index.
+ *            Device layout: rows*cols/2 bytes of codes (codes 2i and 2i+1 of a row in
+ *            byte i, low nibble first), then (at the next 256-byte boundary) a plane of
+ *            rows*(cols/32) scale bytes s + 127.  cols % 32 == 0.  Decode and verify run
+ *            it through the per-layer kernels (vector dots, as the page notes for one
+ *            row); the one-launch decode and the chunked prefill do not take it.
  * ---------------------------------------------------------------------------------- */
 /* Bytes a packed [rows][cols] matrix occupies (0 on an invalid request). */
 size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols);
@@ -109,6 +121,11 @@ int kda_pack_device(int dtype, const float* src_dev, int64_t rows, int64_t cols,
  * on `stream` and unpacked on the host before the call returns. */
 int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_host,
                     int8_t* qs_host, void* stream);
+
+/* Canonical view of an MXFP4-packed matrix in host memory: e8m0_host [rows][cols/32] (the
+ * scale bytes s + 127) and codes_host [rows][cols] (one 4-bit code a byte).  Synchronous. */
+int kda_unpack_mxfp4(const void* packed_dev, int64_t rows, int64_t cols, uint8_t* e8m0_host,
+                     uint8_t* codes_host, void* stream);
 
 /* The same view written to device memory (d16_dev, qs_dev), asynchronous on `stream`. */
 int kda_unpack_q8_0_device(const void* packed_dev, int64_t rows, int64_t cols,

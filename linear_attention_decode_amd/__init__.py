@@ -14,7 +14,7 @@ import ctypes as C
 from typing import Dict, List, Optional, Sequence
 
 from . import _lib
-from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_OP_DECODE, KDA_OP_PREFILL, KDA_OP_SCAN,  # noqa: F401
+from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_MXFP4, KDA_OP_DECODE, KDA_OP_PREFILL, KDA_OP_SCAN,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
                    KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, KDA_K_GEMM, KDA_K_CHUNK,
                    KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError,
@@ -83,6 +83,17 @@ def kda_unpack_q8_0(packed, rows: int, cols: int, stream=None):
     _lib.call("kda_unpack_q8_0", _p(packed), rows, cols, d16.ctypes.data_as(C.c_void_p),
               qs.ctypes.data_as(C.c_void_p), _s(stream))
     return d16, qs
+
+
+def kda_unpack_mxfp4(packed, rows: int, cols: int, stream=None):
+    """Canonical view of an MXFP4-packed matrix in host memory: (e8m0 uint8 numpy
+    [rows][cols/32], codes uint8 numpy [rows][cols]).  Synchronous."""
+    import numpy as np
+    e = np.empty((rows, cols // 32), dtype=np.uint8)
+    c = np.empty((rows, cols), dtype=np.uint8)
+    _lib.call("kda_unpack_mxfp4", _p(packed), rows, cols, e.ctypes.data_as(C.c_void_p),
+              c.ctypes.data_as(C.c_void_p), _s(stream))
+    return e, c
 
 
 def kda_unpack_q8_0_device(packed, rows: int, cols: int, stream=None):

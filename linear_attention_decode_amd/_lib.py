@@ -11,13 +11,13 @@ LIB_PATH = os.path.join(_PKG, "libkda.so")
 
 KDA_OK, KDA_E_ARG, KDA_E_SHAPE, KDA_E_ALIGN, KDA_E_DTYPE, KDA_E_WORKSPACE, KDA_E_HIP, \
     KDA_E_UNSUPPORTED = range(8)
-KDA_F32, KDA_BF16, KDA_Q8_0 = 0, 1, 2
+KDA_F32, KDA_BF16, KDA_Q8_0, KDA_MXFP4 = 0, 1, 2, 3
 KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL, KDA_OP_SCAN = 0, 1, 2, 3
 KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE = 0, 1, 2, 3, 4
 KDA_Q_PERSISTENT = 0
 KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, \
     KDA_K_GEMM, KDA_K_CHUNK = range(9)
-DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0}
+DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0, "mxfp4": KDA_MXFP4}
 KDA_GATE_KDA, KDA_GATE_SAFE, KDA_GATE_SCALAR = 0, 1, 2
 GATES = {"kda": KDA_GATE_KDA, "safe": KDA_GATE_SAFE, "scalar": KDA_GATE_SCALAR}
 
@@ -27,7 +27,7 @@ EXPORTS = (
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
     "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
-    "kda_decode_step_static", "kda_prefill_scan",
+    "kda_decode_step_static", "kda_prefill_scan", "kda_unpack_mxfp4",
 )
 
 
@@ -75,6 +75,7 @@ def lib():
             "kda_pack_device": (C.c_int, [C.c_int, vp, i64, i64, vp, vp]),
             "kda_unpack_q8_0": (C.c_int, [vp, i64, i64, vp, vp, vp]),
             "kda_unpack_q8_0_device": (C.c_int, [vp, i64, i64, vp, vp, vp]),
+            "kda_unpack_mxfp4": (C.c_int, [vp, i64, i64, vp, vp, vp]),
             "kda_model_create": (C.c_int, [C.POINTER(KdaDims), C.POINTER(KdaLayer), C.POINTER(vp)]),
             "kda_model_destroy": (None, [vp]),
             "kda_model_set_option": (C.c_int, [vp, C.c_int, i64]),

@@ -616,6 +616,36 @@ void host_pack_q8_0(const float* src, int64_t rows, int64_t cols, uint8_t* dst) 
     }
 }
 
+// MXFP4 on the host, the same rule as the device kernel pack_mxfp4 (pack.hip).
+uint32_t host_e2m1_code(float v) {
+  const float a = std::fabs(v);
+  const uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                       (a >= 3.5f) + (a > 5.0f);
+  return ((v < 0.0f && idx > 0) ? 8u : 0u) | idx;
+}
+
+void host_pack_mxfp4(const float* src, int64_t rows, int64_t cols, uint8_t* dst) {
+  const int64_t nb = cols / 32;
+  uint8_t* eplane = dst + mx4_scale_offset(rows, cols);
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t j = 0; j < nb; ++j) {
+      const float* x = src + r * cols + j * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i) amax = std::fmax(amax, std::fabs(x[i]));
+      int s = -127;
+      if (amax > 0.0f) {
+        int ex = 0;
+        (void)std::frexp(amax, &ex);
+        s = std::min(std::max(ex - 1 - 2, -127), 127);
+      }
+      uint8_t* q = dst + r * (cols / 2) + j * 16;
+      for (int i = 0; i < 16; ++i)
+        q[i] = (uint8_t)(host_e2m1_code(std::ldexp(x[2 * i], -s)) |
+                         (host_e2m1_code(std::ldexp(x[2 * i + 1], -s)) << 4));
+      eplane[r * nb + j] = (uint8_t)(s + 127);
+    }
+}
+
 }  // namespace
 
 // =======================================================================================
@@ -647,21 +677,26 @@ size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols) {
     case KDA_Q8_0:
       if (cols % 32) return 0;
       return q8_scale_offset(rows, cols) + (size_t)rows * (cols / 32) * 2;
+    case KDA_MXFP4:
+      if (cols % 32) return 0;
+      return mx4_scale_offset(rows, cols) + (size_t)rows * (cols / 32);
     default: return 0;
   }
 }
 
 int kda_pack(int dtype, const float* src_host, int64_t rows, int64_t cols, void* dst_dev,
              void* stream) {
-  if (dtype < KDA_F32 || dtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
+  if (dtype < KDA_F32 || dtype > KDA_MXFP4) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
   if (!src_host || !dst_dev) return fail(KDA_E_ARG, "null pointer");
   if (rows <= 0 || cols <= 0) return fail(KDA_E_SHAPE, "rows/cols must be positive");
-  if (dtype == KDA_Q8_0 && cols % 32) return fail(KDA_E_SHAPE, "Q8_0 needs cols %% 32 == 0");
+  if ((dtype == KDA_Q8_0 || dtype == KDA_MXFP4) && cols % 32)
+    return fail(KDA_E_SHAPE, "block formats need cols %% 32 == 0");
   if (!aligned16(dst_dev)) return fail(KDA_E_ALIGN, "dst_dev must be 16-byte aligned");
   const size_t bytes = kda_packed_bytes(dtype, rows, cols);
   std::vector<uint8_t> buf(bytes, 0);
   if (dtype == KDA_F32) std::memcpy(buf.data(), src_host, (size_t)rows * cols * 4);
   else if (dtype == KDA_BF16) host_pack_bf16(src_host, reinterpret_cast<uint16_t*>(buf.data()), rows * cols);
+  else if (dtype == KDA_MXFP4) host_pack_mxfp4(src_host, rows, cols, buf.data());
   else host_pack_q8_0(src_host, rows, cols, buf.data());
   hipStream_t s = (hipStream_t)stream;
   KDA_HIP(hipMemcpyAsync(dst_dev, buf.data(), bytes, hipMemcpyHostToDevice, s));
@@ -671,10 +706,11 @@ int kda_pack(int dtype, const float* src_host, int64_t rows, int64_t cols, void*
 
 int kda_pack_device(int dtype, const float* src_dev, int64_t rows, int64_t cols, void* dst_dev,
                     void* stream) {
-  if (dtype < KDA_F32 || dtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
+  if (dtype < KDA_F32 || dtype > KDA_MXFP4) return fail(KDA_E_DTYPE, "unknown dtype %d", dtype);
   if (!src_dev || !dst_dev) return fail(KDA_E_ARG, "null pointer");
   if (rows <= 0 || cols <= 0) return fail(KDA_E_SHAPE, "rows/cols must be positive");
-  if (dtype == KDA_Q8_0 && cols % 32) return fail(KDA_E_SHAPE, "Q8_0 needs cols %% 32 == 0");
+  if ((dtype == KDA_Q8_0 || dtype == KDA_MXFP4) && cols % 32)
+    return fail(KDA_E_SHAPE, "block formats need cols %% 32 == 0");
   if (!aligned16(src_dev) || !aligned16(dst_dev)) return fail(KDA_E_ALIGN, "pointers must be 16-byte aligned");
   KDA_HIP(launch_pack(dtype, src_dev, rows, cols, dst_dev, (hipStream_t)stream));
   return KDA_OK;
@@ -695,6 +731,21 @@ int kda_unpack_q8_0(const void* packed_dev, int64_t rows, int64_t cols, uint16_t
   return KDA_OK;
 }
 
+int kda_unpack_mxfp4(const void* packed_dev, int64_t rows, int64_t cols, uint8_t* e8m0_host,
+                     uint8_t* codes_host, void* stream) {
+  if (!packed_dev || !e8m0_host || !codes_host) return fail(KDA_E_ARG, "null pointer");
+  if (rows <= 0 || cols <= 0 || cols % 32) return fail(KDA_E_SHAPE, "bad MXFP4 shape");
+  const size_t bytes = kda_packed_bytes(KDA_MXFP4, rows, cols);
+  std::vector<uint8_t> buf(bytes);
+  hipStream_t s = (hipStream_t)stream;
+  KDA_HIP(hipMemcpyAsync(buf.data(), packed_dev, bytes, hipMemcpyDeviceToHost, s));
+  KDA_HIP(hipStreamSynchronize(s));
+  const size_t n = (size_t)rows * cols;
+  for (size_t i = 0; i < n; ++i) codes_host[i] = (buf[i / 2] >> (4 * (i & 1))) & 0x0Fu;
+  std::memcpy(e8m0_host, buf.data() + mx4_scale_offset(rows, cols), n / 32);
+  return KDA_OK;
+}
+
 int kda_unpack_q8_0_device(const void* packed_dev, int64_t rows, int64_t cols, uint16_t* d16_dev,
                            int8_t* qs_dev, void* stream) {
   if (!packed_dev || !d16_dev || !qs_dev) return fail(KDA_E_ARG, "null pointer");
@@ -707,14 +758,14 @@ int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** 
   if (!dims || !layers || !out) return fail(KDA_E_ARG, "null pointer");
   *out = nullptr;
   const kda_dims& d = *dims;
-  if (d.wtype < KDA_F32 || d.wtype > KDA_Q8_0) return fail(KDA_E_DTYPE, "unknown wtype %d", d.wtype);
+  if (d.wtype < KDA_F32 || d.wtype > KDA_MXFP4) return fail(KDA_E_DTYPE, "unknown wtype %d", d.wtype);
   if (d.n_layers < 1 || d.n_heads < 1 || d.d_model < 1) return fail(KDA_E_SHAPE, "sizes must be positive");
   if (d.d_k != d.d_v) return fail(KDA_E_SHAPE, "d_k must equal d_v");
   if (d.d_k != 64 && d.d_k != 128) return fail(KDA_E_SHAPE, "d_k must be 64 or 128");
   if (d.conv_k != 4) return fail(KDA_E_SHAPE, "conv_k must be 4");
   if (d.rank_f < 1 || d.rank_g < 1 || d.rank_f > 256 || d.rank_g > 256)
     return fail(KDA_E_SHAPE, "ranks must be in 1..256");
-  const int gran = d.wtype == KDA_Q8_0 ? 32 : (d.wtype == KDA_BF16 ? 8 : 4);
+  const int gran = (d.wtype == KDA_Q8_0 || d.wtype == KDA_MXFP4) ? 32 : (d.wtype == KDA_BF16 ? 8 : 4);
   if (d.d_model % gran || d.rank_f % gran || d.rank_g % gran || (d.n_heads * d.d_v) % gran)
     return fail(KDA_E_SHAPE, "input dims must be multiples of %d for this weight type", gran);
   if (d.d_model % 4) return fail(KDA_E_SHAPE, "d_model %% 4 != 0");

@@ -24,6 +24,8 @@ template <>
 struct WFmt<kBF16> { static constexpr int kElems = 8; static constexpr int kBytes = 2; };
 template <>
 struct WFmt<kQ8> { static constexpr int kElems = 16; static constexpr int kBytes = 1; };
+template <>
+struct WFmt<kMX4> { static constexpr int kElems = 32; static constexpr int kBytes = 1; };
 
 // Dot of one 16-byte weight chunk with 16/8/4 LDS inputs (Q8_0: biased, un-scaled).
 template <int WT>
@@ -67,9 +69,8 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
   __shared__ float scal[NC * kGemvMaxHeads];                   // per-column / per-head scales
   __shared__ float red[4 * NC];                                // [4][NC]
   constexpr int EL = WFmt<WT>::kElems;
-  constexpr int BY = WFmt<WT>::kBytes;
   // 16-byte chunks per lane per row kept in flight: a 2048-wide row in one pass
-  constexpr int U = (WT == kQ8) ? 2 : (WT == kBF16 ? 4 : 8);
+  constexpr int U = (WT == kMX4) ? 1 : (WT == kQ8) ? 2 : (WT == kBF16 ? 4 : 8);
   constexpr int RPW = kGemvRowsPerWave;
   const int K = P.K;
   const int K4 = K / 4;
@@ -96,8 +97,10 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
         wv[r][u] = make_uint4(0, 0, 0, 0);
         dsc[r][u] = 0.0f;
         if (row < sg.rows && c < nchunk) {
-          wv[r][u] = load_stream16(sg.m.w + ((size_t)row * K + (size_t)c * EL) * BY);
+          wv[r][u] = load_stream16(sg.m.w + ((size_t)row * nchunk + c) * 16);
           if constexpr (WT == kQ8) dsc[r][u] = __half2float(sg.m.d[(size_t)row * (K / 32) + (c >> 1)]);
+          // MXFP4: the block scale 2^(e - 127), halved for the doubled element values
+          if constexpr (WT == kMX4) dsc[r][u] = __builtin_amdgcn_ldexpf(1.0f, (int)sg.m.e[(size_t)row * (K / 32) + c] - 128);
         }
       }
     }
@@ -271,11 +274,15 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
           if (c < nchunk) {
 #pragma unroll
             for (int n = 0; n < NC; ++n) {
-              const float d = chunk_dot<WT>(wv[r][u], xs + n * K + c * EL);
-              if constexpr (WT == kQ8)
-                acc[r][n] += dsc[r][u] * (d - 128.0f * xsum[n * (K / 16) + c]);
-              else
-                acc[r][n] += d;
+              if constexpr (WT == kMX4) {
+                acc[r][n] = fmaf(dsc[r][u], mx4_chunk_dot2(wv[r][u], xs + n * K + c * EL), acc[r][n]);
+              } else {
+                const float d = chunk_dot<WT>(wv[r][u], xs + n * K + c * EL);
+                if constexpr (WT == kQ8)
+                  acc[r][n] += dsc[r][u] * (d - 128.0f * xsum[n * (K / 16) + c]);
+                else
+                  acc[r][n] += d;
+              }
             }
           }
         }
@@ -335,10 +342,12 @@ hipError_t launch_gemv(int wt, int prologue, const GemvParams& p, int grid, hipS
   if (prologue == kProX) {
     if (wt == kF32) return launch_nc<kF32, kProX>(p, grid, s);
     if (wt == kBF16) return launch_nc<kBF16, kProX>(p, grid, s);
+    if (wt == kMX4) return launch_nc<kMX4, kProX>(p, grid, s);
     return launch_nc<kQ8, kProX>(p, grid, s);
   }
   if (wt == kF32) return launch_nc<kF32, kProGatedNorm>(p, grid, s);
   if (wt == kBF16) return launch_nc<kBF16, kProGatedNorm>(p, grid, s);
+  if (wt == kMX4) return launch_nc<kMX4, kProGatedNorm>(p, grid, s);
   return launch_nc<kQ8, kProGatedNorm>(p, grid, s);
 }
 

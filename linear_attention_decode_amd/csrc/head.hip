@@ -28,6 +28,8 @@ template <>
 struct HFmt<kBF16> { static constexpr int kElems = 8; static constexpr int kBytes = 2; };
 template <>
 struct HFmt<kQ8> { static constexpr int kElems = 16; static constexpr int kBytes = 1; };
+template <>
+struct HFmt<kMX4> { static constexpr int kElems = 32; static constexpr int kBytes = 1; };
 
 // Dot of one 16-byte chunk of a packed row with LDS inputs (Q8_0: q = byte - 128, unscaled).
 template <int WT>
@@ -73,7 +75,6 @@ constexpr int kGateCols = 16;    // columns staged per round (a multiple of ever
 template <int WT, int CPR>
 __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P) {
   constexpr int EL = HFmt<WT>::kElems;
-  constexpr int BY = HFmt<WT>::kBytes;
   __shared__ __align__(16) float s_lr[kGateCols][2 * kMaxRank];
   const int tid = threadIdx.x;
   // forget rows (one per key channel, or one per head for the scalar gate), then gate rows
@@ -90,8 +91,9 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
   if (valid) {
     const PackedMat M = f ? P.fb : P.gb;
     const int r = f ? row : row - FR;
-    w = *reinterpret_cast<const uint4*>(M.w + ((size_t)r * rank + (size_t)c * EL) * BY);
+    w = *reinterpret_cast<const uint4*>(M.w + ((size_t)r * (rank / EL) + c) * 16);
     if constexpr (WT == kQ8) sc = __half2float(M.d[(size_t)r * (rank / 32) + (c >> 1)]);
+    if constexpr (WT == kMX4) sc = __builtin_amdgcn_ldexpf(1.0f, (int)M.e[(size_t)r * (rank / 32) + c] - 128);
     if (f) {
       bias = P.dt_bias[row];
       ah = P.a_log[scalar ? row : row / P.dk];
@@ -132,7 +134,10 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
         const int nn = nb + g;
         float part = 0.0f;
         if (valid && nn < nc) {
-          part = hchunk_dot<WT>(w, (f ? s_lr[nn] : s_lr[nn] + rank) + c * EL);
+          if constexpr (WT == kMX4)
+            part = sc * mx4_chunk_dot2(w, (f ? s_lr[nn] : s_lr[nn] + rank) + c * EL);
+          else
+            part = hchunk_dot<WT>(w, (f ? s_lr[nn] : s_lr[nn] + rank) + c * EL);
           if constexpr (WT == kQ8) part *= sc;
         }
         part = group_sum(part, CPR);
@@ -253,8 +258,7 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
 
 template <int WT>
 static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
-  constexpr int BY = HFmt<WT>::kBytes;
-  const int cpr = p.rank * BY / 16;
+  const int cpr = p.rank / HFmt<WT>::kElems;
   const int items = ((p.gate == kGateScalar ? p.K / p.dk : p.K) + p.V) * cpr;
   const dim3 grid((items + kGateThreads - 1) / kGateThreads,
                   std::min(8, (p.N + kGateCols - 1) / kGateCols));
@@ -281,6 +285,8 @@ hipError_t launch_gates(const GatesParams& p, hipStream_t s) {
     launch_gates_wt<kF32>(p, s);
   else if (p.wt == kBF16)
     launch_gates_wt<kBF16>(p, s);
+  else if (p.wt == kMX4)
+    launch_gates_wt<kMX4>(p, s);
   else
     launch_gates_wt<kQ8>(p, s);
   return hipGetLastError();
@@ -288,9 +294,9 @@ hipError_t launch_gates(const GatesParams& p, hipStream_t s) {
 
 bool head_supported(int dk, int wt, int rank_f, int rank_g) {
   (void)dk;
-  const int by = wt == kF32 ? 4 : (wt == kBF16 ? 2 : 1);
-  if (rank_f != rank_g || rank_f > kMaxRank) return false;
-  const int cpr = rank_f * by / 16;
+  const int el = wt == kF32 ? 4 : (wt == kBF16 ? 8 : (wt == kMX4 ? 32 : 16));
+  if (rank_f != rank_g || rank_f > kMaxRank || rank_f % el) return false;
+  const int cpr = rank_f / el;
   return cpr >= 1 && cpr <= 16 && (cpr & (cpr - 1)) == 0;
 }
 

@@ -9,7 +9,7 @@
 
 namespace kda {
 
-enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2 };
+enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2, kMX4 = 3 };
 enum GateForm { kGateKda = 0, kGateSafe = 1, kGateScalar = 2 };
 
 // A packed weight matrix as the kernels see it.
@@ -21,11 +21,44 @@ inline size_t q8_scale_offset(int64_t rows, int64_t cols) {
   return align_up((size_t)rows * (size_t)cols, 256);
 }
 
+// Byte offset of the MXFP4 scale plane inside a packed matrix (after rows*cols/2 bytes of
+// 4-bit codes).
+inline size_t mx4_scale_offset(int64_t rows, int64_t cols) {
+  return align_up((size_t)rows * (size_t)cols / 2, 256);
+}
+
 inline PackedMat packed_view(const void* base, int wt, int64_t rows, int64_t cols) {
   PackedMat m;
   m.w = static_cast<const uint8_t*>(base);
   if (wt == kQ8) m.d = reinterpret_cast<const __half*>(m.w + q8_scale_offset(rows, cols));
+  if (wt == kMX4) m.e = m.w + mx4_scale_offset(rows, cols);
   return m;
+}
+
+// 16 bytes of MXFP4 codes (32 elements, code 2i in the low nibble of byte i) times 32
+// inputs: sum over the elements of twice the E2M1 value times x (the caller halves the
+// block scale).  The doubled magnitudes 0, 1, 2, 3, 4, 6, 8, 12 of codes & 7 come from a
+// byte permute of two constant words; the sign (code bit 3) flips the float's sign bit.
+__device__ __forceinline__ float mx4_chunk_dot2(const uint4 w, const float* __restrict__ x) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // codes of elements 8 i + 2 k + half, k = 0..3, one per byte
+      const uint32_t c = (wd[i] >> (4 * half)) & 0x0F0F0F0Fu;
+      const uint32_t mag = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, c & 0x07070707u);
+      const uint32_t sg = (c & 0x08080808u) << 4;      // sign into bit 7 of each byte
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = __uint_as_float(__float_as_uint((float)((mag >> (8 * k)) & 0xffu)) ^
+                                        (((sg >> (8 * k)) & 0x80u) << 24));
+        s = fmaf(v, x[8 * i + 2 * k + half], s);
+      }
+    }
+  }
+  return s;
 }
 
 // ---------------------------------------------------------------------------------------

@@ -58,6 +58,46 @@ __global__ void pack_q8_0(const float* __restrict__ src, int64_t rows, int64_t c
   dplane[b] = h;
 }
 
+// MXFP4 (OCP Microscaling format v1.0), one thread per block of 32: s = floor(log2 amax) - 2
+// clamped to [-127, 127], X = 2^s; each element the E2M1 value nearest to x / X (ties to
+// the even mantissa bit), clamped to 6: with a = |x / X| the grid index is the count of
+// the thresholds 0.25 < a, 0.75 <= a, 1.25 < a, 1.75 <= a, 2.5 < a, 3.5 <= a, 5 < a that
+// hold (the midpoints of the grid 0, .5, 1, 1.5, 2, 3, 4, 6; at a midpoint the index with
+// mantissa bit 0 wins).  Code = sign << 3 | index (no sign on 0); codes 2 i, 2 i + 1 of a
+// block share byte i (low nibble first); the scale byte is s + 127.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = fabsf(v);
+  const uint32_t idx = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) +
+                       (a >= 3.5f) + (a > 5.0f);
+  return ((v < 0.0f && idx > 0) ? 8u : 0u) | idx;
+}
+
+__global__ void pack_mxfp4(const float* __restrict__ src, int64_t rows, int64_t cols,
+                           uint8_t* __restrict__ codes, uint8_t* __restrict__ eplane) {
+  const int64_t nb_row = cols / 32;
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= rows * nb_row) return;
+  const int64_t r = b / nb_row, j = b - r * nb_row;
+  const float* x = src + r * cols + j * 32;
+  float v[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    v[i] = x[i];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  int s = -127;
+  if (amax > 0.0f) s = min(max(__builtin_amdgcn_frexp_expf(amax) - 1 - 2, -127), 127);
+  uint8_t* q = codes + r * (cols / 2) + j * 16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t lo = e2m1_code(__builtin_amdgcn_ldexpf(v[2 * i], -s));
+    const uint32_t hi = e2m1_code(__builtin_amdgcn_ldexpf(v[2 * i + 1], -s));
+    q[i] = (uint8_t)(lo | (hi << 4));
+  }
+  eplane[b] = (uint8_t)(s + 127);
+}
+
 __global__ void unpack_q8_0(const uint8_t* __restrict__ qs, const __half* __restrict__ dplane,
                             int64_t rows, int64_t cols, uint16_t* __restrict__ d16,
                             int8_t* __restrict__ qo) {
@@ -76,6 +116,9 @@ hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, voi
     pack_copy_f32<<<grid_for(n, 256), 256, 0, s>>>(src, static_cast<float*>(dst), n);
   } else if (wt == kBF16) {
     pack_bf16<<<grid_for(n, 256), 256, 0, s>>>(src, static_cast<uint16_t*>(dst), n);
+  } else if (wt == kMX4) {
+    uint8_t* q = static_cast<uint8_t*>(dst);
+    pack_mxfp4<<<grid_for(n / 32, 128), 128, 0, s>>>(src, rows, cols, q, q + mx4_scale_offset(rows, cols));
   } else {
     uint8_t* q = static_cast<uint8_t*>(dst);
     __half* d = reinterpret_cast<__half*>(q + q8_scale_offset(rows, cols));

@@ -8,8 +8,10 @@
 namespace kda {
 
 struct PackedMat {
-  const uint8_t* w = nullptr;   // F32/BF16 data, or the Q8_0 byte plane (q + 128)
+  const uint8_t* w = nullptr;   // F32/BF16 data, the Q8_0 byte plane (q + 128), or the
+                                // MXFP4 code plane (two 4-bit codes a byte)
   const __half* d = nullptr;    // Q8_0 scale plane [rows][cols/32]
+  const uint8_t* e = nullptr;   // MXFP4 scale plane [rows][cols/32] (E8M0: 2^(e - 127))
 };
 
 // ---------------------------------------------------------------------------------------

@@ -36,6 +36,18 @@
 #define KDA_GLOBAL __attribute__((address_space(1)))
 #define KDA_CONST __attribute__((address_space(4)))
 
+// Phase timestamps for profiling builds (-DKDA_TRACE): thread 0 of every block records the
+// 100 MHz real-time counter at up to 8 points of each layer in LDS, and the block copies
+// them to a device table when it leaves; kda_trace_read copies the table out.  Product
+// builds compile none of it.
+#ifdef KDA_TRACE
+constexpr int kTraceLayers = 64, kTraceSlots = 8;
+#define KDA_STAMP(l, k) \
+  do { if (threadIdx.x == 0 && (l) < kTraceLayers) sm.stamps[(l)][(k)] = __builtin_amdgcn_s_memrealtime(); } while (0)
+#else
+#define KDA_STAMP(l, k) do { } while (0)
+#endif
+
 namespace kda {
 
 constexpr int kPT = 256;         // threads per block
@@ -495,6 +507,9 @@ struct Smem {
   alignas(16) int8_t gpl[4 * 256];   // head block: planes of [f_lr | g_lr]; [3] = 0
   float ginv[8];                     // head block: 1 / scale of each 32-element block of them
   alignas(16) int any[2][4];       // block_any: per-wave votes, two alternating sets
+#ifdef KDA_TRACE
+  uint64_t stamps[kTraceLayers][kTraceSlots];
+#endif
 };
 
 // Block-wide OR of pred (every thread of the block calls it): each wave's vote goes to LDS,
@@ -552,6 +567,7 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   float* win = P.win + (size_t)l * 3 * C;
   float v[NV];
   int bad = 0;
+  KDA_STAMP(l, 0);
   if (l == 0) {
 #pragma unroll
     for (int k = 0; k < NV; ++k) v[k] = *gp(P.x_in + run_elem(k, wave, lane));
@@ -561,8 +577,10 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
     // land, the fetch that brings them is also their detection
     uint32_t pend[3] = {0u, 0u, 0u};
     if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag - 1u, pend))) return false;
+    KDA_STAMP(l, 1);
     bad = !poll_runs<NV>(P.xbuf + (size_t)((l - 1) & 1) * D, tag - 1u, v, P);
     keep_live(pend);
+    KDA_STAMP(l, 2);
   }
   float ss = 0.0f;
 #pragma unroll
@@ -578,7 +596,9 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
 #pragma unroll
   for (int tile = 0; tile < kPTiles; ++tile)
     if (tile < ntiles) sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
+  KDA_STAMP(l, 3);
   if (block_any(sm, 1, bad)) return false;
+  KDA_STAMP(l, 4);
   // thread t finishes row p0 + t: RMSNorm scale, conv + SiLU + window roll for q/k/v channels
   if (tid < rows) {
     const int row = R.p0 + tid;
@@ -602,6 +622,7 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
       *gpw(z + 2 * C) = pre;
     }
   }
+  KDA_STAMP(l, 5);
   if (l + 1 < P.n_layers) {
     hold_prefetch();
     issue_proj<U>(P, Lt[l + 1], win + 3 * C, R.p0, R.p1, pr);
@@ -629,6 +650,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   // every input is requested at once; the low-rank rows and beta (finished first by their
   // projection blocks) are waited for before the gates, q / k / v after them
   constexpr int i_lr = 2 * dk + kHCols;          // first low-rank input
+  KDA_STAMP(l, 0);
   uint64_t w[3];
   const uint64_t* src[3];
 #pragma unroll
@@ -666,6 +688,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   };
   {
     const int bad = !wait_slots(true);
+    KDA_STAMP(l, 1);
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int i = tid + k * kPT;
@@ -697,6 +720,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
       }
     }
     if (block_any(sm, 0, bad)) return false;
+    KDA_STAMP(l, 2);
   }
   // request the q/k/v words again now: the round trip overlaps the gates below, and the
   // replies are merged only after them.  Only slots that hold q/k/v inputs are requested: a
@@ -751,6 +775,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     if (g < 2) sm.s_al[16 * (wave + 4 * g) + m] = al;
     else if (g == 2) sm.s_gt[16 * wave + m] = gt;
   }
+  KDA_STAMP(l, 3);
   {
     // q, k, v
 #pragma unroll
@@ -763,6 +788,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
       if (i < i_lr) sm.s_in[i] = __uint_as_float((uint32_t)w[k]);
     }
     if (block_any(sm, 1, bad)) return false;
+    KDA_STAMP(l, 4);
   }
   // delta rule: lane (rg, cq) holds rows 8 rg .. + 8 of columns jl .. + 4 (block-local jl)
   const int rg = lane & 15, cq = lane >> 4;
@@ -822,6 +848,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     put(P.obuf + P.H * dv + (h * kHSplit + half) * 4 + wave, tag, tot);
     if (wave == 0) put(flag_slot(P, kFlagH, blockIdx.x), tag, 0.0f);
   }
+  KDA_STAMP(l, 5);
   // off the critical path: write the state back, request the next layer's
   float* Sb = Sl + (size_t)h * dk * dv + j;
 #pragma unroll
@@ -847,7 +874,9 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
   // once the first head block has posted, fetch the output words of the wave's heads and
   // their partials (lane kParts t + i: partial i of head 4 t + wave)
   uint32_t pend[3] = {0u, 0u, 0u};
+  KDA_STAMP(l, 0);
   if (block_any(sm, 0, wave0_wait_flags(P, kFlagH, kHSplit * P.H, tag, pend))) return false;
+  KDA_STAMP(l, 1);
   const bool has = lane < kParts * NT;
   const uint64_t* src = P.obuf + D + (4 * (has ? lane / kParts : 0) + wave) * kParts + lane % kParts;
   uint64_t pw = has ? peek(src) : tagged(tag, 0.0f);
@@ -861,6 +890,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
     }
   }
   keep_live(pend);
+  KDA_STAMP(l, 2);
   // the normalised heads (run t = head 4 t + wave), then their planes
   // lane kParts t ends up with head t's sum of squares; every lane computes a scale, lane
   // kParts t's is head t's
@@ -883,7 +913,9 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
 #pragma unroll
   for (int tile = 0; tile < kOTiles; ++tile)
     sm.part[(16 * tile + (lane & 15)) * 16 + 4 * wave + (lane >> 4)] = y[tile];
+  KDA_STAMP(l, 3);
   if (block_any(sm, 1, bad)) return false;
+  KDA_STAMP(l, 4);
   if (tid < 16 * kOTiles) {
     const int row = R.or0 + tid;
     const float4* q = reinterpret_cast<const float4*>(sm.part + 16 * tid);
@@ -895,6 +927,7 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
     put(P.xbuf + (size_t)(l & 1) * D + row, tag, xn);
     if (l + 1 == P.n_layers) *gpw(P.y_out + row) = xn;
   }
+  KDA_STAMP(l, 5);
   return true;
 }
 
@@ -946,10 +979,18 @@ __device__ __forceinline__ void run_role(const PersistParams& P, Smem& sm, int e
 }
 
 // U = D / 1024 (16-byte chunks per lane per row), CPR = rank / 16
+#ifdef KDA_TRACE
+__device__ uint64_t g_trace[kMaxPersistBlocks * kTraceLayers * kTraceSlots];
+#endif
+
 template <int U, int CPR>
 __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const PersistParams P) {
   __shared__ Smem sm;
   const int b = blockIdx.x;
+#ifdef KDA_TRACE
+  for (int i = threadIdx.x; i < kTraceLayers * kTraceSlots; i += kPT) (&sm.stamps[0][0])[i] = 0;
+  __syncthreads();
+#endif
   // a model whose earlier step failed a wait keeps its error word until the host resets it:
   // every block then leaves before it touches the state, the window or the output (the
   // word is requested first and looked at after the block's first weight requests)
@@ -957,6 +998,11 @@ __global__ __launch_bounds__(kPT, 1) void decode_persistent_kernel(const Persist
   if (b < kHSplit * P.H) run_role<U, CPR, 1>(P, sm, err0);
   else if (b >= P.o_first_block && b < P.o_first_block + P.o_blocks) run_role<U, CPR, 2>(P, sm, err0);
   else run_role<U, CPR, 0>(P, sm, err0);
+#ifdef KDA_TRACE
+  __syncthreads();
+  for (int i = threadIdx.x; i < kTraceLayers * kTraceSlots; i += kPT)
+    g_trace[(size_t)b * kTraceLayers * kTraceSlots + i] = (&sm.stamps[0][0])[i];
+#endif
 }
 
 // One thread per 16-byte chunk of the matrix-core order (persist.h): chunk
@@ -1048,6 +1094,17 @@ hipError_t launch_persistent(const PersistParams& p, int blocks, bool cooperativ
   if (cooperative) return hipLaunchCooperativeKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
   return hipLaunchKernel(fn, dim3(blocks), dim3(kPT), args, 0, s);
 }
+
+#ifdef KDA_TRACE
+}  // namespace kda
+// Copies the phase timestamps of the last one-launch step ([blocks][64 layers][8 points]
+// of 100 MHz counter values, 0 where a block recorded nothing).  Profiling builds only.
+extern "C" int kda_trace_read(void* host, size_t bytes) {
+  const size_t n = sizeof(kda::g_trace) < bytes ? sizeof(kda::g_trace) : bytes;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(kda::g_trace), n, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0 : 6;
+}
+namespace kda {
+#endif
 
 int persistent_max_blocks() {
   int dev = 0, cus = 0, per = 0;
