@@ -11,12 +11,15 @@ Prints ONE JSON line: tokens/s over K timed steps, HBM roofline of the dominant 
 (timed with hipEvents on the launch stream), and the CPU oracle on a bounded sample.
 
 Other workloads (--workload, one JSON line each, for the secondary measurements):
-  layer    one BF16 layer, B=1 decode (effective GB/s; the 38 MB set fits the MALL)
+  layer    one BF16 layer, B=1 decode (effective GB/s; the 38 MB set fits the MALL;
+           --copies 8 rotates 8 weight copies so that each step streams from HBM)
+  tiny     the D=256 fp32 layer (parity workload; wall time and the oracle timed multi-
+           and single-threaded)
   verify   the stack, B=8 sequences x T=4 tokens a step + commit of the accepted prefix
   prefill  one BF16 layer, B=4 x L=8192 chunked prefill (MFMA-bound)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload stack|layer|verify|prefill] [--per-layer]
+                    [--workload stack|layer|tiny|verify|prefill] [--per-layer] [--copies N]
 """
 from __future__ import annotations
 
@@ -83,8 +86,9 @@ def algorithmic_bytes(w) -> dict:
             "token_weights_state": weights_state * w.n_layers}
 
 
-def cpu_baseline(run, budget_s: float = 15.0):
-    """The float64 oracle, as it stands, on the first tokens of the same workload."""
+def cpu_baseline(run, budget_s: float = 15.0, single_thread: bool = False):
+    """The float64 oracle, as it stands, on the first tokens of the same workload (with
+    single_thread, also timed with its BLAS limited to one thread)."""
     import threadpoolctl
     from oracle import kda as ok
 
@@ -96,14 +100,30 @@ def cpu_baseline(run, budget_s: float = 15.0):
     log(f"[cpu] oracle weights prepared in {time.time() - t0:.1f}s")
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
+    res = _oracle_decode_rate(ok, layers, run, budget_s, threads)
+    if single_thread:
+        with threadpoolctl.threadpool_limits(1):
+            one = _oracle_decode_rate(ok, layers, run, budget_s / 2, 1)
+        res["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                                "sample": one["sample"]}
+    return res
+
+
+def _oracle_decode_rate(ok, layers, run, budget_s, threads):
+    w = run.workload
+    d = w.dims
     n = 0
     t0 = time.time()
     S = [[run.s0[l, 0].astype(np.float64)] for l in range(w.n_layers)]
     Z = [[np.zeros((3, d.conv_channels))] for _ in range(w.n_layers)]
     while True:
         xt = run.x[n % w.steps, 0, 0].astype(np.float64)[None, :]   # inputs reused cyclically
-        _, s_new, z_new = ok.stack_step(layers, xt, [S[l][0] for l in range(w.n_layers)],
-                                        [Z[l][0] for l in range(w.n_layers)])
+        if w.prenorm_residual:
+            _, s_new, z_new = ok.stack_step(layers, xt, [S[l][0] for l in range(w.n_layers)],
+                                            [Z[l][0] for l in range(w.n_layers)])
+        else:
+            _, s1, z1 = ok.layer_forward(layers[0], xt, S[0][0], Z[0][0])
+            s_new, z_new = [s1], [z1]
         for l in range(w.n_layers):
             S[l][0], Z[l][0] = s_new[l], z_new[l]
         n += 1
@@ -145,19 +165,42 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     model.set_option(kda.KDA_OPT_GRAPH, 1)
     model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
     one_launch = not args.per_layer and model.persistent_blocks() > 0 and B == 1
+    models = [model]
+    if args.copies > 1:
+        # more weight copies than fit the 256 MB last-level cache, used in turn, so that each
+        # step streams its weights from HBM (a copy per model, the state shared)
+        for _ in range(args.copies - 1):
+            m2 = kda.KdaModel(run.layers, n_heads=d.n_heads, d_k=d.d_k, d_v=d.d_v, wtype=w.wtype,
+                              prenorm_residual=w.prenorm_residual, norm_eps=w.norm_eps,
+                              l2_eps=w.l2_eps)
+            m2.set_option(kda.KDA_OPT_GRAPH, 1)
+            m2.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
+            models.append(m2)
+        log(f"[bench] {len(models)} weight copies used in turn")
     path = (f"one launch per token ({model.persistent_blocks()} blocks)" if one_launch
             else "per-layer kernels replayed as one hipGraph")
     log(f"[bench] path: {path}")
+    # each step's input row is copied into one fixed input buffer first (as a serving loop
+    # writes its next token's embedding), so that the captured graph of the per-layer path
+    # is replayed, not captured again for every new input pointer
+    xin = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        xin.copy_(xs[i])
+        models[i % len(models)].decode_step(xin, y, st, ws)
+
     for i in range(args.warmup):
-        model.decode_step(xs[i], y, st, ws)
+        step(i)
     torch.cuda.synchronize()
     # ---- timed region: K steps, inputs resident in HBM ----
     t0 = time.perf_counter()
     for i in range(args.steps):
-        model.decode_step(xs[args.warmup + i], y, st, ws)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     model.status()
+    for m2 in models[1:]:
+        m2.close()
     tok_s = B * args.steps / el
     ms_step = el * 1e3 / args.steps
     log(f"[bench] {args.steps} steps in {el * 1e3:.2f} ms: {tok_s:.1f} tokens/s")
@@ -166,7 +209,8 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     model.set_option(kda.KDA_OPT_TIMING, 1)
     model.timing(kda.KDA_K_PROJ, reset=True)
     for i in range(args.steps):
-        model.decode_step(xs[args.warmup + i], y, st, ws)
+        xin.copy_(xs[args.warmup + i])
+        model.decode_step(xin, y, st, ws)
     torch.cuda.synchronize()
     model.status()
     times = timed_kinds(model, kda, {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES,
@@ -183,6 +227,19 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     dom, roof = roofline_entry(per, "hbm", HBM_PEAK_GBS, "GB/s")
     roof["traffic"] = step_traffic() if dom == "step" else None
     step_gbs = ab["token_weights_state"] / (ms_step * 1e-3) / 1e9
+    # the measured sequential-read ceiling over a buffer the size of a token's bytes (the
+    # byte pricing of antirez/ds4 PR #964 prices against such a ceiling); reported beside
+    # the vendor peak, never in place of it
+    ceil_bytes = max(ab["token_weights_state"] if w.n_layers > 1 else 8 * ab["token_weights_state"],
+                     1 << 28)
+    probe = torch.empty(ceil_bytes // 16 * 16, dtype=torch.uint8, device="cuda")
+    ceil_ms = kda.kda_stream_read_probe(probe, 20)
+    del probe
+    ceiling = ceil_bytes / (ceil_ms * 1e-3) / 1e9
+    roof["ceiling_gbs"] = round(ceiling, 1)
+    roof["frac_of_ceiling"] = round(roof["achieved"] / ceiling, 4)
+    log(f"[bench] sequential-read ceiling {ceiling:.0f} GB/s over {ceil_bytes / 1e6:.0f} MB; "
+        f"the kernel reaches {roof['frac_of_ceiling']:.3f} of it")
     config = {"workload": f"kda-{w.n_layers}L-{w.wtype}-decode" if w.n_layers > 1
               else f"kda-layer-{w.wtype}-decode",
               "layers": w.n_layers, "d_model": d.d_model, "heads": d.n_heads, "d_k": d.d_k,
@@ -192,10 +249,16 @@ def bench_stack(args, torch, synth, kda, w, run, model):
               "step_hbm_gbs": round(step_gbs, 1),
               "step_hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
               "kernels": rounded(per)}
+    if args.copies > 1:
+        config["weight_copies"] = args.copies
+        config["workload"] += f"-{args.copies}copies"
     if w.name == "stack":
         config["workload"] = "kda-stack-34L-q8_0-decode"
-    metric = ("KDA decode tokens/s (34-layer stack, B=1)" if w.name == "stack"
-              else "KDA decode tokens/s (one BF16 layer, B=1)")
+    if w.name == "tiny":
+        config["workload"] = "kda-tiny-layer-f32-decode"
+    metric = {"stack": "KDA decode tokens/s (34-layer stack, B=1)",
+              "layer": "KDA decode tokens/s (one BF16 layer, B=1)",
+              "tiny": "KDA decode tokens/s (tiny fp32 layer, B=1)"}[w.name]
     return metric, tok_s, "tokens/s", ms_step, config, roof
 
 
@@ -234,10 +297,16 @@ def bench_verify(args, torch, synth, kda, w, run, model):
     ys = torch.empty((B, T, d.d_model), dtype=torch.float32, device="cuda")
     acc = torch.from_numpy(np.ascontiguousarray(run.accept).astype(np.int32)).cuda()
     model.set_option(kda.KDA_OPT_GRAPH, 1)
+    # fixed input and accept buffers (a serving loop's draft batch and sampler output), so
+    # that the captured verify and commit graphs are replayed
+    xin = torch.empty((B, T, d.d_model), dtype=torch.float32, device="cuda")
+    ain = torch.empty((B,), dtype=torch.int32, device="cuda")
 
     def step(i):
-        model.verify_steps(xs[i], T, ys, st, vlog, ws)
-        model.verify_commit(st, vlog, T, acc[i])
+        xin.copy_(xs[i])
+        model.verify_steps(xin, T, ys, st, vlog, ws)
+        ain.copy_(acc[i])
+        model.verify_commit(st, vlog, T, ain)
 
     for i in range(args.warmup):
         step(i)
@@ -365,8 +434,8 @@ def rounded(per):
 
 
 def cpu_baseline_for(name, run, budget_s):
-    if name in ("stack", "layer"):
-        return cpu_baseline(run, budget_s)
+    if name in ("stack", "layer", "tiny"):
+        return cpu_baseline(run, budget_s, single_thread=name in ("layer", "tiny"))
     from oracle import kda as ok
     w = run.workload
     d = w.dims
@@ -405,7 +474,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--workload", default="stack", choices=("stack", "layer", "verify", "prefill"))
+    ap.add_argument("--workload", default="stack",
+                    choices=("stack", "layer", "tiny", "verify", "prefill"))
+    ap.add_argument("--copies", type=int, default=1,
+                    help="decode workloads: weight copies used in turn (8 keeps the BF16 layer "
+                         "out of the last-level cache)")
     ap.add_argument("--per-layer", action="store_true",
                     help="time the per-layer hipGraph decode instead of the one-launch step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -442,8 +515,8 @@ def main():
                          prenorm_residual=w.prenorm_residual, norm_eps=w.norm_eps,
                          l2_eps=w.l2_eps)
     log(f"[bench] packed {w.wtype} weights on the device in {time.time() - t0:.1f}s")
-    fn = {"stack": bench_stack, "layer": bench_stack, "verify": bench_verify,
-          "prefill": bench_prefill}[args.workload]
+    fn = {"stack": bench_stack, "layer": bench_stack, "tiny": bench_stack,
+          "verify": bench_verify, "prefill": bench_prefill}[args.workload]
     metric, value, unit, ms_step, config, roof = fn(args, torch, synth, kda, w, run, model)
     model.close()
 

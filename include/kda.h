@@ -230,6 +230,16 @@ typedef enum { KDA_K_PROJ = 0, KDA_K_HEAD = 1, KDA_K_OUT = 2, KDA_K_COMMIT = 3,
  * reset; synchronises on the recorded events.  reset != 0 clears the counters. */
 int kda_timing_query(kda_model* m, int kind, double* total_ms, int64_t* launches, int reset);
 
+/* Measurement utility (not part of the step): the device's sequential-read ceiling.
+ * Reads `bytes` of buf_dev (16-byte aligned; its first 4 bytes per block may be
+ * overwritten with a checksum in the rare case it takes one value) `reps` times after one
+ * warm-up read, with 4 blocks per CU of 16-byte non-temporal loads, and returns the mean
+ * milliseconds per read in *ms_per_read (hipEvents on `stream`; synchronous).  A buffer
+ * larger than the 256 MB last-level cache measures HBM.  Errors: KDA_E_ARG, KDA_E_ALIGN,
+ * KDA_E_HIP. */
+int kda_stream_read_probe(const void* buf_dev, size_t bytes, int reps, void* stream,
+                          float* ms_per_read);
+
 /* Device workspace bytes an op needs for `batch` sequences and `tokens` tokens each
  * (decode: tokens = 1; verify: T; prefill: L). */
 size_t kda_workspace_bytes(const kda_model* m, int op, int32_t batch, int64_t tokens);

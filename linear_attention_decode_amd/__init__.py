@@ -184,6 +184,14 @@ def kda_prefill_scan(handle, x, L: int, y, st, ws, stream=None) -> None:
     _lib.call("kda_prefill_scan", handle, _p(x), L, _p(y), C.byref(s), _p(ws), ws.numel(), _s(stream))
 
 
+def kda_stream_read_probe(buf, reps: int = 10, stream=None) -> float:
+    """Mean ms per sequential read of the cuda tensor `buf` (measurement utility)."""
+    ms = C.c_float()
+    _lib.call("kda_stream_read_probe", _p(buf), buf.numel() * buf.element_size(), reps,
+              _s(stream), C.byref(ms))
+    return ms.value
+
+
 def kda_conv_window_canonical(handle, st, out, stream=None) -> None:
     """out: cuda fp32 [n_layers][B][conv_k - 1][C], oldest token first."""
     s = _state(st)

@@ -27,7 +27,7 @@ EXPORTS = (
     "kda_timing_query", "kda_workspace_bytes", "kda_decode_step", "kda_verify_log_bytes",
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
     "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
-    "kda_decode_step_static", "kda_prefill_scan", "kda_unpack_mxfp4",
+    "kda_decode_step_static", "kda_prefill_scan", "kda_unpack_mxfp4", "kda_stream_read_probe",
 )
 
 
@@ -76,6 +76,7 @@ def lib():
             "kda_unpack_q8_0": (C.c_int, [vp, i64, i64, vp, vp, vp]),
             "kda_unpack_q8_0_device": (C.c_int, [vp, i64, i64, vp, vp, vp]),
             "kda_unpack_mxfp4": (C.c_int, [vp, i64, i64, vp, vp, vp]),
+            "kda_stream_read_probe": (C.c_int, [vp, sz, C.c_int, vp, C.POINTER(C.c_float)]),
             "kda_model_create": (C.c_int, [C.POINTER(KdaDims), C.POINTER(KdaLayer), C.POINTER(vp)]),
             "kda_model_destroy": (None, [vp]),
             "kda_model_set_option": (C.c_int, [vp, C.c_int, i64]),

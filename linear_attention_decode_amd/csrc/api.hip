@@ -55,20 +55,14 @@ struct LayerDev {
   const uint16_t* gbd = nullptr;
 };
 
-struct GraphKey {
-  const void* x = nullptr;
-  void* y = nullptr;
-  float* S = nullptr;
-  float* conv = nullptr;
-  void* ws = nullptr;
-  const int* active = nullptr;
-  int batch = 0;
-  hipStream_t stream = nullptr;
-  bool operator==(const GraphKey& o) const {
-    return x == o.x && y == o.y && S == o.S && conv == o.conv && ws == o.ws &&
-           active == o.active && batch == o.batch && stream == o.stream;
-  }
+// A captured hipGraph of one op (decode, verify or commit) and the arguments it was
+// captured for (pointers, sizes, stream): replayed while they match, captured again when
+// one changes.
+struct GraphSlot {
+  std::vector<uintptr_t> key;
+  hipGraphExec_t exec = nullptr;
 };
+enum { kGraphDecode = 0, kGraphVerify = 1, kGraphCommit = 2, kGraphSlots = 3 };
 
 struct TimedLaunch {
   hipEvent_t a, b;
@@ -83,10 +77,9 @@ struct kda_model {
   // options
   bool use_graph = true;
   bool timing = false;
-  // graph cache (decode)
+  // graph cache (decode, verify, commit)
   hipStream_t cap_stream = nullptr;
-  hipGraphExec_t exec = nullptr;
-  GraphKey key;
+  GraphSlot graphs[kGraphSlots];
   // one-launch decode (batch 1)
   bool use_persist = true;
   bool coop = false;                // cooperative launch of the one-launch decode
@@ -352,9 +345,36 @@ int enqueue_decode(kda_model* m, const float* x, float* y, const kda_state* st, 
 }
 
 void drop_graph(kda_model* m) {
-  if (m->exec) (void)hipGraphExecDestroy(m->exec);
-  m->exec = nullptr;
-  m->key = GraphKey{};
+  for (GraphSlot& g : m->graphs) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    g.exec = nullptr;
+    g.key.clear();
+  }
+}
+
+// Replays the op's graph for `key`, capturing `enqueue` (on the model's capture stream)
+// first when the slot holds none or one for other arguments.
+template <typename F>
+int run_graph(kda_model* m, int slot, std::vector<uintptr_t> key, hipStream_t s, F&& enqueue) {
+  GraphSlot& g = m->graphs[slot];
+  key.push_back((uintptr_t)s);
+  if (!g.exec || g.key != key) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    g.exec = nullptr;
+    g.key.clear();
+    hipGraph_t graph = nullptr;
+    KDA_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
+    const int r = enqueue(m->cap_stream);
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
+    if (r) { if (graph) (void)hipGraphDestroy(graph); return r; }
+    if (e != hipSuccess) return fail(KDA_E_HIP, "graph capture: %s", hipGetErrorString(e));
+    e = hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e != hipSuccess) { g.exec = nullptr; return fail(KDA_E_HIP, "graph instantiate: %s", hipGetErrorString(e)); }
+    g.key = std::move(key);
+  }
+  KDA_HIP(hipGraphLaunch(g.exec, s));
+  return KDA_OK;
 }
 
 int check_state(const kda_model* m, const kda_state* st) {
@@ -948,25 +968,12 @@ int decode_impl(kda_model* m, const float* x_dev, float* y_dev, const kda_state*
   if (eager) return enqueue_decode(m, x_dev, y_dev, st, ws, s, false, active);
   if (!m->use_graph || m->timing) return enqueue_decode(m, x_dev, y_dev, st, ws, s, m->timing, active);
 
-  GraphKey k;
-  k.x = x_dev; k.y = y_dev; k.S = st->S_dev; k.conv = st->conv_dev; k.ws = ws_dev;
-  k.active = active;
-  k.batch = st->batch; k.stream = s;
-  if (!m->exec || !(k == m->key)) {
-    drop_graph(m);
-    hipGraph_t g = nullptr;
-    KDA_HIP(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeRelaxed));
-    r = enqueue_decode(m, x_dev, y_dev, st, ws, m->cap_stream, false, active);
-    hipError_t e = hipStreamEndCapture(m->cap_stream, &g);
-    if (r) { if (g) (void)hipGraphDestroy(g); return r; }
-    if (e != hipSuccess) return fail(KDA_E_HIP, "graph capture: %s", hipGetErrorString(e));
-    e = hipGraphInstantiate(&m->exec, g, nullptr, nullptr, 0);
-    (void)hipGraphDestroy(g);
-    if (e != hipSuccess) { m->exec = nullptr; return fail(KDA_E_HIP, "graph instantiate: %s", hipGetErrorString(e)); }
-    m->key = k;
-  }
-  KDA_HIP(hipGraphLaunch(m->exec, s));
-  return KDA_OK;
+  const std::vector<uintptr_t> key = {(uintptr_t)x_dev, (uintptr_t)y_dev, (uintptr_t)st->S_dev,
+                                      (uintptr_t)st->conv_dev, (uintptr_t)ws_dev,
+                                      (uintptr_t)active, (uintptr_t)st->batch};
+  return run_graph(m, kGraphDecode, key, s, [&](hipStream_t cs) {
+    return enqueue_decode(m, x_dev, y_dev, st, ws, cs, false, active);
+  });
 }
 
 }  // namespace
@@ -1028,15 +1035,22 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   const size_t log_proj = (size_t)B * T * m->proj_stride;
   const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
   const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
-  for (int l = 0; l < m->d.n_layers; ++l) {
-    const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
-    float* lp = logf + l * log_layer;
-    r = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
-                      st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj,
-                      lp + log_proj + log_ag, wl, ws, false, s, m->timing);
-    if (r) return r;
-  }
-  return KDA_OK;
+  auto enqueue = [&](hipStream_t cs, bool rec) {
+    for (int l = 0; l < m->d.n_layers; ++l) {
+      const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
+      float* lp = logf + l * log_layer;
+      const int rr = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
+                                   st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj,
+                                   lp + log_proj + log_ag, wl, ws, false, cs, rec);
+      if (rr) return rr;
+    }
+    return (int)KDA_OK;
+  };
+  if (!m->use_graph || m->timing) return enqueue(s, m->timing);
+  const std::vector<uintptr_t> key = {(uintptr_t)x_dev, (uintptr_t)y_dev, (uintptr_t)st->S_dev,
+                                      (uintptr_t)st->conv_dev, (uintptr_t)log_dev,
+                                      (uintptr_t)ws_dev, (uintptr_t)B, (uintptr_t)T};
+  return run_graph(m, kGraphVerify, key, s, [&](hipStream_t cs) { return enqueue(cs, false); });
 }
 
 int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
@@ -1058,6 +1072,7 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, si
   const size_t log_proj = (size_t)B * T * m->proj_stride;
   const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
   const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
+  auto enqueue = [&](hipStream_t cs, bool rec) {
   for (int l = 0; l < d.n_layers; ++l) {
     const LayerDev& L = m->layers[l];
     HeadParams hp;
@@ -1074,10 +1089,16 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, si
     hp.write_state = 1; hp.ntok = accept_dev; hp.write_out = 0;
     hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
     hp.win_commit = win;      // the window roll runs in the same launch, after the replay
-    r = timed(m, KDA_K_COMMIT, s, m->timing, [&] { return launch_head(hp, s); });
-    if (r) return r;
+    const int rr = timed(m, KDA_K_COMMIT, cs, rec, [&] { return launch_head(hp, cs); });
+    if (rr) return rr;
   }
-  return KDA_OK;
+  return (int)KDA_OK;
+  };
+  if (!m->use_graph || m->timing) return enqueue(s, m->timing);
+  const std::vector<uintptr_t> key = {(uintptr_t)st->S_dev, (uintptr_t)st->conv_dev,
+                                      (uintptr_t)log_dev, (uintptr_t)accept_dev, (uintptr_t)B,
+                                      (uintptr_t)T};
+  return run_graph(m, kGraphCommit, key, s, [&](hipStream_t cs) { return enqueue(cs, false); });
 }
 
 int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,

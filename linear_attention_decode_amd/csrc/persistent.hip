@@ -588,8 +588,10 @@ __device__ __forceinline__ bool phase_p(const PersistParams& P, Smem& sm, const 
   ss = wave_sum(ss);
   if (lane == 0) sm.red[wave] = ss;
   const float inv_s = quantize_runs<NV, D>(v, ss, sm.planes);
+  KDA_STAMP(l, 6);
   i32x4 a[NT][2];
   run_operands<NT, D>(sm.planes, a);
+  KDA_STAMP(l, 7);
   const int rows = R.p1 - R.p0, ntiles = (rows + 15) >> 4;
   float y[kPTiles];
   mfma_tiles<NT, kPTiles>(a, pr.w, pr.d, inv_s, ntiles, y);
@@ -822,6 +824,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     e0 += s.x * kk; e1 += s.y * kk; e2 += s.z * kk; e3 += s.w * kk;
   }
   e0 = sum16(e0); e1 = sum16(e1); e2 = sum16(e2); e3 = sum16(e3);
+  KDA_STAMP(l, 6);
   const float d0 = beta * (vv.x - e0), d1 = beta * (vv.y - e1);
   const float d2 = beta * (vv.z - e2), d3 = beta * (vv.w - e3);
   float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
@@ -833,6 +836,7 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     o0 += s.x * qq; o1 += s.y * qq; o2 += s.z * qq; o3 += s.w * qq;
   }
   o0 = sum16(o0); o1 = sum16(o1); o2 = sum16(o2); o3 = sum16(o3);
+  KDA_STAMP(l, 7);
   // gated outputs (the norm scale comes later) and this wave's partial sum of o^2
   if (rg == 0) {
     uint64_t* ob = P.obuf + h * dv + j;
@@ -906,8 +910,10 @@ __device__ __forceinline__ bool phase_o(const PersistParams& P, Smem& sm, const 
     ss = fmaf(v[2 * t + 1], v[2 * t + 1], ss);
   }
   const float inv_s = quantize_runs<NV, D>(v, wave_sum(ss), sm.planes);
+  KDA_STAMP(l, 6);
   i32x4 a[NT][2];
   run_operands<NT, D>(sm.planes, a);
+  KDA_STAMP(l, 7);
   float y[kOTiles];
   mfma_tiles<NT, kOTiles>(a, orr.w, orr.d, inv_s, kOTiles, y);
 #pragma unroll

@@ -156,3 +156,40 @@ def test_verify_commit_rejects_short_log():
         model.verify_commit(st, small, 4, acc)
     assert ei.value.status == kda._lib.KDA_E_WORKSPACE
     model.close()
+
+
+def test_verify_commit_graph_replays_equal_eager():
+    """Verify and commit captured as hipGraphs and replayed from fixed buffers (inputs and
+    accept lengths copied in by the program between replays, with synchronisations) give
+    bit for bit what the eager launches give, on every step."""
+    import torch
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=2, batch=3, steps=4, seed=53)
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    B, T = w.batch, w.tokens
+    _say("verify + commit: graph replays vs eager, 2 layers B=3 T=4, 4 steps")
+    outs = {}
+    for graph in (True, False):
+        model.set_option(kda.KDA_OPT_GRAPH, 1 if graph else 0)
+        st = model.new_state(B)
+        st.S.copy_(torch.from_numpy(run.s0))
+        ws = model.workspace(kda.KDA_OP_VERIFY, B, T)
+        log = model.verify_log(B, T)
+        xin = torch.empty((B, T, model.d_model), dtype=torch.float32, device="cuda")
+        ain = torch.empty((B,), dtype=torch.int32, device="cuda")
+        y = torch.empty_like(xin)
+        rec = []
+        for t in range(w.steps):
+            xin.copy_(torch.from_numpy(np.ascontiguousarray(run.x[t])))
+            ain.copy_(torch.from_numpy(run.accept[t].copy()))
+            model.verify_steps(xin, T, y, st, log, ws)
+            model.verify_commit(st, log, T, ain)
+            torch.cuda.synchronize()
+            rec.append((y.cpu().numpy().copy(), st.S.cpu().numpy().copy(), st.conv.cpu().numpy().copy()))
+        outs[graph] = rec
+    for (ya, Sa, Za), (yb, Sb, Zb) in zip(outs[True], outs[False]):
+        np.testing.assert_array_equal(ya, yb)
+        np.testing.assert_array_equal(Sa, Sb)
+        np.testing.assert_array_equal(Za, Zb)
+    model.close()
