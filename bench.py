@@ -264,7 +264,8 @@ def bench_stack(args, torch, synth, kda, w, run, model):
 
 def verify_bytes(w):
     """Algorithmic bytes per verify step (B sequences x T tokens): every layer's weights once
-    and each sequence's state read once (verify) plus read + written once (commit)."""
+    and each sequence's state read once and written once (the previous step's commit is
+    replayed inside the verify's head kernel, from the log rows of its accepted tokens)."""
     d = w.dims
     D, K, V, H = d.d_model, d.key_dim, d.value_dim, d.n_heads
     C = d.conv_channels
@@ -278,7 +279,7 @@ def verify_bytes(w):
     state = H * d.d_k * d.d_v * 4
     per = {"proj": proj_w + N * (D + rows) * 4,
            "gates": q8(K, d.rank_f) + q8(V, d.rank_g) + N * (d.rank_f + d.rank_g + K + V) * 4,
-           "head": w.batch * state + N * (rows + K + V + 2 * V) * 4,
+           "head": w.batch * 2 * state + N * (rows + K + V + 2 * V) * 4 + N * (2 * K + V + H) * 4,
            "out": q8(D, V) + N * (2 * V + 2 * D) * 4,
            "commit": w.batch * 2 * state}
     floor = w.n_layers * (proj_w + q8(K, d.rank_f) + q8(V, d.rank_g) + q8(D, V)
@@ -306,14 +307,16 @@ def bench_verify(args, torch, synth, kda, w, run, model):
         xin.copy_(xs[i])
         model.verify_steps(xin, T, ys, st, vlog, ws)
         ain.copy_(acc[i])
-        model.verify_commit(st, vlog, T, ain)
+        model.verify_commit(st, vlog, T, ain)      # recorded; folded into the next verify
 
     for i in range(args.warmup):
         step(i)
+    model.flush(st)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(args.warmup + i)
+    model.flush(st)                                 # the last step's commit, applied
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     accepted = int(run.accept[args.warmup:args.warmup + args.steps].clip(1, T).sum())
@@ -324,6 +327,7 @@ def bench_verify(args, torch, synth, kda, w, run, model):
     model.timing(kda.KDA_K_PROJ, reset=True)
     for i in range(args.steps):
         step(args.warmup + i)
+    model.flush(st)
     torch.cuda.synchronize()
     times = timed_kinds(model, kda, {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES,
                                      "head": kda.KDA_K_HEAD, "out": kda.KDA_K_OUT,

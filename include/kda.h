@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -281,23 +281,55 @@ int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const
                            void* stream);
 
 /* Verify (multi-token, read-only on the state): T tokens per sequence, x_dev [B][T][D],
- * run in order through every layer from the state in st, which is NOT modified.  Writes
- * y_dev [B][T][D] for every token and a replay log (kda_verify_log_bytes) that
- * kda_verify_commit uses.  The read-only verify and the later commit of an accepted
- * prefix are the verify / commit-after-k modes of the gdn_step kernel in the regolith
- * GDN audit (opus_gdn_qsa, section 2).  1 <= T <= 8. */
+ * run in order through every layer from the state in st.  Writes y_dev [B][T][D] for
+ * every token and a replay log that kda_verify_commit uses.  The read-only verify and the
+ * later commit of an accepted prefix are the verify / commit-after-k modes of the gdn_step
+ * kernel in the regolith GDN audit (opus_gdn_qsa, section 2).  1 <= T <= 8.
+ *
+ * Folded commit.  kda_verify_commit only records the accepted lengths; the next
+ * kda_verify_steps on the same state and log applies them first, inside its own kernels:
+ * per (sequence, layer, head) the state is read once, the accepted tokens of the previous
+ * verify are replayed from the log, the state is written once, and the new tokens run from
+ * it in registers; the conv window moves on in the projection kernel the same way.  So the
+ * state is read once and written once per step, and st holds the state after the last
+ * applied commit.  Every other call that reads or writes st (kda_decode_step and its
+ * variants, kda_prefill_scan, kda_prefill_chunked, kda_conv_window_canonical) and
+ * kda_state_flush apply a pending commit first, and a verify on st through another log
+ * applies that log's.  A caller that reads st's buffers itself, copies them (a snapshot)
+ * or frees them, or frees or reuses the log, calls kda_state_flush first (and synchronises
+ * as for any asynchronous call).
+ *
+ * log_dev: device memory of log_bytes >= kda_verify_log_bytes(m, B, T), 16-byte aligned,
+ * owned by the caller and left to the library between a verify and the call that applies
+ * its commit: a header of the accepted lengths ([B] int32) and two halves that
+ * consecutive verifies alternate (the one being written, the one whose commit is folded
+ * in), each holding per layer the pre-conv projections, alpha and gate, and the activated
+ * q|k|v of the B*T tokens.  A commit must follow the verify it commits on that state and
+ * log, with no call that writes st in between (such a call retires the verify).  Errors:
+ * KDA_E_ARG, KDA_E_ALIGN, KDA_E_SHAPE, KDA_E_WORKSPACE (log or workspace too small; a log
+ * sized for T serves every T' <= T), KDA_E_HIP; after a failed call the state is
+ * undefined. */
 size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T);
 int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
                      const kda_state* st, void* log_dev, size_t log_bytes, void* ws_dev,
                      size_t ws_bytes, void* stream);
-/* Commit: advance st to the state and conv window reached after accept_dev[b] tokens
- * (device int32 [B], each in 1..T) of the last kda_verify_steps on this log.  The result
- * equals decoding those tokens.  log_bytes is the size of log_dev; it must hold a verify of
- * st->batch sequences and T tokens (kda_verify_log_bytes), else KDA_E_WORKSPACE.  The
- * accept lengths are device data, which the host cannot read without a synchronisation:
- * the kernel clamps a value outside 1..T to that range. */
+/* Commit: st becomes the state and conv window reached after accept_dev[b] tokens (device
+ * int32 [B], each in 1..T) of the last kda_verify_steps on this state and log; the result
+ * equals decoding those tokens.  Recorded, not run: the lengths are copied into the log
+ * header on `stream` (accept_dev may be reused once the stream has passed this call) and
+ * applied by the next call on st (above).  T must be the verify's T and log_bytes the size
+ * it was given.  KDA_E_ARG if no verify of T tokens on this state and log waits for a
+ * commit (none made, one already committed, or retired by a call that wrote st); at most
+ * 64 commits may be pending on one model.  The accept lengths are device data, which the
+ * host cannot read without a synchronisation: the kernels clamp a value outside 1..T to
+ * that range. */
 int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
                       int32_t T, const int32_t* accept_dev, void* stream);
+/* Apply the commit pending on st, if any (the replay of the accepted tokens into the
+ * state and the window, enqueued on `stream`); nothing to do otherwise.  Needed before the
+ * caller reads, copies or frees st's buffers or the log itself.  Errors: KDA_E_ARG,
+ * KDA_E_ALIGN, KDA_E_HIP. */
+int kda_state_flush(kda_model* m, const kda_state* st, void* stream);
 
 /* Sequential-scan prefill of L tokens per sequence, for prompts too short for the
  * chunked form to pay (the sequential prompt scan gdn_scan_r of the regolith audit
@@ -319,10 +351,9 @@ int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
 /* The conv windows of every layer and sequence in the canonical layout
  * out_dev [n_layers][B][conv_k - 1][C] fp32, oldest token first (the "conv_state" of the
  * pure decode step in "Thirty tiny kernels per layer", section "Why mx.compile fits here
- * and not elsewhere").  Asynchronous device-to-device copy on `stream`; st is not
- * modified. */
-int kda_conv_window_canonical(const kda_model* m, const kda_state* st, float* out_dev,
-                              void* stream);
+ * and not elsewhere").  Asynchronous device-to-device copy on `stream`, after a pending
+ * commit on st is applied. */
+int kda_conv_window_canonical(kda_model* m, const kda_state* st, float* out_dev, void* stream);
 
 /* Chunked prefill of L tokens per sequence through a single-layer model (n_layers == 1,
  * prenorm_residual == 0): x_dev [B][L][D] (x_dtype KDA_BF16 bit patterns or KDA_F32),

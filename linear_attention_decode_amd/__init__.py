@@ -168,14 +168,20 @@ def kda_decode_step_masked(handle, x, y, st, active, ws, stream=None) -> None:
 
 def kda_verify_steps(handle, x, T: int, y, st, log, ws, stream=None) -> None:
     s = _state(st)
-    _lib.call("kda_verify_steps", handle, _p(x), T, _p(y), C.byref(s), _p(log), log.numel(),
-              _p(ws), ws.numel(), _s(stream))
+    _lib.call("kda_verify_steps", handle, _p(x), T, _p(y), C.byref(s), _p(log),
+              log.numel() * log.element_size(), _p(ws), ws.numel(), _s(stream))
 
 
 def kda_verify_commit(handle, st, log, T: int, accept, stream=None) -> None:
     s = _state(st)
     _lib.call("kda_verify_commit", handle, C.byref(s), _p(log), log.numel() * log.element_size(),
               T, _p(accept), _s(stream))
+
+
+def kda_state_flush(handle, st, stream=None) -> None:
+    """Apply a commit pending on st (before st's buffers are read, copied or freed)."""
+    s = _state(st)
+    _lib.call("kda_state_flush", handle, C.byref(s), _s(stream))
 
 
 def kda_prefill_scan(handle, x, L: int, y, st, ws, stream=None) -> None:
@@ -314,6 +320,9 @@ class KdaModel:
 
     def verify_commit(self, st: KdaStateBuf, log, T: int, accept, stream=None) -> None:
         kda_verify_commit(self.handle, st, log, T, accept, stream)
+
+    def flush(self, st: KdaStateBuf, stream=None) -> None:
+        kda_state_flush(self.handle, st, stream)
 
     def conv_window(self, st: KdaStateBuf, stream=None):
         """The canonical conv windows [n_layers][B][3][C] (oldest first) as a new tensor."""

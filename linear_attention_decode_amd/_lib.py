@@ -28,6 +28,7 @@ EXPORTS = (
     "kda_verify_steps", "kda_verify_commit", "kda_prefill_chunked", "kda_model_query",
     "kda_model_status", "kda_conv_window_canonical", "kda_decode_step_masked",
     "kda_decode_step_static", "kda_prefill_scan", "kda_unpack_mxfp4", "kda_stream_read_probe",
+    "kda_state_flush",
 )
 
 
@@ -91,6 +92,7 @@ def lib():
             "kda_verify_log_bytes": (sz, [vp, i32, i32]),
             "kda_verify_steps": (C.c_int, [vp, vp, i32, vp, C.POINTER(KdaState), vp, sz, vp, sz, vp]),
             "kda_verify_commit": (C.c_int, [vp, C.POINTER(KdaState), vp, sz, i32, vp, vp]),
+            "kda_state_flush": (C.c_int, [vp, C.POINTER(KdaState), vp]),
             "kda_conv_window_canonical": (C.c_int, [vp, C.POINTER(KdaState), vp, vp]),
             "kda_prefill_chunked": (C.c_int, [vp, vp, C.c_int, i64, i32, vp, C.POINTER(KdaState), vp, sz, vp]),
         }

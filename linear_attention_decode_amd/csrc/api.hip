@@ -62,7 +62,20 @@ struct GraphSlot {
   std::vector<uintptr_t> key;
   hipGraphExec_t exec = nullptr;
 };
-enum { kGraphDecode = 0, kGraphVerify = 1, kGraphCommit = 2, kGraphSlots = 3 };
+enum { kGraphDecode = 0, kGraphVerify = 1, kGraphVerifyOdd = 2, kGraphCommit = 3, kGraphSlots = 4 };
+
+// A verify log on one state: which half of the log the last verify wrote (and for how many
+// tokens) while no commit of it is recorded, and the half and length of a commit recorded
+// by kda_verify_commit and not yet applied to the state (-1: none).
+struct LogRec {
+  const float* S = nullptr;
+  const float* conv = nullptr;
+  int B = 0;
+  const void* log = nullptr;
+  size_t log_bytes = 0;
+  int last_half = -1, last_T = 0;
+  int pend_half = -1, pend_T = 0;
+};
 
 struct TimedLaunch {
   hipEvent_t a, b;
@@ -80,6 +93,8 @@ struct kda_model {
   // graph cache (decode, verify, commit)
   hipStream_t cap_stream = nullptr;
   GraphSlot graphs[kGraphSlots];
+  // verify logs in use on this model's states (the folded commit's bookkeeping)
+  std::vector<LogRec> logs;
   // one-launch decode (batch 1)
   bool use_persist = true;
   bool coop = false;                // cooperative launch of the one-launch decode
@@ -233,10 +248,20 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
 // Verify passes `act`: the projections stay pre-conv (they are logged for the commit's
 // window roll) and the activated q|k|v go to act; decode applies the conv in the
 // projection epilogue and rolls the window there.
+// The previous verify's log rows of one layer, replayed ahead of this verify's tokens (a
+// commit folded into the verify after it).
+struct FoldSrc {
+  const float* proj = nullptr;
+  const float* ag = nullptr;
+  const float* act = nullptr;
+  const int* ntok = nullptr;      // accepted tokens per sequence (the log header)
+  int T = 0;                      // tokens per sequence of that verify
+};
+
 int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T,
                   float* S, float* win, float* proj, float* ag, float* act, const WsLayout& wl,
                   char* ws, bool write_state, hipStream_t s, bool rec,
-                  const int* active = nullptr, bool roll = false) {
+                  const int* active = nullptr, bool roll = false, const FoldSrc* fold = nullptr) {
   const kda_dims& d = m->d;
   const LayerDev& L = m->layers[l];
   const int N = B * T;
@@ -265,6 +290,11 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
     pp.act = act;
     pp.T = T;
   }
+  if (fold) {
+    pp.pre_proj = fold->proj;
+    pp.pre_ntok = fold->ntok;
+    pp.pre_T = fold->T;
+  }
   const int g1 = proj_grid(pp);
   int r = timed(m, KDA_K_PROJ, s, rec, [&] {
     if (skinny_supported(d.wtype, N, pp.K)) return launch_skinny(kProX, pp, ws + wl.sk, s);
@@ -274,7 +304,9 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
 
   if (act && !conv_fused) {
     r = timed(m, KDA_K_PROJ, s, rec, [&] {
-      return launch_conv_seq(proj, m->proj_stride, win, L.conv_w, act, B, T, m->C, s);
+      return launch_conv_seq(proj, m->proj_stride, win, L.conv_w, act, B, T, m->C,
+                             fold ? fold->proj : nullptr, fold ? fold->ntok : nullptr,
+                             fold ? fold->T : 0, s);
     });
     if (r) return r;
   }
@@ -298,6 +330,13 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   // a multi-token step that keeps its state (the sequential-scan prefill) rolls the window
   // by all T tokens after the state write, in the same launch
   if (roll) hp.win_commit = win;
+  if (fold) {
+    hp.pre_proj = fold->proj;
+    hp.pre_act = fold->act;
+    hp.pre_ag = fold->ag;
+    hp.pre_ntok = fold->ntok;
+    hp.pre_T = fold->T;
+  }
   r = timed(m, KDA_K_HEAD, s, rec, [&] { return launch_head(hp, s); });
   if (r) return r;
 
@@ -382,6 +421,137 @@ int check_state(const kda_model* m, const kda_state* st) {
   if (st->batch < 1) return fail(KDA_E_SHAPE, "state batch %d < 1", st->batch);
   if (!aligned16(st->S_dev) || !aligned16(st->conv_dev)) return fail(KDA_E_ALIGN, "state not 16-byte aligned");
   return KDA_OK;
+}
+
+// ---- verify logs: a header of the accepted lengths ([B] int32, 256-byte aligned), then two
+// halves that alternate between consecutive verifies (the one being written, the one whose
+// commit it folds in).  A half holds per layer: pre-conv projections [B T][proj_stride] |
+// alpha, gate [B T][K + V] | activated q|k|v [B T][C].
+size_t log_hdr_bytes(int B) { return align_up((size_t)B * 4, 256); }
+size_t log_layer_floats(const kda_model* m, int B, int T) {
+  return (size_t)B * T * (m->proj_stride + m->Kq + m->V + m->C);
+}
+size_t log_half_bytes(const kda_model* m, int B, int T) {
+  return align_up(log_layer_floats(m, B, T) * m->d.n_layers * 4, 256);
+}
+size_t log_half_cap(size_t log_bytes, int B) {
+  const size_t hdr = log_hdr_bytes(B);
+  return log_bytes < hdr ? 0 : ((log_bytes - hdr) / 2) & ~size_t(255);
+}
+
+struct LogLayer {
+  float* proj;
+  float* ag;
+  float* act;
+};
+LogLayer log_layer(const kda_model* m, const void* log, size_t log_bytes, int B, int T, int half,
+                   int l) {
+  char* base = static_cast<char*>(const_cast<void*>(log)) + log_hdr_bytes(B) +
+               (size_t)half * log_half_cap(log_bytes, B);
+  float* lp = reinterpret_cast<float*>(base) + (size_t)l * log_layer_floats(m, B, T);
+  LogLayer r;
+  r.proj = lp;
+  r.ag = lp + (size_t)B * T * m->proj_stride;
+  r.act = r.ag + (size_t)B * T * (m->Kq + m->V);
+  return r;
+}
+
+bool same_state(const LogRec& r, const kda_state* st) {
+  return r.S == st->S_dev || r.conv == st->conv_dev;
+}
+
+LogRec* find_log(kda_model* m, const kda_state* st, const void* log, size_t log_bytes) {
+  for (auto& r : m->logs)
+    if (r.S == st->S_dev && r.conv == st->conv_dev && r.B == st->batch && r.log == log &&
+        r.log_bytes == log_bytes)
+      return &r;
+  return nullptr;
+}
+
+// Apply a recorded commit: each layer's head kernel replays the accepted tokens from the log
+// into the state, then rolls the window by their logged pre-conv projections.
+int apply_commit(kda_model* m, LogRec& rc, hipStream_t s, bool eager) {
+  const kda_dims& d = m->d;
+  const int B = rc.B, T = rc.pend_T, half = rc.pend_half;
+  const int* accept = static_cast<const int*>(rc.log);
+  float* S = const_cast<float*>(rc.S);
+  float* conv = const_cast<float*>(rc.conv);
+  auto enqueue = [&](hipStream_t cs, bool rec) {
+    for (int l = 0; l < d.n_layers; ++l) {
+      const LayerDev& L = m->layers[l];
+      const LogLayer ll = log_layer(m, rc.log, rc.log_bytes, B, T, half, l);
+      HeadParams hp;
+      hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
+      hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
+      hp.B = B; hp.T = T;
+      hp.proj = ll.proj; hp.proj_stride = m->proj_stride;
+      hp.act = ll.act;
+      hp.alpha_gate = ll.ag;
+      hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
+      hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
+      hp.S = S + (size_t)l * B * d.n_heads * d.d_k * d.d_v;
+      hp.write_state = 1; hp.ntok = accept; hp.write_out = 0;
+      hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
+      // the window roll runs in the same launch, after the replay
+      hp.win_commit = conv + (size_t)l * B * (d.conv_k - 1) * m->C;
+      const int rr = timed(m, KDA_K_COMMIT, cs, rec, [&] { return launch_head(hp, cs); });
+      if (rr) return rr;
+    }
+    return (int)KDA_OK;
+  };
+  int r;
+  if (!m->use_graph || m->timing || eager) {
+    r = enqueue(s, m->timing && !eager);
+  } else {
+    const std::vector<uintptr_t> key = {(uintptr_t)rc.S, (uintptr_t)rc.conv, (uintptr_t)rc.log,
+                                        (uintptr_t)rc.log_bytes, (uintptr_t)B, (uintptr_t)T,
+                                        (uintptr_t)half};
+    r = run_graph(m, kGraphCommit, key, s, [&](hipStream_t cs) { return enqueue(cs, false); });
+  }
+  rc.pend_half = -1;
+  return r;
+}
+
+// Before a call that reads or writes a state: apply the commits pending on it (except the
+// one `keep` folds in itself; `eager`: launched directly, no graph captured).  A call that
+// writes the state (`writes`) also retires every verify on it not yet committed: a commit
+// after it would no longer follow its verify.
+int flush_state(kda_model* m, const kda_state* st, hipStream_t s, bool writes,
+                const LogRec* keep = nullptr, bool eager = false) {
+  for (auto& rc : m->logs) {
+    if (&rc == keep || !same_state(rc, st)) continue;
+    if (rc.pend_half >= 0) {
+      const int r = apply_commit(m, rc, s, eager);
+      if (r) return r;
+    }
+    if (writes) rc.last_half = -1;
+  }
+  return KDA_OK;
+}
+
+// The record of (state, log), made if there is none; records with nothing left to commit or
+// apply are dropped first.  At most kMaxLogs verifies wait for a commit at once (the oldest
+// is retired beyond that); null if that many commits are pending.
+constexpr size_t kMaxLogs = 64;
+LogRec* add_log(kda_model* m, const kda_state* st, const void* log, size_t log_bytes) {
+  if (LogRec* r = find_log(m, st, log, log_bytes)) return r;
+  m->logs.erase(std::remove_if(m->logs.begin(), m->logs.end(),
+                               [](const LogRec& rc) { return rc.last_half < 0 && rc.pend_half < 0; }),
+                m->logs.end());
+  if (m->logs.size() >= kMaxLogs) {
+    auto it = std::find_if(m->logs.begin(), m->logs.end(),
+                           [](const LogRec& rc) { return rc.pend_half < 0; });
+    if (it == m->logs.end()) return nullptr;
+    m->logs.erase(it);
+  }
+  LogRec rc;
+  rc.S = st->S_dev;
+  rc.conv = st->conv_dev;
+  rc.B = st->batch;
+  rc.log = log;
+  rc.log_bytes = log_bytes;
+  m->logs.push_back(rc);
+  return &m->logs.back();
 }
 
 // One-launch decode: eligible for batch 1, Q8_0 stacks with d_k = d_v = 128, H*d_v = D in
@@ -953,6 +1123,8 @@ int decode_impl(kda_model* m, const float* x_dev, float* y_dev, const kda_state*
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
+  r = flush_state(m, st, s, true, nullptr, eager);
+  if (r) return r;
   if (!active && m->use_persist && m->pers_ok && st->batch == 1) {
     if (m->epoch >= 0x7fffffffu / (uint32_t)m->d.n_layers) {
       r = reset_exchange(m);
@@ -1010,7 +1182,7 @@ int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const
 
 size_t kda_verify_log_bytes(const kda_model* m, int32_t batch, int32_t T) {
   if (!m || batch < 1 || T < 1) return 0;
-  return (size_t)m->d.n_layers * batch * T * (m->proj_stride + m->Kq + m->V + m->C) * 4;
+  return log_hdr_bytes(batch) + 2 * log_half_bytes(m, batch, T);
 }
 
 int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
@@ -1023,34 +1195,62 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   if (!aligned16(x_dev) || !aligned16(y_dev) || !aligned16(log_dev) || !aligned16(ws_dev))
     return fail(KDA_E_ALIGN, "unaligned pointer");
   const int B = st->batch;
-  if (log_bytes < kda_verify_log_bytes(m, B, T)) return fail(KDA_E_WORKSPACE, "log buffer too small");
+  if (log_half_cap(log_bytes, B) < log_half_bytes(m, B, T))
+    return fail(KDA_E_WORKSPACE, "log of %zu bytes is smaller than a verify of B=%d, T=%d needs (%zu)",
+                log_bytes, B, T, kda_verify_log_bytes(m, B, T));
   WsLayout wl = ws_layout(m, (int64_t)B * T);
   if (ws_bytes < wl.total) return fail(KDA_E_WORKSPACE, "workspace %zu < %zu", ws_bytes, wl.total);
   r = check_poison(m);
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
   char* ws = static_cast<char*>(ws_dev);
-  float* logf = static_cast<float*>(log_dev);
-  // log per layer: pre-conv projections | alpha, gate | activated q, k, v
-  const size_t log_proj = (size_t)B * T * m->proj_stride;
-  const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
-  const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
+  // commits pending on this state through other logs are applied first; one recorded on
+  // this log is folded into this verify
+  const LogRec* mine = find_log(m, st, log_dev, log_bytes);
+  r = flush_state(m, st, s, true, mine);
+  if (r) return r;
+  LogRec* rc = add_log(m, st, log_dev, log_bytes);
+  if (!rc) return fail(KDA_E_ARG, "%zu commits are pending on this model: apply some with kda_state_flush",
+                       kMaxLogs);
+  const bool fold = rc->pend_half >= 0;
+  const int half = fold ? 1 - rc->pend_half : 0;
+  const int pT = rc->pend_T, phalf = rc->pend_half;
   auto enqueue = [&](hipStream_t cs, bool rec) {
     for (int l = 0; l < m->d.n_layers; ++l) {
       const float* xin = (l == 0 || !m->d.prenorm_residual) ? x_dev : y_dev;
-      float* lp = logf + l * log_layer;
+      const LogLayer ll = log_layer(m, log_dev, log_bytes, B, T, half, l);
+      FoldSrc fs;
+      if (fold) {
+        const LogLayer pl = log_layer(m, log_dev, log_bytes, B, pT, phalf, l);
+        fs.proj = pl.proj;
+        fs.ag = pl.ag;
+        fs.act = pl.act;
+        fs.ntok = static_cast<const int*>(log_dev);
+        fs.T = pT;
+      }
       const int rr = enqueue_layer(m, l, xin, y_dev, B, T, st->S_dev + l * state_layer_stride(m, B),
-                                   st->conv_dev + l * win_layer_stride(m, B), lp, lp + log_proj,
-                                   lp + log_proj + log_ag, wl, ws, false, cs, rec);
+                                   st->conv_dev + l * win_layer_stride(m, B), ll.proj, ll.ag,
+                                   ll.act, wl, ws, false, cs, rec, nullptr, false,
+                                   fold ? &fs : nullptr);
       if (rr) return rr;
     }
     return (int)KDA_OK;
   };
-  if (!m->use_graph || m->timing) return enqueue(s, m->timing);
-  const std::vector<uintptr_t> key = {(uintptr_t)x_dev, (uintptr_t)y_dev, (uintptr_t)st->S_dev,
-                                      (uintptr_t)st->conv_dev, (uintptr_t)log_dev,
-                                      (uintptr_t)ws_dev, (uintptr_t)B, (uintptr_t)T};
-  return run_graph(m, kGraphVerify, key, s, [&](hipStream_t cs) { return enqueue(cs, false); });
+  if (!m->use_graph || m->timing) {
+    r = enqueue(s, m->timing);
+  } else {
+    const std::vector<uintptr_t> key = {(uintptr_t)x_dev, (uintptr_t)y_dev, (uintptr_t)st->S_dev,
+                                        (uintptr_t)st->conv_dev, (uintptr_t)log_dev,
+                                        (uintptr_t)log_bytes, (uintptr_t)ws_dev, (uintptr_t)B,
+                                        (uintptr_t)T, (uintptr_t)fold, (uintptr_t)pT};
+    r = run_graph(m, half ? kGraphVerifyOdd : kGraphVerify, key, s,
+                  [&](hipStream_t cs) { return enqueue(cs, false); });
+  }
+  rc = find_log(m, st, log_dev, log_bytes);
+  rc->pend_half = -1;
+  rc->last_half = r ? -1 : half;
+  rc->last_T = T;
+  return r;
 }
 
 int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, size_t log_bytes,
@@ -1060,45 +1260,33 @@ int kda_verify_commit(kda_model* m, const kda_state* st, const void* log_dev, si
   if (r) return r;
   if (T < 1 || T > 8) return fail(KDA_E_SHAPE, "T must be in 1..8");
   const int B = st->batch;
-  if (log_bytes < kda_verify_log_bytes(m, B, T))
+  if (log_half_cap(log_bytes, B) < log_half_bytes(m, B, T))
     return fail(KDA_E_WORKSPACE, "log of %zu bytes is smaller than a verify of B=%d, T=%d writes (%zu)",
                 log_bytes, B, T, kda_verify_log_bytes(m, B, T));
   if (!aligned16(log_dev) || ((uintptr_t)accept_dev & 3u)) return fail(KDA_E_ALIGN, "unaligned pointer");
   r = check_poison(m);
   if (r) return r;
-  hipStream_t s = (hipStream_t)stream;
-  const kda_dims& d = m->d;
-  const float* logf = static_cast<const float*>(log_dev);
-  const size_t log_proj = (size_t)B * T * m->proj_stride;
-  const size_t log_ag = (size_t)B * T * (m->Kq + m->V);
-  const size_t log_layer = log_proj + log_ag + (size_t)B * T * m->C;
-  auto enqueue = [&](hipStream_t cs, bool rec) {
-  for (int l = 0; l < d.n_layers; ++l) {
-    const LayerDev& L = m->layers[l];
-    HeadParams hp;
-    hp.alpha_gate = logf + l * log_layer + log_proj;
-    hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
-    hp.rank_f = d.rank_f; hp.rank_g = d.rank_g;
-    hp.B = B; hp.T = T;
-    hp.proj = logf + l * log_layer; hp.proj_stride = m->proj_stride;
-    hp.act = logf + l * log_layer + log_proj + log_ag;
-    float* win = st->conv_dev + l * win_layer_stride(m, B);
-    hp.wt = d.wtype; hp.fb = L.fb; hp.gb = L.gb;
-    hp.a_log = L.a_log; hp.dt_bias = L.dt_bias;
-    hp.S = st->S_dev + l * state_layer_stride(m, B);
-    hp.write_state = 1; hp.ntok = accept_dev; hp.write_out = 0;
-    hp.l2_eps = d.l2_eps; hp.q_scale = m->q_scale;
-    hp.win_commit = win;      // the window roll runs in the same launch, after the replay
-    const int rr = timed(m, KDA_K_COMMIT, cs, rec, [&] { return launch_head(hp, cs); });
-    if (rr) return rr;
-  }
-  return (int)KDA_OK;
-  };
-  if (!m->use_graph || m->timing) return enqueue(s, m->timing);
-  const std::vector<uintptr_t> key = {(uintptr_t)st->S_dev, (uintptr_t)st->conv_dev,
-                                      (uintptr_t)log_dev, (uintptr_t)accept_dev, (uintptr_t)B,
-                                      (uintptr_t)T};
-  return run_graph(m, kGraphCommit, key, s, [&](hipStream_t cs) { return enqueue(cs, false); });
+  LogRec* rc = find_log(m, st, log_dev, log_bytes);
+  if (!rc || rc->last_half < 0 || rc->last_T != T)
+    return fail(KDA_E_ARG, "no verify of T=%d tokens on this state and log to commit (a commit "
+                "follows its verify, with no other call on the state in between)", T);
+  // the accepted lengths go to the log header: the caller's buffer is free again once the
+  // stream has passed this point
+  KDA_HIP(hipMemcpyAsync(const_cast<void*>(log_dev), accept_dev, (size_t)B * 4,
+                         hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  rc->pend_half = rc->last_half;
+  rc->pend_T = T;
+  rc->last_half = -1;
+  return KDA_OK;
+}
+
+int kda_state_flush(kda_model* m, const kda_state* st, void* stream) {
+  if (!m) return fail(KDA_E_ARG, "null model");
+  int r = check_state(m, st);
+  if (r) return r;
+  r = check_poison(m);
+  if (r) return r;
+  return flush_state(m, st, (hipStream_t)stream, false);
 }
 
 int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
@@ -1114,6 +1302,8 @@ int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
   r = check_poison(m);
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
+  r = flush_state(m, st, s, true);
+  if (r) return r;
   char* ws = static_cast<char*>(ws_dev);
   const int D = m->d.d_model;
   float* xs = reinterpret_cast<float*>(ws + sl.xs);
@@ -1139,13 +1329,14 @@ int kda_prefill_scan(kda_model* m, const float* x_dev, int64_t L, float* y_dev,
   return KDA_OK;
 }
 
-int kda_conv_window_canonical(const kda_model* m, const kda_state* st, float* out_dev,
-                              void* stream) {
+int kda_conv_window_canonical(kda_model* m, const kda_state* st, float* out_dev, void* stream) {
   if (!m || !out_dev) return fail(KDA_E_ARG, "null pointer");
   int r = check_state(m, st);
   if (r) return r;
   if (!aligned16(out_dev)) return fail(KDA_E_ALIGN, "unaligned pointer");
   r = check_poison(m);
+  if (r) return r;
+  r = flush_state(m, st, (hipStream_t)stream, false);
   if (r) return r;
   // the device window is already [n_layers][B][conv_k - 1][C], oldest token first
   const size_t n = (size_t)m->d.n_layers * win_layer_stride(m, st->batch);
@@ -1177,6 +1368,8 @@ int kda_prefill_chunked(kda_model* m, const void* x_dev, int x_dtype, int64_t L,
   r = check_poison(m);
   if (r) return r;
   hipStream_t s = (hipStream_t)stream;
+  r = flush_state(m, st, s, true);
+  if (r) return r;
   char* ws = static_cast<char*>(ws_dev);
   const LayerDev& Ly = m->layers[0];
   const int64_t M = (int64_t)B * L;

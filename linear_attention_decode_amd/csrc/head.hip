@@ -327,9 +327,6 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   const int nparts = dv / CW;
   const int rl = P.rank_f + P.rank_g;
 
-  int ntok = P.T;
-  if (P.ntok) ntok = min(max(P.ntok[b], 1), P.T);
-
   float* Sb = P.S + ((size_t)b * H + h) * DK * dv + j;
   float4 st[RPT];
 #pragma unroll
@@ -345,11 +342,17 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     float4 gate;
     float braw;
   };
+  // pass 0 (a commit folded into this verify): the previous verify's accepted tokens from
+  // its log, state only, then the state written back; pass 1: this call's tokens
+  const float* src_proj = P.proj;
+  const float* src_act = P.act;
+  const float* src_ag = P.alpha_gate;
+  int Ts = P.T;
   auto load_tok = [&](int t, Tok& x) {
-    const int n = b * P.T + t;
-    const float* prow = P.proj + (size_t)n * P.proj_stride;
-    const float* arow = P.act ? P.act + (size_t)n * C : prow;   // activated q | k | v
-    const float* ag = P.alpha_gate + (size_t)n * (K + H * dv);
+    const int n = b * Ts + t;
+    const float* prow = src_proj + (size_t)n * P.proj_stride;
+    const float* arow = src_act ? src_act + (size_t)n * C : prow;   // activated q | k | v
+    const float* ag = src_ag + (size_t)n * (K + H * dv);
 #pragma unroll
     for (int i = 0; i < RPT; i += 4) {
       const float4 a = *reinterpret_cast<const float4*>(arow + cq0 + i);
@@ -364,63 +367,73 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
     x.braw = prow[C + rl + h];
   };
-  Tok nxt;
-  load_tok(0, nxt);
-  for (int t = 0; t < ntok; ++t) {
-    const int n = b * P.T + t;
-    Tok cur = nxt;
-    if (t + 1 < ntok) load_tok(t + 1, nxt);
-    float (&qv)[RPT] = cur.qv;
-    float (&kv)[RPT] = cur.kv;
-    float (&al)[RPT] = cur.al;
-    float (&v4)[4] = cur.v4;
-    const float4 gate = cur.gate;
-    const float beta = sigmoid_f(cur.braw);
-    // L2 norms over the head's DK rows: local rows, then the 8 row groups
-    float aq = 0.0f, ak = 0.0f;
+  for (int pass = P.pre_ntok ? 0 : 1; pass < 2; ++pass) {
+    const int* nt = P.ntok;
+    if (pass == 0) {
+      src_proj = P.pre_proj; src_act = P.pre_act; src_ag = P.pre_ag; Ts = P.pre_T;
+      nt = P.pre_ntok;
+    } else {
+      src_proj = P.proj; src_act = P.act; src_ag = P.alpha_gate; Ts = P.T;
+    }
+    const int ntok = nt ? min(max(nt[b], 1), Ts) : Ts;
+    const bool outp = pass == 1 && P.write_out;
+    Tok nxt;
+    load_tok(0, nxt);
+    for (int t = 0; t < ntok; ++t) {
+      const int n = b * Ts + t;
+      Tok cur = nxt;
+      if (t + 1 < ntok) load_tok(t + 1, nxt);
+      float (&qv)[RPT] = cur.qv;
+      float (&kv)[RPT] = cur.kv;
+      float (&al)[RPT] = cur.al;
+      float (&v4)[4] = cur.v4;
+      const float4 gate = cur.gate;
+      const float beta = sigmoid_f(cur.braw);
+      // L2 norms over the head's DK rows: local rows, then the 8 row groups
+      float aq = 0.0f, ak = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) { aq += qv[i] * qv[i]; ak += kv[i] * kv[i]; }
-    const float inv_q = P.q_scale / sqrtf(rowsum<RG>(aq) + P.l2_eps);
-    const float inv_k = 1.0f / sqrtf(rowsum<RG>(ak) + P.l2_eps);
+      for (int i = 0; i < RPT; ++i) { aq += qv[i] * qv[i]; ak += kv[i] * kv[i]; }
+      const float inv_q = P.q_scale / sqrtf(rowsum<RG>(aq) + P.l2_eps);
+      const float inv_k = 1.0f / sqrtf(rowsum<RG>(ak) + P.l2_eps);
 
-    float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+      float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float a = al[i], kk = kv[i] * inv_k;
-      st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
-      e0 += st[i].x * kk; e1 += st[i].y * kk; e2 += st[i].z * kk; e3 += st[i].w * kk;
-    }
-    e0 = rowsum<RG>(e0); e1 = rowsum<RG>(e1); e2 = rowsum<RG>(e2); e3 = rowsum<RG>(e3);
-    const float d0 = beta * (v4[0] - e0), d1 = beta * (v4[1] - e1);
-    const float d2 = beta * (v4[2] - e2), d3 = beta * (v4[3] - e3);
-    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const float kk = kv[i] * inv_k, qq = qv[i] * inv_q;
-      st[i].x += kk * d0; st[i].y += kk * d1; st[i].z += kk * d2; st[i].w += kk * d3;
-      o0 += st[i].x * qq; o1 += st[i].y * qq; o2 += st[i].z * qq; o3 += st[i].w * qq;
-    }
-    o0 = rowsum<RG>(o0); o1 = rowsum<RG>(o1); o2 = rowsum<RG>(o2); o3 = rowsum<RG>(o3);
-    if (P.write_out) {
-      if (rg == 0) {
-        const size_t g = (size_t)n * H * dv + h * dv + j;
-        *reinterpret_cast<float4*>(P.o + g) = make_float4(o0, o1, o2, o3);
-        *reinterpret_cast<float4*>(P.gate + g) = gate;
+      for (int i = 0; i < RPT; ++i) {
+        const float a = al[i], kk = kv[i] * inv_k;
+        st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
+        e0 += st[i].x * kk; e1 += st[i].y * kk; e2 += st[i].z * kk; e3 += st[i].w * kk;
       }
-      // o^2 over the wave's columns: each row of 16 lanes holds 16 / RG column quads
-      float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
-      if constexpr (RG == 8) q2 += dpp_mov<kDppRor8>(q2);
-      const int qb = __float_as_int(q2);
-      const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
-                        (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
-      if (lane == 0) P.ss[((size_t)n * H + h) * nparts + cb] = tot;
-    }
-  }
-
-  if (P.write_state && (!P.active || P.active[b])) {
+      e0 = rowsum<RG>(e0); e1 = rowsum<RG>(e1); e2 = rowsum<RG>(e2); e3 = rowsum<RG>(e3);
+      const float d0 = beta * (v4[0] - e0), d1 = beta * (v4[1] - e1);
+      const float d2 = beta * (v4[2] - e2), d3 = beta * (v4[3] - e3);
+      float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];
+      for (int i = 0; i < RPT; ++i) {
+        const float kk = kv[i] * inv_k, qq = qv[i] * inv_q;
+        st[i].x += kk * d0; st[i].y += kk * d1; st[i].z += kk * d2; st[i].w += kk * d3;
+        o0 += st[i].x * qq; o1 += st[i].y * qq; o2 += st[i].z * qq; o3 += st[i].w * qq;
+      }
+      if (outp) {
+        o0 = rowsum<RG>(o0); o1 = rowsum<RG>(o1); o2 = rowsum<RG>(o2); o3 = rowsum<RG>(o3);
+        if (rg == 0) {
+          const size_t g = (size_t)n * H * dv + h * dv + j;
+          *reinterpret_cast<float4*>(P.o + g) = make_float4(o0, o1, o2, o3);
+          *reinterpret_cast<float4*>(P.gate + g) = gate;
+        }
+        // o^2 over the wave's columns: each row of 16 lanes holds 16 / RG column quads
+        float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
+        if constexpr (RG == 8) q2 += dpp_mov<kDppRor8>(q2);
+        const int qb = __float_as_int(q2);
+        const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
+                          (__int_as_float(__builtin_amdgcn_readlane(qb, 32)) + __int_as_float(__builtin_amdgcn_readlane(qb, 48)));
+        if (lane == 0) P.ss[((size_t)n * H + h) * nparts + cb] = tot;
+      }
+    }
+    if (pass == 0 || (P.write_state && (!P.active || P.active[b]))) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];
+    }
   }
 
   // commit: the window becomes the last 3 of (window, p_0 .. p_{a-1}) per (sequence,
@@ -456,15 +469,31 @@ hipError_t launch_head(const HeadParams& p, hipStream_t s) {
 }
 
 // Conv + SiLU over a sequence's T tokens, one thread per (channel, sequence); the window is
-// read, not rolled (verify leaves the state as committed).
-__global__ void conv_seq_kernel(const float* __restrict__ plog, int stride,
-                                const float* __restrict__ win, const float* __restrict__ conv_w,
-                                float* __restrict__ act, int T, int C) {
+// read, not rolled (verify leaves the state as committed), except for the roll by a
+// previous verify's accepted tokens when a commit is folded in.
+__global__ void conv_seq_kernel(const float* __restrict__ plog, int stride, float* __restrict__ win,
+                                const float* __restrict__ conv_w, float* __restrict__ act, int T,
+                                int C, const float* __restrict__ pre_plog,
+                                const int* __restrict__ pre_ntok, int pre_T) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   const int b = blockIdx.y;
   if (c >= C) return;
-  const float* z = win + (size_t)b * 3 * C + c;
-  float z0 = z[0], z1 = z[C], z2 = z[2 * C];
+  float* z = win + (size_t)b * 3 * C + c;
+  float z0, z1, z2;
+  if (pre_ntok) {
+    const int a = min(max(pre_ntok[b], 1), pre_T);
+    const float* pp = pre_plog + (size_t)b * pre_T * stride + c;
+    z0 = a < 3 ? z[(size_t)a * C] : pp[(size_t)(a - 3) * stride];
+    z1 = a < 2 ? z[(size_t)(a + 1) * C] : pp[(size_t)(a - 2) * stride];
+    z2 = pp[(size_t)(a - 1) * stride];
+    z[0] = z0;
+    z[C] = z1;
+    z[2 * C] = z2;
+  } else {
+    z0 = z[0];
+    z1 = z[C];
+    z2 = z[2 * C];
+  }
   const float4 w = *reinterpret_cast<const float4*>(conv_w + (size_t)c * 4);
   // tokens in groups of 8, each group's projections requested together
   for (int t0 = 0; t0 < T; t0 += 8) {
@@ -484,10 +513,12 @@ __global__ void conv_seq_kernel(const float* __restrict__ plog, int stride,
   }
 }
 
-hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
-                           const float* conv_w, float* act, int B, int T, int C, hipStream_t s) {
+hipError_t launch_conv_seq(const float* plog, int proj_stride, float* win, const float* conv_w,
+                           float* act, int B, int T, int C, const float* pre_plog,
+                           const int* pre_ntok, int pre_T, hipStream_t s) {
   dim3 grid((C + 255) / 256, B);
-  conv_seq_kernel<<<grid, 256, 0, s>>>(plog, proj_stride, win, conv_w, act, T, C);
+  conv_seq_kernel<<<grid, 256, 0, s>>>(plog, proj_stride, win, conv_w, act, T, C, pre_plog,
+                                       pre_ntok, pre_T);
   return hipGetLastError();
 }
 

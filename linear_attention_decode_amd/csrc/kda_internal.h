@@ -109,6 +109,12 @@ struct GemvParams {
   // conv over sequence b's window and its tokens 0..t, the window left as it is
   float* act = nullptr;           // [N][C]
   int T = 0;
+  // verify with a commit folded in: the window first moves on by the previous verify's
+  // accepted tokens, pre_ntok[b] of them (clamped 1..pre_T), whose pre-conv projections
+  // are rows b pre_T + t of pre_proj ([B pre_T][out_stride]), and is written back
+  const float* pre_proj = nullptr;
+  const int* pre_ntok = nullptr;
+  int pre_T = 0;
 };
 
 constexpr int kGemvKSmall = 2048;   // input length of the multi-column variants
@@ -149,6 +155,15 @@ struct HeadParams {
   // [B] or null: a sequence with active[b] == 0 keeps its state (its outputs are still
   // computed from it)
   const int* active = nullptr;
+  // verify with a commit folded in (pre_ntok != null): first the previous verify's accepted
+  // tokens, pre_ntok[b] of them (clamped 1..pre_T), replayed from its log (rows
+  // n = b pre_T + t of pre_proj / pre_act / pre_ag, laid out as proj / act / alpha_gate),
+  // and the state written back once; then this call's T tokens as above
+  const float* pre_proj = nullptr;
+  const float* pre_act = nullptr;
+  const float* pre_ag = nullptr;
+  const int* pre_ntok = nullptr;
+  int pre_T = 0;
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
@@ -177,8 +192,12 @@ bool head_supported(int dk, int wt, int rank_f, int rank_g);
 
 // Conv + SiLU over T tokens per sequence from the committed window (left unchanged):
 // act[b*T + t][c] from the pre-conv projections plog[b*T + t][c] (stride proj_stride).
-hipError_t launch_conv_seq(const float* plog, int proj_stride, const float* win,
-                           const float* conv_w, float* act, int B, int T, int C, hipStream_t s);
+// With pre_ntok (a commit folded in) the window first moves on by the previous verify's
+// accepted tokens (pre_ntok[b], clamped 1..pre_T, rows b pre_T + t of pre_plog) and is
+// written back.
+hipError_t launch_conv_seq(const float* plog, int proj_stride, float* win, const float* conv_w,
+                           float* act, int B, int T, int C, const float* pre_plog,
+                           const int* pre_ntok, int pre_T, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------
 // Chunked prefill.

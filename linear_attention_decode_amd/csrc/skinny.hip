@@ -182,6 +182,9 @@ struct SkParams {
   float* act = nullptr;
   int T = 0;
   const int* active = nullptr;
+  const float* pre_proj = nullptr;
+  const int* pre_ntok = nullptr;
+  int pre_T = 0;
 };
 
 // 8 weight bytes u -> 8 fp16 values 1024 + u (byte permutes against 0x64 high bytes)
@@ -348,15 +351,31 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   }
   if (sg.conv_chan >= 0 && P.act) {
     // verify: each (row, sequence) runs the causal conv + SiLU over the sequence's window
-    // and its T tokens in order; the window is read, not rolled (the commit rolls it)
+    // and its T tokens in order; the window is read, not rolled (the commit rolls it), but
+    // a commit folded into this verify first moves it on by the previous verify's accepted
+    // tokens, from that verify's logged projections, and writes it back
     __syncthreads();
     const int nb = P.N / P.T;
     for (int e = tid; e < nrows * nb; e += kSkThreads) {
       const int row = e / nb, b = e - row * nb;
       const int c = sg.conv_chan + row0 + row;
       const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
-      const float* z = P.win + (size_t)b * 3 * P.C + c;
-      float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
+      float* z = P.win + (size_t)b * 3 * P.C + c;
+      float z0, z1, z2;
+      if (P.pre_ntok) {
+        const int a = min(max(P.pre_ntok[b], 1), P.pre_T);
+        const float* pp = P.pre_proj + (size_t)b * P.pre_T * P.out_stride + sg.out_off + row0 + row;
+        z0 = a < 3 ? z[(size_t)a * P.C] : pp[(size_t)(a - 3) * P.out_stride];
+        z1 = a < 2 ? z[(size_t)(a + 1) * P.C] : pp[(size_t)(a - 2) * P.out_stride];
+        z2 = pp[(size_t)(a - 1) * P.out_stride];
+        z[0] = z0;
+        z[P.C] = z1;
+        z[2 * P.C] = z2;
+      } else {
+        z0 = z[0];
+        z1 = z[P.C];
+        z2 = z[2 * P.C];
+      }
       for (int t = 0; t < P.T; ++t) {
         const float pv = s_row[row][b * P.T + t];
         const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * pv;
@@ -394,6 +413,9 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.act = g.act;
   p.T = g.T;
   p.active = g.active;
+  p.pre_proj = g.pre_proj;
+  p.pre_ntok = g.pre_ntok;
+  p.pre_T = g.pre_T;
   const int KG = g.K / 2048;
   if (prologue == kProX) {
     if (KG == 2) skinny_prep_kernel<kProX, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_abi_version(L):
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3
 
 
 def test_packed_bytes(L):
@@ -104,3 +104,14 @@ def test_model_create_rejects_null_and_unaligned(L):
 def test_status_strings(L):
     for s in range(8):
         assert L.kda_status_string(s)
+
+
+def test_verify_calls_validate_before_launch(L):
+    """Null model or state pointers are refused by the verify, commit and flush calls."""
+    from linear_attention_decode_amd import _lib
+    p = C.c_void_p(4096)
+    st = _lib.KdaState(None, None, 1)
+    assert L.kda_state_flush(None, C.byref(st), None) == _lib.KDA_E_ARG
+    assert L.kda_verify_commit(None, C.byref(st), p, 1 << 20, 4, p, None) == _lib.KDA_E_ARG
+    assert L.kda_verify_steps(None, p, 4, p, C.byref(st), p, 1 << 20, p, 1 << 20, None) == _lib.KDA_E_ARG
+    assert L.kda_verify_log_bytes(None, 1, 4) == 0

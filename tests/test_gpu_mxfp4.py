@@ -110,6 +110,7 @@ def test_verify_and_scan_mxfp4():
             assert range_rel(yy[b], ry) <= OUT_RTOL
             for l in range(2):
                 S[l][b], Z[l][b] = s2[l], z2[l]
+    model.flush(st)
     assert np.abs(st.S.cpu().numpy() - np.array([[S[l][b] for b in range(2)] for l in range(2)])).max() <= STATE_ATOL
     # then a scan prefill of 10 tokens from the committed state
     _say("  scan prefill 10 tokens from the committed state")
