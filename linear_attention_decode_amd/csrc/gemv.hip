@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
           const int c = sg.conv_chan + row;
           const float4 w = ep_w[r];
           float* z = P.win + (size_t)n * 3 * P.C + c;
-          const float y = w.x * ep_z[r][0] + w.y * ep_z[r][1] + w.z * ep_z[r][2] + w.w * v;
+          const float y = conv4_f(w, ep_z[r][0], ep_z[r][1], ep_z[r][2], v);
           if (!P.active || P.active[n]) {
             z[0] = ep_z[r][1];
             z[P.C] = ep_z[r][2];

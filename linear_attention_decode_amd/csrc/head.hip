@@ -13,6 +13,8 @@
 // Value columns are independent, so each wave owns 32 of them with the whole key
 // dimension in registers and needs no other wave; the state is read once and written
 // once per call (verify keeps it in registers across its tokens and writes nothing).
+#include <utility>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -314,6 +316,22 @@ __device__ __forceinline__ float rowsum(float v) {
   else return sum16(v);
 }
 
+// f(integral_constant<U>) for U = FIRST, FIRST + 1, ... while U < n (at most LAST - 1),
+// each call nested inside the test of the one before
+template <int U, int LAST, typename F>
+__device__ __forceinline__ void unroll_nested(int n, F& f) {
+  if constexpr (U < LAST) {
+    if (U < n) {
+      f(std::integral_constant<int, U>{});
+      unroll_nested<U + 1, LAST>(n, f);
+    }
+  }
+}
+
+// token steps unrolled per round of the head kernel's token loop (even: the two input sets
+// alternate), enough for a verify with a folded commit (at most 8 + 8 tokens) in one round
+constexpr int kHeadUnroll = 16;
+
 template <int DK, int CW>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   constexpr int RG = 256 / CW;
@@ -336,23 +354,25 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   const int cq0 = h * DK + r0, ck0 = K + h * DK + r0, cv0 = 2 * K + h * dv + j;
 
   // token inputs (q, k rows and v columns of this lane; alpha rows; gate columns; beta),
-  // requested one token ahead of their use
+  // requested two tokens ahead of their use
   struct Tok {
     float qv[RPT], kv[RPT], al[RPT], v4[4];
     float4 gate;
     float braw;
   };
-  // pass 0 (a commit folded into this verify): the previous verify's accepted tokens from
-  // its log, state only, then the state written back; pass 1: this call's tokens
-  const float* src_proj = P.proj;
-  const float* src_act = P.act;
-  const float* src_ag = P.alpha_gate;
-  int Ts = P.T;
-  auto load_tok = [&](int t, Tok& x) {
-    const int n = b * Ts + t;
-    const float* prow = src_proj + (size_t)n * P.proj_stride;
-    const float* arow = src_act ? src_act + (size_t)n * C : prow;   // activated q | k | v
-    const float* ag = src_ag + (size_t)n * (K + H * dv);
+  // One sequence of tokens: first (a commit folded into this verify) the previous verify's
+  // accepted tokens from its log, state only, after which the state is written back; then
+  // this call's tokens
+  const int a_pre = P.pre_ntok ? min(max(P.pre_ntok[b], 1), P.pre_T) : 0;
+  const int a_cur = P.ntok ? min(max(P.ntok[b], 1), P.T) : P.T;
+  const int total = a_pre + a_cur;
+  auto load_tok = [&](int u, Tok& x) __attribute__((always_inline)) {
+    const bool pre = u < a_pre;
+    const int n = pre ? b * P.pre_T + u : b * P.T + (u - a_pre);
+    const float* prow = (pre ? P.pre_proj : P.proj) + (size_t)n * P.proj_stride;
+    const float* sact = pre ? P.pre_act : P.act;
+    const float* arow = sact ? sact + (size_t)n * C : prow;   // activated q | k | v
+    const float* ag = (pre ? P.pre_ag : P.alpha_gate) + (size_t)n * (K + H * dv);
 #pragma unroll
     for (int i = 0; i < RPT; i += 4) {
       const float4 a = *reinterpret_cast<const float4*>(arow + cq0 + i);
@@ -367,32 +387,25 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
     x.braw = prow[C + rl + h];
   };
-  for (int pass = P.pre_ntok ? 0 : 1; pass < 2; ++pass) {
-    const int* nt = P.ntok;
-    if (pass == 0) {
-      src_proj = P.pre_proj; src_act = P.pre_act; src_ag = P.pre_ag; Ts = P.pre_T;
-      nt = P.pre_ntok;
-    } else {
-      src_proj = P.proj; src_act = P.act; src_ag = P.alpha_gate; Ts = P.T;
-    }
-    const int ntok = nt ? min(max(nt[b], 1), Ts) : Ts;
-    const bool outp = pass == 1 && P.write_out;
-    Tok nxt;
-    load_tok(0, nxt);
-    for (int t = 0; t < ntok; ++t) {
-      const int n = b * Ts + t;
-      Tok cur = nxt;
-      if (t + 1 < ntok) load_tok(t + 1, nxt);
-      float (&qv)[RPT] = cur.qv;
-      float (&kv)[RPT] = cur.kv;
-      float (&al)[RPT] = cur.al;
-      float (&v4)[4] = cur.v4;
-      const float4 gate = cur.gate;
-      const float beta = sigmoid_f(cur.braw);
-      // L2 norms over the head's DK rows: local rows, then the 8 row groups
+  // token u of the sequence from the inputs in x: state update, outputs (this call's
+  // tokens), and the state written back after the last replayed token.  Every
+  // multiply-add is an explicit fma, so each unrolled copy rounds the same way (a token's
+  // results do not depend on its position in the launch: a folded commit gives the bits
+  // of a separate replay)
+  auto process = [&](const Tok& x, int u) __attribute__((always_inline)) {
+    const bool outp = u >= a_pre && P.write_out;
+    const int n = b * P.T + (u - a_pre);
+    {
+      const float (&qv)[RPT] = x.qv;
+      const float (&kv)[RPT] = x.kv;
+      const float (&al)[RPT] = x.al;
+      const float (&v4)[4] = x.v4;
+      const float4 gate = x.gate;
+      const float beta = sigmoid_f(x.braw);
+      // L2 norms over the head's DK rows: local rows, then the row groups
       float aq = 0.0f, ak = 0.0f;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) { aq += qv[i] * qv[i]; ak += kv[i] * kv[i]; }
+      for (int i = 0; i < RPT; ++i) { aq = __builtin_fmaf(qv[i], qv[i], aq); ak = __builtin_fmaf(kv[i], kv[i], ak); }
       const float inv_q = P.q_scale / sqrtf(rowsum<RG>(aq) + P.l2_eps);
       const float inv_k = 1.0f / sqrtf(rowsum<RG>(ak) + P.l2_eps);
 
@@ -401,7 +414,8 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
       for (int i = 0; i < RPT; ++i) {
         const float a = al[i], kk = kv[i] * inv_k;
         st[i].x *= a; st[i].y *= a; st[i].z *= a; st[i].w *= a;
-        e0 += st[i].x * kk; e1 += st[i].y * kk; e2 += st[i].z * kk; e3 += st[i].w * kk;
+        e0 = __builtin_fmaf(st[i].x, kk, e0); e1 = __builtin_fmaf(st[i].y, kk, e1);
+        e2 = __builtin_fmaf(st[i].z, kk, e2); e3 = __builtin_fmaf(st[i].w, kk, e3);
       }
       e0 = rowsum<RG>(e0); e1 = rowsum<RG>(e1); e2 = rowsum<RG>(e2); e3 = rowsum<RG>(e3);
       const float d0 = beta * (v4[0] - e0), d1 = beta * (v4[1] - e1);
@@ -410,8 +424,10 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const float kk = kv[i] * inv_k, qq = qv[i] * inv_q;
-        st[i].x += kk * d0; st[i].y += kk * d1; st[i].z += kk * d2; st[i].w += kk * d3;
-        o0 += st[i].x * qq; o1 += st[i].y * qq; o2 += st[i].z * qq; o3 += st[i].w * qq;
+        st[i].x = __builtin_fmaf(kk, d0, st[i].x); st[i].y = __builtin_fmaf(kk, d1, st[i].y);
+        st[i].z = __builtin_fmaf(kk, d2, st[i].z); st[i].w = __builtin_fmaf(kk, d3, st[i].w);
+        o0 = __builtin_fmaf(st[i].x, qq, o0); o1 = __builtin_fmaf(st[i].y, qq, o1);
+        o2 = __builtin_fmaf(st[i].z, qq, o2); o3 = __builtin_fmaf(st[i].w, qq, o3);
       }
       if (outp) {
         o0 = rowsum<RG>(o0); o1 = rowsum<RG>(o1); o2 = rowsum<RG>(o2); o3 = rowsum<RG>(o3);
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
           *reinterpret_cast<float4*>(P.gate + g) = gate;
         }
         // o^2 over the wave's columns: each row of 16 lanes holds 16 / RG column quads
-        float q2 = o0 * o0 + o1 * o1 + o2 * o2 + o3 * o3;
+        float q2 = __builtin_fmaf(o3, o3, __builtin_fmaf(o2, o2, __builtin_fmaf(o1, o1, o0 * o0)));
         if constexpr (RG == 8) q2 += dpp_mov<kDppRor8>(q2);
         const int qb = __float_as_int(q2);
         const float tot = (__int_as_float(__builtin_amdgcn_readlane(qb, 0)) + __int_as_float(__builtin_amdgcn_readlane(qb, 16))) +
@@ -429,11 +445,37 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
         if (lane == 0) P.ss[((size_t)n * H + h) * nparts + cb] = tot;
       }
     }
-    if (pass == 0 || (P.write_state && (!P.active || P.active[b]))) {
+    if (u + 1 == a_pre) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
         *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];
     }
+  };
+  // two input sets in flight, used in turn; the token loop is unrolled into rounds of
+  // nested steps (step u runs only after steps 0 .. u-1), so the compiler sees exactly
+  // which loads are still outstanding at each use and waits for one set while the other's
+  // are in flight; past the last token the loads repeat it
+  Tok x0, x1;
+  load_tok(0, x0);
+  load_tok(min(1, total - 1), x1);
+  for (int base = 0; base < total; base += kHeadUnroll) {
+    auto step = [&](auto uc) __attribute__((always_inline)) {
+      constexpr int k = decltype(uc)::value;
+      const int u = base + k;
+      if constexpr ((k & 1) == 0) {
+        process(x0, u);
+        load_tok(min(u + 2, total - 1), x0);
+      } else {
+        process(x1, u);
+        load_tok(min(u + 2, total - 1), x1);
+      }
+    };
+    unroll_nested<0, kHeadUnroll>(total - base, step);
+  }
+  if (P.write_state && (!P.active || P.active[b])) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      *reinterpret_cast<float4*>(Sb + (size_t)(r0 + i) * dv) = st[i];
   }
 
   // commit: the window becomes the last 3 of (window, p_0 .. p_{a-1}) per (sequence,
@@ -503,7 +545,7 @@ __global__ void conv_seq_kernel(const float* __restrict__ plog, int stride, floa
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if (t0 + t < T) {
-        const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * p[t];
+        const float y = conv4_f(w, z0, z1, z2, p[t]);
         z0 = z1;
         z1 = z2;
         z2 = p[t];

@@ -9,6 +9,14 @@
 
 namespace kda {
 
+// Causal depthwise conv of one channel over (window z0, z1, z2 oldest first, this token x)
+// with taps w: one fixed chain of fused multiply-adds, so every per-layer kernel that
+// computes it (decode, verify, the sequential scan) gets the same bits whatever the
+// compiler would have contracted
+__device__ __forceinline__ float conv4_f(const float4 w, float z0, float z1, float z2, float x) {
+  return __builtin_fmaf(w.w, x, __builtin_fmaf(w.z, z2, __builtin_fmaf(w.y, z1, w.x * z0)));
+}
+
 enum WType { kF32 = 0, kBF16 = 1, kQ8 = 2, kMX4 = 3 };
 enum GateForm { kGateKda = 0, kGateSafe = 1, kGateScalar = 2 };
 
@@ -127,7 +135,7 @@ int gemv_cols_per_pass(int N);
 // ---------------------------------------------------------------------------------------
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
 // ---------------------------------------------------------------------------------------
-constexpr int kHeadCols = 32;      // value columns per wave (one partial sum of o^2 each)
+constexpr int kHeadCols = 16;      // value columns per wave (one partial sum of o^2 each)
 
 struct HeadParams {
   int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;

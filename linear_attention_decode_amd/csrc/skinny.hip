@@ -245,7 +245,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   uint2 a[KB4];
 #pragma unroll
   for (int j = 0; j < KB4; ++j) {
-    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32));
+    const u32x2 v = *reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32);
     a[j] = make_uint2(v.x, v.y);
   }
   // B operand: a ring of PD k blocks of hi/lo fragments ahead of the MFMAs
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
       const float4 w = *reinterpret_cast<const float4*>(P.conv_w + (size_t)c * 4);
       float* z = P.win + (size_t)n * 3 * P.C + c;
       const float z0 = z[0], z1 = z[P.C], z2 = z[2 * P.C];
-      const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * v;
+      const float y = conv4_f(w, z0, z1, z2, v);
       if (!P.active || P.active[n]) {
         z[0] = z1;
         z[P.C] = z2;
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
       }
       for (int t = 0; t < P.T; ++t) {
         const float pv = s_row[row][b * P.T + t];
-        const float y = w.x * z0 + w.y * z1 + w.z * z2 + w.w * pv;
+        const float y = conv4_f(w, z0, z1, z2, pv);
         z0 = z1;
         z1 = z2;
         z2 = pv;
