@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import (KDA_BF16, KDA_F32, KDA_Q8_0, KDA_MXFP4, KDA_OP_DECODE, KDA_OP_PREFILL, KDA_OP_SCAN,  # noqa: F401
                    KDA_OP_VERIFY, KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_K_PROJ, KDA_K_HEAD,
                    KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, KDA_K_GEMM, KDA_K_CHUNK,
-                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, DTYPES, KdaError,
+                   KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE, KDA_Q_PERSISTENT, KDA_Q_OWNS_WEIGHTS, DTYPES, KdaError,
                    KDA_GATE_KDA, KDA_GATE_SAFE, KDA_GATE_SCALAR, GATES)
 
 _PROJ_NAMES = ("wq", "wk", "wv", "wo", "fa", "fb", "wbeta", "ga", "gb")
@@ -285,6 +285,19 @@ class KdaModel:
     def packed(self, l: int, name: str):
         """Packed device buffer of matrix `name` of layer `l`."""
         return self._packed[(l, name)]
+
+    def owns_weights(self) -> bool:
+        """True if the library reads only its own copy of the packed matrices."""
+        return kda_model_query(self.handle, KDA_Q_OWNS_WEIGHTS) == 1
+
+    def release_packed(self) -> bool:
+        """Drop the packed buffers this binding made, if the model no longer reads them."""
+        if not self.owns_weights():
+            return False
+        ids = {id(b) for b in self._packed.values()}
+        self._keep = [t for t in self._keep if id(t) not in ids]
+        self._packed = {}
+        return True
 
     def new_state(self, batch: int) -> KdaStateBuf:
         return KdaStateBuf(self.n_layers, batch, self.n_heads, self.d_k, self.d_v,

@@ -15,6 +15,7 @@ KDA_F32, KDA_BF16, KDA_Q8_0, KDA_MXFP4 = 0, 1, 2, 3
 KDA_OP_DECODE, KDA_OP_VERIFY, KDA_OP_PREFILL, KDA_OP_SCAN = 0, 1, 2, 3
 KDA_OPT_GRAPH, KDA_OPT_TIMING, KDA_OPT_PERSISTENT, KDA_OPT_WAIT_US, KDA_OPT_COOPERATIVE = 0, 1, 2, 3, 4
 KDA_Q_PERSISTENT = 0
+KDA_Q_OWNS_WEIGHTS = 1
 KDA_K_PROJ, KDA_K_HEAD, KDA_K_OUT, KDA_K_COMMIT, KDA_K_PREFILL, KDA_K_GATES, KDA_K_STEP, \
     KDA_K_GEMM, KDA_K_CHUNK = range(9)
 DTYPES = {"f32": KDA_F32, "bf16": KDA_BF16, "q8_0": KDA_Q8_0, "mxfp4": KDA_MXFP4}

@@ -48,7 +48,14 @@ struct LayerDev {
   const float* a_log;
   const float* dt_bias;
   const float* o_norm_w;
-  // F_b and G_b in gate-tile order (the one-launch decode's copy; null without it)
+  // The model's own copy of the Q8_0 weights in matrix-core order (made for one-launch
+  // eligible stacks; null otherwise): the fused projection rows and W_o (bytes and scales),
+  // F_b and G_b in gate-tile order.  Where it exists every kernel reads it and never the
+  // caller's packed buffers.
+  const int8_t* pw = nullptr;
+  const uint16_t* pd = nullptr;
+  const int8_t* ow = nullptr;
+  const uint16_t* od = nullptr;
   const int8_t* fbw = nullptr;
   const uint16_t* fbd = nullptr;
   const int8_t* gbw = nullptr;
@@ -134,10 +141,12 @@ WsLayout ws_layout(const kda_model* m, int64_t N) {
   w.o = off;    off = align_up(off + (size_t)N * m->V * 4, 256);
   w.gate = off; off = align_up(off + (size_t)N * m->V * 4, 256);
   w.ss = off;   off = align_up(off + (size_t)N * m->d.n_heads * (m->d.d_v / kHeadCols) * 4, 256);
-  // MFMA column-fragment scratch of the skinny projections (Q8_0 with 9..64 columns)
+  // MFMA column-fragment scratch of the skinny projections (Q8_0 with 9..64 columns, or
+  // 1..64 for a model with its own matrix-core copy)
   const int Kmax = std::max(m->d.d_model, m->V);
   w.sk = off;
-  if (skinny_supported(m->d.wtype, (int)N, m->d.d_model) || skinny_supported(m->d.wtype, (int)N, m->V))
+  if (m->mma_w) off = align_up(off + skinny_scratch_bytes((int)std::min<int64_t>(N, 64), Kmax), 256);
+  else if (skinny_supported(m->d.wtype, (int)N, m->d.d_model) || skinny_supported(m->d.wtype, (int)N, m->V))
     off = align_up(off + skinny_scratch_bytes((int)N, Kmax), 256);
   w.total = off;
   return w;
@@ -217,6 +226,12 @@ void proj_segments(const kda_model* m, const LayerDev& L, GemvParams& p, bool co
   for (int i = 0; i < 6; ++i) {
     GemvSeg& s = p.seg[i];
     s.m = mats[i];
+    if (L.pw) {
+      // the model's copy: each matrix starts at a 16-row tile of the fused rows
+      s.m = PackedMat{};
+      s.m.w = reinterpret_cast<const uint8_t*>(L.pw) + (size_t)off * d.d_model;
+      s.m.d = reinterpret_cast<const __half*>(L.pd) + (size_t)off * (d.d_model / 32);
+    }
     s.rows = rows[i];
     s.first_tile = tile;
     s.out_off = off;
@@ -225,6 +240,7 @@ void proj_segments(const kda_model* m, const LayerDev& L, GemvParams& p, bool co
     off += rows[i];
   }
   p.nseg = 6;
+  p.mma = L.pw ? 1 : 0;
 }
 
 int proj_grid(const GemvParams& p) {
@@ -242,6 +258,36 @@ int enqueue_gates(kda_model* m, const LayerDev& L, const float* proj, int N, flo
   gp.gate = d.gate; gp.gate_lb = d.gate_lb;
   gp.fbw = L.fbw; gp.fbd = L.fbd; gp.gbw = L.gbw; gp.gbd = L.gbd;
   return timed(m, KDA_K_GATES, s, rec, [&] { return launch_gates(gp, s); });
+}
+
+// A matrix-core product over any number of columns, for a model with its own weight copy:
+// launches of at most 64 columns (whole sequences of T tokens each when the verify conv
+// runs in the epilogue), every per-column pointer moved on by the launch's first column.
+hipError_t launch_skinny_cols(int prologue, const GemvParams& g, int T, void* scratch, hipStream_t s) {
+  const int per = g.act ? (64 / T) * T : 64;
+  for (int n0 = 0; n0 < g.N; n0 += per) {
+    GemvParams c = g;
+    c.N = std::min(per, g.N - n0);
+    if (c.x) c.x += (size_t)n0 * g.x_stride;
+    if (c.o) c.o += (size_t)n0 * g.K;
+    if (c.gate) c.gate += (size_t)n0 * g.K;
+    if (c.ss) c.ss += (size_t)n0 * g.H * g.ncb;
+    c.out += (size_t)n0 * g.out_stride;
+    if (c.resid) c.resid += (size_t)n0 * g.out_stride;
+    if (c.act) {
+      const int b0 = n0 / T;
+      c.act += (size_t)n0 * g.C;
+      if (c.win) c.win += (size_t)b0 * 3 * g.C;
+      if (c.pre_proj) c.pre_proj += (size_t)b0 * g.pre_T * g.out_stride;
+      if (c.pre_ntok) c.pre_ntok += b0;
+    } else {
+      if (c.win) c.win += (size_t)n0 * 3 * g.C;
+      if (c.active) c.active += n0;
+    }
+    const hipError_t e = launch_skinny(prologue, c, scratch, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // One layer of decode (T = 1) or verify (T > 1): projections, gates, per-head step, o_proj.
@@ -270,8 +316,11 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   float* gate = reinterpret_cast<float*>(ws + wl.gate);
   float* ss = reinterpret_cast<float*>(ws + wl.ss);
 
-  // verify on the matrix-core path runs its conv in the projection epilogue
-  const bool conv_fused = act && skinny_supported(d.wtype, N, d.d_model);
+  // the matrix-core products: always for a model with its own weight copy (which only they
+  // read), else for 9..64 columns; verify there runs its conv in the projection epilogue
+  const bool mma = L.pw != nullptr;
+  auto use_skinny = [&](int K) { return mma || skinny_supported(d.wtype, N, K); };
+  const bool conv_fused = act && use_skinny(d.d_model);
   GemvParams pp;
   proj_segments(m, L, pp, decode || conv_fused);
   pp.K = d.d_model;
@@ -297,7 +346,8 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   }
   const int g1 = proj_grid(pp);
   int r = timed(m, KDA_K_PROJ, s, rec, [&] {
-    if (skinny_supported(d.wtype, N, pp.K)) return launch_skinny(kProX, pp, ws + wl.sk, s);
+    if (mma) return launch_skinny_cols(kProX, pp, T, ws + wl.sk, s);
+    if (use_skinny(pp.K)) return launch_skinny(kProX, pp, ws + wl.sk, s);
     return launch_gemv(d.wtype, kProX, pp, g1, s);
   });
   if (r) return r;
@@ -342,6 +392,12 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
 
   GemvParams po;
   po.seg[0].m = L.wo;
+  if (mma) {
+    po.seg[0].m = PackedMat{};
+    po.seg[0].m.w = reinterpret_cast<const uint8_t*>(L.ow);
+    po.seg[0].m.d = reinterpret_cast<const __half*>(L.od);
+    po.mma = 1;
+  }
   po.seg[0].rows = d.d_model;
   po.seg[0].first_tile = 0;
   po.seg[0].out_off = 0;
@@ -357,7 +413,8 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   po.resid = d.prenorm_residual ? x_in : nullptr;
   const int g2 = (d.d_model + kGemvRowsPerBlock - 1) / kGemvRowsPerBlock;
   return timed(m, KDA_K_OUT, s, rec, [&] {
-    if (skinny_supported(d.wtype, N, po.K)) return launch_skinny(kProGatedNorm, po, ws + wl.sk, s);
+    if (mma) return launch_skinny_cols(kProGatedNorm, po, T, ws + wl.sk, s);
+    if (use_skinny(po.K)) return launch_skinny(kProGatedNorm, po, ws + wl.sk, s);
     return launch_gemv(d.wtype, kProGatedNorm, po, g2, s);
   });
 }
@@ -683,8 +740,12 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   p.q_blocks = m->C / 48;
   m->pers_blocks = nb;
   m->pers_ok = true;
-  // the per-layer path's many-column gates read the same F_b / G_b copies
+  // the per-layer path reads the same copies (and never the caller's buffers again)
   for (int l = 0; l < d.n_layers; ++l) {
+    m->layers[l].pw = host[l].pw;
+    m->layers[l].pd = host[l].pd;
+    m->layers[l].ow = host[l].ow;
+    m->layers[l].od = host[l].od;
     m->layers[l].fbw = host[l].fbw;
     m->layers[l].fbd = host[l].fbd;
     m->layers[l].gbw = host[l].gbw;
@@ -1078,6 +1139,7 @@ int kda_model_query(const kda_model* m, int what) {
   if (!m) return -1;
   switch (what) {
     case KDA_Q_PERSISTENT: return m->pers_ok ? m->pers_blocks : 0;
+    case KDA_Q_OWNS_WEIGHTS: return m->mma_w ? 1 : 0;
     default: return -1;
   }
 }

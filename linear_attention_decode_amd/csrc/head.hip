@@ -275,7 +275,7 @@ static void launch_gates_wt(const GatesParams& p, hipStream_t s) {
 
 hipError_t launch_gates(const GatesParams& p, hipStream_t s) {
   const int nbq = p.rank / 32;
-  if (p.fbw && p.gate == kGateKda && p.wt == kQ8 && p.N > 1 && (p.rank == 32 || p.rank == 64 || p.rank == 128) &&
+  if (p.fbw && p.gate == kGateKda && p.wt == kQ8 && (p.rank == 32 || p.rank == 64 || p.rank == 128) &&
       p.K % 16 == 0 && p.V % 16 == 0) {
     const dim3 grid(((p.K + p.V) / 16 + 3) / 4, (p.N + kGmCols - 1) / kGmCols);
     if (nbq == 1) gates_mfma_kernel<2><<<grid, 256, 0, s>>>(p);

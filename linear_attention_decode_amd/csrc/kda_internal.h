@@ -123,6 +123,9 @@ struct GemvParams {
   const float* pre_proj = nullptr;
   const int* pre_ntok = nullptr;
   int pre_T = 0;
+  // launch_skinny only: the Q8_0 matrices (seg[i].m: w at the segment's first 16-row tile,
+  // d at its scales) are in the one-launch decode's matrix-core order
+  int mma = 0;
 };
 
 constexpr int kGemvKSmall = 2048;   // input length of the multi-column variants

@@ -7,6 +7,9 @@ namespace kda {
 // True when launch_skinny handles this product: Q8_0 weights, 8 < N <= 64 columns,
 // K in {2048, 4096}.
 bool skinny_supported(int wt, int N, int K);
+// True when launch_skinny handles a product whose Q8_0 matrices are in the one-launch
+// decode's matrix-core order (GemvParams::mma): 1 <= N <= 64 columns, K in {1024, 2048}.
+bool skinny_mma_supported(int N, int K);
 // Device scratch the column preparation needs for N columns of length K.
 size_t skinny_scratch_bytes(int N, int K);
 // Same product, prologue and epilogue as launch_gemv(kQ8, prologue, g, ...), on MFMA.

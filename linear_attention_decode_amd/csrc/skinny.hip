@@ -39,6 +39,8 @@ bool skinny_supported(int wt, int N, int K) {
   return wt == kQ8 && N > 8 && N <= 64 && (K == 2048 || K == 4096);
 }
 
+bool skinny_mma_supported(int N, int K) { return N >= 1 && N <= 64 && (K == 1024 || K == 2048); }
+
 struct SkScratch {
   uint4* fh;        // [K/32][NT][64] fp16 x 8: hi parts, B-operand layout
   uint4* fl;        // same, lo parts
@@ -73,14 +75,15 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// KG = K / 2048 groups of 8 consecutive elements per thread (all loaded in one pass).
+// KG = ceil(K / 2048) groups of 8 consecutive elements per thread (all loaded in one
+// pass; groups past K are empty).
 template <int PRO, int KG>
 __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParams P, int NT,
                                                                  SkScratch S) {
   __shared__ float red[2][4];
   __shared__ float scal[kGemvMaxHeads];
   const int n = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  constexpr int K = KG * 2048;
+  const int K = P.K;
   const bool live = n < P.N;   // block-uniform
   if (PRO == kProGatedNorm && live) {
     if (tid < P.H) {
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParam
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (live) {
+      if (live && k0 < K) {
         if constexpr (PRO == kProX) {
           x = *reinterpret_cast<const float4*>(P.x + (size_t)n * P.x_stride + k0 + 4 * h2);
         } else {
@@ -143,6 +146,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParam
 #pragma unroll
   for (int q = 0; q < KG; ++q) {
     const int k0 = 8 * (tid + kSkThreads * q), kb = k0 >> 5, g = (k0 >> 3) & 3;
+    if (k0 >= K) break;
     _Float16 hi[8], lo[8];
     float s = 0.0f;
 #pragma unroll
@@ -199,7 +203,11 @@ __device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
 }
 
 // NT column tiles of 16; KB4 = K / 128 k blocks per wave.
-template <int NT, int KB4>
+// MMA: the Q8_0 matrices are in the matrix-core order of the one-launch decode (persist.h:
+// per 16-row tile, 16-byte chunks c = ((w * 2U + t) * 2 + h) * 64 + r + 16 g holding row r,
+// bytes 16 h .. + 15 of block 4 (4 t + w) + g as signed q; the tile's scales at
+// ((w * 64 + r + 16 g) * 2U + t)), U = K / 1024.
+template <int NT, int KB4, bool MMA>
 __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
   constexpr int KB = 4 * KB4;
   constexpr int PD = 4;                          // k blocks of B fragments in flight
@@ -226,8 +234,12 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
 #pragma unroll
   for (int u = 0; u < kScLoads; ++u) {
     const int i = min(tid + u * kSkThreads, KB * kSkRows / 8 - 1);
-    const int r = min(i / (KB / 8), nrows - 1), c8 = i % (KB / 8);
-    sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + r) * KB + 8 * c8);
+    if constexpr (MMA) {
+      sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)row0 * KB + 8 * i);
+    } else {
+      const int r = min(i / (KB / 8), nrows - 1), c8 = i % (KB / 8);
+      sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + r) * KB + 8 * c8);
+    }
   }
   constexpr int kXsLoads = (KB * NT * 4 + kSkThreads - 1) / kSkThreads;
   f32x4v xv[kXsLoads];
@@ -245,8 +257,18 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   uint2 a[KB4];
 #pragma unroll
   for (int j = 0; j < KB4; ++j) {
-    const u32x2 v = *reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32);
-    a[j] = make_uint2(v.x, v.y);
+    if constexpr (MMA) {
+      constexpr int U2 = KB4 / 4;                // 2U
+      const int kb = kb0 + j, g = kb & 3, w = (kb >> 2) & 3, t = kb >> 4;
+      const uint8_t* cp = sg.m.w + (size_t)row0 * K +
+                          ((size_t)(((w * U2 + t) * 2 + (ag >> 1)) * 64 + (lane & 15) + 16 * g)) * 16 +
+                          8 * (ag & 1);
+      const u32x2 v = *reinterpret_cast<const u32x2*>(cp);
+      a[j] = make_uint2(v.x ^ 0x80808080u, v.y ^ 0x80808080u);   // q -> q + 128
+    } else {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32);
+      a[j] = make_uint2(v.x, v.y);
+    }
   }
   // B operand: a ring of PD k blocks of hi/lo fragments ahead of the MFMAs
   const u32x4* fh = reinterpret_cast<const u32x4*>(P.S.fh) + lane;
@@ -268,12 +290,21 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     for (int u = 0; u < kScLoads; ++u) {
       const int i = tid + u * kSkThreads;
       if (i < KB * kSkRows / 8) {
-        const int r = i / (KB / 8), c8 = i % (KB / 8);
         const uint32_t w[4] = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const unsigned short bits = (unsigned short)((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-          s_sc[8 * c8 + e][r] = r < nrows ? __ushort_as_half(bits) : __float2half(0.0f);
+          int r, kb;
+          if constexpr (MMA) {
+            constexpr int U2 = KB4 / 4;
+            const int q = 8 * i + e, t = q % U2, L = (q / U2) & 63, wv = q / (U2 * 64);
+            r = L & 15;
+            kb = 4 * (4 * t + wv) + (L >> 4);
+          } else {
+            r = i / (KB / 8);
+            kb = 8 * (i % (KB / 8)) + e;
+          }
+          s_sc[kb][r] = r < nrows ? __ushort_as_half(bits) : __float2half(0.0f);
         }
       }
     }
@@ -427,11 +458,13 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int KB4 = g.K / 128;
-#define KDA_SK_CASE(nt, kb4) \
-  if (NT == nt && KB4 == kb4) skinny_gemm_kernel<nt, kb4><<<tiles, kSkThreads, 0, s>>>(p);
-  KDA_SK_CASE(1, 8) KDA_SK_CASE(2, 8) KDA_SK_CASE(3, 8) KDA_SK_CASE(4, 8)
-  KDA_SK_CASE(1, 16) KDA_SK_CASE(2, 16) KDA_SK_CASE(3, 16) KDA_SK_CASE(4, 16)
-  KDA_SK_CASE(1, 32) KDA_SK_CASE(2, 32) KDA_SK_CASE(3, 32) KDA_SK_CASE(4, 32)
+#define KDA_SK_CASE(nt, kb4, mm) \
+  if (NT == nt && KB4 == kb4 && (g.mma != 0) == mm) skinny_gemm_kernel<nt, kb4, mm><<<tiles, kSkThreads, 0, s>>>(p);
+  KDA_SK_CASE(1, 8, false) KDA_SK_CASE(2, 8, false) KDA_SK_CASE(3, 8, false) KDA_SK_CASE(4, 8, false)
+  KDA_SK_CASE(1, 16, false) KDA_SK_CASE(2, 16, false) KDA_SK_CASE(3, 16, false) KDA_SK_CASE(4, 16, false)
+  KDA_SK_CASE(1, 32, false) KDA_SK_CASE(2, 32, false) KDA_SK_CASE(3, 32, false) KDA_SK_CASE(4, 32, false)
+  KDA_SK_CASE(1, 8, true) KDA_SK_CASE(2, 8, true) KDA_SK_CASE(3, 8, true) KDA_SK_CASE(4, 8, true)
+  KDA_SK_CASE(1, 16, true) KDA_SK_CASE(2, 16, true) KDA_SK_CASE(3, 16, true) KDA_SK_CASE(4, 16, true)
 #undef KDA_SK_CASE
   return hipGetLastError();
 }
