@@ -336,7 +336,11 @@ template <int DK, int CW>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   constexpr int RG = 256 / CW;
   constexpr int RPT = DK / RG;
-  const int cb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // block id = cb * (H B) + h * B + b: the dv / CW waves of one (sequence, head), which
+  // read the same q, k and alpha rows, are H B apart, so on one XCD (blocks go round-robin
+  // over the 8) whenever H B is a multiple of 8, and those rows come from its L2
+  const int hb = (int)blockIdx.x % (P.H * P.B);
+  const int cb = (int)blockIdx.x / (P.H * P.B), h = hb / P.B, b = hb - h * P.B;
   const int lane = threadIdx.x;
   const int rg = lane % RG, cq = lane / RG;
   const int H = P.H, dv = P.dv, C = P.C, K = H * DK;
@@ -482,8 +486,8 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   // channel), a = the accepted tokens; every wave of the grid takes a strided share (the
   // replay above reads the logged activations, never the window)
   if (P.win_commit) {
-    const int nwave = gridDim.x * gridDim.y * gridDim.z;
-    const int wid = (blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x;
+    const int nwave = gridDim.x;
+    const int wid = blockIdx.x;
     for (int i = wid * 64 + lane; i < C * P.B; i += nwave * 64) {
       const int sb = i / C, c = i - sb * C;
       const int a = P.ntok ? min(max(P.ntok[sb], 1), P.T) : P.T;
@@ -502,7 +506,7 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
 }
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
-  dim3 grid(p.dv / kHeadCols, p.H, p.B);
+  const dim3 grid((p.dv / kHeadCols) * p.H * p.B);
   if (p.dk == 128)
     head_kernel<128, kHeadCols><<<grid, 64, 0, s>>>(p);
   else
