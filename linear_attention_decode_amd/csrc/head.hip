@@ -185,6 +185,28 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
   __shared__ float ginv[kGmCols][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.y * kGmCols, nc = min(kGmCols, P.N - n0);
+  // this wave's weight tile, scales, bias and A_log are requested first: they do not depend
+  // on the columns, so their latency overlaps the columns' load and quantisation below
+  const int ftiles = P.K / 16, tau = blockIdx.x * 4 + wave;
+  const bool live = tau < (P.K + P.V) / 16;
+  const bool f = tau < ftiles;
+  const int tl = f ? tau : tau - ftiles;
+  const int m = lane & 15, g = lane >> 4;
+  i32x4g bw0 = {0, 0, 0, 0}, bw1 = {0, 0, 0, 0};
+  float dsc = 0.0f;
+  if (live && g < NB) {
+    const int8_t* bp = (f ? P.fbw : P.gbw) + (size_t)tl * 16 * rank + (g * 16 + m) * 16;
+    bw0 = *reinterpret_cast<const i32x4g*>(bp);
+    bw1 = *reinterpret_cast<const i32x4g*>(bp + NB * 256);
+    const uint16_t* dp = (f ? P.fbd : P.gbd) + ((size_t)tl * NB + g) * 16 + m;
+    dsc = __half2float(__ushort_as_half(*dp));
+  }
+  const int row = 16 * tau + m;              // alpha rows, then gate rows
+  float bias = 0.0f, ah = 0.0f;
+  if (live && f) {
+    bias = P.dt_bias[row];
+    ah = P.a_log[row / P.dk];
+  }
   {
     // thread t: column t / 32, element t % 32 of each 32-element block (a half-wave a block)
     const int cn = tid >> 5, j = tid & 31;
@@ -209,26 +231,7 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
     for (int e = 2 * rank + j; e < 256; e += 32) gpl[cn][3][e] = 0;
   }
   __syncthreads();
-  const int ftiles = P.K / 16, tau = blockIdx.x * 4 + wave;
-  if (tau >= (P.K + P.V) / 16) return;
-  const bool f = tau < ftiles;
-  const int tl = f ? tau : tau - ftiles;
-  const int m = lane & 15, g = lane >> 4;
-  i32x4g bw0 = {0, 0, 0, 0}, bw1 = {0, 0, 0, 0};
-  float dsc = 0.0f;
-  if (g < NB) {
-    const int8_t* bp = (f ? P.fbw : P.gbw) + (size_t)tl * 16 * rank + (g * 16 + m) * 16;
-    bw0 = *reinterpret_cast<const i32x4g*>(bp);
-    bw1 = *reinterpret_cast<const i32x4g*>(bp + NB * 256);
-    const uint16_t* dp = (f ? P.fbd : P.gbd) + ((size_t)tl * NB + g) * 16 + m;
-    dsc = __half2float(__ushort_as_half(*dp));
-  }
-  const int row = 16 * tau + m;              // alpha rows, then gate rows
-  float bias = 0.0f, ah = 0.0f;
-  if (f) {
-    bias = P.dt_bias[row];
-    ah = P.a_log[row / P.dk];
-  }
+  if (!live) return;
   const int8_t* abase = &gpl[0][(m >> 2) == g && g < NB ? (m & 3) : 3][(f ? 0 : rank) + 32 * g];
   const i32x4g zero = {0, 0, 0, 0};
   float res[2];
