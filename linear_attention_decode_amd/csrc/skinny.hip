@@ -202,18 +202,20 @@ __device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
   return __builtin_bit_cast(f16x8, r);
 }
 
-// NT column tiles of 16; KB4 = K / 128 k blocks per wave.
+// NT column tiles of 16; KB4 = K / 128 k blocks per wave; RT row tiles of 16 per block
+// (each wave's B fragments serve all of them).
 // MMA: the Q8_0 matrices are in the matrix-core order of the one-launch decode (persist.h:
 // per 16-row tile, 16-byte chunks c = ((w * 2U + t) * 2 + h) * 64 + r + 16 g holding row r,
 // bytes 16 h .. + 15 of block 4 (4 t + w) + g as signed q; the tile's scales at
 // ((w * 64 + r + 16 g) * 2U + t)), U = K / 1024.
-template <int NT, int KB4, bool MMA>
+template <int NT, int KB4, bool MMA, int RT>
 __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
   constexpr int KB = 4 * KB4;
   constexpr int PD = 4;                          // k blocks of B fragments in flight
-  __shared__ float part[4][NT][64][4];           // per-wave partial outputs
-  __shared__ float s_row[kSkRows][NT * 16];      // verify conv: the block's rows, all columns
-  __shared__ __half s_sc[KB][kSkRows];           // [k block][row] Q8_0 scales
+  constexpr int ROWS = kSkRows * RT;             // weight rows per block
+  __shared__ float part[4][RT][NT][64][4];       // per-wave partial outputs
+  __shared__ float s_row[ROWS][NT * 16];         // verify conv: the block's rows, all columns
+  __shared__ __half s_sc[KB][ROWS];              // [k block][row] Q8_0 scales
   __shared__ __align__(16) float s_xs[KB][NT * 16];   // [k block][column] block sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -223,21 +225,25 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
 #pragma unroll
   for (int i = 1; i < kMaxSegs; ++i)
     if (i < P.nseg && (int)blockIdx.x >= P.seg[i].first_tile) sg = P.seg[i];
-  const int row0 = ((int)blockIdx.x - sg.first_tile) * kSkRows;
-  const int nrows = min(kSkRows, sg.rows - row0);
+  const int row0 = ((int)blockIdx.x - sg.first_tile) * ROWS;
+  const int nrows = min(ROWS, sg.rows - row0);
+  // a row tile past the segment's last repeats the first (its rows are not stored)
+  auto tile_of = [&](int rt) { return 16 * rt < nrows ? rt : 0; };
 
   // scales [k block][row] and block sums: loaded first (ahead of the weights in the
   // in-order load counter), stored to LDS after the weight requests are out
   // scales: row r's KB halves are contiguous; 8 per 16-byte load
-  constexpr int kScLoads = (KB * kSkRows / 8 + kSkThreads - 1) / kSkThreads;
+  constexpr int kScPer = KB * kSkRows / 8;       // 16-byte loads per row tile
+  constexpr int kScLoads = (kScPer * RT + kSkThreads - 1) / kSkThreads;
   u32x4 sv[kScLoads];
 #pragma unroll
   for (int u = 0; u < kScLoads; ++u) {
-    const int i = min(tid + u * kSkThreads, KB * kSkRows / 8 - 1);
+    const int i = min(tid + u * kSkThreads, kScPer * RT - 1);
+    const int rt = tile_of(i / kScPer), ii = i % kScPer;
     if constexpr (MMA) {
-      sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)row0 * KB + 8 * i);
+      sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + 16 * rt) * KB + 8 * ii);
     } else {
-      const int r = min(i / (KB / 8), nrows - 1), c8 = i % (KB / 8);
+      const int r = min(16 * rt + ii / (KB / 8), nrows - 1), c8 = ii % (KB / 8);
       sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + r) * KB + 8 * c8);
     }
   }
@@ -249,25 +255,30 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     xv[u] = reinterpret_cast<const f32x4v*>(P.S.xsum)[i];
   }
   __builtin_amdgcn_sched_barrier(0);
-  // A operand: lane holds row (lane & 15), bytes 8 (lane >> 4) .. + 7 of each k block;
-  // the wave's whole K range is requested up front
-  const int ar = min(lane & 15, nrows - 1), ag = lane >> 4;
-  const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K + 8 * ag;
+  // A operand: lane holds row (lane & 15) of each row tile, bytes 8 (lane >> 4) .. + 7 of
+  // each k block; the wave's whole K range is requested up front
+  const int ag = lane >> 4;
   const int kb0 = wave * KB4;
-  uint2 a[KB4];
+  uint2 a[RT][KB4];
 #pragma unroll
-  for (int j = 0; j < KB4; ++j) {
-    if constexpr (MMA) {
-      constexpr int U2 = KB4 / 4;                // 2U
-      const int kb = kb0 + j, g = kb & 3, w = (kb >> 2) & 3, t = kb >> 4;
-      const uint8_t* cp = sg.m.w + (size_t)row0 * K +
-                          ((size_t)(((w * U2 + t) * 2 + (ag >> 1)) * 64 + (lane & 15) + 16 * g)) * 16 +
-                          8 * (ag & 1);
-      const u32x2 v = *reinterpret_cast<const u32x2*>(cp);
-      a[j] = make_uint2(v.x ^ 0x80808080u, v.y ^ 0x80808080u);   // q -> q + 128
-    } else {
-      const u32x2 v = *reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32);
-      a[j] = make_uint2(v.x, v.y);
+  for (int rt = 0; rt < RT; ++rt) {
+    const int tr = tile_of(rt);
+    const int ar = min(16 * tr + (lane & 15), nrows - 1);
+    const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K + 8 * ag;
+#pragma unroll
+    for (int j = 0; j < KB4; ++j) {
+      if constexpr (MMA) {
+        constexpr int U2 = KB4 / 4;              // 2U
+        const int kb = kb0 + j, g = kb & 3, w = (kb >> 2) & 3, t = kb >> 4;
+        const uint8_t* cp = sg.m.w + (size_t)(row0 + 16 * tr) * K +
+                            ((size_t)(((w * U2 + t) * 2 + (ag >> 1)) * 64 + (lane & 15) + 16 * g)) * 16 +
+                            8 * (ag & 1);
+        const u32x2 v = *reinterpret_cast<const u32x2*>(cp);
+        a[rt][j] = make_uint2(v.x ^ 0x80808080u, v.y ^ 0x80808080u);   // q -> q + 128
+      } else {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(wrow + (size_t)(kb0 + j) * 32);
+        a[rt][j] = make_uint2(v.x, v.y);
+      }
     }
   }
   // B operand: a ring of PD k blocks of hi/lo fragments ahead of the MFMAs
@@ -289,7 +300,8 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
 #pragma unroll
     for (int u = 0; u < kScLoads; ++u) {
       const int i = tid + u * kSkThreads;
-      if (i < KB * kSkRows / 8) {
+      if (i < kScPer * RT) {
+        const int rt = i / kScPer, ii = i % kScPer;
         const uint32_t w[4] = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -297,13 +309,14 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
           int r, kb;
           if constexpr (MMA) {
             constexpr int U2 = KB4 / 4;
-            const int q = 8 * i + e, t = q % U2, L = (q / U2) & 63, wv = q / (U2 * 64);
+            const int q = 8 * ii + e, t = q % U2, L = (q / U2) & 63, wv = q / (U2 * 64);
             r = L & 15;
             kb = 4 * (4 * t + wv) + (L >> 4);
           } else {
-            r = i / (KB / 8);
-            kb = 8 * (i % (KB / 8)) + e;
+            r = ii / (KB / 8);
+            kb = 8 * (ii % (KB / 8)) + e;
           }
+          r += 16 * rt;
           s_sc[kb][r] = r < nrows ? __ushort_as_half(bits) : __float2half(0.0f);
         }
       }
@@ -316,48 +329,60 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   }
   __syncthreads();
 
-  f32x4v acc[NT];
+  f32x4v acc[RT][NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[rt][t] = f32x4v{0.f, 0.f, 0.f, 0.f};
   const int og = lane >> 4, oc = lane & 15;      // output rows 4 og .. + 3, column oc (+ 16 t)
 #pragma unroll
   for (int j = 0; j < KB4; ++j) {
     const int kb = kb0 + j, slot = j % PD;
-    const f16x8 av = bytes_to_f16(a[j]);
-    const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][4 * og]);
-    const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
-    const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
-    const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
-    const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
-    f32x4v o[NT];
+    f32x4v o[RT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bh[slot][t]),
-                                                    f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bl[slot][t]),
-                                                    o[t], 0, 0, 0);
+    for (int rt = 0; rt < RT; ++rt) {
+      const f16x8 av = bytes_to_f16(a[rt][j]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bh[slot][t]),
+                                                          f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bl[slot][t]),
+                                                          o[rt][t], 0, 0, 0);
+      }
     }
     if (j + PD < KB4) load_b(j + PD, slot);
+    float bias[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float bias = 1152.0f * s_xs[kb][t * 16 + oc];
-      acc[t][0] += d0 * (o[t][0] - bias);
-      acc[t][1] += d1 * (o[t][1] - bias);
-      acc[t][2] += d2 * (o[t][2] - bias);
-      acc[t][3] += d3 * (o[t][3] - bias);
+    for (int t = 0; t < NT; ++t) bias[t] = 1152.0f * s_xs[kb][t * 16 + oc];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][16 * rt + 4 * og]);
+      const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
+      const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
+      const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
+      const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[rt][t][0] += d0 * (o[rt][t][0] - bias[t]);
+        acc[rt][t][1] += d1 * (o[rt][t][1] - bias[t]);
+        acc[rt][t][2] += d2 * (o[rt][t][2] - bias[t]);
+        acc[rt][t][3] += d3 * (o[rt][t][3] - bias[t]);
+      }
     }
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
+  for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][t][lane][i] = acc[t][i];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave][rt][t][lane][i] = acc[rt][t][i];
   __syncthreads();
-  // sum the four waves' partials and run the epilogue: thread -> (t, lane, i)
-  for (int e = tid; e < NT * 64 * 4; e += kSkThreads) {
-    const int t = e / 256, l = (e >> 2) & 63, i = e & 3;
-    const int row = 4 * (l >> 4) + i, n = t * 16 + (l & 15);
+  // sum the four waves' partials and run the epilogue: thread -> (rt, t, lane, i)
+  for (int e = tid; e < RT * NT * 64 * 4; e += kSkThreads) {
+    const int rt = e / (NT * 256), t = (e / 256) % NT, l = (e >> 2) & 63, i = e & 3;
+    const int row = 16 * rt + 4 * (l >> 4) + i, n = t * 16 + (l & 15);
     if (row >= nrows || n >= P.N) continue;
-    float v = (part[0][t][l][i] + part[1][t][l][i]) + (part[2][t][l][i] + part[3][t][l][i]);
+    float v = (part[0][rt][t][l][i] + part[1][rt][t][l][i]) + (part[2][rt][t][l][i] + part[3][rt][t][l][i]);
     v *= P.S.cscale[n];
     const int grow = row0 + row;
     if (sg.conv_chan >= 0 && P.act) {
@@ -423,6 +448,11 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   const int NT = (g.N + 15) / 16;
   SkParams p;
   p.nseg = g.nseg;
+  // two 16-row tiles per block (each B fragment used twice) when that still leaves at
+  // least 192 blocks and the operands fit the registers (up to 32 columns, K = 2048)
+  int rows32 = 0;
+  for (int i = 0; i < g.nseg; ++i) rows32 += (g.seg[i].rows + 31) / 32;
+  const int RT = (rows32 >= 192 && NT <= 2 && g.K == 2048) ? 2 : 1;
   int tiles = 0;
   for (int i = 0; i < g.nseg; ++i) {
     p.seg[i].m = g.seg[i].m;
@@ -430,7 +460,7 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
     p.seg[i].first_tile = tiles;
     p.seg[i].out_off = g.seg[i].out_off;
     p.seg[i].conv_chan = g.seg[i].conv_chan;
-    tiles += (g.seg[i].rows + kSkRows - 1) / kSkRows;
+    tiles += (g.seg[i].rows + kSkRows * RT - 1) / (kSkRows * RT);
   }
   p.K = g.K;
   p.N = g.N;
@@ -458,13 +488,15 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int KB4 = g.K / 128;
-#define KDA_SK_CASE(nt, kb4, mm) \
-  if (NT == nt && KB4 == kb4 && (g.mma != 0) == mm) skinny_gemm_kernel<nt, kb4, mm><<<tiles, kSkThreads, 0, s>>>(p);
-  KDA_SK_CASE(1, 8, false) KDA_SK_CASE(2, 8, false) KDA_SK_CASE(3, 8, false) KDA_SK_CASE(4, 8, false)
-  KDA_SK_CASE(1, 16, false) KDA_SK_CASE(2, 16, false) KDA_SK_CASE(3, 16, false) KDA_SK_CASE(4, 16, false)
-  KDA_SK_CASE(1, 32, false) KDA_SK_CASE(2, 32, false) KDA_SK_CASE(3, 32, false) KDA_SK_CASE(4, 32, false)
-  KDA_SK_CASE(1, 8, true) KDA_SK_CASE(2, 8, true) KDA_SK_CASE(3, 8, true) KDA_SK_CASE(4, 8, true)
-  KDA_SK_CASE(1, 16, true) KDA_SK_CASE(2, 16, true) KDA_SK_CASE(3, 16, true) KDA_SK_CASE(4, 16, true)
+#define KDA_SK_CASE(nt, kb4, mm, rt) \
+  if (NT == nt && KB4 == kb4 && (g.mma != 0) == mm && RT == rt) \
+    skinny_gemm_kernel<nt, kb4, mm, rt><<<tiles, kSkThreads, 0, s>>>(p);
+  KDA_SK_CASE(1, 8, false, 1) KDA_SK_CASE(2, 8, false, 1) KDA_SK_CASE(3, 8, false, 1) KDA_SK_CASE(4, 8, false, 1)
+  KDA_SK_CASE(1, 16, false, 1) KDA_SK_CASE(2, 16, false, 1) KDA_SK_CASE(3, 16, false, 1) KDA_SK_CASE(4, 16, false, 1)
+  KDA_SK_CASE(1, 32, false, 1) KDA_SK_CASE(2, 32, false, 1) KDA_SK_CASE(3, 32, false, 1) KDA_SK_CASE(4, 32, false, 1)
+  KDA_SK_CASE(1, 8, true, 1) KDA_SK_CASE(2, 8, true, 1) KDA_SK_CASE(3, 8, true, 1) KDA_SK_CASE(4, 8, true, 1)
+  KDA_SK_CASE(1, 16, true, 1) KDA_SK_CASE(2, 16, true, 1) KDA_SK_CASE(3, 16, true, 1) KDA_SK_CASE(4, 16, true, 1)
+  KDA_SK_CASE(1, 16, false, 2) KDA_SK_CASE(2, 16, false, 2) KDA_SK_CASE(1, 16, true, 2) KDA_SK_CASE(2, 16, true, 2)
 #undef KDA_SK_CASE
   return hipGetLastError();
 }
