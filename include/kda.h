@@ -304,7 +304,8 @@ int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const
  * applied commit.  Every other call that reads or writes st (kda_decode_step and its
  * variants, kda_prefill_scan, kda_prefill_chunked, kda_conv_window_canonical) and
  * kda_state_flush apply a pending commit first, and a verify on st through another log
- * applies that log's.  A caller that reads st's buffers itself, copies them (a snapshot)
+ * applies that log's; a verify of another state through the same log applies a commit
+ * pending in it first.  A caller that reads st's buffers itself, copies them (a snapshot)
  * or frees them, or frees or reuses the log, calls kda_state_flush first (and synchronises
  * as for any asynchronous call).
  *

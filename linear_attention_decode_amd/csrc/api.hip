@@ -586,6 +586,21 @@ int flush_state(kda_model* m, const kda_state* st, hipStream_t s, bool writes,
   return KDA_OK;
 }
 
+// Before a verify writes `log`: a commit pending through the same memory for another state
+// is applied first (its rows are about to be overwritten), and that state's uncommitted
+// verify through it is retired.
+int flush_log(kda_model* m, const void* log, const kda_state* st, hipStream_t s) {
+  for (auto& rc : m->logs) {
+    if (rc.log != log || same_state(rc, st)) continue;
+    if (rc.pend_half >= 0) {
+      const int r = apply_commit(m, rc, s, false);
+      if (r) return r;
+    }
+    rc.last_half = -1;
+  }
+  return KDA_OK;
+}
+
 // The record of (state, log), made if there is none; records with nothing left to commit or
 // apply are dropped first.  At most kMaxLogs verifies wait for a commit at once (the oldest
 // is retired beyond that); null if that many commits are pending.
@@ -1270,6 +1285,8 @@ int kda_verify_steps(kda_model* m, const float* x_dev, int32_t T, float* y_dev,
   // this log is folded into this verify
   const LogRec* mine = find_log(m, st, log_dev, log_bytes);
   r = flush_state(m, st, s, true, mine);
+  if (r) return r;
+  r = flush_log(m, log_dev, st, s);
   if (r) return r;
   LogRec* rc = add_log(m, st, log_dev, log_bytes);
   if (!rc) return fail(KDA_E_ARG, "%zu commits are pending on this model: apply some with kda_state_flush",

@@ -364,3 +364,51 @@ def test_commit_misuse_refused():
     model.flush(st)
     assert torch.equal(st.S, S1) and not torch.equal(S0, S1)
     model.close()
+
+
+def test_two_states_sharing_one_log():
+    """Two independent states verified through one log in turn: the second state's verify
+    applies the commit the first one left pending in that log before overwriting it, so
+    both committed states match the oracle."""
+    import torch
+    import linear_attention_decode_amd as kda
+    w = synth.scaled(synth.WORKLOADS["verify"], n_layers=2, batch=2, steps=2, seed=57)
+    run = synth.draw_run(w)
+    layers = oracle_layers(run)
+    model = gpu_model(run)
+    B, T = w.batch, w.tokens
+    _say("two states, one log")
+    log = model.verify_log(B, T)
+    ws = model.workspace(kda.KDA_OP_VERIFY, B, T)
+    sts, refs = [], []
+    for i in range(2):
+        st = model.new_state(B)
+        st.S.copy_(torch.from_numpy(run.s0))
+        sts.append(st)
+        refs.append(([[np.array(run.s0[l, b], np.float64) for b in range(B)] for l in range(2)],
+                     [[np.zeros((3, w.dims.conv_channels)) for _ in range(B)] for _ in range(2)]))
+    for t in range(w.steps):
+        for i in range(2):
+            x = torch.from_numpy(np.ascontiguousarray(run.x[t] * (1.0 + 0.5 * i))).float().cuda()
+            y = torch.empty_like(x)
+            model.verify_steps(x, T, y, sts[i], log, ws)
+            acc = run.accept[t] if i == 0 else run.accept[t][::-1].copy()
+            model.verify_commit(sts[i], log, T, torch.from_numpy(acc.astype(np.int32)).cuda())
+            S, Z = refs[i]
+            yy = y.cpu().numpy()
+            for b in range(B):
+                ry, s2, z2 = ok.stack_step(layers, (run.x[t, b] * (1.0 + 0.5 * i)).astype(np.float64),
+                                           [S[l][b] for l in range(2)], [Z[l][b] for l in range(2)],
+                                           keep_after=int(acc[b]))
+                assert range_rel(yy[b], ry) <= OUT_RTOL, f"step {t} state {i} seq {b}"
+                for l in range(2):
+                    S[l][b], Z[l][b] = s2[l], z2[l]
+    for i in range(2):
+        model.flush(sts[i])
+        torch.cuda.synchronize()
+        S, Z = refs[i]
+        rS = np.array([[S[l][b] for b in range(B)] for l in range(2)])
+        rZ = np.array([[Z[l][b] for b in range(B)] for l in range(2)])
+        assert np.abs(sts[i].S.cpu().numpy() - rS).max() <= STATE_ATOL, f"state {i}"
+        assert range_rel(sts[i].conv.cpu().numpy(), rZ) <= OUT_RTOL
+    model.close()
