@@ -53,13 +53,14 @@ def test_gate_forms_decode(gate, wtype):
     _say(f"  out {e:.2e}")
 
 
-@pytest.mark.parametrize("gate", ["safe", "scalar"])
-def test_gate_forms_full_size_stack(gate):
+@pytest.mark.parametrize("gate,B", [("safe", 1), ("scalar", 1), ("safe", 12)])
+def test_gate_forms_full_size_stack(gate, B):
     """D=2048, 16 heads, Q8_0, 3 layers (the one-launch kernel takes only the KDA gate, so
-    these run the per-layer kernels), 6 steps."""
+    these run the per-layer kernels on the caller's row-major weights), 6 steps; B = 12
+    takes the matrix-core projections with two 16-row tiles a block."""
     d = synth.LayerDims(d_model=2048, n_heads=16, d_k=128, d_v=128, rank_f=128, rank_g=128, gate=gate)
-    w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=3, steps=6, seed=103)
-    _say(f"decode gate={gate} q8_0 D=2048 3 layers 6 steps")
+    w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=3, steps=6, batch=B, seed=103)
+    _say(f"decode gate={gate} q8_0 D=2048 3 layers 6 steps B={B}")
     run = synth.draw_run(w)
     if gate == "safe":
         _safe_params(run, 104)
