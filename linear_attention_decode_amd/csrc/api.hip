@@ -360,8 +360,13 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
     });
     if (r) return r;
   }
-  r = enqueue_gates(m, L, proj, N, ag, s, rec);
-  if (r) return r;
+  // one-token decode of a few sequences: the head kernel computes its own gates (each of
+  // its waves re-reads all of its head's F_b rows, which a wide batch would pay for)
+  const bool fuse_gates = decode && !fold && B <= kFuseGatesMaxB;
+  if (!fuse_gates) {
+    r = enqueue_gates(m, L, proj, N, ag, s, rec);
+    if (r) return r;
+  }
 
   HeadParams hp;
   hp.H = d.n_heads; hp.dk = d.d_k; hp.dv = d.d_v; hp.C = m->C;
@@ -380,6 +385,11 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   // a multi-token step that keeps its state (the sequential-scan prefill) rolls the window
   // by all T tokens after the state write, in the same launch
   if (roll) hp.win_commit = win;
+  if (fuse_gates) {
+    hp.fuse_gates = 1;
+    hp.gate_form = d.gate; hp.gate_lb = d.gate_lb;
+    hp.fbw = L.fbw; hp.fbd = L.fbd; hp.gbw = L.gbw; hp.gbd = L.gbd;
+  }
   if (fold) {
     hp.pre_proj = fold->proj;
     hp.pre_act = fold->act;

@@ -13,6 +13,7 @@
 // Value columns are independent, so each wave owns 32 of them with the whole key
 // dimension in registers and needs no other wave; the state is read once and written
 // once per call (verify keeps it in registers across its tokens and writes nothing).
+#include <type_traits>
 #include <utility>
 
 #include "kda_device.h"
@@ -335,13 +336,172 @@ __device__ __forceinline__ void unroll_nested(int n, F& f) {
 // alternate), enough for a verify with a folded commit (at most 8 + 8 tokens) in one round
 constexpr int kHeadUnroll = 16;
 
-template <int DK, int CW>
+// Fused decode gates (one token, no replay): each head wave computes the gates it needs
+// from the token's f_lr, g_lr itself instead of reading them from a gates launch: alpha of
+// all DK forget rows of its head (lane l takes rows l, l + 64, ... whole, so no reduction;
+// the scalar form: the head's one row, a chunk a lane) and sigmoid of its CW output-gate
+// rows (four lanes a row).  Every chunk is requested first thing in the kernel, ahead of the
+// state; f_lr | g_lr are staged in LDS and read as broadcasts.  (Measured against a variant
+// with whole-wave coalesced loads transposed through LDS: the staging cost more than the
+// coalescing saved.)  GT = kGateOrder reads a model's own Q8_0 copy in gate-tile order
+// (signed q, see gates_mfma_kernel): 16-byte half hh of block g of row r at
+// ((r/16 * 2 + hh) * NB + g) * 16 + r % 16, its scale at (r/16 * NB + g) * 16 + r % 16.
+constexpr int kGateOrder = kQ8 + 100;
+constexpr int kFgGateChunks = 4;    // chunks of a gate row a lane (four lanes a row)
+
+// chunk c of row r: its 16 bytes and the raw bits of its scale (fp16 for Q8_0, the E8M0
+// exponent for MXFP4; converted where used, so a load is not waited for early); wb, sb are
+// the matrix's data and scale planes
+template <int GT>
+__device__ __forceinline__ void fg_chunk(const uint8_t* wb, const void* sb, int r, int c, int rank,
+                                         uint4& w, uint32_t& sc) {
+  if constexpr (GT == kGateOrder) {
+    const int NB = rank / 32, tile = r >> 4, m = r & 15, g = c >> 1;
+    w = *reinterpret_cast<const uint4*>(wb + ((size_t)((tile * 2 + (c & 1)) * NB + g) * 16 + m) * 16);
+    sc = static_cast<const uint16_t*>(sb)[(size_t)(tile * NB + g) * 16 + m];
+  } else {
+    constexpr int EL = HFmt<GT>::kElems;
+    w = *reinterpret_cast<const uint4*>(wb + ((size_t)r * (rank / EL) + c) * 16);
+    if constexpr (GT == kQ8)
+      sc = static_cast<const uint16_t*>(sb)[(size_t)r * (rank / 32) + (c >> 1)];
+    else if constexpr (GT == kMX4)
+      sc = static_cast<const uint8_t*>(sb)[(size_t)r * (rank / 32) + c];
+    else
+      sc = 0;
+  }
+}
+
+template <int GT>
+__device__ __forceinline__ float fg_dot(uint4 w, uint32_t sc, const float* __restrict__ x) {
+  if constexpr (GT == kGateOrder) {
+    w.x ^= 0x80808080u; w.y ^= 0x80808080u; w.z ^= 0x80808080u; w.w ^= 0x80808080u;
+    return __half2float(__ushort_as_half((unsigned short)sc)) * hchunk_dot<kQ8>(w, x);
+  } else if constexpr (GT == kMX4) {
+    return __builtin_amdgcn_ldexpf(1.0f, (int)sc - 128) * mx4_chunk_dot2(w, x);
+  } else if constexpr (GT == kQ8) {
+    return __half2float(__ushort_as_half((unsigned short)sc)) * hchunk_dot<kQ8>(w, x);
+  } else {
+    return hchunk_dot<GT>(w, x);
+  }
+}
+
+// alpha of the head's DK forget rows into s_al, sigmoid of the wave's CW output-gate rows
+// into s_gt.  start() requests every input (the first RC chunks of each forget row, the gate
+// chunks, f_lr | g_lr, bias, A_log); finish() waits for them and computes (requesting any
+// further chunks of long rows as it goes).  n is the token's column, cb the wave's column
+// block.
+template <int GT, int DK, int CW>
+struct FusedGates {
+  static constexpr int EL = HFmt<GT == kGateOrder ? kQ8 : GT>::kElems;
+  static constexpr int RL = DK / 64;            // forget rows a lane
+  // forget-row chunks in flight a row: all 16 of a 128-rank BF16 row; 8 for the byte formats
+  // (the scales take registers too)
+  static constexpr int RC = (GT == kBF16 || GT == kF32) ? 16 : 8;
+  static_assert(CW == 16, "four lanes a gate row");
+  int cpr, rank, h;
+  bool scalar;
+  float ah;
+  float bias[RL];
+  float4 lv[2];
+  const uint8_t* fwp;
+  const void* fsp;
+  uint4 fw[RL][RC];
+  uint32_t fs[RL][RC];
+  uint4 gw[kFgGateChunks];
+  uint32_t gs[kFgGateChunks];
+
+  __device__ __forceinline__ void issue_rows(int c0) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int i = 0; i < RL; ++i)
+#pragma unroll
+      for (int c = 0; c < RC; ++c)   // (clamped, not branched: no wait where paths join)
+        fg_chunk<GT>(fwp, fsp, h * DK + lane + 64 * i, min(c0 + c, cpr - 1), rank, fw[i][c], fs[i][c]);
+  }
+
+  __device__ __forceinline__ void start(const HeadParams& P, int n, int h_, int cb) {
+    const int lane = threadIdx.x & 63;
+    h = h_;
+    rank = P.rank_f;
+    cpr = rank / EL;
+    scalar = P.gate_form == kGateScalar;
+    constexpr bool go = GT == kGateOrder;
+    fwp = go ? reinterpret_cast<const uint8_t*>(P.fbw) : P.fb.w;
+    fsp = go ? static_cast<const void*>(P.fbd)
+             : (GT == kMX4 ? static_cast<const void*>(P.fb.e) : static_cast<const void*>(P.fb.d));
+    const uint8_t* gwp = go ? reinterpret_cast<const uint8_t*>(P.gbw) : P.gb.w;
+    const void* gsp = go ? static_cast<const void*>(P.gbd)
+                         : (GT == kMX4 ? static_cast<const void*>(P.gb.e) : static_cast<const void*>(P.gb.d));
+    if (scalar)
+      fg_chunk<GT>(fwp, fsp, h, min(lane, cpr - 1), rank, fw[0][0], fs[0][0]);
+    else
+      issue_rows(0);
+    const int grow = h * P.dv + cb * CW + (lane >> 2);
+#pragma unroll
+    for (int k = 0; k < kFgGateChunks; ++k)
+      fg_chunk<GT>(gwp, gsp, grow, min((lane & 3) + 4 * k, cpr - 1), rank, gw[k], gs[k]);
+    const float* lr = P.proj + (size_t)n * P.proj_stride + P.C;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)     // 2 rank floats: at most 128 float4s
+      lv[k] = *reinterpret_cast<const float4*>(lr + 4 * min(lane + 64 * k, rank / 2 - 1));
+#pragma unroll
+    for (int i = 0; i < RL; ++i) bias[i] = P.dt_bias[scalar ? h : h * DK + lane + 64 * i];
+    ah = P.a_log[h];
+  }
+
+  __device__ __forceinline__ void finish(const HeadParams& P, float* s_gl, float* s_al, float* s_gt) {
+    const int lane = threadIdx.x & 63;
+    // (lanes past the vector store its last float4 again: the same value)
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      *reinterpret_cast<float4*>(s_gl + 4 * min(lane + 64 * k, rank / 2 - 1)) = lv[k];
+    __syncthreads();
+    if (scalar) {
+      float f = lane < cpr ? fg_dot<GT>(fw[0][0], fs[0][0], s_gl + lane * EL) : 0.0f;
+      f = group_sum(f, 16);                     // cpr <= 16: lanes 0..15 hold the row
+      f = __shfl(f, 0);
+      const float a = forget_alpha_f(kGateKda, f + bias[0], ah, P.gate_lb);
+#pragma unroll
+      for (int i = 0; i < RL; ++i) s_al[lane + 64 * i] = a;
+    } else {
+      float f[RL];
+#pragma unroll
+      for (int i = 0; i < RL; ++i) f[i] = 0.0f;
+      for (int c0 = 0;;) {
+#pragma unroll
+        for (int i = 0; i < RL; ++i)
+#pragma unroll
+          for (int c = 0; c < RC; ++c)
+            if (c0 + c < cpr) f[i] += fg_dot<GT>(fw[i][c], fs[i][c], s_gl + (c0 + c) * EL);
+        c0 += RC;
+        if (c0 >= cpr) break;
+        issue_rows(c0);
+      }
+#pragma unroll
+      for (int i = 0; i < RL; ++i)
+        s_al[lane + 64 * i] = forget_alpha_f(P.gate_form, f[i] + bias[i], ah, P.gate_lb);
+    }
+    float g = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kFgGateChunks; ++k) {
+      const int c = (lane & 3) + 4 * k;
+      if (c < cpr) g += fg_dot<GT>(gw[k], gs[k], s_gl + rank + c * EL);
+    }
+    g = group_sum(g, 4);
+    if ((lane & 3) == 0) s_gt[lane >> 2] = sigmoid_f(g);
+    __syncthreads();
+  }
+};
+struct FusedNone {};
+
+template <int DK, int CW, int GT>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   constexpr int RG = 256 / CW;
   constexpr int RPT = DK / RG;
   // block id = cb * (H B) + h * B + b: the dv / CW waves of one (sequence, head), which
-  // read the same q, k and alpha rows, are H B apart, so on one XCD (blocks go round-robin
-  // over the 8) whenever H B is a multiple of 8, and those rows come from its L2
+  // read the same q, k and alpha rows (and with fused gates the same F_b rows), are H B
+  // apart, so on one XCD (blocks go round-robin over the 8) whenever H B is a multiple of
+  // 8, and those rows come from its L2
   const int hb = (int)blockIdx.x % (P.H * P.B);
   const int cb = (int)blockIdx.x / (P.H * P.B), h = hb / P.B, b = hb - h * P.B;
   const int lane = threadIdx.x;
@@ -351,6 +511,8 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   const int r0 = rg * RPT;                     // this lane's first key row
   const int nparts = dv / CW;
   const int rl = P.rank_f + P.rank_g;
+  std::conditional_t<(GT >= 0), FusedGates<(GT >= 0 ? GT : kF32), DK, CW>, FusedNone> fg;
+  if constexpr (GT >= 0) fg.start(P, b, h, cb);
 
   float* Sb = P.S + ((size_t)b * H + h) * DK * dv + j;
   float4 st[RPT];
@@ -384,14 +546,16 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
     for (int i = 0; i < RPT; i += 4) {
       const float4 a = *reinterpret_cast<const float4*>(arow + cq0 + i);
       const float4 k4 = *reinterpret_cast<const float4*>(arow + ck0 + i);
-      const float4 g4 = *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
       x.qv[i] = a.x; x.qv[i + 1] = a.y; x.qv[i + 2] = a.z; x.qv[i + 3] = a.w;
       x.kv[i] = k4.x; x.kv[i + 1] = k4.y; x.kv[i + 2] = k4.z; x.kv[i + 3] = k4.w;
-      x.al[i] = g4.x; x.al[i + 1] = g4.y; x.al[i + 2] = g4.z; x.al[i + 3] = g4.w;
+      if constexpr (GT < 0) {
+        const float4 g4 = *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
+        x.al[i] = g4.x; x.al[i + 1] = g4.y; x.al[i + 2] = g4.z; x.al[i + 3] = g4.w;
+      }
     }
     const float4 a = *reinterpret_cast<const float4*>(arow + cv0);
     x.v4[0] = a.x; x.v4[1] = a.y; x.v4[2] = a.z; x.v4[3] = a.w;
-    x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
+    if constexpr (GT < 0) x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
     x.braw = prow[C + rl + h];
   };
   // token u of the sequence from the inputs in x: state update, outputs (this call's
@@ -463,21 +627,34 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   // which loads are still outstanding at each use and waits for one set while the other's
   // are in flight; past the last token the loads repeat it
   Tok x0, x1;
-  load_tok(0, x0);
-  load_tok(min(1, total - 1), x1);
-  for (int base = 0; base < total; base += kHeadUnroll) {
-    auto step = [&](auto uc) __attribute__((always_inline)) {
-      constexpr int k = decltype(uc)::value;
-      const int u = base + k;
-      if constexpr ((k & 1) == 0) {
-        process(x0, u);
-        load_tok(min(u + 2, total - 1), x0);
-      } else {
-        process(x1, u);
-        load_tok(min(u + 2, total - 1), x1);
-      }
-    };
-    unroll_nested<0, kHeadUnroll>(total - base, step);
+  if constexpr (GT >= 0) {
+    // fused decode gates: the sequence's one token, its gates computed here
+    __shared__ __align__(16) float s_gl[2 * kMaxRank];
+    __shared__ __align__(16) float s_al[DK];
+    __shared__ __align__(16) float s_gt[CW];
+    load_tok(0, x0);
+    fg.finish(P, s_gl, s_al, s_gt);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) x0.al[i] = s_al[r0 + i];
+    x0.gate = *reinterpret_cast<const float4*>(s_gt + cq * 4);
+    process(x0, 0);
+  } else {
+    load_tok(0, x0);
+    load_tok(min(1, total - 1), x1);
+    for (int base = 0; base < total; base += kHeadUnroll) {
+      auto step = [&](auto uc) __attribute__((always_inline)) {
+        constexpr int k = decltype(uc)::value;
+        const int u = base + k;
+        if constexpr ((k & 1) == 0) {
+          process(x0, u);
+          load_tok(min(u + 2, total - 1), x0);
+        } else {
+          process(x1, u);
+          load_tok(min(u + 2, total - 1), x1);
+        }
+      };
+      unroll_nested<0, kHeadUnroll>(total - base, step);
+    }
   }
   if (P.write_state && (!P.active || P.active[b])) {
 #pragma unroll
@@ -508,12 +685,23 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   }
 }
 
-hipError_t launch_head(const HeadParams& p, hipStream_t s) {
-  const dim3 grid((p.dv / kHeadCols) * p.H * p.B);
+template <int GT>
+static void launch_head_gt(const HeadParams& p, const dim3 grid, hipStream_t s) {
   if (p.dk == 128)
-    head_kernel<128, kHeadCols><<<grid, 64, 0, s>>>(p);
+    head_kernel<128, kHeadCols, GT><<<grid, 64, 0, s>>>(p);
   else
-    head_kernel<64, kHeadCols><<<grid, 64, 0, s>>>(p);
+    head_kernel<64, kHeadCols, GT><<<grid, 64, 0, s>>>(p);
+}
+
+hipError_t launch_head(const HeadParams& p, hipStream_t s) {
+  if (p.fuse_gates && (p.T != 1 || p.pre_ntok)) return hipErrorInvalidValue;
+  const dim3 grid((p.dv / kHeadCols) * p.H * p.B);
+  if (!p.fuse_gates) launch_head_gt<-1>(p, grid, s);
+  else if (p.fbw) launch_head_gt<kGateOrder>(p, grid, s);
+  else if (p.wt == kF32) launch_head_gt<kF32>(p, grid, s);
+  else if (p.wt == kBF16) launch_head_gt<kBF16>(p, grid, s);
+  else if (p.wt == kMX4) launch_head_gt<kMX4>(p, grid, s);
+  else launch_head_gt<kQ8>(p, grid, s);
   return hipGetLastError();
 }
 

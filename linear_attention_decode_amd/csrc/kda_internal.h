@@ -175,9 +175,22 @@ struct HeadParams {
   const float* pre_ag = nullptr;
   const int* pre_ntok = nullptr;
   int pre_T = 0;
+  // decode (T = 1, no folded commit): compute the gates here instead of reading alpha_gate:
+  // alpha of the head's rows from F_b (fb, or the gate-order copy fbw/fbd of a model that
+  // owns its weights) and f_lr, the wave's output-gate columns from G_b and g_lr (proj at C
+  // and C + rank_f), in the gate form gate_form
+  int fuse_gates = 0;
+  int gate_form = 0;
+  float gate_lb = 0.f;
+  const int8_t* fbw = nullptr;
+  const uint16_t* fbd = nullptr;
+  const int8_t* gbw = nullptr;
+  const uint16_t* gbd = nullptr;
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
+// decode batches up to this many sequences run the gates inside the head kernel
+constexpr int kFuseGatesMaxB = 8;
 
 struct GatesParams {
   int N = 0, K = 0, V = 0, dk = 0, rank = 0, C = 0, wt = 0;
