@@ -1,6 +1,8 @@
 """GPU parity of the forget-gate forms other than KDA's per-channel softplus gate: the
 lower-bounded ("safe") gate and the per-head scalar gate of the gated delta rule, through
-decode (per-layer kernels), verify + commit and chunked prefill, against the oracle."""
+decode (per-layer kernels), verify + commit and chunked prefill, against the oracle; and
+decode's two ways of computing the gates (inside the head kernel for up to 8 sequences, a
+gates launch above that) against each other."""
 import sys
 
 import numpy as np
@@ -53,11 +55,12 @@ def test_gate_forms_decode(gate, wtype):
     _say(f"  out {e:.2e}")
 
 
-@pytest.mark.parametrize("gate,B", [("safe", 1), ("scalar", 1), ("safe", 12)])
+@pytest.mark.parametrize("gate,B", [("safe", 1), ("scalar", 1), ("safe", 12), ("scalar", 12)])
 def test_gate_forms_full_size_stack(gate, B):
     """D=2048, 16 heads, Q8_0, 3 layers (the one-launch kernel takes only the KDA gate, so
-    these run the per-layer kernels on the caller's row-major weights), 6 steps; B = 12
-    takes the matrix-core projections with two 16-row tiles a block."""
+    these run the per-layer kernels on the caller's row-major weights), 6 steps; B = 1 has
+    the head kernel compute the gates, B = 12 runs the gates kernel and takes the
+    matrix-core projections with two 16-row tiles a block."""
     d = synth.LayerDims(d_model=2048, n_heads=16, d_k=128, d_v=128, rank_f=128, rank_g=128, gate=gate)
     w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=3, steps=6, batch=B, seed=103)
     _say(f"decode gate={gate} q8_0 D=2048 3 layers 6 steps B={B}")
@@ -137,4 +140,44 @@ def test_gate_forms_prefill(gate):
     e = max(range_rel(yy[b, t], ry[b, t]) for b in range(2) for t in range(150))
     assert e <= OUT_RTOL, e
     assert np.abs(st.S.cpu().numpy()[0] - rS).max() <= STATE_ATOL
+    model.close()
+
+
+@pytest.mark.parametrize("gate,wtype", [("kda", "bf16"), ("safe", "q8_0"), ("scalar", "f32"),
+                                        ("kda", "mxfp4")])
+def test_fused_and_separate_gates_agree(gate, wtype):
+    """The same 8 sequences decoded as a batch of 8 (gates inside the head kernel) and as
+    the first 8 rows of a batch of 9 (gates kernel): outputs and states agree to fp32
+    rounding (the two sum each gate row's dot in a different order), 4 steps, 2 layers."""
+    import torch
+    d = synth.LayerDims(d_model=512, n_heads=4, d_k=128, d_v=128, rank_f=64, rank_g=64, gate=gate)
+    w9 = synth.scaled(synth.WORKLOADS["stack"], dims=d, wtype=wtype, n_layers=2, batch=9, steps=4,
+                      seed=107)
+    _say(f"fused vs separate gates: gate={gate} {wtype} B=8 vs B=9, 2 layers, 4 steps")
+    run = synth.draw_run(w9)
+    if gate == "safe":
+        _safe_params(run, 108)
+    model = gpu_model(run)
+    model.set_option(2, 0)
+    res = {}
+    for B in (8, 9):
+        st = model.new_state(B)
+        st.S.copy_(torch.from_numpy(np.ascontiguousarray(run.s0[:, :B])))
+        ws = model.workspace(0, B)
+        ys = []
+        for t in range(w9.steps):
+            x = torch.from_numpy(np.ascontiguousarray(run.x[t, :B, 0, :])).cuda()
+            y = torch.empty_like(x)
+            model.decode_step(x, y, st, ws)
+            ys.append(y.cpu().numpy())
+        torch.cuda.synchronize()
+        res[B] = (np.array(ys), st.S.cpu().numpy(), st.conv.cpu().numpy())
+    y8, S8, Z8 = res[8]
+    y9, S9, Z9 = res[9]
+    ey = max(range_rel(y8[t], y9[t, :8]) for t in range(w9.steps))
+    es = np.abs(S8 - S9[:, :8]).max()
+    _say(f"  out {ey:.2e} state {es:.2e}")
+    assert ey <= 1e-5, ey
+    assert es <= 1e-5, es
+    assert range_rel(Z8, Z9[:, :8]) <= 1e-5
     model.close()
