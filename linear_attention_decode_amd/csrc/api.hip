@@ -362,7 +362,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   }
   // one-token decode of a few sequences: the head kernel computes its own gates (each of
   // its waves re-reads all of its head's F_b rows, which a wide batch would pay for)
-  const bool fuse_gates = decode && !fold && B <= kFuseGatesMaxB;
+  const bool fuse_gates = decode && !fold && B <= (L.fbw ? kFuseGatesMaxBOwned : kFuseGatesMaxB);
   if (!fuse_gates) {
     r = enqueue_gates(m, L, proj, N, ag, s, rec);
     if (r) return r;

@@ -189,8 +189,10 @@ struct HeadParams {
 };
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
-// decode batches up to this many sequences run the gates inside the head kernel
+// decode batches up to this many sequences run the gates inside the head kernel (row-major
+// F_b, G_b; a model's own gate-tile-order copy, read 16 contiguous rows at a time)
 constexpr int kFuseGatesMaxB = 8;
+constexpr int kFuseGatesMaxBOwned = 16;
 
 struct GatesParams {
   int N = 0, K = 0, V = 0, dk = 0, rank = 0, C = 0, wt = 0;
