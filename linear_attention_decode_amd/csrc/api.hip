@@ -325,6 +325,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   proj_segments(m, L, pp, decode || conv_fused);
   pp.K = d.d_model;
   pp.N = N;
+  pp.wt = d.wtype;
   pp.x = x_in;
   pp.x_stride = d.d_model;
   pp.prenorm = d.prenorm_residual;
@@ -415,6 +416,7 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   po.nseg = 1;
   po.K = m->V;
   po.N = N;
+  po.wt = d.wtype;
   po.o = o; po.gate = gate; po.ss = ss; po.onw = L.o_norm_w;
   po.H = d.n_heads; po.dv = d.d_v; po.ncb = d.d_v / kHeadCols;
   po.eps = d.norm_eps;

@@ -126,6 +126,8 @@ struct GemvParams {
   // launch_skinny only: the Q8_0 matrices (seg[i].m: w at the segment's first 16-row tile,
   // d at its scales) are in the one-launch decode's matrix-core order
   int mma = 0;
+  // launch_skinny only: the weight format (kQ8 or kBF16)
+  int wt = kQ8;
 };
 
 constexpr int kGemvKSmall = 2048;   // input length of the multi-column variants

@@ -17,12 +17,18 @@
 //                 roll, residual) run unchanged.
 // The result differs from the fp32 GEMV only by rounding: x is carried to ~22 bits by the
 // hi/lo pair, the weight values are exact, and the MFMA accumulates in fp32.
+// BF16 weights (BF = true) go to v_mfma_f32_16x16x32_bf16 as they are, against x split into
+// two BF16 terms (hi = bf16(x), lo = bf16(x - hi): ~16 significant bits, as in the prefill
+// GEMMs); no scales or bias, the MFMAs accumulate over the whole K range.
+#include <type_traits>
+
 #include "kda_device.h"
 #include "skinny.h"
 
 namespace kda {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -36,7 +42,11 @@ size_t skinny_scratch_bytes(int N, int K) {
 }
 
 bool skinny_supported(int wt, int N, int K) {
-  return wt == kQ8 && N > 8 && N <= 64 && (K == 2048 || K == 4096);
+  // Q8_0 from 9 columns (the vector GEMV streams its bytes fast enough below), BF16 from 5
+  // (its vector GEMV pays an unpack and N FMAs a weight: 49 us for the D = 2048 projections
+  // at 8 columns against 12 here; at 2 columns the GEMV's 14 us beat the prep + GEMM pair)
+  return ((wt == kQ8 && N > 8 && (K == 2048 || K == 4096)) || (wt == kBF16 && N > 4 && K == 2048)) &&
+         N <= 64;
 }
 
 bool skinny_mma_supported(int N, int K) { return N >= 1 && N <= 64 && (K == 1024 || K == 2048); }
@@ -66,6 +76,12 @@ __device__ __forceinline__ uint32_t pack_h2(_Float16 a, _Float16 b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// fp32 -> BF16 bits, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // ------------------------------------------------------------------------------------
 // skinny_prep: column n of the (prologue-applied) input -> fp16 hi/lo fragments.
 // ------------------------------------------------------------------------------------
@@ -77,7 +93,7 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // KG = ceil(K / 2048) groups of 8 consecutive elements per thread (all loaded in one
 // pass; groups past K are empty).
-template <int PRO, int KG>
+template <int PRO, int KG, bool BF>
 __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParams P, int NT,
                                                                  SkScratch S) {
   __shared__ float red[2][4];
@@ -147,19 +163,31 @@ __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParam
   for (int q = 0; q < KG; ++q) {
     const int k0 = 8 * (tid + kSkThreads * q), kb = k0 >> 5, g = (k0 >> 3) & 3;
     if (k0 >= K) break;
-    _Float16 hi[8], lo[8];
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = v[q][j] * up;
-      hi[j] = (_Float16)x;
-      const float hv = (float)hi[j];
-      lo[j] = (_Float16)(x - hv);
-      s += hv + (float)lo[j];
-    }
     const size_t fi = ((size_t)kb * NT + ct) * 64 + nl + 16 * g;
-    S.fh[fi] = make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
-    S.fl[fi] = make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
+    float s = 0.0f;
+    if constexpr (BF) {
+      uint32_t hb[8], lb[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = v[q][j] * up;
+        hb[j] = bf16_bits(x);
+        lb[j] = bf16_bits(x - __uint_as_float(hb[j] << 16));
+      }
+      S.fh[fi] = make_uint4(hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16);
+      S.fl[fi] = make_uint4(lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16);
+    } else {
+      _Float16 hi[8], lo[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = v[q][j] * up;
+        hi[j] = (_Float16)x;
+        const float hv = (float)hi[j];
+        lo[j] = (_Float16)(x - hv);
+        s += hv + (float)lo[j];
+      }
+      S.fh[fi] = make_uint4(pack_h2(hi[0], hi[1]), pack_h2(hi[2], hi[3]), pack_h2(hi[4], hi[5]), pack_h2(hi[6], hi[7]));
+      S.fl[fi] = make_uint4(pack_h2(lo[0], lo[1]), pack_h2(lo[2], lo[3]), pack_h2(lo[4], lo[5]), pack_h2(lo[6], lo[7]));
+    }
     // the four threads of a k block are consecutive lanes
     s = group_sum(s, 4);
     if (g == 0) S.xsum[(size_t)kb * NT * 16 + n] = s;
@@ -208,7 +236,7 @@ __device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
 // per 16-row tile, 16-byte chunks c = ((w * 2U + t) * 2 + h) * 64 + r + 16 g holding row r,
 // bytes 16 h .. + 15 of block 4 (4 t + w) + g as signed q; the tile's scales at
 // ((w * 64 + r + 16 g) * 2U + t)), U = K / 1024.
-template <int NT, int KB4, bool MMA, int RT>
+template <int NT, int KB4, bool MMA, int RT, bool BF>
 __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
   constexpr int KB = 4 * KB4;
   constexpr int PD = 4;                          // k blocks of B fragments in flight
@@ -234,8 +262,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   // in-order load counter), stored to LDS after the weight requests are out
   // scales: row r's KB halves are contiguous; 8 per 16-byte load
   constexpr int kScPer = KB * kSkRows / 8;       // 16-byte loads per row tile
-  constexpr int kScLoads = (kScPer * RT + kSkThreads - 1) / kSkThreads;
-  u32x4 sv[kScLoads];
+  constexpr int kScLoadsN = (kScPer * RT + kSkThreads - 1) / kSkThreads;
+  constexpr int kScLoads = BF ? 0 : kScLoadsN;   // (BF16: no scales, no block sums)
+  u32x4 sv[kScLoadsN];
 #pragma unroll
   for (int u = 0; u < kScLoads; ++u) {
     const int i = min(tid + u * kSkThreads, kScPer * RT - 1);
@@ -247,8 +276,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
       sv[u] = *reinterpret_cast<const u32x4*>(sg.m.d + (size_t)(row0 + r) * KB + 8 * c8);
     }
   }
-  constexpr int kXsLoads = (KB * NT * 4 + kSkThreads - 1) / kSkThreads;
-  f32x4v xv[kXsLoads];
+  constexpr int kXsLoadsN = (KB * NT * 4 + kSkThreads - 1) / kSkThreads;
+  constexpr int kXsLoads = BF ? 0 : kXsLoadsN;
+  f32x4v xv[kXsLoadsN];
 #pragma unroll
   for (int u = 0; u < kXsLoads; ++u) {
     const int i = min(tid + u * kSkThreads, KB * NT * 4 - 1);
@@ -256,18 +286,21 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   }
   __builtin_amdgcn_sched_barrier(0);
   // A operand: lane holds row (lane & 15) of each row tile, bytes 8 (lane >> 4) .. + 7 of
-  // each k block; the wave's whole K range is requested up front
+  // each k block (BF16: elements 8 (lane >> 4) .. + 7, 16 bytes); the wave's whole K range
+  // is requested up front
   const int ag = lane >> 4;
   const int kb0 = wave * KB4;
-  uint2 a[RT][KB4];
+  std::conditional_t<BF, uint4, uint2> a[RT][KB4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int tr = tile_of(rt);
     const int ar = min(16 * tr + (lane & 15), nrows - 1);
-    const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K + 8 * ag;
+    const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K * (BF ? 2 : 1) + (BF ? 16 : 8) * ag;
 #pragma unroll
     for (int j = 0; j < KB4; ++j) {
-      if constexpr (MMA) {
+      if constexpr (BF) {
+        a[rt][j] = *reinterpret_cast<const uint4*>(wrow + (size_t)(kb0 + j) * 64);
+      } else if constexpr (MMA) {
         constexpr int U2 = KB4 / 4;              // 2U
         const int kb = kb0 + j, g = kb & 3, w = (kb >> 2) & 3, t = kb >> 4;
         const uint8_t* cp = sg.m.w + (size_t)(row0 + 16 * tr) * K +
@@ -338,35 +371,50 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
 #pragma unroll
   for (int j = 0; j < KB4; ++j) {
     const int kb = kb0 + j, slot = j % PD;
-    f32x4v o[RT][NT];
+    if constexpr (BF) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const f16x8 av = bytes_to_f16(a[rt][j]);
+      for (int rt = 0; rt < RT; ++rt) {
+        const bf16x8s av = __builtin_bit_cast(bf16x8s, a[rt][j]);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bh[slot][t]),
-                                                          f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bl[slot][t]),
-                                                          o[rt][t], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8s, bh[slot][t]),
+                                                               acc[rt][t], 0, 0, 0);
+          acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8s, bl[slot][t]),
+                                                               acc[rt][t], 0, 0, 0);
+        }
       }
-    }
-    if (j + PD < KB4) load_b(j + PD, slot);
-    float bias[NT];
+      if (j + PD < KB4) load_b(j + PD, slot);
+    } else {
+      f32x4v o[RT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) bias[t] = 1152.0f * s_xs[kb][t * 16 + oc];
+      for (int rt = 0; rt < RT; ++rt) {
+        const f16x8 av = bytes_to_f16(a[rt][j]);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][16 * rt + 4 * og]);
-      const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
-      const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
-      const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
-      const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+        for (int t = 0; t < NT; ++t) {
+          o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bh[slot][t]),
+                                                            f32x4v{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          o[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(f16x8, bl[slot][t]),
+                                                            o[rt][t], 0, 0, 0);
+        }
+      }
+      if (j + PD < KB4) load_b(j + PD, slot);
+      float bias[NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        acc[rt][t][0] += d0 * (o[rt][t][0] - bias[t]);
-        acc[rt][t][1] += d1 * (o[rt][t][1] - bias[t]);
-        acc[rt][t][2] += d2 * (o[rt][t][2] - bias[t]);
-        acc[rt][t][3] += d3 * (o[rt][t][3] - bias[t]);
+      for (int t = 0; t < NT; ++t) bias[t] = 1152.0f * s_xs[kb][t * 16 + oc];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint2 sc2 = *reinterpret_cast<const uint2*>(&s_sc[kb][16 * rt + 4 * og]);
+        const float d0 = __half2float(__ushort_as_half((unsigned short)(sc2.x & 0xffffu)));
+        const float d1 = __half2float(__ushort_as_half((unsigned short)(sc2.x >> 16)));
+        const float d2 = __half2float(__ushort_as_half((unsigned short)(sc2.y & 0xffffu)));
+        const float d3 = __half2float(__ushort_as_half((unsigned short)(sc2.y >> 16)));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[rt][t][0] += d0 * (o[rt][t][0] - bias[t]);
+          acc[rt][t][1] += d1 * (o[rt][t][1] - bias[t]);
+          acc[rt][t][2] += d2 * (o[rt][t][2] - bias[t]);
+          acc[rt][t][3] += d3 * (o[rt][t][3] - bias[t]);
+        }
       }
     }
   }
@@ -452,7 +500,7 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   // least 192 blocks and the operands fit the registers (up to 32 columns, K = 2048)
   int rows32 = 0;
   for (int i = 0; i < g.nseg; ++i) rows32 += (g.seg[i].rows + 31) / 32;
-  const int RT = (rows32 >= 192 && NT <= 2 && g.K == 2048) ? 2 : 1;
+  const int RT = (g.wt != kBF16 && rows32 >= 192 && NT <= 2 && g.K == 2048) ? 2 : 1;
   int tiles = 0;
   for (int i = 0; i < g.nseg; ++i) {
     p.seg[i].m = g.seg[i].m;
@@ -477,26 +525,33 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.pre_proj = g.pre_proj;
   p.pre_ntok = g.pre_ntok;
   p.pre_T = g.pre_T;
-  const int KG = g.K / 2048;
-  if (prologue == kProX) {
-    if (KG == 2) skinny_prep_kernel<kProX, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
-    else skinny_prep_kernel<kProX, 1><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
-  } else {
-    if (KG == 2) skinny_prep_kernel<kProGatedNorm, 2><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
-    else skinny_prep_kernel<kProGatedNorm, 1><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
-  }
+  const int KG = g.K > 2048 ? 2 : 1;             // 8-element groups a thread (K <= 4096)
+  const bool bf = g.wt == kBF16;
+#define KDA_SK_PREP(pro, kg, b) \
+  if ((prologue == kProX) == (pro == kProX) && KG == kg && bf == b) \
+    skinny_prep_kernel<pro, kg, b><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
+  KDA_SK_PREP(kProX, 1, false) KDA_SK_PREP(kProX, 2, false)
+  KDA_SK_PREP(kProGatedNorm, 1, false) KDA_SK_PREP(kProGatedNorm, 2, false)
+  KDA_SK_PREP(kProX, 1, true) KDA_SK_PREP(kProX, 2, true)
+  KDA_SK_PREP(kProGatedNorm, 1, true) KDA_SK_PREP(kProGatedNorm, 2, true)
+#undef KDA_SK_PREP
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int KB4 = g.K / 128;
 #define KDA_SK_CASE(nt, kb4, mm, rt) \
-  if (NT == nt && KB4 == kb4 && (g.mma != 0) == mm && RT == rt) \
-    skinny_gemm_kernel<nt, kb4, mm, rt><<<tiles, kSkThreads, 0, s>>>(p);
+  if (!bf && NT == nt && KB4 == kb4 && (g.mma != 0) == mm && RT == rt) \
+    skinny_gemm_kernel<nt, kb4, mm, rt, false><<<tiles, kSkThreads, 0, s>>>(p);
+#define KDA_SK_BF(nt, kb4) \
+  if (bf && NT == nt && KB4 == kb4 && RT == 1) \
+    skinny_gemm_kernel<nt, kb4, false, 1, true><<<tiles, kSkThreads, 0, s>>>(p);
   KDA_SK_CASE(1, 8, false, 1) KDA_SK_CASE(2, 8, false, 1) KDA_SK_CASE(3, 8, false, 1) KDA_SK_CASE(4, 8, false, 1)
   KDA_SK_CASE(1, 16, false, 1) KDA_SK_CASE(2, 16, false, 1) KDA_SK_CASE(3, 16, false, 1) KDA_SK_CASE(4, 16, false, 1)
   KDA_SK_CASE(1, 32, false, 1) KDA_SK_CASE(2, 32, false, 1) KDA_SK_CASE(3, 32, false, 1) KDA_SK_CASE(4, 32, false, 1)
   KDA_SK_CASE(1, 8, true, 1) KDA_SK_CASE(2, 8, true, 1) KDA_SK_CASE(3, 8, true, 1) KDA_SK_CASE(4, 8, true, 1)
   KDA_SK_CASE(1, 16, true, 1) KDA_SK_CASE(2, 16, true, 1) KDA_SK_CASE(3, 16, true, 1) KDA_SK_CASE(4, 16, true, 1)
   KDA_SK_CASE(1, 16, false, 2) KDA_SK_CASE(2, 16, false, 2) KDA_SK_CASE(1, 16, true, 2) KDA_SK_CASE(2, 16, true, 2)
+  KDA_SK_BF(1, 16) KDA_SK_BF(2, 16) KDA_SK_BF(3, 16) KDA_SK_BF(4, 16)
+#undef KDA_SK_BF
 #undef KDA_SK_CASE
   return hipGetLastError();
 }

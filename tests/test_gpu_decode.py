@@ -164,6 +164,24 @@ def test_decode_batched_q8_0_matrix_cores(torch, B):
     _say(f"  B={B}: out {e:.2e} state {s:.2e}")
 
 
+@pytest.mark.parametrize("B", [5, 9, 33])
+def test_decode_batched_bf16_matrix_cores(torch, B):
+    """BF16 weights with 5..64 columns take the MFMA products (BF16 weights against x as two
+    BF16 terms): a 2-layer D=2048 BF16 stack, 4 steps."""
+    w = synth.scaled(synth.WORKLOADS["stack"], wtype="bf16", n_layers=2, batch=B, steps=4, seed=70 + B)
+    _say(f"decode batched bf16 B={B} 2 layers D=2048 4 steps (MFMA projections)")
+    e, s = _decode_parity(w, w.steps, snap_every=2, expect_persistent=False)
+    _say(f"  B={B}: out {e:.2e} state {s:.2e}")
+
+
+def test_decode_layer_bf16_batched(torch):
+    """The BF16 layer workload (no pre-norm, no residual) at B=6: MFMA products."""
+    w = synth.scaled(synth.WORKLOADS["layer"], batch=6, steps=6)
+    _say("decode layer bf16 B=6 6 steps (MFMA projections)")
+    e, s = _decode_parity(w, w.steps, snap_every=3)
+    _say(f"  out {e:.2e} state {s:.2e}")
+
+
 @pytest.mark.timeout(900)
 def test_decode_stack_full_run_128_steps(torch):
     """The stack workload as configured: 34 Q8_0 layers, B=1, all 128 decode steps through

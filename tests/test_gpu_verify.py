@@ -122,6 +122,13 @@ def test_verify_ragged_columns_matrix_cores():
     _check(w, w.steps)
 
 
+def test_verify_bf16_matrix_cores():
+    """A BF16 stack: B=3 x T=4 = 12 token positions at D=2048 on the BF16 MFMA products."""
+    w = synth.scaled(synth.WORKLOADS["verify"], wtype="bf16", n_layers=2, batch=3, steps=3, seed=37)
+    _say("verify 2 layers B=3 T=4 D=2048 bf16, 3 steps (MFMA projections)")
+    _check(w, w.steps)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3])
 def test_verify_token_counts(T):
     d = synth.LayerDims(d_model=96, n_heads=3, d_k=64, d_v=64, rank_f=32, rank_g=32)
