@@ -361,9 +361,15 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
     });
     if (r) return r;
   }
-  // one-token decode of a few sequences: the head kernel computes its own gates (each of
-  // its waves re-reads all of its head's F_b rows, which a wide batch would pay for)
-  const bool fuse_gates = decode && !fold && B <= (L.fbw ? kFuseGatesMaxBOwned : kFuseGatesMaxB);
+  // one token a sequence for a few sequences: the head kernel computes its own gates (each
+  // of its waves re-reads all of its head's F_b rows, which a wide batch would pay for); a
+  // model with its own gate-tile-order copy on the matrix cores, others with vector dots.
+  // (The matrix-core form takes up to 8 tokens, but at 4, verify's, its serial chain per
+  // token cost more than the separate launch: 22.8 us against 11.3 + 7.1.)
+  const bool mfma_gates = L.fbw && d.gate == KDA_GATE_KDA && d.d_k == 128 &&
+                          (d.rank_f == 32 || d.rank_f == 64 || d.rank_f == 128) && T == 1 &&
+                          !fold && B <= kFuseGatesMaxBOwned;
+  const bool fuse_gates = mfma_gates || (decode && !fold && !L.fbw && B <= kFuseGatesMaxB);
   if (!fuse_gates) {
     r = enqueue_gates(m, L, proj, N, ag, s, rec);
     if (r) return r;
@@ -387,7 +393,8 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   // by all T tokens after the state write, in the same launch
   if (roll) hp.win_commit = win;
   if (fuse_gates) {
-    hp.fuse_gates = 1;
+    hp.fuse_gates = mfma_gates ? 2 : 1;
+    if (act) hp.ag_out = ag;       // verify and scan: a replay of these tokens reads them
     hp.gate_form = d.gate; hp.gate_lb = d.gate_lb;
     hp.fbw = L.fbw; hp.fbd = L.fbd; hp.gbw = L.gbw; hp.gbd = L.gbd;
   }

@@ -178,10 +178,51 @@ __global__ __launch_bounds__(kGateThreads) void gates_kernel(const GatesParams P
 typedef int i32x4g __attribute__((ext_vector_type(4)));
 constexpr int kGmCols = 8;       // token columns per block
 
+// The steps of the matrix-core gates, shared with the head kernel's own gates, each with
+// contraction off so that both places round alike (the gates are then bit for bit the same
+// whichever kernel computes them).
+// Element u of a 32-element block held by a half-wave: its three planes and the block's
+// inverse scale.
+struct GmPlanes {
+  int8_t q0, q1, q2;
+  float inv;
+};
+__device__ __forceinline__ GmPlanes gm_quantise(float u) {
+#pragma clang fp contract(off)
+  constexpr float M = 12582912.0f;
+  float ss = sum16(u * u);
+  ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));   // lane ^ 16
+  const int ex = (__builtin_amdgcn_frexp_expf(ss) + 1) >> 1;
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, 6 - ex);
+  const float t0 = fmaf(u, sc, M), q0 = t0 - M, r0 = fmaf(u, sc, -q0);
+  const float t1 = fmaf(r0, 128.0f, M), q1 = t1 - M, r1 = fmaf(r0, 128.0f, -q1);
+  const float t2 = fmaf(r1, 128.0f, M);
+  return {(int8_t)__float_as_uint(t0), (int8_t)__float_as_uint(t1), (int8_t)__float_as_uint(t2),
+          __builtin_amdgcn_ldexpf(1.0f, ex - 6)};
+}
+// One (tile, column) MFMA result: block g's plane dots in lane group g, weighed by the
+// block's weight scale dsc and inverse input scale gi (live: g < blocks), summed over the
+// four groups (every group ends with the total).
+__device__ __forceinline__ float gm_row(const i32x4g c, float dsc, float gi, bool live) {
+#pragma clang fp contract(off)
+  const float v = fmaf((float)(c[1] * 128 + c[2]), 1.0f / 16384.0f, (float)c[0]);
+  float y = live ? dsc * gi * v : 0.0f;
+  y += __shfl_xor(y, 16);
+  y += __shfl_xor(y, 32);
+  return y;
+}
+__device__ __forceinline__ float gm_alpha(float ah, float x) {
+#pragma clang fp contract(off)
+  return expf(-expf(ah) * softplus_f(x));
+}
+__device__ __forceinline__ float gm_gate(float x) {
+#pragma clang fp contract(off)
+  return sigmoid_f(x);
+}
+
 template <int CPR>
 __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
   constexpr int NB = CPR / 2, rank = CPR * 16;     // Q8_0 blocks per row, rank
-  constexpr float M = 12582912.0f;
   __shared__ __align__(16) int8_t gpl[kGmCols][4][256];   // [column][plane][f | g]; plane 3 = 0
   __shared__ float ginv[kGmCols][8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -214,19 +255,13 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
 #pragma unroll
     for (int blk = 0; blk < 2 * NB; ++blk) {
       const float u = cn < nc ? P.proj[(size_t)(n0 + cn) * P.proj_stride + P.C + 32 * blk + j] : 0.0f;
-      float ss = sum16(u * u);
-      ss += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(ss), 0x401F));   // lane ^ 16
-      const int ex = (__builtin_amdgcn_frexp_expf(ss) + 1) >> 1;
-      const float sc = __builtin_amdgcn_ldexpf(1.0f, 6 - ex);
-      const float t0 = fmaf(u, sc, M), q0 = t0 - M, r0 = fmaf(u, sc, -q0);
-      const float t1 = fmaf(r0, 128.0f, M), q1 = t1 - M, r1 = fmaf(r0, 128.0f, -q1);
-      const float t2 = fmaf(r1, 128.0f, M);
+      const GmPlanes q = gm_quantise(u);
       const int e = 32 * blk + j;
-      gpl[cn][0][e] = (int8_t)__float_as_uint(t0);
-      gpl[cn][1][e] = (int8_t)__float_as_uint(t1);
-      gpl[cn][2][e] = (int8_t)__float_as_uint(t2);
+      gpl[cn][0][e] = q.q0;
+      gpl[cn][1][e] = q.q1;
+      gpl[cn][2][e] = q.q2;
       gpl[cn][3][e] = 0;
-      if (j == 0) ginv[cn][blk] = __builtin_amdgcn_ldexpf(1.0f, ex - 6);
+      if (j == 0) ginv[cn][blk] = q.inv;
     }
     // the rest of the zero plane (lane groups past the last block read it)
     for (int e = 2 * rank + j; e < 256; e += 32) gpl[cn][3][e] = 0;
@@ -245,11 +280,7 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
       const int8_t* pa = abase + cn * 4 * 256;
       i32x4g c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa), bw0, zero, 0, 0, 0);
       c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa + 16), bw1, c, 0, 0, 0);
-      const float v = fmaf((float)(c[1] * 128 + c[2]), 1.0f / 16384.0f, (float)c[0]);
-      float y = g < NB ? dsc * ginv[cn][(f ? 0 : NB) + g] * v : 0.0f;
-      y += __shfl_xor(y, 16);
-      y += __shfl_xor(y, 32);
-      ys[q] = y;
+      ys[q] = gm_row(c, dsc, ginv[cn][(f ? 0 : NB) + min(g, NB - 1)], g < NB);
     }
     res[r] = g == 0 ? ys[0] : g == 1 ? ys[1] : g == 2 ? ys[2] : ys[3];
   }
@@ -257,8 +288,7 @@ __global__ __launch_bounds__(256) void gates_mfma_kernel(const GatesParams P) {
   for (int r = 0; r < 2; ++r) {
     const int cn = 4 * r + g;
     if (cn < nc)
-      P.out[(size_t)(n0 + cn) * (P.K + P.V) + row] =
-          f ? expf(-expf(ah) * softplus_f(res[r] + bias)) : sigmoid_f(res[r]);
+      P.out[(size_t)(n0 + cn) * (P.K + P.V) + row] = f ? gm_alpha(ah, res[r] + bias) : gm_gate(res[r]);
   }
 }
 
@@ -343,10 +373,8 @@ constexpr int kHeadUnroll = 16;
 // rows (four lanes a row).  Every chunk is requested first thing in the kernel, ahead of the
 // state; f_lr | g_lr are staged in LDS and read as broadcasts.  (Measured against a variant
 // with whole-wave coalesced loads transposed through LDS: the staging cost more than the
-// coalescing saved.)  GT = kGateOrder reads a model's own Q8_0 copy in gate-tile order
-// (signed q, see gates_mfma_kernel): 16-byte half hh of block g of row r at
-// ((r/16 * 2 + hh) * NB + g) * 16 + r % 16, its scale at (r/16 * NB + g) * 16 + r % 16.
-constexpr int kGateOrder = kQ8 + 100;
+// coalescing saved.)  Row-major F_b, G_b; a model's own gate-tile-order copy takes the
+// matrix-core form below.
 constexpr int kFgGateChunks = 4;    // chunks of a gate row a lane (four lanes a row)
 
 // chunk c of row r: its 16 bytes and the raw bits of its scale (fp16 for Q8_0, the E8M0
@@ -355,28 +383,19 @@ constexpr int kFgGateChunks = 4;    // chunks of a gate row a lane (four lanes a
 template <int GT>
 __device__ __forceinline__ void fg_chunk(const uint8_t* wb, const void* sb, int r, int c, int rank,
                                          uint4& w, uint32_t& sc) {
-  if constexpr (GT == kGateOrder) {
-    const int NB = rank / 32, tile = r >> 4, m = r & 15, g = c >> 1;
-    w = *reinterpret_cast<const uint4*>(wb + ((size_t)((tile * 2 + (c & 1)) * NB + g) * 16 + m) * 16);
-    sc = static_cast<const uint16_t*>(sb)[(size_t)(tile * NB + g) * 16 + m];
-  } else {
-    constexpr int EL = HFmt<GT>::kElems;
-    w = *reinterpret_cast<const uint4*>(wb + ((size_t)r * (rank / EL) + c) * 16);
-    if constexpr (GT == kQ8)
-      sc = static_cast<const uint16_t*>(sb)[(size_t)r * (rank / 32) + (c >> 1)];
-    else if constexpr (GT == kMX4)
-      sc = static_cast<const uint8_t*>(sb)[(size_t)r * (rank / 32) + c];
-    else
-      sc = 0;
-  }
+  constexpr int EL = HFmt<GT>::kElems;
+  w = *reinterpret_cast<const uint4*>(wb + ((size_t)r * (rank / EL) + c) * 16);
+  if constexpr (GT == kQ8)
+    sc = static_cast<const uint16_t*>(sb)[(size_t)r * (rank / 32) + (c >> 1)];
+  else if constexpr (GT == kMX4)
+    sc = static_cast<const uint8_t*>(sb)[(size_t)r * (rank / 32) + c];
+  else
+    sc = 0;
 }
 
 template <int GT>
 __device__ __forceinline__ float fg_dot(uint4 w, uint32_t sc, const float* __restrict__ x) {
-  if constexpr (GT == kGateOrder) {
-    w.x ^= 0x80808080u; w.y ^= 0x80808080u; w.z ^= 0x80808080u; w.w ^= 0x80808080u;
-    return __half2float(__ushort_as_half((unsigned short)sc)) * hchunk_dot<kQ8>(w, x);
-  } else if constexpr (GT == kMX4) {
+  if constexpr (GT == kMX4) {
     return __builtin_amdgcn_ldexpf(1.0f, (int)sc - 128) * mx4_chunk_dot2(w, x);
   } else if constexpr (GT == kQ8) {
     return __half2float(__ushort_as_half((unsigned short)sc)) * hchunk_dot<kQ8>(w, x);
@@ -392,7 +411,7 @@ __device__ __forceinline__ float fg_dot(uint4 w, uint32_t sc, const float* __res
 // block.
 template <int GT, int DK, int CW>
 struct FusedGates {
-  static constexpr int EL = HFmt<GT == kGateOrder ? kQ8 : GT>::kElems;
+  static constexpr int EL = HFmt<GT>::kElems;
   static constexpr int RL = DK / 64;            // forget rows a lane
   // forget-row chunks in flight a row: all 16 of a 128-rank BF16 row; 8 for the byte formats
   // (the scales take registers too)
@@ -425,13 +444,10 @@ struct FusedGates {
     rank = P.rank_f;
     cpr = rank / EL;
     scalar = P.gate_form == kGateScalar;
-    constexpr bool go = GT == kGateOrder;
-    fwp = go ? reinterpret_cast<const uint8_t*>(P.fbw) : P.fb.w;
-    fsp = go ? static_cast<const void*>(P.fbd)
-             : (GT == kMX4 ? static_cast<const void*>(P.fb.e) : static_cast<const void*>(P.fb.d));
-    const uint8_t* gwp = go ? reinterpret_cast<const uint8_t*>(P.gbw) : P.gb.w;
-    const void* gsp = go ? static_cast<const void*>(P.gbd)
-                         : (GT == kMX4 ? static_cast<const void*>(P.gb.e) : static_cast<const void*>(P.gb.d));
+    fwp = P.fb.w;
+    fsp = GT == kMX4 ? static_cast<const void*>(P.fb.e) : static_cast<const void*>(P.fb.d);
+    const uint8_t* gwp = P.gb.w;
+    const void* gsp = GT == kMX4 ? static_cast<const void*>(P.gb.e) : static_cast<const void*>(P.gb.d);
     if (scalar)
       fg_chunk<GT>(fwp, fsp, h, min(lane, cpr - 1), rank, fw[0][0], fs[0][0]);
     else
@@ -494,6 +510,118 @@ struct FusedGates {
 };
 struct FusedNone {};
 
+// Gates of this call's tokens on the int8 matrix cores, inside the head kernel, for a model
+// with its own gate-tile-order copy (KDA form, rank = 16 CPR in {32, 64, 128}): the same
+// arithmetic, in the same order, as gates_mfma_kernel (so the gates are bit for bit those
+// of the separate launch).  The wave's 8 forget tiles (the head's DK rows) and its gate tile
+// are requested at kernel entry; each of the call's T tokens (at most kFmMaxTok) is
+// quantised into three 7-bit planes per 32-element block in LDS, then per (token, tile) two
+// MFMAs give each lane group a block's plane dots, which the block scales weigh and the
+// four groups sum.  alpha goes to s_al[t][row], gate to s_gt[t][column], and (ag_out set) to
+// the rows that a later replay of these tokens reads.
+constexpr int kGateMfma = 200;   // head_kernel GT = kGateMfma + CPR
+constexpr int kFmMaxTok = 8;
+
+template <int CPR, int DK, int CW>
+struct FusedGatesMfma {
+  static constexpr int NB = CPR / 2, rank = CPR * 16;
+  static constexpr int FT = DK / 16;             // forget tiles of the head
+  static constexpr int RL = DK / 64;             // forget rows a lane in the last pass
+  static constexpr int NP = 2 * rank / 64;       // 64-element passes over f_lr | g_lr
+  i32x4g bw[FT + 1][2];
+  uint32_t bd[FT + 1];
+  float dtb[RL];
+  float ah;
+  float u[kFmMaxTok][NP];                         // f_lr | g_lr of the tokens, lane's elements
+
+  // n0, T: this call's tokens (columns of proj)
+  __device__ __forceinline__ void start(const HeadParams& P, int h, int cb, int n0, int T) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    // (token index clamped, not branched on: no wait where paths would join)
+#pragma unroll
+    for (int t = 0; t < kFmMaxTok; ++t) {
+      const float* lr = P.proj + (size_t)(n0 + min(t, T - 1)) * P.proj_stride + P.C;
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) u[t][pp] = lr[64 * pp + lane];
+    }
+    const int gc = min(g, NB - 1);               // groups past the last block: any valid
+#pragma unroll                                   // bytes (their A operand is the zero plane)
+    for (int tt = 0; tt <= FT; ++tt) {
+      const bool f = tt < FT;
+      const int tl = f ? h * FT + tt : (h * P.dv + cb * CW) >> 4;
+      const int8_t* bp = (f ? P.fbw : P.gbw) + (size_t)tl * 16 * rank + (gc * 16 + m) * 16;
+      bw[tt][0] = *reinterpret_cast<const i32x4g*>(bp);
+      bw[tt][1] = *reinterpret_cast<const i32x4g*>(bp + NB * 256);
+      bd[tt] = (f ? P.fbd : P.gbd)[((size_t)tl * NB + gc) * 16 + m];
+    }
+#pragma unroll
+    for (int i = 0; i < RL; ++i) dtb[i] = P.dt_bias[h * DK + lane + 64 * i];
+    ah = P.a_log[h];
+  }
+
+  // tokens n0 .. n0 + T - 1 (columns of proj / alpha_gate)
+  __device__ __forceinline__ void finish(const HeadParams& P, int n0, int T, int h, int cb,
+                                         int8_t (*gpl)[4][256], float (*ginv)[8],
+                                         float (*s_al)[DK], float (*s_gt)[CW]) {
+    const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+    // quantise: element e = 64 p + lane of f_lr | g_lr, block e / 32 on a half-wave
+#pragma unroll
+    for (int t = 0; t < kFmMaxTok; ++t) {
+      if (t >= T) break;
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) {
+        const int e = 64 * pp + lane, blk = e >> 5, jj = e & 31;
+        const GmPlanes q = gm_quantise(this->u[t][pp]);
+        gpl[t][0][e] = q.q0;
+        gpl[t][1][e] = q.q1;
+        gpl[t][2][e] = q.q2;
+        if (jj == 0) ginv[t][blk] = q.inv;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gpl[t][3][64 * k + lane] = 0;
+    }
+    __syncthreads();
+    // per (token, tile): the raw row dots, stored by lane group 0
+    const int8_t* abase0 = &gpl[0][(m >> 2) == g && g < NB ? (m & 3) : 3][32 * g];
+    const i32x4g zero = {0, 0, 0, 0};
+    for (int t = 0; t < T; ++t) {
+      const int8_t* abase = abase0 + (size_t)t * 4 * 256;
+#pragma unroll
+      for (int tt = 0; tt <= FT; ++tt) {
+        const bool f = tt < FT;
+        const int8_t* pa = abase + (f ? 0 : rank);
+        i32x4g c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa), bw[tt][0], zero, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(*reinterpret_cast<const i32x4g*>(pa + 16), bw[tt][1], c, 0, 0, 0);
+        const float dsc = __half2float(__ushort_as_half((unsigned short)bd[tt]));
+        const float y = gm_row(c, dsc, ginv[t][(f ? 0 : NB) + min(g, NB - 1)], g < NB);
+        if (g == 0) {
+          if (f) s_al[t][16 * tt + m] = y;
+          else s_gt[t][m] = y;
+        }
+      }
+    }
+    __syncthreads();
+    // the forms, a row (or column) a lane
+    const size_t agw = (size_t)(P.H * DK + P.H * P.dv);
+    for (int t = 0; t < T; ++t) {
+      float* agr = P.ag_out + (size_t)(n0 + t) * agw;
+#pragma unroll
+      for (int i = 0; i < RL; ++i) {
+        const int r = lane + 64 * i;
+        const float a = gm_alpha(ah, s_al[t][r] + dtb[i]);
+        s_al[t][r] = a;
+        if (P.ag_out && cb == 0) agr[h * DK + r] = a;
+      }
+      if (lane < CW) {
+        const float gt = gm_gate(s_gt[t][lane]);
+        s_gt[t][lane] = gt;
+        if (P.ag_out) agr[P.H * DK + h * P.dv + cb * CW + lane] = gt;
+      }
+    }
+    __syncthreads();
+  }
+};
+
 template <int DK, int CW, int GT>
 __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   constexpr int RG = 256 / CW;
@@ -511,8 +639,14 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   const int r0 = rg * RPT;                     // this lane's first key row
   const int nparts = dv / CW;
   const int rl = P.rank_f + P.rank_g;
-  std::conditional_t<(GT >= 0), FusedGates<(GT >= 0 ? GT : kF32), DK, CW>, FusedNone> fg;
-  if constexpr (GT >= 0) fg.start(P, b, h, cb);
+  constexpr bool kMf = GT >= kGateMfma;           // gates of this call's tokens on MFMA
+  std::conditional_t<(GT >= kGateMfma), FusedGatesMfma<(kMf ? GT - kGateMfma : 8), DK, CW>,
+                     std::conditional_t<(GT >= 0), FusedGates<(GT >= 0 && !kMf ? GT : kF32), DK, CW>,
+                                        FusedNone>> fg;
+  __shared__ __align__(16) float s_mal[kMf ? kFmMaxTok : 1][kMf ? DK : 1];
+  __shared__ __align__(16) float s_mgt[kMf ? kFmMaxTok : 1][kMf ? CW : 1];
+  if constexpr (kMf) fg.start(P, h, cb, b * P.T, P.T);
+  else if constexpr (GT >= 0) fg.start(P, b, h, cb);
 
   float* Sb = P.S + ((size_t)b * H + h) * DK * dv + j;
   float4 st[RPT];
@@ -548,14 +682,17 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
       const float4 k4 = *reinterpret_cast<const float4*>(arow + ck0 + i);
       x.qv[i] = a.x; x.qv[i + 1] = a.y; x.qv[i + 2] = a.z; x.qv[i + 3] = a.w;
       x.kv[i] = k4.x; x.kv[i + 1] = k4.y; x.kv[i + 2] = k4.z; x.kv[i + 3] = k4.w;
-      if constexpr (GT < 0) {
-        const float4 g4 = *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
+      if constexpr (GT < 0 || kMf) {
+        const float4 g4 = kMf && !pre ? *reinterpret_cast<const float4*>(&s_mal[u - a_pre][r0 + i])
+                                      : *reinterpret_cast<const float4*>(ag + h * DK + r0 + i);
         x.al[i] = g4.x; x.al[i + 1] = g4.y; x.al[i + 2] = g4.z; x.al[i + 3] = g4.w;
       }
     }
     const float4 a = *reinterpret_cast<const float4*>(arow + cv0);
     x.v4[0] = a.x; x.v4[1] = a.y; x.v4[2] = a.z; x.v4[3] = a.w;
-    if constexpr (GT < 0) x.gate = *reinterpret_cast<const float4*>(ag + K + h * dv + j);
+    if constexpr (GT < 0 || kMf)
+      x.gate = kMf && !pre ? *reinterpret_cast<const float4*>(&s_mgt[u - a_pre][cq * 4])
+                           : *reinterpret_cast<const float4*>(ag + K + h * dv + j);
     x.braw = prow[C + rl + h];
   };
   // token u of the sequence from the inputs in x: state update, outputs (this call's
@@ -627,7 +764,12 @@ __global__ __launch_bounds__(64) void head_kernel(const HeadParams P) {
   // which loads are still outstanding at each use and waits for one set while the other's
   // are in flight; past the last token the loads repeat it
   Tok x0, x1;
-  if constexpr (GT >= 0) {
+  if constexpr (kMf) {
+    __shared__ __align__(16) int8_t s_gpl[kFmMaxTok][4][256];
+    __shared__ float s_ginv[kFmMaxTok][8];
+    fg.finish(P, b * P.T, a_cur, h, cb, s_gpl, s_ginv, s_mal, s_mgt);
+  }
+  if constexpr (GT >= 0 && !kMf) {
     // fused decode gates: the sequence's one token, its gates computed here
     __shared__ __align__(16) float s_gl[2 * kMaxRank];
     __shared__ __align__(16) float s_al[DK];
@@ -694,10 +836,19 @@ static void launch_head_gt(const HeadParams& p, const dim3 grid, hipStream_t s) 
 }
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s) {
-  if (p.fuse_gates && (p.T != 1 || p.pre_ntok)) return hipErrorInvalidValue;
+  if (p.fuse_gates == 1 && (p.T != 1 || p.pre_ntok)) return hipErrorInvalidValue;
   const dim3 grid((p.dv / kHeadCols) * p.H * p.B);
+  if (p.fuse_gates == 2) {
+    const int cpr = p.rank_f / 16;
+    if (p.dk != 128 || p.T > kFmMaxTok || p.gate_form != kGateKda || !p.fbw || p.rank_g != p.rank_f ||
+        (cpr != 2 && cpr != 4 && cpr != 8))
+      return hipErrorInvalidValue;
+    if (cpr == 2) head_kernel<128, kHeadCols, kGateMfma + 2><<<grid, 64, 0, s>>>(p);
+    else if (cpr == 4) head_kernel<128, kHeadCols, kGateMfma + 4><<<grid, 64, 0, s>>>(p);
+    else head_kernel<128, kHeadCols, kGateMfma + 8><<<grid, 64, 0, s>>>(p);
+    return hipGetLastError();
+  }
   if (!p.fuse_gates) launch_head_gt<-1>(p, grid, s);
-  else if (p.fbw) launch_head_gt<kGateOrder>(p, grid, s);
   else if (p.wt == kF32) launch_head_gt<kF32>(p, grid, s);
   else if (p.wt == kBF16) launch_head_gt<kBF16>(p, grid, s);
   else if (p.wt == kMX4) launch_head_gt<kMX4>(p, grid, s);

@@ -177,11 +177,15 @@ struct HeadParams {
   const float* pre_ag = nullptr;
   const int* pre_ntok = nullptr;
   int pre_T = 0;
-  // decode (T = 1, no folded commit): compute the gates here instead of reading alpha_gate:
-  // alpha of the head's rows from F_b (fb, or the gate-order copy fbw/fbd of a model that
-  // owns its weights) and f_lr, the wave's output-gate columns from G_b and g_lr (proj at C
-  // and C + rank_f), in the gate form gate_form
+  // fuse_gates = 1, decode (T = 1, no folded commit): compute the gates here instead of
+  // reading alpha_gate: alpha of the head's rows from F_b (fb) and f_lr, the wave's
+  // output-gate columns from G_b and g_lr (proj at C and C + rank_f), in the gate form
+  // gate_form (row-major fb, gb).  fuse_gates = 2: the same for this call's T <= 8 tokens
+  // of a model with its own gate-tile-order copy (fbw/fbd, gbw/gbd; KDA form, rank_f in
+  // {32, 64, 128}, d_k = 128) on the matrix cores, also written to ag_out ([N][H*dk + H*dv]
+  // as alpha_gate) when that is set (a replayed commit reads them there)
   int fuse_gates = 0;
+  float* ag_out = nullptr;
   int gate_form = 0;
   float gate_lb = 0.f;
   const int8_t* fbw = nullptr;
@@ -192,7 +196,7 @@ struct HeadParams {
 
 hipError_t launch_head(const HeadParams& p, hipStream_t s);
 // decode batches up to this many sequences run the gates inside the head kernel (row-major
-// F_b, G_b; a model's own gate-tile-order copy, read 16 contiguous rows at a time)
+// F_b, G_b with vector dots; a model's own gate-tile-order copy on the matrix cores)
 constexpr int kFuseGatesMaxB = 8;
 constexpr int kFuseGatesMaxBOwned = 16;
 

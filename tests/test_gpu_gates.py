@@ -181,3 +181,36 @@ def test_fused_and_separate_gates_agree(gate, wtype):
     assert es <= 1e-5, es
     assert range_rel(Z8, Z9[:, :8]) <= 1e-5
     model.close()
+
+
+def test_matrix_core_gates_in_head_bit_exact():
+    """A model with its own gate-tile-order copy computes the gates inside the head kernel on
+    the matrix cores for up to 16 decode sequences, and with the separate gates launch above
+    that; both take the same arithmetic in the same order, so 16 sequences decoded alone and
+    as the first 16 rows of a batch of 17 agree bit for bit (2 layers, 3 steps)."""
+    import torch
+    w = synth.scaled(synth.WORKLOADS["stack"], n_layers=2, batch=17, steps=3, seed=109)
+    _say("matrix-core gates in the head kernel vs the gates launch: B=16 vs B=17, bit for bit")
+    run = synth.draw_run(w)
+    model = gpu_model(run)
+    assert model.owns_weights()
+    model.set_option(2, 0)
+    res = {}
+    for B in (16, 17):
+        st = model.new_state(B)
+        st.S.copy_(torch.from_numpy(np.ascontiguousarray(run.s0[:, :B])))
+        ws = model.workspace(0, B)
+        ys = []
+        for t in range(w.steps):
+            x = torch.from_numpy(np.ascontiguousarray(run.x[t, :B, 0, :])).cuda()
+            y = torch.empty_like(x)
+            model.decode_step(x, y, st, ws)
+            ys.append(y.cpu().numpy())
+        torch.cuda.synchronize()
+        res[B] = (np.array(ys), st.S.cpu().numpy(), st.conv.cpu().numpy())
+    y16, S16, Z16 = res[16]
+    y17, S17, Z17 = res[17]
+    assert np.array_equal(y16, y17[:, :16])
+    assert np.array_equal(S16, S17[:, :16])
+    assert np.array_equal(Z16, Z17[:, :16])
+    model.close()
