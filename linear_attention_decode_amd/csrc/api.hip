@@ -364,8 +364,8 @@ int enqueue_layer(kda_model* m, int l, const float* x_in, float* y, int B, int T
   // one token a sequence for a few sequences: the head kernel computes its own gates (each
   // of its waves re-reads all of its head's F_b rows, which a wide batch would pay for); a
   // model with its own gate-tile-order copy on the matrix cores, others with vector dots.
-  // (The matrix-core form takes up to 8 tokens, but at 4, verify's, its serial chain per
-  // token cost more than the separate launch: 22.8 us against 11.3 + 7.1.)
+  // (A matrix-core form for up to 8 tokens cost more than the separate launch at verify's 4
+  // tokens a sequence: 22.8 us against 11.3 + 7.1.)
   const bool mfma_gates = L.fbw && d.gate == KDA_GATE_KDA && d.d_k == 128 &&
                           (d.rank_f == 32 || d.rank_f == 64 || d.rank_f == 128) && T == 1 &&
                           !fold && B <= kFuseGatesMaxBOwned;

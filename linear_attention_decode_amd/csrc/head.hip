@@ -514,13 +514,15 @@ struct FusedNone {};
 // with its own gate-tile-order copy (KDA form, rank = 16 CPR in {32, 64, 128}): the same
 // arithmetic, in the same order, as gates_mfma_kernel (so the gates are bit for bit those
 // of the separate launch).  The wave's 8 forget tiles (the head's DK rows) and its gate tile
-// are requested at kernel entry; each of the call's T tokens (at most kFmMaxTok) is
+// are requested at kernel entry; each of the call's T tokens (at most kFmMaxTok: one-token
+// steps only, since at verify's 4 tokens the per-token serial chain below cost more than the
+// separate launch) is
 // quantised into three 7-bit planes per 32-element block in LDS, then per (token, tile) two
 // MFMAs give each lane group a block's plane dots, which the block scales weigh and the
 // four groups sum.  alpha goes to s_al[t][row], gate to s_gt[t][column], and (ag_out set) to
 // the rows that a later replay of these tokens reads.
 constexpr int kGateMfma = 200;   // head_kernel GT = kGateMfma + CPR
-constexpr int kFmMaxTok = 8;
+constexpr int kFmMaxTok = 1;
 
 template <int CPR, int DK, int CW>
 struct FusedGatesMfma {

@@ -180,7 +180,7 @@ struct HeadParams {
   // fuse_gates = 1, decode (T = 1, no folded commit): compute the gates here instead of
   // reading alpha_gate: alpha of the head's rows from F_b (fb) and f_lr, the wave's
   // output-gate columns from G_b and g_lr (proj at C and C + rank_f), in the gate form
-  // gate_form (row-major fb, gb).  fuse_gates = 2: the same for this call's T <= 8 tokens
+  // gate_form (row-major fb, gb).  fuse_gates = 2: the same for this call's T = 1 token
   // of a model with its own gate-tile-order copy (fbw/fbd, gbw/gbd; KDA form, rank_f in
   // {32, 64, 128}, d_k = 128) on the matrix cores, also written to ag_out ([N][H*dk + H*dv]
   // as alpha_gate) when that is set (a replayed commit reads them there)
