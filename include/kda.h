@@ -98,7 +98,9 @@ const char* kda_last_error(void);
  *            byte i, low nibble first), then (at the next 256-byte boundary) a plane of
  *            rows*(cols/32) scale bytes s + 127.  cols % 32 == 0.  Decode and verify run
  *            it through the per-layer kernels (vector dots, as the page notes for one
- *            row); the one-launch decode and the chunked prefill do not take it.
+ *            row; from 5 columns the matrix cores, after gfx950's exact scaled FP4 ->
+ *            BF16 conversion); the one-launch decode and the chunked prefill do not take
+ *            it.
  * ---------------------------------------------------------------------------------- */
 /* Bytes a packed [rows][cols] matrix occupies (0 on an invalid request). */
 size_t kda_packed_bytes(int dtype, int64_t rows, int64_t cols);

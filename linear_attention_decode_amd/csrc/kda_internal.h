@@ -126,7 +126,7 @@ struct GemvParams {
   // launch_skinny only: the Q8_0 matrices (seg[i].m: w at the segment's first 16-row tile,
   // d at its scales) are in the one-launch decode's matrix-core order
   int mma = 0;
-  // launch_skinny only: the weight format (kQ8 or kBF16)
+  // launch_skinny only: the weight format (kQ8, kBF16 or kMX4)
   int wt = kQ8;
 };
 

@@ -1,11 +1,11 @@
-// Q8_0 or BF16 weights times a few columns on the matrix cores (skinny.hip).
+// Q8_0, BF16 or MXFP4 weights times a few columns on the matrix cores (skinny.hip).
 #pragma once
 #include "kda_internal.h"
 
 namespace kda {
 
 // True when launch_skinny handles this product: Q8_0 weights, 8 < N <= 64 columns,
-// K in {2048, 4096}; BF16 weights, 4 < N <= 64 columns, K = 2048.
+// K in {2048, 4096}; BF16 or MXFP4 weights, 4 < N <= 64 columns, K = 2048.
 bool skinny_supported(int wt, int N, int K);
 // True when launch_skinny handles a product whose Q8_0 matrices are in the one-launch
 // decode's matrix-core order (GemvParams::mma): 1 <= N <= 64 columns, K in {1024, 2048}.

@@ -19,7 +19,10 @@
 // hi/lo pair, the weight values are exact, and the MFMA accumulates in fp32.
 // BF16 weights (BF = true) go to v_mfma_f32_16x16x32_bf16 as they are, against x split into
 // two BF16 terms (hi = bf16(x), lo = bf16(x - hi): ~16 significant bits, as in the prefill
-// GEMMs); no scales or bias, the MFMAs accumulate over the whole K range.
+// GEMMs); no scales or bias, the MFMAs accumulate over the whole K range.  MXFP4 weights
+// (FP4 = true) take the same path after gfx950's scaled FP4 -> BF16 conversion
+// (v_cvt_scalef32_pk_bf16_fp4, two codes a byte, low nibble first, times the block's E8M0
+// scale), which is exact: every E2M1 value times a power of two is a BF16 value.
 #include <type_traits>
 
 #include "kda_device.h"
@@ -29,6 +32,7 @@ namespace kda {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2s __attribute__((ext_vector_type(2)));
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
@@ -45,7 +49,8 @@ bool skinny_supported(int wt, int N, int K) {
   // Q8_0 from 9 columns (the vector GEMV streams its bytes fast enough below), BF16 from 5
   // (its vector GEMV pays an unpack and N FMAs a weight: 49 us for the D = 2048 projections
   // at 8 columns against 12 here; at 2 columns the GEMV's 14 us beat the prep + GEMM pair)
-  return ((wt == kQ8 && N > 8 && (K == 2048 || K == 4096)) || (wt == kBF16 && N > 4 && K == 2048)) &&
+  return ((wt == kQ8 && N > 8 && (K == 2048 || K == 4096)) ||
+          ((wt == kBF16 || wt == kMX4) && N > 4 && K == 2048)) &&
          N <= 64;
 }
 
@@ -236,7 +241,17 @@ __device__ __forceinline__ f16x8 bytes_to_f16(const uint2 w) {
 // per 16-row tile, 16-byte chunks c = ((w * 2U + t) * 2 + h) * 64 + r + 16 g holding row r,
 // bytes 16 h .. + 15 of block 4 (4 t + w) + g as signed q; the tile's scales at
 // ((w * 64 + r + 16 g) * 2U + t)), U = K / 1024.
-template <int NT, int KB4, bool MMA, int RT, bool BF>
+// 8 MXFP4 codes (4 bytes, low nibble first) times 2^(e - 127) as 8 BF16 values
+__device__ __forceinline__ bf16x8s fp4x8_to_bf16(uint32_t codes, uint32_t e) {
+  const float sc = __builtin_amdgcn_ldexpf(1.0f, (int)e - 127);
+  const bf16x2s p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+  const bf16x2s p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+  const bf16x2s p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+  const bf16x2s p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+  return bf16x8s{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int NT, int KB4, bool MMA, int RT, bool BF, bool FP4 = false>
 __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkParams P) {
   constexpr int KB = 4 * KB4;
   constexpr int PD = 4;                          // k blocks of B fragments in flight
@@ -290,15 +305,21 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
   // is requested up front
   const int ag = lane >> 4;
   const int kb0 = wave * KB4;
-  std::conditional_t<BF, uint4, uint2> a[RT][KB4];
+  // (MXFP4: 4 bytes of codes, elements 8 (lane >> 4) .. + 7, and the block's scale byte)
+  std::conditional_t<BF, std::conditional_t<FP4, uint32_t, uint4>, uint2> a[RT][KB4];
+  uint32_t ae[FP4 ? RT : 1][FP4 ? KB4 : 1];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int tr = tile_of(rt);
     const int ar = min(16 * tr + (lane & 15), nrows - 1);
-    const uint8_t* wrow = sg.m.w + (size_t)(row0 + ar) * K * (BF ? 2 : 1) + (BF ? 16 : 8) * ag;
+    const uint8_t* wrow = FP4 ? sg.m.w + (size_t)(row0 + ar) * (K / 2) + 4 * ag
+                              : sg.m.w + (size_t)(row0 + ar) * K * (BF ? 2 : 1) + (BF ? 16 : 8) * ag;
 #pragma unroll
     for (int j = 0; j < KB4; ++j) {
-      if constexpr (BF) {
+      if constexpr (FP4) {
+        a[rt][j] = *reinterpret_cast<const uint32_t*>(wrow + (size_t)(kb0 + j) * 16);
+        ae[rt][j] = sg.m.e[(size_t)(row0 + ar) * KB + kb0 + j];
+      } else if constexpr (BF) {
         a[rt][j] = *reinterpret_cast<const uint4*>(wrow + (size_t)(kb0 + j) * 64);
       } else if constexpr (MMA) {
         constexpr int U2 = KB4 / 4;              // 2U
@@ -374,7 +395,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void skinny_gemm_kernel(const SkPara
     if constexpr (BF) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const bf16x8s av = __builtin_bit_cast(bf16x8s, a[rt][j]);
+        bf16x8s av;
+        if constexpr (FP4) av = fp4x8_to_bf16(a[rt][j], ae[rt][j]);
+        else av = __builtin_bit_cast(bf16x8s, a[rt][j]);
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8s, bh[slot][t]),
@@ -500,7 +523,7 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   // least 192 blocks and the operands fit the registers (up to 32 columns, K = 2048)
   int rows32 = 0;
   for (int i = 0; i < g.nseg; ++i) rows32 += (g.seg[i].rows + 31) / 32;
-  const int RT = (g.wt != kBF16 && rows32 >= 192 && NT <= 2 && g.K == 2048) ? 2 : 1;
+  const int RT = (g.wt == kQ8 && rows32 >= 192 && NT <= 2 && g.K == 2048) ? 2 : 1;
   int tiles = 0;
   for (int i = 0; i < g.nseg; ++i) {
     p.seg[i].m = g.seg[i].m;
@@ -526,7 +549,7 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   p.pre_ntok = g.pre_ntok;
   p.pre_T = g.pre_T;
   const int KG = g.K > 2048 ? 2 : 1;             // 8-element groups a thread (K <= 4096)
-  const bool bf = g.wt == kBF16;
+  const bool bf = g.wt == kBF16 || g.wt == kMX4, fp4 = g.wt == kMX4;
 #define KDA_SK_PREP(pro, kg, b) \
   if ((prologue == kProX) == (pro == kProX) && KG == kg && bf == b) \
     skinny_prep_kernel<pro, kg, b><<<NT * 16, kSkThreads, 0, s>>>(g, NT, p.S);
@@ -542,8 +565,10 @@ hipError_t launch_skinny(int prologue, const GemvParams& g, void* scratch, hipSt
   if (!bf && NT == nt && KB4 == kb4 && (g.mma != 0) == mm && RT == rt) \
     skinny_gemm_kernel<nt, kb4, mm, rt, false><<<tiles, kSkThreads, 0, s>>>(p);
 #define KDA_SK_BF(nt, kb4) \
-  if (bf && NT == nt && KB4 == kb4 && RT == 1) \
-    skinny_gemm_kernel<nt, kb4, false, 1, true><<<tiles, kSkThreads, 0, s>>>(p);
+  if (bf && !fp4 && NT == nt && KB4 == kb4 && RT == 1) \
+    skinny_gemm_kernel<nt, kb4, false, 1, true><<<tiles, kSkThreads, 0, s>>>(p); \
+  if (fp4 && NT == nt && KB4 == kb4 && RT == 1) \
+    skinny_gemm_kernel<nt, kb4, false, 1, true, true><<<tiles, kSkThreads, 0, s>>>(p);
   KDA_SK_CASE(1, 8, false, 1) KDA_SK_CASE(2, 8, false, 1) KDA_SK_CASE(3, 8, false, 1) KDA_SK_CASE(4, 8, false, 1)
   KDA_SK_CASE(1, 16, false, 1) KDA_SK_CASE(2, 16, false, 1) KDA_SK_CASE(3, 16, false, 1) KDA_SK_CASE(4, 16, false, 1)
   KDA_SK_CASE(1, 32, false, 1) KDA_SK_CASE(2, 32, false, 1) KDA_SK_CASE(3, 32, false, 1) KDA_SK_CASE(4, 32, false, 1)
