@@ -98,7 +98,7 @@ const char* kda_last_error(void);
  *            byte i, low nibble first), then (at the next 256-byte boundary) a plane of
  *            rows*(cols/32) scale bytes s + 127.  cols % 32 == 0.  Decode and verify run
  *            it through the per-layer kernels (vector dots, as the page notes for one
- *            row; from 5 columns the matrix cores, after gfx950's exact scaled FP4 ->
+ *            row; from 2 columns the matrix cores, after gfx950's exact scaled FP4 ->
  *            BF16 conversion); the one-launch decode and the chunked prefill do not take
  *            it.
  * ---------------------------------------------------------------------------------- */

@@ -5,7 +5,7 @@
 namespace kda {
 
 // True when launch_skinny handles this product: Q8_0 weights, 8 < N <= 64 columns,
-// K in {2048, 4096}; BF16 or MXFP4 weights, 4 < N <= 64 columns, K = 2048.
+// K in {2048, 4096}; BF16 weights, 4 < N <= 64 columns, MXFP4 weights, 1 < N <= 64, K = 2048.
 bool skinny_supported(int wt, int N, int K);
 // True when launch_skinny handles a product whose Q8_0 matrices are in the one-launch
 // decode's matrix-core order (GemvParams::mma): 1 <= N <= 64 columns, K in {1024, 2048}.

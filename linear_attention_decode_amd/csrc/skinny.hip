@@ -48,9 +48,10 @@ size_t skinny_scratch_bytes(int N, int K) {
 bool skinny_supported(int wt, int N, int K) {
   // Q8_0 from 9 columns (the vector GEMV streams its bytes fast enough below), BF16 from 5
   // (its vector GEMV pays an unpack and N FMAs a weight: 49 us for the D = 2048 projections
-  // at 8 columns against 12 here; at 2 columns the GEMV's 14 us beat the prep + GEMM pair)
-  return ((wt == kQ8 && N > 8 && (K == 2048 || K == 4096)) ||
-          ((wt == kBF16 || wt == kMX4) && N > 4 && K == 2048)) &&
+  // at 8 columns against 12 here; at 2 columns the GEMV's 14 us beat the prep + GEMM pair),
+  // MXFP4 from 2 (its vector GEMV's code decoding: 36 us at 2 columns, 79 at 4)
+  return ((wt == kQ8 && N > 8 && (K == 2048 || K == 4096)) || (wt == kBF16 && N > 4 && K == 2048) ||
+          (wt == kMX4 && N > 1 && K == 2048)) &&
          N <= 64;
 }
 

@@ -66,7 +66,7 @@ def test_decode_mxfp4_small_stack(gate):
 
 def test_decode_mxfp4_stack_d2048():
     """The stack workload's shapes (D=2048, 16 heads, rank 128) with MXFP4 projections,
-    4 layers, B = 1, 4 (vector dots) and 9 (matrix cores: the codes converted to BF16 by
+    4 layers, B = 1 (vector dots), 4 and 9 (matrix cores: the codes converted to BF16 by
     gfx950's scaled FP4 conversion), 6 steps, per-layer kernels."""
     for B in (1, 4, 9):
         w = synth.scaled(synth.WORKLOADS["stack"], wtype="mxfp4", n_layers=4, batch=B, steps=6, seed=162 + B)
