@@ -45,26 +45,23 @@ inline PackedMat packed_view(const void* base, int wt, int64_t rows, int64_t col
 
 // 16 bytes of MXFP4 codes (32 elements, code 2i in the low nibble of byte i) times 32
 // inputs: sum over the elements of twice the E2M1 value times x (the caller halves the
-// block scale).  The doubled magnitudes 0, 1, 2, 3, 4, 6, 8, 12 of codes & 7 come from a
-// byte permute of two constant words; the sign (code bit 3) flips the float's sign bit.
+// block scale).  gfx950's packed FP4 conversion with scale 2 turns a byte's two codes (low
+// nibble into the first float) into the doubled values, exactly; the products are summed
+// in the order elements 8 i + 2 k + half, the low nibbles of a word's bytes first.
 __device__ __forceinline__ float mx4_chunk_dot2(const uint4 w, const float* __restrict__ x) {
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
   float s = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    const f32x2v v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 2.0f, 0),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 2.0f, 1),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 2.0f, 2),
+                         __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wd[i], 2.0f, 3)};
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // codes of elements 8 i + 2 k + half, k = 0..3, one per byte
-      const uint32_t c = (wd[i] >> (4 * half)) & 0x0F0F0F0Fu;
-      const uint32_t mag = __builtin_amdgcn_perm(0x0C080604u, 0x03020100u, c & 0x07070707u);
-      const uint32_t sg = (c & 0x08080808u) << 4;      // sign into bit 7 of each byte
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float v = __uint_as_float(__float_as_uint((float)((mag >> (8 * k)) & 0xffu)) ^
-                                        (((sg >> (8 * k)) & 0x80u) << 24));
-        s = fmaf(v, x[8 * i + 2 * k + half], s);
-      }
-    }
+      for (int k = 0; k < 4; ++k) s = fmaf(v[k][half], x[8 * i + 2 * k + half], s);
   }
   return s;
 }
