@@ -552,18 +552,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // ---------------------------------------------------------------------------------------
-// Scan over the chunks of one (sequence, head): a block of two waves owns 32 value columns
-// (16 per wave) and keeps those state columns in MFMA accumulators for the whole sequence.
-// Each chunk's operands stream through LDS in four segments, shared by both waves:
+// Scan over the chunks of one (sequence, head): a block of four waves; waves 0 and 1 own 32
+// value columns (16 each) and keep those state columns in MFMA accumulators for the whole
+// sequence, waves 2 and 3 only stream each chunk's operands into LDS.  A chunk's operands
+// come in four segments, shared by both computing waves:
 //   0: -W              D = -W S
 //   1: q 2^G           O = (q 2^G) S
 //   2: A | U | dec     D += U, O += A D (then stored), S <- diag(dec) S
 //   3: Kt^T            S += Kt^T D
-// Segment n lands in slot n % 4 by direct global->LDS loads issued three segments ahead,
-// so each load has three compute phases to arrive.  Every wave issues the same number of
-// loads per segment, so a wait for "at most the loads of the next two segments
-// outstanding" (vector memory operations retire in order) means the segment about to be
-// read has landed; the barrier that follows makes that true for both waves' loads.
+// The segments go round five LDS slots (the whole LDS) by direct global->LDS loads issued
+// four segments ahead of their use: the scan is bound by these loads (~120 KB per block and
+// chunk), not by its products.  Only the loading waves issue loads, so a wait for "at most
+// the loads of the three later segments outstanding" (vector memory operations retire in
+// order) means the segment about to be read has landed, and the computing waves' output
+// stores count against no such wait.  One barrier per segment hands the segment to the
+// computing waves and the slot they have finished with back to the loaders.
 // ---------------------------------------------------------------------------------------
 template <int D>
 struct ScanSeg {
@@ -575,11 +578,13 @@ struct ScanSeg {
   static constexpr int FD = D / 4;                  // dec
   static constexpr int S2 = FA + FU + FD;
   static constexpr int SLOT = FW > FK ? (FW > S2 ? FW : S2) : (FK > S2 ? FK : S2);
-  // loads per wave (= per lane) of each segment
+  static constexpr int NSLOT = 5;
+  // loads per loading wave (= per lane) of each segment
   static constexpr int NLD[4] = {FW / 128, FW / 128, FA / 128 + FU / 128 + 1, FK / 128};
   static_assert(FW % 128 == 0 && FK % 128 == 0 && FA % 128 == 0 && FU % 128 == 0 && FD <= 128,
                 "segment pieces are whole rounds of 128 loads");
-  static_assert(4 * SLOT * 16 <= 160 * 1024, "LDS");
+  static_assert(NSLOT * SLOT * 16 <= 160 * 1024, "LDS");
+  static_assert(NLD[0] + NLD[1] + NLD[2] + NLD[3] - 1 < 64, "vmcnt");
 };
 
 struct ScanSrc {
@@ -596,27 +601,29 @@ __device__ __forceinline__ void dma16(const u32x4_t* src, u32x4_t* lds_wave_base
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(lds) : "m0");
 }
 
+// Segment SEG of chunk c into slot, by the two loading waves (lt = thread 0..127 among
+// them, lw = loading wave 0 or 1).
 template <int D, int SEG>
-__device__ __forceinline__ void scan_issue(const ScanSrc& g, size_t c, u32x4_t* slot, int tid,
-                                           int lane, int wave) {
+__device__ __forceinline__ void scan_issue(const ScanSrc& g, size_t c, u32x4_t* slot, int lt,
+                                           int lane, int lw) {
   using Sg = ScanSeg<D>;
   if constexpr (SEG == 0 || SEG == 1) {
-    const u32x4_t* src = (SEG == 0 ? g.W : g.Q) + c * Sg::FW + tid;
+    const u32x4_t* src = (SEG == 0 ? g.W : g.Q) + c * Sg::FW + lt;
 #pragma unroll
-    for (int u = 0; u < Sg::FW / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * wave);
+    for (int u = 0; u < Sg::FW / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * lw);
   } else if constexpr (SEG == 2) {
-    const u32x4_t* sa = g.A + c * Sg::FA + tid;
+    const u32x4_t* sa = g.A + c * Sg::FA + lt;
 #pragma unroll
-    for (int u = 0; u < Sg::FA / 128; ++u) dma16(sa + 128 * u, slot + 128 * u + 64 * wave);
-    const u32x4_t* su = g.U + c * (Sg::NJ * 4 * 64) + tid;
+    for (int u = 0; u < Sg::FA / 128; ++u) dma16(sa + 128 * u, slot + 128 * u + 64 * lw);
+    const u32x4_t* su = g.U + c * (Sg::NJ * 4 * 64) + lt;
 #pragma unroll
-    for (int u = 0; u < Sg::FU / 128; ++u) dma16(su + 128 * u, slot + Sg::FA + 128 * u + 64 * wave);
+    for (int u = 0; u < Sg::FU / 128; ++u) dma16(su + 128 * u, slot + Sg::FA + 128 * u + 64 * lw);
     if (lane < Sg::FD / 2)
-      dma16(g.D + c * Sg::FD + wave * (Sg::FD / 2) + lane, slot + Sg::FA + Sg::FU + wave * (Sg::FD / 2));
+      dma16(g.D + c * Sg::FD + lw * (Sg::FD / 2) + lane, slot + Sg::FA + Sg::FU + lw * (Sg::FD / 2));
   } else {
-    const u32x4_t* src = g.K + c * Sg::FK + tid;
+    const u32x4_t* src = g.K + c * Sg::FK + lt;
 #pragma unroll
-    for (int u = 0; u < Sg::FK / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * wave);
+    for (int u = 0; u < Sg::FK / 128; ++u) dma16(src + 128 * u, slot + 128 * u + 64 * lw);
   }
 }
 
@@ -628,6 +635,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" : : "n"(N) : "memory");
 }
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" : : : "memory"); }
+// the computing waves' barrier: their LDS reads of the segment just used have returned
+__device__ __forceinline__ void lds_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
 
 // acc[mt] += sum_p F(mt, p) B[p] for the four token tiles mt, fragment mt * KS + p of the
 // slot; the fragments of step p + 1 are read while step p runs on the matrix cores.
@@ -674,13 +685,11 @@ __device__ __forceinline__ void key_tiles_times(const u32x4_t* slot, const Frag 
 }
 
 template <int D>
-__global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) {
+__global__ __launch_bounds__(256) void chunk_scan_kernel(const PrefillParams P) {
   using Sg = ScanSeg<D>;
   constexpr int KS = Sg::KS, MTI = Sg::MTI, NJ2 = Sg::NJ / 2;
-  __shared__ u32x4_t slot0[Sg::SLOT];
-  __shared__ u32x4_t slot1[Sg::SLOT];
-  __shared__ u32x4_t slot2[Sg::SLOT];
-  __shared__ u32x4_t slot3[Sg::SLOT];
+  constexpr int N0 = Sg::NLD[0], N1 = Sg::NLD[1], N2 = Sg::NLD[2], N3 = Sg::NLD[3];
+  __shared__ u32x4_t slots[Sg::NSLOT * Sg::SLOT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q4 = lane >> 4, r16 = lane & 15;
   // the blocks of one (sequence, head) on one XCD (blocks go round-robin over 8)
@@ -695,39 +704,70 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) 
     nj2 = id % NJ2;
   }
   const int b = g / P.H, h = g - b * P.H;
-  const int j = 16 * (2 * nj2 + wave) + r16;
-  float* Sgl = P.S + (size_t)g * D * D;
   const int nch = P.nch;
   const size_t gc = (size_t)g * nch;
+  // global segment gs = 4 c + s sits in slot gs % 5
+  auto slot_of = [&](int gs) { return slots + (gs % Sg::NSLOT) * Sg::SLOT; };
 
-  ScanSrc src;
-  src.W = static_cast<const u32x4_t*>(P.Wf) + gc * Sg::FW;
-  src.Q = static_cast<const u32x4_t*>(P.Qf) + gc * Sg::FW;
-  src.K = static_cast<const u32x4_t*>(P.Kf) + gc * Sg::FK;
-  src.A = static_cast<const u32x4_t*>(P.Af) + gc * Sg::FA;
-  src.U = reinterpret_cast<const u32x4_t*>(P.Uf) + gc * (Sg::NJ * 4 * 64) + nj2 * Sg::FU;
-  src.D = reinterpret_cast<const u32x4_t*>(P.dec) + gc * Sg::FD;
+  if (wave >= 2) {
+    // ---- loading waves: segment 4 c + s + 4 (chunk c + 1, segment s) is issued into the
+    // slot of segment 4 c + s - 1 once the barrier before segment 4 c + s has passed ----
+    const int lt = tid - 128, lw = wave - 2;
+    ScanSrc src;
+    src.W = static_cast<const u32x4_t*>(P.Wf) + gc * Sg::FW;
+    src.Q = static_cast<const u32x4_t*>(P.Qf) + gc * Sg::FW;
+    src.K = static_cast<const u32x4_t*>(P.Kf) + gc * Sg::FK;
+    src.A = static_cast<const u32x4_t*>(P.Af) + gc * Sg::FA;
+    src.U = reinterpret_cast<const u32x4_t*>(P.Uf) + gc * (Sg::NJ * 4 * 64) + nj2 * Sg::FU;
+    src.D = reinterpret_cast<const u32x4_t*>(P.dec) + gc * Sg::FD;
+    scan_issue<D, 0>(src, 0, slot_of(0), lt, lane, lw);
+    scan_issue<D, 1>(src, 0, slot_of(1), lt, lane, lw);
+    scan_issue<D, 2>(src, 0, slot_of(2), lt, lane, lw);
+    scan_issue<D, 3>(src, 0, slot_of(3), lt, lane, lw);
+#pragma unroll 1
+    for (int c = 0; c < nch; ++c) {
+      const bool more = c + 1 < nch;
+      const int g0 = 4 * c;
+      // each wait leaves in flight only the loads of the segments issued after the one
+      // about to be read (in the last chunk: those of its own later segments)
+      wait_vm_lgkm0<N1 + N2 + N3>();
+      block_barrier();
+      if (more) scan_issue<D, 0>(src, c + 1, slot_of(g0 + 4), lt, lane, lw);
+      if (more) wait_vm_lgkm0<N2 + N3 + N0>();
+      else wait_vm_lgkm0<N2 + N3>();
+      block_barrier();
+      if (more) scan_issue<D, 1>(src, c + 1, slot_of(g0 + 5), lt, lane, lw);
+      if (more) wait_vm_lgkm0<N3 + N0 + N1>();
+      else wait_vm_lgkm0<N3>();
+      block_barrier();
+      if (more) scan_issue<D, 2>(src, c + 1, slot_of(g0 + 6), lt, lane, lw);
+      if (more) wait_vm_lgkm0<N0 + N1 + N2>();
+      else wait_vm_lgkm0<0>();
+      block_barrier();
+      if (more) scan_issue<D, 3>(src, c + 1, slot_of(g0 + 7), lt, lane, lw);
+    }
+    return;
+  }
 
+  // ---- computing waves ----
+  const int j = 16 * (2 * nj2 + wave) + r16;
+  float* Sgl = P.S + (size_t)g * D * D;
   f32x4_t S[MTI];
 #pragma unroll
   for (int mt = 0; mt < MTI; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) S[mt][r] = Sgl[(size_t)(16 * mt + 4 * q4 + r) * D + j];
 
-  // the first chunk's four segments
-  scan_issue<D, 0>(src, 0, slot0, tid, lane, wave);
-  scan_issue<D, 1>(src, 0, slot1, tid, lane, wave);
-  scan_issue<D, 2>(src, 0, slot2, tid, lane, wave);
-  scan_issue<D, 3>(src, 0, slot3, tid, lane, wave);
-  wait_vm_lgkm0<Sg::NLD[1] + Sg::NLD[2] + Sg::NLD[3]>();
-  block_barrier();
-
   const size_t orow = (size_t)P.H * D;
   f32x4_t Dm[4], Om[4];
   Frag sf[KS], df[2];
 #pragma unroll 1
   for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
+    const int g0 = 4 * c;
+    const u32x4_t* slot0 = slot_of(g0);
+    const u32x4_t* slot1 = slot_of(g0 + 1);
+    const u32x4_t* slot2 = slot_of(g0 + 2);
+    const u32x4_t* slot3 = slot_of(g0 + 3);
     // ---- segment 0: D = -W S (state columns as B operands, k = key channel permuted) ----
 #pragma unroll
     for (int p = 0; p < KS; ++p) {
@@ -738,20 +778,15 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) 
     }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Dm[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lds_done_barrier();
     row_tiles_times<KS>(slot0, sf, Dm, lane);
-    // segment 1 must have landed; segments 2, 3 may still be in flight
-    wait_vm_lgkm0<Sg::NLD[2] + Sg::NLD[3]>();
-    block_barrier();
-    if (more) scan_issue<D, 0>(src, c + 1, slot0, tid, lane, wave);
     // ---- segment 1: O = (q 2^G) S ----
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) Om[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    lds_done_barrier();
     row_tiles_times<KS>(slot1, sf, Om, lane);
-    if (more) wait_vm_lgkm0<Sg::NLD[3] + Sg::NLD[0]>();
-    else wait_vm_lgkm0<Sg::NLD[3]>();
-    block_barrier();
-    if (more) scan_issue<D, 1>(src, c + 1, slot1, tid, lane, wave);
     // ---- segment 2: D += U; O += A D; S <- diag(dec) S ----
+    lds_done_barrier();
     {
       const f32x4_t* sU = reinterpret_cast<const f32x4_t*>(slot2 + Sg::FA) + wave * 4 * 64;
       const f32x4_t* sD = reinterpret_cast<const f32x4_t*>(slot2 + Sg::FA + Sg::FU);
@@ -779,10 +814,6 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) 
 #pragma unroll
       for (int mt = 0; mt < MTI; ++mt) S[mt] = S[mt] * sD[4 * mt + q4];
     }
-    if (more) wait_vm_lgkm0<Sg::NLD[0] + Sg::NLD[1]>();
-    else wait_vm_lgkm0<0>();
-    block_barrier();
-    if (more) scan_issue<D, 2>(src, c + 1, slot2, tid, lane, wave);
     {
       const int t0 = c * CS, nt = min(CS, P.L - t0);
       float* og = P.o + ((size_t)b * P.L + t0) * orow + (size_t)h * D + j;
@@ -795,12 +826,8 @@ __global__ __launch_bounds__(128) void chunk_scan_kernel(const PrefillParams P) 
         }
     }
     // ---- segment 3: S += (k 2^(G_last - G))^T D ----
+    lds_done_barrier();
     key_tiles_times<MTI>(slot3, df, S, lane);
-    if (more) {
-      wait_vm_lgkm0<Sg::NLD[1] + Sg::NLD[2]>();
-      block_barrier();
-      scan_issue<D, 3>(src, c + 1, slot3, tid, lane, wave);
-    }
   }
 #pragma unroll
   for (int mt = 0; mt < MTI; ++mt)
@@ -939,9 +966,9 @@ hipError_t launch_chunk_prep(const PrefillParams& p, hipStream_t s) {
 hipError_t launch_chunk_scan(const PrefillParams& p, hipStream_t s) {
   const int blocks = p.B * p.H * (p.dk / 32);
   if (p.dk == 128)
-    chunk_scan_kernel<128><<<blocks, 128, 0, s>>>(p);
+    chunk_scan_kernel<128><<<blocks, 256, 0, s>>>(p);
   else
-    chunk_scan_kernel<64><<<blocks, 128, 0, s>>>(p);
+    chunk_scan_kernel<64><<<blocks, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
