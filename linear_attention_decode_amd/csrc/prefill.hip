@@ -88,15 +88,18 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------------------------------
-// Preparation: one block of 4 waves per (chunk, head, sequence); RF = rank of the forget
+// Preparation: one block of 8 waves per (chunk, head, sequence), two per SIMD (the phases
+// are chains of dependent steps, which a second wave on the SIMD overlaps); RF = rank of the forget
 // gate's low-rank projection.
 // ---------------------------------------------------------------------------------------
 template <int DK, int RF>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void chunk_prep_kernel(const PrefillParams P) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_prep_kernel(const PrefillParams P) {
   using Lds = PrepLds<DK>;
   constexpr int RS = Lds::RS, AS = Lds::AS, KS = DK / 32;
   constexpr int FS = RF + 4;           // row stride of the staged f_lr rows
-  constexpr int NTW = DK / 64;         // 16-column tiles per wave (gate GEMM, U)
+  constexpr int NW = 8, NT = 64 * NW;  // waves and threads of the block
+  constexpr int NCT = DK / 16;         // 16-channel tiles (gate GEMM; value tiles of U)
+  constexpr int NTW = (NCT + NW - 1) / NW;   // of them per wave: tile wave + NW n
   static_assert(CS * FS <= Lds::FL_FLOATS, "f_lr staging");
   __shared__ __attribute__((aligned(16))) float sm[Lds::TOTAL];
   float* sQ = sm + Lds::Q;
@@ -134,11 +137,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // ---- f_lr rows (staged in LDS for the gate GEMM) and this wave's F_b fragments, issued
   //      ahead of the conv loads ----
-  constexpr int NFL = CS * RF / 4 / 256;
+  constexpr int NFL = CS * RF / 4 / NT;
+  static_assert(CS * RF / 4 % NT == 0, "f_lr rows");
   f32x4_t fl[NFL];
 #pragma unroll
   for (int u = 0; u < NFL; ++u) {
-    const int e = tid + 256 * u;
+    const int e = tid + NT * u;
     const int t = min(e / (RF / 4), nt - 1), c4 = e % (RF / 4);
     fl[u] = *reinterpret_cast<const f32x4_t*>(P.P + (row0 + t) * P.proj_stride + P.C + 4 * c4);
   }
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int n = 0; n < NTW; ++n)
 #pragma unroll
     for (int ks = 0; ks < RF / 32; ++ks) {
-      const int i = 16 * (wave * NTW + n) + r16;
+      const int i = 16 * min(wave + NW * n, NCT - 1) + r16;   // past the head: a copy, unused
       // (the scalar gate has one F_b row per head: every channel of the head reads it)
       const size_t frow = P.gate == kGateScalar ? (size_t)h : (size_t)h * DK + i;
       fbf[n][ks] = *reinterpret_cast<const u32x4_t*>(P.Fb + frow * RF + 32 * ks + 8 * q4);
@@ -157,13 +161,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   {
     constexpr int NG = DK / 4;
     constexpr int ITEMS = 2 * 8 * NG;
-    constexpr int NIT = ITEMS / 256;
-    static_assert(ITEMS % 256 == 0, "conv items");
+    constexpr int NIT = (ITEMS + NT - 1) / NT;
+    static_assert(ITEMS % NT == 0 || ITEMS < NT, "conv items");
     // all input rows and weights first (one round trip), then the conv of each item
     f32x4_t xin[NIT][11], w[NIT][4];
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
-      const int it = tid + 256 * u;
+      const int it = min(tid + NT * u, ITEMS - 1);   // past the items: a copy of the last
       const int c4 = it % NG, rg = (it / NG) % 8, mat = it / (8 * NG);
       const int ch = mat * P.H * DK + h * DK + 4 * c4;
 #pragma unroll
@@ -173,7 +177,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 #pragma unroll
     for (int u = 0; u < NIT; ++u) {
-      const int it = tid + 256 * u;
+      const int it = tid + NT * u;
+      if (it >= ITEMS) continue;
       const int c4 = it % NG, rg = (it / NG) % 8, mat = it / (8 * NG);
       float* dst = (mat ? sK : sQ) + 4 * c4;
 #pragma unroll
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 #pragma unroll
   for (int u = 0; u < NFL; ++u) {
-    const int e = tid + 256 * u;
+    const int e = tid + NT * u;
     *reinterpret_cast<f32x4_t*>(sFL + (e / (RF / 4)) * FS + 4 * (e % (RF / 4))) = fl[u];
   }
   lds_barrier();
@@ -226,7 +231,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const float ea = safe ? P.a_log[h] : fexp(P.a_log[h]);
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
-      const int i = 16 * (wave * NTW + n) + r16;
+      if (wave + NW * n >= NCT) continue;
+      const int i = 16 * (wave + NW * n) + r16;
       const float bias = P.dt_bias[P.gate == kGateScalar ? h : h * DK + i];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -256,8 +262,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- normalised q and k rows; inclusive prefix sums of the log2-decays per channel and
   //      the decay range of each 16-row block ----
 #pragma unroll
-  for (int u = 0; u < 2 * CS * DK / 4 / 256; ++u) {
-    const int e = tid + 256 * u;
+  for (int u = 0; u < 2 * CS * DK / 4 / NT; ++u) {
+    const int e = tid + NT * u;
     const int c4 = e % (DK / 4), row = (e / (DK / 4)) % CS, mat = e / (CS * DK / 4);
     f32x4_t* v = reinterpret_cast<f32x4_t*>((mat ? sK : sQ) + row * RS + 4 * c4);
     *v = *v * sInv[mat * CS + row];
@@ -278,33 +284,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   lds_barrier();
 
-  // ---- q 2^G in operand order (row tile = wave) ----
+  // ---- q 2^G in operand order (row tile wave & 3, key steps of half wave >> 2) ----
   {
-    const int t = 16 * wave + r16;
+    const int t = 16 * (wave & 3) + r16;
 #pragma unroll
-    for (int p = 0; p < KS; ++p) {
+    for (int pp = 0; pp < KS / 2; ++pp) {
+      const int p = (wave >> 2) * (KS / 2) + pp;
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 32 * p + (e < 4 ? 4 * q4 + e : 16 + 4 * q4 + e - 4);
         x[e] = sQ[t * RS + i] * ex2(sG[t * RS + i]);
       }
-      store_frag(Qf, wave * KS + p, lane, split8(x));
+      store_frag(Qf, (wave & 3) * KS + p, lane, split8(x));
     }
   }
 
   // ---- A and L together as transposed products, for row block I and key blocks
   //      J in [j0, j1]:  X^T[s][t] = sum_i (k_s 2^(R_I - G_s))[i] (x_t 2^(G_t - R_I))[i],
-  //      x = q for A and k for L; the two share every decay factor.  Waves: (I 3, J 0-1),
-  //      (I 3, J 2-3), (I 2, J 0-2), (I 1, J 0-1) then (I 0, J 0).  The wave that ends a row
-  //      block at its diagonal also writes the zero blocks above it ----
-  {
-    const int npass = wave == 3 ? 2 : 1;
-#pragma unroll 1
-    for (int pass = 0; pass < npass; ++pass) {
-      const int I = wave < 2 ? 3 : (wave == 2 ? 2 : 1 - pass);
-      const int j0 = wave == 1 ? 2 : 0;
-      const int j1 = wave == 0 ? 1 : I;
+  //      x = q for A and k for L; the two share every decay factor.  Waves 0-5: (I 3,
+  //      J 0-1), (I 3, J 2-3), (I 2, J 0-1), (I 2, J 2), (I 1, J 0-1), (I 0, J 0).  The wave
+  //      that ends a row block at its diagonal also writes the zero blocks above it ----
+  if (wave < 6) {
+    {
+      const int I = wave < 2 ? 3 : (wave < 4 ? 2 : 5 - wave);
+      const int j0 = (wave == 1 || wave == 3) ? 2 : 0;
+      const int j1 = (wave == 0 || wave == 2 || wave == 4) ? 1 : I;
       const bool fac = sFlag[I] == 0.0f;                  // factored diagonal block
       const int t = 16 * I + r16;
       f32x4_t accA[3], accL[3];
@@ -376,8 +381,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll 1
   for (int I = 0; I < NB; ++I) {
     if (sFlag[I] == 0.0f) continue;
-    const int t = 16 * I + (tid >> 4), s = 16 * I + (tid & 15);
-    if (s <= t) {
+    const int t = 16 * I + ((tid >> 4) & 15), s = 16 * I + (tid & 15);
+    if (tid < 256 && s <= t) {
       float aa = 0.0f, al = 0.0f;
       for (int i = 0; i < DK; ++i) {
         const float ks = sK[s * RS + i] * ex2(sG[t * RS + i] - sG[s * RS + i]);
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   lds_barrier();
 
   // ---- conv inputs of U's right-hand side beta silu(conv(v)): for value tile
-  //      nj = wave + 4 n and token step kk, lane (r16, q4) needs channel 16 nj + r16 at
+  //      nj = wave + 8 n and token step kk, lane (r16, q4) needs channel 16 nj + r16 at
   //      tokens 32 kk + 8 q4 .. + 7, i.e. 11 input rows; issued here, used after the inverse ----
   float vin[NTW][2][11];
   f32x4_t vw[NTW];
@@ -399,7 +404,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int chv = 2 * P.H * DK + h * DK;
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
-      const int ch = chv + 16 * (wave + 4 * n) + r16;
+      const int ch = chv + 16 * min(wave + NW * n, NCT - 1) + r16;   // past the head: unused
       vw[n] = *reinterpret_cast<const f32x4_t*>(P.conv_w + (size_t)ch * 4);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk)
@@ -407,17 +412,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int k = 0; k < 11; ++k) vin[n][kk][k] = *conv_src(32 * kk + 8 * q4 - 3 + k, ch);
     }
   }
-  // ---- A in operand order (row tile = wave) ----
+  // ---- A in operand order (row tile wave & 3, key step wave >> 2) ----
   {
-    const int t = 16 * wave + r16;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    const int t = 16 * (wave & 3) + r16;
+    {
+      const int p = wave >> 2;
       float x[8];
       const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(sA + t * AS + 32 * p + 4 * q4);
       const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(sA + t * AS + 32 * p + 16 + 4 * q4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) { x[e] = a0[e]; x[4 + e] = a1[e]; }
-      store_frag(Af, wave * 2 + p, lane, split8(x));
+      store_frag(Af, (wave & 3) * 2 + p, lane, split8(x));
     }
   }
   // ---- diagonal blocks of T = (I + L)^-1 (forward substitution per column); zeros above ----
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int r = 0; r < 16; ++r) sT[(16 * I + r) * AS + 16 * I + j] = x[r];
   } else {
-    for (int e = tid - 64; e < 6 * 256; e += 192) {
+    for (int e = tid - 64; e < 6 * 256; e += NT - 64) {
       const int tile = e >> 8, r = (e >> 4) & 15, cc = e & 15;
       const int I = tile < 3 ? 0 : (tile < 5 ? 1 : 2);
       const int J = tile < 3 ? 1 + tile : (tile < 5 ? tile - 1 : 3);
@@ -445,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // ---- (k 2^(G_last - G))^T in operand order ----
   {
     const float* gl = sG + (CS - 1) * RS;
-    for (int f = wave; f < (DK / 16) * 2; f += 4) {
+    for (int f = wave; f < (DK / 16) * 2; f += NW) {
       const int mt = f >> 1, p = f & 1;
       const int i = 16 * mt + r16;
       float x[8];
@@ -493,18 +498,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       lds_load8(sT + (16 * n + r16) * AS + 32 * kk + 8 * q4, x);
       tf[n][kk] = split8(x);
     }
-  // ---- W^T = (beta 2^G k)^T T^T for key tiles 2w, 2w+1: -W in operand order ----
-  if (wave < KS) {
-    f32x4_t acc[2][NB];
+  // ---- W^T = (beta 2^G k)^T T^T: wave w takes key tiles 2 kp, 2 kp + 1 (kp = w % KS) for
+  //      the token tiles n with n % GS = w / KS (interleaved, so that with T lower
+  //      triangular every wave runs the same products): -W in operand order ----
+  {
+    constexpr int GS = NW / KS, NPW = NB / GS;
+    static_assert(NW % KS == 0 && NB % GS == 0, "W split");
+    const int kp = wave % KS, g0 = wave / KS;
+    f32x4_t acc[2][NPW];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int n = 0; n < NB; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < NPW; ++q) acc[m][q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const int i = 16 * (2 * wave + m) + r16;
+        const int i = 16 * (2 * kp + m) + r16;
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -514,20 +524,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const Frag fa = split8(x);
 #pragma unroll
         for (int n = 0; n < NB; ++n)
-          if (kk <= n / 2) acc[m][n] = mma3(fa, tf[n][kk], acc[m][n]);
+          if (n % GS == g0 && kk <= n / 2) acc[m][n / GS] = mma3(fa, tf[n][kk], acc[m][n / GS]);
       }
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
+      if (n % GS != g0) continue;
       float x[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { x[r] = -acc[0][n][r]; x[4 + r] = -acc[1][n][r]; }
-      store_frag(Wf, n * KS + wave, lane, split8(x));
+      for (int r = 0; r < 4; ++r) { x[r] = -acc[0][n / GS][r]; x[4 + r] = -acc[1][n / GS][r]; }
+      store_frag(Wf, n * KS + kp, lane, split8(x));
     }
   }
-  // ---- U = T (beta v) for value tiles w, w + 4, in accumulator order ----
+  // ---- U = T (beta v) for value tiles w + 8 n, in accumulator order ----
 #pragma unroll
   for (int n = 0; n < NTW; ++n) {
-    const int nj = wave + 4 * n;
+    const int nj = wave + NW * n;
+    if (nj >= NCT) continue;
     Frag fv[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
@@ -951,13 +963,13 @@ __global__ void prefill_window_kernel(const PrefillParams P) {
 hipError_t launch_chunk_prep(const PrefillParams& p, hipStream_t s) {
   dim3 grid(p.nch, p.H, p.B);
   if (p.dk == 128 && p.rank_f == 128)
-    chunk_prep_kernel<128, 128><<<grid, 256, 0, s>>>(p);
+    chunk_prep_kernel<128, 128><<<grid, 512, 0, s>>>(p);
   else if (p.dk == 128 && p.rank_f == 64)
-    chunk_prep_kernel<128, 64><<<grid, 256, 0, s>>>(p);
+    chunk_prep_kernel<128, 64><<<grid, 512, 0, s>>>(p);
   else if (p.dk == 64 && p.rank_f == 128)
-    chunk_prep_kernel<64, 128><<<grid, 256, 0, s>>>(p);
+    chunk_prep_kernel<64, 128><<<grid, 512, 0, s>>>(p);
   else if (p.dk == 64 && p.rank_f == 64)
-    chunk_prep_kernel<64, 64><<<grid, 256, 0, s>>>(p);
+    chunk_prep_kernel<64, 64><<<grid, 512, 0, s>>>(p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
