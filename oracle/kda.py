@@ -20,7 +20,7 @@ Sources, cited by page title and section:
          key dimension, beta = sigmoid(W_b x), the output gate sigmoid(g_b(g_a(x))) and
          RMSNorm eps = 1e-6.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * state S[h] is [dk][dv], row = key channel; the update order is
       S' = diag(alpha) S ; delta = beta (v - S'^T k) ; S = S' + k delta^T ; o = S^T q
     (the output is read after the update).  This is the recurrence whose chunking the
