@@ -853,7 +853,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const PrefillParams P) 
 // BF16), then per token the RMS over the head's d_v values, the norm weight and the gate.
 // Wave w owns value tiles w * NTW .. w * NTW + NTW - 1, all four token tiles.
 // ---------------------------------------------------------------------------------------
-template <int D>
+template <int D, int RG>
 __global__ __launch_bounds__(256) void chunk_gnorm_kernel(const PrefillParams P) {
   constexpr int NTW = D / 64;                       // value tiles per wave
   __shared__ float part[4][CS];
@@ -870,28 +870,41 @@ __global__ __launch_bounds__(256) void chunk_gnorm_kernel(const PrefillParams P)
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int n = 0; n < NTW; ++n) acc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // every g_lr row and G_b fragment of all RG / 32 k-steps is requested before the first
+  // product (one round trip a block; a k-step at a time took one each)
+  constexpr int NKS = RG / 32;
   const float* glr = P.P + P.C + P.rank_f;
-#pragma unroll 1
-  for (int k0 = 0; k0 < P.rank_g; k0 += 32) {
-    Frag fa[4];
+  f32x4_t ga[NKS][4][2];
+  u32x4_t gb[NKS][NTW];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int t = min(16 * mt + r16, nt - 1);
-      const float* src = glr + (row0 + t) * P.proj_stride + k0 + 8 * q4;
-      const f32x4_t a0 = *reinterpret_cast<const f32x4_t*>(src);
-      const f32x4_t a1 = *reinterpret_cast<const f32x4_t*>(src + 4);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { x[e] = a0[e]; x[4 + e] = a1[e]; }
-      fa[mt] = split8(x);
+      const float* src = glr + (row0 + t) * P.proj_stride + 32 * ks + 8 * q4;
+      ga[ks][mt][0] = *reinterpret_cast<const f32x4_t*>(src);
+      ga[ks][mt][1] = *reinterpret_cast<const f32x4_t*>(src + 4);
     }
 #pragma unroll
     for (int n = 0; n < NTW; ++n) {
       const int j = 16 * (wave * NTW + n) + r16;
-      const u32x4_t fb = *reinterpret_cast<const u32x4_t*>(P.Gb + ((size_t)h * D + j) * P.rank_g + k0 + 8 * q4);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][n] = mma2(fa[mt], fb, acc[mt][n]);
+      gb[ks][n] = *reinterpret_cast<const u32x4_t*>(P.Gb + ((size_t)h * D + j) * RG + 32 * ks + 8 * q4);
     }
+  }
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    Frag fa[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { x[e] = ga[ks][mt][0][e]; x[4 + e] = ga[ks][mt][1][e]; }
+      fa[mt] = split8(x);
+    }
+#pragma unroll
+    for (int n = 0; n < NTW; ++n)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][n] = mma2(fa[mt], gb[ks][n], acc[mt][n]);
   }
   // o in the accumulator layout; per-token sums of squares over the head
   float ov[4][NTW][4];
@@ -986,10 +999,15 @@ hipError_t launch_chunk_scan(const PrefillParams& p, hipStream_t s) {
 
 hipError_t launch_chunk_gnorm(const PrefillParams& p, hipStream_t s) {
   dim3 grid(p.nch, p.H, p.B);
-  if (p.dk == 128)
-    chunk_gnorm_kernel<128><<<grid, 256, 0, s>>>(p);
+  if (p.rank_g != 64 && p.rank_g != 128) return hipErrorInvalidValue;
+  if (p.dk == 128 && p.rank_g == 128)
+    chunk_gnorm_kernel<128, 128><<<grid, 256, 0, s>>>(p);
+  else if (p.dk == 128)
+    chunk_gnorm_kernel<128, 64><<<grid, 256, 0, s>>>(p);
+  else if (p.rank_g == 128)
+    chunk_gnorm_kernel<64, 128><<<grid, 256, 0, s>>>(p);
   else
-    chunk_gnorm_kernel<64><<<grid, 256, 0, s>>>(p);
+    chunk_gnorm_kernel<64, 64><<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
