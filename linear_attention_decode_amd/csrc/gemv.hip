@@ -209,9 +209,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams P) 
       if (tid < nc * H) {
         const int n = tid / H, h = tid - n * H;
         const float* sp = P.ss + ((size_t)(c0 + n) * H + h) * P.ncb;
-        float a = 0.0f;
-        for (int j = 0; j < P.ncb; ++j) a += sp[j];
-        scal[tid] = 1.0f / sqrtf(a / (float)P.dv + P.eps);
+        scal[tid] = 1.0f / sqrtf(sum_partials(sp, P.ncb) / (float)P.dv + P.eps);
       }
       __syncthreads();
 #pragma unroll

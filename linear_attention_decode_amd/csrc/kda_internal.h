@@ -138,6 +138,21 @@ int gemv_cols_per_pass(int N);
 // Per-head kernel: conv (verify/commit), L2 norms, gates, delta rule, read-out.
 // ---------------------------------------------------------------------------------------
 constexpr int kHeadCols = 16;      // value columns per wave (one partial sum of o^2 each)
+constexpr int kMaxNcb = 128 / kHeadCols;   // partial sums a head has (d_v is 64 or 128)
+
+// The sum of a head's ncb (1 .. kMaxNcb) partial sums of o^2, added in order j = 0 .. ncb - 1.
+// Every load is issued at once (indices clamped into the head, the extra terms added as +0,
+// which leaves the sum's bits unchanged): a loop over the runtime count waited for each
+// load in turn.
+__device__ __forceinline__ float sum_partials(const float* sp, int ncb) {
+  float x[kMaxNcb];
+#pragma unroll
+  for (int j = 0; j < kMaxNcb; ++j) x[j] = sp[min(j, ncb - 1)];
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxNcb; ++j) a += j < ncb ? x[j] : 0.0f;
+  return a;
+}
 
 struct HeadParams {
   int H = 0, dk = 0, dv = 0, C = 0, rank_f = 0, rank_g = 0;

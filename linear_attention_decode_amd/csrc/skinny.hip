@@ -110,9 +110,7 @@ __global__ __launch_bounds__(kSkThreads) void skinny_prep_kernel(const GemvParam
   if (PRO == kProGatedNorm && live) {
     if (tid < P.H) {
       const float* sp = P.ss + ((size_t)n * P.H + tid) * P.ncb;
-      float a = 0.0f;
-      for (int j = 0; j < P.ncb; ++j) a += sp[j];
-      scal[tid] = 1.0f / sqrtf(a / (float)P.dv + P.eps);
+      scal[tid] = 1.0f / sqrtf(sum_partials(sp, P.ncb) / (float)P.dv + P.eps);
     }
     __syncthreads();
   }
