@@ -645,7 +645,8 @@ LogRec* add_log(kda_model* m, const kda_state* st, const void* log, size_t log_b
   return &m->logs.back();
 }
 
-// One-launch decode: eligible for batch 1, Q8_0 stacks with d_k = d_v = 128, H*d_v = D in
+// One-launch decode: eligible for batch 1, Q8_0 (or MXFP4, held for it as the exactly equal
+// Q8_0) stacks with d_k = d_v = 128, H*d_v = D in
 // {1024, 2048}, low-rank gates of rank 32, 64 or 128, and enough co-resident blocks for the
 // static work split (two blocks per head, D/16 output-projection blocks after them, at most
 // 32 projection rows per remaining block).
@@ -673,7 +674,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const int nb = persistent_max_blocks();
   const int ob0 = 2 * d.n_heads, nob = d.d_model / 32;
   const int rank = d.rank_f;
-  bool ok = nb > 0 && nb <= kMaxPersistBlocks && d.wtype == KDA_Q8_0 && d.prenorm_residual &&
+  const bool mx4 = d.wtype == KDA_MXFP4;
+  bool ok = nb > 0 && nb <= kMaxPersistBlocks && (d.wtype == KDA_Q8_0 || mx4) && d.prenorm_residual &&
             d.gate == KDA_GATE_KDA &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
@@ -693,6 +695,22 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const size_t per_layer = pw + ow + 2 * (pd + od) + (size_t)(KF + KG) * (rank + 2 * nbr);
   hipError_t e = hipMalloc(&m->mma_w, per_layer * d.n_layers);
   if (e != hipSuccess) return e;
+  // MXFP4: a layer's matrices are first expanded to the Q8_0 layout holding the same values
+  // (twice each E2M1 value as the int8 code, half the E8M0 scale as the fp16 one), in a
+  // scratch area reused layer by layer; the per-layer kernels keep reading the caller's
+  // MXFP4 buffers (the 4-bit bytes), only the one-launch kernel reads the int8 copy
+  const int64_t xr[9] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads, D, KF, KG};
+  const int64_t xc[9] = {D, D, D, D, D, D, m->V, rank, rank};
+  size_t xoff[10] = {};
+  uint8_t* xq = nullptr;
+  int* xbad = nullptr;
+  if (mx4) {
+    for (int i = 0; i < 9; ++i)
+      xoff[i + 1] = align_up(xoff[i] + q8_scale_offset(xr[i], xc[i]) + (size_t)xr[i] * (xc[i] / 32) * 2, 256);
+    e = hipMalloc(&xq, xoff[9]);
+    if (e == hipSuccess) e = hipMalloc(&xbad, sizeof(int));
+    if (e == hipSuccess) e = hipMemset(xbad, 0, sizeof(int));
+  }
   std::vector<PersistLayer> host(d.n_layers);
   for (int l = 0; l < d.n_layers && e == hipSuccess; ++l) {
     const LayerDev& L = m->layers[l];
@@ -710,12 +728,22 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     P.gbw = gbase + (size_t)KF * rank;
     P.fbd = reinterpret_cast<const uint16_t*>(gbase + (size_t)(KF + KG) * rank);
     P.gbd = P.fbd + (size_t)KF * nbr;
+    // the Q8_0 sources: the caller's matrices, or their expansion (W_q, W_k, W_v, F_a, G_a,
+    // W_beta, W_o, F_b, G_b)
+    PackedMat q8[9] = {L.wq, L.wk, L.wv, L.fa, L.ga, L.wbeta, L.wo, L.fb, L.gb};
+    if (mx4) {
+      for (int i = 0; i < 9 && e == hipSuccess; ++i) {
+        e = launch_mx4_to_q8(q8[i].w, xr[i], xc[i], xq + xoff[i], xbad, nullptr);
+        q8[i] = packed_view(xq + xoff[i], kQ8, xr[i], xc[i]);
+      }
+      if (e != hipSuccess) break;
+    }
     const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
     MmaSource src{};
     int first = 0;
     for (int i = 0; i < 6; ++i) {
-      src.w[i] = P.seg[i].w;
-      src.d[i] = P.seg[i].d;
+      src.w[i] = q8[i].w;
+      src.d[i] = q8[i].d;
       src.first[i] = first;
       first += rows[i];
     }
@@ -723,17 +751,29 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     e = launch_mma_order(src, m->proj_rows, D, const_cast<int8_t*>(P.pw), const_cast<uint16_t*>(P.pd), nullptr);
     if (e != hipSuccess) break;
     MmaSource so{};
-    so.w[0] = L.wo.w;
-    so.d[0] = L.wo.d;
+    so.w[0] = q8[6].w;
+    so.d[0] = q8[6].d;
     so.nseg = 1;
     e = launch_mma_order(so, D, D, const_cast<int8_t*>(P.ow), const_cast<uint16_t*>(P.od), nullptr);
     if (e != hipSuccess) break;
-    e = launch_gate_order(L.fb.w, L.fb.d, KF, rank, const_cast<int8_t*>(P.fbw), const_cast<uint16_t*>(P.fbd), nullptr);
+    e = launch_gate_order(q8[7].w, q8[7].d, KF, rank, const_cast<int8_t*>(P.fbw), const_cast<uint16_t*>(P.fbd), nullptr);
     if (e != hipSuccess) break;
-    e = launch_gate_order(L.gb.w, L.gb.d, KG, rank, const_cast<int8_t*>(P.gbw), const_cast<uint16_t*>(P.gbd), nullptr);
+    e = launch_gate_order(q8[8].w, q8[8].d, KG, rank, const_cast<int8_t*>(P.gbw), const_cast<uint16_t*>(P.gbd), nullptr);
+    // (the scratch is rewritten by the next layer's expansion)
+    if (mx4 && e == hipSuccess) e = hipDeviceSynchronize();
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
+  int bad = 0;
+  if (mx4 && e == hipSuccess && xbad) e = hipMemcpy(&bad, xbad, sizeof(int), hipMemcpyDeviceToHost);
+  if (xq) (void)hipFree(xq);
+  if (xbad) (void)hipFree(xbad);
   if (e != hipSuccess) return e;
+  if (bad) {
+    // a scale with no fp16 power of two: the stack stays on the per-layer kernels
+    (void)hipFree(m->mma_w);
+    m->mma_w = nullptr;
+    return hipSuccess;
+  }
   (void)layers;
   e = hipMalloc(&m->d_layers, sizeof(PersistLayer) * d.n_layers);
   if (e != hipSuccess) return e;
@@ -774,8 +814,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   p.q_blocks = m->C / 48;
   m->pers_blocks = nb;
   m->pers_ok = true;
-  // the per-layer path reads the same copies (and never the caller's buffers again)
-  for (int l = 0; l < d.n_layers; ++l) {
+  // the per-layer path reads the same copies (and never the caller's buffers again); an
+  // MXFP4 stack keeps its per-layer kernels on the caller's 4-bit buffers
+  for (int l = 0; l < d.n_layers && !mx4; ++l) {
     m->layers[l].pw = host[l].pw;
     m->layers[l].pd = host[l].pd;
     m->layers[l].ow = host[l].ow;
@@ -1173,7 +1214,7 @@ int kda_model_query(const kda_model* m, int what) {
   if (!m) return -1;
   switch (what) {
     case KDA_Q_PERSISTENT: return m->pers_ok ? m->pers_blocks : 0;
-    case KDA_Q_OWNS_WEIGHTS: return m->mma_w ? 1 : 0;
+    case KDA_Q_OWNS_WEIGHTS: return m->mma_w && m->d.wtype == KDA_Q8_0 ? 1 : 0;
     default: return -1;
   }
 }

@@ -306,5 +306,9 @@ hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, voi
                        hipStream_t s);
 hipError_t launch_unpack_q8(const void* packed, int64_t rows, int64_t cols, uint16_t* d16,
                             int8_t* qs, hipStream_t s);
+// An MXFP4-packed [rows][cols] matrix as the Q8_0 layout holding the same values (q8 has
+// Q8_0's packed size); *bad is set if a nonzero block's scale has no fp16 power of two.
+hipError_t launch_mx4_to_q8(const void* mx4, int64_t rows, int64_t cols, void* q8, int* bad,
+                            hipStream_t s);
 
 }  // namespace kda

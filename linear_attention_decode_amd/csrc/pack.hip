@@ -107,7 +107,46 @@ __global__ void unpack_q8_0(const uint8_t* __restrict__ qs, const __half* __rest
   if (i < n / 32) d16[i] = __half_as_ushort(dplane[i]);
 }
 
+// MXFP4 -> Q8_0, exactly: twice an element's E2M1 value is an integer in -12..12 (the
+// int8 code) and half the block's E8M0 scale, 2^(e - 128), is an fp16 power of two for
+// e - 128 in [-24, 15]; a block whose codes are all +-0 takes scale 0 whatever its e.  A
+// nonzero block outside that range sets *bad (the matrix then cannot be held as Q8_0).
+// One thread per code byte (two elements), and per scale block.
+__global__ void mx4_to_q8(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ eplane,
+                          int64_t rows, int64_t cols, uint8_t* __restrict__ qs,
+                          __half* __restrict__ dplane, int* __restrict__ bad) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = rows * cols;
+  if (i < n / 2) {
+    const uint32_t b = codes[i];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = (b >> (4 * h)) & 15u, k = c & 7u;
+      // doubled magnitudes of grid indices 0..7: 0 1 2 3 4 6 8 12
+      const int mag = (int)(((k < 4 ? 0x03020100u : 0x0C080604u) >> (8 * (k & 3))) & 0xffu);
+      qs[2 * i + h] = (uint8_t)(128 + ((c & 8u) ? -mag : mag));
+    }
+  }
+  if (i < n / 32) {
+    const uint4 blk = *reinterpret_cast<const uint4*>(codes + 16 * i);   // the block's 32 codes
+    const bool zero = ((blk.x | blk.y | blk.z | blk.w) & 0x77777777u) == 0u;
+    const int e = (int)eplane[i] - 128;
+    if (!zero && (e < -24 || e > 15)) atomicOr(bad, 1);
+    dplane[i] = __float2half(zero ? 0.0f : __builtin_amdgcn_ldexpf(1.0f, e));
+  }
+}
+
 static inline int grid_for(int64_t n, int t) { return (int)((n + t - 1) / t); }
+
+hipError_t launch_mx4_to_q8(const void* mx4, int64_t rows, int64_t cols, void* q8, int* bad,
+                            hipStream_t s) {
+  const uint8_t* c = static_cast<const uint8_t*>(mx4);
+  uint8_t* q = static_cast<uint8_t*>(q8);
+  mx4_to_q8<<<grid_for(rows * cols / 2, 256), 256, 0, s>>>(
+      c, c + mx4_scale_offset(rows, cols), rows, cols, q,
+      reinterpret_cast<__half*>(q + q8_scale_offset(rows, cols)), bad);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(int wt, const float* src, int64_t rows, int64_t cols, void* dst,
                        hipStream_t s) {

@@ -66,21 +66,48 @@ def test_decode_mxfp4_small_stack(gate):
 
 def test_decode_mxfp4_stack_d2048():
     """The stack workload's shapes (D=2048, 16 heads, rank 128) with MXFP4 projections,
-    4 layers, B = 1 (vector dots), 4 and 9 (matrix cores: the codes converted to BF16 by
-    gfx950's scaled FP4 conversion), 6 steps, per-layer kernels."""
+    4 layers, 6 steps: B = 1 through the one-launch kernel (on the exact int8 expansion of
+    the codes) and through the per-layer kernels (vector dots), B = 4 and 9 per layer
+    (matrix cores: the codes converted to BF16 by gfx950's scaled FP4 conversion).  The
+    per-layer kernels read the caller's 4-bit buffers, so the model owns no copy."""
     for B in (1, 4, 9):
         w = synth.scaled(synth.WORKLOADS["stack"], wtype="mxfp4", n_layers=4, batch=B, steps=6, seed=162 + B)
         _say(f"decode mxfp4 D=2048 4 layers B={B} 6 steps")
         run = synth.draw_run(w)
         model = gpu_model(run)
-        assert model.persistent_blocks() == 0
-        y, S, Z, _ = gpu_decode(model, run, w.steps)
+        assert model.persistent_blocks() > 0 and not model.owns_weights()
         ry, rS, rZ, _ = ok.decode_run(oracle_layers(run), run.x, run.s0, True)
-        e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
-        assert e <= OUT_RTOL, e
-        assert np.abs(S - rS).max() <= STATE_ATOL
+        for persistent in ((True, False) if B == 1 else (False,)):
+            y, S, Z, _ = gpu_decode(model, run, w.steps, persistent=persistent)
+            e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
+            assert e <= OUT_RTOL, e
+            assert np.abs(S - rS).max() <= STATE_ATOL
+            _say(f"  B={B} {'one launch' if persistent and B == 1 else 'per layer'}: out {e:.2e}")
         model.close()
-        _say(f"  B={B}: out {e:.2e}")
+
+
+@pytest.mark.parametrize("case", ["zero_block", "scale_beyond_fp16"])
+def test_mxfp4_one_launch_eligibility(case):
+    """An MXFP4 stack runs the one-launch decode when every nonzero block's scale has an fp16
+    power of two: a block of zeros (E8M0 exponent -127) does not stop it; W_q scaled by
+    2^-30 (exponents far below fp16's) keeps the stack on the per-layer kernels.  Either way
+    B = 1 matches the oracle (2 layers, 4 steps)."""
+    w = synth.scaled(synth.WORKLOADS["stack"], wtype="mxfp4", n_layers=2, batch=1, steps=4, seed=168)
+    _say(f"mxfp4 one-launch eligibility: {case}")
+    run = synth.draw_run(w)
+    if case == "zero_block":
+        run.layers[1]["wo"][5, 64:96] = 0.0
+    else:
+        run.layers[0]["wq"] *= np.float32(2.0 ** -30)
+    model = gpu_model(run)
+    assert (model.persistent_blocks() > 0) == (case == "zero_block")
+    y, S, Z, _ = gpu_decode(model, run, w.steps)
+    ry, rS, rZ, _ = ok.decode_run(oracle_layers(run), run.x, run.s0, True)
+    e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
+    assert e <= OUT_RTOL, e
+    assert np.abs(S - rS).max() <= STATE_ATOL
+    model.close()
+    _say(f"  out {e:.2e}")
 
 
 def test_verify_and_scan_mxfp4():
