@@ -59,6 +59,12 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def synth_default_wtype(name):
+    """The weight format a decode workload is defined with."""
+    import synth
+    return synth.WORKLOADS[name].wtype
+
+
 def algorithmic_bytes(w) -> dict:
     """Bytes each kernel of one layer must move at B=1 (weights incl. Q8_0 scales,
     state, conv window, activations), and the per-token total of the stack."""
@@ -69,6 +75,8 @@ def algorithmic_bytes(w) -> dict:
     def q8(rows, cols):   # packed bytes of one matrix in the workload's weight format
         if w.wtype == "q8_0":
             return rows * cols + rows * (cols // 32) * 2
+        if w.wtype == "mxfp4":
+            return rows * cols // 2 + rows * (cols // 32)
         return rows * cols * (2 if w.wtype == "bf16" else 4)
 
     proj_w = q8(K, D) * 2 + q8(V, D) + q8(d.rank_f, D) + q8(d.rank_g, D) + q8(H, D)
@@ -225,7 +233,8 @@ def bench_stack(args, torch, synth, kda, w, run, model):
         log(f"[bench] kernel {k}: {n} launches, avg {avg_us:.2f} us, "
             f"{per[k]['rate']:.0f} GB/s algorithmic")
     dom, roof = roofline_entry(per, "hbm", HBM_PEAK_GBS, "GB/s")
-    roof["traffic"] = step_traffic() if dom == "step" else None
+    # (the counted traffic is that of the Q8_0 step)
+    roof["traffic"] = step_traffic() if dom == "step" and w.wtype == "q8_0" else None
     step_gbs = ab["token_weights_state"] / (ms_step * 1e-3) / 1e9
     # the measured sequential-read ceiling over a buffer the size of a token's bytes (the
     # byte pricing of antirez/ds4 PR #964 prices against such a ceiling); reported beside
@@ -253,12 +262,14 @@ def bench_stack(args, torch, synth, kda, w, run, model):
         config["weight_copies"] = args.copies
         config["workload"] += f"-{args.copies}copies"
     if w.name == "stack":
-        config["workload"] = "kda-stack-34L-q8_0-decode"
+        config["workload"] = f"kda-stack-34L-{w.wtype}-decode"
     if w.name == "tiny":
-        config["workload"] = "kda-tiny-layer-f32-decode"
+        config["workload"] = f"kda-tiny-layer-{w.wtype}-decode"
     metric = {"stack": "KDA decode tokens/s (34-layer stack, B=1)",
               "layer": "KDA decode tokens/s (one BF16 layer, B=1)",
               "tiny": "KDA decode tokens/s (tiny fp32 layer, B=1)"}[w.name]
+    if w.wtype != synth_default_wtype(w.name):
+        metric += f", {w.wtype} weights"
     return metric, tok_s, "tokens/s", ms_step, config, roof
 
 
@@ -480,6 +491,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--workload", default="stack",
                     choices=("stack", "layer", "tiny", "verify", "prefill"))
+    ap.add_argument("--wtype", default=None, choices=("f32", "bf16", "q8_0", "mxfp4"),
+                    help="decode workloads (stack, layer, tiny): the same shapes with another "
+                         "weight format")
     ap.add_argument("--copies", type=int, default=1,
                     help="decode workloads: weight copies used in turn (8 keeps the BF16 layer "
                          "out of the last-level cache)")
@@ -508,6 +522,11 @@ def main():
     import linear_attention_decode_amd as kda
 
     w = synth.WORKLOADS[args.workload]
+    if args.wtype:
+        if args.workload not in ("stack", "layer", "tiny"):
+            print("--wtype applies to the decode workloads (stack, layer, tiny)", file=sys.stderr)
+            sys.exit(2)
+        w = synth.scaled(w, wtype=args.wtype)
     if args.workload != "prefill":
         w = synth.scaled(w, steps=max(args.steps + args.warmup, 1))
     t0 = time.time()
