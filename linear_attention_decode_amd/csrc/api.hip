@@ -110,6 +110,7 @@ struct kda_model {
   int wall_khz = 0;                 // wall-clock ticks per millisecond
   PersistLayer* d_layers = nullptr;
   int8_t* mma_w = nullptr;          // projection rows and W_o of every layer, matrix-core order
+  float* dtb_rep = nullptr;         // scalar-gate stack: dt_bias[h] repeated over the head's d_k
   uint64_t* xchg = nullptr;         // exchange words (xbuf | pbuf | gbuf | obuf)
   int* err = nullptr;
   int* err_host = nullptr;          // host-mapped: set by a step whose wait between blocks ran out
@@ -646,7 +647,8 @@ LogRec* add_log(kda_model* m, const kda_state* st, const void* log, size_t log_b
 }
 
 // One-launch decode: eligible for batch 1, Q8_0 (or MXFP4, held for it as the exactly equal
-// Q8_0) stacks with d_k = d_v = 128, H*d_v = D in
+// Q8_0) stacks with the KDA gate (or the scalar one, whose per-head F_b row and dt_bias it
+// takes repeated over the head's channels) and d_k = d_v = 128, H*d_v = D in
 // {1024, 2048}, low-rank gates of rank 32, 64 or 128, and enough co-resident blocks for the
 // static work split (two blocks per head, D/16 output-projection blocks after them, at most
 // 32 projection rows per remaining block).
@@ -674,9 +676,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const int nb = persistent_max_blocks();
   const int ob0 = 2 * d.n_heads, nob = d.d_model / 32;
   const int rank = d.rank_f;
-  const bool mx4 = d.wtype == KDA_MXFP4;
+  const bool mx4 = d.wtype == KDA_MXFP4, scal = d.gate == KDA_GATE_SCALAR;
   bool ok = nb > 0 && nb <= kMaxPersistBlocks && (d.wtype == KDA_Q8_0 || mx4) && d.prenorm_residual &&
-            d.gate == KDA_GATE_KDA &&
+            (d.gate == KDA_GATE_KDA || scal) &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
             (rank == 32 || rank == 64 || rank == 128);
@@ -697,19 +699,24 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   if (e != hipSuccess) return e;
   // MXFP4: a layer's matrices are first expanded to the Q8_0 layout holding the same values
   // (twice each E2M1 value as the int8 code, half the E8M0 scale as the fp16 one), in a
-  // scratch area reused layer by layer; the per-layer kernels keep reading the caller's
-  // MXFP4 buffers (the 4-bit bytes), only the one-launch kernel reads the int8 copy
-  const int64_t xr[9] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads, D, KF, KG};
-  const int64_t xc[9] = {D, D, D, D, D, D, m->V, rank, rank};
-  size_t xoff[10] = {};
+  // scratch area reused layer by layer; the scalar gate's F_b (one row a head) is repeated
+  // there over the head's d_k rows.  The per-layer kernels of such a stack keep reading the
+  // caller's buffers; only the one-launch kernel reads the copy.
+  const int FR = scal ? d.n_heads : KF;          // F_b rows as the caller packed them
+  const int64_t xr[10] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads, D, FR, KG, KF};
+  const int64_t xc[10] = {D, D, D, D, D, D, m->V, rank, rank, rank};
+  size_t xoff[11] = {};
   uint8_t* xq = nullptr;
   int* xbad = nullptr;
-  if (mx4) {
-    for (int i = 0; i < 9; ++i)
-      xoff[i + 1] = align_up(xoff[i] + q8_scale_offset(xr[i], xc[i]) + (size_t)xr[i] * (xc[i] / 32) * 2, 256);
-    e = hipMalloc(&xq, xoff[9]);
+  if (mx4 || scal) {
+    for (int i = 0; i < 10; ++i) {
+      const bool used = i < 9 ? mx4 : scal;
+      xoff[i + 1] = xoff[i] + (used ? align_up(q8_scale_offset(xr[i], xc[i]) + (size_t)xr[i] * (xc[i] / 32) * 2, 256) : 0);
+    }
+    e = hipMalloc(&xq, xoff[10]);
     if (e == hipSuccess) e = hipMalloc(&xbad, sizeof(int));
     if (e == hipSuccess) e = hipMemset(xbad, 0, sizeof(int));
+    if (e == hipSuccess && scal) e = hipMalloc(&m->dtb_rep, sizeof(float) * KF * d.n_layers);
   }
   std::vector<PersistLayer> host(d.n_layers);
   for (int l = 0; l < d.n_layers && e == hipSuccess; ++l) {
@@ -738,6 +745,14 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
       }
       if (e != hipSuccess) break;
     }
+    if (scal) {
+      e = launch_q8_repeat_rows(q8[7].w, d.n_heads, rank, d.d_k, xq + xoff[9], nullptr);
+      q8[7] = packed_view(xq + xoff[9], kQ8, KF, rank);
+      if (e == hipSuccess)
+        e = launch_f32_repeat(L.dt_bias, d.n_heads, d.d_k, m->dtb_rep + (size_t)l * KF, nullptr);
+      P.dt_bias = m->dtb_rep + (size_t)l * KF;
+      if (e != hipSuccess) break;
+    }
     const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
     MmaSource src{};
     int first = 0;
@@ -760,7 +775,7 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     if (e != hipSuccess) break;
     e = launch_gate_order(q8[8].w, q8[8].d, KG, rank, const_cast<int8_t*>(P.gbw), const_cast<uint16_t*>(P.gbd), nullptr);
     // (the scratch is rewritten by the next layer's expansion)
-    if (mx4 && e == hipSuccess) e = hipDeviceSynchronize();
+    if ((mx4 || scal) && e == hipSuccess) e = hipDeviceSynchronize();
   }
   if (e == hipSuccess) e = hipDeviceSynchronize();
   int bad = 0;
@@ -772,6 +787,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
     // a scale with no fp16 power of two: the stack stays on the per-layer kernels
     (void)hipFree(m->mma_w);
     m->mma_w = nullptr;
+    if (m->dtb_rep) (void)hipFree(m->dtb_rep);
+    m->dtb_rep = nullptr;
     return hipSuccess;
   }
   (void)layers;
@@ -815,8 +832,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   m->pers_blocks = nb;
   m->pers_ok = true;
   // the per-layer path reads the same copies (and never the caller's buffers again); an
-  // MXFP4 stack keeps its per-layer kernels on the caller's 4-bit buffers
-  for (int l = 0; l < d.n_layers && !mx4; ++l) {
+  // MXFP4 or scalar-gate stack keeps its per-layer kernels on the caller's buffers
+  for (int l = 0; l < d.n_layers && !mx4 && !scal; ++l) {
     m->layers[l].pw = host[l].pw;
     m->layers[l].pd = host[l].pd;
     m->layers[l].ow = host[l].ow;
@@ -1160,6 +1177,7 @@ void kda_model_destroy(kda_model* m) {
   drop_graph(m);
   if (m->d_layers) (void)hipFree(m->d_layers);
   if (m->mma_w) (void)hipFree(m->mma_w);
+  if (m->dtb_rep) (void)hipFree(m->dtb_rep);
   if (m->xchg) (void)hipFree(m->xchg);
   if (m->err) (void)hipFree(m->err);
   if (m->err_host) (void)hipHostFree(m->err_host);
@@ -1214,7 +1232,8 @@ int kda_model_query(const kda_model* m, int what) {
   if (!m) return -1;
   switch (what) {
     case KDA_Q_PERSISTENT: return m->pers_ok ? m->pers_blocks : 0;
-    case KDA_Q_OWNS_WEIGHTS: return m->mma_w && m->d.wtype == KDA_Q8_0 ? 1 : 0;
+    case KDA_Q_OWNS_WEIGHTS:
+      return m->mma_w && m->d.wtype == KDA_Q8_0 && m->d.gate == KDA_GATE_KDA ? 1 : 0;
     default: return -1;
   }
 }

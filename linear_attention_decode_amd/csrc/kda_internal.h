@@ -310,5 +310,10 @@ hipError_t launch_unpack_q8(const void* packed, int64_t rows, int64_t cols, uint
 // Q8_0's packed size); *bad is set if a nonzero block's scale has no fp16 power of two.
 hipError_t launch_mx4_to_q8(const void* mx4, int64_t rows, int64_t cols, void* q8, int* bad,
                             hipStream_t s);
+// A Q8_0-packed [rows][cols] matrix as [rows * rep][cols], each row repeated rep times
+// (out has Q8_0's packed size for rows * rep rows); and n floats each repeated rep times.
+hipError_t launch_q8_repeat_rows(const void* q8, int64_t rows, int64_t cols, int rep, void* out,
+                                 hipStream_t s);
+hipError_t launch_f32_repeat(const float* in, int64_t n, int rep, float* out, hipStream_t s);
 
 }  // namespace kda

@@ -138,6 +138,45 @@ __global__ void mx4_to_q8(const uint8_t* __restrict__ codes, const uint8_t* __re
 
 static inline int grid_for(int64_t n, int t) { return (int)((n + t - 1) / t); }
 
+// Q8_0 [rows][cols] -> Q8_0 [rows * rep][cols] with every row repeated rep times in place
+// (output row r is input row r / rep): bytes and scales copied, one thread per byte.
+__global__ void q8_repeat_rows(const uint8_t* __restrict__ qs, const __half* __restrict__ dplane,
+                               int64_t rows, int64_t cols, int rep, uint8_t* __restrict__ qo,
+                               __half* __restrict__ dout) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t n = rows * rep * cols;
+  if (i < n) {
+    const int64_t r = i / cols, c = i - r * cols;
+    qo[i] = qs[(r / rep) * cols + c];
+  }
+  if (i < n / 32) {
+    const int64_t r = i / (cols / 32), b = i - r * (cols / 32);
+    dout[i] = dplane[(r / rep) * (cols / 32) + b];
+  }
+}
+
+// out[l][h * rep + i] = in[l][h] for l < layers, h < heads, i < rep
+__global__ void f32_repeat(const float* __restrict__ in, int64_t n_in, int rep,
+                           float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_in * rep) out[i] = in[i / rep];
+}
+
+hipError_t launch_q8_repeat_rows(const void* q8, int64_t rows, int64_t cols, int rep, void* out,
+                                 hipStream_t s) {
+  const uint8_t* q = static_cast<const uint8_t*>(q8);
+  uint8_t* o = static_cast<uint8_t*>(out);
+  q8_repeat_rows<<<grid_for(rows * rep * cols, 256), 256, 0, s>>>(
+      q, reinterpret_cast<const __half*>(q + q8_scale_offset(rows, cols)), rows, cols, rep, o,
+      reinterpret_cast<__half*>(o + q8_scale_offset(rows * rep, cols)));
+  return hipGetLastError();
+}
+
+hipError_t launch_f32_repeat(const float* in, int64_t n, int rep, float* out, hipStream_t s) {
+  f32_repeat<<<grid_for(n * rep, 256), 256, 0, s>>>(in, n, rep, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx4_to_q8(const void* mx4, int64_t rows, int64_t cols, void* q8, int* bad,
                             hipStream_t s) {
   const uint8_t* c = static_cast<const uint8_t*>(mx4);
