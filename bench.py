@@ -40,8 +40,8 @@ BF16_PEAK_TFLOPS = 2500.0      # dense MFMA, bf16
 # HBM bytes per launch of the one-launch step from rocprofv3 FETCH_SIZE + WRITE_SIZE, each
 # scaled by the same counter on a plain 256 MiB copy (FETCH x2.0, WRITE x1.0), valid while
 # the kernel's sources hash to "sha256" (see profiles/ for the runs).
-STEP_TRAFFIC = {"bytes": 744144064,
-                "sha256": "09311fc4c9e50850ed750311e342ad25de194d09bbc636b6f9ad06cf7bf6eb02",
+STEP_TRAFFIC = {"bytes": 744120053,
+                "sha256": "f9fd605861c8b505db628d44373596d762f3aa44982023aa9e6d52a873e91c91",
                 "sources": ("persistent.hip", "kda_device.h", "persist.h")}
 
 

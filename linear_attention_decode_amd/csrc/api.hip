@@ -647,8 +647,8 @@ LogRec* add_log(kda_model* m, const kda_state* st, const void* log, size_t log_b
 }
 
 // One-launch decode: eligible for batch 1, Q8_0 (or MXFP4, held for it as the exactly equal
-// Q8_0) stacks with the KDA gate (or the scalar one, whose per-head F_b row and dt_bias it
-// takes repeated over the head's channels) and d_k = d_v = 128, H*d_v = D in
+// Q8_0) stacks with the KDA gate, the lower-bounded one or the scalar one (whose per-head
+// F_b row and dt_bias it takes repeated over the head's channels), d_k = d_v = 128, H*d_v = D in
 // {1024, 2048}, low-rank gates of rank 32, 64 or 128, and enough co-resident blocks for the
 // static work split (two blocks per head, D/16 output-projection blocks after them, at most
 // 32 projection rows per remaining block).
@@ -677,8 +677,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   const int ob0 = 2 * d.n_heads, nob = d.d_model / 32;
   const int rank = d.rank_f;
   const bool mx4 = d.wtype == KDA_MXFP4, scal = d.gate == KDA_GATE_SCALAR;
+  const bool safe = d.gate == KDA_GATE_SAFE;
   bool ok = nb > 0 && nb <= kMaxPersistBlocks && (d.wtype == KDA_Q8_0 || mx4) && d.prenorm_residual &&
-            (d.gate == KDA_GATE_KDA || scal) &&
+            (d.gate == KDA_GATE_KDA || scal || safe) &&
             d.d_k == 128 && d.d_v == 128 && m->V == d.d_model &&
             (d.d_model == 1024 || d.d_model == 2048) && d.rank_f == d.rank_g &&
             (rank == 32 || rank == 64 || rank == 128);
@@ -813,6 +814,8 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   PersistParams& p = m->pp;
   p.n_layers = d.n_layers; p.D = d.d_model; p.H = d.n_heads; p.dk = d.d_k; p.dv = d.d_v;
   p.C = m->C; p.rank = d.rank_f; p.proj_rows = m->proj_rows;
+  p.gate_safe = safe ? 1 : 0;
+  p.gate_lb = d.gate_lb;
   const int rows[6] = {m->Kq, m->Kq, m->V, d.rank_f, d.rank_g, d.n_heads};
   int first = 0;
   for (int i = 0; i < 6; ++i) { p.seg_first[i] = first; first += rows[i]; }
@@ -832,8 +835,9 @@ hipError_t persist_setup(kda_model* m, const kda_layer* layers) {
   m->pers_blocks = nb;
   m->pers_ok = true;
   // the per-layer path reads the same copies (and never the caller's buffers again); an
-  // MXFP4 or scalar-gate stack keeps its per-layer kernels on the caller's buffers
-  for (int l = 0; l < d.n_layers && !mx4 && !scal; ++l) {
+  // MXFP4, scalar- or lower-bounded-gate stack keeps its per-layer kernels on the caller's
+  // buffers (their matrix-core gates compute KDA's form)
+  for (int l = 0; l < d.n_layers && !mx4 && !scal && !safe; ++l) {
     m->layers[l].pw = host[l].pw;
     m->layers[l].pd = host[l].pd;
     m->layers[l].ow = host[l].ow;

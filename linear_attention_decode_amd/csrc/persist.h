@@ -40,6 +40,8 @@ struct PersistParams {
   int n_layers = 0, D = 0, H = 0, dk = 0, dv = 0, C = 0, rank = 0, proj_rows = 0;
   int seg_first[6] = {};
   float eps = 0.f, l2_eps = 0.f, q_scale = 0.f;
+  int gate_safe = 0;                     // 1: the lower-bounded gate (else KDA's)
+  float gate_lb = 0.f;                   // its bound (log of alpha lies in (gate_lb, 0))
   const PersistLayer* layers = nullptr;  // device array [n_layers]
   float* S = nullptr;                    // [n_layers][H][dk][dv]
   float* win = nullptr;                  // [n_layers][3][C]

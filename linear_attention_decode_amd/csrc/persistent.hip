@@ -738,7 +738,8 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
   const float* s_k = sm.s_in + dk;
   const float* s_v = sm.s_in + 2 * dk;
   const float beta = sigmoid_hw(sm.s_in[2 * dk + kHCols + 2 * rank]);
-  // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)), gate = sigmoid(G_b g_lr), on the
+  // alpha = exp(-exp(A_log) softplus(F_b f_lr + dt_bias)) (KDA; the lower-bounded gate:
+  // exp(lb sigmoid(-(F_b f_lr + dt_bias) A_log)), A_log as given), gate = sigmoid(G_b g_lr), on the
   // int8 matrix cores as the projections: A row 4 i + p holds plane p of block i on lane
   // group i, B the tile's Q8_0 bytes, so accumulator lane (n, g) holds block g's three plane
   // dots for row n.  Each block's two scales are applied there and the four lane groups
@@ -772,8 +773,9 @@ __device__ __forceinline__ bool phase_h(const PersistParams& P, Smem& sm, int l,
     y1 += __shfl_xor(y1, 32);
     y2 += __shfl_xor(y2, 32);
     const float pre = g == 0 ? y0 : g == 1 ? y1 : y2;
-    const float al = exp_hw(-exp_hw(hr.ea) * softplus_hw(pre + hr.dtb));   // (both forms in
-    const float gt = sigmoid_hw(pre);                                      // every lane: no branch)
+    const float al = P.gate_safe ? exp_hw(P.gate_lb * sigmoid_hw(-(pre + hr.dtb) * hr.ea))
+                                 : exp_hw(-exp_hw(hr.ea) * softplus_hw(pre + hr.dtb));
+    const float gt = sigmoid_hw(pre);   // (alpha and gate in every lane: no lane branch)
     if (g < 2) sm.s_al[16 * (wave + 4 * g) + m] = al;
     else if (g == 2) sm.s_gt[16 * wave + m] = gt;
   }

@@ -59,9 +59,9 @@ def test_gate_forms_decode(gate, wtype):
 def test_gate_forms_full_size_stack(gate, B):
     """D=2048, 16 heads, Q8_0, 3 layers, 6 steps.  The per-layer kernels read the caller's
     row-major weights: B = 1 has the head kernel compute the gates, B = 12 runs the gates
-    kernel and takes the matrix-core projections with two 16-row tiles a block.  The scalar
-    gate's B = 1 also runs the one-launch kernel (its per-head F_b row and dt_bias repeated
-    over the head's channels); the safe gate has no one-launch form."""
+    kernel and takes the matrix-core projections with two 16-row tiles a block.  B = 1 also
+    runs the one-launch kernel: the safe gate's formula is one of its two, the scalar gate
+    takes its per-head F_b row and dt_bias repeated over the head's channels."""
     d = synth.LayerDims(d_model=2048, n_heads=16, d_k=128, d_v=128, rank_f=128, rank_g=128, gate=gate)
     w = synth.scaled(synth.WORKLOADS["stack"], dims=d, n_layers=3, steps=6, batch=B, seed=103)
     _say(f"decode gate={gate} q8_0 D=2048 3 layers 6 steps B={B}")
@@ -70,9 +70,9 @@ def test_gate_forms_full_size_stack(gate, B):
         _safe_params(run, 104)
     layers = oracle_layers(run)
     model = gpu_model(run)
-    assert (model.persistent_blocks() > 0) == (gate == "scalar") and not model.owns_weights()
+    assert model.persistent_blocks() > 0 and not model.owns_weights()
     ry, rS, rZ, _ = ok.decode_run(layers, run.x, run.s0, True)
-    for persistent in ((True, False) if gate == "scalar" and B == 1 else (False,)):
+    for persistent in ((True, False) if B == 1 else (False,)):
         y, S, Z, _ = gpu_decode(model, run, w.steps, persistent=persistent)
         e = max(range_rel(y[t], ry[t]) for t in range(w.steps))
         assert e <= OUT_RTOL, e
