@@ -179,9 +179,9 @@ typedef struct {
  * during this call, and every kernel of every call on it reads only that copy: the
  * caller's packed buffers (wq .. gb) may be freed or reused once this call has returned,
  * so the weights sit in device memory once.  Any other model reads the caller's packed
- * buffers in every call (an eligible MXFP4 or scalar-gate model too, in its per-layer
- * kernels; its one-launch decode reads a copy of its own), and they must stay valid and
- * unchanged until kda_model_destroy.  conv_w, a_log, dt_bias and o_norm_w are always read from the
+ * buffers in every call (an eligible MXFP4, safe- or scalar-gate model too, in its
+ * per-layer kernels; its one-launch decode reads a copy of its own), and they must stay
+ * valid and unchanged until kda_model_destroy.  conv_w, a_log, dt_bias and o_norm_w are always read from the
  * caller's buffers.  Errors: KDA_E_ARG, KDA_E_SHAPE (d_k != d_v, d_k not 64/128,
  * conv_k != 4, D % 32, ranks % 32 for Q8_0, ...), KDA_E_ALIGN, KDA_E_HIP. */
 int kda_model_create(const kda_dims* dims, const kda_layer* layers, kda_model** out);
@@ -213,8 +213,8 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
  * matrices (see kda_model_create), else 0.
  * KDA_Q_PERSISTENT: number of blocks of the one-launch decode, 0 if the model is
  * not eligible (it needs Q8_0 weights, or MXFP4 weights whose nonzero blocks all have a
- * scale 2^(e - 127) with e - 128 in [-24, 15], the KDA or the scalar gate (the safe gate
- * has no one-launch form), a pre-norm residual stack, d_k = d_v = 128,
+ * scale 2^(e - 127) with e - 128 in [-24, 15], any of the three gate forms, a pre-norm
+ * residual stack, d_k = d_v = 128,
  * H*d_v = D in {1024, 2048}, rank_f = rank_g in {32, 64, 128}, H <= 32, and one
  * co-resident block per CU with 2 H + D/32 + C/48 + ceil((proj_rows - C)/16) <= CUs).  For it kda_model_create allocates
  * ~130 KB of exchange words, flags and layer table, and a copy of every layer's projection
@@ -224,8 +224,8 @@ int kda_model_set_option(kda_model* m, int option, int64_t value);
  * the int8 code and half the block scale as the fp16 one; the scalar gate's one F_b row
  * and dt_bias a head enter repeated over the head's d_k channels): for a Q8_0 KDA-gate
  * stack the one-launch decode and every per-layer kernel read that copy
- * (KDA_Q_OWNS_WEIGHTS), for MXFP4 or the scalar gate the one-launch decode alone, so later
- * changes to the caller's weights reach it only through a new model. */
+ * (KDA_Q_OWNS_WEIGHTS), for MXFP4 or the other gate forms the one-launch decode alone, so
+ * later changes to the caller's weights reach it only through a new model. */
 typedef enum { KDA_Q_PERSISTENT = 0, KDA_Q_OWNS_WEIGHTS = 1 } kda_query;
 int kda_model_query(const kda_model* m, int what);
 
