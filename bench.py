@@ -188,12 +188,16 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     path = (f"one launch per token ({model.persistent_blocks()} blocks)" if one_launch
             else "per-layer kernels replayed as one hipGraph")
     log(f"[bench] path: {path}")
-    # each step's input row is copied into one fixed input buffer first (as a serving loop
-    # writes its next token's embedding), so that the captured graph of the per-layer path
-    # is replayed, not captured again for every new input pointer
+    # the per-layer path copies each step's input row into one fixed input buffer first (as
+    # a serving loop writes its next token's embedding), so that its captured graph is
+    # replayed, not captured again for every new input pointer; the one-launch kernel is a
+    # plain launch that takes any input pointer, so it reads the step's row where it lies
     xin = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
 
     def step(i):
+        if one_launch:
+            models[i % len(models)].decode_step(xs[i], y, st, ws)
+            return
         xin.copy_(xs[i])
         models[i % len(models)].decode_step(xin, y, st, ws)
 
