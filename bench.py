@@ -5,7 +5,8 @@ Default workload (the headline metric): the 34-layer KDA stack (D=2048, 16 heads
 d_k=d_v=128, all projections Q8_0, fp32 state [16][128][128] + 3-token conv window per
 layer, pre-RMSNorm residual stream), batch 1, synthetic seeded weights and inputs.  A step
 is one token through all 34 layers: one launch of the one-launch decode kernel
-(or, with --per-layer, the per-layer kernels replayed as one hipGraph).
+(or, with --per-layer, the per-layer kernels, launched directly or with --graph
+replayed as one hipGraph).
 
 Prints ONE JSON line: tokens/s over K timed steps, HBM roofline of the dominant kernel
 (timed with hipEvents on the launch stream), and the CPU oracle on a bounded sample.
@@ -19,7 +20,7 @@ Other workloads (--workload, one JSON line each, for the secondary measurements)
   prefill  one BF16 layer, B=4 x L=8192 chunked prefill (MFMA-bound)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--workload stack|layer|tiny|verify|prefill] [--per-layer] [--copies N]
+                    [--workload stack|layer|tiny|verify|prefill] [--per-layer] [--graph] [--copies N]
 """
 from __future__ import annotations
 
@@ -170,7 +171,7 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     xs = torch.from_numpy(np.ascontiguousarray(run.x[:, :, 0, :])).cuda()   # [steps][B][D]
     y = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
 
-    model.set_option(kda.KDA_OPT_GRAPH, 1)
+    model.set_option(kda.KDA_OPT_GRAPH, 1 if args.graph else 0)
     model.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
     one_launch = not args.per_layer and model.persistent_blocks() > 0 and B == 1
     models = [model]
@@ -181,21 +182,22 @@ def bench_stack(args, torch, synth, kda, w, run, model):
             m2 = kda.KdaModel(run.layers, n_heads=d.n_heads, d_k=d.d_k, d_v=d.d_v, wtype=w.wtype,
                               prenorm_residual=w.prenorm_residual, norm_eps=w.norm_eps,
                               l2_eps=w.l2_eps)
-            m2.set_option(kda.KDA_OPT_GRAPH, 1)
+            m2.set_option(kda.KDA_OPT_GRAPH, 1 if args.graph else 0)
             m2.set_option(kda.KDA_OPT_PERSISTENT, 0 if args.per_layer else 1)
             models.append(m2)
         log(f"[bench] {len(models)} weight copies used in turn")
     path = (f"one launch per token ({model.persistent_blocks()} blocks)" if one_launch
-            else "per-layer kernels replayed as one hipGraph")
+            else "per-layer kernels replayed as one hipGraph" if args.graph
+            else "per-layer kernels launched directly")
     log(f"[bench] path: {path}")
-    # the per-layer path copies each step's input row into one fixed input buffer first (as
-    # a serving loop writes its next token's embedding), so that its captured graph is
-    # replayed, not captured again for every new input pointer; the one-launch kernel is a
-    # plain launch that takes any input pointer, so it reads the step's row where it lies
+    # with --graph each step's input row is copied into one fixed input buffer first (as a
+    # serving loop writes its next token's embedding), so that the captured graph is
+    # replayed, not captured again for every new input pointer; launched directly (and the
+    # one-launch kernel always is) the kernels read the step's row where it lies
     xin = torch.empty((B, d.d_model), dtype=torch.float32, device="cuda")
 
     def step(i):
-        if one_launch:
+        if not args.graph:
             models[i % len(models)].decode_step(xs[i], y, st, ws)
             return
         xin.copy_(xs[i])
@@ -221,8 +223,7 @@ def bench_stack(args, torch, synth, kda, w, run, model):
     model.set_option(kda.KDA_OPT_TIMING, 1)
     model.timing(kda.KDA_K_PROJ, reset=True)
     for i in range(args.steps):
-        xin.copy_(xs[args.warmup + i])
-        model.decode_step(xin, y, st, ws)
+        model.decode_step(xs[args.warmup + i], y, st, ws)
     torch.cuda.synchronize()
     model.status()
     times = timed_kinds(model, kda, {"proj": kda.KDA_K_PROJ, "gates": kda.KDA_K_GATES,
@@ -312,17 +313,19 @@ def bench_verify(args, torch, synth, kda, w, run, model):
     xs = torch.from_numpy(np.ascontiguousarray(run.x)).cuda()             # [steps][B][T][D]
     ys = torch.empty((B, T, d.d_model), dtype=torch.float32, device="cuda")
     acc = torch.from_numpy(np.ascontiguousarray(run.accept).astype(np.int32)).cuda()
-    model.set_option(kda.KDA_OPT_GRAPH, 1)
-    # fixed input and accept buffers (a serving loop's draft batch and sampler output), so
-    # that the captured verify and commit graphs are replayed
+    model.set_option(kda.KDA_OPT_GRAPH, 1 if args.graph else 0)
+    # with --graph: fixed input and accept buffers (a serving loop's draft batch and sampler
+    # output), so that the captured verify and commit graphs are replayed
     xin = torch.empty((B, T, d.d_model), dtype=torch.float32, device="cuda")
     ain = torch.empty((B,), dtype=torch.int32, device="cuda")
 
     def step(i):
-        xin.copy_(xs[i])
-        model.verify_steps(xin, T, ys, st, vlog, ws)
-        ain.copy_(acc[i])
-        model.verify_commit(st, vlog, T, ain)      # recorded; folded into the next verify
+        if args.graph:
+            xin.copy_(xs[i])
+            ain.copy_(acc[i])
+        xi, ai = (xin, ain) if args.graph else (xs[i], acc[i])
+        model.verify_steps(xi, T, ys, st, vlog, ws)
+        model.verify_commit(st, vlog, T, ai)       # recorded; folded into the next verify
 
     for i in range(args.warmup):
         step(i)
@@ -362,6 +365,7 @@ def bench_verify(args, torch, synth, kda, w, run, model):
     config = {"workload": "kda-stack-34L-q8_0-verify-B8-T4", "layers": w.n_layers,
               "d_model": d.d_model, "heads": d.n_heads, "batch": B, "tokens_per_step": T,
               "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)",
+              "launch": "hipGraph replays" if args.graph else "kernels launched directly",
               "accepted_tokens_per_s": round(accepted / el, 1),
               "bytes_floor_per_step": floor, "step_hbm_gbs": round(gbs, 1),
               "step_hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "kernels": rounded(per)}
@@ -502,7 +506,10 @@ def main():
                     help="decode workloads: weight copies used in turn (8 keeps the BF16 layer "
                          "out of the last-level cache)")
     ap.add_argument("--per-layer", action="store_true",
-                    help="time the per-layer hipGraph decode instead of the one-launch step")
+                    help="time the per-layer decode instead of the one-launch step")
+    ap.add_argument("--graph", action="store_true",
+                    help="per-layer decode and verify: replay captured hipGraphs (inputs "
+                         "copied into fixed buffers) instead of launching the kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")

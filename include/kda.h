@@ -189,8 +189,13 @@ void kda_model_destroy(kda_model* m);
 
 /* Options. */
 typedef enum {
-  KDA_OPT_GRAPH = 0,       /* 1 (default): decode steps replay a captured hipGraph of all
-                              layers, re-captured when a pointer or the batch changes */
+  KDA_OPT_GRAPH = 0,       /* 1: decode, verify and commit replay a captured hipGraph of
+                              all layers, re-captured when a pointer or the batch changes;
+                              0 (default): the same kernels launched directly.  On MI355X
+                              with ROCm 7.2 a replay measured no faster than the launches
+                              (a single layer 2x slower a token, 34 layers 0.7-1.4 %
+                              slower); it is for callers that need a fixed host cost a
+                              step.  The one-launch decode never uses a graph. */
   KDA_OPT_TIMING = 1,      /* 1: record hipEvents around every kernel launch (no graph) */
   KDA_OPT_PERSISTENT = 2,  /* 1 (default): batch-1 decode of an eligible model runs every
                               layer in one launch (see kda_model_query) */

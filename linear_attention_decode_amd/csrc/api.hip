@@ -95,7 +95,7 @@ struct kda_model {
   int C = 0, Kq = 0, V = 0, proj_rows = 0, proj_stride = 0;
   float q_scale = 0.f;
   // options
-  bool use_graph = true;
+  bool use_graph = false;
   bool timing = false;
   // graph cache (decode, verify, commit)
   hipStream_t cap_stream = nullptr;
