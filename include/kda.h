@@ -297,8 +297,8 @@ int kda_decode_step_static(kda_model* m, const float* x_dev, float* y_dev, const
  * would have had (computed from the unchanged state; callers normally ignore it).  A
  * sequence with a nonzero entry is decoded exactly as by kda_decode_step.  Left padding is
  * a mask that is 0 until a sequence's first token, ragged lengths one that is 0 after its
- * last.  Runs the per-layer kernels (never the one-launch kernel), replayed as a hipGraph
- * keyed also on active_dev.  Errors as kda_decode_step, KDA_E_ARG for a null mask and
+ * last.  Runs the per-layer kernels (never the one-launch kernel); with KDA_OPT_GRAPH = 1
+ * they replay as a hipGraph keyed also on active_dev.  Errors as kda_decode_step, KDA_E_ARG for a null mask and
  * KDA_E_ALIGN for a mask that is not 4-byte aligned. */
 int kda_decode_step_masked(kda_model* m, const float* x_dev, float* y_dev, const kda_state* st,
                            const int32_t* active_dev, void* ws_dev, size_t ws_bytes,
